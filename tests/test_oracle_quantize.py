@@ -1,0 +1,94 @@
+"""Pins of the oracle's fixed-point encoding (CPU only).
+
+The pages fix int64 fixed-point cells (bonsai "9. Parallelism & determinism",
+"The idea") but not the scale.  The reading pinned here: k = 30 - e with
+2^(e-1) <= max|c| < 2^e, q = rint(c * 2^k) with ties to even.  These tests
+check it against hand-worked values, against exact sums of the raw floats
+(math.fsum) within the rounding bound, and against its range guarantee.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def test_hand_pin_round_half_even():
+    # M = 1 -> e = 1 -> k = 29.  2^-30 * 2^29 = 0.5 -> 0; 3 * 2^-30 * 2^29 = 1.5 -> 2.
+    g = np.array([1.0, 2.0 ** -30, 3 * 2.0 ** -30], dtype=np.float32)
+    q, k = oracle.quantize(g, require_nonneg=False)
+    assert k == 29
+    assert q.tolist() == [2 ** 29, 0, 2]
+
+
+def test_ties_to_even_both_signs():
+    # M = 2^29 - 2^5 ... pick M = 1.0 (k = 29) and values at exact half steps.
+    step = 2.0 ** -29
+    vals = [1.0, 0.5 * step, 1.5 * step, 2.5 * step, -0.5 * step, -1.5 * step, -2.5 * step,
+            3.5 * step]
+    q, k = oracle.quantize(np.array(vals, dtype=np.float32), require_nonneg=False)
+    assert k == 29
+    assert q.tolist() == [2 ** 29, 0, 2, 2, 0, -2, -2, 4]
+
+
+@pytest.mark.parametrize("m,expect_k", [
+    (1.0, 29), (0.5, 30), (0.75, 30), (1.5, 29), (2.0, 28), (3.0, 28),
+    (2.0 ** 31, -2), (1e-30, 30 - math.frexp(np.float32(1e-30))[1]),
+])
+def test_scale_exponent(m, expect_k):
+    q, k = oracle.quantize(np.array([m, -m / 4], dtype=np.float32), require_nonneg=False)
+    assert k == expect_k
+    assert abs(int(q[0])) <= 2 ** 30
+
+
+def test_zero_vector_gives_k0():
+    q, k = oracle.quantize(np.zeros(5, dtype=np.float32), require_nonneg=True)
+    assert k == 0 and not q.any()
+
+
+def test_negative_zero_is_zero_even_for_hessian():
+    q, k = oracle.quantize(np.array([-0.0, 0.5], dtype=np.float32), require_nonneg=True)
+    assert q.tolist() == [0, 2 ** 29]
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_nonfinite_rejected(bad):
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.quantize(np.array([0.5, bad], dtype=np.float32), require_nonneg=False)
+    assert e.value.status == oracle.E_NONFINITE
+
+
+def test_negative_hessian_rejected():
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize(np.array([0.5, -1e-20], dtype=np.float32), require_nonneg=True)
+    # the same vector is a valid gradient
+    oracle.quantize(np.array([0.5, -1e-20], dtype=np.float32), require_nonneg=False)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_range_and_sum_error_bound(seed):
+    """|q| <= 2^30, max element hits [2^29, 2^30], and for any subset the
+    fixed-point sum differs from the exact float sum by <= count * 2^-(k+1)."""
+    rng = np.random.default_rng(seed)
+    n = 5000
+    scale = 10.0 ** rng.uniform(-20, 20)
+    c = (rng.standard_normal(n) * scale).astype(np.float32)
+    q, k = oracle.quantize(c, require_nonneg=False)
+    assert np.abs(q.astype(np.int64)).max() <= 2 ** 30
+    assert np.abs(q.astype(np.int64)).max() >= 2 ** 29
+    for _ in range(5):
+        sub = rng.random(n) < rng.uniform(0.01, 1.0)
+        cnt = int(sub.sum())
+        exact = math.fsum(float(x) for x in c[sub])
+        fixed = math.ldexp(float(int(q[sub].astype(np.int64).sum())), -k)
+        assert abs(fixed - exact) <= cnt * math.ldexp(1.0, -(k + 1)) * (1 + 1e-12) + abs(exact) * 2 ** -52
+
+
+def test_wide_dynamic_range_exact_where_representable():
+    # values that are multiples of 2^-k encode exactly
+    c = np.array([1.0, 0.25, -0.125, 2.0 ** -29, -(2.0 ** -28)], dtype=np.float32)
+    q, k = oracle.quantize(c, require_nonneg=False)
+    assert k == 29
+    back = [math.ldexp(int(v), -k) for v in q]
+    assert back == [float(x) for x in c]
