@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Level histogram build benchmark on one MI355X.
+
+A step is one pass of the whole device path over one batch of synthetic input:
+begin_tree (quantize), then every level's build_level + subtract_siblings +
+find_splits.  The default workload is the tall-narrow case: 10,000,000 rows x
+28 u8 features, one depthwise tree, levels 0..7.  Its row lists per level are
+fixed once before timing (the host partition is not part of the device path),
+so the timed steps replay the same tree with every input resident in HBM.
+
+Prints one JSON line:  value = built cells (rows x features of every node
+built from rows) per second over the timed steps, in G cell-updates/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "level histogram build G cell-updates/s (rows x features) + % of HBM peak"
+
+WORKLOAD_NAMES = {
+    "c1": "tiny root 4,096 x 8 u8 (256 bins), root build + split",
+    "c2": "depth-6 level 1,000,000 x 100 u8 (80 uniform + 20 skewed features), 32 Dirichlet nodes: build 16 smaller + subtract + split",
+    "c3": "tall narrow 10,000,000 x 28 u8 (256 bins), logistic grad/hess, one depthwise tree levels 0-7",
+    "c4": "wide 131,072 x 16,384 u8 (256 bins), root + level 3 (8 nodes): build + subtract + split",
+    "c5": "high-cardinality 2,000,000 x 50 u16 (1,024 bins + 40% missing), 128 Dirichlet nodes: build 64 smaller + subtract + split",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Plan:
+    """What one step enqueues, and its work accounting."""
+
+    def __init__(self):
+        self.levels = []          # (kind, LevelPlan, parent_hist)
+        self.cells = 0            # built rows x features per step
+        self.fill_bytes = 0       # algorithmic bytes of the build kernels per step
+        self.level_notes = []
+
+
+def fill_alg_bytes(w, built_rows: int, n_built_nodes: int, root: bool) -> int:
+    """Algorithmic bytes of one build: bins w*cells, (g,h) 8 B/row (+4 B row
+    index below the root), and one 16 B write per output slot."""
+    wbytes = w.bins.dtype.itemsize
+    per_row = 8 if root else 12
+    return (wbytes * built_rows * w.n_features + per_row * built_rows
+            + 16 * w.n_features * w.n_slots * n_built_nodes)
+
+
+def prepare(ctx, w, g, h, torch):
+    from histogram_gradient_boosted_amd import tree
+    plan = Plan()
+    if w.kind == "tree":
+        plans = tree.plan_tree(ctx, w.bins, w.n_bins, g, h, w.depth, w.lam, w.gamma)
+        plan.tree = plans
+        for lp in plans:
+            nb = 1 if lp.depth == 0 else lp.n_pairs
+            plan.cells += lp.built_rows * w.n_features
+            plan.fill_bytes += fill_alg_bytes(w, lp.built_rows, nb, lp.depth == 0)
+            plan.level_notes.append({"depth": lp.depth, "nodes": lp.n_nodes, "built_rows": lp.built_rows})
+        return plan
+    plan.tree = None
+    ctx.begin_tree(g, h)
+    dev = torch.device("cuda", ctx.device)
+    if w.kind in ("root", "root+level"):
+        rp = tree.root_plan(ctx)
+        plan.levels.append(("root", rp, None))
+        plan.cells += w.n_rows * w.n_features
+        plan.fill_bytes += fill_alg_bytes(w, w.n_rows, 1, True)
+        plan.level_notes.append({"depth": 0, "nodes": 1, "built_rows": w.n_rows})
+    if w.kind in ("level", "root+level"):
+        L = w.level
+        parents = torch.empty((L.n_pairs, w.n_features, w.n_slots, 2), dtype=torch.int64, device=dev)
+        ctx.build_level(parents, torch.from_numpy(L.parent_row_index).to(dev),
+                        L.parent_offsets.astype(np.int32))
+        lp = tree.level_plan_from_children(ctx, 1, L.children_row_index, L.children_offsets,
+                                           np.arange(L.n_pairs, dtype=np.int32))
+        plan.levels.append(("level", lp, parents))
+        plan.cells += lp.built_rows * w.n_features
+        plan.fill_bytes += fill_alg_bytes(w, lp.built_rows, lp.n_pairs, False)
+        plan.level_notes.append({"nodes": lp.n_nodes, "built_rows": lp.built_rows})
+    ctx.sync()
+    return plan
+
+
+def step(ctx, w, plan, g, h):
+    from histogram_gradient_boosted_amd import tree
+    if plan.tree is not None:
+        tree.replay_tree(ctx, plan.tree, g, h, w.lam, w.gamma)
+        return
+    ctx.begin_tree(g, h)
+    for kind, lp, parents in plan.levels:
+        if kind == "root":
+            tree.run_root(ctx, lp, w.lam, w.gamma)
+        else:
+            tree.run_level(ctx, lp, parents, w.lam, w.gamma)
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The oracle, as it stands, on the host: the same step (quantize, builds of
+    the built nodes, subtraction, split scan), grown with its own partition."""
+    import oracle
+    oracle.build()
+    t_work = 0.0
+    cells = 0
+
+    def timed(fn, *a):
+        nonlocal t_work
+        t0 = time.perf_counter()
+        r = fn(*a)
+        t_work += time.perf_counter() - t0
+        return r
+
+    qg, kg = timed(oracle.quantize, w.grad, False)
+    qh, kh = timed(oracle.quantize, w.hess, True)
+    B, M = w.n_bins, w.has_missing
+    sample = "full step"
+    if w.kind in ("root", "root+level", "tree"):
+        hist = timed(oracle.build_hist, w.bins, B, M, qg, qh)
+        cells += w.n_rows * w.n_features
+        sp = timed(oracle.find_splits, hist, B, M, kg, kh, w.lam, w.gamma)
+    if w.kind == "tree":
+        rows, offs = None, None
+        parent = hist
+        for d in range(1, w.depth):
+            if t_work > budget_s:
+                sample = f"levels 0..{d - 1} of the tree (time budget)"
+                break
+            rows, offs = oracle.partition(w.bins, B, rows, offs, sp)   # untimed host step
+            if len(offs) == 1:
+                break
+            counts = np.diff(offs)
+            bir = (counts[1::2] < counts[0::2]).astype(np.uint8)
+            P = len(bir)
+            blist = [rows[offs[2 * i + bir[i]]:offs[2 * i + bir[i] + 1]] for i in range(P)]
+            boffs = np.zeros(P + 1, np.int64)
+            np.cumsum([len(x) for x in blist], out=boffs[1:])
+            brows = np.concatenate(blist).astype(np.int32)
+            built = timed(oracle.build_hist, w.bins, B, M, qg, qh, brows, boffs)
+            cells += int(boffs[-1]) * w.n_features
+            child = np.zeros((2 * P,) + built.shape[1:], np.int64)
+            child[2 * np.arange(P) + bir] = built
+            # parents of this level are the previous level's split nodes, in order
+            split_nodes = np.nonzero(sp["feature"] >= 0)[0]
+            timed(oracle.subtract, parent[split_nodes], child, bir)
+            sp = timed(oracle.find_splits, child, B, M, kg, kh, w.lam, w.gamma)
+            parent = child
+    if w.kind in ("level", "root+level"):
+        L = w.level
+        parents = oracle.build_hist(w.bins, B, M, qg, qh, L.parent_row_index, L.parent_offsets)
+        built = timed(oracle.build_hist, w.bins, B, M, qg, qh, L.built_row_index, L.built_offsets)
+        cells += int(L.built_offsets[-1]) * w.n_features
+        child = np.zeros((2 * L.n_pairs,) + built.shape[1:], np.int64)
+        child[L.built_slots] = built
+        timed(oracle.subtract, parents, child, L.built_is_right)
+        timed(oracle.find_splits, child, B, M, kg, kh, w.lam, w.gamma)
+    return {"value": cells / t_work / 1e9, "unit": "G cell-updates/s", "cores": 1,
+            "kind": "oracle", "seconds": round(t_work, 3),
+            "sample": f"{sample} of workload {w.name}: serial C oracle (gcc -O2), 1 thread, "
+                      f"{cells} built cells"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from histogram_gradient_boosted_amd import binding, synth
+
+    if not torch.cuda.is_available() or not binding.available():
+        print("no HIP device available", file=sys.stderr)
+        sys.exit(1)
+
+    t0 = time.time()
+    w = synth.make(args.config, seed=args.seed)
+    log(f"[bench] workload {args.config}: {w.n_rows} x {w.n_features}, generated in {time.time() - t0:.1f}s")
+    torch.cuda.set_device(0)
+    ctx = binding.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    plan = prepare(ctx, w, g, h, torch)
+    log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
+
+    for _ in range(args.warmup):
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+
+    ctx.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prof = {k: ctx.profile_query(k) for k in binding.KERNELS}
+    ctx.profile_enable(False)
+
+    # the same steps without per-kernel events, for the event overhead
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall_noprof = time.perf_counter() - t1
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = plan.cells * args.steps / wall / 1e9
+    fill_ms, fill_launches = prof["fill"]
+    fill_ms_step = fill_ms / args.steps
+    achieved = plan.fill_bytes / (fill_ms_step * 1e-3) / 1e9 if fill_ms_step > 0 else 0.0
+    breakdown = {k: round(v[0] / args.steps, 4) for k, v in prof.items()}
+    log(f"[bench] per-step device ms by kernel class: {breakdown}; launches {{{', '.join(f'{k}: {v[1] // args.steps}' for k, v in prof.items())}}}")
+    log(f"[bench] wall ms/step {ms_per_step:.3f} (events on), {wall_noprof * 1e3 / args.steps:.3f} (events off)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "G cell-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
+                   "rows": w.n_rows, "features": w.n_features, "bins": w.n_bins,
+                   "built_cells_per_step": plan.cells, "levels": plan.level_notes},
+        "build_only_gcells_per_s": round(plan.cells / (fill_ms_step + breakdown["gather"] + breakdown["zero"]) / 1e6, 3)
+        if fill_ms_step > 0 else None,
+        "ms_per_step_events_off": round(wall_noprof * 1e3 / args.steps, 4),
+        "kernel_ms_per_step": breakdown,
+        "roofline": {"bound": "hbm", "kernel": "k_fill_lds", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "alg_bytes_per_step": plan.fill_bytes,
+                     "launches_per_step": fill_launches // max(args.steps, 1),
+                     "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
+    }
+    ctx.close()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""Thin ctypes binding over libhgb.so (include/hgb.h).
+
+Argument marshalling only: torch tensors carry device memory and the stream;
+every step of the computation runs in the library's HIP kernels.  The binding
+checks what the C ABI cannot see -- tensor devices, dtypes, contiguity and
+buffer sizes -- so that no kernel is ever handed a buffer too small for it.
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhgb.so")
+
+HGB_OK, HGB_E_INVALID, HGB_E_STATE, HGB_E_UNSUPPORTED, HGB_E_NONFINITE, HGB_E_DEVICE = range(6)
+_STATUS_NAMES = {0: "HGB_OK", 1: "HGB_E_INVALID", 2: "HGB_E_STATE", 3: "HGB_E_UNSUPPORTED",
+                 4: "HGB_E_NONFINITE", 5: "HGB_E_DEVICE"}
+MAX_SLOTS = 4096
+
+# hgb_split, 56 bytes
+SPLIT_DTYPE = np.dtype([
+    ("feature", "<i4"), ("bin", "<i4"), ("default_left", "<i4"), ("pad", "<i4"),
+    ("gain", "<f8"),
+    ("g_left", "<i8"), ("h_left", "<i8"), ("g_total", "<i8"), ("h_total", "<i8"),
+])
+SPLIT_BYTES = 56
+
+EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb_sync",
+            "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
+            "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
+            "hgb_profile_query")
+
+KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5}
+
+
+class HGBError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libhgb.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: run __graft_entry__.build() "
+                          "(or python -m histogram_gradient_boosted_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+    lib.hgb_available.argtypes = []
+    lib.hgb_available.restype = c_int
+    lib.hgb_create.argtypes = [c_int, vp, ctypes.POINTER(vp)]
+    lib.hgb_create.restype = c_int
+    lib.hgb_destroy.argtypes = [vp]
+    lib.hgb_destroy.restype = None
+    lib.hgb_last_error.argtypes = [vp]
+    lib.hgb_last_error.restype = ctypes.c_char_p
+    lib.hgb_sync.argtypes = [vp]
+    lib.hgb_sync.restype = c_int
+    lib.hgb_upload_bins.argtypes = [vp, vp, c_int, c_int, i32, i32, i32, i32]
+    lib.hgb_upload_bins.restype = c_int
+    lib.hgb_begin_tree.argtypes = [vp, vp, vp]
+    lib.hgb_begin_tree.restype = c_int
+    lib.hgb_get_scales.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.hgb_get_scales.restype = c_int
+    lib.hgb_build_level.argtypes = [vp, vp, vp, i32, vp, vp]
+    lib.hgb_build_level.restype = c_int
+    lib.hgb_subtract_siblings.argtypes = [vp, vp, vp, vp, vp, i32]
+    lib.hgb_subtract_siblings.restype = c_int
+    lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
+    lib.hgb_find_splits.restype = c_int
+    lib.hgb_profile_enable.argtypes = [vp, c_int]
+    lib.hgb_profile_enable.restype = c_int
+    lib.hgb_profile_query.argtypes = [vp, c_int, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]
+    lib.hgb_profile_query.restype = c_int
+    _lib = lib
+    return lib
+
+
+def available() -> bool:
+    """hgb_available(): a usable HIP device is present."""
+    return bool(load().hgb_available())
+
+
+def _i32_host(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def splits_to_numpy(t) -> np.ndarray:
+    """View a uint8 tensor/array of N*56 bytes (hgb_split records) as a record array."""
+    import torch
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.frombuffer(np.ascontiguousarray(t).tobytes(), dtype=SPLIT_DTYPE)
+
+
+class Context:
+    """One hgb_ctx: resident bins, the current tree's fixed-point (g, h), scratch.
+
+    stream: a torch.cuda.Stream (default: the current stream of `device`)."""
+
+    def __init__(self, device: int = 0, stream=None):
+        import torch
+        self._torch = torch
+        self._lib = load()
+        self.device = int(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self.stream = stream
+        h = ctypes.c_void_p()
+        st = self._lib.hgb_create(self.device, ctypes.c_void_p(stream.cuda_stream), ctypes.byref(h))
+        if st != HGB_OK:
+            raise HGBError(st, "hgb_create failed")
+        self._h = h
+        self.n_rows = self.n_features = self.n_bins = self.n_slots = 0
+        self.has_missing = False
+
+    # -- plumbing ---------------------------------------------------------
+    def _check(self, st: int, what: str):
+        if st != HGB_OK:
+            msg = self._lib.hgb_last_error(self._h)
+            raise HGBError(st, f"{what}: {msg.decode() if msg else ''}")
+
+    def _dev(self, t, name, dtype=None, numel=None):
+        torch = self._torch
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device.index != self.device:
+            raise ValueError(f"{name} must be a CUDA tensor on device {self.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if numel is not None and t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+        return ctypes.c_void_p(t.data_ptr())
+
+    @property
+    def node_elems(self) -> int:
+        return self.n_features * self.n_slots * 2
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.hgb_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sync(self):
+        self._check(self._lib.hgb_sync(self._h), "sync")
+
+    def profile_enable(self, on: bool = True):
+        self._check(self._lib.hgb_profile_enable(self._h, int(bool(on))), "profile_enable")
+
+    def profile_query(self, kernel: str):
+        """(total device ms, launches) of a kernel class since the last reset."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        self._check(self._lib.hgb_profile_query(self._h, KERNELS[kernel], ctypes.byref(ms),
+                                                ctypes.byref(n)), "profile_query")
+        return float(ms.value), int(n.value)
+
+    # -- the five verbs ---------------------------------------------------
+    def upload_bins(self, bins, n_bins: int, has_missing: bool):
+        """bins: [F][n] uint8/uint16 numpy array (host) or 1-/2-byte CUDA tensor."""
+        torch = self._torch
+        if isinstance(bins, torch.Tensor):
+            if bins.element_size() not in (1, 2) or bins.dim() != 2:
+                raise ValueError("bins tensor must be 2-D with 1- or 2-byte elements")
+            ptr = self._dev(bins, "bins")
+            w, on_dev = bins.element_size(), 1
+            F, n = bins.shape
+            keep = bins
+        else:
+            keep = np.ascontiguousarray(bins)
+            if keep.dtype not in (np.uint8, np.uint16) or keep.ndim != 2:
+                raise ValueError("bins array must be 2-D uint8 or uint16")
+            ptr = ctypes.c_void_p(keep.ctypes.data)
+            w, on_dev = keep.dtype.itemsize, 0
+            F, n = keep.shape
+        self._check(self._lib.hgb_upload_bins(self._h, ptr, w, on_dev, int(n), int(F),
+                                              int(n_bins), int(bool(has_missing))), "upload_bins")
+        del keep
+        self.n_rows, self.n_features, self.n_bins = int(n), int(F), int(n_bins)
+        self.has_missing = bool(has_missing)
+        self.n_slots = self.n_bins + (1 if self.has_missing else 0)
+
+    def begin_tree(self, grad, hess):
+        torch = self._torch
+        g = self._dev(grad, "grad", torch.float32, self.n_rows)
+        h = self._dev(hess, "hess", torch.float32, self.n_rows)
+        self._check(self._lib.hgb_begin_tree(self._h, g, h), "begin_tree")
+
+    def get_scales(self):
+        kg, kh = ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.hgb_get_scales(self._h, ctypes.byref(kg), ctypes.byref(kh)),
+                    "get_scales")
+        return int(kg.value), int(kh.value)
+
+    def build_level(self, hist, row_index=None, node_offsets=None, out_slot=None):
+        """Histograms of a level's nodes into `hist` ([slots][F][S][2] int64 CUDA tensor)."""
+        torch = self._torch
+        if row_index is None:
+            n_nodes = 1
+            offs = None
+            ri = None
+        else:
+            offs = _i32_host(node_offsets)
+            n_nodes = int(offs.shape[0]) - 1
+            ri = self._dev(row_index, "row_index", torch.int32, int(offs[-1]) if n_nodes >= 0 else 0)
+        slots = None if out_slot is None else _i32_host(out_slot)
+        top = (int(slots.max()) + 1) if slots is not None and slots.size else n_nodes
+        hp = self._dev(hist, "hist", torch.int64, top * self.node_elems)
+        self._check(self._lib.hgb_build_level(
+            self._h, ri,
+            None if offs is None else offs.ctypes.data_as(ctypes.c_void_p), n_nodes, hp,
+            None if slots is None else slots.ctypes.data_as(ctypes.c_void_p)), "build_level")
+
+    def subtract_siblings(self, parent, child, built_is_right, parent_slot=None):
+        """child[2i + 1 - r] = parent[parent_slot[i]] - child[2i + r], r = built_is_right[i]."""
+        torch = self._torch
+        bir = np.ascontiguousarray(np.asarray(built_is_right), dtype=np.uint8)
+        P = int(bir.shape[0])
+        ps = None if parent_slot is None else _i32_host(parent_slot)
+        if ps is not None and ps.shape[0] != P:
+            raise ValueError("parent_slot must have one entry per pair")
+        ptop = (int(ps.max()) + 1) if ps is not None and P else P
+        pp = self._dev(parent, "parent", torch.int64, ptop * self.node_elems)
+        cp = self._dev(child, "child", torch.int64, 2 * P * self.node_elems)
+        self._check(self._lib.hgb_subtract_siblings(
+            self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
+            None if ps is None else ps.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings")
+
+    def find_splits(self, hist, n_nodes: int, lam: float, gamma: float, out):
+        """out: uint8 CUDA tensor of at least n_nodes * 56 bytes (hgb_split records)."""
+        torch = self._torch
+        hp = self._dev(hist, "hist", torch.int64, int(n_nodes) * self.node_elems)
+        op = self._dev(out, "out", torch.uint8, int(n_nodes) * SPLIT_BYTES)
+        self._check(self._lib.hgb_find_splits(self._h, hp, int(n_nodes), float(lam),
+                                              float(gamma), op), "find_splits")

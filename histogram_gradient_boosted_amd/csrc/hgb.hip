@@ -1,0 +1,635 @@
+// hgb: C ABI of the level histogram build (see include/hgb.h for the contract).
+//
+// Host side of the library: the context, argument validation, per-call launch
+// planning and the staging of small plans to the device.  The kernels live in
+// hgb_kernels.h.
+#include "hgb.h"
+#include "hgb_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace hgb;
+
+namespace {
+
+// LDS bytes one fill block may use for its (g, h) tile.
+constexpr int kFillLdsBudget = 64 * 1024;
+constexpr int kFillThreads = 256;
+constexpr int kStages = 4;
+
+struct Stage {
+    void* host = nullptr;
+    void* dev = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+
+}  // namespace
+
+struct hgb_ctx {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    std::string err;
+
+    // dataset plane
+    void* bins = nullptr;
+    int bin_bytes = 0;
+    int64_t n = 0;
+    int F = 0, B = 0, S = 0, has_missing = 0;
+    bool have_data = false;
+
+    // gradient plane
+    int2* q = nullptr;
+    int64_t q_cap = 0;
+    int k_g = 0, k_h = 0;
+    bool have_tree = false;
+
+    // level scratch
+    int2* gh = nullptr;
+    int64_t gh_cap = 0;
+    FeatureBest* best = nullptr;
+    int64_t best_cap = 0;
+    long long* totals = nullptr;
+    int64_t totals_cap = 0;
+
+    // small device words: [0..1] max patterns, [2] error flags
+    uint32_t* dev_words = nullptr;
+    uint32_t* host_words = nullptr;   // pinned
+
+    Stage stage[kStages];
+    int stage_next = 0;
+
+    // optional per-kernel timing
+    bool prof = false;
+    std::vector<hipEvent_t> ev_pool;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending[HGB_KERNEL_COUNT];
+    double prof_ms[HGB_KERNEL_COUNT] = {};
+    int64_t prof_launches[HGB_KERNEL_COUNT] = {};
+};
+
+namespace {
+
+hgb_status fail(hgb_ctx* c, hgb_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+    return st;
+}
+
+#define HGB_HIP(c, expr)                                                                   \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail((c), HGB_E_DEVICE, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+#define HGB_LAUNCHED(c, what)                                                              \
+    do {                                                                                   \
+        hipError_t e_ = hipGetLastError();                                                 \
+        if (e_ != hipSuccess)                                                              \
+            return fail((c), HGB_E_DEVICE, "launch of %s failed: %s", what,                \
+                        hipGetErrorString(e_));                                            \
+    } while (0)
+
+template <typename T>
+hgb_status grow(hgb_ctx* c, T** p, int64_t* cap, int64_t need)
+{
+    if (need <= *cap) return HGB_OK;
+    if (*p) {
+        HGB_HIP(c, hipStreamSynchronize(c->stream));
+        HGB_HIP(c, hipFree(*p));
+        *p = nullptr;
+        *cap = 0;
+    }
+    int64_t want = std::max<int64_t>(need, 1024);
+    HGB_HIP(c, hipMalloc((void**)p, sizeof(T) * (size_t)want));
+    *cap = want;
+    return HGB_OK;
+}
+
+// Copy `bytes` of host data to a device staging buffer on the stream.  The
+// stage is released (event recorded) by stage_release after its consumers have
+// been enqueued; a stage is reused only once that event has completed.
+hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
+{
+    Stage& s = c->stage[c->stage_next];
+    c->stage_next = (c->stage_next + 1) % kStages;
+    if (s.pending) {
+        HGB_HIP(c, hipEventSynchronize(s.ev));
+        s.pending = false;
+    }
+    if (bytes > s.cap) {
+        if (s.host) HGB_HIP(c, hipHostFree(s.host));
+        if (s.dev) HGB_HIP(c, hipFree(s.dev));
+        s.host = s.dev = nullptr;
+        size_t want = std::max<size_t>(bytes, 4096);
+        HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
+        HGB_HIP(c, hipMalloc(&s.dev, want));
+        s.cap = want;
+    }
+    if (!s.ev) HGB_HIP(c, hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+    if (bytes) {
+        std::memcpy(s.host, src, bytes);
+        HGB_HIP(c, hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, c->stream));
+    }
+    *out = &s;
+    return HGB_OK;
+}
+
+hgb_status stage_release(hgb_ctx* c, Stage* s)
+{
+    HGB_HIP(c, hipEventRecord(s->ev, c->stream));
+    s->pending = true;
+    return HGB_OK;
+}
+
+hipEvent_t pool_event(hgb_ctx* c)
+{
+    if (!c->ev_pool.empty()) {
+        hipEvent_t e = c->ev_pool.back();
+        c->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets the launches of one kernel class with events when timing is on.
+struct ProfScope {
+    hgb_ctx* c;
+    int kernel;
+    hipEvent_t start = nullptr;
+    ProfScope(hgb_ctx* ctx, int k) : c(ctx), kernel(k)
+    {
+        if (!c->prof) return;
+        start = pool_event(c);
+        if (start && hipEventRecord(start, c->stream) != hipSuccess) {
+            c->ev_pool.push_back(start);
+            start = nullptr;
+        }
+    }
+    ~ProfScope()
+    {
+        if (!start) return;
+        hipEvent_t stop = pool_event(c);
+        if (stop && hipEventRecord(stop, c->stream) == hipSuccess) {
+            c->ev_pending[kernel].emplace_back(start, stop);
+        } else {
+            c->ev_pool.push_back(start);
+            if (stop) c->ev_pool.push_back(stop);
+        }
+    }
+};
+
+int grid_for(int64_t work, int threads, int cap)
+{
+    int64_t g = (work + threads - 1) / threads;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
+}
+
+int fill_tile_features(int S, int F)
+{
+    int t = kFillLdsBudget / (S * 16);
+    return std::max(1, std::min(t, F));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hgb_available(void)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) return 0;
+    return n > 0 ? 1 : 0;
+}
+
+hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
+{
+    if (!out) return HGB_E_INVALID;
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return HGB_E_DEVICE;
+    if (device < 0 || device >= n) return HGB_E_INVALID;
+    if (hipSetDevice(device) != hipSuccess) return HGB_E_DEVICE;
+    hgb_ctx* c = new hgb_ctx();
+    c->device = device;
+    c->stream = (hipStream_t)hip_stream;
+    if (hipMalloc((void**)&c->dev_words, 64) != hipSuccess ||
+        hipHostMalloc((void**)&c->host_words, 64, hipHostMallocDefault) != hipSuccess ||
+        hipMemset(c->dev_words, 0, 64) != hipSuccess) {
+        hgb_destroy(c);
+        return HGB_E_DEVICE;
+    }
+    *out = c;
+    return HGB_OK;
+}
+
+void hgb_destroy(hgb_ctx* c)
+{
+    if (!c) return;
+    // Best-effort teardown: errors here have nowhere to go.
+    (void)hipSetDevice(c->device);
+    (void)hipStreamSynchronize(c->stream);
+    for (Stage& s : c->stage) {
+        if (s.ev) (void)hipEventDestroy(s.ev);
+        if (s.host) (void)hipHostFree(s.host);
+        if (s.dev) (void)hipFree(s.dev);
+    }
+    for (auto& v : c->ev_pending)
+        for (auto& pr : v) {
+            (void)hipEventDestroy(pr.first);
+            (void)hipEventDestroy(pr.second);
+        }
+    for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+    (void)hipFree(c->bins);
+    (void)hipFree(c->q);
+    (void)hipFree(c->gh);
+    (void)hipFree(c->best);
+    (void)hipFree(c->totals);
+    (void)hipFree(c->dev_words);
+    (void)hipHostFree(c->host_words);
+    delete c;
+}
+
+const char* hgb_last_error(const hgb_ctx* c)
+{
+    return c ? c->err.c_str() : "null context";
+}
+
+hgb_status hgb_sync(hgb_ctx* c)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    HGB_HIP(c, hipSetDevice(c->device));
+    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
+                              c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    uint32_t flags = c->host_words[2];
+    if (flags) {
+        k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words + 2, 1);
+        HGB_LAUNCHED(c, "k_clear_u32");
+        HGB_HIP(c, hipStreamSynchronize(c->stream));
+        if (flags & kErrRowIndex)
+            return fail(c, HGB_E_INVALID, "a row index outside [0, n_rows) was skipped");
+    }
+    return HGB_OK;
+}
+
+hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_device,
+                           int32_t n_rows, int32_t n_features, int32_t n_bins,
+                           int32_t has_missing)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!bins || n_rows <= 0 || n_features <= 0 || n_bins <= 0)
+        return fail(c, HGB_E_INVALID, "upload_bins: empty matrix or null pointer");
+    if (bin_bytes != 1 && bin_bytes != 2)
+        return fail(c, HGB_E_INVALID, "upload_bins: bin_bytes must be 1 or 2");
+    if (n_features > 0xffff) return fail(c, HGB_E_UNSUPPORTED, "upload_bins: more than 65535 features");
+    const int S = n_bins + (has_missing ? 1 : 0);
+    const int max_value = bin_bytes == 1 ? 255 : 65535;
+    if (S - 1 > max_value)
+        return fail(c, HGB_E_INVALID, "upload_bins: %d slots do not fit %d-byte bins", S, bin_bytes);
+    if (S > HGB_MAX_SLOTS)
+        return fail(c, HGB_E_UNSUPPORTED, "upload_bins: %d slots exceed the LDS plan (%d)", S,
+                    HGB_MAX_SLOTS);
+    HGB_HIP(c, hipSetDevice(c->device));
+    c->have_tree = false;
+    c->have_data = false;
+    const int64_t total = (int64_t)n_rows * n_features;
+    const size_t bytes = (size_t)total * bin_bytes;
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    if (c->bins) {
+        HGB_HIP(c, hipFree(c->bins));
+        c->bins = nullptr;
+    }
+    HGB_HIP(c, hipMalloc(&c->bins, bytes));
+    HGB_HIP(c, hipMemcpyAsync(c->bins, bins, bytes,
+                              on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                              c->stream));
+    k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 1);
+    HGB_LAUNCHED(c, "k_clear_u32");
+    const int grid = grid_for(total, 256, 4096);
+    if (bin_bytes == 1)
+        k_bins_max<uint8_t><<<grid, 256, 0, c->stream>>>((const uint8_t*)c->bins, total, c->dev_words);
+    else
+        k_bins_max<uint16_t><<<grid, 256, 0, c->stream>>>((const uint16_t*)c->bins, total, c->dev_words);
+    HGB_LAUNCHED(c, "k_bins_max");
+    HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 4, hipMemcpyDeviceToHost, c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    if (c->host_words[0] >= (uint32_t)S)
+        return fail(c, HGB_E_INVALID, "upload_bins: stored value %u is not a slot (S = %d)",
+                    c->host_words[0], S);
+    c->bin_bytes = bin_bytes;
+    c->n = n_rows;
+    c->F = n_features;
+    c->B = n_bins;
+    c->S = S;
+    c->has_missing = has_missing ? 1 : 0;
+    c->have_data = true;
+    return HGB_OK;
+}
+
+hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_data) return fail(c, HGB_E_STATE, "begin_tree before upload_bins");
+    if (!grad || !hess) return fail(c, HGB_E_INVALID, "begin_tree: null gradient pointer");
+    HGB_HIP(c, hipSetDevice(c->device));
+    c->have_tree = false;
+    hgb_status st = grow(c, &c->q, &c->q_cap, c->n);
+    if (st != HGB_OK) return st;
+    k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 2);
+    HGB_LAUNCHED(c, "k_clear_u32");
+    {
+        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
+        k_grad_hess_max<<<grid_for(c->n, 256, 2048), 256, 0, c->stream>>>(grad, hess, c->n,
+                                                                           c->dev_words);
+    }
+    HGB_LAUNCHED(c, "k_grad_hess_max");
+    HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    const uint32_t pg = c->host_words[0], ph = c->host_words[1];
+    if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
+    if (ph >= 0x7f800000u)
+        return fail(c, HGB_E_NONFINITE, "begin_tree: NaN, Inf or negative hessian");
+    int k[2];
+    const uint32_t pat[2] = {pg, ph};
+    for (int i = 0; i < 2; ++i) {
+        float m;
+        std::memcpy(&m, &pat[i], 4);
+        if (m == 0.0f) {
+            k[i] = 0;
+        } else {
+            int e = 0;
+            (void)std::frexp((double)m, &e);
+            k[i] = 30 - e;
+        }
+    }
+    c->k_g = k[0];
+    c->k_h = k[1];
+    {
+        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
+        k_quantize<<<grid_for(c->n, 256, 4096), 256, 0, c->stream>>>(
+            grad, hess, c->n, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
+    }
+    HGB_LAUNCHED(c, "k_quantize");
+    c->have_tree = true;
+    return HGB_OK;
+}
+
+hgb_status hgb_get_scales(const hgb_ctx* c, int32_t* k_g, int32_t* k_h)
+{
+    if (!c || !k_g || !k_h) return HGB_E_INVALID;
+    if (!c->have_tree) return HGB_E_STATE;
+    *k_g = c->k_g;
+    *k_h = c->k_h;
+    return HGB_OK;
+}
+
+hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
+                           int32_t n_nodes, int64_t* hist, const int32_t* out_slot)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "build_level before begin_tree");
+    if (!hist) return fail(c, HGB_E_INVALID, "build_level: null histogram buffer");
+    if (n_nodes < 1 || n_nodes > 65535)
+        return fail(c, HGB_E_INVALID, "build_level: n_nodes must be in [1, 65535]");
+    // The root is row_index == NULL with node_offsets == NULL.  With offsets
+    // given, row_index may be NULL only when every node is empty.
+    const bool root = !row_index && !node_offsets;
+    if (row_index && !node_offsets)
+        return fail(c, HGB_E_INVALID, "build_level: node_offsets required with row_index");
+    if (root && n_nodes != 1)
+        return fail(c, HGB_E_INVALID, "build_level: the root (no row index) is one node");
+    std::vector<int64_t> begin(n_nodes), count(n_nodes);
+    if (root) {
+        begin[0] = 0;
+        count[0] = c->n;
+    } else {
+        if (node_offsets[0] != 0) return fail(c, HGB_E_INVALID, "build_level: offsets must start at 0");
+        for (int i = 0; i < n_nodes; ++i) {
+            if (node_offsets[i + 1] < node_offsets[i])
+                return fail(c, HGB_E_INVALID, "build_level: offsets decrease at node %d", i);
+            begin[i] = node_offsets[i];
+            count[i] = (int64_t)node_offsets[i + 1] - node_offsets[i];
+        }
+        if (!row_index && node_offsets[n_nodes] != 0)
+            return fail(c, HGB_E_INVALID, "build_level: row_index is NULL but the nodes hold rows");
+    }
+    std::vector<int32_t> slots(n_nodes);
+    for (int i = 0; i < n_nodes; ++i) {
+        slots[i] = out_slot ? out_slot[i] : i;
+        if (slots[i] < 0) return fail(c, HGB_E_INVALID, "build_level: negative output slot");
+    }
+    {
+        std::vector<int32_t> sorted = slots;
+        std::sort(sorted.begin(), sorted.end());
+        if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+            return fail(c, HGB_E_INVALID, "build_level: two nodes share an output slot");
+    }
+    HGB_HIP(c, hipSetDevice(c->device));
+    const int64_t total = root ? c->n : (int64_t)node_offsets[n_nodes];
+    const int T = fill_tile_features(c->S, c->F);
+    const int n_tiles = (c->F + T - 1) / T;
+    const int64_t node_elems = (int64_t)c->F * c->S * 2;
+
+    // rows per item: aim for about 2048 items over the level
+    int64_t ch = (total * n_tiles + 2047) / 2048;
+    ch = (ch + 255) / 256 * 256;
+    ch = std::min<int64_t>(std::max<int64_t>(ch, 4096), 1 << 16);
+
+    std::vector<FillItem> items;
+    std::vector<int32_t> zero_slots;
+    for (int i = 0; i < n_nodes; ++i) {
+        const int64_t nch = (count[i] + ch - 1) / ch;
+        if (count[i] == 0 || nch > 1) zero_slots.push_back(slots[i]);
+        for (int t = 0; t < n_tiles; ++t) {
+            const int f0 = t * T;
+            const int nf = std::min(T, c->F - f0);
+            for (int64_t j = 0; j < nch; ++j) {
+                FillItem it{};
+                it.out_slot = slots[i];
+                it.row_begin = (int32_t)(begin[i] + j * ch);
+                it.row_end = (int32_t)std::min<int64_t>(begin[i] + (j + 1) * ch, begin[i] + count[i]);
+                it.f0_nf = f0 | (nf << 16);
+                it.atomic_merge = nch > 1 ? 1 : 0;
+                items.push_back(it);
+            }
+        }
+    }
+
+    const int2* gh = c->q;
+    if (!root) {
+        hgb_status st = grow(c, &c->gh, &c->gh_cap, std::max<int64_t>(total, 1));
+        if (st != HGB_OK) return st;
+        if (total > 0) {
+            ProfScope ps(c, HGB_KERNEL_GATHER);
+            k_gather<<<grid_for(total, 256, 8192), 256, 0, c->stream>>>(c->q, row_index, total, c->n,
+                                                                        c->gh, c->dev_words + 2);
+            HGB_LAUNCHED(c, "k_gather");
+        }
+        gh = c->gh;
+    }
+    if (!zero_slots.empty()) {
+        Stage* s = nullptr;
+        hgb_status st = stage_upload(c, zero_slots.data(), zero_slots.size() * sizeof(int32_t), &s);
+        if (st != HGB_OK) return st;
+        dim3 grid(grid_for(node_elems, 256, 1024), (unsigned)zero_slots.size());
+        {
+            ProfScope ps(c, HGB_KERNEL_ZERO);
+            k_zero_slices<<<grid, 256, 0, c->stream>>>(hist, (const int32_t*)s->dev, node_elems);
+        }
+        HGB_LAUNCHED(c, "k_zero_slices");
+        st = stage_release(c, s);
+        if (st != HGB_OK) return st;
+    }
+    if (!items.empty()) {
+        Stage* s = nullptr;
+        hgb_status st = stage_upload(c, items.data(), items.size() * sizeof(FillItem), &s);
+        if (st != HGB_OK) return st;
+        const size_t lds = (size_t)2 * T * c->S * sizeof(unsigned long long);
+        const FillItem* dev_items = (const FillItem*)s->dev;
+        ProfScope ps(c, HGB_KERNEL_FILL);
+        if (c->bin_bytes == 1)
+            k_fill_lds<uint8_t><<<(unsigned)items.size(), kFillThreads, lds, c->stream>>>(
+                (const uint8_t*)c->bins, c->n, c->F, c->S, gh, row_index, dev_items,
+                (unsigned long long*)hist);
+        else
+            k_fill_lds<uint16_t><<<(unsigned)items.size(), kFillThreads, lds, c->stream>>>(
+                (const uint16_t*)c->bins, c->n, c->F, c->S, gh, row_index, dev_items,
+                (unsigned long long*)hist);
+        HGB_LAUNCHED(c, "k_fill_lds");
+        st = stage_release(c, s);
+        if (st != HGB_OK) return st;
+    }
+    return HGB_OK;
+}
+
+hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* child,
+                                 const uint8_t* built_is_right, const int32_t* parent_slot,
+                                 int32_t n_pairs)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_data) return fail(c, HGB_E_STATE, "subtract_siblings before upload_bins");
+    if (n_pairs < 0 || n_pairs > 65535)
+        return fail(c, HGB_E_INVALID, "subtract_siblings: n_pairs out of range");
+    if (n_pairs == 0) return HGB_OK;
+    if (!parent || !child || !built_is_right)
+        return fail(c, HGB_E_INVALID, "subtract_siblings: null pointer");
+    // per pair: parent slot (int32) and built side, staged together
+    std::vector<int32_t> plan(2 * (size_t)n_pairs);
+    for (int i = 0; i < n_pairs; ++i) {
+        const int32_t ps = parent_slot ? parent_slot[i] : i;
+        if (ps < 0) return fail(c, HGB_E_INVALID, "subtract_siblings: negative parent slot");
+        plan[2 * i] = ps;
+        plan[2 * i + 1] = built_is_right[i] ? 1 : 0;
+    }
+    HGB_HIP(c, hipSetDevice(c->device));
+    Stage* s = nullptr;
+    hgb_status st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
+    if (st != HGB_OK) return st;
+    const int64_t pair_vec = (int64_t)c->F * c->S;   // longlong2 per slot
+    dim3 grid(grid_for(pair_vec, 256, 2048), (unsigned)n_pairs);
+    {
+        ProfScope ps(c, HGB_KERNEL_SUBTRACT);
+        k_subtract<<<grid, 256, 0, c->stream>>>((const longlong2*)parent, (longlong2*)child,
+                                                (const int32_t*)s->dev, pair_vec);
+    }
+    HGB_LAUNCHED(c, "k_subtract");
+    return stage_release(c, s);
+}
+
+hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
+                           double gamma, hgb_split* out)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "find_splits before begin_tree");
+    if (n_nodes < 0 || n_nodes > 65535)
+        return fail(c, HGB_E_INVALID, "find_splits: n_nodes out of range");
+    if (!(lambda >= 0.0) || !std::isfinite(lambda) || !std::isfinite(gamma))
+        return fail(c, HGB_E_INVALID, "find_splits: lambda must be finite and >= 0, gamma finite");
+    if (n_nodes == 0) return HGB_OK;
+    if (!hist || !out) return fail(c, HGB_E_INVALID, "find_splits: null pointer");
+    HGB_HIP(c, hipSetDevice(c->device));
+    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * c->F);
+    if (st != HGB_OK) return st;
+    st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
+    if (st != HGB_OK) return st;
+    const int waves = 4;
+    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
+    ProfScope ps(c, HGB_KERNEL_SPLIT);
+    k_split_feature<<<grid, waves * kWave, 0, c->stream>>>(
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),
+        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals);
+    HGB_LAUNCHED(c, "k_split_feature");
+    static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
+    k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F,
+                                                             (SplitOut*)out);
+    HGB_LAUNCHED(c, "k_split_reduce");
+    return HGB_OK;
+}
+
+hgb_status hgb_profile_enable(hgb_ctx* c, int enable)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    HGB_HIP(c, hipSetDevice(c->device));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    for (int k = 0; k < HGB_KERNEL_COUNT; ++k) {
+        for (auto& pr : c->ev_pending[k]) {
+            c->ev_pool.push_back(pr.first);
+            c->ev_pool.push_back(pr.second);
+        }
+        c->ev_pending[k].clear();
+        c->prof_ms[k] = 0.0;
+        c->prof_launches[k] = 0;
+    }
+    c->prof = enable != 0;
+    return HGB_OK;
+}
+
+hgb_status hgb_profile_query(hgb_ctx* c, int kernel, double* total_ms, int64_t* launches)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (kernel < 0 || kernel >= HGB_KERNEL_COUNT || !total_ms || !launches)
+        return fail(c, HGB_E_INVALID, "profile_query: bad kernel id or null output");
+    HGB_HIP(c, hipSetDevice(c->device));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    for (int k = 0; k < HGB_KERNEL_COUNT; ++k) {
+        for (auto& pr : c->ev_pending[k]) {
+            float ms = 0.0f;
+            HGB_HIP(c, hipEventElapsedTime(&ms, pr.first, pr.second));
+            c->prof_ms[k] += ms;
+            c->prof_launches[k] += 1;
+            c->ev_pool.push_back(pr.first);
+            c->ev_pool.push_back(pr.second);
+        }
+        c->ev_pending[k].clear();
+    }
+    *total_ms = c->prof_ms[kernel];
+    *launches = c->prof_launches[kernel];
+    return HGB_OK;
+}
+
+}  // extern "C"

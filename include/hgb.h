@@ -1,0 +1,214 @@
+/*
+ * hgb -- level histogram build for histogram gradient-boosted trees, MI355X
+ * (gfx950) native.  C ABI over hand-written HIP kernels.
+ *
+ * The operation, per tree level: for every row of every node that is built
+ * from rows, add the row's (gradient, hessian) into one bin of every feature's
+ * histogram; derive each larger sibling as parent minus the smaller one; scan
+ * every feature's bins with the XGBoost-style gain and pick each node's split.
+ *
+ * Sources (the pages this library restates):
+ *   [bonsai-10]  bonsai docs, "10: CUDA histogram backend"
+ *   [bonsai-9]   bonsai guide, "9. Parallelism & determinism"
+ *   [bonsai-E6]  bonsai engine notes, "E6. The wide-data wall"
+ *   [ybb]        ybb.press article on GBDT engine engineering (sections 1-10)
+ *
+ * Conventions shared by every entry point:
+ *   - n = rows, F = features, B = value bins per feature, S = B + has_missing
+ *     histogram slots per feature.  A histogram slot is 16 bytes: int64 gradient
+ *     sum then int64 hessian sum.  A node's histogram is [F][S][2] int64, and a
+ *     level buffer is [node slots][F][S][2] int64, row-major.
+ *   - Pointers named *_dev are device pointers on the context's device; *_host
+ *     are host pointers that are read before the call returns.  The caller owns
+ *     every argument buffer; the context owns its resident copies and scratch.
+ *   - Work is enqueued asynchronously on the context's stream.  Arguments are
+ *     validated synchronously; a rejected call enqueues nothing and returns a
+ *     status, with a message from hgb_last_error().  A call that passed
+ *     validation does not fail at launch time.  Conditions that can only be seen
+ *     on the device (a row index out of range) are skipped by the kernels and
+ *     reported by the next hgb_sync().
+ *   - A context is not thread safe; use one per host thread.
+ */
+#ifndef HGB_H
+#define HGB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hgb_ctx hgb_ctx;
+
+typedef enum {
+    HGB_OK = 0,
+    HGB_E_INVALID = 1,      /* bad argument, size, offset or bin value */
+    HGB_E_STATE = 2,        /* call out of order (e.g. build before begin_tree) */
+    HGB_E_UNSUPPORTED = 3,  /* shape beyond the kernels' plan (too many bins) */
+    HGB_E_NONFINITE = 4,    /* NaN/Inf gradient or hessian, or a negative hessian */
+    HGB_E_DEVICE = 5        /* HIP runtime error, or no usable device */
+} hgb_status;
+
+/* One node's best split.  56 bytes, naturally aligned. */
+typedef struct {
+    int32_t feature;       /* -1 when no candidate is valid */
+    int32_t bin;           /* value bins <= bin go left; -1 when none */
+    int32_t default_left;  /* 1: rows in the missing slot go left */
+    int32_t pad;           /* always 0 */
+    double gain;           /* -inf when no candidate is valid */
+    int64_t g_left;        /* fixed-point gradient sum of the left side */
+    int64_t h_left;        /* fixed-point hessian sum of the left side */
+    int64_t g_total;       /* node totals (feature 0's slot sums) */
+    int64_t h_total;
+} hgb_split;
+
+/* Largest S = n_bins + has_missing the kernels accept. */
+#define HGB_MAX_SLOTS 4096
+
+/* 1 when a HIP device is present and usable, else 0 (tests skip on 0). */
+int hgb_available(void);
+
+/* Create a context on `device`, enqueueing on `hip_stream` (a hipStream_t;
+ * NULL selects the device's null stream).  *out receives the context. */
+hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out);
+
+/* Release the context and everything it owns.  Synchronizes its stream. */
+void hgb_destroy(hgb_ctx* ctx);
+
+/* Message describing the last failed call on this context ("" if none).
+ * Valid until the next call on the context. */
+const char* hgb_last_error(const hgb_ctx* ctx);
+
+/* Block until the context's stream has drained.  Returns HGB_E_INVALID if a
+ * kernel met a row index outside [0, n) since the previous hgb_sync (those
+ * entries were skipped), HGB_E_DEVICE on a runtime error, else HGB_OK. */
+hgb_status hgb_sync(hgb_ctx* ctx);
+
+/*
+ * Make the binned matrix resident ([bonsai-10] "The device context
+ * lifecycle": the feature-major binned matrix is uploaded once per dataset;
+ * u8 when every feature fits 256 bins, u16 otherwise).
+ *
+ * bins:        feature-major [n_features][n_rows], element size bin_bytes
+ *              (1 = uint8, 2 = uint16); host memory if on_device == 0, device
+ *              memory on the context's device otherwise.  Copied; the caller
+ *              keeps ownership.
+ * n_bins:      value bins per feature (B).  A stored value b < B is value bin b.
+ * has_missing: when nonzero the value B is the missing sentinel, counted in
+ *              histogram slot B (S = B + 1).  Otherwise S = B.
+ * Errors: HGB_E_INVALID for non-positive sizes, bin_bytes not 1/2, B too large
+ *         for the element type, or any stored value >= S (checked on the
+ *         device, synchronously); HGB_E_UNSUPPORTED when S > HGB_MAX_SLOTS.
+ * Invalidates the current tree (begin_tree must be called again).
+ */
+hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on_device,
+                           int32_t n_rows, int32_t n_features, int32_t n_bins,
+                           int32_t has_missing);
+
+/*
+ * Start a tree: fixed-point encode the per-row gradients and hessians
+ * ([bonsai-9] "The idea": device histogram cells are int64 fixed point, so a
+ * sum of cells is one integer whatever the order of the additions).
+ *
+ * For c in {grad, hess}: M = max |c_i|; k = 0 if M == 0, else k = 30 - e with
+ * 2^(e-1) <= M < 2^e; q_i = round-half-even(c_i * 2^k).  |q_i| <= 2^30.
+ *
+ * grad_dev, hess_dev: fp32 [n_rows] device arrays (n_rows of upload_bins).
+ * Synchronizes the stream once (the scales are needed on the host).
+ * Errors: HGB_E_STATE before upload_bins; HGB_E_NONFINITE for a NaN/Inf value
+ *         or a hessian < 0 (-0.0 counts as 0) -- no tree is started then.
+ */
+hgb_status hgb_begin_tree(hgb_ctx* ctx, const float* grad_dev, const float* hess_dev);
+
+/* The current tree's scales: a fixed-point sum X stands for X * 2^-k. */
+hgb_status hgb_get_scales(const hgb_ctx* ctx, int32_t* k_g, int32_t* k_h);
+
+/*
+ * Build the histograms of a level's nodes from rows ([bonsai-E6] "Two fills,
+ * one choice": for every row of a node, add its gradient and hessian into one
+ * bin of every feature's histogram; [bonsai-10] "Level batching": all nodes of
+ * a level in one pass).  Cells are exact int64 sums of the fixed-point values.
+ *
+ * row_index_dev:     int32, the nodes' row lists concatenated, node i owning
+ *                    entries [node_offsets[i], node_offsets[i+1]).  Order within
+ *                    a node does not change the result.  May be NULL when every
+ *                    node is empty.
+ * node_offsets_host: int32 [n_nodes + 1], starts at 0, non-decreasing.  When
+ *                    both row_index_dev and node_offsets_host are NULL the call
+ *                    builds the root: one node (n_nodes must be 1) holding rows
+ *                    0..n-1 in order.
+ * hist_dev:          level buffer; node i's histogram is written, in full, at
+ *                    node slot out_slot_host[i] (i when out_slot_host is NULL).
+ *                    The caller sizes it to cover every slot written.
+ * Errors: HGB_E_STATE before begin_tree; HGB_E_INVALID for bad offsets, slots
+ *         (negative, or two nodes on one slot) or n_nodes < 1.
+ */
+hgb_status hgb_build_level(hgb_ctx* ctx, const int32_t* row_index_dev,
+                           const int32_t* node_offsets_host, int32_t n_nodes,
+                           int64_t* hist_dev, const int32_t* out_slot_host);
+
+/*
+ * Derive every pair's other child: other = parent - built, slot by slot, exact
+ * ([ybb] section 3, histogram subtraction; integer cells need no clamp).
+ *
+ * parent_dev:          level buffer of the parents; pair i's parent is at node
+ *                      slot parent_slot_host[i] (i when parent_slot_host is NULL).
+ * child_dev:           [2*n_pairs][F][S][2] int64; pair i's children are node
+ *                      slots 2i (left) and 2i+1 (right).  The built child is at
+ *                      2i + built_is_right_host[i]; the other one is written.
+ * built_is_right_host: uint8 [n_pairs].
+ * parent_slot_host:    int32 [n_pairs] or NULL.
+ * Errors: HGB_E_STATE before upload_bins; HGB_E_INVALID for n_pairs outside
+ *         [0, 65535] or a negative parent slot.
+ */
+hgb_status hgb_subtract_siblings(hgb_ctx* ctx, const int64_t* parent_dev, int64_t* child_dev,
+                                 const uint8_t* built_is_right_host,
+                                 const int32_t* parent_slot_host, int32_t n_pairs);
+
+/*
+ * Best split of every node of a level ([ybb] section 1: the gain
+ * G_L^2/(H_L+lambda) + G_R^2/(H_R+lambda) - G^2/(H+lambda) - gamma, here without
+ * the constant factor 1/2; section 4: missing rows tried on each side;
+ * [bonsai-9] "In bonsai": ties resolved as a serial scan in feature order).
+ *
+ * For each feature, candidates (b, d) for b in [0, B) and d in {right} (or
+ * {right, left} when has_missing): the left side holds value bins <= b plus the
+ * missing slot if d is left.  Valid iff both integer hessian sums are > 0.
+ * Sums are converted as (double)X * 2^-k, the gain evaluated in fp64 left to
+ * right without fused multiply-add.  The best is the largest gain; ties go to
+ * the smallest feature, then bin, then right before left.
+ *
+ * hist_dev: [n_nodes][F][S][2] int64.  out_dev: hgb_split [n_nodes] (device).
+ * Errors: HGB_E_STATE before begin_tree; HGB_E_INVALID for n_nodes < 0,
+ *         lambda < 0 or non-finite lambda/gamma.
+ */
+hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_nodes,
+                           double lambda, double gamma, hgb_split* out_dev);
+
+/*
+ * Per-kernel device timing ([bonsai-10] "The kernel": the pages' backend
+ * prints an upload / gpu / unpack breakdown when asked).  When enabled, every
+ * launch is bracketed by HIP events on the context's stream.
+ */
+typedef enum {
+    HGB_KERNEL_QUANTIZE = 0,   /* begin_tree: max-reduce + quantize */
+    HGB_KERNEL_GATHER = 1,     /* build_level: level-order (g, h) gather */
+    HGB_KERNEL_ZERO = 2,       /* build_level: zeroing of atomically merged slices */
+    HGB_KERNEL_FILL = 3,       /* build_level: LDS histogram fill + merge */
+    HGB_KERNEL_SUBTRACT = 4,   /* subtract_siblings */
+    HGB_KERNEL_SPLIT = 5,      /* find_splits (both kernels) */
+    HGB_KERNEL_COUNT = 6
+} hgb_kernel;
+
+/* Turn timing on (nonzero) or off, and reset the counters. */
+hgb_status hgb_profile_enable(hgb_ctx* ctx, int enable);
+
+/* Total device milliseconds and launch count of one kernel class since the
+ * last reset.  Synchronizes the stream.  HGB_E_INVALID for a bad id. */
+hgb_status hgb_profile_query(hgb_ctx* ctx, int kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
