@@ -32,7 +32,7 @@ SPLIT_BYTES = 56
 EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb_sync",
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
             "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
-            "hgb_profile_query")
+            "hgb_profile_query", "hgb_set_precision")
 
 KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5}
 
@@ -74,6 +74,8 @@ def load():
     lib.hgb_upload_bins.restype = c_int
     lib.hgb_begin_tree.argtypes = [vp, vp, vp]
     lib.hgb_begin_tree.restype = c_int
+    lib.hgb_set_precision.argtypes = [vp, i32]
+    lib.hgb_set_precision.restype = c_int
     lib.hgb_get_scales.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.hgb_get_scales.restype = c_int
     lib.hgb_build_level.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -205,6 +207,10 @@ class Context:
         g = self._dev(grad, "grad", torch.float32, self.n_rows)
         h = self._dev(hess, "hess", torch.float32, self.n_rows)
         self._check(self._lib.hgb_begin_tree(self._h, g, h), "begin_tree")
+
+    def set_precision(self, bits: int):
+        """Fixed-point precision (bits below the largest |value|) of the next begin_tree."""
+        self._check(self._lib.hgb_set_precision(self._h, int(bits)), "set_precision")
 
     def get_scales(self):
         kg, kh = ctypes.c_int32(), ctypes.c_int32()

@@ -20,9 +20,18 @@ using namespace hgb;
 
 namespace {
 
-// LDS bytes one fill block may use for its (g, h) tile.
-constexpr int kFillLdsBudget = 64 * 1024;
-constexpr int kFillThreads = 256;
+// gfx950: 160 KiB of LDS per CU.  The root fill runs one 1024-thread block
+// per CU; the level fills run two 512-thread blocks per CU.
+constexpr int64_t kRootLdsBudget = 160 * 1024;
+constexpr int64_t kLevelLdsBudget = 80 * 1024;
+constexpr int kRootThreads = 1024;
+constexpr int kLevelThreads = 512;
+// Aim for about this many fill blocks per level (several per CU).
+constexpr int64_t kFillTargetItems = 1536;
+// Keep a row-major copy of the bins when a row takes at most this many bytes.
+constexpr int64_t kRowMajorMaxRowBytes = 512;
+// Default fixed-point precision of begin_tree (bits below the largest value).
+constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 4;
 
 struct Stage {
@@ -40,8 +49,11 @@ struct hgb_ctx {
     hipStream_t stream = nullptr;
     std::string err;
 
-    // dataset plane
+    // dataset plane: feature-major bins, plus a row-major copy when rows are
+    // narrow enough for a row to sit in a cache line or two
     void* bins = nullptr;
+    void* bins_rm = nullptr;
+    int64_t rm_stride = 0;   // bytes per row of the row-major copy (multiple of 16)
     int bin_bytes = 0;
     int64_t n = 0;
     int F = 0, B = 0, S = 0, has_missing = 0;
@@ -50,6 +62,7 @@ struct hgb_ctx {
     // gradient plane
     int2* q = nullptr;
     int64_t q_cap = 0;
+    int precision = kDefaultPrecision;
     int k_g = 0, k_h = 0;
     bool have_tree = false;
 
@@ -201,10 +214,164 @@ int grid_for(int64_t work, int threads, int cap)
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-int fill_tile_features(int S, int F)
+// ---------------------------------------------------------------------------
+// Fill planning
+// ---------------------------------------------------------------------------
+
+enum FillKind { kFillRoot = 0, kFillCols = 1, kFillRowsKind = 2 };
+
+// Launch shape of one build_level fill.
+struct FillPlan {
+    FillKind kind;
+    int acc;            // kWide / kPacked
+    int lc;             // log2 of the privatized copy count
+    int tile;           // features per item (root, cols: NF; rows: features per load)
+    int lt;             // rows: bytes loaded per row
+    int threads;
+    int64_t step_rows;  // rows a block consumes per step
+    int64_t max_chunk;  // rows per item that keep packed sums exact (0: no bound)
+    size_t lds_bytes;
+};
+
+int64_t feature_lds(int acc, int S, int lc)
 {
-    int t = kFillLdsBudget / (S * 16);
-    return std::max(1, std::min(t, F));
+    return (int64_t)(acc == kWide ? 2 : 1) * S * 8 * (1 << lc);
+}
+
+// Packed sums stay exact while every copy-slot sees at most
+// kPackedRowsPerCopy rows.  Copy c is used by threads / C threads, each taking
+// `per_thread` rows per step, so an item may hold this many whole steps.
+int64_t packed_max_chunk(int threads, int lc, int per_thread)
+{
+    const int64_t per_copy_step = (int64_t)(threads >> lc) * per_thread;
+    const int64_t steps = kPackedRowsPerCopy / per_copy_step;
+    return steps * threads * per_thread;   // 0 when even one step is too many
+}
+
+FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
+{
+    FillPlan p{};
+    p.acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
+    const int S = c->S;
+    const int w = c->bin_bytes;
+    if (root || !rm) {
+        p.kind = root ? kFillRoot : kFillCols;
+        p.threads = root ? kRootThreads : kLevelThreads;
+        const int per_thread = root ? kRootRows : kLevelEntries;
+        const int64_t budget = root ? kRootLdsBudget : kLevelLdsBudget;
+        // most copies (up to 16) that leave room for one feature
+        p.lc = 4;
+        while (p.lc > 0 && feature_lds(p.acc, S, p.lc) > budget) --p.lc;
+        // packed sums need several copies per block to stay exact; where they
+        // do not fit, accumulate both components in full width (exact for any
+        // precision)
+        if (p.acc == kPacked && packed_max_chunk(p.threads, p.lc, per_thread) == 0) {
+            p.acc = kWide;
+            p.lc = 4;
+            while (p.lc > 0 && feature_lds(p.acc, S, p.lc) > budget) --p.lc;
+        }
+        const int64_t per_feature = feature_lds(p.acc, S, p.lc);
+        const int64_t fit = budget / per_feature;
+        p.tile = fit >= 4 ? 4 : (fit >= 2 ? 2 : 1);
+        while (p.tile > c->F) p.tile >>= 1;
+        p.lt = 0;
+        p.lds_bytes = (size_t)(per_feature * p.tile);
+        p.step_rows = (int64_t)p.threads * per_thread;
+        p.max_chunk = p.acc == kPacked ? packed_max_chunk(p.threads, p.lc, per_thread) : 0;
+        return p;
+    }
+    // row-major level fill: the widest row load (16 bytes down to 2) whose
+    // features fit the budget with at least the minimum copy count
+    p.kind = kFillRowsKind;
+    p.threads = kLevelThreads;
+    const int min_lc = p.acc == kPacked ? 1 : 0;
+    p.lt = 0;
+    for (int lt = 16; lt >= 2 && !p.lt; lt >>= 1) {
+        if (lt < w) break;
+        const int tf = lt / w;
+        for (int lc = 4; lc >= min_lc; --lc) {
+            if (tf * feature_lds(p.acc, S, lc) <= kLevelLdsBudget &&
+                (p.acc == kWide || packed_max_chunk(p.threads, lc, kLevelEntries) > 0)) {
+                p.lt = lt;
+                p.lc = lc;
+                break;
+            }
+        }
+    }
+    if (!p.lt) {   // huge S: one feature, one copy
+        p.lt = w;
+        p.lc = min_lc;
+    }
+    p.tile = p.lt / w;
+    p.lds_bytes = (size_t)(p.tile * feature_lds(p.acc, S, p.lc));
+    p.step_rows = (int64_t)p.threads * kLevelEntries;
+    p.max_chunk = p.acc == kPacked ? packed_max_chunk(p.threads, p.lc, kLevelEntries) : 0;
+    return p;
+}
+
+template <typename K>
+hgb_status set_lds(hgb_ctx* c, K kernel, size_t bytes)
+{
+    HGB_HIP(c, hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)bytes));
+    return HGB_OK;
+}
+
+struct FillArgs {
+    const int2* gh;
+    const int32_t* row_index;
+    const FillItem* items;
+    int n_items;
+    int vec_ok;
+    int64_t* hist;
+};
+
+template <typename BinT, int ACC>
+hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
+{
+    const unsigned grid = (unsigned)(8 * ((a.n_items + 7) / 8));
+    unsigned long long* hist = (unsigned long long*)a.hist;
+    const BinT* bins = (const BinT*)c->bins;
+    hgb_status st = HGB_OK;
+#define HGB_LAUNCH(kern, ...)                                                            \
+    do {                                                                                 \
+        st = set_lds(c, kern, p.lds_bytes);                                              \
+        if (st != HGB_OK) return st;                                                     \
+        kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
+    } while (0)
+    if (p.kind == kFillRoot) {
+        switch (p.tile) {
+        case 1: HGB_LAUNCH((k_fill_root<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
+        case 2: HGB_LAUNCH((k_fill_root<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
+        default: HGB_LAUNCH((k_fill_root<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
+        }
+    } else if (p.kind == kFillCols) {
+        switch (p.tile) {
+        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        default: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        }
+    } else {
+        const uint8_t* rm = (const uint8_t*)c->bins_rm;
+        switch (p.lt) {
+        case 16: HGB_LAUNCH((k_fill_rows<BinT, 16, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        case 8: HGB_LAUNCH((k_fill_rows<BinT, 8, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        case 4: HGB_LAUNCH((k_fill_rows<BinT, 4, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        default: HGB_LAUNCH((k_fill_rows<BinT, 2, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        }
+    }
+#undef HGB_LAUNCH
+    HGB_LAUNCHED(c, "fill");
+    return HGB_OK;
+}
+
+hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
+{
+    if (c->bin_bytes == 1)
+        return p.acc == kPacked ? launch_fill_acc<uint8_t, kPacked>(c, p, a)
+                                : launch_fill_acc<uint8_t, kWide>(c, p, a);
+    return p.acc == kPacked ? launch_fill_acc<uint16_t, kPacked>(c, p, a)
+                            : launch_fill_acc<uint16_t, kWide>(c, p, a);
 }
 
 }  // namespace
@@ -257,6 +424,7 @@ void hgb_destroy(hgb_ctx* c)
         }
     for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
     (void)hipFree(c->bins);
+    (void)hipFree(c->bins_rm);
     (void)hipFree(c->q);
     (void)hipFree(c->gh);
     (void)hipFree(c->best);
@@ -318,6 +486,10 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
         HGB_HIP(c, hipFree(c->bins));
         c->bins = nullptr;
     }
+    if (c->bins_rm) {
+        HGB_HIP(c, hipFree(c->bins_rm));
+        c->bins_rm = nullptr;
+    }
     HGB_HIP(c, hipMalloc(&c->bins, bytes));
     HGB_HIP(c, hipMemcpyAsync(c->bins, bins, bytes,
                               on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
@@ -335,6 +507,20 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
     if (c->host_words[0] >= (uint32_t)S)
         return fail(c, HGB_E_INVALID, "upload_bins: stored value %u is not a slot (S = %d)",
                     c->host_words[0], S);
+    if ((int64_t)n_features * bin_bytes <= kRowMajorMaxRowBytes) {
+        const int64_t stride = ((int64_t)n_features * bin_bytes + 15) / 16 * 16;
+        HGB_HIP(c, hipMalloc(&c->bins_rm, (size_t)(stride * n_rows)));
+        HGB_HIP(c, hipMemsetAsync(c->bins_rm, 0, (size_t)(stride * n_rows), c->stream));
+        c->rm_stride = stride;
+        dim3 tgrid((unsigned)((n_rows + 63) / 64), (unsigned)((n_features + 63) / 64));
+        if (bin_bytes == 1)
+            k_transpose<uint8_t><<<tgrid, 256, 0, c->stream>>>((const uint8_t*)c->bins,
+                                                              (uint8_t*)c->bins_rm, n_rows, n_features, stride);
+        else
+            k_transpose<uint16_t><<<tgrid, 256, 0, c->stream>>>((const uint16_t*)c->bins,
+                                                               (uint8_t*)c->bins_rm, n_rows, n_features, stride);
+        HGB_LAUNCHED(c, "k_transpose");
+    }
     c->bin_bytes = bin_bytes;
     c->n = n_rows;
     c->F = n_features;
@@ -379,7 +565,7 @@ hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
         } else {
             int e = 0;
             (void)std::frexp((double)m, &e);
-            k[i] = 30 - e;
+            k[i] = c->precision - e;
         }
     }
     c->k_g = k[0];
@@ -391,6 +577,17 @@ hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
     }
     HGB_LAUNCHED(c, "k_quantize");
     c->have_tree = true;
+    return HGB_OK;
+}
+
+hgb_status hgb_set_precision(hgb_ctx* c, int32_t bits)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (bits < 1 || bits > 30)
+        return fail(c, HGB_E_INVALID, "set_precision: bits must be in [1, 30]");
+    c->precision = bits;
+    c->have_tree = false;
     return HGB_OK;
 }
 
@@ -447,35 +644,54 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     }
     HGB_HIP(c, hipSetDevice(c->device));
     const int64_t total = root ? c->n : (int64_t)node_offsets[n_nodes];
-    const int T = fill_tile_features(c->S, c->F);
+    // The root reads rows in order; other levels read through the row index,
+    // from the row-major copy when there is one.
+    const bool rm = !root && c->bins_rm != nullptr;
+    const FillPlan plan = plan_fill(c, root, rm);
+    const int T = plan.tile;
     const int n_tiles = (c->F + T - 1) / T;
     const int64_t node_elems = (int64_t)c->F * c->S * 2;
 
-    // rows per item: aim for about 2048 items over the level
-    int64_t ch = (total * n_tiles + 2047) / 2048;
-    ch = (ch + 255) / 256 * 256;
-    ch = std::min<int64_t>(std::max<int64_t>(ch, 4096), 1 << 16);
+    // Rows per item: about kFillTargetItems items over the level, in whole
+    // block steps, and within the packed-exactness bound.
+    int64_t ch = (total * n_tiles + kFillTargetItems - 1) / kFillTargetItems;
+    ch = std::max<int64_t>((ch + plan.step_rows - 1) / plan.step_rows * plan.step_rows, plan.step_rows);
+    if (plan.max_chunk > 0) ch = std::min(ch, plan.max_chunk);
 
+    // Item order decides which items share an L2 (the kernel gives each XCD a
+    // contiguous run).  Root and row-major levels: (node, chunk, tile) -- the
+    // tiles of one row chunk read the same rows.  Feature-major levels:
+    // (tile, chunk, node) -- the nodes of one tile read the same columns.
     std::vector<FillItem> items;
     std::vector<int32_t> zero_slots;
+    std::vector<int64_t> nchunks(n_nodes);
+    int64_t max_ch = 0;
     for (int i = 0; i < n_nodes; ++i) {
-        const int64_t nch = (count[i] + ch - 1) / ch;
-        if (count[i] == 0 || nch > 1) zero_slots.push_back(slots[i]);
-        for (int t = 0; t < n_tiles; ++t) {
-            const int f0 = t * T;
-            const int nf = std::min(T, c->F - f0);
-            for (int64_t j = 0; j < nch; ++j) {
-                FillItem it{};
-                it.out_slot = slots[i];
-                it.row_begin = (int32_t)(begin[i] + j * ch);
-                it.row_end = (int32_t)std::min<int64_t>(begin[i] + (j + 1) * ch, begin[i] + count[i]);
-                it.f0_nf = f0 | (nf << 16);
-                it.atomic_merge = nch > 1 ? 1 : 0;
-                items.push_back(it);
-            }
-        }
+        nchunks[i] = (count[i] + ch - 1) / ch;
+        max_ch = std::max(max_ch, nchunks[i]);
+        if (count[i] == 0 || nchunks[i] > 1) zero_slots.push_back(slots[i]);
     }
-
+    auto push = [&](int i, int64_t j, int t) {
+        const int f0 = t * T;
+        const int nf = std::min(T, c->F - f0);
+        FillItem it{};
+        it.out_slot = slots[i];
+        it.row_begin = (int32_t)(begin[i] + j * ch);
+        it.row_end = (int32_t)std::min<int64_t>(begin[i] + (j + 1) * ch, begin[i] + count[i]);
+        it.f0_nf = f0 | (nf << 16);
+        it.atomic_merge = nchunks[i] > 1 ? 1 : 0;
+        items.push_back(it);
+    };
+    if (plan.kind != kFillCols) {
+        for (int i = 0; i < n_nodes; ++i)
+            for (int64_t j = 0; j < nchunks[i]; ++j)
+                for (int t = 0; t < n_tiles; ++t) push(i, j, t);
+    } else {
+        for (int t = 0; t < n_tiles; ++t)
+            for (int64_t j = 0; j < max_ch; ++j)
+                for (int i = 0; i < n_nodes; ++i)
+                    if (j < nchunks[i]) push(i, j, t);
+    }
     const int2* gh = c->q;
     if (!root) {
         hgb_status st = grow(c, &c->gh, &c->gh_cap, std::max<int64_t>(total, 1));
@@ -505,18 +721,18 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         Stage* s = nullptr;
         hgb_status st = stage_upload(c, items.data(), items.size() * sizeof(FillItem), &s);
         if (st != HGB_OK) return st;
-        const size_t lds = (size_t)2 * T * c->S * sizeof(unsigned long long);
-        const FillItem* dev_items = (const FillItem*)s->dev;
+        FillArgs a;
+        a.gh = gh;
+        a.row_index = row_index;
+        a.items = (const FillItem*)s->dev;
+        a.n_items = (int)items.size();
+        // 8-row vector loads of the root need rows aligned to 8 (chunk starts
+        // are whole steps)
+        a.vec_ok = (c->n % 8 == 0) ? 1 : 0;
+        a.hist = hist;
         ProfScope ps(c, HGB_KERNEL_FILL);
-        if (c->bin_bytes == 1)
-            k_fill_lds<uint8_t><<<(unsigned)items.size(), kFillThreads, lds, c->stream>>>(
-                (const uint8_t*)c->bins, c->n, c->F, c->S, gh, row_index, dev_items,
-                (unsigned long long*)hist);
-        else
-            k_fill_lds<uint16_t><<<(unsigned)items.size(), kFillThreads, lds, c->stream>>>(
-                (const uint16_t*)c->bins, c->n, c->F, c->S, gh, row_index, dev_items,
-                (unsigned long long*)hist);
-        HGB_LAUNCHED(c, "k_fill_lds");
+        st = launch_fill(c, plan, a);
+        if (st != HGB_OK) return st;
         st = stage_release(c, s);
         if (st != HGB_OK) return st;
     }

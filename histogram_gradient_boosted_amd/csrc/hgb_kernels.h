@@ -82,6 +82,32 @@ __global__ __launch_bounds__(256) void k_bins_max(const BinT* __restrict__ bins,
     if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(out, m);
 }
 
+// upload_bins: row-major copy of the feature-major matrix, dst row r at byte
+// r * row_stride (row_stride >= F * sizeof(BinT), padding zeroed beforehand),
+// through a 64 x 64 LDS tile so both sides stay coalesced.
+template <typename BinT>
+__global__ __launch_bounds__(256) void k_transpose(const BinT* __restrict__ src,
+                                                   uint8_t* __restrict__ dst, int64_t n, int F,
+                                                   int64_t row_stride)
+{
+    __shared__ BinT tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int f0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63;
+    const int ty = threadIdx.x >> 6;
+    for (int j = ty; j < 64; j += 4) {
+        const int f = f0 + j;
+        const int64_t r = r0 + tx;
+        if (f < F && r < n) tile[j][tx] = src[(int64_t)f * n + r];
+    }
+    __syncthreads();
+    for (int j = ty; j < 64; j += 4) {
+        const int64_t r = r0 + j;
+        const int f = f0 + tx;
+        if (r < n && f < F) ((BinT*)(dst + r * row_stride))[f] = tile[tx][j];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // build_level
 // ---------------------------------------------------------------------------
@@ -126,59 +152,437 @@ __global__ __launch_bounds__(256) void k_zero_slices(int64_t* __restrict__ hist,
         base[e] = 0;
 }
 
-// LDS-staged fill.  Each block owns one FillItem: it accumulates the item's
-// rows into a block-private LDS histogram of its feature tile (separate int64
-// planes for g and h, slot-major per feature), then merges the tile into the
-// level buffer -- a plain store when the item covers the whole node, an int64
-// atomic add otherwise.  Integer adds make the result independent of the order
-// in which lanes, waves and blocks land.
+// Work-item order for the fill: consecutive block ids are dispatched to the
+// eight XCDs in turn, and each XCD has its own L2.  Give each XCD a contiguous
+// run of items so that the feature tiles of one row chunk -- which share that
+// chunk's (g, h) reads -- run at the same time on the same L2.
+__device__ inline int xcd_item(int bid, int n_items)
+{
+    const int per = (n_items + 7) >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Fill kernels
+//
+// Every fill block owns one FillItem and keeps a block-private histogram of its
+// feature tile in LDS, with C = 2^lc copies interleaved at 8-byte granularity
+// (word slot * C + copy); lane l adds into copy l mod C.  With C = 16 the 16 lanes
+// that the LDS serves together always hit 16 different bank pairs, so random
+// bins cause no bank conflicts and a hot bin shared by every lane (a skewed
+// feature) costs no more than a uniform one.  At the end the copies are summed
+// and the tile is written to the level buffer: a plain store when the item
+// covers its whole node, an int64 atomic add otherwise.  Integer adds make the
+// result independent of the order in which lanes, waves and blocks land.
+//
+// Two accumulation modes:
+//   kWide    two ds_add_u64 per cell, one per component (gradient and hessian
+//            planes, [nf][2][S][C] u64).  Exact for any fixed-point precision.
+//   kPacked  one ds_add_u64 per cell on qh * 2^32 + qg ([nf][S][C] u64).  Each
+//            copy-slot sums at most kPackedRowsPerCopy rows of |q| <= 2^19, so
+//            the low half never leaves the int32 range and both sums decode
+//            exactly: G = sign-extended low 32 bits, H = (V - G) / 2^32.
+// ---------------------------------------------------------------------------
+enum { kWide = 0, kPacked = 1 };
+constexpr int kPackedMaxBits = 19;
+constexpr int kPackedRowsPerCopy = 4095;
+
+struct CellVal {
+    unsigned long long a, b;
+};
+
+template <int ACC>
+__device__ inline CellVal cell_val(int qg, int qh)
+{
+    CellVal v;
+    if (ACC == kWide) {
+        v.a = (unsigned long long)(long long)qg;
+        v.b = (unsigned long long)(long long)qh;
+    } else {
+        v.a = ((unsigned long long)(uint32_t)qh << 32) + (unsigned long long)(long long)qg;
+        v.b = 0ull;
+    }
+    return v;
+}
+
+template <int ACC>
+__device__ inline void lds_add(unsigned long long* lcopy, int plane, int lc, int f, int b, CellVal v)
+{
+    unsigned long long* p = lcopy + f * (ACC == kWide ? 2 : 1) * plane + (b << lc);
+    atomicAdd(p, v.a);
+    if (ACC == kWide) atomicAdd(p + plane, v.b);
+}
+
+// Zero the block's LDS tile: nf * planes * S * C words.
+__device__ inline void lds_zero(unsigned long long* lds, int words)
+{
+    ulonglong2* l2 = (ulonglong2*)lds;
+    for (int i = threadIdx.x; i < (words >> 1); i += blockDim.x) l2[i] = make_ulonglong2(0ull, 0ull);
+    if ((words & 1) && threadIdx.x == 0) lds[words - 1] = 0ull;
+}
+
+// Sum the copies of every cell of the tile (rotated start, so neighbouring
+// lanes read different banks) and write it to the level buffer.
+template <int ACC>
+__device__ inline void lds_flush(const unsigned long long* lds, int nf, int S, int plane, int lc,
+                                 unsigned long long* out, bool atomic_merge)
+{
+    const int cells = nf * S;
+    const int C = 1 << lc;
+    for (int i = threadIdx.x; i < cells; i += blockDim.x) {
+        const int f = i / S;
+        const int sl = i - f * S;
+        const unsigned long long* pg = lds + f * (ACC == kWide ? 2 : 1) * plane + (sl << lc);
+        long long g = 0, h = 0;
+        for (int cc = 0; cc < C; ++cc) {
+            const int c = (cc + i) & (C - 1);
+            if (ACC == kWide) {
+                g += (long long)pg[c];
+                h += (long long)pg[plane + c];
+            } else {
+                const long long v = (long long)pg[c];
+                const long long lo = (long long)(int)(unsigned)(v & 0xffffffffll);
+                g += lo;
+                h += (v - lo) >> 32;
+            }
+        }
+        if (atomic_merge) {
+            if (g) atomicAdd(&out[2 * i], (unsigned long long)g);
+            if (h) atomicAdd(&out[2 * i + 1], (unsigned long long)h);
+        } else {
+            out[2 * i] = (unsigned long long)g;
+            out[2 * i + 1] = (unsigned long long)h;
+        }
+    }
+}
+
+// Root fill: the level's one node holds every row in order, so each thread
+// reads 8 consecutive rows per step -- a 16-byte (g, h) load per two rows and
+// one 8- or 16-byte bin load per feature -- and loads the next step while it
+// adds the current one.  NF features per block (the host gives every item NF).
+constexpr int kRootRows = 8;
+
 template <typename BinT>
-__global__ __launch_bounds__(256) void k_fill_lds(const BinT* __restrict__ bins, int64_t n,
-                                                  int n_features, int S,
-                                                  const int2* __restrict__ gh,
-                                                  const int32_t* __restrict__ row_index,
-                                                  const FillItem* __restrict__ items,
-                                                  unsigned long long* __restrict__ hist)
+struct Bins8;
+template <>
+struct Bins8<uint8_t> {
+    uint2 w;
+    __device__ inline void load(const uint8_t* p) { w = *(const uint2*)p; }
+    __device__ inline int at(int j) const
+    {
+        const uint32_t x = j < 4 ? w.x : w.y;
+        return (int)((x >> (8 * (j & 3))) & 0xffu);
+    }
+};
+template <>
+struct Bins8<uint16_t> {
+    uint4 w;
+    __device__ inline void load(const uint16_t* p) { w = *(const uint4*)p; }
+    __device__ inline int at(int j) const
+    {
+        const uint32_t x = j < 2 ? w.x : (j < 4 ? w.y : (j < 6 ? w.z : w.w));
+        return (int)((x >> (16 * (j & 1))) & 0xffffu);
+    }
+};
+
+template <typename BinT, int NF>
+struct RootStep {
+    int4 q[kRootRows / 2];
+    Bins8<BinT> b[NF];
+};
+
+template <typename BinT, int NF, int ACC>
+__global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bins, int64_t n,
+                                                    int n_features, int S, int lc,
+                                                    const int2* __restrict__ q,
+                                                    const FillItem* __restrict__ items, int n_items,
+                                                    int vec_ok, unsigned long long* __restrict__ hist)
 {
     extern __shared__ unsigned long long lds[];
-    const FillItem it = items[blockIdx.x];
+    const int item = xcd_item(blockIdx.x, n_items);
+    if (item >= n_items) return;
+    const FillItem it = items[item];
     const int f0 = it.f0_nf & 0xffff;
-    const int nf = it.f0_nf >> 16;
-    const int cells = nf * S;
-    unsigned long long* lg = lds;
-    unsigned long long* lh = lds + cells;
-    for (int i = threadIdx.x; i < 2 * cells; i += blockDim.x) lds[i] = 0ull;
+    constexpr int PL = ACC == kWide ? 2 : 1;
+    const int plane = S << lc;
+    lds_zero(lds, NF * PL * plane);
     __syncthreads();
 
-    const BinT* col0 = bins + (int64_t)f0 * n;
-    for (int64_t k = it.row_begin + threadIdx.x; k < it.row_end; k += blockDim.x) {
-        int64_t r = row_index ? (int64_t)row_index[k] : k;
-        if ((uint64_t)r >= (uint64_t)n) continue;   // flagged by the gather
-        const int2 v = gh[k];
-        const unsigned long long vg = (unsigned long long)(long long)v.x;
-        const unsigned long long vh = (unsigned long long)(long long)v.y;
-        const BinT* p = col0 + r;
-        for (int f = 0; f < nf; ++f) {
-            const int b = (int)p[(int64_t)f * n];
-            atomicAdd(&lg[f * S + b], vg);
-            atomicAdd(&lh[f * S + b], vh);
+    unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
+    const BinT* const col0 = bins + (int64_t)f0 * n;
+    const int64_t rb = it.row_begin, re = it.row_end;
+    constexpr int R = kRootRows;
+    const int64_t step = (int64_t)blockDim.x * R;
+    int64_t k = rb + (int64_t)threadIdx.x * R;
+
+    auto load = [&](int64_t at, RootStep<BinT, NF>& st) {
+        const int4* g4 = (const int4*)(q + at);
+#pragma unroll
+        for (int j = 0; j < R / 2; ++j) st.q[j] = g4[j];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) st.b[f].load(col0 + (int64_t)f * n + at);
+    };
+    auto accumulate = [&](const RootStep<BinT, NF>& st) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int4 qq = st.q[j >> 1];
+            const CellVal v = cell_val<ACC>((j & 1) ? qq.z : qq.x, (j & 1) ? qq.w : qq.y);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, st.b[f].at(j), v);
         }
-    }
-    __syncthreads();
+    };
 
-    unsigned long long* out = hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2;
-    if (it.atomic_merge) {
-        for (int i = threadIdx.x; i < cells; i += blockDim.x) {
-            const unsigned long long a = lg[i], b = lh[i];
-            if (a) atomicAdd(&out[2 * i], a);
-            if (b) atomicAdd(&out[2 * i + 1], b);
+    if (vec_ok) {
+        RootStep<BinT, NF> A, B;
+        if (k + R <= re) {
+            load(k, A);
+            for (;;) {
+                const int64_t kb = k + step;
+                const bool more_b = kb + R <= re;
+                if (more_b) load(kb, B);
+                accumulate(A);
+                k = kb;
+                if (!more_b) break;
+                const int64_t ka = k + step;
+                const bool more_a = ka + R <= re;
+                if (more_a) load(ka, A);
+                accumulate(B);
+                k = ka;
+                if (!more_a) break;
+            }
+        }
+        // the one thread whose next step runs past the end takes the tail
+        for (int64_t r = k; r < re && r < k + R; ++r) {
+            const int2 g = q[r];
+            const CellVal v = cell_val<ACC>(g.x, g.y);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
         }
     } else {
-        for (int i = threadIdx.x; i < cells; i += blockDim.x) {
-            out[2 * i] = lg[i];
-            out[2 * i + 1] = lh[i];
+        for (int64_t r = rb + threadIdx.x; r < re; r += blockDim.x) {
+            const int2 g = q[r];
+            const CellVal v = cell_val<ACC>(g.x, g.y);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
         }
     }
+    __syncthreads();
+    lds_flush<ACC>(lds, NF, S, plane, lc,
+                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                      it.atomic_merge != 0);
+}
+
+// Level fills read their rows through the row index.  Each thread takes
+// kLevelEntries entries per step, strided by the block size so that index and
+// (g, h) loads stay coalesced and only the bin loads scatter, in a two-stage
+// pipeline: the next step's indices are in flight while this step's bins
+// load, and this step's bins while the previous step adds.
+constexpr int kLevelEntries = 8;
+
+template <int E>
+struct Entries {
+    int32_t r[E];
+    int2 g[E];
+    bool ok[E];
+};
+
+template <int E>
+__device__ inline void load_entries(Entries<E>& en, const int32_t* __restrict__ row_index,
+                                    const int2* __restrict__ gh, int64_t base, int64_t rb,
+                                    int64_t re)
+{
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t kk = base + (int64_t)e * blockDim.x + threadIdx.x;
+        en.ok[e] = kk < re;
+        const int64_t kc = en.ok[e] ? kk : rb;   // past the end: a valid address, masked below
+        en.r[e] = row_index[kc];
+        en.g[e] = gh[kc];
+    }
+}
+
+template <int E>
+__device__ inline void check_entries(Entries<E>& en, int64_t n)
+{
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        en.ok[e] = en.ok[e] && (uint32_t)en.r[e] < (uint64_t)n;
+        if (!en.ok[e]) en.r[e] = 0;
+    }
+}
+
+// Feature-major level fill (wide matrices): NF features per block, each bin a
+// scattered one-element load.
+template <typename BinT, int NF, int ACC>
+__global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
+                                                   int n_features, int S, int lc,
+                                                   const int2* __restrict__ gh,
+                                                   const int32_t* __restrict__ row_index,
+                                                   const FillItem* __restrict__ items, int n_items,
+                                                   unsigned long long* __restrict__ hist)
+{
+    extern __shared__ unsigned long long lds[];
+    const int item = xcd_item(blockIdx.x, n_items);
+    if (item >= n_items) return;
+    const FillItem it = items[item];
+    const int f0 = it.f0_nf & 0xffff;
+    constexpr int PL = ACC == kWide ? 2 : 1;
+    const int plane = S << lc;
+    lds_zero(lds, NF * PL * plane);
+    __syncthreads();
+
+    unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
+    const BinT* const col0 = bins + (int64_t)f0 * n;
+    const int64_t rb = it.row_begin, re = it.row_end;
+    constexpr int E = kLevelEntries;
+    const int64_t step = (int64_t)blockDim.x * E;
+
+    struct Data {
+        int b[NF][E];
+    };
+    auto load_data = [&](const Entries<E>& en, Data& d) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int e = 0; e < E; ++e) d.b[f][e] = (int)col0[(int64_t)f * n + en.r[e]];
+    };
+    auto accumulate = [&](const Entries<E>& en, const Data& d) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (!en.ok[e]) continue;   // idle lanes must not pile onto one address
+            const CellVal v = cell_val<ACC>(en.g[e].x, en.g[e].y);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, d.b[f][e], v);
+        }
+    };
+
+    Entries<E> ea, eb;
+    Data da;
+    int64_t base = rb;
+    load_entries<E>(ea, row_index, gh, base, rb, re);
+    check_entries<E>(ea, n);
+    load_data(ea, da);
+    for (;;) {
+        const int64_t nb = base + step;
+        const bool more = nb < re;
+        if (more) load_entries<E>(eb, row_index, gh, nb, rb, re);
+        accumulate(ea, da);
+        if (!more) break;
+        check_entries<E>(eb, n);
+        load_data(eb, da);
+        ea = eb;
+        base = nb;
+    }
+    __syncthreads();
+    lds_flush<ACC>(lds, NF, S, plane, lc,
+                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                      it.atomic_merge != 0);
+}
+
+// Row-major level fill (narrow matrices).  The resident row-major copy pads
+// each row to a multiple of 16 bytes, so a row sits in one or two 64-byte
+// sectors and a sparse node costs about a sector per row instead of a cache
+// line per row and feature.  Each block covers the LT bytes of a row that hold
+// its feature tile (LT / sizeof(BinT) features), read with one load per row.
+template <int LT>
+struct Chunk;
+template <>
+struct Chunk<16> {
+    uint4 w;
+    __device__ inline void load(const uint8_t* p) { w = *(const uint4*)p; }
+    __device__ inline uint32_t word(int i) const { return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w)); }
+};
+template <>
+struct Chunk<8> {
+    uint2 w;
+    __device__ inline void load(const uint8_t* p) { w = *(const uint2*)p; }
+    __device__ inline uint32_t word(int i) const { return i == 0 ? w.x : w.y; }
+};
+template <>
+struct Chunk<4> {
+    uint32_t w;
+    __device__ inline void load(const uint8_t* p) { w = *(const uint32_t*)p; }
+    __device__ inline uint32_t word(int) const { return w; }
+};
+template <>
+struct Chunk<2> {
+    uint32_t w;   // low 16 bits hold the data
+    __device__ inline void load(const uint8_t* p) { w = (uint32_t)*(const uint16_t*)p; }
+    __device__ inline uint32_t word(int) const { return w; }
+};
+
+template <typename BinT, int LT, int ACC>
+__global__ __launch_bounds__(512) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
+                                                   int64_t row_stride, int64_t n, int n_features,
+                                                   int S, int lc, const int2* __restrict__ gh,
+                                                   const int32_t* __restrict__ row_index,
+                                                   const FillItem* __restrict__ items, int n_items,
+                                                   unsigned long long* __restrict__ hist)
+{
+    extern __shared__ unsigned long long lds[];
+    const int item = xcd_item(blockIdx.x, n_items);
+    if (item >= n_items) return;
+    const FillItem it = items[item];
+    const int f0 = it.f0_nf & 0xffff;
+    const int nf = it.f0_nf >> 16;   // <= LT / sizeof(BinT)
+    constexpr int PL = ACC == kWide ? 2 : 1;
+    constexpr int TF = LT / (int)sizeof(BinT);
+    const int plane = S << lc;
+    lds_zero(lds, nf * PL * plane);
+    __syncthreads();
+
+    unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
+    const uint8_t* const tile = bins_rm + (int64_t)f0 * sizeof(BinT);
+    const int64_t rb = it.row_begin, re = it.row_end;
+    constexpr int E = kLevelEntries;
+    const int64_t step = (int64_t)blockDim.x * E;
+
+    struct Data {
+        Chunk<LT> c[E];
+    };
+    auto load_data = [&](const Entries<E>& en, Data& d) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            d.c[e].load(tile + (int64_t)en.r[e] * row_stride);
+        }
+    };
+    auto accumulate = [&](const Entries<E>& en, const Data& d) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (!en.ok[e]) continue;   // idle lanes must not pile onto one address
+            const CellVal v = cell_val<ACC>(en.g[e].x, en.g[e].y);
+#pragma unroll
+            for (int f = 0; f < TF; ++f) {
+                if (f >= nf) break;
+                const uint32_t w = d.c[e].word((f * (int)sizeof(BinT)) >> 2);
+                const int b = sizeof(BinT) == 1 ? (int)((w >> (8 * (f & 3))) & 0xffu)
+                                                : (int)((w >> (16 * (f & 1))) & 0xffffu);
+                lds_add<ACC>(lcopy, plane, lc, f, b, v);
+            }
+        }
+    };
+
+    Entries<E> ea, eb;
+    Data da;
+    int64_t base = rb;
+    load_entries<E>(ea, row_index, gh, base, rb, re);
+    check_entries<E>(ea, n);
+    load_data(ea, da);
+    for (;;) {
+        const int64_t nb = base + step;
+        const bool more = nb < re;
+        if (more) load_entries<E>(eb, row_index, gh, nb, rb, re);
+        accumulate(ea, da);
+        if (!more) break;
+        check_entries<E>(eb, n);
+        load_data(eb, da);
+        ea = eb;
+        base = nb;
+    }
+    __syncthreads();
+    lds_flush<ACC>(lds, nf, S, plane, lc,
+                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                      it.atomic_merge != 0);
 }
 
 // ---------------------------------------------------------------------------

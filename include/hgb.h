@@ -110,8 +110,9 @@ hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on
  * ([bonsai-9] "The idea": device histogram cells are int64 fixed point, so a
  * sum of cells is one integer whatever the order of the additions).
  *
- * For c in {grad, hess}: M = max |c_i|; k = 0 if M == 0, else k = 30 - e with
- * 2^(e-1) <= M < 2^e; q_i = round-half-even(c_i * 2^k).  |q_i| <= 2^30.
+ * For c in {grad, hess}: M = max |c_i|; k = 0 if M == 0, else k = P - e with
+ * 2^(e-1) <= M < 2^e; q_i = round-half-even(c_i * 2^k).  |q_i| <= 2^P.  P is
+ * the context's precision (hgb_set_precision, default 30).
  *
  * grad_dev, hess_dev: fp32 [n_rows] device arrays (n_rows of upload_bins).
  * Synchronizes the stream once (the scales are needed on the host).
@@ -119,6 +120,13 @@ hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on
  *         or a hessian < 0 (-0.0 counts as 0) -- no tree is started then.
  */
 hgb_status hgb_begin_tree(hgb_ctx* ctx, const float* grad_dev, const float* hess_dev);
+
+/* Fixed-point precision P of the next begin_tree, in bits below the largest
+ * |value| (1..30, default 30).  Any P gives exact int64 cells; at P <= 19 the
+ * fill packs both components of a cell into one 64-bit LDS add (the packing of
+ * [ybb] section 7), which halves its LDS traffic.  Ends the current tree.
+ * Errors: HGB_E_INVALID for bits outside [1, 30]. */
+hgb_status hgb_set_precision(hgb_ctx* ctx, int32_t bits);
 
 /* The current tree's scales: a fixed-point sum X stands for X * 2^-k. */
 hgb_status hgb_get_scales(const hgb_ctx* ctx, int32_t* k_g, int32_t* k_h);

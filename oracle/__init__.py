@@ -63,7 +63,7 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        lib.oracle_quantize.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+        lib.oracle_quantize.argtypes = [vp, i64, ctypes.c_int, i32, vp, vp]
         lib.oracle_quantize.restype = ctypes.c_int
         lib.oracle_check_bins.argtypes = [vp, ctypes.c_int, i64, i32, i32, i32]
         lib.oracle_check_bins.restype = ctypes.c_int
@@ -95,12 +95,12 @@ def _bins_arg(bins):
     raise TypeError("bins must be uint8 or uint16")
 
 
-def quantize(c, require_nonneg: bool):
-    """Fixed-point encode one component.  Returns (q int32 [n], k)."""
+def quantize(c, require_nonneg: bool, bits: int = 30):
+    """Fixed-point encode one component at `bits` of precision.  Returns (q int32 [n], k)."""
     c = np.ascontiguousarray(c, dtype=np.float32)
     q = np.empty(c.shape[0], dtype=np.int32)
     k = ctypes.c_int32(0)
-    st = _load().oracle_quantize(_ptr(c), c.shape[0], int(bool(require_nonneg)),
+    st = _load().oracle_quantize(_ptr(c), c.shape[0], int(bool(require_nonneg)), int(bits),
                                  _ptr(q), ctypes.byref(k))
     if st != OK:
         raise OracleError(st, "quantize")

@@ -41,16 +41,20 @@
  * any order.  The pages do not give the scale.  Reading used here:
  *
  *   M = max_i |c_i|.  If M == 0 then k = 0, else with 2^(e-1) <= M < 2^e
- *   (the frexp exponent e) k = 30 - e.  q_i = rint(c_i * 2^k), rounding half
- *   to even.  c_i * 2^k is exact in double, and |q_i| <= 2^30, so q fits int32
- *   and a sum over fewer than 2^32 rows fits int64.
+ *   (the frexp exponent e) k = P - e for a precision of P bits (1..30).
+ *   q_i = rint(c_i * 2^k), rounding half to even.  c_i * 2^k is exact in
+ *   double, and |q_i| <= 2^P <= 2^30, so q fits int32 and a sum over fewer
+ *   than 2^32 rows fits int64.  P = 30 is the default; a smaller P is the
+ *   narrower fixed point that the ybb.press article, section 7, packs two to
+ *   a 64-bit word.
  *
  * Non-finite values are rejected; for the hessian (require_nonneg = 1) so are
  * negative values.  -0.0 counts as zero.
  */
-int oracle_quantize(const float* c, int64_t n, int require_nonneg,
+int oracle_quantize(const float* c, int64_t n, int require_nonneg, int32_t bits,
                     int32_t* q_out, int32_t* k_out)
 {
+    if (bits < 1 || bits > 30) return ORACLE_E_INVALID;
     double m = 0.0;
     for (int64_t i = 0; i < n; ++i) {
         double x = (double)c[i];
@@ -63,7 +67,7 @@ int oracle_quantize(const float* c, int64_t n, int require_nonneg,
     if (m != 0.0) {
         int e = 0;
         (void)frexp(m, &e);      /* m = f * 2^e with 0.5 <= f < 1 */
-        k = 30 - e;
+        k = bits - e;
     }
     for (int64_t i = 0; i < n; ++i) {
         double scaled = ldexp((double)c[i], k);   /* exact */

@@ -27,7 +27,7 @@ typedef struct {
     int64_t g_total, h_total;
 } oracle_split;
 
-int oracle_quantize(const float* c, int64_t n, int require_nonneg,
+int oracle_quantize(const float* c, int64_t n, int require_nonneg, int32_t bits,
                     int32_t* q_out, int32_t* k_out);
 
 int oracle_check_bins(const void* bins, int bin_bytes, int64_t n_rows,

@@ -40,14 +40,15 @@ def hgb(torch):
 
 # ---------------------------------------------------------------- helpers ---
 
-def oracle_quantized(w):
-    qg, kg = oracle.quantize(w.grad, False)
-    qh, kh = oracle.quantize(w.hess, True)
+def oracle_quantized(w, bits=30):
+    qg, kg = oracle.quantize(w.grad, False, bits)
+    qh, kh = oracle.quantize(w.hess, True, bits)
     return qg, qh, kg, kh
 
 
-def new_ctx(hgb, w, torch):
+def new_ctx(hgb, w, torch, bits=30):
     ctx = hgb.Context(0)
+    ctx.set_precision(bits)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
@@ -75,11 +76,11 @@ def gpu_splits(hgb, ctx, hist_t, n_nodes, lam, gamma, torch):
     return hgb.splits_to_numpy(out)[:n_nodes]
 
 
-def run_level_both(hgb, torch, w, check_exact_gain=False):
+def run_level_both(hgb, torch, w, check_exact_gain=False, bits=30):
     """Parents + built children + subtraction + splits on the GPU vs the oracle."""
     L = w.level
-    ctx, g, h = new_ctx(hgb, w, torch)
-    qg, qh, kg, kh = oracle_quantized(w)
+    ctx, g, h = new_ctx(hgb, w, torch, bits)
+    qg, qh, kg, kh = oracle_quantized(w, bits)
     assert ctx.get_scales() == (kg, kh)
     F, S = w.n_features, w.n_slots
     P = L.n_pairs
@@ -110,9 +111,9 @@ def run_level_both(hgb, torch, w, check_exact_gain=False):
     return sp
 
 
-def run_root_both(hgb, torch, w):
-    ctx, g, h = new_ctx(hgb, w, torch)
-    qg, qh, kg, kh = oracle_quantized(w)
+def run_root_both(hgb, torch, w, bits=30):
+    ctx, g, h = new_ctx(hgb, w, torch, bits)
+    qg, qh, kg, kh = oracle_quantized(w, bits)
     assert ctx.get_scales() == (kg, kh)
     t = torch.full((1, w.n_features, w.n_slots, 2), -3, dtype=torch.int64, device="cuda")
     ctx.build_level(t)
@@ -166,14 +167,26 @@ SMALL = [
 
 
 @pytest.mark.parametrize("seed,n,F,B,missing,children,u16", SMALL)
-@pytest.mark.parametrize("wide", [False, True])
-def test_small_random(hgb, torch, seed, n, F, B, missing, children, u16, wide):
-    say("small", seed, n, F, B, missing, children, u16, wide)
+@pytest.mark.parametrize("wide,bits", [(False, 30), (True, 30), (False, 19), (True, 12)])
+def test_small_random(hgb, torch, seed, n, F, B, missing, children, u16, wide, bits):
+    say("small", seed, n, F, B, missing, children, u16, wide, bits)
     w = synth.random_small(seed, n, F, B, missing, children, wide_grad=wide, u16=u16)
     if children == 0:
-        run_root_both(hgb, torch, w)
+        run_root_both(hgb, torch, w, bits)
     else:
-        run_level_both(hgb, torch, w, check_exact_gain=True)
+        run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
+
+
+@pytest.mark.parametrize("name,n,F", [("c2", 300_000, 100), ("c5", 300_000, 50),
+                                      ("c4", 8_192, 1_024), ("c1", None, None)])
+def test_packed_precision_configs(hgb, torch, name, n, F):
+    """Precision 19 selects packed (g, h) accumulation in the fill."""
+    say("packed", name, n, F)
+    w = synth.make(name, n_rows=n, n_features=F)
+    if w.level is not None:
+        run_level_both(hgb, torch, w, check_exact_gain=True, bits=19)
+    if w.kind in ("root", "root+level"):
+        run_root_both(hgb, torch, w, bits=19)
 
 
 def test_c1_full(hgb, torch):
@@ -201,8 +214,8 @@ def test_c4(hgb, torch, n, F):
     run_level_both(hgb, torch, w, check_exact_gain=True)
 
 
-def oracle_tree(w, depth):
-    qg, qh, kg, kh = oracle_quantized(w)
+def oracle_tree(w, depth, bits=30):
+    qg, qh, kg, kh = oracle_quantized(w, bits)
     levels = []
     hist = oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh)
     sp = oracle.find_splits(hist, w.n_bins, w.has_missing, kg, kh, w.lam, w.gamma)
@@ -218,17 +231,18 @@ def oracle_tree(w, depth):
     return levels
 
 
-@pytest.mark.parametrize("n", [300_000, None])
-def test_c3_tree(hgb, torch, n):
-    say("c3 tree", n)
+@pytest.mark.parametrize("n,bits", [(300_000, 30), (None, 30), (300_000, 19), (None, 19)])
+def test_c3_tree(hgb, torch, n, bits):
+    say("c3 tree", n, bits)
     from histogram_gradient_boosted_amd import tree
     w = synth.make("c3", n_rows=n)
     ctx = hgb.Context(0)
+    ctx.set_precision(bits)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
     plans = tree.plan_tree(ctx, w.bins, w.n_bins, g, h, w.depth, w.lam, w.gamma)
-    want = oracle_tree(w, w.depth)
+    want = oracle_tree(w, w.depth, bits)
     assert len(plans) == len(want) == 8
     for d, (plan, (rows, offs, hist, sp)) in enumerate(zip(plans, want)):
         say("c3 level", d)

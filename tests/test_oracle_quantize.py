@@ -92,3 +92,25 @@ def test_wide_dynamic_range_exact_where_representable():
     assert k == 29
     back = [math.ldexp(int(v), -k) for v in q]
     assert back == [float(x) for x in c]
+
+
+def test_precision_one_bit():
+    # M = 0.75 -> e = 0 -> k = 1: 0.75 * 2 = 1.5 -> 2 (= 2^P), 0.25 * 2 = 0.5 -> 0
+    q, k = oracle.quantize(np.array([0.75, 0.25, -0.5], dtype=np.float32), False, bits=1)
+    assert k == 1 and q.tolist() == [2, 0, -1]
+
+
+@pytest.mark.parametrize("bits", [4, 8, 19, 29])
+def test_precision_bits(bits):
+    """k = P - e: the largest value lands in [2^(P-1), 2^P] and half-steps round to even."""
+    step = 2.0 ** -(bits - 1)          # M = 1 -> e = 1 -> k = P - 1
+    vals = [1.0, 0.5 * step, 1.5 * step, -2.5 * step]
+    q, k = oracle.quantize(np.array(vals, dtype=np.float32), require_nonneg=False, bits=bits)
+    assert k == bits - 1
+    assert q.tolist() == [2 ** (bits - 1), 0, 2, -2]
+
+
+@pytest.mark.parametrize("bits", [0, 31])
+def test_precision_out_of_range(bits):
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize(np.ones(3, dtype=np.float32), require_nonneg=True, bits=bits)
