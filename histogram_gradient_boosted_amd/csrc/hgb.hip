@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -20,14 +21,16 @@ using namespace hgb;
 
 namespace {
 
-// gfx950: 160 KiB of LDS per CU.  The root fill runs one 1024-thread block
-// per CU; the level fills run two 512-thread blocks per CU.
-constexpr int64_t kRootLdsBudget = 160 * 1024;
-constexpr int64_t kLevelLdsBudget = 80 * 1024;
+// gfx950: 160 KiB of LDS per CU; every fill runs one 1024-thread block per CU.
+constexpr int64_t kFillLdsBudget = 160 * 1024;
 constexpr int kRootThreads = 1024;
-constexpr int kLevelThreads = 512;
-// Aim for about this many fill blocks per level (several per CU).
-constexpr int64_t kFillTargetItems = 1536;
+constexpr int kLevelThreads = 1024;
+// Fill items per CU: the root gets one equal share per CU (equal items finish
+// together, and fewer items mean fewer merges of partial histograms); other
+// levels, with nodes of very different sizes, get several smaller items per
+// CU for balance.
+constexpr int64_t kRootItemsPerCu = 1;
+constexpr int64_t kLevelItemsPerCu = 4;
 // Keep a row-major copy of the bins when a row takes at most this many bytes.
 constexpr int64_t kRowMajorMaxRowBytes = 512;
 // Default fixed-point precision of begin_tree (bits below the largest value).
@@ -46,6 +49,7 @@ struct Stage {
 
 struct hgb_ctx {
     int device = 0;
+    int n_cu = 256;
     hipStream_t stream = nullptr;
     std::string err;
 
@@ -80,6 +84,14 @@ struct hgb_ctx {
 
     Stage stage[kStages];
     int stage_next = 0;
+
+    // HGB_DEBUG_PLAN=1 in the environment prints each fill plan to stderr
+    bool debug_plan = false;
+    // HGB_FILL_TUNE="key=value,..." overrides the fill planner (developer
+    // tuning): root_lc, root_tile, root_ipc, level_lc, level_tile, level_ipc
+    // (ipc = items per CU), align (rows an item boundary is a multiple of);
+    // -1 keeps the planner's choice.
+    int tune[7] = {-1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
     bool prof = false;
@@ -229,83 +241,103 @@ struct FillPlan {
     int lt;             // rows: bytes loaded per row
     int threads;
     int64_t step_rows;  // rows a block consumes per step
-    int64_t max_chunk;  // rows per item that keep packed sums exact (0: no bound)
+    int drain;          // packed: steps between drains of the copies (0: wide)
     size_t lds_bytes;
 };
 
+// LDS bytes per feature of a tile: the copies, plus the packed accumulator.
 int64_t feature_lds(int acc, int S, int lc)
 {
-    return (int64_t)(acc == kWide ? 2 : 1) * S * 8 * (1 << lc);
+    return (int64_t)tile_words(acc, 1, S, lc) * 8;
 }
 
 // Packed sums stay exact while every copy-slot sees at most
-// kPackedRowsPerCopy rows.  Copy c is used by threads / C threads, each taking
-// `per_thread` rows per step, so an item may hold this many whole steps.
-int64_t packed_max_chunk(int threads, int lc, int per_thread)
+// kPackedRowsPerCopy rows between drains.  Copy c is used by threads / C
+// threads, each taking `per_thread` rows per step; the root kernel may add up
+// to kRootRows - 1 tail rows on one copy after its last step.  Returns the
+// steps between drains (0: not even one step fits).
+int packed_drain_steps(int threads, int lc, int per_thread)
 {
     const int64_t per_copy_step = (int64_t)(threads >> lc) * per_thread;
-    const int64_t steps = kPackedRowsPerCopy / per_copy_step;
-    return steps * threads * per_thread;   // 0 when even one step is too many
+    return (int)((kPackedRowsPerCopy - (kRootRows - 1)) / per_copy_step);
+}
+
+// Cost model of the fill per cell (seconds), from microbenchmarks on the
+// MI355X: random-bin ds_add_u64 runs at kLdsOps[lc] lanes per clock per CU
+// with 2^lc lane-interleaved copies; bins stream from HBM at ~6 TB/s and the
+// (g, h) pair, re-read by every feature tile of a row chunk, mostly from L2 at
+// ~15 TB/s.  The two overlap imperfectly.
+double fill_cost(int acc, int lc, int tile, int w)
+{
+    static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
+    const double lds = (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * 2.4e9 * 256);
+    const double mem = w / 6.0e12 + (8.0 / tile) / 15.0e12;
+    return std::max(lds, mem) + 0.25 * std::min(lds, mem);
 }
 
 FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
 {
     FillPlan p{};
-    p.acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
     const int S = c->S;
     const int w = c->bin_bytes;
-    if (root || !rm) {
-        p.kind = root ? kFillRoot : kFillCols;
-        p.threads = root ? kRootThreads : kLevelThreads;
-        const int per_thread = root ? kRootRows : kLevelEntries;
-        const int64_t budget = root ? kRootLdsBudget : kLevelLdsBudget;
-        // most copies (up to 16) that leave room for one feature
-        p.lc = 4;
-        while (p.lc > 0 && feature_lds(p.acc, S, p.lc) > budget) --p.lc;
-        // packed sums need several copies per block to stay exact; where they
-        // do not fit, accumulate both components in full width (exact for any
-        // precision)
-        if (p.acc == kPacked && packed_max_chunk(p.threads, p.lc, per_thread) == 0) {
-            p.acc = kWide;
-            p.lc = 4;
-            while (p.lc > 0 && feature_lds(p.acc, S, p.lc) > budget) --p.lc;
-        }
-        const int64_t per_feature = feature_lds(p.acc, S, p.lc);
-        const int64_t fit = budget / per_feature;
-        p.tile = fit >= 4 ? 4 : (fit >= 2 ? 2 : 1);
-        while (p.tile > c->F) p.tile >>= 1;
-        p.lt = 0;
-        p.lds_bytes = (size_t)(per_feature * p.tile);
-        p.step_rows = (int64_t)p.threads * per_thread;
-        p.max_chunk = p.acc == kPacked ? packed_max_chunk(p.threads, p.lc, per_thread) : 0;
-        return p;
-    }
-    // row-major level fill: the widest row load (16 bytes down to 2) whose
-    // features fit the budget with at least the minimum copy count
-    p.kind = kFillRowsKind;
-    p.threads = kLevelThreads;
-    const int min_lc = p.acc == kPacked ? 1 : 0;
-    p.lt = 0;
-    for (int lt = 16; lt >= 2 && !p.lt; lt >>= 1) {
-        if (lt < w) break;
-        const int tf = lt / w;
-        for (int lc = 4; lc >= min_lc; --lc) {
-            if (tf * feature_lds(p.acc, S, lc) <= kLevelLdsBudget &&
-                (p.acc == kWide || packed_max_chunk(p.threads, lc, kLevelEntries) > 0)) {
-                p.lt = lt;
-                p.lc = lc;
-                break;
+    p.kind = root ? kFillRoot : (rm ? kFillRowsKind : kFillCols);
+    p.threads = root ? kRootThreads : kLevelThreads;
+    auto per_thread_of = [&](int tile) {
+        return p.kind == kFillRoot ? kRootRows : (p.kind == kFillCols ? cols_entries(tile) : kLevelEntries);
+    };
+    const int64_t budget = kFillLdsBudget;
+    const int want_acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
+    // Candidate tiles: NF in {1, 2, 4, 8} features (root, cols), or the
+    // features of one 16/8/4/2-byte row load (rows).
+    double best = 1e300;
+    bool found = false;
+    for (int acc : {want_acc, (int)kWide}) {
+        if (found) break;   // fall back to wide sums only when packed cannot fit
+        for (int lc = 4; lc >= 0; --lc) {
+            const int64_t per_feature = feature_lds(acc, S, lc);
+            const int force_lc = c->tune[root ? 0 : 3];
+            if (force_lc >= 0 && lc != force_lc) continue;
+            for (int k = 0; k < 4; ++k) {
+                int tile, lt = 0;
+                if (p.kind == kFillRowsKind) {
+                    lt = 16 >> k;
+                    if (lt < w) continue;
+                    tile = lt / w;
+                } else {
+                    tile = 8 >> k;
+                }
+                const int force_tile = c->tune[root ? 1 : 4];
+                if (force_tile > 0 && tile != force_tile) continue;
+                if (tile * per_feature > budget) continue;
+                if (p.kind == kFillRoot && w == 2 && tile > 4) continue;   // register-bound
+                if (acc == kPacked && packed_drain_steps(p.threads, lc, per_thread_of(tile)) == 0) continue;
+                // a tile much wider than the matrix wastes nothing but LDS
+                const int eff = std::min(tile, c->F);
+                const double cost = fill_cost(acc, lc, eff, w);
+                if (cost < best) {
+                    best = cost;
+                    found = true;
+                    p.acc = acc;
+                    p.lc = lc;
+                    p.tile = tile;
+                    p.lt = lt;
+                }
             }
         }
     }
-    if (!p.lt) {   // huge S: one feature, one copy
-        p.lt = w;
-        p.lc = min_lc;
+    if (!found) {   // one wide feature of one copy always fits (S <= HGB_MAX_SLOTS)
+        p.acc = kWide;
+        p.lc = 0;
+        p.tile = 1;
+        p.lt = p.kind == kFillRowsKind ? w : 0;
     }
-    p.tile = p.lt / w;
+    if (p.kind != kFillRowsKind) {
+        // rows loads cover exactly `tile` features; the others take min(NF, F)
+        while (p.tile > 1 && (p.tile >> 1) >= c->F) p.tile >>= 1;
+    }
     p.lds_bytes = (size_t)(p.tile * feature_lds(p.acc, S, p.lc));
-    p.step_rows = (int64_t)p.threads * kLevelEntries;
-    p.max_chunk = p.acc == kPacked ? packed_max_chunk(p.threads, p.lc, kLevelEntries) : 0;
+    p.step_rows = (int64_t)p.threads * per_thread_of(p.tile);
+    p.drain = p.acc == kPacked ? packed_drain_steps(p.threads, p.lc, per_thread_of(p.tile)) : 0;
     return p;
 }
 
@@ -323,6 +355,7 @@ struct FillArgs {
     const FillItem* items;
     int n_items;
     int vec_ok;
+    int drain;
     int64_t* hist;
 };
 
@@ -340,24 +373,32 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
     } while (0)
     if (p.kind == kFillRoot) {
+#define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist)
         switch (p.tile) {
-        case 1: HGB_LAUNCH((k_fill_root<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
-        case 2: HGB_LAUNCH((k_fill_root<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
-        default: HGB_LAUNCH((k_fill_root<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist); break;
+        case 1: HGB_ROOT(1); break;
+        case 2: HGB_ROOT(2); break;
+        case 3: HGB_ROOT(3); break;
+        case 4: HGB_ROOT(4); break;
+        case 5: HGB_ROOT(5); break;
+        case 6: HGB_ROOT(6); break;
+        case 7: HGB_ROOT(7); break;
+        default: HGB_ROOT(8); break;
         }
+#undef HGB_ROOT
     } else if (p.kind == kFillCols) {
         switch (p.tile) {
-        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
-        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
-        default: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
         }
     } else {
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
         switch (p.lt) {
-        case 16: HGB_LAUNCH((k_fill_rows<BinT, 16, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
-        case 8: HGB_LAUNCH((k_fill_rows<BinT, 8, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
-        case 4: HGB_LAUNCH((k_fill_rows<BinT, 4, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
-        default: HGB_LAUNCH((k_fill_rows<BinT, 2, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, hist); break;
+        case 16: HGB_LAUNCH((k_fill_rows<BinT, 16, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        case 8: HGB_LAUNCH((k_fill_rows<BinT, 8, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        case 4: HGB_LAUNCH((k_fill_rows<BinT, 4, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        default: HGB_LAUNCH((k_fill_rows<BinT, 2, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
         }
     }
 #undef HGB_LAUNCH
@@ -395,6 +436,25 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     if (hipSetDevice(device) != hipSuccess) return HGB_E_DEVICE;
     hgb_ctx* c = new hgb_ctx();
     c->device = device;
+    if (const char* e = std::getenv("HGB_DEBUG_PLAN")) c->debug_plan = e[0] == '1';
+    if (const char* e = std::getenv("HGB_FILL_TUNE")) {
+        static const char* keys[7] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align"};
+        std::string spec(e);
+        size_t pos = 0;
+        while (pos < spec.size()) {
+            size_t end = spec.find(',', pos);
+            if (end == std::string::npos) end = spec.size();
+            const std::string kv = spec.substr(pos, end - pos);
+            const size_t eq = kv.find('=');
+            if (eq != std::string::npos)
+                for (int k = 0; k < 7; ++k)
+                    if (kv.compare(0, eq, keys[k]) == 0) c->tune[k] = std::atoi(kv.c_str() + eq + 1);
+            pos = end + 1;
+        }
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+        c->n_cu = prop.multiProcessorCount;
     c->stream = (hipStream_t)hip_stream;
     if (hipMalloc((void**)&c->dev_words, 64) != hipSuccess ||
         hipHostMalloc((void**)&c->host_words, 64, hipHostMallocDefault) != hipSuccess ||
@@ -543,10 +603,11 @@ hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
     if (st != HGB_OK) return st;
     k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 2);
     HGB_LAUNCHED(c, "k_clear_u32");
+    const int vec = ((uintptr_t)grad % 16 == 0 && (uintptr_t)hess % 16 == 0) ? 1 : 0;
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_grad_hess_max<<<grid_for(c->n, 256, 2048), 256, 0, c->stream>>>(grad, hess, c->n,
-                                                                           c->dev_words);
+        k_grad_hess_max<<<grid_for((c->n + 3) / 4, 256, 1024), 256, 0, c->stream>>>(grad, hess, c->n,
+                                                                                 vec, c->dev_words);
     }
     HGB_LAUNCHED(c, "k_grad_hess_max");
     HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
@@ -572,8 +633,8 @@ hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
     c->k_h = k[1];
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_quantize<<<grid_for(c->n, 256, 4096), 256, 0, c->stream>>>(
-            grad, hess, c->n, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
+        k_quantize<<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
+            grad, hess, c->n, vec, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
     }
     HGB_LAUNCHED(c, "k_quantize");
     c->have_tree = true;
@@ -647,22 +708,62 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     // The root reads rows in order; other levels read through the row index,
     // from the row-major copy when there is one.
     const bool rm = !root && c->bins_rm != nullptr;
-    const FillPlan plan = plan_fill(c, root, rm);
-    const int T = plan.tile;
-    const int n_tiles = (c->F + T - 1) / T;
+    const FillPlan plan0 = plan_fill(c, root, rm);
     const int64_t node_elems = (int64_t)c->F * c->S * 2;
 
-    // Rows per item: about kFillTargetItems items over the level, in whole
-    // block steps, and within the packed-exactness bound.
-    int64_t ch = (total * n_tiles + kFillTargetItems - 1) / kFillTargetItems;
-    ch = std::max<int64_t>((ch + plan.step_rows - 1) / plan.step_rows * plan.step_rows, plan.step_rows);
-    if (plan.max_chunk > 0) ch = std::min(ch, plan.max_chunk);
+    // Feature tiles (f0, width).  Root tiles have exactly the kernel's width:
+    // full tiles of plan.tile, then the remainder split into powers of two,
+    // each width its own launch.  Level tiles are plan.tile wide, the last one
+    // possibly narrower (those kernels take the width at run time).
+    std::vector<std::pair<int, int>> tiles;
+    FillPlan plan = plan0;
+    if (root) {
+        // equal tiles when a divisor of F close to the planned width exists
+        for (int d = plan.tile; d >= 1 && 2 * d > plan.tile; --d)
+            if (c->F % d == 0) {
+                plan.tile = d;
+                break;
+            }
+    }
+    {
+        int f0 = 0;
+        for (; f0 + plan.tile <= c->F; f0 += plan.tile) tiles.emplace_back(f0, plan.tile);
+        if (f0 < c->F) {
+            if (root) {
+                for (int wdt = plan.tile >> 1; wdt >= 1; wdt >>= 1)
+                    if (f0 + wdt <= c->F) {
+                        tiles.emplace_back(f0, wdt);
+                        f0 += wdt;
+                    }
+            } else {
+                tiles.emplace_back(f0, c->F - f0);
+            }
+        }
+    }
+    const int n_tiles = (int)tiles.size();
+    for (const auto& t : tiles)
+        if (t.second < 1 || (root && t.second > 8) || t.first + t.second > c->F)
+            return fail(c, HGB_E_DEVICE, "build_level: internal error in the tile plan");
+
+    // Rows per item: about (items per CU) x (CUs) items of equal size over the
+    // level, a multiple of 8 rows (the root's vector groups).
+    int64_t ipc = root ? kRootItemsPerCu : kLevelItemsPerCu;
+    if (c->tune[root ? 2 : 5] > 0) ipc = c->tune[root ? 2 : 5];
+    const int64_t target = ipc * c->n_cu;
+    // Item boundaries on 128-row multiples keep the root's bin and (g, h)
+    // loads cache-line aligned.
+    int64_t align = 128;
+    if (c->tune[6] > 0) align = (c->tune[6] + 7) / 8 * 8;
+    int64_t ch = (total * n_tiles + target - 1) / target;
+    ch = std::max<int64_t>((ch + align - 1) / align * align, align);
 
     // Item order decides which items share an L2 (the kernel gives each XCD a
     // contiguous run).  Root and row-major levels: (node, chunk, tile) -- the
     // tiles of one row chunk read the same rows.  Feature-major levels:
     // (tile, chunk, node) -- the nodes of one tile read the same columns.
-    std::vector<FillItem> items;
+    // groups[w]: the items of root tiles of width w (one launch each; root
+    // widths are 1, 2, 4 or 8).  Level items all go to groups[0].
+    std::vector<FillItem> groups[9];
     std::vector<int32_t> zero_slots;
     std::vector<int64_t> nchunks(n_nodes);
     int64_t max_ch = 0;
@@ -671,16 +772,16 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         max_ch = std::max(max_ch, nchunks[i]);
         if (count[i] == 0 || nchunks[i] > 1) zero_slots.push_back(slots[i]);
     }
+    size_t n_items = 0;
     auto push = [&](int i, int64_t j, int t) {
-        const int f0 = t * T;
-        const int nf = std::min(T, c->F - f0);
         FillItem it{};
         it.out_slot = slots[i];
         it.row_begin = (int32_t)(begin[i] + j * ch);
         it.row_end = (int32_t)std::min<int64_t>(begin[i] + (j + 1) * ch, begin[i] + count[i]);
-        it.f0_nf = f0 | (nf << 16);
+        it.f0_nf = tiles[t].first | (tiles[t].second << 16);
         it.atomic_merge = nchunks[i] > 1 ? 1 : 0;
-        items.push_back(it);
+        groups[root ? tiles[t].second : 0].push_back(it);
+        ++n_items;
     };
     if (plan.kind != kFillCols) {
         for (int i = 0; i < n_nodes; ++i)
@@ -692,6 +793,13 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
                 for (int i = 0; i < n_nodes; ++i)
                     if (j < nchunks[i]) push(i, j, t);
     }
+    if (n_items > (size_t)INT32_MAX / 8)
+        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many fill items");
+    if (c->debug_plan)
+        std::fprintf(stderr,
+                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d drain %d chunk %lld items %zu lds %zu\n",
+                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.drain, (long long)ch,
+                     n_items, plan.lds_bytes);
     const int2* gh = c->q;
     if (!root) {
         hgb_status st = grow(c, &c->gh, &c->gh_cap, std::max<int64_t>(total, 1));
@@ -717,21 +825,29 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         st = stage_release(c, s);
         if (st != HGB_OK) return st;
     }
-    if (!items.empty()) {
+    for (int wdt = 8; wdt >= 0; --wdt) {
+        std::vector<FillItem>& items = groups[wdt];
+        if (items.empty()) continue;
         Stage* s = nullptr;
         hgb_status st = stage_upload(c, items.data(), items.size() * sizeof(FillItem), &s);
         if (st != HGB_OK) return st;
+        FillPlan gp = plan;
+        if (root && wdt > 0) {
+            gp.tile = wdt;
+            gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc));
+        }
         FillArgs a;
         a.gh = gh;
         a.row_index = row_index;
         a.items = (const FillItem*)s->dev;
         a.n_items = (int)items.size();
         // 8-row vector loads of the root need rows aligned to 8 (chunk starts
-        // are whole steps)
+        // are multiples of 8)
         a.vec_ok = (c->n % 8 == 0) ? 1 : 0;
+        a.drain = std::max(plan.drain, 1);
         a.hist = hist;
         ProfScope ps(c, HGB_KERNEL_FILL);
-        st = launch_fill(c, plan, a);
+        st = launch_fill(c, gp, a);
         if (st != HGB_OK) return st;
         st = stage_release(c, s);
         if (st != HGB_OK) return st;

@@ -25,26 +25,50 @@ __global__ void k_clear_u32(uint32_t* p, int n)
     if (i < n) p[i] = 0u;
 }
 
+__device__ inline uint32_t abs_pattern(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+__device__ inline uint32_t hess_pattern(float x)
+{
+    const uint32_t b = __float_as_uint(x);
+    return b == 0x80000000u ? 0u : b;
+}
+
+// Four rows per thread per step (16-byte loads, when `vec` says both arrays
+// are 16-byte aligned); the leftover rows one by one at the end.
 __global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__ g,
                                                        const float* __restrict__ h, int64_t n,
-                                                       uint32_t* __restrict__ out)
+                                                       int vec, uint32_t* __restrict__ out)
 {
     uint32_t mg = 0, mh = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        uint32_t bg = __float_as_uint(g[i]) & 0x7fffffffu;
-        uint32_t bh = __float_as_uint(h[i]);
-        if (bh == 0x80000000u) bh = 0u;
-        mg = bg > mg ? bg : mg;
-        mh = bh > mh ? bh : mh;
+    const int64_t n4 = vec ? (n >> 2) : 0;
+    const float4* g4 = (const float4*)g;
+    const float4* h4 = (const float4*)h;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 a = g4[i], b = h4[i];
+        mg = max(mg, max(max(abs_pattern(a.x), abs_pattern(a.y)), max(abs_pattern(a.z), abs_pattern(a.w))));
+        mh = max(mh, max(max(hess_pattern(b.x), hess_pattern(b.y)), max(hess_pattern(b.z), hess_pattern(b.w))));
+    }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        mg = max(mg, abs_pattern(g[i]));
+        mh = max(mh, hess_pattern(h[i]));
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
-        uint32_t og = __shfl_xor(mg, off, kWave);
-        uint32_t oh = __shfl_xor(mh, off, kWave);
-        mg = og > mg ? og : mg;
-        mh = oh > mh ? oh : mh;
+        mg = max(mg, (uint32_t)__shfl_xor((int)mg, off, kWave));
+        mh = max(mh, (uint32_t)__shfl_xor((int)mh, off, kWave));
     }
+    // one pair of atomics per block: same-address atomics serialize at the L2
+    __shared__ uint32_t red[2][256 / kWave];
+    const int wv = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) {
+        red[0][wv] = mg;
+        red[1][wv] = mh;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < (int)(blockDim.x / kWave); ++i) {
+            mg = max(mg, red[0][i]);
+            mh = max(mh, red[1][i]);
+        }
         atomicMax(&out[0], mg);
         atomicMax(&out[1], mh);
     }
@@ -53,15 +77,27 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__
 // q = round-half-even(c * 2^k), both components packed per row as (qg, qh).
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ g,
                                                   const float* __restrict__ h, int64_t n,
-                                                  double scale_g, double scale_h,
+                                                  int vec, double scale_g, double scale_h,
                                                   int2* __restrict__ q)
 {
+    // exact: power-of-two scaling of an fp32 value in double, then ties-to-even
+    auto enc = [&](float a, float b) {
+        return make_int2((int)__builtin_rint((double)a * scale_g),
+                         (int)__builtin_rint((double)b * scale_h));
+    };
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        double a = (double)g[i] * scale_g;   // exact: power-of-two scaling of an fp32
-        double b = (double)h[i] * scale_h;
-        q[i] = make_int2((int)__builtin_rint(a), (int)__builtin_rint(b));
+    const int64_t n4 = vec ? (n >> 2) : 0;
+    const float4* g4 = (const float4*)g;
+    const float4* h4 = (const float4*)h;
+    int4* q4 = (int4*)q;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 a = g4[i], b = h4[i];
+        const int2 r0 = enc(a.x, b.x), r1 = enc(a.y, b.y), r2 = enc(a.z, b.z), r3 = enc(a.w, b.w);
+        q4[2 * i] = make_int4(r0.x, r0.y, r1.x, r1.y);
+        q4[2 * i + 1] = make_int4(r2.x, r2.y, r3.x, r3.y);
     }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        q[i] = enc(g[i], h[i]);
 }
 
 // upload_bins: largest stored value, to validate every value is a slot.
@@ -179,9 +215,10 @@ __device__ inline int xcd_item(int bid, int n_items)
 //   kWide    two ds_add_u64 per cell, one per component (gradient and hessian
 //            planes, [nf][2][S][C] u64).  Exact for any fixed-point precision.
 //   kPacked  one ds_add_u64 per cell on qh * 2^32 + qg ([nf][S][C] u64).  Each
-//            copy-slot sums at most kPackedRowsPerCopy rows of |q| <= 2^19, so
-//            the low half never leaves the int32 range and both sums decode
-//            exactly: G = sign-extended low 32 bits, H = (V - G) / 2^32.
+//            copy-slot sums at most kPackedRowsPerCopy rows of |q| <= 2^19
+//            between drains into an int64 accumulator, so the low half never
+//            leaves the int32 range and both sums decode exactly:
+//            G = sign-extended low 32 bits, H = (V - G) / 2^32.
 // ---------------------------------------------------------------------------
 enum { kWide = 0, kPacked = 1 };
 constexpr int kPackedMaxBits = 19;
@@ -221,30 +258,61 @@ __device__ inline void lds_zero(unsigned long long* lds, int words)
     if ((words & 1) && threadIdx.x == 0) lds[words - 1] = 0ull;
 }
 
-// Sum the copies of every cell of the tile (rotated start, so neighbouring
-// lanes read different banks) and write it to the level buffer.
-template <int ACC>
-__device__ inline void lds_flush(const unsigned long long* lds, int nf, int S, int plane, int lc,
-                                 unsigned long long* out, bool atomic_merge)
+// Packed mode keeps, after the copies, an int64 accumulator [nf][S][2] in LDS.
+// Every `drain` steps the copies are decoded into it and zeroed, so a block
+// can cover any number of rows while each copy-slot stays within
+// kPackedRowsPerCopy rows between drains.
+__device__ inline void lds_drain(unsigned long long* lds, int nf, int S, int plane, int lc)
 {
+    long long* acc = (long long*)(lds + nf * plane);
     const int cells = nf * S;
     const int C = 1 << lc;
     for (int i = threadIdx.x; i < cells; i += blockDim.x) {
         const int f = i / S;
         const int sl = i - f * S;
-        const unsigned long long* pg = lds + f * (ACC == kWide ? 2 : 1) * plane + (sl << lc);
+        unsigned long long* pg = lds + f * plane + (sl << lc);
         long long g = 0, h = 0;
         for (int cc = 0; cc < C; ++cc) {
-            const int c = (cc + i) & (C - 1);
-            if (ACC == kWide) {
+            const int c = (cc + i) & (C - 1);   // rotated start: neighbouring lanes, other banks
+            const long long v = (long long)pg[c];
+            const long long lo = (long long)(int)(unsigned)(v & 0xffffffffll);
+            g += lo;
+            h += (v - lo) >> 32;
+            pg[c] = 0ull;
+        }
+        acc[2 * i] += g;
+        acc[2 * i + 1] += h;
+    }
+}
+
+// Sum the tile's copies (wide) or take the drained accumulator (packed) and
+// write the tile to the level buffer: a plain store when the item covers its
+// whole node, an int64 atomic add otherwise.
+template <int ACC>
+__device__ inline void lds_finish(unsigned long long* lds, int nf, int S, int plane, int lc,
+                                  unsigned long long* out, bool atomic_merge)
+{
+    if (ACC == kPacked) {
+        lds_drain(lds, nf, S, plane, lc);
+        __syncthreads();
+    }
+    const int cells = nf * S;
+    const int C = 1 << lc;
+    const long long* acc = (const long long*)(lds + nf * plane);
+    for (int i = threadIdx.x; i < cells; i += blockDim.x) {
+        long long g = 0, h = 0;
+        if (ACC == kWide) {
+            const int f = i / S;
+            const int sl = i - f * S;
+            const unsigned long long* pg = lds + f * 2 * plane + (sl << lc);
+            for (int cc = 0; cc < C; ++cc) {
+                const int c = (cc + i) & (C - 1);
                 g += (long long)pg[c];
                 h += (long long)pg[plane + c];
-            } else {
-                const long long v = (long long)pg[c];
-                const long long lo = (long long)(int)(unsigned)(v & 0xffffffffll);
-                g += lo;
-                h += (v - lo) >> 32;
             }
+        } else {
+            g = acc[2 * i];
+            h = acc[2 * i + 1];
         }
         if (atomic_merge) {
             if (g) atomicAdd(&out[2 * i], (unsigned long long)g);
@@ -256,10 +324,16 @@ __device__ inline void lds_flush(const unsigned long long* lds, int nf, int S, i
     }
 }
 
+// LDS words of a tile: the copies, plus the packed accumulator.
+__host__ __device__ inline int tile_words(int acc_mode, int nf, int S, int lc)
+{
+    return acc_mode == kWide ? nf * 2 * (S << lc) : nf * (S << lc) + nf * S * 2;
+}
+
 // Root fill: the level's one node holds every row in order, so each thread
 // reads 8 consecutive rows per step -- a 16-byte (g, h) load per two rows and
 // one 8- or 16-byte bin load per feature -- and loads the next step while it
-// adds the current one.  NF features per block (the host gives every item NF).
+// adds the current one.  NF features per block.
 constexpr int kRootRows = 8;
 
 template <typename BinT>
@@ -296,16 +370,16 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
                                                     int n_features, int S, int lc,
                                                     const int2* __restrict__ q,
                                                     const FillItem* __restrict__ items, int n_items,
-                                                    int vec_ok, unsigned long long* __restrict__ hist)
+                                                    int vec_ok, int drain,
+                                                    unsigned long long* __restrict__ hist)
 {
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
     if (item >= n_items) return;
     const FillItem it = items[item];
-    const int f0 = it.f0_nf & 0xffff;
-    constexpr int PL = ACC == kWide ? 2 : 1;
+    const int f0 = it.f0_nf & 0xffff;   // every item of this launch has exactly NF features
     const int plane = S << lc;
-    lds_zero(lds, NF * PL * plane);
+    lds_zero(lds, tile_words(ACC, NF, S, lc));
     __syncthreads();
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
@@ -313,7 +387,7 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     const int64_t rb = it.row_begin, re = it.row_end;
     constexpr int R = kRootRows;
     const int64_t step = (int64_t)blockDim.x * R;
-    int64_t k = rb + (int64_t)threadIdx.x * R;
+    const int64_t off = (int64_t)threadIdx.x * R;
 
     auto load = [&](int64_t at, RootStep<BinT, NF>& st) {
         const int4* g4 = (const int4*)(q + at);
@@ -322,54 +396,73 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
 #pragma unroll
         for (int f = 0; f < NF; ++f) st.b[f].load(col0 + (int64_t)f * n + at);
     };
-    auto accumulate = [&](const RootStep<BinT, NF>& st) {
+    // `live` is false for a thread whose group lies past the item: it then
+    // adds zeros (to valid bins), which keeps the loop free of divergence.
+    auto accumulate = [&](const RootStep<BinT, NF>& st, bool live) {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int4 qq = st.q[j >> 1];
-            const CellVal v = cell_val<ACC>((j & 1) ? qq.z : qq.x, (j & 1) ? qq.w : qq.y);
+            const int gv = live ? ((j & 1) ? qq.z : qq.x) : 0;
+            const int hv = live ? ((j & 1) ? qq.w : qq.y) : 0;
+            const CellVal v = cell_val<ACC>(gv, hv);
 #pragma unroll
             for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, st.b[f].at(j), v);
         }
     };
+    auto add_row = [&](int64_t r) {
+        const int2 g = q[r];
+        const CellVal v = cell_val<ACC>(g.x, g.y);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
+    };
+    // packed: decode the copies into the accumulator every `drain` steps (the
+    // step loop is uniform across the block, so the barriers are too)
+    auto drain_now = [&]() {
+        __syncthreads();
+        lds_drain(lds, NF, S, plane, lc);
+        __syncthreads();
+    };
 
     if (vec_ok) {
+        // Whole 8-row groups; the rows after the last whole group are added
+        // one by one afterwards.  Loads are issued unconditionally (clamped to
+        // a valid group), since a load under a branch would make the compiler
+        // wait for it at the join; the next step's loads are in flight while
+        // the current step adds.
+        const int64_t full = (re - rb) / R;
+        const int64_t gend = rb + full * R;
+        const int64_t n_steps = (full + blockDim.x - 1) / blockDim.x;
+        const int64_t last = full > 0 ? gend - R : rb;
+        int dcount = 0;
         RootStep<BinT, NF> A, B;
-        if (k + R <= re) {
-            load(k, A);
-            for (;;) {
-                const int64_t kb = k + step;
-                const bool more_b = kb + R <= re;
-                if (more_b) load(kb, B);
-                accumulate(A);
-                k = kb;
-                if (!more_b) break;
-                const int64_t ka = k + step;
-                const bool more_a = ka + R <= re;
-                if (more_a) load(ka, A);
-                accumulate(B);
-                k = ka;
-                if (!more_a) break;
-            }
+        if (n_steps > 0) load(rb + off + R <= gend ? rb + off : last, A);
+        for (int64_t s = 0; s < n_steps; s += 2) {
+            const int64_t a_at = rb + s * step + off;
+            const int64_t b_at = a_at + step;
+            load(b_at + R <= gend ? b_at : last, B);
+            accumulate(A, a_at + R <= gend);
+            if (ACC == kPacked && ++dcount == drain) { drain_now(); dcount = 0; }
+            if (s + 1 >= n_steps) break;
+            const int64_t c_at = b_at + step;
+            load(c_at + R <= gend ? c_at : last, A);
+            accumulate(B, b_at + R <= gend);
+            if (ACC == kPacked && ++dcount == drain) { drain_now(); dcount = 0; }
         }
-        // the one thread whose next step runs past the end takes the tail
-        for (int64_t r = k; r < re && r < k + R; ++r) {
-            const int2 g = q[r];
-            const CellVal v = cell_val<ACC>(g.x, g.y);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
-        }
+        if (threadIdx.x == 0)
+            for (int64_t r = gend; r < re; ++r) add_row(r);
     } else {
-        for (int64_t r = rb + threadIdx.x; r < re; r += blockDim.x) {
-            const int2 g = q[r];
-            const CellVal v = cell_val<ACC>(g.x, g.y);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
+        const int64_t n_steps = (re - rb + blockDim.x - 1) / blockDim.x;
+        int dcount = 0;
+        for (int64_t s = 0; s < n_steps; ++s) {
+            const int64_t r = rb + s * blockDim.x + threadIdx.x;
+            if (r < re) add_row(r);
+            if (ACC == kPacked && ++dcount == drain * R) { drain_now(); dcount = 0; }
         }
     }
     __syncthreads();
-    lds_flush<ACC>(lds, NF, S, plane, lc,
-                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                      it.atomic_merge != 0);
+    lds_finish<ACC>(lds, NF, S, plane, lc,
+                    hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                    it.atomic_merge != 0);
 }
 
 // Level fills read their rows through the row index.  Each thread takes
@@ -378,6 +471,9 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
 // pipeline: the next step's indices are in flight while this step's bins
 // load, and this step's bins while the previous step adds.
 constexpr int kLevelEntries = 8;
+// Entries per thread and step of the feature-major level fill with NF features
+// (fewer for wide tiles, so the step's bins stay in registers).
+__host__ __device__ constexpr int cols_entries(int nf) { return nf >= 8 ? 4 : kLevelEntries; }
 
 template <int E>
 struct Entries {
@@ -414,27 +510,27 @@ __device__ inline void check_entries(Entries<E>& en, int64_t n)
 // Feature-major level fill (wide matrices): NF features per block, each bin a
 // scattered one-element load.
 template <typename BinT, int NF, int ACC>
-__global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
+__global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
                                                    int n_features, int S, int lc,
                                                    const int2* __restrict__ gh,
                                                    const int32_t* __restrict__ row_index,
                                                    const FillItem* __restrict__ items, int n_items,
-                                                   unsigned long long* __restrict__ hist)
+                                                   int drain, unsigned long long* __restrict__ hist)
 {
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
     if (item >= n_items) return;
     const FillItem it = items[item];
     const int f0 = it.f0_nf & 0xffff;
-    constexpr int PL = ACC == kWide ? 2 : 1;
+    const int nf = it.f0_nf >> 16;   // <= NF
     const int plane = S << lc;
-    lds_zero(lds, NF * PL * plane);
+    lds_zero(lds, tile_words(ACC, nf, S, lc));
     __syncthreads();
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
     const BinT* const col0 = bins + (int64_t)f0 * n;
     const int64_t rb = it.row_begin, re = it.row_end;
-    constexpr int E = kLevelEntries;
+    constexpr int E = cols_entries(NF);
     const int64_t step = (int64_t)blockDim.x * E;
 
     struct Data {
@@ -442,9 +538,9 @@ __global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins
     };
     auto load_data = [&](const Entries<E>& en, Data& d) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+        for (int f = 0; f < NF; ++f)   // a feature past the tile re-reads the last one
 #pragma unroll
-            for (int e = 0; e < E; ++e) d.b[f][e] = (int)col0[(int64_t)f * n + en.r[e]];
+            for (int e = 0; e < E; ++e) d.b[f][e] = (int)col0[(int64_t)(f < nf ? f : nf - 1) * n + en.r[e]];
     };
     auto accumulate = [&](const Entries<E>& en, const Data& d) {
 #pragma unroll
@@ -452,7 +548,8 @@ __global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins
             if (!en.ok[e]) continue;   // idle lanes must not pile onto one address
             const CellVal v = cell_val<ACC>(en.g[e].x, en.g[e].y);
 #pragma unroll
-            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, d.b[f][e], v);
+            for (int f = 0; f < NF; ++f)
+                if (f < nf) lds_add<ACC>(lcopy, plane, lc, f, d.b[f][e], v);
         }
     };
 
@@ -462,11 +559,16 @@ __global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins
     load_entries<E>(ea, row_index, gh, base, rb, re);
     check_entries<E>(ea, n);
     load_data(ea, da);
-    for (;;) {
+    for (int64_t s = 0;; ++s) {   // uniform across the block
         const int64_t nb = base + step;
         const bool more = nb < re;
-        if (more) load_entries<E>(eb, row_index, gh, nb, rb, re);
+        load_entries<E>(eb, row_index, gh, nb, rb, re);   // unconditional, see k_fill_root
         accumulate(ea, da);
+        if (ACC == kPacked && (s + 1) % drain == 0) {
+            __syncthreads();
+            lds_drain(lds, nf, S, plane, lc);
+            __syncthreads();
+        }
         if (!more) break;
         check_entries<E>(eb, n);
         load_data(eb, da);
@@ -474,7 +576,7 @@ __global__ __launch_bounds__(512) void k_fill_cols(const BinT* __restrict__ bins
         base = nb;
     }
     __syncthreads();
-    lds_flush<ACC>(lds, NF, S, plane, lc,
+    lds_finish<ACC>(lds, nf, S, plane, lc,
                       hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
                       it.atomic_merge != 0);
 }
@@ -512,12 +614,12 @@ struct Chunk<2> {
 };
 
 template <typename BinT, int LT, int ACC>
-__global__ __launch_bounds__(512) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
+__global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
                                                    int S, int lc, const int2* __restrict__ gh,
                                                    const int32_t* __restrict__ row_index,
                                                    const FillItem* __restrict__ items, int n_items,
-                                                   unsigned long long* __restrict__ hist)
+                                                   int drain, unsigned long long* __restrict__ hist)
 {
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
@@ -525,10 +627,9 @@ __global__ __launch_bounds__(512) void k_fill_rows(const uint8_t* __restrict__ b
     const FillItem it = items[item];
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= LT / sizeof(BinT)
-    constexpr int PL = ACC == kWide ? 2 : 1;
     constexpr int TF = LT / (int)sizeof(BinT);
     const int plane = S << lc;
-    lds_zero(lds, nf * PL * plane);
+    lds_zero(lds, tile_words(ACC, nf, S, lc));
     __syncthreads();
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
@@ -568,11 +669,16 @@ __global__ __launch_bounds__(512) void k_fill_rows(const uint8_t* __restrict__ b
     load_entries<E>(ea, row_index, gh, base, rb, re);
     check_entries<E>(ea, n);
     load_data(ea, da);
-    for (;;) {
+    for (int64_t s = 0;; ++s) {   // uniform across the block
         const int64_t nb = base + step;
         const bool more = nb < re;
-        if (more) load_entries<E>(eb, row_index, gh, nb, rb, re);
+        load_entries<E>(eb, row_index, gh, nb, rb, re);   // unconditional, see k_fill_root
         accumulate(ea, da);
+        if (ACC == kPacked && (s + 1) % drain == 0) {
+            __syncthreads();
+            lds_drain(lds, nf, S, plane, lc);
+            __syncthreads();
+        }
         if (!more) break;
         check_entries<E>(eb, n);
         load_data(eb, da);
@@ -580,7 +686,7 @@ __global__ __launch_bounds__(512) void k_fill_rows(const uint8_t* __restrict__ b
         base = nb;
     }
     __syncthreads();
-    lds_flush<ACC>(lds, nf, S, plane, lc,
+    lds_finish<ACC>(lds, nf, S, plane, lc,
                       hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
                       it.atomic_merge != 0);
 }

@@ -374,3 +374,24 @@ def test_error_paths(hgb, torch):
     with pytest.raises(ValueError):
         ctx.build_level(torch.empty(3, dtype=torch.int64, device="cuda"))
     ctx.close()
+
+
+def test_unaligned_gradient_views(hgb, torch):
+    """Gradient tensors that start 4 bytes into an allocation take the scalar path."""
+    say("unaligned gradients")
+    w = synth.random_small(50, 10_003, 3, 64, False, 0)
+    big_g = torch.zeros(w.n_rows + 1, dtype=torch.float32, device="cuda")
+    big_h = torch.zeros(w.n_rows + 1, dtype=torch.float32, device="cuda")
+    big_g[1:] = torch.from_numpy(w.grad).cuda()
+    big_h[1:] = torch.from_numpy(w.hess).cuda()
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    ctx.begin_tree(big_g[1:], big_h[1:])
+    t = torch.empty((1, 3, 64, 2), dtype=torch.int64, device="cuda")
+    ctx.build_level(t)
+    ctx.sync()
+    got = t.cpu().numpy()
+    qg, qh, kg, kh = oracle_quantized(w)
+    assert ctx.get_scales() == (kg, kh)
+    ctx.close()
+    assert np.array_equal(got, oracle.build_hist(w.bins, 64, False, qg, qh))
