@@ -30,9 +30,18 @@ constexpr int kLevelThreads = 1024;
 // levels, with nodes of very different sizes, get several smaller items per
 // CU for balance.
 constexpr int64_t kRootItemsPerCu = 1;
-constexpr int64_t kLevelItemsPerCu = 4;
+// Level fills: blocks per CU, each taking an equal share of the level's rows.
+constexpr int64_t kLevelBlocksPerCu = 1;
+// Fixed cost of one fill item, in rows per cell of its tile: zeroing the tile,
+// the pipeline's ramp and writing the tile out weigh about as much as this
+// many rows.
+constexpr double kPieceRowsPerCell = 0.25;
+// A node split over more blocks than this is merged in several groups, added
+// into its zeroed slot with atomics.
+constexpr int kMergeGroup = 32;
 // Keep a row-major copy of the bins when a row takes at most this many bytes.
 constexpr int64_t kRowMajorMaxRowBytes = 512;
+constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
 // Default fixed-point precision of begin_tree (bits below the largest value).
 constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 4;
@@ -73,6 +82,8 @@ struct hgb_ctx {
     // level scratch
     int2* gh = nullptr;
     int64_t gh_cap = 0;
+    long long* partial = nullptr;   // partial histograms of nodes split over several blocks
+    int64_t partial_cap = 0;
     FeatureBest* best = nullptr;
     int64_t best_cap = 0;
     long long* totals = nullptr;
@@ -89,9 +100,10 @@ struct hgb_ctx {
     bool debug_plan = false;
     // HGB_FILL_TUNE="key=value,..." overrides the fill planner (developer
     // tuning): root_lc, root_tile, root_ipc, level_lc, level_tile, level_ipc
-    // (ipc = items per CU), align (rows an item boundary is a multiple of);
-    // -1 keeps the planner's choice.
-    int tune[7] = {-1, -1, -1, -1, -1, -1, -1};
+    // (ipc = items per CU), align (rows an item boundary is a multiple of),
+    // piece (fixed cost of a level item, in rows); -1 keeps the planner's
+    // choice.
+    int tune[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
     bool prof = false;
@@ -242,8 +254,16 @@ struct FillPlan {
     int threads;
     int64_t step_rows;  // rows a block consumes per step
     int drain;          // packed: steps between drains of the copies (0: wide)
+    int ra;             // rows, packed: register-accumulator cells per thread (0: LDS)
     size_t lds_bytes;
 };
+
+// Row-major level fills with a register accumulator: cells per thread and
+// entries per thread and step.
+constexpr int kRegAccCells = 8;
+constexpr int kRegAccEntries = 2;
+// Entries per thread and step of the wide row-major fill.
+constexpr int kWideRowEntries = 4;
 
 // LDS bytes per feature of a tile: the copies, plus the packed accumulator.
 int64_t feature_lds(int acc, int S, int lc)
@@ -275,8 +295,87 @@ double fill_cost(int acc, int lc, int tile, int w)
     return std::max(lds, mem) + 0.25 * std::min(lds, mem);
 }
 
+// Row-major level fills read scattered rows, and each feature tile of a row
+// fetches that row's whole 128-byte line again; cost per row (seconds) of a
+// plan with n_tiles tiles, from the same LDS rates, ~5 TB/s of scattered line
+// fetches, and the packed drains (lane-contiguous LDS reads and writes).
+double rows_cost(int acc, int lc, int F, int n_tiles, double drain_ops_per_row)
+{
+    static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
+    const double clk = 2.4e9 * 256;
+    const double lds = F * (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * clk) + drain_ops_per_row / (16.0 * clk);
+    const double mem = n_tiles * (128.0 / 5.0e12 + 12.0 / 10.0e12);
+    return std::max(lds, mem) + 0.25 * std::min(lds, mem);
+}
+
+FillPlan plan_rows(const hgb_ctx* c)
+{
+    FillPlan p{};
+    p.kind = kFillRowsKind;
+    p.threads = kLevelThreads;
+    const int S = c->S, w = c->bin_bytes, F = c->F;
+    const int want_acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
+    double best = 1e300;
+    bool found = false;
+    for (int acc : {want_acc, (int)kWide}) {
+        if (found) break;
+        for (int lt = 32; lt >= 2; lt >>= 1) {
+            if (lt < w) continue;
+            const int tile = lt / w;
+            const int force_tile = c->tune[4];
+            if (force_tile > 0 && tile != force_tile) continue;
+            const int nf = std::min(tile, F);
+            const int n_tiles = (F + nf - 1) / nf;
+            for (int lc = 4; lc >= 0; --lc) {
+                const int force_lc = c->tune[3];
+                if (force_lc >= 0 && lc != force_lc) continue;
+                {
+                    // packed sums live in registers, wide sums in LDS
+                    const int ra = acc == kPacked ? kRegAccCells : 0;
+                    if (ra > 0 && nf * S > ra * kLevelThreads) continue;
+                    const int e = ra > 0 ? kRegAccEntries : kWideRowEntries;
+                    const int64_t words = (int64_t)nf * (acc == kWide ? 2 : 1) * (S << lc);
+                    if (words * 8 > kFillLdsBudget) continue;
+                    int drain = 0;
+                    double drain_ops = 0.0;
+                    if (acc == kPacked) {
+                        drain = packed_drain_steps(kLevelThreads, lc, e);
+                        if (drain == 0) continue;
+                        drain_ops = 2.0 * nf * S * (1 << lc) / ((double)kLevelThreads * e * drain) * n_tiles;
+                    }
+                    const double cost = rows_cost(acc, lc, F, n_tiles, drain_ops);
+                    if (cost < best) {
+                        best = cost;
+                        found = true;
+                        p.acc = acc;
+                        p.lc = lc;
+                        p.tile = tile;
+                        p.lt = lt;
+                        p.ra = ra;
+                        p.drain = drain;
+                        p.step_rows = (int64_t)kLevelThreads * e;
+                        p.lds_bytes = (size_t)words * 8;
+                    }
+                }
+            }
+        }
+    }
+    if (!found) {   // one wide feature of one copy always fits (S <= HGB_MAX_SLOTS)
+        p.acc = kWide;
+        p.lc = 0;
+        p.tile = 1;
+        p.lt = w;
+        p.ra = 0;
+        p.drain = 0;
+        p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
+        p.lds_bytes = (size_t)2 * S * 8;
+    }
+    return p;
+}
+
 FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
 {
+    if (!root && rm) return plan_rows(c);
     FillPlan p{};
     const int S = c->S;
     const int w = c->bin_bytes;
@@ -353,16 +452,21 @@ struct FillArgs {
     const int2* gh;
     const int32_t* row_index;
     const FillItem* items;
-    int n_items;
+    int n_items;               // root: one block per item
+    const int32_t* block_first;   // levels: items of block b are [block_first[b], block_first[b + 1])
+    int n_blocks;
     int vec_ok;
     int drain;
     int64_t* hist;
+    int64_t* partial;
 };
 
 template <typename BinT, int ACC>
 hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 {
-    const unsigned grid = (unsigned)(8 * ((a.n_items + 7) / 8));
+    const int n_grid = p.kind == kFillRoot ? a.n_items : a.n_blocks;
+    const unsigned grid = (unsigned)(8 * ((n_grid + 7) / 8));
+    unsigned long long* partial = (unsigned long long*)a.partial;
     unsigned long long* hist = (unsigned long long*)a.hist;
     const BinT* bins = (const BinT*)c->bins;
     hgb_status st = HGB_OK;
@@ -387,19 +491,35 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 #undef HGB_ROOT
     } else if (p.kind == kFillCols) {
         switch (p.tile) {
-        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
+        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
+        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
+        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
         }
     } else {
+        // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-        switch (p.lt) {
-        case 16: HGB_LAUNCH((k_fill_rows<BinT, 16, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        case 8: HGB_LAUNCH((k_fill_rows<BinT, 8, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        case 4: HGB_LAUNCH((k_fill_rows<BinT, 4, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
-        default: HGB_LAUNCH((k_fill_rows<BinT, 2, ACC>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.n_items, a.drain, hist); break;
+#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial)
+        if constexpr (ACC == kPacked) {
+            if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            switch (p.lt) {
+            case 32: HGB_ROWS(32, kRegAccCells, kRegAccEntries); break;
+            case 16: HGB_ROWS(16, kRegAccCells, kRegAccEntries); break;
+            case 8: HGB_ROWS(8, kRegAccCells, kRegAccEntries); break;
+            case 4: HGB_ROWS(4, kRegAccCells, kRegAccEntries); break;
+            default: HGB_ROWS(2, kRegAccCells, kRegAccEntries); break;
+            }
+        } else {
+            if (p.ra != 0) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            switch (p.lt) {
+            case 32: HGB_ROWS(32, 0, kWideRowEntries); break;
+            case 16: HGB_ROWS(16, 0, kWideRowEntries); break;
+            case 8: HGB_ROWS(8, 0, kWideRowEntries); break;
+            case 4: HGB_ROWS(4, 0, kWideRowEntries); break;
+            default: HGB_ROWS(2, 0, kWideRowEntries); break;
+            }
         }
+#undef HGB_ROWS
     }
 #undef HGB_LAUNCH
     HGB_LAUNCHED(c, "fill");
@@ -413,6 +533,222 @@ hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
                                 : launch_fill_acc<uint8_t, kWide>(c, p, a);
     return p.acc == kPacked ? launch_fill_acc<uint16_t, kPacked>(c, p, a)
                             : launch_fill_acc<uint16_t, kWide>(c, p, a);
+}
+
+// Zero whole node slots of the level buffer.
+hgb_status zero_node_slices(hgb_ctx* c, int64_t* hist, const int32_t* slots, size_t n_slots)
+{
+    if (n_slots == 0) return HGB_OK;
+    Stage* s = nullptr;
+    hgb_status st = stage_upload(c, slots, n_slots * sizeof(int32_t), &s);
+    if (st != HGB_OK) return st;
+    const int64_t node_elems = (int64_t)c->F * c->S * 2;
+    dim3 grid(grid_for(node_elems, 256, 1024), (unsigned)n_slots);
+    {
+        ProfScope ps(c, HGB_KERNEL_ZERO);
+        k_zero_slices<<<grid, 256, 0, c->stream>>>(hist, (const int32_t*)s->dev, node_elems);
+    }
+    HGB_LAUNCHED(c, "k_zero_slices");
+    return stage_release(c, s);
+}
+
+// Fill of a level below the root.  The level order is cut into equal shares
+// of rows, one per block (kLevelBlocksPerCu per CU, divided among the feature
+// tiles), so every CU gets the same work whatever the node sizes.  A share
+// crosses node boundaries: its block takes one item per node it touches, in
+// order.  A node that lies inside one share is stored straight into its slot;
+// a node split over several shares leaves one partial histogram per share,
+// and a merge kernel sums them into the slot (coalesced, no contended
+// atomics).
+hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::pair<int, int>>& tiles,
+                      const int32_t* row_index, const std::vector<int64_t>& begin,
+                      const std::vector<int64_t>& count, const std::vector<int32_t>& slots,
+                      int64_t total, int64_t* hist)
+{
+    const int n_nodes = (int)begin.size();
+    const int n_tiles = (int)tiles.size();
+    const int64_t node_elems = (int64_t)c->F * c->S * 2;
+    int64_t bpc = kLevelBlocksPerCu;
+    if (c->tune[5] > 0) bpc = c->tune[5];
+    const int64_t shares = std::max<int64_t>(1, bpc * c->n_cu / n_tiles);
+    int64_t align = 128;
+    if (c->tune[6] > 0) align = (c->tune[6] + 7) / 8 * 8;
+    // Balance shares by cost, not rows: a piece costs its rows plus a fixed
+    // kPieceRows (zeroing the tile, the pipeline's ramp, writing the tile
+    // out), so a share that touches many small nodes takes fewer rows.
+    int64_t piece_rows = std::max<int64_t>((int64_t)(kPieceRowsPerCell * std::min(plan.tile, c->F) * c->S), 1);
+    if (c->tune[7] >= 0) piece_rows = std::max(c->tune[7], 1);
+    int64_t nonempty = 0;
+    for (int i = 0; i < n_nodes; ++i) nonempty += count[i] > 0;
+    int64_t budget = 0;
+
+    // pieces of each share, in level order: (node, begin, end, chunk of node)
+    struct Piece {
+        int node;
+        int64_t rb, re;
+        int chunk;
+    };
+    std::vector<Piece> pieces;
+    std::vector<int64_t> share_first;
+    std::vector<int> pieces_of;
+    auto cut = [&]() {
+        pieces.clear();
+        share_first.assign(1, 0);
+        pieces_of.assign(n_nodes, 0);
+        int64_t left = budget;   // cost left in the current share
+        bool open = false;       // the current share holds a piece
+        for (int i = 0; i < n_nodes; ++i) {
+            int64_t at = begin[i];
+            const int64_t end = begin[i] + count[i];
+            while (at < end) {
+                if (open && left < piece_rows + align) {   // close the share
+                    share_first.push_back((int64_t)pieces.size());
+                    left = budget;
+                    open = false;
+                }
+                int64_t take = std::min(end - at, left - piece_rows);
+                // inside a node, cut on multiples of `align` rows
+                if (at + take < end) take = std::max<int64_t>(take / align * align, align);
+                take = std::min(take, end - at);
+                pieces.push_back({i, at, at + take, pieces_of[i]++});
+                left -= piece_rows + take;
+                open = true;
+                at += take;
+            }
+        }
+        if (open) share_first.push_back((int64_t)pieces.size());
+        return (int64_t)share_first.size() - 1;
+    };
+    // The smallest budget whose cut fits one round of blocks (binary search;
+    // a larger budget never needs more shares).
+    {
+        int64_t lo = std::max<int64_t>((total + piece_rows * nonempty + shares - 1) / shares,
+                                       piece_rows + align);
+        int64_t hi = std::max<int64_t>(total + piece_rows * (nonempty + 1) + align, lo);
+        while (lo < hi) {
+            budget = lo + (hi - lo) / 2;
+            if (cut() <= shares) hi = budget;
+            else lo = budget + 1;
+        }
+        budget = lo;
+    }
+    const int64_t n_shares = cut();
+    const int64_t len = budget;
+
+    // partial slots and merges of split nodes; slots to zero first
+    std::vector<int32_t> partial_base(n_nodes, -1);
+    std::vector<MergeEntry> merges;
+    std::vector<int32_t> zero_slots;
+    int64_t n_partial = 0;
+    for (int i = 0; i < n_nodes; ++i) {
+        if (count[i] == 0) zero_slots.push_back(slots[i]);
+        if (pieces_of[i] <= 1) continue;
+        partial_base[i] = (int32_t)n_partial;
+        const int groups = (pieces_of[i] + kMergeGroup - 1) / kMergeGroup;
+        if (groups > 1) zero_slots.push_back(slots[i]);
+        for (int g = 0; g < groups; ++g) {
+            MergeEntry m{};
+            m.out_slot = slots[i];
+            m.first = (int32_t)(n_partial + (int64_t)g * kMergeGroup);
+            m.count = std::min(kMergeGroup, pieces_of[i] - g * kMergeGroup);
+            m.atomic = groups > 1 ? 1 : 0;
+            merges.push_back(m);
+        }
+        n_partial += pieces_of[i];
+    }
+    if (n_partial > INT32_MAX / 2 || (int64_t)merges.size() > 65535)
+        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many partial histograms");
+
+    // blocks (share, tile), tile fastest: the tiles of one share read the same
+    // rows, and the kernel gives each XCD a contiguous run of blocks
+    std::vector<FillItem> items;
+    std::vector<int32_t> block_first;
+    items.reserve(pieces.size() * (size_t)n_tiles);
+    block_first.reserve((size_t)n_shares * n_tiles + 1);
+    for (int64_t r = 0; r < n_shares; ++r)
+        for (int t = 0; t < n_tiles; ++t) {
+            block_first.push_back((int32_t)items.size());
+            for (int64_t k = share_first[r]; k < share_first[r + 1]; ++k) {
+                const Piece& pc = pieces[k];
+                FillItem it{};
+                if (partial_base[pc.node] >= 0) {
+                    it.out_slot = partial_base[pc.node] + pc.chunk;
+                    it.dest = kDestPartial;
+                } else {
+                    it.out_slot = slots[pc.node];
+                    it.dest = kDestStore;
+                }
+                it.row_begin = (int32_t)pc.rb;
+                it.row_end = (int32_t)pc.re;
+                it.f0_nf = tiles[t].first | (tiles[t].second << 16);
+                items.push_back(it);
+            }
+        }
+    block_first.push_back((int32_t)items.size());
+    const int n_blocks = (int)(block_first.size() - 1);
+    if (items.size() > (size_t)INT32_MAX / 8 || n_blocks > INT32_MAX / 8)
+        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many fill items");
+    if (c->debug_plan)
+        std::fprintf(stderr,
+                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d drain %d chunk %lld items %zu "
+                     "lds %zu blocks %d partials %lld merges %zu\n",
+                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.drain,
+                     (long long)len, items.size(), plan.lds_bytes, n_blocks, (long long)n_partial,
+                     merges.size());
+
+    hgb_status st = HGB_OK;
+    if (n_partial > 0) {
+        st = grow(c, &c->partial, &c->partial_cap, n_partial * node_elems);
+        if (st != HGB_OK) return st;
+    }
+    if (total > 0) {
+        st = grow(c, &c->gh, &c->gh_cap, total);
+        if (st != HGB_OK) return st;
+        ProfScope ps(c, HGB_KERNEL_GATHER);
+        k_gather<<<grid_for(total, 256, 8192), 256, 0, c->stream>>>(c->q, row_index, total, c->n, c->gh,
+                                                                    c->dev_words + 2);
+        HGB_LAUNCHED(c, "k_gather");
+    }
+    st = zero_node_slices(c, hist, zero_slots.data(), zero_slots.size());
+    if (st != HGB_OK) return st;
+    if (items.empty()) return HGB_OK;
+
+    // one upload: items, block list, merges (each part 256-byte aligned)
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t off_blocks = up(items.size() * sizeof(FillItem));
+    const size_t off_merges = off_blocks + up(block_first.size() * sizeof(int32_t));
+    const size_t bytes = off_merges + merges.size() * sizeof(MergeEntry);
+    std::vector<uint8_t> blob(bytes, 0);
+    std::memcpy(blob.data(), items.data(), items.size() * sizeof(FillItem));
+    std::memcpy(blob.data() + off_blocks, block_first.data(), block_first.size() * sizeof(int32_t));
+    if (!merges.empty())
+        std::memcpy(blob.data() + off_merges, merges.data(), merges.size() * sizeof(MergeEntry));
+    Stage* sg = nullptr;
+    st = stage_upload(c, blob.data(), bytes, &sg);
+    if (st != HGB_OK) return st;
+    const uint8_t* dev = (const uint8_t*)sg->dev;
+    {
+        FillArgs a{};
+        a.gh = c->gh;
+        a.row_index = row_index;
+        a.items = (const FillItem*)dev;
+        a.block_first = (const int32_t*)(dev + off_blocks);
+        a.n_blocks = n_blocks;
+        a.drain = std::max(plan.drain, 1);
+        a.hist = hist;
+        a.partial = (int64_t*)c->partial;
+        ProfScope ps(c, HGB_KERNEL_FILL);
+        st = launch_fill(c, plan, a);
+        if (st != HGB_OK) return st;
+        if (!merges.empty()) {
+            const int64_t node_vec = (int64_t)c->F * c->S;
+            dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
+            k_merge<<<grid, 256, 0, c->stream>>>((const longlong2*)c->partial, (longlong2*)hist,
+                                                 (const MergeEntry*)(dev + off_merges), node_vec);
+            HGB_LAUNCHED(c, "k_merge");
+        }
+    }
+    return stage_release(c, sg);
 }
 
 }  // namespace
@@ -438,7 +774,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     c->device = device;
     if (const char* e = std::getenv("HGB_DEBUG_PLAN")) c->debug_plan = e[0] == '1';
     if (const char* e = std::getenv("HGB_FILL_TUNE")) {
-        static const char* keys[7] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align"};
+        static const char* keys[8] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align", "piece"};
         std::string spec(e);
         size_t pos = 0;
         while (pos < spec.size()) {
@@ -447,7 +783,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
             const std::string kv = spec.substr(pos, end - pos);
             const size_t eq = kv.find('=');
             if (eq != std::string::npos)
-                for (int k = 0; k < 7; ++k)
+                for (int k = 0; k < 8; ++k)
                     if (kv.compare(0, eq, keys[k]) == 0) c->tune[k] = std::atoi(kv.c_str() + eq + 1);
             pos = end + 1;
         }
@@ -487,6 +823,7 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipFree(c->bins_rm);
     (void)hipFree(c->q);
     (void)hipFree(c->gh);
+    (void)hipFree(c->partial);
     (void)hipFree(c->best);
     (void)hipFree(c->totals);
     (void)hipFree(c->dev_words);
@@ -569,8 +906,10 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
                     c->host_words[0], S);
     if ((int64_t)n_features * bin_bytes <= kRowMajorMaxRowBytes) {
         const int64_t stride = ((int64_t)n_features * bin_bytes + 15) / 16 * 16;
-        HGB_HIP(c, hipMalloc(&c->bins_rm, (size_t)(stride * n_rows)));
-        HGB_HIP(c, hipMemsetAsync(c->bins_rm, 0, (size_t)(stride * n_rows), c->stream));
+        // kRowMajorSlack bytes after the last row: a tile's load may run past
+        // the end of a row, into the next row or this slack
+        HGB_HIP(c, hipMalloc(&c->bins_rm, (size_t)(stride * n_rows + kRowMajorSlack)));
+        HGB_HIP(c, hipMemsetAsync(c->bins_rm, 0, (size_t)(stride * n_rows + kRowMajorSlack), c->stream));
         c->rm_stride = stride;
         dim3 tgrid((unsigned)((n_rows + 63) / 64), (unsigned)((n_features + 63) / 64));
         if (bin_bytes == 1)
@@ -709,7 +1048,6 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     // from the row-major copy when there is one.
     const bool rm = !root && c->bins_rm != nullptr;
     const FillPlan plan0 = plan_fill(c, root, rm);
-    const int64_t node_elems = (int64_t)c->F * c->S * 2;
 
     // Feature tiles (f0, width).  Root tiles have exactly the kernel's width:
     // full tiles of plan.tile, then the remainder split into powers of two,
@@ -745,104 +1083,62 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         if (t.second < 1 || (root && t.second > 8) || t.first + t.second > c->F)
             return fail(c, HGB_E_DEVICE, "build_level: internal error in the tile plan");
 
-    // Rows per item: about (items per CU) x (CUs) items of equal size over the
-    // level, a multiple of 8 rows (the root's vector groups).
-    int64_t ipc = root ? kRootItemsPerCu : kLevelItemsPerCu;
-    if (c->tune[root ? 2 : 5] > 0) ipc = c->tune[root ? 2 : 5];
+    if (!root) return fill_level(c, plan, tiles, row_index, begin, count, slots, total, hist);
+
+    // Root items: about (items per CU) x (CUs) items of equal size, a multiple
+    // of 128 rows, which keeps the bin and (g, h) loads cache-line aligned.
+    int64_t ipc = kRootItemsPerCu;
+    if (c->tune[2] > 0) ipc = c->tune[2];
     const int64_t target = ipc * c->n_cu;
-    // Item boundaries on 128-row multiples keep the root's bin and (g, h)
-    // loads cache-line aligned.
     int64_t align = 128;
     if (c->tune[6] > 0) align = (c->tune[6] + 7) / 8 * 8;
-    int64_t ch = (total * n_tiles + target - 1) / target;
+    // Equal items, at most `target` of them: one item more than a multiple of
+    // the resident blocks would cost a whole extra round.
+    const int64_t chunks = std::max<int64_t>(1, target / n_tiles);
+    int64_t ch = (total + chunks - 1) / chunks;
     ch = std::max<int64_t>((ch + align - 1) / align * align, align);
+    const int64_t nchunks = (total + ch - 1) / ch;
 
-    // Item order decides which items share an L2 (the kernel gives each XCD a
-    // contiguous run).  Root and row-major levels: (node, chunk, tile) -- the
-    // tiles of one row chunk read the same rows.  Feature-major levels:
-    // (tile, chunk, node) -- the nodes of one tile read the same columns.
-    // groups[w]: the items of root tiles of width w (one launch each; root
-    // widths are 1, 2, 4 or 8).  Level items all go to groups[0].
+    // Item order (chunk, tile): the tiles of one row chunk read the same
+    // (g, h) rows, and the kernel gives each XCD a contiguous run of items.
+    // groups[w]: the items of tiles of width w, one launch each.
     std::vector<FillItem> groups[9];
-    std::vector<int32_t> zero_slots;
-    std::vector<int64_t> nchunks(n_nodes);
-    int64_t max_ch = 0;
-    for (int i = 0; i < n_nodes; ++i) {
-        nchunks[i] = (count[i] + ch - 1) / ch;
-        max_ch = std::max(max_ch, nchunks[i]);
-        if (count[i] == 0 || nchunks[i] > 1) zero_slots.push_back(slots[i]);
-    }
     size_t n_items = 0;
-    auto push = [&](int i, int64_t j, int t) {
-        FillItem it{};
-        it.out_slot = slots[i];
-        it.row_begin = (int32_t)(begin[i] + j * ch);
-        it.row_end = (int32_t)std::min<int64_t>(begin[i] + (j + 1) * ch, begin[i] + count[i]);
-        it.f0_nf = tiles[t].first | (tiles[t].second << 16);
-        it.atomic_merge = nchunks[i] > 1 ? 1 : 0;
-        groups[root ? tiles[t].second : 0].push_back(it);
-        ++n_items;
-    };
-    if (plan.kind != kFillCols) {
-        for (int i = 0; i < n_nodes; ++i)
-            for (int64_t j = 0; j < nchunks[i]; ++j)
-                for (int t = 0; t < n_tiles; ++t) push(i, j, t);
-    } else {
-        for (int t = 0; t < n_tiles; ++t)
-            for (int64_t j = 0; j < max_ch; ++j)
-                for (int i = 0; i < n_nodes; ++i)
-                    if (j < nchunks[i]) push(i, j, t);
-    }
-    if (n_items > (size_t)INT32_MAX / 8)
-        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many fill items");
+    for (int64_t j = 0; j < nchunks; ++j)
+        for (int t = 0; t < n_tiles; ++t) {
+            FillItem it{};
+            it.out_slot = slots[0];
+            it.row_begin = (int32_t)(j * ch);
+            it.row_end = (int32_t)std::min<int64_t>((j + 1) * ch, total);
+            it.f0_nf = tiles[t].first | (tiles[t].second << 16);
+            it.dest = nchunks > 1 ? kDestAtomic : kDestStore;
+            groups[tiles[t].second].push_back(it);
+            ++n_items;
+        }
     if (c->debug_plan)
         std::fprintf(stderr,
-                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d drain %d chunk %lld items %zu lds %zu\n",
-                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.drain, (long long)ch,
+                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d drain %d chunk %lld items %zu lds %zu\n",
+                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.drain, (long long)ch,
                      n_items, plan.lds_bytes);
-    const int2* gh = c->q;
-    if (!root) {
-        hgb_status st = grow(c, &c->gh, &c->gh_cap, std::max<int64_t>(total, 1));
-        if (st != HGB_OK) return st;
-        if (total > 0) {
-            ProfScope ps(c, HGB_KERNEL_GATHER);
-            k_gather<<<grid_for(total, 256, 8192), 256, 0, c->stream>>>(c->q, row_index, total, c->n,
-                                                                        c->gh, c->dev_words + 2);
-            HGB_LAUNCHED(c, "k_gather");
-        }
-        gh = c->gh;
-    }
-    if (!zero_slots.empty()) {
-        Stage* s = nullptr;
-        hgb_status st = stage_upload(c, zero_slots.data(), zero_slots.size() * sizeof(int32_t), &s);
-        if (st != HGB_OK) return st;
-        dim3 grid(grid_for(node_elems, 256, 1024), (unsigned)zero_slots.size());
-        {
-            ProfScope ps(c, HGB_KERNEL_ZERO);
-            k_zero_slices<<<grid, 256, 0, c->stream>>>(hist, (const int32_t*)s->dev, node_elems);
-        }
-        HGB_LAUNCHED(c, "k_zero_slices");
-        st = stage_release(c, s);
+    if (nchunks > 1) {
+        hgb_status st = zero_node_slices(c, hist, slots.data(), 1);
         if (st != HGB_OK) return st;
     }
-    for (int wdt = 8; wdt >= 0; --wdt) {
+    for (int wdt = 8; wdt >= 1; --wdt) {
         std::vector<FillItem>& items = groups[wdt];
         if (items.empty()) continue;
         Stage* s = nullptr;
         hgb_status st = stage_upload(c, items.data(), items.size() * sizeof(FillItem), &s);
         if (st != HGB_OK) return st;
         FillPlan gp = plan;
-        if (root && wdt > 0) {
-            gp.tile = wdt;
-            gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc));
-        }
-        FillArgs a;
-        a.gh = gh;
-        a.row_index = row_index;
+        gp.tile = wdt;
+        gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc));
+        FillArgs a{};
+        a.gh = c->q;
         a.items = (const FillItem*)s->dev;
         a.n_items = (int)items.size();
-        // 8-row vector loads of the root need rows aligned to 8 (chunk starts
-        // are multiples of 8)
+        // 8-row vector loads need rows aligned to 8 (chunk starts are
+        // multiples of 128)
         a.vec_ok = (c->n % 8 == 0) ? 1 : 0;
         a.drain = std::max(plan.drain, 1);
         a.hist = hist;

@@ -166,15 +166,54 @@ __global__ __launch_bounds__(256) void k_gather(const int2* __restrict__ q,
 }
 
 // One unit of fill work: rows [row_begin, row_end) of the level order, features
-// [f0, f0 + nf), accumulated for the node whose histogram lands at out_slot.
+// [f0, f0 + nf), accumulated for one node.  `dest` says where the sums go:
+// stored into slot out_slot of the level buffer (kDestStore), stored into
+// slot out_slot of the partial buffer (kDestPartial: a node split over several
+// items, merged afterwards), or added there with int64 atomics (kDestAtomic).
+enum { kDestStore = 0, kDestPartial = 1, kDestAtomic = 2 };
 struct FillItem {
     int32_t out_slot;
     int32_t row_begin;
     int32_t row_end;
     int32_t f0_nf;       // f0 | (nf << 16)
-    int32_t atomic_merge;
+    int32_t dest;
     int32_t pad[3];
 };
+
+// Merge of a node split over several items: the sum of `count` partial slots
+// from `first` on, stored into (or, for a node merged in several groups,
+// added with atomics to) slot out_slot of the level buffer.
+struct MergeEntry {
+    int32_t out_slot;
+    int32_t first;
+    int32_t count;
+    int32_t atomic;
+};
+
+__global__ __launch_bounds__(256) void k_merge(const longlong2* __restrict__ partial,
+                                               longlong2* __restrict__ hist,
+                                               const MergeEntry* __restrict__ plan, int64_t node_vec)
+{
+    const MergeEntry m = plan[blockIdx.y];
+    const longlong2* src = partial + (int64_t)m.first * node_vec;
+    longlong2* dst = hist + (int64_t)m.out_slot * node_vec;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < node_vec; e += stride) {
+        long long g = 0, h = 0;
+#pragma unroll 8
+        for (int j = 0; j < m.count; ++j) {
+            const longlong2 v = src[(int64_t)j * node_vec + e];
+            g += v.x;
+            h += v.y;
+        }
+        if (m.atomic) {
+            atomicAdd((unsigned long long*)&dst[e].x, (unsigned long long)g);
+            atomicAdd((unsigned long long*)&dst[e].y, (unsigned long long)h);
+        } else {
+            dst[e] = make_longlong2(g, h);
+        }
+    }
+}
 
 // Zero whole node slices of the level buffer (nodes merged with atomics, and
 // empty nodes).  grid.y = slice, grid.x strides over the slice's elements.
@@ -248,6 +287,18 @@ __device__ inline void lds_add(unsigned long long* lcopy, int plane, int lc, int
     unsigned long long* p = lcopy + f * (ACC == kWide ? 2 : 1) * plane + (b << lc);
     atomicAdd(p, v.a);
     if (ACC == kWide) atomicAdd(p + plane, v.b);
+}
+
+// The same add, addressed as feature base + (bin * C | copy): the per-lane copy
+// joins the bin's offset instead of a per-lane base pointer, so an unrolled
+// feature loop keeps one uniform base per feature rather than one per lane.
+template <int ACC>
+__device__ inline void lds_add_at(unsigned long long* lds, int cpy, int plane, int lc, int f, int b,
+                                  CellVal v)
+{
+    const int idx = f * (ACC == kWide ? 2 : 1) * plane + ((b << lc) | cpy);
+    atomicAdd(lds + idx, v.a);
+    if (ACC == kWide) atomicAdd(lds + idx + plane, v.b);
 }
 
 // Zero the block's LDS tile: nf * planes * S * C words.
@@ -462,7 +513,7 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     __syncthreads();
     lds_finish<ACC>(lds, NF, S, plane, lc,
                     hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                    it.atomic_merge != 0);
+                    it.dest == kDestAtomic);
 }
 
 // Level fills read their rows through the row index.  Each thread takes
@@ -510,17 +561,13 @@ __device__ inline void check_entries(Entries<E>& en, int64_t n)
 // Feature-major level fill (wide matrices): NF features per block, each bin a
 // scattered one-element load.
 template <typename BinT, int NF, int ACC>
-__global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
-                                                   int n_features, int S, int lc,
-                                                   const int2* __restrict__ gh,
-                                                   const int32_t* __restrict__ row_index,
-                                                   const FillItem* __restrict__ items, int n_items,
-                                                   int drain, unsigned long long* __restrict__ hist)
+__device__ inline void fill_cols_item(unsigned long long* lds, const FillItem& it,
+                                      const BinT* __restrict__ bins, int64_t n, int n_features,
+                                      int S, int lc, const int2* __restrict__ gh,
+                                      const int32_t* __restrict__ row_index, int drain,
+                                      unsigned long long* __restrict__ hist,
+                                      unsigned long long* __restrict__ partial)
 {
-    extern __shared__ unsigned long long lds[];
-    const int item = xcd_item(blockIdx.x, n_items);
-    if (item >= n_items) return;
-    const FillItem it = items[item];
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= NF
     const int plane = S << lc;
@@ -528,6 +575,7 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
     __syncthreads();
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
+    const int idle_bin = (int)((threadIdx.x >> lc) % (unsigned)S);
     const BinT* const col0 = bins + (int64_t)f0 * n;
     const int64_t rb = it.row_begin, re = it.row_end;
     constexpr int E = cols_entries(NF);
@@ -545,11 +593,12 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
     auto accumulate = [&](const Entries<E>& en, const Data& d) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            if (!en.ok[e]) continue;   // idle lanes must not pile onto one address
-            const CellVal v = cell_val<ACC>(en.g[e].x, en.g[e].y);
+            // branch-free, as in the row-major fill
+            const bool ok = en.ok[e];
+            const CellVal v = cell_val<ACC>(ok ? en.g[e].x : 0, ok ? en.g[e].y : 0);
 #pragma unroll
             for (int f = 0; f < NF; ++f)
-                if (f < nf) lds_add<ACC>(lcopy, plane, lc, f, d.b[f][e], v);
+                if (f < nf) lds_add<ACC>(lcopy, plane, lc, f, ok ? d.b[f][e] : idle_bin, v);
         }
     };
 
@@ -577,8 +626,34 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
     }
     __syncthreads();
     lds_finish<ACC>(lds, nf, S, plane, lc,
-                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                      it.atomic_merge != 0);
+                    (it.dest == kDestPartial ? partial : hist) +
+                        ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                    it.dest == kDestAtomic);
+}
+
+
+// Level fills run one block per CU-sized share of the level: block b takes
+// the items [block_first[b], block_first[b + 1]) in turn -- consecutive pieces
+// of the level order, one per node that the share touches.
+template <typename BinT, int NF, int ACC>
+__global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
+                                                   int n_features, int S, int lc,
+                                                   const int2* __restrict__ gh,
+                                                   const int32_t* __restrict__ row_index,
+                                                   const FillItem* __restrict__ items,
+                                                   const int32_t* __restrict__ block_first, int n_blocks,
+                                                   int drain, unsigned long long* __restrict__ hist,
+                                                   unsigned long long* __restrict__ partial)
+{
+    extern __shared__ unsigned long long lds[];
+    const int blk = xcd_item(blockIdx.x, n_blocks);
+    if (blk >= n_blocks) return;
+    const int i1 = block_first[blk + 1];
+    for (int ii = block_first[blk]; ii < i1; ++ii) {
+        fill_cols_item<BinT, NF, ACC>(lds, items[ii], bins, n, n_features, S, lc, gh, row_index,
+                                      drain, hist, partial);
+        __syncthreads();
+    }
 }
 
 // Row-major level fill (narrow matrices).  The resident row-major copy pads
@@ -588,6 +663,21 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
 // its feature tile (LT / sizeof(BinT) features), read with one load per row.
 template <int LT>
 struct Chunk;
+template <>
+struct Chunk<32> {
+    uint4 w0, w1;
+    __device__ inline void load(const uint8_t* p)
+    {
+        w0 = *(const uint4*)p;
+        w1 = *(const uint4*)(p + 16);
+    }
+    __device__ inline uint32_t word(int i) const
+    {
+        const uint4& w = i < 4 ? w0 : w1;
+        const int j = i & 3;
+        return j == 0 ? w.x : (j == 1 ? w.y : (j == 2 ? w.z : w.w));
+    }
+};
 template <>
 struct Chunk<16> {
     uint4 w;
@@ -613,82 +703,201 @@ struct Chunk<2> {
     __device__ inline uint32_t word(int) const { return w; }
 };
 
-template <typename BinT, int LT, int ACC>
-__global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
-                                                   int64_t row_stride, int64_t n, int n_features,
-                                                   int S, int lc, const int2* __restrict__ gh,
-                                                   const int32_t* __restrict__ row_index,
-                                                   const FillItem* __restrict__ items, int n_items,
-                                                   int drain, unsigned long long* __restrict__ hist)
+// Packed sums with the int64 accumulator in registers instead of LDS: thread t
+// owns the cells t + k * blockDim.x, k < RA, of the tile.  The whole LDS then
+// holds copies, so one block covers a whole narrow row (every feature of a
+// row-major line) and each row's line is fetched once per level.
+template <int RA>
+struct RegAcc {
+    long long g[RA], h[RA];
+};
+
+template <int RA>
+__device__ inline void reg_drain(unsigned long long* lds, int cells, int S, int plane, int lc,
+                                 RegAcc<RA>& a)
 {
-    extern __shared__ unsigned long long lds[];
-    const int item = xcd_item(blockIdx.x, n_items);
-    if (item >= n_items) return;
-    const FillItem it = items[item];
+    const int C = 1 << lc;
+#pragma unroll
+    for (int k = 0; k < RA; ++k) {
+        const int i = threadIdx.x + k * blockDim.x;
+        if (i < cells) {
+            const int f = i / S;
+            const int sl = i - f * S;
+            unsigned long long* pg = lds + f * plane + (sl << lc);
+            for (int c = 0; c < C; ++c) {
+                const long long v = (long long)pg[c];
+                const long long lo = (long long)(int)(unsigned)(v & 0xffffffffll);
+                a.g[k] += lo;
+                a.h[k] += (v - lo) >> 32;
+                pg[c] = 0ull;
+            }
+        }
+    }
+}
+
+template <int RA>
+__device__ inline void reg_finish(const RegAcc<RA>& a, int cells, unsigned long long* out,
+                                  bool atomic_merge)
+{
+#pragma unroll
+    for (int k = 0; k < RA; ++k) {
+        const int i = threadIdx.x + k * blockDim.x;
+        if (i < cells) {
+            if (atomic_merge) {
+                if (a.g[k]) atomicAdd(&out[2 * i], (unsigned long long)a.g[k]);
+                if (a.h[k]) atomicAdd(&out[2 * i + 1], (unsigned long long)a.h[k]);
+            } else {
+                out[2 * i] = (unsigned long long)a.g[k];
+                out[2 * i + 1] = (unsigned long long)a.h[k];
+            }
+        }
+    }
+}
+
+// RA > 0 (packed only): register accumulator of RA cells per thread; E
+// entries per thread and step.
+template <typename BinT, int LT, int ACC, int RA, int E>
+__device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
+                                      const uint8_t* __restrict__ bins_rm, int64_t row_stride,
+                                      int64_t n, int n_features, int S, int lc,
+                                      const int2* __restrict__ gh,
+                                      const int32_t* __restrict__ row_index, int drain,
+                                      unsigned long long* __restrict__ hist,
+                                      unsigned long long* __restrict__ partial)
+{
+    static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= LT / sizeof(BinT)
     constexpr int TF = LT / (int)sizeof(BinT);
     const int plane = S << lc;
-    lds_zero(lds, tile_words(ACC, nf, S, lc));
+    const int cells = nf * S;
+    lds_zero(lds, nf * (ACC == kWide ? 2 : 1) * plane);
     __syncthreads();
+    RegAcc<(RA > 0 ? RA : 1)> racc;
+#pragma unroll
+    for (int k = 0; k < (RA > 0 ? RA : 1); ++k) racc.g[k] = racc.h[k] = 0;
 
-    unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
+    const int cpy = threadIdx.x & ((1 << lc) - 1);
     const uint8_t* const tile = bins_rm + (int64_t)f0 * sizeof(BinT);
     const int64_t rb = it.row_begin, re = it.row_end;
-    constexpr int E = kLevelEntries;
     const int64_t step = (int64_t)blockDim.x * E;
 
+    // Per step: the row chunks and (g, h) pairs of E entries per thread, the
+    // entries strided by the block size (index and (g, h) loads coalesced).
     struct Data {
         Chunk<LT> c[E];
+        int2 g[E];
+        bool ok[E];
     };
-    auto load_data = [&](const Entries<E>& en, Data& d) {
+    // Row indices of a step: loaded one step ahead of its rows.
+    struct Index {
+        int32_t r[E];
+        bool in[E];   // inside the item
+    };
+    auto load_index = [&](int64_t s, Index& x) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            d.c[e].load(tile + (int64_t)en.r[e] * row_stride);
+            const int64_t kk = rb + s * step + (int64_t)e * blockDim.x + threadIdx.x;
+            x.in[e] = kk < re;
+            x.r[e] = row_index[x.in[e] ? kk : rb];   // past the end: a valid address, masked
         }
     };
-    auto accumulate = [&](const Entries<E>& en, const Data& d) {
+    auto load_rows = [&](int64_t s, const Index& x, Data& d) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            if (!en.ok[e]) continue;   // idle lanes must not pile onto one address
-            const CellVal v = cell_val<ACC>(en.g[e].x, en.g[e].y);
+            const int64_t kk = rb + s * step + (int64_t)e * blockDim.x + threadIdx.x;
+            d.ok[e] = x.in[e] && (uint32_t)x.r[e] < (uint64_t)n;
+            d.c[e].load(tile + (int64_t)(d.ok[e] ? x.r[e] : 0) * row_stride);
+            d.g[e] = gh[x.in[e] ? kk : rb];
+        }
+    };
+    // Idle entries and features past the tile's nf are skipped.  (The loads
+    // that a step's adds use were issued a whole step earlier, ahead of the
+    // previous adds, so the compiler cannot sink them into these branches.)
+    auto accumulate = [&](const Data& d) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (!d.ok[e]) continue;
+            const CellVal v = cell_val<ACC>(d.g[e].x, d.g[e].y);
+            // The feature's base offset is stepped here rather than hoisted:
+            // 32 hoisted values would not fit the scalar registers.
+            int fb = 0;
 #pragma unroll
             for (int f = 0; f < TF; ++f) {
                 if (f >= nf) break;
                 const uint32_t w = d.c[e].word((f * (int)sizeof(BinT)) >> 2);
                 const int b = sizeof(BinT) == 1 ? (int)((w >> (8 * (f & 3))) & 0xffu)
                                                 : (int)((w >> (16 * (f & 1))) & 0xffffu);
-                lds_add<ACC>(lcopy, plane, lc, f, b, v);
+                lds_add_at<ACC>(lds + fb, cpy, plane, lc, 0, b, v);
+                fb += (ACC == kWide ? 2 : 1) * plane;
+                asm volatile("" : "+s"(fb));
             }
         }
     };
 
-    Entries<E> ea, eb;
-    Data da;
-    int64_t base = rb;
-    load_entries<E>(ea, row_index, gh, base, rb, re);
-    check_entries<E>(ea, n);
-    load_data(ea, da);
-    for (int64_t s = 0;; ++s) {   // uniform across the block
-        const int64_t nb = base + step;
-        const bool more = nb < re;
-        load_entries<E>(eb, row_index, gh, nb, rb, re);   // unconditional, see k_fill_root
-        accumulate(ea, da);
+    // Pipeline: step s waits for what step s - 1 issued (its own rows and
+    // (g, h), and the indices of s + 1), issues the rows of s + 1 and the
+    // indices of s + 2, then adds.  The memory counter retires in issue
+    // order, and that one wait is all a step needs: every load it covers had
+    // a whole step of adds to land.  Two data buffers alternate (the loop is
+    // unrolled by two), so no register copy waits on a load in flight; the
+    // index buffer is consumed before it is reloaded.  Loads past the item
+    // are clamped to valid addresses and masked (unconditional, see
+    // k_fill_root).
+    const int64_t n_steps = (re - rb + step - 1) / step;
+    Index x;
+    Data d0, d1;
+    load_index(0, x);
+    load_rows(0, x, d0);
+    load_index(1, x);
+    auto run_step = [&](int64_t s, Data& cur, Data& next) {
+        load_rows(s + 1, x, next);
+        __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+        load_index(s + 2, x);
+        __builtin_amdgcn_sched_barrier(0);
+        accumulate(cur);
         if (ACC == kPacked && (s + 1) % drain == 0) {
             __syncthreads();
-            lds_drain(lds, nf, S, plane, lc);
+            reg_drain(lds, cells, S, plane, lc, racc);
             __syncthreads();
         }
-        if (!more) break;
-        check_entries<E>(eb, n);
-        load_data(eb, da);
-        ea = eb;
-        base = nb;
+    };
+    for (int64_t s = 0; s < n_steps; s += 2) {   // uniform across the block
+        run_step(s, d0, d1);
+        if (s + 1 >= n_steps) break;
+        run_step(s + 1, d1, d0);
     }
     __syncthreads();
-    lds_finish<ACC>(lds, nf, S, plane, lc,
-                      hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                      it.atomic_merge != 0);
+    unsigned long long* const out = (it.dest == kDestPartial ? partial : hist) +
+                                    ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2;
+    if (RA > 0) {
+        reg_drain(lds, cells, S, plane, lc, racc);
+        reg_finish(racc, cells, out, it.dest == kDestAtomic);
+    } else {
+        lds_finish<ACC>(lds, nf, S, plane, lc, out, it.dest == kDestAtomic);
+    }
+}
+
+
+template <typename BinT, int LT, int ACC, int RA, int E>
+__global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
+                                                   int64_t row_stride, int64_t n, int n_features,
+                                                   int S, int lc, const int2* __restrict__ gh,
+                                                   const int32_t* __restrict__ row_index,
+                                                   const FillItem* __restrict__ items,
+                                                   const int32_t* __restrict__ block_first, int n_blocks,
+                                                   int drain, unsigned long long* __restrict__ hist,
+                                                   unsigned long long* __restrict__ partial)
+{
+    extern __shared__ unsigned long long lds[];
+    const int blk = xcd_item(blockIdx.x, n_blocks);
+    if (blk >= n_blocks) return;
+    const int i1 = block_first[blk + 1];
+    for (int ii = block_first[blk]; ii < i1; ++ii) {
+        fill_rows_item<BinT, LT, ACC, RA, E>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
+                                             lc, gh, row_index, drain, hist, partial);
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
