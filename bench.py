@@ -26,6 +26,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# The fill class timed for the roofline: the LDS fill kernels and the merge of
+# split nodes' partial histograms (bracketed together by the library's events
+# on its stream).
+FILL_KERNELS = "k_fill_root / k_fill_rows / k_fill_cols + k_merge"
 METRIC = "level histogram build G cell-updates/s (rows x features) + % of HBM peak"
 
 WORKLOAD_NAMES = {
@@ -109,11 +113,11 @@ def step(ctx, w, plan, g, h):
             tree.run_level(ctx, lp, parents, w.lam, w.gamma)
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
-    """The oracle, as it stands, on the host: the same step (quantize, builds of
-    the built nodes, subtraction, split scan), grown with its own partition."""
+def _oracle_pass(w, budget_s: float):
+    """One step of the oracle, as it stands, on the host: quantize, builds of
+    the built nodes, subtraction, split scan, the tree grown with its own
+    (untimed) partition.  Returns (built cells, timed seconds, sample)."""
     import oracle
-    oracle.build()
     t_work = 0.0
     cells = 0
 
@@ -167,10 +171,47 @@ def cpu_baseline(w, budget_s: float = 20.0):
         child[L.built_slots] = built
         timed(oracle.subtract, parents, child, L.built_is_right)
         timed(oracle.find_splits, child, B, M, kg, kh, w.lam, w.gamma)
+    return cells, t_work, sample
+
+
+def cpu_baseline(w, min_s: float = 10.0, max_reps: int = 30, budget_s: float = 20.0):
+    """The oracle timed on one host core: whole steps repeated until about
+    min_s seconds of timed work (a step larger than budget_s is cut after the
+    level that crosses it)."""
+    import oracle
+    oracle.build()
+    cells = 0
+    t_work = 0.0
+    reps = 0
+    sample = ""
+    while reps < max_reps and (reps == 0 or t_work < min_s):
+        c, t, sample = _oracle_pass(w, budget_s)
+        cells += c
+        t_work += t
+        reps += 1
     return {"value": cells / t_work / 1e9, "unit": "G cell-updates/s", "cores": 1,
             "kind": "oracle", "seconds": round(t_work, 3),
-            "sample": f"{sample} of workload {w.name}: serial C oracle (gcc -O2), 1 thread, "
-                      f"{cells} built cells"}
+            "sample": f"{reps} x ({sample}) of workload {w.name}: serial C oracle (gcc -O2), "
+                      f"1 thread, {cells} built cells"}
+
+
+def traffic_record(config: str, precision: int):
+    """HBM traffic of the fill class measured with rocprofv3 counters
+    (FETCH_SIZE, WRITE_SIZE, calibrated against a copy of known size) by
+    bench_counters.py, per step; None when no record exists for this workload
+    or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{config}_p{precision}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import bench_counters
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") != bench_counters.source_hash():
+            return None
+        return int(rec["fill_traffic"]["bytes_per_step"])
+    except Exception:
+        return None
 
 
 def main():
@@ -181,6 +222,9 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--precision", type=int, default=30,
+                    help="fixed-point bits P (k = P - e); 30 is the int64-cell default, "
+                         "P <= 19 selects the packed one-atomic fill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -200,6 +244,7 @@ def main():
     log(f"[bench] workload {args.config}: {w.n_rows} x {w.n_features}, generated in {time.time() - t0:.1f}s")
     torch.cuda.set_device(0)
     ctx = binding.Context(0)
+    ctx.set_precision(args.precision)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
@@ -211,7 +256,7 @@ def main():
     ctx.sync()
     torch.cuda.synchronize()
 
-    ctx.profile_enable(True)
+    # the timed steps (no per-kernel events)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
@@ -219,17 +264,20 @@ def main():
     ctx.sync()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    prof = {k: ctx.profile_query(k) for k in binding.KERNELS}
-    ctx.profile_enable(False)
 
-    # the same steps without per-kernel events, for the event overhead
+    # the same steps again with the library's per-kernel events (recorded on
+    # its own stream around each kernel class), for the breakdown and the
+    # fill kernels' duration
+    ctx.profile_enable(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
         step(ctx, w, plan, g, h)
     ctx.sync()
     torch.cuda.synchronize()
-    wall_noprof = time.perf_counter() - t1
+    wall_prof = time.perf_counter() - t1
+    prof = {k: ctx.profile_query(k) for k in binding.KERNELS}
+    ctx.profile_enable(False)
 
     ms_per_step = wall * 1e3 / args.steps
     value = plan.cells * args.steps / wall / 1e9
@@ -238,7 +286,7 @@ def main():
     achieved = plan.fill_bytes / (fill_ms_step * 1e-3) / 1e9 if fill_ms_step > 0 else 0.0
     breakdown = {k: round(v[0] / args.steps, 4) for k, v in prof.items()}
     log(f"[bench] per-step device ms by kernel class: {breakdown}; launches {{{', '.join(f'{k}: {v[1] // args.steps}' for k, v in prof.items())}}}")
-    log(f"[bench] wall ms/step {ms_per_step:.3f} (events on), {wall_noprof * 1e3 / args.steps:.3f} (events off)")
+    log(f"[bench] wall ms/step {ms_per_step:.3f} (timed, events off), {wall_prof * 1e3 / args.steps:.3f} (events on)")
 
     result = {
         "metric": METRIC,
@@ -258,14 +306,16 @@ def main():
                    "built_cells_per_step": plan.cells, "levels": plan.level_notes},
         "build_only_gcells_per_s": round(plan.cells / (fill_ms_step + breakdown["gather"] + breakdown["zero"]) / 1e6, 3)
         if fill_ms_step > 0 else None,
-        "ms_per_step_events_off": round(wall_noprof * 1e3 / args.steps, 4),
+        "ms_per_step_events_on": round(wall_prof * 1e3 / args.steps, 4),
         "kernel_ms_per_step": breakdown,
-        "roofline": {"bound": "hbm", "kernel": "k_fill_lds", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": FILL_KERNELS, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": traffic_record(args.config, args.precision),
+                     "traffic_unit": "HBM bytes per step (fetch + write, calibrated counters)",
                      "alg_bytes_per_step": plan.fill_bytes,
                      "launches_per_step": fill_launches // max(args.steps, 1),
                      "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
+        "precision_bits": args.precision,
     }
     ctx.close()
     if not args.no_cpu_baseline:

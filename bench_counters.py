@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""HBM traffic of the benchmark's fill kernels from rocprofv3 counters.
+
+Runs, each as its own child process under `rocprofv3 --pmc`:
+  * a calibration: a device-to-device copy of COPY_BYTES, whose FETCH_SIZE and
+    WRITE_SIZE readings give the factor from counter KiB to bytes moved;
+  * the benchmark step driver (this file with --drive) for 1 and for 3 steps,
+    once per counter.  The difference of the two runs, halved, is one step's
+    traffic: the set-up work (data upload, the first tree that fixes the row
+    lists) cancels out.
+
+Writes profiles/counters_<config>_p<bits>.json (read by bench.py, which reports
+it as roofline.traffic while the kernel sources are unchanged) and a short text
+summary beside it.  Run from the repository root on a machine with the GPU:
+
+    python bench_counters.py --config c3 --precision 30
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import hashlib
+import json
+import os
+import shutil
+import sqlite3
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+FILL_CLASS = ("k_fill_root", "k_fill_rows", "k_fill_cols", "k_merge")
+OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_split_feature", "k_split_reduce",
+         "k_quantize", "k_grad_hess_max")
+SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boosted_amd/csrc/*.h",
+           "include/*.h")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the public header."""
+    h = hashlib.sha256()
+    for pat in SOURCES:
+        for path in sorted(glob.glob(os.path.join(ROOT, pat))):
+            h.update(os.path.relpath(path, ROOT).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def drive(config: str, precision: int, steps: int) -> None:
+    """Set up the benchmark workload and run `steps` steps (no timing)."""
+    sys.path.insert(0, ROOT)
+    import torch
+    import bench
+    from histogram_gradient_boosted_amd import binding, synth
+    w = synth.make(config)
+    ctx = binding.Context(0)
+    ctx.set_precision(precision)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    plan = bench.prepare(ctx, w, g, h, torch)
+    for _ in range(steps):
+        bench.step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+    ctx.close()
+    print(f"drive {config} p{precision}: {steps} steps done", flush=True)
+
+
+def copy_kernel() -> None:
+    """Four device-to-device copies of COPY_BYTES."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copy done", flush=True)
+
+
+REUSE = False   # --reuse: read the databases a previous run left under --out
+
+
+def run_counter(counter: str, out_dir: str, args: list, log_path: str) -> str:
+    """One rocprofv3 pass (from /tmp, the program right after --)."""
+    if REUSE:
+        dbs = glob.glob(os.path.join(out_dir, "**", "*.db"), recursive=True)
+        if not dbs:
+            raise SystemExit(f"--reuse: no counter database under {out_dir}")
+        return dbs[0]
+    if os.path.exists(out_dir):
+        shutil.rmtree(out_dir)
+    env = dict(os.environ, TMPDIR="/tmp")
+    cmd = ["timeout", "-s", "KILL", "600", "rocprofv3", "--pmc", counter, "-d", out_dir, "-o", "p",
+           "--", sys.executable] + args
+    print("[counters]", " ".join(cmd), flush=True)
+    with open(log_path, "w") as log:
+        r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT)
+    dbs = glob.glob(os.path.join(out_dir, "**", "*.db"), recursive=True)
+    if r.returncode != 0 and not dbs:
+        raise SystemExit(f"rocprofv3 pass failed ({r.returncode}); see {log_path}")
+    if not dbs:
+        raise SystemExit(f"no counter database under {out_dir}")
+    return dbs[0]
+
+
+def read_counter(db: str, counter: str) -> dict:
+    """Sum of the counter (KiB) and dispatch count per kernel base name."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+    out = collections.defaultdict(lambda: [0.0, 0])
+    for name, cname, value in rows:
+        if cname != counter:
+            continue
+        base = name.split("(")[0].replace("void ", "").split("<")[0].split("::")[-1].strip()
+        out[base][0] += value
+        out[base][1] += 1
+    return dict(out)
+
+
+def trace_summary(db: str, step_equiv: int, command: str) -> str:
+    """Per-kernel durations from a rocprofv3 --kernel-trace database."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, start, end from kernels").fetchall()
+    per = collections.defaultdict(list)
+    for name, start, end in rows:
+        per[name.split("(")[0].replace("void ", "").strip()].append((end - start) / 1e3)
+    lines = [f"# Kernel trace: `{command}`", "",
+             "rocprofv3 --kernel-trace --stats; durations in microseconds.  One process runs "
+             f"{step_equiv} step-equivalents of the tree (the set-up tree, warm-up, the timed and "
+             "the event-timed passes); 'per step' divides the total by that.", "",
+             "| kernel | dispatches | total us | avg us | min us | max us | us per step |",
+             "|---|---|---|---|---|---|---|"]
+    fill_total = 0.0
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        tot = sum(ds)
+        base = name.split("<")[0].split("::")[-1]
+        if base in FILL_CLASS:
+            fill_total += tot
+        lines.append(f"| {name} | {len(ds)} | {tot:.1f} | {tot / len(ds):.2f} | {min(ds):.2f} | "
+                     f"{max(ds):.2f} | {tot / step_equiv:.2f} |")
+    lines += ["", f"Fill class ({', '.join(FILL_CLASS)}): {fill_total / step_equiv:.1f} us per step."]
+    return "\n".join(lines) + "\n"
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--config", default="c3")
+    ap.add_argument("--precision", type=int, default=30)
+    ap.add_argument("--drive", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--copy", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--steps", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
+    ap.add_argument("--reuse", action="store_true",
+                    help="summarize the databases already under --out instead of profiling")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="summarize a rocprofv3 kernel-trace database instead")
+    ap.add_argument("--step-equiv", type=int, default=44)
+    ap.add_argument("--trace-command", default="")
+    ap.add_argument("--trace-out")
+    args = ap.parse_args()
+    if args.trace_summary:
+        text = trace_summary(args.trace_summary, args.step_equiv, args.trace_command)
+        if args.trace_out:
+            with open(args.trace_out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
+    if args.drive:
+        drive(args.config, args.precision, args.steps)
+        return
+    if args.copy:
+        copy_kernel()
+        return
+
+    global REUSE
+    REUSE = args.reuse
+    me = os.path.abspath(__file__)
+    os.makedirs(args.out, exist_ok=True)
+    t0 = time.time()
+    raw = {}
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        tag = counter.lower()
+        db = run_counter(counter, os.path.join(args.out, f"copy_{tag}"), [me, "--copy"],
+                         os.path.join(args.out, f"copy_{tag}.log"))
+        per = read_counter(db, counter)
+        copies = {k: v for k, v in per.items() if "copy" in k.lower()}
+        if not copies:
+            raise SystemExit(f"no copy kernel in the calibration run: {sorted(per)}")
+        kib, n = max(copies.values(), key=lambda v: v[0])
+        cal[counter] = {"kib_per_copy": kib / n, "factor": COPY_BYTES / (kib / n * 1024.0)}
+        for steps in (1, 3):
+            db = run_counter(counter, os.path.join(args.out, f"{args.config}_p{args.precision}_{tag}_{steps}"),
+                             [me, "--drive", "--config", args.config, "--precision", str(args.precision),
+                              "--steps", str(steps)],
+                             os.path.join(args.out, f"{args.config}_p{args.precision}_{tag}_{steps}.log"))
+            raw[(counter, steps)] = read_counter(db, counter)
+
+    kernels = sorted(set(k for d in raw.values() for k in d) & set(FILL_CLASS + OTHER))
+    per_step = {}
+    for k in kernels:
+        rec = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            a = raw[(counter, 3)].get(k, [0.0, 0])
+            b = raw[(counter, 1)].get(k, [0.0, 0])
+            kib = (a[0] - b[0]) / 2.0
+            rec[counter] = {"kib_raw": round(kib, 1),
+                            "bytes": int(kib * 1024.0 * cal[counter]["factor"]),
+                            "dispatches": (a[1] - b[1]) // 2}
+        per_step[k] = rec
+    fill_fetch = sum(per_step[k]["FETCH_SIZE"]["bytes"] for k in per_step if k in FILL_CLASS)
+    fill_write = sum(per_step[k]["WRITE_SIZE"]["bytes"] for k in per_step if k in FILL_CLASS)
+    record = {
+        "config": args.config,
+        "precision": args.precision,
+        "source_hash": source_hash(),
+        "command": f"python bench_counters.py --config {args.config} --precision {args.precision}",
+        "calibration": {"copy_bytes": COPY_BYTES, **cal},
+        "per_step": per_step,
+        "fill_traffic": {"bytes_per_step": fill_fetch + fill_write, "fetch_bytes": fill_fetch,
+                         "write_bytes": fill_write, "kernels": list(FILL_CLASS)},
+        "seconds": round(time.time() - t0, 1),
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    base = os.path.join(ROOT, "profiles", f"counters_{args.config}_p{args.precision}")
+    with open(base + ".json", "w") as f:
+        json.dump(record, f, indent=1)
+    lines = [f"# HBM traffic per step, {args.config}, P = {args.precision}", "",
+             f"Command: `{record['command']}` (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE;",
+             "per step = (3-step run - 1-step run) / 2).", "",
+             "Calibration, device-to-device copy of 1 GiB: "
+             f"FETCH_SIZE reads {cal['FETCH_SIZE']['kib_per_copy']:.0f} KiB (factor "
+             f"{cal['FETCH_SIZE']['factor']:.3f}), WRITE_SIZE reads {cal['WRITE_SIZE']['kib_per_copy']:.0f} KiB "
+             f"(factor {cal['WRITE_SIZE']['factor']:.3f}).", "",
+             "| kernel | dispatches/step | fetch KiB raw | fetch bytes | write KiB raw | write bytes |",
+             "|---|---|---|---|---|---|"]
+    for k, rec in per_step.items():
+        lines.append(f"| {k} | {rec['FETCH_SIZE']['dispatches']} | {rec['FETCH_SIZE']['kib_raw']:.0f} | "
+                     f"{rec['FETCH_SIZE']['bytes']:,} | {rec['WRITE_SIZE']['kib_raw']:.0f} | "
+                     f"{rec['WRITE_SIZE']['bytes']:,} |")
+    lines += ["", f"Fill class ({', '.join(FILL_CLASS)}): {fill_fetch + fill_write:,} bytes per step "
+              f"({fill_fetch:,} fetched, {fill_write:,} written).", "",
+              f"Kernel sources sha256: `{record['source_hash']}`."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -282,17 +282,17 @@ int packed_drain_steps(int threads, int lc, int per_thread)
     return (int)((kPackedRowsPerCopy - (kRootRows - 1)) / per_copy_step);
 }
 
-// Cost model of the fill per cell (seconds), from microbenchmarks on the
-// MI355X: random-bin ds_add_u64 runs at kLdsOps[lc] lanes per clock per CU
-// with 2^lc lane-interleaved copies; bins stream from HBM at ~6 TB/s and the
-// (g, h) pair, re-read by every feature tile of a row chunk, mostly from L2 at
-// ~15 TB/s.  The two overlap imperfectly.
+// Cost model of the root and feature-major fills per cell (seconds), fitted
+// to measurements on the MI355X: random-bin ds_add_u64 runs at kLdsOps[lc]
+// lanes per clock per CU with 2^lc lane-interleaved copies, bins stream from
+// HBM at ~6 TB/s, and every feature tile of a row chunk re-reads and unpacks
+// the (g, h) pair (~30 TB/s equivalent).  In these kernels the terms add up
+// rather than overlap.
 double fill_cost(int acc, int lc, int tile, int w)
 {
     static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
     const double lds = (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * 2.4e9 * 256);
-    const double mem = w / 6.0e12 + (8.0 / tile) / 15.0e12;
-    return std::max(lds, mem) + 0.25 * std::min(lds, mem);
+    return lds + w / 6.0e12 + (8.0 / tile) / 30.0e12;
 }
 
 // Row-major level fills read scattered rows, and each feature tile of a row
