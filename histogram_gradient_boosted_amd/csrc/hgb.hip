@@ -44,10 +44,10 @@ constexpr int64_t kRowMajorMaxRowBytes = 512;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
 // Default fixed-point precision of begin_tree (bits below the largest value).
 constexpr int kDefaultPrecision = 30;
-constexpr int kStages = 4;
+constexpr int kStages = 16;
 
 struct Stage {
-    void* host = nullptr;
+    void* host = nullptr;   // pinned
     void* dev = nullptr;
     size_t cap = 0;
     hipEvent_t ev = nullptr;
@@ -157,9 +157,12 @@ hgb_status grow(hgb_ctx* c, T** p, int64_t* cap, int64_t need)
     return HGB_OK;
 }
 
-// Copy `bytes` of host data to a device staging buffer on the stream.  The
-// stage is released (event recorded) by stage_release after its consumers have
-// been enqueued; a stage is reused only once that event has completed.
+// Copy `bytes` of host data (a launch plan: items, slot lists) to a device
+// staging buffer on the stream.  The stage is released (event recorded) by
+// stage_release after its consumers have been enqueued; a stage is reused
+// only once that event has completed.  (Kernels reading the pinned buffer in
+// place, or copies on a second stream ordered by events, both measured
+// slower than these small in-stream copies.)
 hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
 {
     Stage& s = c->stage[c->stage_next];
@@ -172,6 +175,7 @@ hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
         if (s.host) HGB_HIP(c, hipHostFree(s.host));
         if (s.dev) HGB_HIP(c, hipFree(s.dev));
         s.host = s.dev = nullptr;
+        s.cap = 0;
         size_t want = std::max<size_t>(bytes, 4096);
         HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
         HGB_HIP(c, hipMalloc(&s.dev, want));
@@ -499,7 +503,7 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
     } else {
         // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial)
+#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
@@ -536,20 +540,18 @@ hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 }
 
 // Zero whole node slots of the level buffer.
-hgb_status zero_node_slices(hgb_ctx* c, int64_t* hist, const int32_t* slots, size_t n_slots)
+// Zero whole node slots of the level buffer; the slot list is on the device.
+hgb_status launch_zero(hgb_ctx* c, int64_t* hist, const int32_t* slots_dev, size_t n_slots)
 {
     if (n_slots == 0) return HGB_OK;
-    Stage* s = nullptr;
-    hgb_status st = stage_upload(c, slots, n_slots * sizeof(int32_t), &s);
-    if (st != HGB_OK) return st;
     const int64_t node_elems = (int64_t)c->F * c->S * 2;
     dim3 grid(grid_for(node_elems, 256, 1024), (unsigned)n_slots);
     {
         ProfScope ps(c, HGB_KERNEL_ZERO);
-        k_zero_slices<<<grid, 256, 0, c->stream>>>(hist, (const int32_t*)s->dev, node_elems);
+        k_zero_slices<<<grid, 256, 0, c->stream>>>(hist, slots_dev, node_elems);
     }
     HGB_LAUNCHED(c, "k_zero_slices");
-    return stage_release(c, s);
+    return HGB_OK;
 }
 
 // Fill of a level below the root.  The level order is cut into equal shares
@@ -701,7 +703,9 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         st = grow(c, &c->partial, &c->partial_cap, n_partial * node_elems);
         if (st != HGB_OK) return st;
     }
-    if (total > 0) {
+    // the row-major fill reads each row's (g, h) itself; the others read
+    // them gathered into level order
+    if (total > 0 && plan.kind != kFillRowsKind) {
         st = grow(c, &c->gh, &c->gh_cap, total);
         if (st != HGB_OK) return st;
         ProfScope ps(c, HGB_KERNEL_GATHER);
@@ -709,23 +713,28 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
                                                                     c->dev_words + 2);
         HGB_LAUNCHED(c, "k_gather");
     }
-    st = zero_node_slices(c, hist, zero_slots.data(), zero_slots.size());
-    if (st != HGB_OK) return st;
-    if (items.empty()) return HGB_OK;
+    if (items.empty() && zero_slots.empty()) return HGB_OK;
 
-    // one upload: items, block list, merges (each part 256-byte aligned)
+    // one upload: items, block list, merges, slots to zero (each part
+    // 256-byte aligned)
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t off_blocks = up(items.size() * sizeof(FillItem));
     const size_t off_merges = off_blocks + up(block_first.size() * sizeof(int32_t));
-    const size_t bytes = off_merges + merges.size() * sizeof(MergeEntry);
+    const size_t off_zero = off_merges + up(merges.size() * sizeof(MergeEntry));
+    const size_t bytes = off_zero + zero_slots.size() * sizeof(int32_t);
     std::vector<uint8_t> blob(bytes, 0);
-    std::memcpy(blob.data(), items.data(), items.size() * sizeof(FillItem));
+    if (!items.empty()) std::memcpy(blob.data(), items.data(), items.size() * sizeof(FillItem));
     std::memcpy(blob.data() + off_blocks, block_first.data(), block_first.size() * sizeof(int32_t));
     if (!merges.empty())
         std::memcpy(blob.data() + off_merges, merges.data(), merges.size() * sizeof(MergeEntry));
+    if (!zero_slots.empty())
+        std::memcpy(blob.data() + off_zero, zero_slots.data(), zero_slots.size() * sizeof(int32_t));
     Stage* sg = nullptr;
     st = stage_upload(c, blob.data(), bytes, &sg);
     if (st != HGB_OK) return st;
+    st = launch_zero(c, hist, (const int32_t*)((const uint8_t*)sg->dev + off_zero), zero_slots.size());
+    if (st != HGB_OK) return st;
+    if (items.empty()) return stage_release(c, sg);
     const uint8_t* dev = (const uint8_t*)sg->dev;
     {
         FillArgs a{};
@@ -1120,22 +1129,37 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
                      "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d drain %d chunk %lld items %zu lds %zu\n",
                      (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.drain, (long long)ch,
                      n_items, plan.lds_bytes);
+    // one upload: the root's slot (to zero before atomic merges), then each
+    // width's items (each part 256-byte aligned)
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    size_t offs[9] = {};
+    size_t bytes = 256;
+    for (int wdt = 8; wdt >= 1; --wdt) {
+        offs[wdt] = bytes;
+        bytes += up(groups[wdt].size() * sizeof(FillItem));
+    }
+    std::vector<uint8_t> blob(bytes, 0);
+    std::memcpy(blob.data(), &slots[0], sizeof(int32_t));
+    for (int wdt = 8; wdt >= 1; --wdt)
+        if (!groups[wdt].empty())
+            std::memcpy(blob.data() + offs[wdt], groups[wdt].data(), groups[wdt].size() * sizeof(FillItem));
+    Stage* sg = nullptr;
+    hgb_status st = stage_upload(c, blob.data(), bytes, &sg);
+    if (st != HGB_OK) return st;
+    const uint8_t* dev = (const uint8_t*)sg->dev;
     if (nchunks > 1) {
-        hgb_status st = zero_node_slices(c, hist, slots.data(), 1);
+        st = launch_zero(c, hist, (const int32_t*)dev, 1);
         if (st != HGB_OK) return st;
     }
     for (int wdt = 8; wdt >= 1; --wdt) {
         std::vector<FillItem>& items = groups[wdt];
         if (items.empty()) continue;
-        Stage* s = nullptr;
-        hgb_status st = stage_upload(c, items.data(), items.size() * sizeof(FillItem), &s);
-        if (st != HGB_OK) return st;
         FillPlan gp = plan;
         gp.tile = wdt;
         gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc));
         FillArgs a{};
         a.gh = c->q;
-        a.items = (const FillItem*)s->dev;
+        a.items = (const FillItem*)(dev + offs[wdt]);
         a.n_items = (int)items.size();
         // 8-row vector loads need rows aligned to 8 (chunk starts are
         // multiples of 128)
@@ -1145,10 +1169,8 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         ProfScope ps(c, HGB_KERNEL_FILL);
         st = launch_fill(c, gp, a);
         if (st != HGB_OK) return st;
-        st = stage_release(c, s);
-        if (st != HGB_OK) return st;
     }
-    return HGB_OK;
+    return stage_release(c, sg);
 }
 
 hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* child,
@@ -1172,18 +1194,25 @@ hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* chi
         plan[2 * i + 1] = built_is_right[i] ? 1 : 0;
     }
     HGB_HIP(c, hipSetDevice(c->device));
-    Stage* s = nullptr;
-    hgb_status st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
-    if (st != HGB_OK) return st;
     const int64_t pair_vec = (int64_t)c->F * c->S;   // longlong2 per slot
     dim3 grid(grid_for(pair_vec, 256, 2048), (unsigned)n_pairs);
+    SubtractInline inl{};
+    Stage* s = nullptr;
+    const int32_t* plan_dev = nullptr;
+    if (n_pairs <= kSubtractInlinePairs) {
+        std::memcpy(inl.v, plan.data(), plan.size() * sizeof(int32_t));
+    } else {
+        hgb_status st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
+        if (st != HGB_OK) return st;
+        plan_dev = (const int32_t*)s->dev;
+    }
     {
         ProfScope ps(c, HGB_KERNEL_SUBTRACT);
-        k_subtract<<<grid, 256, 0, c->stream>>>((const longlong2*)parent, (longlong2*)child,
-                                                (const int32_t*)s->dev, pair_vec);
+        k_subtract<<<grid, 256, 0, c->stream>>>((const longlong2*)parent, (longlong2*)child, plan_dev,
+                                                inl, pair_vec);
     }
     HGB_LAUNCHED(c, "k_subtract");
-    return stage_release(c, s);
+    return s ? stage_release(c, s) : HGB_OK;
 }
 
 hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,

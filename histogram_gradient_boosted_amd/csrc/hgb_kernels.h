@@ -760,10 +760,10 @@ template <typename BinT, int LT, int ACC, int RA, int E>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
                                       int64_t n, int n_features, int S, int lc,
-                                      const int2* __restrict__ gh,
+                                      const int2* __restrict__ q,
                                       const int32_t* __restrict__ row_index, int drain,
                                       unsigned long long* __restrict__ hist,
-                                      unsigned long long* __restrict__ partial)
+                                      unsigned long long* __restrict__ partial, int& bad)
 {
     static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
     const int f0 = it.f0_nf & 0xffff;
@@ -805,10 +805,11 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     auto load_rows = [&](int64_t s, const Index& x, Data& d) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const int64_t kk = rb + s * step + (int64_t)e * blockDim.x + threadIdx.x;
             d.ok[e] = x.in[e] && (uint32_t)x.r[e] < (uint64_t)n;
-            d.c[e].load(tile + (int64_t)(d.ok[e] ? x.r[e] : 0) * row_stride);
-            d.g[e] = gh[x.in[e] ? kk : rb];
+            bad |= (int)x.in[e] & (int)!d.ok[e];
+            const int64_t r = d.ok[e] ? x.r[e] : 0;
+            d.c[e].load(tile + r * row_stride);
+            d.g[e] = q[r];   // the level-order gather, fused: the row's (g, h) beside its bins
         }
     };
     // Idle entries and features past the tile's nf are skipped.  (The loads
@@ -882,35 +883,44 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 template <typename BinT, int LT, int ACC, int RA, int E>
 __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
-                                                   int S, int lc, const int2* __restrict__ gh,
+                                                   int S, int lc, const int2* __restrict__ q,
                                                    const int32_t* __restrict__ row_index,
                                                    const FillItem* __restrict__ items,
                                                    const int32_t* __restrict__ block_first, int n_blocks,
                                                    int drain, unsigned long long* __restrict__ hist,
-                                                   unsigned long long* __restrict__ partial)
+                                                   unsigned long long* __restrict__ partial,
+                                                   uint32_t* __restrict__ err)
 {
     extern __shared__ unsigned long long lds[];
     const int blk = xcd_item(blockIdx.x, n_blocks);
     if (blk >= n_blocks) return;
     const int i1 = block_first[blk + 1];
+    int bad = 0;   // a row index outside [0, n): skipped, and flagged
     for (int ii = block_first[blk]; ii < i1; ++ii) {
         fill_rows_item<BinT, LT, ACC, RA, E>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
-                                             lc, gh, row_index, drain, hist, partial);
+                                             lc, q, row_index, drain, hist, partial, bad);
         __syncthreads();
     }
+    if (bad) atomicOr(err, kErrRowIndex);
 }
 
 // ---------------------------------------------------------------------------
 // subtract_siblings: other = parent - built, for every pair, elementwise.
 // ---------------------------------------------------------------------------
+// A small plan travels in the kernel's arguments (no upload).
+constexpr int kSubtractInlinePairs = 256;
+struct SubtractInline {
+    int32_t v[2 * kSubtractInlinePairs];   // per pair: parent slot, built side
+};
+
 __global__ __launch_bounds__(256) void k_subtract(const longlong2* __restrict__ parent,
                                                   longlong2* __restrict__ child,
                                                   const int32_t* __restrict__ plan,
-                                                  int64_t pair_vec)
+                                                  const SubtractInline inl, int64_t pair_vec)
 {
     const int pair = blockIdx.y;
-    const int32_t pslot = plan[2 * pair];
-    const int r = plan[2 * pair + 1];
+    const int32_t pslot = plan ? plan[2 * pair] : inl.v[2 * pair];
+    const int r = plan ? plan[2 * pair + 1] : inl.v[2 * pair + 1];
     const longlong2* p = parent + (int64_t)pslot * pair_vec;
     const longlong2* b = child + (int64_t)(2 * pair + r) * pair_vec;
     longlong2* o = child + (int64_t)(2 * pair + 1 - r) * pair_vec;

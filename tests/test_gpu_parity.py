@@ -309,6 +309,30 @@ def test_out_slots_scattered(hgb, torch):
     assert np.array_equal(got[slots], want)
 
 
+@pytest.mark.parametrize("n_pairs", [1, 256, 257, 600])
+def test_subtract_plan_sizes(hgb, torch, n_pairs):
+    """Small plans travel in the kernel's arguments, larger ones are uploaded:
+    both against the oracle's subtraction, with parents taken out of order."""
+    say("subtract plan sizes", n_pairs)
+    w = synth.random_small(43, 1_000, 3, 16, False, 0)
+    F, S = w.n_features, w.n_slots
+    rng = np.random.default_rng(n_pairs)
+    parent = rng.integers(-2**40, 2**40, size=(n_pairs + 3, F, S, 2), dtype=np.int64)
+    child = rng.integers(-2**40, 2**40, size=(2 * n_pairs, F, S, 2), dtype=np.int64)
+    bir = rng.integers(0, 2, size=n_pairs).astype(np.uint8)
+    pslot = rng.permutation(n_pairs + 3)[:n_pairs].astype(np.int32)
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    par_t = torch.from_numpy(parent).cuda()
+    ch_t = torch.from_numpy(child).cuda()
+    ctx.subtract_siblings(par_t, ch_t, bir, pslot)
+    ctx.sync()
+    got = ch_t.cpu().numpy()
+    ctx.close()
+    want = oracle.subtract(parent[pslot], child.copy(), bir)
+    assert np.array_equal(got, want)
+
+
 # ----------------------------------------------------------------- errors ---
 
 def test_error_paths(hgb, torch):
