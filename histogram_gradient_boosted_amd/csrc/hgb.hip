@@ -40,7 +40,9 @@ constexpr double kPieceRowsPerCell = 0.25;
 // into its zeroed slot with atomics.
 constexpr int kMergeGroup = 32;
 // Keep a row-major copy of the bins when a row takes at most this many bytes.
-constexpr int64_t kRowMajorMaxRowBytes = 512;
+// Rows up to this many bytes get a row-major copy (C4's 16 KB rows included):
+// below the root, a level reads only its built rows' lines from it.
+constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
 // Default fixed-point precision of begin_tree (bits below the largest value).
 constexpr int kDefaultPrecision = 30;
@@ -299,16 +301,20 @@ double fill_cost(int acc, int lc, int tile, int w)
     return lds + w / 6.0e12 + (8.0 / tile) / 30.0e12;
 }
 
-// Row-major level fills read scattered rows, and each feature tile of a row
-// fetches that row's whole 128-byte line again; cost per row (seconds) of a
-// plan with n_tiles tiles, from the same LDS rates, ~5 TB/s of scattered line
-// fetches, and the packed drains (lane-contiguous LDS reads and writes).
-double rows_cost(int acc, int lc, int F, int n_tiles, double drain_ops_per_row)
+// Row-major level fills read scattered rows.  Cost per row (seconds) of a plan
+// with n_tiles feature tiles: the LDS adds at the same rates as above (plus
+// the packed drains: lane-contiguous LDS reads and writes); each row's lines
+// from HBM once at ~5 TB/s (the tiles of a share run side by side on one XCD
+// and share them through L2); and per tile a 64-byte L2 transfer of the row's
+// segment plus its index and (g, h), at ~10 TB/s (fitted to C3 and C4 level
+// timings).
+double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, double drain_ops_per_row)
 {
     static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
     const double clk = 2.4e9 * 256;
     const double lds = F * (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * clk) + drain_ops_per_row / (16.0 * clk);
-    const double mem = n_tiles * (128.0 / 5.0e12 + 12.0 / 10.0e12);
+    const double lines = (double)std::max<int64_t>((row_bytes + 127) / 128, 1) * 128.0;
+    const double mem = lines / 5.0e12 + n_tiles * (64.0 + 12.0) / 10.0e12;
     return std::max(lds, mem) + 0.25 * std::min(lds, mem);
 }
 
@@ -347,7 +353,7 @@ FillPlan plan_rows(const hgb_ctx* c)
                         if (drain == 0) continue;
                         drain_ops = 2.0 * nf * S * (1 << lc) / ((double)kLevelThreads * e * drain) * n_tiles;
                     }
-                    const double cost = rows_cost(acc, lc, F, n_tiles, drain_ops);
+                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops);
                     if (cost < best) {
                         best = cost;
                         found = true;
@@ -1228,6 +1234,7 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     if (n_nodes == 0) return HGB_OK;
     if (!hist || !out) return fail(c, HGB_E_INVALID, "find_splits: null pointer");
     HGB_HIP(c, hipSetDevice(c->device));
+    static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
     hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * c->F);
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
@@ -1239,7 +1246,6 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),
         std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals);
     HGB_LAUNCHED(c, "k_split_feature");
-    static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
     k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F,
                                                              (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");

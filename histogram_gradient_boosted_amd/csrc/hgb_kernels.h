@@ -43,11 +43,23 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__
     const int64_t n4 = vec ? (n >> 2) : 0;
     const float4* g4 = (const float4*)g;
     const float4* h4 = (const float4*)h;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const float4 a = g4[i], b = h4[i];
+    auto fold = [&](const float4& a, const float4& b) {
         mg = max(mg, max(max(abs_pattern(a.x), abs_pattern(a.y)), max(abs_pattern(a.z), abs_pattern(a.w))));
         mh = max(mh, max(max(hess_pattern(b.x), hess_pattern(b.y)), max(hess_pattern(b.z), hess_pattern(b.w))));
+    };
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // four strided groups in flight per thread
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        float4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = g4[i + u * stride];
+            b[u] = h4[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold(a[u], b[u]);
     }
+    for (; i < n4; i += stride) fold(g4[i], h4[i]);
     for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         mg = max(mg, abs_pattern(g[i]));
         mh = max(mh, hess_pattern(h[i]));
@@ -986,20 +998,19 @@ __device__ inline double split_gain(double gl, double hl, double gr, double hr, 
     return s - gamma;
 }
 
-// One wave per (node, feature): totals, a lane-contiguous prefix scan of the
+// One wave, one (node, feature): totals, a lane-contiguous prefix scan of the
 // value bins, the gain of every (bin, direction) candidate, a wave argmax.
-__global__ __launch_bounds__(256) void k_split_feature(const long long* __restrict__ hist,
-                                                       int n_features, int n_bins, int S,
-                                                       int has_missing, double scale_g,
-                                                       double scale_h, double lam, double gamma,
-                                                       FeatureBest* __restrict__ best,
-                                                       long long* __restrict__ totals)
+// Every lane returns the result (gain -inf and code -1 when no candidate).
+struct WaveBest {
+    FeatureBest fb;
+    long long G, H;   // the feature's slot sums: the node totals
+};
+
+__device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, int n_bins,
+                                             int has_missing, double scale_g, double scale_h,
+                                             double lam, double gamma)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    const int node = blockIdx.y;
-    if (f >= n_features) return;
-    const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
     const int per = (n_bins + kWave - 1) / kWave;
     const int b0 = lane * per;
     const int b1 = min(b0 + per, n_bins);
@@ -1058,15 +1069,35 @@ __global__ __launch_bounds__(256) void k_split_feature(const long long* __restri
     }
     const long long wgl = wave_shfl_i64(bgl, src);
     const long long whl = wave_shfl_i64(bhl, src);
+    WaveBest r;
+    r.fb.gain = rc < 0 ? -__builtin_inf() : rg;
+    r.fb.code = rc;
+    r.fb.pad = 0;
+    r.fb.g_left = rc < 0 ? 0 : wgl;
+    r.fb.h_left = rc < 0 ? 0 : whl;
+    r.G = G;
+    r.H = H;
+    return r;
+}
+
+// One wave per (node, feature), results to best[node][feature]; node totals
+// from feature 0.
+__global__ __launch_bounds__(256) void k_split_feature(const long long* __restrict__ hist,
+                                                       int n_features, int n_bins, int S,
+                                                       int has_missing, double scale_g,
+                                                       double scale_h, double lam, double gamma,
+                                                       FeatureBest* __restrict__ best,
+                                                       long long* __restrict__ totals)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int node = blockIdx.y;
+    if (f >= n_features) return;
+    const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
+    const WaveBest r = wave_feature_best(hf, n_bins, has_missing, scale_g, scale_h, lam, gamma);
     if (lane == 0) {
-        FeatureBest out;
-        out.gain = rc < 0 ? -__builtin_inf() : rg;
-        out.code = rc;
-        out.pad = 0;
-        out.g_left = rc < 0 ? 0 : wgl;
-        out.h_left = rc < 0 ? 0 : whl;
-        best[(int64_t)node * n_features + f] = out;
-        if (f == 0) { totals[2 * node] = G; totals[2 * node + 1] = H; }
+        best[(int64_t)node * n_features + f] = r.fb;
+        if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }
     }
 }
 

@@ -214,6 +214,16 @@ def test_c4(hgb, torch, n, F):
     run_level_both(hgb, torch, w, check_exact_gain=True)
 
 
+@pytest.mark.parametrize("missing,bits", [(True, 30), (False, 19)])
+def test_feature_major_levels(hgb, torch, missing, bits):
+    """Rows wider than the row-major copy's limit (64 KiB: here 33,000 u16
+    features) are filled from the feature-major matrix."""
+    F, u16 = 33_000, True
+    say("feature-major levels", F, missing, u16, bits)
+    w = synth.random_small(44, 1_200, F, 256, missing, 6, u16=u16)
+    run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
+
+
 def oracle_tree(w, depth, bits=30):
     qg, qh, kg, kh = oracle_quantized(w, bits)
     levels = []
