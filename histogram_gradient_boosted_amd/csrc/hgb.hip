@@ -1242,9 +1242,21 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     const int waves = 4;
     dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
     ProfScope ps(c, HGB_KERNEL_SPLIT);
-    k_split_feature<<<grid, waves * kWave, 0, c->stream>>>(
-        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),
-        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals);
+    // a lane's bins in registers when there are at most 16 of them (and the
+    // buffer is 16-byte aligned); otherwise read twice from memory
+    const int per = (c->B + kWave - 1) / kWave;
+    const bool aligned = ((uintptr_t)hist & 15) == 0;
+#define HGB_SPLIT(PER)                                                                              \
+    k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
+        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals)
+    if (!aligned || per > 16) HGB_SPLIT(0);
+    else if (per <= 1) HGB_SPLIT(1);
+    else if (per <= 2) HGB_SPLIT(2);
+    else if (per <= 4) HGB_SPLIT(4);
+    else if (per <= 8) HGB_SPLIT(8);
+    else HGB_SPLIT(16);
+#undef HGB_SPLIT
     HGB_LAUNCHED(c, "k_split_feature");
     k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F,
                                                              (SplitOut*)out);

@@ -1006,17 +1006,46 @@ struct WaveBest {
     long long G, H;   // the feature's slot sums: the node totals
 };
 
+// PER > 0: the lane's PER slots are read once, 16 bytes at a time, into
+// registers (PER >= ceil(n_bins / 64)); PER == 0: any bin count, two passes
+// over memory.
+template <int PER>
 __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, int n_bins,
                                              int has_missing, double scale_g, double scale_h,
                                              double lam, double gamma)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int per = (n_bins + kWave - 1) / kWave;
+    const int per = PER > 0 ? PER : (n_bins + kWave - 1) / kWave;
     const int b0 = lane * per;
     const int b1 = min(b0 + per, n_bins);
+    longlong2 v[PER > 0 ? PER : 1];
+    if (PER > 0) {
+        const longlong2* h2 = (const longlong2*)hf;
+#pragma unroll
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) {
+            const int b = b0 + j;
+            const longlong2 t = h2[min(b, n_bins - 1)];   // unconditional, masked below
+            v[j] = b < b1 ? t : make_longlong2(0, 0);
+        }
+    }
+    auto slot = [&](int b) -> longlong2 {
+        if (PER > 0) {
+            longlong2 r = make_longlong2(0, 0);
+#pragma unroll
+            for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
+                if (b - b0 == j) r = v[j];
+            return r;
+        }
+        return make_longlong2(hf[2 * b], hf[2 * b + 1]);
+    };
 
     long long sg = 0, sh = 0;
-    for (int b = b0; b < b1; ++b) { sg += hf[2 * b]; sh += hf[2 * b + 1]; }
+    if (PER > 0) {
+#pragma unroll
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) { sg += v[j].x; sh += v[j].y; }
+    } else {
+        for (int b = b0; b < b1; ++b) { sg += hf[2 * b]; sh += hf[2 * b + 1]; }
+    }
     // inclusive scan of lane sums
     long long ig = sg, ih = sh;
     for (int d = 1; d < kWave; d <<= 1) {
@@ -1037,9 +1066,9 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
     long long bgl = 0, bhl = 0;
     long long pg = ig - sg, ph = ih - sh;   // exclusive prefix
     const int n_dirs = has_missing ? 2 : 1;
-    for (int b = b0; b < b1; ++b) {
-        pg += hf[2 * b];
-        ph += hf[2 * b + 1];
+    auto visit = [&](int b, longlong2 sv) {
+        pg += sv.x;
+        ph += sv.y;
         for (int d = 0; d < n_dirs; ++d) {
             const long long GL = pg + (d ? miss_g : 0);
             const long long HL = ph + (d ? miss_h : 0);
@@ -1056,6 +1085,13 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
                 bhl = HL;
             }
         }
+    };
+    if (PER > 0) {
+#pragma unroll
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
+            if (b0 + j < b1) visit(b0 + j, v[j]);
+    } else {
+        for (int b = b0; b < b1; ++b) visit(b, slot(b));
     }
     // wave argmax over (gain, code)
     int src = lane;
@@ -1082,6 +1118,7 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
 
 // One wave per (node, feature), results to best[node][feature]; node totals
 // from feature 0.
+template <int PER>
 __global__ __launch_bounds__(256) void k_split_feature(const long long* __restrict__ hist,
                                                        int n_features, int n_bins, int S,
                                                        int has_missing, double scale_g,
@@ -1094,7 +1131,7 @@ __global__ __launch_bounds__(256) void k_split_feature(const long long* __restri
     const int node = blockIdx.y;
     if (f >= n_features) return;
     const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
-    const WaveBest r = wave_feature_best(hf, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+    const WaveBest r = wave_feature_best<PER>(hf, n_bins, has_missing, scale_g, scale_h, lam, gamma);
     if (lane == 0) {
         best[(int64_t)node * n_features + f] = r.fb;
         if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }

@@ -429,3 +429,28 @@ def test_unaligned_gradient_views(hgb, torch):
     assert ctx.get_scales() == (kg, kh)
     ctx.close()
     assert np.array_equal(got, oracle.build_hist(w.bins, 64, False, qg, qh))
+
+
+@pytest.mark.parametrize("B,missing", [(64, False), (255, True), (1024, True)])
+def test_splits_unaligned_histograms(hgb, torch, B, missing):
+    """A histogram buffer 8 bytes off a 16-byte boundary takes the scan that
+    reads slots from memory; aligned ones keep a lane's slots in registers.
+    Both against the oracle."""
+    say("split alignment", B, missing)
+    w = synth.random_small(51, 20_000, 5, B, missing, 6)
+    L = w.level
+    ctx, g, h = new_ctx(hgb, w, torch)
+    qg, qh, kg, kh = oracle_quantized(w)
+    N = 2 * L.n_pairs
+    elems = N * w.n_features * w.n_slots * 2
+    big = torch.zeros(elems + 2, dtype=torch.int64, device="cuda")
+    want_h = oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh,
+                               L.children_row_index, L.children_offsets)
+    want = oracle.find_splits(want_h, w.n_bins, w.has_missing, kg, kh, w.lam, w.gamma)
+    for off in (2, 1):   # 16-byte aligned, then 8 bytes off
+        view = big[off:off + elems]
+        view.copy_(torch.from_numpy(want_h.reshape(-1)).cuda())
+        sp = gpu_splits(hgb, ctx, view, N, w.lam, w.gamma, torch)
+        assert_splits(sp, want, f"offset {off}")
+        assert np.array_equal(sp["gain"].view(np.int64), want["gain"].view(np.int64))
+    ctx.close()
