@@ -32,9 +32,10 @@ SPLIT_BYTES = 56
 EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb_sync",
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
             "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
-            "hgb_profile_query", "hgb_set_precision")
+            "hgb_profile_query", "hgb_set_precision", "hgb_partition_level")
 
-KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5}
+KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5,
+           "partition": 6}
 
 
 class HGBError(RuntimeError):
@@ -84,6 +85,8 @@ def load():
     lib.hgb_subtract_siblings.restype = c_int
     lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_splits.restype = c_int
+    lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32)]
+    lib.hgb_partition_level.restype = c_int
     lib.hgb_profile_enable.argtypes = [vp, c_int]
     lib.hgb_profile_enable.restype = c_int
     lib.hgb_profile_query.argtypes = [vp, c_int, ctypes.POINTER(ctypes.c_double),
@@ -251,6 +254,29 @@ class Context:
         self._check(self._lib.hgb_subtract_siblings(
             self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
             None if ps is None else ps.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings")
+
+    def partition_level(self, splits, out_rows, row_index=None, node_offsets=None):
+        """Children's rows of every split node into `out_rows` (int32 CUDA tensor).
+
+        `splits`: the level's hgb_split records (uint8 CUDA tensor, as
+        find_splits writes them).  Returns the children's offsets (int32 numpy
+        array, 2c + 1 entries for c nodes with a split)."""
+        torch = self._torch
+        if row_index is None:
+            n_nodes, offs, ri, total = 1, None, None, self.n_rows
+        else:
+            offs = _i32_host(node_offsets)
+            n_nodes = int(offs.shape[0]) - 1
+            total = int(offs[-1])
+            ri = self._dev(row_index, "row_index", torch.int32, total)
+        sp = self._dev(splits, "splits", torch.uint8, n_nodes * SPLIT_BYTES)
+        op = self._dev(out_rows, "out_rows", torch.int32, total) if total else None
+        child = np.zeros(2 * n_nodes + 1, dtype=np.int32)
+        nc = ctypes.c_int32(0)
+        self._check(self._lib.hgb_partition_level(
+            self._h, ri, None if offs is None else offs.ctypes.data_as(ctypes.c_void_p), n_nodes,
+            sp, op, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc)), "partition_level")
+        return child[: nc.value + 1].copy()
 
     def find_splits(self, hist, n_nodes: int, lam: float, gamma: float, out):
         """out: uint8 CUDA tensor of at least n_nodes * 56 bytes (hgb_split records)."""

@@ -86,6 +86,10 @@ struct hgb_ctx {
     int64_t gh_cap = 0;
     long long* partial = nullptr;   // partial histograms of nodes split over several blocks
     int64_t partial_cap = 0;
+    int32_t* part = nullptr;        // partition: chunk counts, left bases, per-node records
+    int64_t part_cap = 0;
+    int32_t* part_host = nullptr;   // pinned copy of the per-node records
+    int64_t part_host_cap = 0;
     FeatureBest* best = nullptr;
     int64_t best_cap = 0;
     long long* totals = nullptr;
@@ -586,8 +590,11 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
     // out), so a share that touches many small nodes takes fewer rows.
     int64_t piece_rows = std::max<int64_t>((int64_t)(kPieceRowsPerCell * std::min(plan.tile, c->F) * c->S), 1);
     if (c->tune[7] >= 0) piece_rows = std::max(c->tune[7], 1);
-    int64_t nonempty = 0;
-    for (int i = 0; i < n_nodes; ++i) nonempty += count[i] > 0;
+    int64_t nonempty = 0, built = 0;   // skipped nodes count 0 rows
+    for (int i = 0; i < n_nodes; ++i) {
+        nonempty += count[i] > 0;
+        built += count[i];
+    }
     int64_t budget = 0;
 
     // pieces of each share, in level order: (node, begin, end, chunk of node)
@@ -630,9 +637,9 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
     // The smallest budget whose cut fits one round of blocks (binary search;
     // a larger budget never needs more shares).
     {
-        int64_t lo = std::max<int64_t>((total + piece_rows * nonempty + shares - 1) / shares,
+        int64_t lo = std::max<int64_t>((built + piece_rows * nonempty + shares - 1) / shares,
                                        piece_rows + align);
-        int64_t hi = std::max<int64_t>(total + piece_rows * (nonempty + 1) + align, lo);
+        int64_t hi = std::max<int64_t>(built + piece_rows * (nonempty + 1) + align, lo);
         while (lo < hi) {
             budget = lo + (hi - lo) / 2;
             if (cut() <= shares) hi = budget;
@@ -649,7 +656,7 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
     std::vector<int32_t> zero_slots;
     int64_t n_partial = 0;
     for (int i = 0; i < n_nodes; ++i) {
-        if (count[i] == 0) zero_slots.push_back(slots[i]);
+        if (count[i] == 0 && slots[i] >= 0) zero_slots.push_back(slots[i]);   // -1: skipped
         if (pieces_of[i] <= 1) continue;
         partial_base[i] = (int32_t)n_partial;
         const int groups = (pieces_of[i] + kMergeGroup - 1) / kMergeGroup;
@@ -839,6 +846,8 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipFree(c->q);
     (void)hipFree(c->gh);
     (void)hipFree(c->partial);
+    (void)hipFree(c->part);
+    if (c->part_host) (void)hipHostFree(c->part_host);
     (void)hipFree(c->best);
     (void)hipFree(c->totals);
     (void)hipFree(c->dev_words);
@@ -1049,10 +1058,14 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     std::vector<int32_t> slots(n_nodes);
     for (int i = 0; i < n_nodes; ++i) {
         slots[i] = out_slot ? out_slot[i] : i;
-        if (slots[i] < 0) return fail(c, HGB_E_INVALID, "build_level: negative output slot");
+        if (slots[i] < -1) return fail(c, HGB_E_INVALID, "build_level: output slot below -1");
+        if (slots[i] == -1 && root) return fail(c, HGB_E_INVALID, "build_level: the root cannot be skipped");
+        if (slots[i] == -1) count[i] = 0;   // skipped: none of its rows are read
     }
     {
-        std::vector<int32_t> sorted = slots;
+        std::vector<int32_t> sorted;
+        for (int32_t v : slots)
+            if (v >= 0) sorted.push_back(v);
         std::sort(sorted.begin(), sorted.end());
         if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
             return fail(c, HGB_E_INVALID, "build_level: two nodes share an output slot");
@@ -1262,6 +1275,124 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
                                                              (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");
     return HGB_OK;
+}
+
+hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
+                               int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
+                               int32_t* child_offsets, int32_t* n_children)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_data) return fail(c, HGB_E_STATE, "partition_level before upload_bins");
+    if (!splits || !child_offsets || !n_children)
+        return fail(c, HGB_E_INVALID, "partition_level: null pointer");
+    if (n_nodes < 1 || n_nodes > 65535)
+        return fail(c, HGB_E_INVALID, "partition_level: n_nodes must be in [1, 65535]");
+    const bool root = !row_index && !node_offsets;
+    if (row_index && !node_offsets)
+        return fail(c, HGB_E_INVALID, "partition_level: node_offsets required with row_index");
+    if (root && n_nodes != 1)
+        return fail(c, HGB_E_INVALID, "partition_level: the root (no row index) is one node");
+    std::vector<int32_t> offs(n_nodes + 1);
+    if (root) {
+        offs[0] = 0;
+        offs[1] = (int32_t)c->n;
+    } else {
+        if (node_offsets[0] != 0) return fail(c, HGB_E_INVALID, "partition_level: offsets must start at 0");
+        for (int i = 0; i <= n_nodes; ++i) {
+            offs[i] = node_offsets[i];
+            if (i > 0 && offs[i] < offs[i - 1])
+                return fail(c, HGB_E_INVALID, "partition_level: offsets decrease at node %d", i - 1);
+        }
+        if (!row_index && offs[n_nodes] != 0)
+            return fail(c, HGB_E_INVALID, "partition_level: row_index is NULL but the nodes hold rows");
+    }
+    if (offs[n_nodes] > 0 && !out_rows) return fail(c, HGB_E_INVALID, "partition_level: null output");
+    HGB_HIP(c, hipSetDevice(c->device));
+
+    // chunks of each node's rows, in node order
+    std::vector<PartItem> items;
+    std::vector<int32_t> first(n_nodes + 1);
+    for (int i = 0; i < n_nodes; ++i) {
+        first[i] = (int32_t)items.size();
+        for (int32_t b = offs[i]; b < offs[i + 1]; b += kPartChunk)
+            items.push_back({i, b, std::min(b + kPartChunk, offs[i + 1]), offs[i]});
+    }
+    first[n_nodes] = (int32_t)items.size();
+    const int64_t n_items = (int64_t)items.size();
+
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t off_first = up(items.size() * sizeof(PartItem));
+    const size_t off_offs = off_first + up(first.size() * sizeof(int32_t));
+    const size_t bytes = off_offs + offs.size() * sizeof(int32_t);
+    std::vector<uint8_t> blob(bytes, 0);
+    if (!items.empty()) std::memcpy(blob.data(), items.data(), items.size() * sizeof(PartItem));
+    std::memcpy(blob.data() + off_first, first.data(), first.size() * sizeof(int32_t));
+    std::memcpy(blob.data() + off_offs, offs.data(), offs.size() * sizeof(int32_t));
+
+    hgb_status st = grow(c, &c->part, &c->part_cap, 2 * n_items + 3 * (int64_t)n_nodes + 1);
+    if (st != HGB_OK) return st;
+    if (c->part_host_cap < 3 * (int64_t)n_nodes) {
+        if (c->part_host) HGB_HIP(c, hipHostFree(c->part_host));
+        c->part_host = nullptr;
+        c->part_host_cap = 0;
+        HGB_HIP(c, hipHostMalloc((void**)&c->part_host, sizeof(int32_t) * 3 * (size_t)n_nodes,
+                                 hipHostMallocDefault));
+        c->part_host_cap = 3 * (int64_t)n_nodes;
+    }
+    int32_t* cnt = c->part;
+    int32_t* left_base = c->part + n_items;
+    int32_t* node_out = c->part + 2 * n_items;
+
+    Stage* sg = nullptr;
+    st = stage_upload(c, blob.data(), bytes, &sg);
+    if (st != HGB_OK) return st;
+    const uint8_t* dev = (const uint8_t*)sg->dev;
+    const PartItem* items_dev = (const PartItem*)dev;
+    const SplitOut* sp = (const SplitOut*)splits;
+    {
+        ProfScope ps(c, HGB_KERNEL_PARTITION);
+        if (n_items > 0) {
+            if (c->bin_bytes == 1)
+                k_part_count<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->dev_words + 2);
+            else
+                k_part_count<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->dev_words + 2);
+            HGB_LAUNCHED(c, "k_part_count");
+        }
+        k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
+                                               (const int32_t*)(dev + off_offs), sp, n_nodes, left_base,
+                                               node_out);
+        HGB_LAUNCHED(c, "k_part_scan");
+        HGB_HIP(c, hipMemcpyAsync(c->part_host, node_out, sizeof(int32_t) * 3 * (size_t)n_nodes,
+                                  hipMemcpyDeviceToHost, c->stream));
+        if (n_items > 0) {
+            if (c->bin_bytes == 1)
+                k_part_scatter<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, left_base, node_out,
+                    out_rows, c->dev_words + 2);
+            else
+                k_part_scatter<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, left_base, node_out,
+                    out_rows, c->dev_words + 2);
+            HGB_LAUNCHED(c, "k_part_scatter");
+        }
+    }
+    st = stage_release(c, sg);
+    if (st != HGB_OK) return st;
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    int32_t nc = 0;
+    child_offsets[0] = 0;
+    for (int i = 0; i < n_nodes; ++i) {
+        if (!c->part_host[3 * i + 2]) continue;
+        const int32_t left = c->part_host[3 * i + 1];
+        child_offsets[nc + 1] = child_offsets[nc] + left;
+        child_offsets[nc + 2] = child_offsets[nc] + (offs[i + 1] - offs[i]);
+        nc += 2;
+    }
+    *n_children = nc;
+    return hgb_sync(c);   // reports a row index outside [0, n)
 }
 
 hgb_status hgb_profile_enable(hgb_ctx* c, int enable)

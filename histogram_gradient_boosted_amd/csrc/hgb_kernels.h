@@ -1198,4 +1198,180 @@ __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// partition_level: route each split node's rows to its two children, keeping
+// their order (a stable partition), children 2j / 2j + 1 of the j-th node with
+// a split.  Three passes over fixed-size chunks of each node's rows: count the
+// rows going left per chunk; scan the counts per node and the output extents
+// over nodes; scatter each row to its place.
+// ---------------------------------------------------------------------------
+constexpr int kPartChunk = 8192;
+
+struct PartItem {
+    int32_t node;
+    int32_t begin, end;   // positions [begin, end) of the node's rows
+    int32_t node_begin;   // the node's first position
+};
+
+__device__ inline bool part_left(int v, int n_bins, const SplitOut& sp)
+{
+    return v == n_bins ? sp.default_left != 0 : v <= sp.bin;
+}
+
+template <typename BinT>
+__device__ inline bool part_row(const BinT* __restrict__ col, int64_t n, int n_bins, const SplitOut& sp,
+                                int64_t r, uint32_t* __restrict__ err)
+{
+    if ((uint64_t)r >= (uint64_t)n) {   // skipped by the fill, routed right here
+        atomicOr(err, kErrRowIndex);
+        return false;
+    }
+    return part_left((int)col[r], n_bins, sp);
+}
+
+template <typename BinT>
+__global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
+                                                     const int32_t* __restrict__ row_index,
+                                                     const PartItem* __restrict__ items,
+                                                     const SplitOut* __restrict__ splits,
+                                                     int32_t* __restrict__ cnt, uint32_t* __restrict__ err)
+{
+    __shared__ int s_sum[1024 / kWave];
+    const PartItem it = items[blockIdx.x];
+    const SplitOut sp = splits[it.node];
+    int c = 0;
+    if (sp.feature >= 0) {
+        const BinT* col = bins + (int64_t)sp.feature * n;
+        for (int k = it.begin + (int)threadIdx.x; k < it.end; k += blockDim.x) {
+            const int64_t r = row_index ? (int64_t)row_index[k] : (int64_t)k;
+            c += part_row(col, n, n_bins, sp, r, err) ? 1 : 0;
+        }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) s_sum[threadIdx.x / kWave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int w = 0; w < (int)(blockDim.x / kWave); ++w) t += s_sum[w];
+        cnt[blockIdx.x] = t;
+    }
+}
+
+// Block-wide exclusive scan of v (blockDim.x values), returning this thread's
+// prefix; *total receives the sum.  Uses s[blockDim.x].
+__device__ inline int block_exclusive_scan(int v, int* s, int* total)
+{
+    s[threadIdx.x] = v;
+    __syncthreads();
+    for (int d = 1; d < (int)blockDim.x; d <<= 1) {
+        const int t = threadIdx.x >= (unsigned)d ? s[threadIdx.x - d] : 0;
+        __syncthreads();
+        s[threadIdx.x] += t;
+        __syncthreads();
+    }
+    const int incl = s[threadIdx.x];
+    *total = s[blockDim.x - 1];
+    __syncthreads();
+    return incl - v;
+}
+
+// One block.  left_base[item]: rows going left in the node's earlier chunks.
+// node_out[3 i + 0..2]: the node's first output position (its children's
+// rows follow those of earlier split nodes), its rows going left, and 1 when
+// it has a split.  The per-chunk counts are scanned across all chunks, then
+// rebased to each node's first chunk.
+__global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ cnt,
+                                                    const PartItem* __restrict__ items, int n_items,
+                                                    const int32_t* __restrict__ first_item,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const SplitOut* __restrict__ splits, int n_nodes,
+                                                    int32_t* __restrict__ left_base,
+                                                    int32_t* __restrict__ node_out)
+{
+    __shared__ int s_scan[1024];
+    int carry = 0, tot = 0;
+    for (int base = 0; base < n_items; base += blockDim.x) {   // exclusive scan of the counts
+        const int j = base + threadIdx.x;
+        const int v = j < n_items ? cnt[j] : 0;
+        const int ex = block_exclusive_scan(v, s_scan, &tot);
+        if (j < n_items) left_base[j] = carry + ex;
+        carry += tot;
+    }
+    const int all = carry;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_nodes; i += blockDim.x) {
+        const int f0 = first_item[i], f1 = first_item[i + 1];
+        const int e0 = f0 < n_items ? left_base[f0] : all;
+        const int e1 = f1 < n_items ? left_base[f1] : all;
+        node_out[3 * i] = e0;   // the node's base, for the rebase below
+        node_out[3 * i + 1] = e1 - e0;
+        node_out[3 * i + 2] = splits[i].feature >= 0 ? 1 : 0;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < n_items; j += blockDim.x) left_base[j] -= node_out[3 * items[j].node];
+    __syncthreads();
+    carry = 0;
+    for (int base = 0; base < n_nodes; base += blockDim.x) {   // output extents over nodes
+        const int i = base + threadIdx.x;
+        const int v = i < n_nodes && node_out[3 * i + 2] ? offsets[i + 1] - offsets[i] : 0;
+        const int ex = block_exclusive_scan(v, s_scan, &tot);
+        if (i < n_nodes) node_out[3 * i] = carry + ex;
+        carry += tot;
+    }
+}
+
+template <typename BinT>
+__global__ __launch_bounds__(1024) void k_part_scatter(const BinT* __restrict__ bins, int64_t n, int n_bins,
+                                                       const int32_t* __restrict__ row_index,
+                                                       const PartItem* __restrict__ items,
+                                                       const SplitOut* __restrict__ splits,
+                                                       const int32_t* __restrict__ left_base,
+                                                       const int32_t* __restrict__ node_out,
+                                                       int32_t* __restrict__ out_rows,
+                                                       uint32_t* __restrict__ err)
+{
+    __shared__ int s_l[1024 / kWave], s_r[1024 / kWave];
+    const PartItem it = items[blockIdx.x];
+    const SplitOut sp = splits[it.node];
+    if (sp.feature < 0) return;   // uniform: the node has no children
+    const BinT* col = bins + (int64_t)sp.feature * n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave;
+    const int lb = left_base[blockIdx.x];
+    int lpos = node_out[3 * it.node] + lb;
+    int rpos = node_out[3 * it.node] + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int k0 = it.begin; k0 < it.end; k0 += blockDim.x) {   // uniform
+        const int k = k0 + (int)threadIdx.x;
+        const bool valid = k < it.end;
+        int64_t r = 0;
+        bool left = false;
+        if (valid) {
+            r = row_index ? (int64_t)row_index[k] : (int64_t)k;
+            left = part_row(col, n, n_bins, sp, r, err);
+        }
+        const unsigned long long lm = __ballot(valid && left);
+        const unsigned long long rm = __ballot(valid && !left);
+        if (lane == 0) {
+            s_l[wv] = __popcll(lm);
+            s_r[wv] = __popcll(rm);
+        }
+        __syncthreads();
+        int lw = 0, rw = 0, lt = 0, rt = 0;
+        for (int w = 0; w < waves; ++w) {
+            if (w < wv) { lw += s_l[w]; rw += s_r[w]; }
+            lt += s_l[w];
+            rt += s_r[w];
+        }
+        if (valid) {
+            const int dst = left ? lpos + lw + __popcll(lm & below) : rpos + rw + __popcll(rm & below);
+            out_rows[dst] = (int32_t)r;
+        }
+        lpos += lt;
+        rpos += rt;
+        __syncthreads();
+    }
+}
+
 }  // namespace hgb

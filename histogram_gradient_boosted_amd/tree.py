@@ -156,3 +156,59 @@ def replay_tree(ctx: Context, plans: List[LevelPlan], grad, hess, lam: float, ga
     run_root(ctx, plans[0], lam, gamma)
     for prev, plan in zip(plans[:-1], plans[1:]):
         run_level(ctx, plan, prev.hist, lam, gamma)
+
+
+@dataclass
+class DeviceLevel:
+    """One level grown entirely on the device (grow_tree_device)."""
+    depth: int
+    n_nodes: int
+    rows: Optional[object]                 # CUDA int32: the nodes' rows (None: the root)
+    offsets: Optional[np.ndarray]          # host int32 [n_nodes + 1] (None: the root)
+    hist: object                           # CUDA int64 [n_nodes][F][S][2]
+    splits: object                         # CUDA uint8 [n_nodes * 56]
+    built_rows: int = 0
+
+
+def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: float) -> List[DeviceLevel]:
+    """Grow levels 0..depth-1 with the rows partitioned on the device.
+
+    Each level: hgb_partition_level lays out the children of the previous
+    level's split nodes (pair j = children 2j, 2j + 1); build_level builds the
+    smaller child of each pair from that layout (the other node's slot is -1,
+    so its rows are skipped); subtract_siblings derives the other; find_splits
+    scores every child.  Only the child sizes and the split records' feature
+    fields come back to the host (to size the next level and name each pair's
+    parent)."""
+    import torch
+    dev = torch.device("cuda", ctx.device)
+    F, S = ctx.n_features, ctx.n_slots
+    ctx.begin_tree(grad, hess)
+    hist = torch.empty((1, F, S, 2), dtype=torch.int64, device=dev)
+    sp = torch.empty(SPLIT_BYTES, dtype=torch.uint8, device=dev)
+    ctx.build_level(hist)
+    ctx.find_splits(hist, 1, lam, gamma, sp)
+    levels = [DeviceLevel(0, 1, None, None, hist, sp, ctx.n_rows)]
+    for d in range(1, depth):
+        prev = levels[-1]
+        total = ctx.n_rows if prev.rows is None else int(prev.offsets[-1])
+        out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        child = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
+        n_nodes = int(child.shape[0]) - 1
+        if n_nodes == 0:
+            break
+        split_nodes = np.nonzero(splits_to_numpy(prev.splits)[: prev.n_nodes]["feature"] >= 0)[0]
+        counts = np.diff(child)
+        bir = _choose_built(counts)
+        P = n_nodes // 2
+        slots = np.full(n_nodes, -1, dtype=np.int32)
+        built = 2 * np.arange(P) + bir
+        slots[built] = built
+        hist = torch.empty((n_nodes, F, S, 2), dtype=torch.int64, device=dev)
+        sp = torch.empty(n_nodes * SPLIT_BYTES, dtype=torch.uint8, device=dev)
+        ctx.build_level(hist, out, child, slots)
+        ctx.subtract_siblings(prev.hist, hist, bir, split_nodes.astype(np.int32))
+        ctx.find_splits(hist, n_nodes, lam, gamma, sp)
+        levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
+    ctx.sync()
+    return levels

@@ -147,9 +147,13 @@ hgb_status hgb_get_scales(const hgb_ctx* ctx, int32_t* k_g, int32_t* k_h);
  *                    0..n-1 in order.
  * hist_dev:          level buffer; node i's histogram is written, in full, at
  *                    node slot out_slot_host[i] (i when out_slot_host is NULL).
- *                    The caller sizes it to cover every slot written.
+ *                    A slot of -1 skips node i: its rows are not read and no
+ *                    slot is written (so a level laid out by
+ *                    hgb_partition_level builds only the smaller child of each
+ *                    pair).  The caller sizes hist_dev to cover every slot
+ *                    written.
  * Errors: HGB_E_STATE before begin_tree; HGB_E_INVALID for bad offsets, slots
- *         (negative, or two nodes on one slot) or n_nodes < 1.
+ *         (below -1, or two nodes on one slot) or n_nodes < 1.
  */
 hgb_status hgb_build_level(hgb_ctx* ctx, const int32_t* row_index_dev,
                            const int32_t* node_offsets_host, int32_t n_nodes,
@@ -194,6 +198,37 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
                            double lambda, double gamma, hgb_split* out_dev);
 
 /*
+ * Route every split node's rows to its children on the device ([bonsai-10]
+ * "The device context lifecycle": the level's rows are partitioned on the
+ * device and only split records cross the bus).  A row goes left when its
+ * stored value for the split feature is a value bin <= the split bin, or is
+ * the missing sentinel and default_left is set.  The partition is stable: rows
+ * keep their order within each child.  Nodes without a split (feature -1) get
+ * no children and their rows are dropped.  The children of the j-th node with
+ * a split (counting such nodes only, in node order) are 2j (left) and 2j + 1
+ * (right).
+ *
+ * row_index_dev, node_offsets_host, n_nodes: the level's nodes as for
+ *                       hgb_build_level (both NULL with n_nodes = 1: the root,
+ *                       rows 0..n-1).
+ * splits_dev:           hgb_split [n_nodes] (device), as find_splits writes them.
+ * out_row_index_dev:    int32, room for every row of the split nodes (at most
+ *                       node_offsets_host[n_nodes], or n for the root): the
+ *                       children's rows, concatenated in child order.
+ * child_offsets_host:   int32 [2 * n_nodes + 1]; on return [0, 2c] hold the
+ *                       children's offsets into out_row_index_dev.
+ * n_children_host:      on return, 2c for c nodes with a split.
+ * Synchronizes the stream (the host needs the child sizes).  A row index
+ * outside [0, n) is routed right and reported as HGB_E_INVALID by this call.
+ * Errors: HGB_E_STATE before upload_bins; HGB_E_INVALID for null pointers or
+ *         bad offsets, n_nodes outside [1, 65535].
+ */
+hgb_status hgb_partition_level(hgb_ctx* ctx, const int32_t* row_index_dev,
+                               const int32_t* node_offsets_host, int32_t n_nodes,
+                               const hgb_split* splits_dev, int32_t* out_row_index_dev,
+                               int32_t* child_offsets_host, int32_t* n_children_host);
+
+/*
  * Per-kernel device timing ([bonsai-10] "The kernel": the pages' backend
  * prints an upload / gpu / unpack breakdown when asked).  When enabled, every
  * launch is bracketed by HIP events on the context's stream.
@@ -205,7 +240,8 @@ typedef enum {
     HGB_KERNEL_FILL = 3,       /* build_level: LDS histogram fill + merge */
     HGB_KERNEL_SUBTRACT = 4,   /* subtract_siblings */
     HGB_KERNEL_SPLIT = 5,      /* find_splits (both kernels) */
-    HGB_KERNEL_COUNT = 6
+    HGB_KERNEL_PARTITION = 6,  /* partition_level (three kernels) */
+    HGB_KERNEL_COUNT = 7
 } hgb_kernel;
 
 /* Turn timing on (nonzero) or off, and reset the counters. */

@@ -1,0 +1,165 @@
+"""GPU parity of the device partition (hgb_partition_level) and of levels grown
+with it, against the oracle's partition and tree.  Row lists and offsets must
+be identical (the partition is stable, so there is exactly one answer)."""
+import numpy as np
+import pytest
+
+import oracle
+from histogram_gradient_boosted_amd import synth
+
+from test_gpu_parity import assert_splits, oracle_quantized, oracle_tree, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _torch
+    from histogram_gradient_boosted_amd import binding
+    if not _torch.cuda.is_available() or not binding.available():
+        pytest.skip("no HIP device")
+    return _torch
+
+
+@pytest.fixture(scope="module")
+def hgb(torch):
+    from histogram_gradient_boosted_amd import binding
+    return binding
+
+
+def splits_dev(torch, sp):
+    return torch.from_numpy(np.ascontiguousarray(sp).view(np.uint8).copy()).cuda()
+
+
+def gpu_partition(hgb, torch, w, sp, rows=None, offs=None):
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    total = w.n_rows if rows is None else int(offs[-1])
+    out = torch.full((max(total, 1),), -5, dtype=torch.int32, device="cuda")
+    ri = None if rows is None else torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int32)).cuda()
+    child = ctx.partition_level(splits_dev(torch, sp), out, ri,
+                                None if offs is None else np.asarray(offs, dtype=np.int32))
+    ctx.close()
+    return out.cpu().numpy()[: int(child[-1])], child
+
+
+SMALL = [
+    # seed, n, F, B, missing, children, u16
+    (60, 1, 2, 3, False, 0, None), (61, 5000, 4, 16, False, 0, None), (62, 9000, 3, 64, True, 0, None),
+    (63, 20000, 5, 256, False, 8, None), (64, 30000, 4, 300, True, 12, True),
+    (65, 17, 2, 4, True, 6, None), (66, 70000, 3, 1024, True, 6, True),
+]
+
+
+@pytest.mark.parametrize("seed,n,F,B,missing,children,u16", SMALL)
+def test_partition_vs_oracle(hgb, torch, seed, n, F, B, missing, children, u16):
+    """Splits from the oracle (some nodes forced to have none); the device
+    partition must reproduce the oracle's row lists and offsets exactly."""
+    say("partition", seed, n, F, B, missing, children)
+    w = synth.random_small(seed, n, F, B, missing, children, u16=u16)
+    qg, qh, kg, kh = oracle_quantized(w)
+    if children == 0:
+        rows, offs = None, None
+        hist = oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh)
+    else:
+        rows, offs = w.level.children_row_index, w.level.children_offsets
+        hist = oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh, rows, offs)
+    sp = oracle.find_splits(hist, w.n_bins, w.has_missing, kg, kh, w.lam, w.gamma)
+    if children >= 4:
+        sp["feature"][1] = -1   # a node without a split: its rows are dropped
+        sp["feature"][children - 1] = -1
+    want_rows, want_offs = oracle.partition(w.bins, w.n_bins, rows, offs, sp)
+    got_rows, got_offs = gpu_partition(hgb, torch, w, sp, rows, offs)
+    assert np.array_equal(got_offs.astype(np.int64), want_offs)
+    assert np.array_equal(got_rows, want_rows)
+
+
+def test_partition_every_direction(hgb, torch):
+    """Splits chosen by hand on every feature and bin edge, both default
+    directions, including bin n_bins - 1 (everything left) and missing rows."""
+    say("partition directions")
+    w = synth.random_small(67, 12_000, 3, 8, True, 18)
+    rows, offs = w.level.children_row_index, w.level.children_offsets
+    sp = np.zeros(18, dtype=oracle.SPLIT_DTYPE)
+    for i in range(18):   # every (feature, bin, default) of 3 x 3 x 2
+        sp[i]["feature"] = i % 3
+        sp[i]["bin"] = [0, 3, 7][(i // 3) % 3]
+        sp[i]["default_left"] = i // 9
+    want_rows, want_offs = oracle.partition(w.bins, w.n_bins, rows, offs, sp)
+    got_rows, got_offs = gpu_partition(hgb, torch, w, sp, rows, offs)
+    assert np.array_equal(got_offs.astype(np.int64), want_offs)
+    assert np.array_equal(got_rows, want_rows)
+
+
+def test_partition_no_splits(hgb, torch):
+    say("partition no splits")
+    w = synth.random_small(68, 3000, 2, 16, False, 4)
+    sp = np.zeros(4, dtype=oracle.SPLIT_DTYPE)
+    sp["feature"] = -1
+    rows, offs = w.level.children_row_index, w.level.children_offsets
+    got_rows, got_offs = gpu_partition(hgb, torch, w, sp, rows, offs)
+    assert got_offs.tolist() == [0] and got_rows.size == 0
+
+
+def test_partition_bad_row_index(hgb, torch):
+    say("partition bad row index")
+    w = synth.random_small(69, 1000, 2, 16, False, 0)
+    sp = np.zeros(1, dtype=oracle.SPLIT_DTYPE)
+    sp["feature"] = 0
+    sp["bin"] = 7
+    rows = np.arange(1000, dtype=np.int32)
+    rows[500] = 5000
+    with pytest.raises(hgb.HGBError) as e:
+        gpu_partition(hgb, torch, w, sp, rows, np.array([0, 1000]))
+    assert e.value.status == hgb.HGB_E_INVALID
+
+
+def test_build_level_skips_slot_minus_one(hgb, torch):
+    """Nodes with output slot -1 are not built and their slots not written."""
+    say("skip slots")
+    w = synth.random_small(70, 40_000, 4, 64, True, 8)
+    L = w.level
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    ctx.begin_tree(g, h)
+    slots = np.array([0, -1, 2, -1, -1, 5, 6, -1], dtype=np.int32)
+    t = torch.full((8, 4, 65, 2), -9, dtype=torch.int64, device="cuda")
+    ctx.build_level(t, torch.from_numpy(L.children_row_index).cuda(),
+                    L.children_offsets.astype(np.int32), slots)
+    ctx.sync()
+    got = t.cpu().numpy()
+    ctx.close()
+    qg, qh, _, _ = oracle_quantized(w)
+    want = oracle.build_hist(w.bins, w.n_bins, True, qg, qh, L.children_row_index, L.children_offsets)
+    for i, s in enumerate(slots):
+        if s >= 0:
+            assert np.array_equal(got[s], want[i]), f"node {i}"
+        else:
+            assert (got[i] == -9).all(), f"slot {i} was written"
+
+
+@pytest.mark.parametrize("n,bits", [(300_000, 30), (300_000, 19), (None, 30)])
+def test_c3_tree_device_partition(hgb, torch, n, bits):
+    """A whole c3 tree grown with the device partition equals the oracle's tree:
+    row lists, offsets, histograms and splits at every level."""
+    say("c3 device tree", n, bits)
+    from histogram_gradient_boosted_amd import tree
+    w = synth.make("c3", n_rows=n)
+    ctx = hgb.Context(0)
+    ctx.set_precision(bits)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    levels = tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+    want = oracle_tree(w, w.depth, bits)
+    assert len(levels) == len(want)
+    for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(levels, want)):
+        say("c3 device level", d)
+        if d > 0:
+            assert np.array_equal(lv.offsets.astype(np.int64), offs)
+            assert np.array_equal(lv.rows.cpu().numpy()[: int(offs[-1])], rows)
+        assert np.array_equal(lv.hist.cpu().numpy(), hist), f"level {d} histograms differ"
+        assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"level {d}")
+    ctx.close()
