@@ -102,6 +102,10 @@ def prepare(ctx, w, g, h, torch):
 
 def step(ctx, w, plan, g, h):
     from histogram_gradient_boosted_amd import tree
+    if getattr(plan, "grow", False):
+        # the whole level loop on the device: partition, build, subtract, split
+        tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        return
     if plan.tree is not None:
         tree.replay_tree(ctx, plan.tree, g, h, w.lam, w.gamma)
         return
@@ -222,6 +226,9 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--grow", action="store_true",
+                    help="tree workloads: grow the tree each step with the device partition "
+                         "(the level loop closed on the device) instead of replaying fixed row lists")
     ap.add_argument("--precision", type=int, default=30,
                     help="fixed-point bits P (k = P - e); 30 is the int64-cell default, "
                          "P <= 19 selects the packed one-atomic fill")
@@ -249,6 +256,11 @@ def main():
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
     plan = prepare(ctx, w, g, h, torch)
+    if args.grow:
+        if plan.tree is None:
+            print("--grow needs a tree workload (c3)", file=sys.stderr)
+            sys.exit(2)
+        plan.grow = True
     log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
 
     for _ in range(args.warmup):
@@ -316,6 +328,8 @@ def main():
                      "launches_per_step": fill_launches // max(args.steps, 1),
                      "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
         "precision_bits": args.precision,
+        "step": "grow: partition + build + subtract + split per level, on the device" if args.grow
+        else "replay: build + subtract + split per level on fixed row lists",
     }
     ctx.close()
     if not args.no_cpu_baseline:

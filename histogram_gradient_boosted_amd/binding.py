@@ -85,7 +85,7 @@ def load():
     lib.hgb_subtract_siblings.restype = c_int
     lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_splits.restype = c_int
-    lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32)]
+    lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32), vp]
     lib.hgb_partition_level.restype = c_int
     lib.hgb_profile_enable.argtypes = [vp, c_int]
     lib.hgb_profile_enable.restype = c_int
@@ -259,8 +259,9 @@ class Context:
         """Children's rows of every split node into `out_rows` (int32 CUDA tensor).
 
         `splits`: the level's hgb_split records (uint8 CUDA tensor, as
-        find_splits writes them).  Returns the children's offsets (int32 numpy
-        array, 2c + 1 entries for c nodes with a split)."""
+        find_splits writes them).  Returns (children's offsets, parents): int32
+        numpy arrays of 2c + 1 and c entries for c nodes with a split, parent j
+        being the node whose children are 2j and 2j + 1."""
         torch = self._torch
         if row_index is None:
             n_nodes, offs, ri, total = 1, None, None, self.n_rows
@@ -272,11 +273,13 @@ class Context:
         sp = self._dev(splits, "splits", torch.uint8, n_nodes * SPLIT_BYTES)
         op = self._dev(out_rows, "out_rows", torch.int32, total) if total else None
         child = np.zeros(2 * n_nodes + 1, dtype=np.int32)
+        parent = np.zeros(n_nodes, dtype=np.int32)
         nc = ctypes.c_int32(0)
         self._check(self._lib.hgb_partition_level(
             self._h, ri, None if offs is None else offs.ctypes.data_as(ctypes.c_void_p), n_nodes,
-            sp, op, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc)), "partition_level")
-        return child[: nc.value + 1].copy()
+            sp, op, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc),
+            parent.ctypes.data_as(ctypes.c_void_p)), "partition_level")
+        return child[: nc.value + 1].copy(), parent[: nc.value // 2].copy()
 
     def find_splits(self, hist, n_nodes: int, lam: float, gamma: float, out):
         """out: uint8 CUDA tensor of at least n_nodes * 56 bytes (hgb_split records)."""

@@ -90,6 +90,8 @@ struct hgb_ctx {
     int64_t part_cap = 0;
     int32_t* part_host = nullptr;   // pinned copy of the per-node records
     int64_t part_host_cap = 0;
+    uint8_t* part_flags = nullptr;  // partition: direction of each position (1 = left)
+    int64_t part_flags_cap = 0;
     FeatureBest* best = nullptr;
     int64_t best_cap = 0;
     long long* totals = nullptr;
@@ -847,6 +849,7 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipFree(c->gh);
     (void)hipFree(c->partial);
     (void)hipFree(c->part);
+    (void)hipFree(c->part_flags);
     if (c->part_host) (void)hipHostFree(c->part_host);
     (void)hipFree(c->best);
     (void)hipFree(c->totals);
@@ -1279,7 +1282,7 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
 
 hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
                                int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
-                               int32_t* child_offsets, int32_t* n_children)
+                               int32_t* child_offsets, int32_t* n_children, int32_t* parent_node)
 {
     if (!c) return HGB_E_INVALID;
     c->err.clear();
@@ -1340,6 +1343,8 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
                                  hipHostMallocDefault));
         c->part_host_cap = 3 * (int64_t)n_nodes;
     }
+    st = grow(c, &c->part_flags, &c->part_flags_cap, std::max<int64_t>(offs[n_nodes], 1));
+    if (st != HGB_OK) return st;
     int32_t* cnt = c->part;
     int32_t* left_base = c->part + n_items;
     int32_t* node_out = c->part + 2 * n_items;
@@ -1355,10 +1360,12 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         if (n_items > 0) {
             if (c->bin_bytes == 1)
                 k_part_count<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->dev_words + 2);
+                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->part_flags,
+                    c->dev_words + 2);
             else
                 k_part_count<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->dev_words + 2);
+                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->part_flags,
+                    c->dev_words + 2);
             HGB_LAUNCHED(c, "k_part_count");
         }
         k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
@@ -1368,14 +1375,8 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         HGB_HIP(c, hipMemcpyAsync(c->part_host, node_out, sizeof(int32_t) * 3 * (size_t)n_nodes,
                                   hipMemcpyDeviceToHost, c->stream));
         if (n_items > 0) {
-            if (c->bin_bytes == 1)
-                k_part_scatter<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, left_base, node_out,
-                    out_rows, c->dev_words + 2);
-            else
-                k_part_scatter<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, left_base, node_out,
-                    out_rows, c->dev_words + 2);
+            k_part_scatter<<<(unsigned)n_items, 1024, 0, c->stream>>>(row_index, items_dev, sp, c->part_flags,
+                                                                      left_base, node_out, out_rows);
             HGB_LAUNCHED(c, "k_part_scatter");
         }
     }
@@ -1389,6 +1390,7 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         const int32_t left = c->part_host[3 * i + 1];
         child_offsets[nc + 1] = child_offsets[nc] + left;
         child_offsets[nc + 2] = child_offsets[nc] + (offs[i + 1] - offs[i]);
+        if (parent_node) parent_node[nc / 2] = i;
         nc += 2;
     }
     *n_children = nc;

@@ -1218,34 +1218,54 @@ __device__ inline bool part_left(int v, int n_bins, const SplitOut& sp)
     return v == n_bins ? sp.default_left != 0 : v <= sp.bin;
 }
 
-template <typename BinT>
-__device__ inline bool part_row(const BinT* __restrict__ col, int64_t n, int n_bins, const SplitOut& sp,
-                                int64_t r, uint32_t* __restrict__ err)
-{
-    if ((uint64_t)r >= (uint64_t)n) {   // skipped by the fill, routed right here
-        atomicOr(err, kErrRowIndex);
-        return false;
-    }
-    return part_left((int)col[r], n_bins, sp);
-}
+// Each thread takes kPartRows consecutive positions of its chunk (1024
+// threads x kPartRows = kPartChunk), loads issued independently and clamped
+// into the chunk.
+constexpr int kPartRows = 8;
+static_assert(kPartChunk == 1024 * kPartRows, "a chunk is one pass of a 1024-thread block");
 
+// Count the rows going left per chunk, and record each position's direction
+// (1 = left) for the scatter.
 template <typename BinT>
 __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
                                                      const int32_t* __restrict__ row_index,
                                                      const PartItem* __restrict__ items,
                                                      const SplitOut* __restrict__ splits,
-                                                     int32_t* __restrict__ cnt, uint32_t* __restrict__ err)
+                                                     int32_t* __restrict__ cnt, uint8_t* __restrict__ flags,
+                                                     uint32_t* __restrict__ err)
 {
     __shared__ int s_sum[1024 / kWave];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     int c = 0;
-    if (sp.feature >= 0) {
+    if (sp.feature >= 0) {   // uniform
         const BinT* col = bins + (int64_t)sp.feature * n;
-        for (int k = it.begin + (int)threadIdx.x; k < it.end; k += blockDim.x) {
-            const int64_t r = row_index ? (int64_t)row_index[k] : (int64_t)k;
-            c += part_row(col, n, n_bins, sp, r, err) ? 1 : 0;
+        const int k0 = it.begin + (int)threadIdx.x * kPartRows;
+        int64_t r[kPartRows];
+#pragma unroll
+        for (int j = 0; j < kPartRows; ++j) {
+            const int kc = min(k0 + j, it.end - 1);
+            r[j] = row_index ? (int64_t)row_index[kc] : (int64_t)kc;
         }
+        int v[kPartRows];
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < kPartRows; ++j) {
+            const bool in = (uint64_t)r[j] < (uint64_t)n;
+            bad |= !in && k0 + j < it.end;
+            v[j] = (int)col[in ? r[j] : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < kPartRows; ++j) {
+            const int k = k0 + j;
+            // a row index outside [0, n) is routed right (and reported)
+            const bool left = (uint64_t)r[j] < (uint64_t)n && part_left(v[j], n_bins, sp);
+            if (k < it.end) {
+                c += left ? 1 : 0;
+                flags[k] = left ? 1 : 0;
+            }
+        }
+        if (bad) atomicOr(err, kErrRowIndex);
     }
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     if ((threadIdx.x & (kWave - 1)) == 0) s_sum[threadIdx.x / kWave] = c;
@@ -1320,58 +1340,49 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
     }
 }
 
-template <typename BinT>
-__global__ __launch_bounds__(1024) void k_part_scatter(const BinT* __restrict__ bins, int64_t n, int n_bins,
-                                                       const int32_t* __restrict__ row_index,
+// Write each row to its place: the chunk's left rows from its left base on,
+// its right rows from its right base on, in order.  One pass per chunk: the
+// thread's left and right counts are scanned across the block together (as
+// left + right * 2^16; a chunk holds at most kPartChunk < 2^16 rows).
+__global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict__ row_index,
                                                        const PartItem* __restrict__ items,
                                                        const SplitOut* __restrict__ splits,
+                                                       const uint8_t* __restrict__ flags,
                                                        const int32_t* __restrict__ left_base,
                                                        const int32_t* __restrict__ node_out,
-                                                       int32_t* __restrict__ out_rows,
-                                                       uint32_t* __restrict__ err)
+                                                       int32_t* __restrict__ out_rows)
 {
-    __shared__ int s_l[1024 / kWave], s_r[1024 / kWave];
+    __shared__ int s_scan[1024];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     if (sp.feature < 0) return;   // uniform: the node has no children
-    const BinT* col = bins + (int64_t)sp.feature * n;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    const int waves = blockDim.x / kWave;
-    const int lb = left_base[blockIdx.x];
-    int lpos = node_out[3 * it.node] + lb;
-    int rpos = node_out[3 * it.node] + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb);
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int k0 = it.begin; k0 < it.end; k0 += blockDim.x) {   // uniform
-        const int k = k0 + (int)threadIdx.x;
-        const bool valid = k < it.end;
-        int64_t r = 0;
-        bool left = false;
-        if (valid) {
-            r = row_index ? (int64_t)row_index[k] : (int64_t)k;
-            left = part_row(col, n, n_bins, sp, r, err);
-        }
-        const unsigned long long lm = __ballot(valid && left);
-        const unsigned long long rm = __ballot(valid && !left);
-        if (lane == 0) {
-            s_l[wv] = __popcll(lm);
-            s_r[wv] = __popcll(rm);
-        }
-        __syncthreads();
-        int lw = 0, rw = 0, lt = 0, rt = 0;
-        for (int w = 0; w < waves; ++w) {
-            if (w < wv) { lw += s_l[w]; rw += s_r[w]; }
-            lt += s_l[w];
-            rt += s_r[w];
-        }
-        if (valid) {
-            const int dst = left ? lpos + lw + __popcll(lm & below) : rpos + rw + __popcll(rm & below);
-            out_rows[dst] = (int32_t)r;
-        }
-        lpos += lt;
-        rpos += rt;
-        __syncthreads();
+    const int k0 = it.begin + (int)threadIdx.x * kPartRows;
+    int32_t r[kPartRows];
+    uint8_t f[kPartRows];
+#pragma unroll
+    for (int j = 0; j < kPartRows; ++j) {
+        const int kc = min(k0 + j, it.end - 1);
+        r[j] = row_index ? row_index[kc] : kc;
+        f[j] = flags[kc];
     }
+    int nl = 0, nr = 0;
+#pragma unroll
+    for (int j = 0; j < kPartRows; ++j)
+        if (k0 + j < it.end) {
+            nl += f[j];
+            nr += 1 - f[j];
+        }
+    int tot;
+    const int ex = block_exclusive_scan(nl + (nr << 16), s_scan, &tot);
+    const int lb = left_base[blockIdx.x];
+    int lpos = node_out[3 * it.node] + lb + (ex & 0xffff);
+    int rpos = node_out[3 * it.node] + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb) + (ex >> 16);
+#pragma unroll
+    for (int j = 0; j < kPartRows; ++j)
+        if (k0 + j < it.end) {
+            if (f[j]) out_rows[lpos++] = r[j];
+            else out_rows[rpos++] = r[j];
+        }
 }
 
 }  // namespace hgb

@@ -177,9 +177,8 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
     level's split nodes (pair j = children 2j, 2j + 1); build_level builds the
     smaller child of each pair from that layout (the other node's slot is -1,
     so its rows are skipped); subtract_siblings derives the other; find_splits
-    scores every child.  Only the child sizes and the split records' feature
-    fields come back to the host (to size the next level and name each pair's
-    parent)."""
+    scores every child.  Only the child sizes and each pair's parent come back
+    to the host (to size and plan the next level)."""
     import torch
     dev = torch.device("cuda", ctx.device)
     F, S = ctx.n_features, ctx.n_slots
@@ -193,11 +192,10 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
         prev = levels[-1]
         total = ctx.n_rows if prev.rows is None else int(prev.offsets[-1])
         out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
-        child = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
+        child, split_nodes = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
         n_nodes = int(child.shape[0]) - 1
         if n_nodes == 0:
             break
-        split_nodes = np.nonzero(splits_to_numpy(prev.splits)[: prev.n_nodes]["feature"] >= 0)[0]
         counts = np.diff(child)
         bir = _choose_built(counts)
         P = n_nodes // 2

@@ -218,6 +218,8 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
  * child_offsets_host:   int32 [2 * n_nodes + 1]; on return [0, 2c] hold the
  *                       children's offsets into out_row_index_dev.
  * n_children_host:      on return, 2c for c nodes with a split.
+ * parent_node_host:     int32 [n_nodes] or NULL; on return entry j holds the
+ *                       node whose children are 2j and 2j + 1.
  * Synchronizes the stream (the host needs the child sizes).  A row index
  * outside [0, n) is routed right and reported as HGB_E_INVALID by this call.
  * Errors: HGB_E_STATE before upload_bins; HGB_E_INVALID for null pointers or
@@ -226,7 +228,8 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
 hgb_status hgb_partition_level(hgb_ctx* ctx, const int32_t* row_index_dev,
                                const int32_t* node_offsets_host, int32_t n_nodes,
                                const hgb_split* splits_dev, int32_t* out_row_index_dev,
-                               int32_t* child_offsets_host, int32_t* n_children_host);
+                               int32_t* child_offsets_host, int32_t* n_children_host,
+                               int32_t* parent_node_host);
 
 /*
  * Per-kernel device timing ([bonsai-10] "The kernel": the pages' backend

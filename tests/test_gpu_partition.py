@@ -37,9 +37,10 @@ def gpu_partition(hgb, torch, w, sp, rows=None, offs=None):
     total = w.n_rows if rows is None else int(offs[-1])
     out = torch.full((max(total, 1),), -5, dtype=torch.int32, device="cuda")
     ri = None if rows is None else torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int32)).cuda()
-    child = ctx.partition_level(splits_dev(torch, sp), out, ri,
-                                None if offs is None else np.asarray(offs, dtype=np.int32))
+    child, parent = ctx.partition_level(splits_dev(torch, sp), out, ri,
+                                        None if offs is None else np.asarray(offs, dtype=np.int32))
     ctx.close()
+    assert np.array_equal(parent, np.nonzero(np.asarray(sp)["feature"] >= 0)[0])
     return out.cpu().numpy()[: int(child[-1])], child
 
 
