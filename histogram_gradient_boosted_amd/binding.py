@@ -32,7 +32,8 @@ SPLIT_BYTES = 56
 EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb_sync",
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
             "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
-            "hgb_profile_query", "hgb_set_precision", "hgb_partition_level")
+            "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
+            "hgb_subtract_find_splits")
 
 KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5,
            "partition": 6}
@@ -87,6 +88,9 @@ def load():
     lib.hgb_find_splits.restype = c_int
     lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32), vp]
     lib.hgb_partition_level.restype = c_int
+    lib.hgb_subtract_find_splits.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_double,
+                                             ctypes.c_double, vp]
+    lib.hgb_subtract_find_splits.restype = c_int
     lib.hgb_profile_enable.argtypes = [vp, c_int]
     lib.hgb_profile_enable.restype = c_int
     lib.hgb_profile_query.argtypes = [vp, c_int, ctypes.POINTER(ctypes.c_double),
@@ -254,6 +258,24 @@ class Context:
         self._check(self._lib.hgb_subtract_siblings(
             self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
             None if ps is None else ps.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings")
+
+    def subtract_find_splits(self, parent, child, built_is_right, lam: float, gamma: float, out,
+                             parent_slot=None):
+        """subtract_siblings then find_splits over the 2P children, in one pass."""
+        torch = self._torch
+        bir = np.ascontiguousarray(np.asarray(built_is_right), dtype=np.uint8)
+        P = int(bir.shape[0])
+        ps = None if parent_slot is None else _i32_host(parent_slot)
+        if ps is not None and ps.shape[0] != P:
+            raise ValueError("parent_slot must have one entry per pair")
+        ptop = (int(ps.max()) + 1) if ps is not None and P else P
+        pp = self._dev(parent, "parent", torch.int64, ptop * self.node_elems)
+        cp = self._dev(child, "child", torch.int64, 2 * P * self.node_elems)
+        op = self._dev(out, "out", torch.uint8, 2 * P * SPLIT_BYTES)
+        self._check(self._lib.hgb_subtract_find_splits(
+            self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
+            None if ps is None else ps.ctypes.data_as(ctypes.c_void_p), P, float(lam), float(gamma),
+            op), "subtract_find_splits")
 
     def partition_level(self, splits, out_rows, row_index=None, node_offsets=None):
         """Children's rows of every split node into `out_rows` (int32 CUDA tensor).

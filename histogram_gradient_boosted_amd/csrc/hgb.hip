@@ -1280,6 +1280,72 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     return HGB_OK;
 }
 
+hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* child,
+                                    const uint8_t* built_is_right, const int32_t* parent_slot,
+                                    int32_t n_pairs, double lambda, double gamma, hgb_split* out)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "subtract_find_splits before begin_tree");
+    if (n_pairs < 0 || n_pairs > 32767)
+        return fail(c, HGB_E_INVALID, "subtract_find_splits: n_pairs out of range");
+    if (!(lambda >= 0.0) || !std::isfinite(lambda) || !std::isfinite(gamma))
+        return fail(c, HGB_E_INVALID, "subtract_find_splits: lambda must be finite and >= 0, gamma finite");
+    if (n_pairs == 0) return HGB_OK;
+    if (!parent || !child || !built_is_right || !out)
+        return fail(c, HGB_E_INVALID, "subtract_find_splits: null pointer");
+    const int per = (c->B + kWave - 1) / kWave;
+    const bool aligned = ((uintptr_t)parent & 15) == 0 && ((uintptr_t)child & 15) == 0;
+    if (!aligned || per > 16) {   // the two passes
+        hgb_status st = hgb_subtract_siblings(c, parent, child, built_is_right, parent_slot, n_pairs);
+        if (st != HGB_OK) return st;
+        return hgb_find_splits(c, child, 2 * n_pairs, lambda, gamma, out);
+    }
+    std::vector<int32_t> plan(2 * (size_t)n_pairs);
+    for (int i = 0; i < n_pairs; ++i) {
+        const int32_t ps = parent_slot ? parent_slot[i] : i;
+        if (ps < 0) return fail(c, HGB_E_INVALID, "subtract_find_splits: negative parent slot");
+        plan[2 * i] = ps;
+        plan[2 * i + 1] = built_is_right[i] ? 1 : 0;
+    }
+    HGB_HIP(c, hipSetDevice(c->device));
+    const int n_nodes = 2 * n_pairs;
+    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * c->F);
+    if (st != HGB_OK) return st;
+    st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
+    if (st != HGB_OK) return st;
+    SubtractInline inl{};
+    Stage* s = nullptr;
+    const int32_t* plan_dev = nullptr;
+    if (n_pairs <= kSubtractInlinePairs) {
+        std::memcpy(inl.v, plan.data(), plan.size() * sizeof(int32_t));
+    } else {
+        st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
+        if (st != HGB_OK) return st;
+        plan_dev = (const int32_t*)s->dev;
+    }
+    const int waves = 4;
+    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_pairs);
+    const double sg = std::ldexp(1.0, -c->k_g), sh = std::ldexp(1.0, -c->k_h);
+    {
+        ProfScope ps(c, HGB_KERNEL_SPLIT);
+#define HGB_SUBSPLIT(PER)                                                                          \
+    k_subtract_split<PER><<<grid, waves * kWave, 0, c->stream>>>(                                  \
+        (const long long*)parent, (long long*)child, plan_dev, inl, c->F, c->B, c->S, c->has_missing, \
+        sg, sh, lambda, gamma, c->best, c->totals)
+        if (per <= 1) HGB_SUBSPLIT(1);
+        else if (per <= 2) HGB_SUBSPLIT(2);
+        else if (per <= 4) HGB_SUBSPLIT(4);
+        else if (per <= 8) HGB_SUBSPLIT(8);
+        else HGB_SUBSPLIT(16);
+#undef HGB_SUBSPLIT
+        HGB_LAUNCHED(c, "k_subtract_split");
+        k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F, (SplitOut*)out);
+        HGB_LAUNCHED(c, "k_split_reduce");
+    }
+    return s ? stage_release(c, s) : HGB_OK;
+}
+
 hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
                                int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
                                int32_t* child_offsets, int32_t* n_children, int32_t* parent_node)

@@ -1006,43 +1006,53 @@ struct WaveBest {
     long long G, H;   // the feature's slot sums: the node totals
 };
 
-// PER > 0: the lane's PER slots are read once, 16 bytes at a time, into
-// registers (PER >= ceil(n_bins / 64)); PER == 0: any bin count, two passes
-// over memory.
+// A lane's value slots [lane * PER, lane * PER + PER) (zeros past n_bins) and
+// the feature's missing slot, held in registers.
 template <int PER>
-__device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, int n_bins,
-                                             int has_missing, double scale_g, double scale_h,
-                                             double lam, double gamma)
+struct LaneSlots {
+    longlong2 v[PER > 0 ? PER : 1];
+    longlong2 miss;
+};
+
+// Read the lane's slots, 16 bytes at a time (PER > 0; the buffer 16-byte
+// aligned), or only the missing slot (PER == 0: the scan reads memory).
+template <int PER>
+__device__ inline void load_lane_slots(const long long* __restrict__ hf, int n_bins, int has_missing,
+                                       LaneSlots<PER>& s)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (PER > 0) {
+        const longlong2* h2 = (const longlong2*)hf;
+        const int b0 = lane * PER;
+        const int b1 = min(b0 + PER, n_bins);
+#pragma unroll
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) {
+            const int b = b0 + j;
+            const longlong2 t = h2[min(b, n_bins - 1)];   // unconditional, masked below
+            s.v[j] = b < b1 ? t : make_longlong2(0, 0);
+        }
+    }
+    s.miss = has_missing ? make_longlong2(hf[2 * n_bins], hf[2 * n_bins + 1]) : make_longlong2(0, 0);
+}
+
+// The wave's best (bin, direction) of one feature: a lane-contiguous prefix
+// scan of the value slots, the gain of every candidate, a wave argmax.  Every
+// lane returns the result (gain -inf and code -1 when no candidate).  PER > 0
+// scans the registers in s; PER == 0 reads the slots from hf (any bin count).
+template <int PER>
+__device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins,
+                                     int has_missing, double scale_g, double scale_h, double lam,
+                                     double gamma)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int per = PER > 0 ? PER : (n_bins + kWave - 1) / kWave;
     const int b0 = lane * per;
     const int b1 = min(b0 + per, n_bins);
-    longlong2 v[PER > 0 ? PER : 1];
-    if (PER > 0) {
-        const longlong2* h2 = (const longlong2*)hf;
-#pragma unroll
-        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) {
-            const int b = b0 + j;
-            const longlong2 t = h2[min(b, n_bins - 1)];   // unconditional, masked below
-            v[j] = b < b1 ? t : make_longlong2(0, 0);
-        }
-    }
-    auto slot = [&](int b) -> longlong2 {
-        if (PER > 0) {
-            longlong2 r = make_longlong2(0, 0);
-#pragma unroll
-            for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
-                if (b - b0 == j) r = v[j];
-            return r;
-        }
-        return make_longlong2(hf[2 * b], hf[2 * b + 1]);
-    };
 
     long long sg = 0, sh = 0;
     if (PER > 0) {
 #pragma unroll
-        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) { sg += v[j].x; sh += v[j].y; }
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j) { sg += s.v[j].x; sh += s.v[j].y; }
     } else {
         for (int b = b0; b < b1; ++b) { sg += hf[2 * b]; sh += hf[2 * b + 1]; }
     }
@@ -1053,8 +1063,8 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
         long long th = wave_shfl_up_i64(ih, d);
         if (lane >= d) { ig += tg; ih += th; }
     }
-    const long long miss_g = has_missing ? hf[2 * n_bins] : 0;
-    const long long miss_h = has_missing ? hf[2 * n_bins + 1] : 0;
+    const long long miss_g = s.miss.x;
+    const long long miss_h = s.miss.y;
     const long long G = wave_shfl_i64(ig, kWave - 1) + miss_g;
     const long long H = wave_shfl_i64(ih, kWave - 1) + miss_h;
     const double g = (double)G * scale_g;
@@ -1089,9 +1099,9 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
     if (PER > 0) {
 #pragma unroll
         for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
-            if (b0 + j < b1) visit(b0 + j, v[j]);
+            if (b0 + j < b1) visit(b0 + j, s.v[j]);
     } else {
-        for (int b = b0; b < b1; ++b) visit(b, slot(b));
+        for (int b = b0; b < b1; ++b) visit(b, make_longlong2(hf[2 * b], hf[2 * b + 1]));
     }
     // wave argmax over (gain, code)
     int src = lane;
@@ -1116,6 +1126,16 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
     return r;
 }
 
+template <int PER>
+__device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, int n_bins,
+                                             int has_missing, double scale_g, double scale_h,
+                                             double lam, double gamma)
+{
+    LaneSlots<PER> s;
+    load_lane_slots<PER>(hf, n_bins, has_missing, s);
+    return wave_scan<PER>(hf, s, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+}
+
 // One wave per (node, feature), results to best[node][feature]; node totals
 // from feature 0.
 template <int PER>
@@ -1135,6 +1155,57 @@ __global__ __launch_bounds__(256) void k_split_feature(const long long* __restri
     if (lane == 0) {
         best[(int64_t)node * n_features + f] = r.fb;
         if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }
+    }
+}
+
+// The level tail in one pass: one wave per (pair, feature) reads the parent
+// and the built child, writes the other child (parent - built) and scans both
+// children, so the children are not read again by a separate split pass.
+template <int PER>
+__global__ __launch_bounds__(256) void k_subtract_split(const long long* __restrict__ parent,
+                                                        long long* __restrict__ child,
+                                                        const int32_t* __restrict__ plan,
+                                                        const SubtractInline inl, int n_features,
+                                                        int n_bins, int S, int has_missing,
+                                                        double scale_g, double scale_h, double lam,
+                                                        double gamma, FeatureBest* __restrict__ best,
+                                                        long long* __restrict__ totals)
+{
+    static_assert(PER > 0, "the fused pass keeps the slots in registers");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int pair = blockIdx.y;
+    if (f >= n_features) return;
+    const int32_t pslot = plan ? plan[2 * pair] : inl.v[2 * pair];
+    const int r = plan ? plan[2 * pair + 1] : inl.v[2 * pair + 1];
+    const int nb = 2 * pair + r, no = 2 * pair + 1 - r;
+    const int64_t fs = (int64_t)S * 2;
+    const long long* hp = parent + ((int64_t)pslot * n_features + f) * fs;
+    const long long* hb = child + ((int64_t)nb * n_features + f) * fs;
+    long long* ho = child + ((int64_t)no * n_features + f) * fs;
+    LaneSlots<PER> sp, sb, so;
+    load_lane_slots<PER>(hp, n_bins, has_missing, sp);
+    load_lane_slots<PER>(hb, n_bins, has_missing, sb);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(sp.v[j].x - sb.v[j].x, sp.v[j].y - sb.v[j].y);
+    so.miss = make_longlong2(sp.miss.x - sb.miss.x, sp.miss.y - sb.miss.y);
+    longlong2* o2 = (longlong2*)ho;
+    const int b0 = lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (b0 + j < n_bins) o2[b0 + j] = so.v[j];
+    if (has_missing && lane == 0) o2[n_bins] = so.miss;
+    const WaveBest wb = wave_scan<PER>(hb, sb, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+    const WaveBest wo = wave_scan<PER>(ho, so, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+    if (lane == 0) {
+        best[(int64_t)nb * n_features + f] = wb.fb;
+        best[(int64_t)no * n_features + f] = wo.fb;
+        if (f == 0) {
+            totals[2 * nb] = wb.G;
+            totals[2 * nb + 1] = wb.H;
+            totals[2 * no] = wo.G;
+            totals[2 * no + 1] = wo.H;
+        }
     }
 }
 

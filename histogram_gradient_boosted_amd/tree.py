@@ -122,12 +122,13 @@ def run_root(ctx: Context, plan: LevelPlan, lam: float, gamma: float):
 
 
 def run_level(ctx: Context, plan: LevelPlan, parent_hist, lam: float, gamma: float):
-    """Build the smaller siblings, subtract for the others, find every split."""
+    """Build the smaller siblings, then subtract for the others and find every
+    split in one pass."""
     if plan.n_nodes == 0:
         return
     ctx.build_level(plan.hist, plan.row_index, plan.offsets, plan.out_slot)
-    ctx.subtract_siblings(parent_hist, plan.hist, plan.built_is_right, plan.parent_slot)
-    ctx.find_splits(plan.hist, plan.n_nodes, lam, gamma, plan.splits)
+    ctx.subtract_find_splits(parent_hist, plan.hist, plan.built_is_right, lam, gamma, plan.splits,
+                             plan.parent_slot)
 
 
 def plan_tree(ctx: Context, bins_host: np.ndarray, n_bins: int, grad, hess, depth: int,
@@ -176,8 +177,8 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
     Each level: hgb_partition_level lays out the children of the previous
     level's split nodes (pair j = children 2j, 2j + 1); build_level builds the
     smaller child of each pair from that layout (the other node's slot is -1,
-    so its rows are skipped); subtract_siblings derives the other; find_splits
-    scores every child.  Only the child sizes and each pair's parent come back
+    so its rows are skipped); subtract_find_splits derives the other and scores
+    every child.  Only the child sizes and each pair's parent come back
     to the host (to size and plan the next level)."""
     import torch
     dev = torch.device("cuda", ctx.device)
@@ -205,8 +206,7 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
         hist = torch.empty((n_nodes, F, S, 2), dtype=torch.int64, device=dev)
         sp = torch.empty(n_nodes * SPLIT_BYTES, dtype=torch.uint8, device=dev)
         ctx.build_level(hist, out, child, slots)
-        ctx.subtract_siblings(prev.hist, hist, bir, split_nodes.astype(np.int32))
-        ctx.find_splits(hist, n_nodes, lam, gamma, sp)
+        ctx.subtract_find_splits(prev.hist, hist, bir, lam, gamma, sp, split_nodes.astype(np.int32))
         levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
     ctx.sync()
     return levels

@@ -198,6 +198,18 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
                            double lambda, double gamma, hgb_split* out_dev);
 
 /*
+ * subtract_siblings followed by find_splits over the 2 * n_pairs children, in
+ * one pass over the histograms: the result (the other children written, one
+ * hgb_split per child in out_dev) is exactly that of the two calls.  Arguments
+ * as for those calls; out_dev holds 2 * n_pairs records.
+ * Errors: as for subtract_siblings and find_splits.
+ */
+hgb_status hgb_subtract_find_splits(hgb_ctx* ctx, const int64_t* parent_dev, int64_t* child_dev,
+                                    const uint8_t* built_is_right_host,
+                                    const int32_t* parent_slot_host, int32_t n_pairs,
+                                    double lambda, double gamma, hgb_split* out_dev);
+
+/*
  * Route every split node's rows to its children on the device ([bonsai-10]
  * "The device context lifecycle": the level's rows are partitioned on the
  * device and only split records cross the bus).  A row goes left when its

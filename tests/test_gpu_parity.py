@@ -76,8 +76,9 @@ def gpu_splits(hgb, ctx, hist_t, n_nodes, lam, gamma, torch):
     return hgb.splits_to_numpy(out)[:n_nodes]
 
 
-def run_level_both(hgb, torch, w, check_exact_gain=False, bits=30):
-    """Parents + built children + subtraction + splits on the GPU vs the oracle."""
+def run_level_both(hgb, torch, w, check_exact_gain=False, bits=30, fused=False):
+    """Parents + built children + subtraction + splits on the GPU vs the oracle
+    (fused: subtraction and splits through subtract_find_splits)."""
     L = w.level
     ctx, g, h = new_ctx(hgb, w, torch, bits)
     qg, qh, kg, kh = oracle_quantized(w, bits)
@@ -92,8 +93,14 @@ def run_level_both(hgb, torch, w, check_exact_gain=False, bits=30):
     ch_t.fill_(-7)   # poison: every slot must be written
     ctx.build_level(ch_t, torch.from_numpy(L.built_row_index).to(dev),
                     L.built_offsets.astype(np.int32), L.built_slots)
-    ctx.subtract_siblings(par_t, ch_t, L.built_is_right)
-    sp = gpu_splits(hgb, ctx, ch_t, 2 * P, w.lam, w.gamma, torch)
+    if fused:
+        out = torch.empty(2 * P * hgb.SPLIT_BYTES, dtype=torch.uint8, device=dev)
+        ctx.subtract_find_splits(par_t, ch_t, L.built_is_right, w.lam, w.gamma, out)
+        ctx.sync()
+        sp = hgb.splits_to_numpy(out)[: 2 * P]
+    else:
+        ctx.subtract_siblings(par_t, ch_t, L.built_is_right)
+        sp = gpu_splits(hgb, ctx, ch_t, 2 * P, w.lam, w.gamma, torch)
     got_par = par_t.cpu().numpy()
     got_ch = ch_t.cpu().numpy()
     ctx.close()
@@ -187,6 +194,22 @@ def test_packed_precision_configs(hgb, torch, name, n, F):
         run_level_both(hgb, torch, w, check_exact_gain=True, bits=19)
     if w.kind in ("root", "root+level"):
         run_root_both(hgb, torch, w, bits=19)
+
+
+@pytest.mark.parametrize("case", ["small8", "small9", "small10", "small11", "small12", "c2", "c5", "c4"])
+def test_subtract_find_splits(hgb, torch, case):
+    """The fused level tail equals subtract_siblings + find_splits (the oracle's
+    subtraction and scan); small12's 4,095 bins take the two-pass fallback."""
+    say("fused tail", case)
+    if case.startswith("small"):
+        row = [r for r in SMALL if r[0] == int(case[5:])][0]
+        seed, n, F, B, missing, children, u16 = row
+        w = synth.random_small(seed, n, F, B, missing, children, u16=u16)
+    elif case == "c4":
+        w = synth.make("c4", n_rows=8_192, n_features=1_024)
+    else:
+        w = synth.make(case, n_rows=200_000)
+    run_level_both(hgb, torch, w, check_exact_gain=True, fused=True)
 
 
 def test_c1_full(hgb, torch):
