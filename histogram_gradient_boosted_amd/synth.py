@@ -85,6 +85,8 @@ class Workload:
     level: Optional[Level] = None
     depth: int = 0              # levels 0..depth-1 for kind == "tree"
     notes: dict = field(default_factory=dict)
+    margin: Optional[np.ndarray] = None   # fp32 [n] raw scores, where the recipe has them
+    label: Optional[np.ndarray] = None    # fp32 [n] labels, where the recipe has them
 
     @property
     def n_rows(self) -> int:
@@ -190,7 +192,8 @@ def make(name: str, seed: int = 0, n_rows: Optional[int] = None,
         prob = 1.0 / (1.0 + np.exp(-margin))
         grad = (prob - label).astype(np.float32)
         hess = (prob * (1.0 - prob)).astype(np.float32)
-        return Workload(name, bins, 256, False, grad, hess, kind="tree", depth=8)
+        return Workload(name, bins, 256, False, grad, hess, kind="tree", depth=8,
+                        margin=margin.astype(np.float32), label=label.astype(np.float32))
 
     if name == "c4":
         bins = s[0].integers(0, 256, size=(F, n), dtype=np.uint8)
@@ -237,3 +240,28 @@ def random_small(seed: int, n_rows: int, n_features: int, n_bins: int,
     lvl = level_from_node_ids(node_id, n_children)
     return Workload(f"small{seed}", bins, n_bins, has_missing, grad, hess,
                     kind="level", level=lvl)
+
+
+def objective_inputs(seed: int, n: int, kind: str, weighted: bool = False):
+    """Scores, labels and (optionally) weights, fp32 [n], for loss `kind`.
+
+    Scores are N(0, 2^2) for 90% of the rows and spread uniformly over a wide
+    range for the rest (+-60 for squared and logistic, so that the logistic
+    probability saturates; +-20 for Poisson, whose exp must stay finite in
+    fp32).  Labels: N(0, 1) for squared, Bernoulli(0.5) in {0, 1} for logistic,
+    Poisson counts with rate e^N(0,1) for Poisson.  Weights U(0.5, 2)."""
+    if kind not in ("squared", "logistic", "poisson"):
+        raise ValueError(f"unknown objective {kind!r}")
+    s = _streams(seed, 5)
+    wide = 20.0 if kind == "poisson" else 60.0
+    margin = s[0].normal(0.0, 2.0, n)
+    far = s[1].random(n) < 0.1
+    margin[far] = s[2].uniform(-wide, wide, int(far.sum()))
+    if kind == "squared":
+        label = s[3].standard_normal(n)
+    elif kind == "logistic":
+        label = (s[3].random(n) < 0.5).astype(np.float64)
+    else:
+        label = s[3].poisson(np.exp(s[3].standard_normal(n))).astype(np.float64)
+    weight = s[4].uniform(0.5, 2.0, n).astype(np.float32) if weighted else None
+    return margin.astype(np.float32), label.astype(np.float32), weight

@@ -7,7 +7,7 @@ path never imports it.
 
 Functions mirror the steps of the method (see oracle.c for the passages each
 one restates): quantize, check_bins, build_hist, subtract, find_splits,
-partition.  All arrays are numpy arrays on the host.
+partition, objective (with its exp).  All arrays are numpy arrays on the host.
 """
 from __future__ import annotations
 
@@ -25,6 +25,11 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 OK = 0
 E_INVALID = 1
 E_NONFINITE = 4
+
+OBJ_SQUARED = 0
+OBJ_LOGISTIC = 1
+OBJ_POISSON = 2
+OBJECTIVES = {"squared": OBJ_SQUARED, "logistic": OBJ_LOGISTIC, "poisson": OBJ_POISSON}
 
 SPLIT_DTYPE = np.dtype([
     ("feature", "<i4"), ("bin", "<i4"), ("default_left", "<i4"), ("pad", "<i4"),
@@ -78,6 +83,10 @@ def _load():
         lib.oracle_partition.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp, i32,
                                          vp, vp, vp]
         lib.oracle_partition.restype = i32
+        lib.oracle_exp_array.argtypes = [vp, i64, vp]
+        lib.oracle_exp_array.restype = None
+        lib.oracle_objective.argtypes = [i32, vp, vp, vp, i64, vp, vp]
+        lib.oracle_objective.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -181,3 +190,27 @@ def partition(bins, n_bins: int, row_index, node_offsets, splits):
                                   _ptr(splits), _ptr(out_ri), _ptr(out_no))
     out_no = out_no[: nc + 1].copy()
     return out_ri[: int(out_no[-1])].copy(), out_no
+
+
+def exp(x):
+    """The oracle's own exp (Cody-Waite reduction, degree-13 Taylor), elementwise, f64."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _load().oracle_exp_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def objective(kind, margin, label, weight=None):
+    """(grad, hess) fp32 [n] of loss `kind` ("squared", "logistic", "poisson" or
+    its code) at scores `margin` for labels `label`, optionally weighted."""
+    code = OBJECTIVES[kind] if isinstance(kind, str) else int(kind)
+    m = np.ascontiguousarray(margin, dtype=np.float32)
+    y = np.ascontiguousarray(label, dtype=np.float32)
+    w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float32)
+    assert y.shape == m.shape and (w is None or w.shape == m.shape)
+    g = np.empty(m.shape[0], dtype=np.float32)
+    h = np.empty(m.shape[0], dtype=np.float32)
+    st = _load().oracle_objective(code, _ptr(m), _ptr(y), _ptr(w), m.shape[0], _ptr(g), _ptr(h))
+    if st != OK:
+        raise OracleError(st, "objective")
+    return g, h

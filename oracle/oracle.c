@@ -19,6 +19,9 @@
  *                 the best (feature, bin, default direction) per node.
  *   partition     route a node's rows to its two children by the chosen split
  *                 (used only to drive a multi-level tree in the tests).
+ *   objective     per-row (grad, hess) of squared-error, logistic or Poisson
+ *                 loss from scores and labels, with an exp written out in
+ *                 full (Cody-Waite reduction, Taylor polynomial).
  *
  * Compiled with gcc -O2 -ffp-contract=off so that the fp64 gain expression is
  * evaluated exactly as written, one rounding per operation.
@@ -327,4 +330,98 @@ int32_t oracle_partition(const void* bins, int bin_bytes, int64_t n_rows,
         }
     }
     return n_children;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Objective gradients                                                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * exp(x) in double, written out so that any implementation that performs the
+ * same IEEE operations in the same order gets the same bits (a libm's exp is
+ * free to differ in the last place from one library to the next).
+ *
+ * Method: Cody and Waite's argument reduction ("Software Manual for the
+ * Elementary Functions", 1980).  x = n ln2 + r with n = rint(x / ln2) and
+ * |r| <= ln2 / 2, where ln 2 is split into a head with 36 significant bits
+ * (so n * head is exact for |n| < 2^17) and the double nearest to the rest;
+ * r = (x - n * head) - n * tail.  exp(r) is the Taylor polynomial of degree 13,
+ * sum r^j / j!, in Horner form (the first dropped term is below 5e-18 for
+ * |r| <= 0.347); the result is that polynomial scaled by 2^n (ldexp, exact
+ * except where the result is subnormal, where it rounds once).
+ * Beyond |x| > 1000 the result is +Inf or 0; NaN propagates.
+ */
+static double oracle_exp(double x)
+{
+    if (x != x) return x;
+    if (x > 1000.0) return INFINITY;
+    if (x < -1000.0) return 0.0;
+    const double inv_ln2 = 1.4426950408889634;            /* 1 / ln 2, rounded */
+    const double ln2_head = 0x1.62e42fefa0000p-1;          /* 36 leading bits of ln 2 */
+    const double ln2_tail = 0x1.cf79abc9e3b3ap-40;         /* ln 2 - head, rounded */
+    const double n = rint(x * inv_ln2);
+    const double r = (x - n * ln2_head) - n * ln2_tail;
+    /* 1/j! for j = 13 down to 0; each j! is exact in double */
+    const double inv_fact[14] = {
+        1.0 / 6227020800.0, 1.0 / 479001600.0, 1.0 / 39916800.0, 1.0 / 3628800.0,
+        1.0 / 362880.0, 1.0 / 40320.0, 1.0 / 5040.0, 1.0 / 720.0, 1.0 / 120.0,
+        1.0 / 24.0, 1.0 / 6.0, 1.0 / 2.0, 1.0, 1.0};
+    double p = inv_fact[0];
+    for (int j = 1; j < 14; ++j) p = p * r + inv_fact[j];
+    return ldexp(p, (int)n);
+}
+
+void oracle_exp_array(const double* x, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp(x[i]);
+}
+
+/*
+ * Per-row gradient and hessian of a twice-differentiable loss at the current
+ * raw score (margin) m of each row, for label y and optional weight w (NULL
+ * means every weight is 1).
+ *
+ * Basis: bonsai "10: CUDA histogram backend", section "The device context
+ * lifecycle": with a device-resident objective (squared error, logistic or
+ * Poisson, weighted or not) begin_tree derives the (grad, hess) pairs on the device from the
+ * resident scores and labels.  The pages name the losses but not their
+ * derivatives; the ones below are the first and second derivatives in m of
+ *
+ *   squared error  (m - y)^2 / 2          g = m - y,         h = 1
+ *   logistic       log(1 + e^m) - y m     g = p - y,         h = p (1 - p),
+ *                                         with p = 1 / (1 + e^-m)
+ *   Poisson        e^m - y m              g = e^m - y,       h = e^m
+ *
+ * each multiplied by the row's weight.  Every quantity is computed in double,
+ * one rounding per operation in the order written (no fused multiply-add),
+ * with oracle_exp above, and the pair is rounded once to fp32, the type that
+ * begin_tree takes.  Nothing is validated here: a non-finite or negative
+ * result is reported by quantization, as for gradients handed in directly.
+ * Returns ORACLE_E_INVALID for an unknown objective.
+ */
+int oracle_objective(int32_t objective, const float* margin, const float* label,
+                     const float* weight, int64_t n, float* grad, float* hess)
+{
+    if (objective < ORACLE_OBJ_SQUARED || objective > ORACLE_OBJ_POISSON) return ORACLE_E_INVALID;
+    for (int64_t i = 0; i < n; ++i) {
+        const double m = (double)margin[i];
+        const double y = (double)label[i];
+        const double w = weight ? (double)weight[i] : 1.0;
+        double g, h;
+        if (objective == ORACLE_OBJ_SQUARED) {
+            g = m - y;
+            h = 1.0;
+        } else if (objective == ORACLE_OBJ_LOGISTIC) {
+            const double p = 1.0 / (1.0 + oracle_exp(-m));
+            g = p - y;
+            h = p * (1.0 - p);
+        } else {
+            const double e = oracle_exp(m);
+            g = e - y;
+            h = e;
+        }
+        grad[i] = (float)(g * w);
+        hess[i] = (float)(h * w);
+    }
+    return ORACLE_OK;
 }

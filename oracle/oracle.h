@@ -17,6 +17,12 @@ enum {
     ORACLE_E_NONFINITE = 4
 };
 
+enum {
+    ORACLE_OBJ_SQUARED = 0,
+    ORACLE_OBJ_LOGISTIC = 1,
+    ORACLE_OBJ_POISSON = 2
+};
+
 typedef struct {
     int32_t feature;       /* -1 when the node has no valid split */
     int32_t bin;           /* value bins <= bin go left */
@@ -53,6 +59,11 @@ int32_t oracle_partition(const void* bins, int bin_bytes, int64_t n_rows,
                          const int64_t* node_offsets, int32_t n_nodes,
                          const oracle_split* splits,
                          int32_t* out_row_index, int64_t* out_offsets);
+
+void oracle_exp_array(const double* x, int64_t n, double* out);
+
+int oracle_objective(int32_t objective, const float* margin, const float* label,
+                     const float* weight, int64_t n, float* grad, float* hess);
 
 #ifdef __cplusplus
 }
