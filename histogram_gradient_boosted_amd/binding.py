@@ -33,7 +33,10 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
             "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
-            "hgb_subtract_find_splits")
+            "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized")
+
+# hgb_objective
+OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
 
 KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5,
            "partition": 6}
@@ -76,6 +79,10 @@ def load():
     lib.hgb_upload_bins.restype = c_int
     lib.hgb_begin_tree.argtypes = [vp, vp, vp]
     lib.hgb_begin_tree.restype = c_int
+    lib.hgb_begin_tree_objective.argtypes = [vp, i32, vp, vp, vp]
+    lib.hgb_begin_tree_objective.restype = c_int
+    lib.hgb_copy_quantized.argtypes = [vp, vp]
+    lib.hgb_copy_quantized.restype = c_int
     lib.hgb_set_precision.argtypes = [vp, i32]
     lib.hgb_set_precision.restype = c_int
     lib.hgb_get_scales.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -214,6 +221,27 @@ class Context:
         g = self._dev(grad, "grad", torch.float32, self.n_rows)
         h = self._dev(hess, "hess", torch.float32, self.n_rows)
         self._check(self._lib.hgb_begin_tree(self._h, g, h), "begin_tree")
+
+    def begin_tree_objective(self, objective, margin, label, weight=None):
+        """Start a tree from (g, h) that the library derives on the device from
+        scores `margin` and labels `label` (and optional weights), for loss
+        `objective` ("squared", "logistic", "poisson" or its hgb_objective code)."""
+        torch = self._torch
+        code = OBJECTIVES[objective] if isinstance(objective, str) else int(objective)
+        m = self._dev(margin, "margin", torch.float32, self.n_rows)
+        y = self._dev(label, "label", torch.float32, self.n_rows)
+        w = None if weight is None else self._dev(weight, "weight", torch.float32, self.n_rows)
+        self._check(self._lib.hgb_begin_tree_objective(self._h, code, m, y, w),
+                    "begin_tree_objective")
+
+    def copy_quantized(self, out=None):
+        """The current tree's (qg, qh) pairs as an int32 [n_rows, 2] CUDA tensor."""
+        torch = self._torch
+        if out is None:
+            out = torch.empty((self.n_rows, 2), dtype=torch.int32, device=f"cuda:{self.device}")
+        q = self._dev(out, "out", torch.int32, 2 * self.n_rows)
+        self._check(self._lib.hgb_copy_quantized(self._h, q), "copy_quantized")
+        return out
 
     def set_precision(self, bits: int):
         """Fixed-point precision (bits below the largest |value|) of the next begin_tree."""

@@ -777,6 +777,68 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
 
 }  // namespace
 
+// Start a tree from any row source: exact maxima of |g| and of h, the scales
+// from their exponents (one stream sync), then the quantize pass, which
+// re-derives each row's (g, h) from the source.
+template <class Src>
+static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
+{
+    HGB_HIP(c, hipSetDevice(c->device));
+    c->have_tree = false;
+    hgb_status st = grow(c, &c->q, &c->q_cap, c->n);
+    if (st != HGB_OK) return st;
+    k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 2);
+    HGB_LAUNCHED(c, "k_clear_u32");
+    {
+        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
+        k_grad_hess_max<Src><<<grid_for((c->n + 3) / 4, 256, 1024), 256, 0, c->stream>>>(src, c->n, vec,
+                                                                                       c->dev_words);
+    }
+    HGB_LAUNCHED(c, "k_grad_hess_max");
+    HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    const uint32_t pg = c->host_words[0], ph = c->host_words[1];
+    if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
+    if (ph >= 0x7f800000u)
+        return fail(c, HGB_E_NONFINITE, "begin_tree: NaN, Inf or negative hessian");
+    int k[2];
+    const uint32_t pat[2] = {pg, ph};
+    for (int i = 0; i < 2; ++i) {
+        float m;
+        std::memcpy(&m, &pat[i], 4);
+        if (m == 0.0f) {
+            k[i] = 0;
+        } else {
+            int e = 0;
+            (void)std::frexp((double)m, &e);
+            k[i] = c->precision - e;
+        }
+    }
+    c->k_g = k[0];
+    c->k_h = k[1];
+    {
+        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
+        k_quantize<Src><<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
+            src, c->n, vec, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
+    }
+    HGB_LAUNCHED(c, "k_quantize");
+    c->have_tree = true;
+    return HGB_OK;
+}
+
+static bool aligned16(const void* p) { return p == nullptr || (uintptr_t)p % 16 == 0; }
+
+static_assert(HGB_OBJ_SQUARED == kObjSquared && HGB_OBJ_LOGISTIC == kObjLogistic &&
+                  HGB_OBJ_POISSON == kObjPoisson,
+              "objective codes");
+
+template <int OBJ>
+static hgb_status begin_tree_objective_as(hgb_ctx* c, const float* m, const float* y, const float* w, int vec)
+{
+    if (w) return begin_tree_from(c, ObjectiveSource<OBJ, true>{m, y, w}, vec);
+    return begin_tree_from(c, ObjectiveSource<OBJ, false>{m, y, nullptr}, vec);
+}
+
 extern "C" {
 
 int hgb_available(void)
@@ -963,47 +1025,34 @@ hgb_status hgb_begin_tree(hgb_ctx* c, const float* grad, const float* hess)
     c->err.clear();
     if (!c->have_data) return fail(c, HGB_E_STATE, "begin_tree before upload_bins");
     if (!grad || !hess) return fail(c, HGB_E_INVALID, "begin_tree: null gradient pointer");
+    const int vec = aligned16(grad) && aligned16(hess);
+    return begin_tree_from(c, GradSource{grad, hess}, vec);
+}
+
+hgb_status hgb_begin_tree_objective(hgb_ctx* c, int32_t objective, const float* margin,
+                                    const float* label, const float* weight)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_data) return fail(c, HGB_E_STATE, "begin_tree_objective before upload_bins");
+    if (!margin || !label) return fail(c, HGB_E_INVALID, "begin_tree_objective: null score or label pointer");
+    const int vec = aligned16(margin) && aligned16(label) && aligned16(weight);
+    switch (objective) {
+    case HGB_OBJ_SQUARED: return begin_tree_objective_as<kObjSquared>(c, margin, label, weight, vec);
+    case HGB_OBJ_LOGISTIC: return begin_tree_objective_as<kObjLogistic>(c, margin, label, weight, vec);
+    case HGB_OBJ_POISSON: return begin_tree_objective_as<kObjPoisson>(c, margin, label, weight, vec);
+    default: return fail(c, HGB_E_INVALID, "begin_tree_objective: unknown objective");
+    }
+}
+
+hgb_status hgb_copy_quantized(hgb_ctx* c, int32_t* q_dev)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!q_dev) return fail(c, HGB_E_INVALID, "copy_quantized: null output");
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "copy_quantized before begin_tree");
     HGB_HIP(c, hipSetDevice(c->device));
-    c->have_tree = false;
-    hgb_status st = grow(c, &c->q, &c->q_cap, c->n);
-    if (st != HGB_OK) return st;
-    k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 2);
-    HGB_LAUNCHED(c, "k_clear_u32");
-    const int vec = ((uintptr_t)grad % 16 == 0 && (uintptr_t)hess % 16 == 0) ? 1 : 0;
-    {
-        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_grad_hess_max<<<grid_for((c->n + 3) / 4, 256, 1024), 256, 0, c->stream>>>(grad, hess, c->n,
-                                                                                 vec, c->dev_words);
-    }
-    HGB_LAUNCHED(c, "k_grad_hess_max");
-    HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
-    HGB_HIP(c, hipStreamSynchronize(c->stream));
-    const uint32_t pg = c->host_words[0], ph = c->host_words[1];
-    if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
-    if (ph >= 0x7f800000u)
-        return fail(c, HGB_E_NONFINITE, "begin_tree: NaN, Inf or negative hessian");
-    int k[2];
-    const uint32_t pat[2] = {pg, ph};
-    for (int i = 0; i < 2; ++i) {
-        float m;
-        std::memcpy(&m, &pat[i], 4);
-        if (m == 0.0f) {
-            k[i] = 0;
-        } else {
-            int e = 0;
-            (void)std::frexp((double)m, &e);
-            k[i] = c->precision - e;
-        }
-    }
-    c->k_g = k[0];
-    c->k_h = k[1];
-    {
-        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_quantize<<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
-            grad, hess, c->n, vec, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
-    }
-    HGB_LAUNCHED(c, "k_quantize");
-    c->have_tree = true;
+    HGB_HIP(c, hipMemcpyAsync(q_dev, c->q, (size_t)c->n * sizeof(int2), hipMemcpyDeviceToDevice, c->stream));
     return HGB_OK;
 }
 

@@ -1,6 +1,7 @@
 // Device kernels of the hgb library (gfx950).  Internal header: included by
-// hgb.hip only.  All integer work is exact; the one floating-point kernel (the
-// split scan) is compiled without fused multiply-add.
+// hgb.hip only.  All integer work is exact; the floating-point work (the
+// objective's (g, h) and the split scan's gain) is compiled without fused
+// multiply-add.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,17 +33,107 @@ __device__ inline uint32_t hess_pattern(float x)
     return b == 0x80000000u ? 0u : b;
 }
 
-// Four rows per thread per step (16-byte loads, when `vec` says both arrays
-// are 16-byte aligned); the leftover rows one by one at the end.
-__global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__ g,
-                                                       const float* __restrict__ h, int64_t n,
-                                                       int vec, uint32_t* __restrict__ out)
+// ---------------------------------------------------------------------------
+// Row sources of begin_tree.  A source yields each row's fp32 (g, h), four
+// rows at a time from 16-byte loads (fetch4) or one at a time (fetch1).
+// ---------------------------------------------------------------------------
+struct GradSource {   // (g, h) handed in directly
+    const float* __restrict__ g;
+    const float* __restrict__ h;
+    __device__ void fetch4(int64_t i4, float4& a, float4& b) const
+    {
+        a = ((const float4*)g)[i4];
+        b = ((const float4*)h)[i4];
+    }
+    __device__ void fetch1(int64_t i, float& a, float& b) const
+    {
+        a = g[i];
+        b = h[i];
+    }
+};
+
+// Device-resident objective: (g, h) derived from scores, labels and weights.
+enum : int { kObjSquared = 0, kObjLogistic = 1, kObjPoisson = 2 };
+
+// e^x in double.  Cody and Waite's reduction (Software Manual for the
+// Elementary Functions, 1980): x = n ln2 + r, n = rint(x / ln2), with ln 2
+// split into a head of 36 significant bits (n * head is exact for |n| < 2^17)
+// and the double nearest the remainder; then the Taylor polynomial of degree
+// 13 in r (|r| <= 0.347, first omitted term < 5e-18) in Horner form, scaled by
+// 2^n with ldexp.  Every step is one IEEE operation (the library is built
+// without contraction), so the bits do not depend on the compiler's choice of
+// instructions.  |x| > 1000 saturates to +Inf / 0.
+__device__ inline double cw_exp(double x)
+{
+    if (x != x) return x;
+    if (x > 1000.0) return __builtin_huge_val();
+    if (x < -1000.0) return 0.0;
+    constexpr double kInvLn2 = 1.4426950408889634;
+    constexpr double kLn2Head = 0x1.62e42fefa0000p-1;
+    constexpr double kLn2Tail = 0x1.cf79abc9e3b3ap-40;
+    const double n = __builtin_rint(x * kInvLn2);
+    const double r = (x - n * kLn2Head) - n * kLn2Tail;
+    // reciprocal factorials, degree 13 first (j! is exact in double for j <= 18)
+    constexpr double kFact[14] = {6227020800.0, 479001600.0, 39916800.0, 3628800.0, 362880.0,
+                                  40320.0,      5040.0,      720.0,      120.0,     24.0,
+                                  6.0,          2.0,         1.0,        1.0};
+    double p = 1.0 / kFact[0];
+#pragma unroll
+    for (int j = 1; j < 14; ++j) p = p * r + 1.0 / kFact[j];
+    return __builtin_ldexp(p, (int)n);
+}
+
+template <int OBJ>
+__device__ inline void objective_row(float m32, float y32, float w32, float& g, float& h)
+{
+    const double m = m32, y = y32, w = w32;
+    double gd, hd;
+    if constexpr (OBJ == kObjSquared) {
+        gd = m - y;
+        hd = 1.0;
+    } else if constexpr (OBJ == kObjLogistic) {
+        const double p = 1.0 / (1.0 + cw_exp(-m));
+        gd = p - y;
+        hd = p * (1.0 - p);
+    } else {
+        const double e = cw_exp(m);
+        gd = e - y;
+        hd = e;
+    }
+    g = (float)(gd * w);
+    h = (float)(hd * w);
+}
+
+template <int OBJ, bool WEIGHTED>
+struct ObjectiveSource {
+    const float* __restrict__ m;
+    const float* __restrict__ y;
+    const float* __restrict__ w;
+    __device__ void fetch4(int64_t i4, float4& a, float4& b) const
+    {
+        const float4 mm = ((const float4*)m)[i4];
+        const float4 yy = ((const float4*)y)[i4];
+        const float4 ww = WEIGHTED ? ((const float4*)w)[i4] : make_float4(1.f, 1.f, 1.f, 1.f);
+        objective_row<OBJ>(mm.x, yy.x, ww.x, a.x, b.x);
+        objective_row<OBJ>(mm.y, yy.y, ww.y, a.y, b.y);
+        objective_row<OBJ>(mm.z, yy.z, ww.z, a.z, b.z);
+        objective_row<OBJ>(mm.w, yy.w, ww.w, a.w, b.w);
+    }
+    __device__ void fetch1(int64_t i, float& a, float& b) const
+    {
+        objective_row<OBJ>(m[i], y[i], WEIGHTED ? w[i] : 1.f, a, b);
+    }
+};
+
+// Four rows per thread per step (16-byte loads, when `vec` says the source's
+// arrays are 16-byte aligned); the leftover rows one by one at the end.
+template <class Src>
+__global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int vec,
+                                                       uint32_t* __restrict__ out)
 {
     uint32_t mg = 0, mh = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t n4 = vec ? (n >> 2) : 0;
-    const float4* g4 = (const float4*)g;
-    const float4* h4 = (const float4*)h;
     auto fold = [&](const float4& a, const float4& b) {
         mg = max(mg, max(max(abs_pattern(a.x), abs_pattern(a.y)), max(abs_pattern(a.z), abs_pattern(a.w))));
         mh = max(mh, max(max(hess_pattern(b.x), hess_pattern(b.y)), max(hess_pattern(b.z), hess_pattern(b.w))));
@@ -52,17 +143,20 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__
     for (; i + 3 * stride < n4; i += 4 * stride) {
         float4 a[4], b[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = g4[i + u * stride];
-            b[u] = h4[i + u * stride];
-        }
+        for (int u = 0; u < 4; ++u) src.fetch4(i + u * stride, a[u], b[u]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) fold(a[u], b[u]);
     }
-    for (; i < n4; i += stride) fold(g4[i], h4[i]);
+    for (; i < n4; i += stride) {
+        float4 a, b;
+        src.fetch4(i, a, b);
+        fold(a, b);
+    }
     for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        mg = max(mg, abs_pattern(g[i]));
-        mh = max(mh, hess_pattern(h[i]));
+        float a, b;
+        src.fetch1(i, a, b);
+        mg = max(mg, abs_pattern(a));
+        mh = max(mh, hess_pattern(b));
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
         mg = max(mg, (uint32_t)__shfl_xor((int)mg, off, kWave));
@@ -87,10 +181,9 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(const float* __restrict__
 }
 
 // q = round-half-even(c * 2^k), both components packed per row as (qg, qh).
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ g,
-                                                  const float* __restrict__ h, int64_t n,
-                                                  int vec, double scale_g, double scale_h,
-                                                  int2* __restrict__ q)
+template <class Src>
+__global__ __launch_bounds__(256) void k_quantize(Src src, int64_t n, int vec, double scale_g,
+                                                  double scale_h, int2* __restrict__ q)
 {
     // exact: power-of-two scaling of an fp32 value in double, then ties-to-even
     auto enc = [&](float a, float b) {
@@ -99,17 +192,19 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ g,
     };
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t n4 = vec ? (n >> 2) : 0;
-    const float4* g4 = (const float4*)g;
-    const float4* h4 = (const float4*)h;
     int4* q4 = (int4*)q;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const float4 a = g4[i], b = h4[i];
+        float4 a, b;
+        src.fetch4(i, a, b);
         const int2 r0 = enc(a.x, b.x), r1 = enc(a.y, b.y), r2 = enc(a.z, b.z), r3 = enc(a.w, b.w);
         q4[2 * i] = make_int4(r0.x, r0.y, r1.x, r1.y);
         q4[2 * i + 1] = make_int4(r2.x, r2.y, r3.x, r3.y);
     }
-    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        q[i] = enc(g[i], h[i]);
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float a, b;
+        src.fetch1(i, a, b);
+        q[i] = enc(a, b);
+    }
 }
 
 // upload_bins: largest stored value, to validate every value is a slot.

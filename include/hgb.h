@@ -121,6 +121,42 @@ hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on
  */
 hgb_status hgb_begin_tree(hgb_ctx* ctx, const float* grad_dev, const float* hess_dev);
 
+/* Losses that hgb_begin_tree_objective differentiates. */
+typedef enum {
+    HGB_OBJ_SQUARED = 0,    /* (m - y)^2 / 2:        g = m - y, h = 1 */
+    HGB_OBJ_LOGISTIC = 1,   /* log(1 + e^m) - y m:   g = p - y, h = p (1 - p), p = 1/(1 + e^-m) */
+    HGB_OBJ_POISSON = 2     /* e^m - y m:            g = e^m - y, h = e^m */
+} hgb_objective;
+
+/*
+ * begin_tree fed by a device-resident objective ([bonsai-10] "The device
+ * context lifecycle": with the objective resident, the (grad, hess) pairs are
+ * derived on the device from the resident scores and labels, so nothing
+ * crosses the bus per tree).
+ *
+ * Per row i, in double, one rounding per operation in the order written and no
+ * fused multiply-add: (g, h) from the table above at m = margin[i],
+ * y = label[i], each times weight[i] (1 when weight_dev is NULL); exp is
+ * computed by Cody-Waite argument reduction (ln 2 split into a 36-bit head
+ * and its rounded remainder, n = rint(x / ln 2)) and the degree-13 Taylor
+ * polynomial in Horner form, scaled by 2^n; it is +Inf above 1000 and 0 below
+ * -1000.  Each of g and h is then rounded once to fp32, and the tree starts
+ * exactly as hgb_begin_tree would with those fp32 arrays (same scales, same
+ * codes, same errors).  The fp32 pairs are never stored.
+ *
+ * margin_dev, label_dev: fp32 [n_rows] device arrays; weight_dev: fp32
+ * [n_rows] or NULL.  The caller owns all three.
+ * Errors: as hgb_begin_tree; HGB_E_INVALID for an unknown objective or a NULL
+ *         margin or label.
+ */
+hgb_status hgb_begin_tree_objective(hgb_ctx* ctx, int32_t objective, const float* margin_dev,
+                                    const float* label_dev, const float* weight_dev);
+
+/* Copy the current tree's fixed-point pairs (qg, qh) into q_dev, int32
+ * [n_rows][2] on the device (stream-ordered; caller owns q_dev).
+ * Errors: HGB_E_STATE before a tree is started. */
+hgb_status hgb_copy_quantized(hgb_ctx* ctx, int32_t* q_dev);
+
 /* Fixed-point precision P of the next begin_tree, in bits below the largest
  * |value| (1..30, default 30).  Any P gives exact int64 cells; at P <= 19 the
  * fill packs both components of a cell into one 64-bit LDS add (the packing of
