@@ -4,9 +4,12 @@
 A step is one pass of the whole device path over one batch of synthetic input:
 begin_tree (quantize), then every level's build_level + subtract_siblings +
 find_splits.  The default workload is the tall-narrow case: 10,000,000 rows x
-28 u8 features, one depthwise tree, levels 0..7.  Its row lists per level are
-fixed once before timing (the host partition is not part of the device path),
-so the timed steps replay the same tree with every input resident in HBM.
+28 u8 features, one depthwise tree, levels 0..7, whose (g, h) are the logistic
+loss's, derived on the device from resident scores and labels
+(begin_tree_objective).  Its row lists per level are fixed once before timing
+(the host partition is not part of the device path), so the timed steps replay
+the same tree with every input resident in HBM; --grow partitions on the
+device instead.
 
 Prints one JSON line:  value = built cells (rows x features of every node
 built from rows) per second over the timed steps, in G cell-updates/s.
@@ -65,6 +68,7 @@ def fill_alg_bytes(w, built_rows: int, n_built_nodes: int, root: bool) -> int:
 
 
 def prepare(ctx, w, g, h, torch):
+    """g may be a tree.Objective (h None): the tree then starts from the device objective."""
     from histogram_gradient_boosted_amd import tree
     plan = Plan()
     if w.kind == "tree":
@@ -77,7 +81,7 @@ def prepare(ctx, w, g, h, torch):
             plan.level_notes.append({"depth": lp.depth, "nodes": lp.n_nodes, "built_rows": lp.built_rows})
         return plan
     plan.tree = None
-    ctx.begin_tree(g, h)
+    tree.begin(ctx, g, h)
     dev = torch.device("cuda", ctx.device)
     if w.kind in ("root", "root+level"):
         rp = tree.root_plan(ctx)
@@ -109,7 +113,7 @@ def step(ctx, w, plan, g, h):
     if plan.tree is not None:
         tree.replay_tree(ctx, plan.tree, g, h, w.lam, w.gamma)
         return
-    ctx.begin_tree(g, h)
+    tree.begin(ctx, g, h)
     for kind, lp, parents in plan.levels:
         if kind == "root":
             tree.run_root(ctx, lp, w.lam, w.gamma)
@@ -117,10 +121,11 @@ def step(ctx, w, plan, g, h):
             tree.run_level(ctx, lp, parents, w.lam, w.gamma)
 
 
-def _oracle_pass(w, budget_s: float):
-    """One step of the oracle, as it stands, on the host: quantize, builds of
-    the built nodes, subtraction, split scan, the tree grown with its own
-    (untimed) partition.  Returns (built cells, timed seconds, sample)."""
+def _oracle_pass(w, budget_s: float, objective: str = "none"):
+    """One step of the oracle, as it stands, on the host: (the objective's
+    gradients,) quantize, builds of the built nodes, subtraction, split scan,
+    the tree grown with its own (untimed) partition.  Returns (built cells,
+    timed seconds, sample)."""
     import oracle
     t_work = 0.0
     cells = 0
@@ -132,8 +137,12 @@ def _oracle_pass(w, budget_s: float):
         t_work += time.perf_counter() - t0
         return r
 
-    qg, kg = timed(oracle.quantize, w.grad, False)
-    qh, kh = timed(oracle.quantize, w.hess, True)
+    if objective != "none":
+        grad, hess = timed(oracle.objective, objective, w.margin, w.label)
+    else:
+        grad, hess = w.grad, w.hess
+    qg, kg = timed(oracle.quantize, grad, False)
+    qh, kh = timed(oracle.quantize, hess, True)
     B, M = w.n_bins, w.has_missing
     sample = "full step"
     if w.kind in ("root", "root+level", "tree"):
@@ -178,7 +187,8 @@ def _oracle_pass(w, budget_s: float):
     return cells, t_work, sample
 
 
-def cpu_baseline(w, min_s: float = 10.0, max_reps: int = 30, budget_s: float = 20.0):
+def cpu_baseline(w, objective: str = "none", min_s: float = 10.0, max_reps: int = 30,
+                 budget_s: float = 20.0):
     """The oracle timed on one host core: whole steps repeated until about
     min_s seconds of timed work (a step larger than budget_s is cut after the
     level that crosses it)."""
@@ -189,7 +199,7 @@ def cpu_baseline(w, min_s: float = 10.0, max_reps: int = 30, budget_s: float = 2
     reps = 0
     sample = ""
     while reps < max_reps and (reps == 0 or t_work < min_s):
-        c, t, sample = _oracle_pass(w, budget_s)
+        c, t, sample = _oracle_pass(w, budget_s, objective)
         cells += c
         t_work += t
         reps += 1
@@ -229,6 +239,10 @@ def main():
     ap.add_argument("--grow", action="store_true",
                     help="tree workloads: grow the tree each step with the device partition "
                          "(the level loop closed on the device) instead of replaying fixed row lists")
+    ap.add_argument("--objective", default="auto", choices=["auto", "none", "logistic"],
+                    help="start each tree from the device objective (logistic: the c3 recipe's "
+                         "loss, from its scores and labels) or from resident (g, h) arrays (none); "
+                         "auto = logistic for c3, none otherwise")
     ap.add_argument("--precision", type=int, default=30,
                     help="fixed-point bits P (k = P - e); 30 is the int64-cell default, "
                          "P <= 19 selects the packed one-atomic fill")
@@ -253,8 +267,19 @@ def main():
     ctx = binding.Context(0)
     ctx.set_precision(args.precision)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
-    g = torch.from_numpy(w.grad).cuda()
-    h = torch.from_numpy(w.hess).cuda()
+    objective = args.objective
+    if objective == "auto":
+        objective = "logistic" if w.margin is not None else "none"
+    if objective != "none":
+        if w.margin is None:
+            print(f"--objective {objective} needs a workload with scores and labels (c3)", file=sys.stderr)
+            sys.exit(2)
+        from histogram_gradient_boosted_amd import tree
+        g = tree.Objective(objective, torch.from_numpy(w.margin).cuda(), torch.from_numpy(w.label).cuda())
+        h = None
+    else:
+        g = torch.from_numpy(w.grad).cuda()
+        h = torch.from_numpy(w.hess).cuda()
     plan = prepare(ctx, w, g, h, torch)
     if args.grow:
         if plan.tree is None:
@@ -328,13 +353,15 @@ def main():
                      "launches_per_step": fill_launches // max(args.steps, 1),
                      "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
         "precision_bits": args.precision,
+        "gradients": "device objective: " + objective + " loss from resident scores and labels"
+        if objective != "none" else "resident fp32 (g, h) arrays",
         "step": "grow: partition + build + subtract + split per level, on the device" if args.grow
         else "replay: build + subtract + split per level on fixed row lists",
     }
     ctx.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, objective)
     print(json.dumps(result), flush=True)
 
 

@@ -46,6 +46,26 @@ class LevelPlan:
         return 0 if self.built_is_right is None else int(self.built_is_right.shape[0])
 
 
+@dataclass
+class Objective:
+    """Scores and labels (CUDA fp32 tensors, optional weights) from which
+    begin_tree_objective derives each row's (g, h) on the device.  Wherever a
+    driver below takes `grad, hess`, an Objective may stand for grad (hess is
+    then None)."""
+    kind: str
+    margin: object
+    label: object
+    weight: Optional[object] = None
+
+
+def begin(ctx: Context, grad, hess=None):
+    """Start a tree from (grad, hess) tensors or from an Objective."""
+    if isinstance(grad, Objective):
+        ctx.begin_tree_objective(grad.kind, grad.margin, grad.label, grad.weight)
+    else:
+        ctx.begin_tree(grad, hess)
+
+
 def _choose_built(counts: np.ndarray) -> np.ndarray:
     """Build the child with fewer rows; the left one on a tie."""
     return (counts[1::2] < counts[0::2]).astype(np.uint8)
@@ -134,7 +154,7 @@ def run_level(ctx: Context, plan: LevelPlan, parent_hist, lam: float, gamma: flo
 def plan_tree(ctx: Context, bins_host: np.ndarray, n_bins: int, grad, hess, depth: int,
               lam: float, gamma: float) -> List[LevelPlan]:
     """Grow levels 0..depth-1 on the device, partitioning rows on the host."""
-    ctx.begin_tree(grad, hess)
+    begin(ctx, grad, hess)
     plans = [root_plan(ctx)]
     run_root(ctx, plans[0], lam, gamma)
     rows, offs = None, None
@@ -153,7 +173,7 @@ def plan_tree(ctx: Context, bins_host: np.ndarray, n_bins: int, grad, hess, dept
 
 def replay_tree(ctx: Context, plans: List[LevelPlan], grad, hess, lam: float, gamma: float):
     """Enqueue the device path of a planned tree (begin_tree + every level)."""
-    ctx.begin_tree(grad, hess)
+    begin(ctx, grad, hess)
     run_root(ctx, plans[0], lam, gamma)
     for prev, plan in zip(plans[:-1], plans[1:]):
         run_level(ctx, plan, prev.hist, lam, gamma)
@@ -183,7 +203,7 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
     import torch
     dev = torch.device("cuda", ctx.device)
     F, S = ctx.n_features, ctx.n_slots
-    ctx.begin_tree(grad, hess)
+    begin(ctx, grad, hess)
     hist = torch.empty((1, F, S, 2), dtype=torch.int64, device=dev)
     sp = torch.empty(SPLIT_BYTES, dtype=torch.uint8, device=dev)
     ctx.build_level(hist)

@@ -7,7 +7,7 @@ path never imports it.
 
 Functions mirror the steps of the method (see oracle.c for the passages each
 one restates): quantize, check_bins, build_hist, subtract, find_splits,
-partition, objective (with its exp).  All arrays are numpy arrays on the host.
+find_level_split, partition, objective (with its exp).  All arrays are numpy arrays on the host.
 """
 from __future__ import annotations
 
@@ -83,6 +83,9 @@ def _load():
         lib.oracle_partition.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp, i32,
                                          vp, vp, vp]
         lib.oracle_partition.restype = i32
+        lib.oracle_find_level_split.argtypes = [vp, i32, i32, i32, i32, i32, i32,
+                                                ctypes.c_double, ctypes.c_double, vp]
+        lib.oracle_find_level_split.restype = None
         lib.oracle_exp_array.argtypes = [vp, i64, vp]
         lib.oracle_exp_array.restype = None
         lib.oracle_objective.argtypes = [i32, vp, vp, vp, i64, vp, vp]
@@ -168,6 +171,18 @@ def find_splits(hist, n_bins: int, has_missing: bool, k_g: int, k_h: int,
     out = np.zeros(N, dtype=SPLIT_DTYPE)
     _load().oracle_find_splits(_ptr(hist), N, F, n_bins, int(has_missing),
                                int(k_g), int(k_h), float(lam), float(gamma), _ptr(out))
+    return out
+
+
+def find_level_split(hist, n_bins: int, has_missing: bool, k_g: int, k_h: int,
+                     lam: float = 1.0, gamma: float = 0.0):
+    """Oblivious level split: n_nodes + 1 records (per node, then the level)."""
+    hist = np.ascontiguousarray(hist, dtype=np.int64)
+    N, F, S, two = hist.shape
+    assert two == 2 and S == n_slots(n_bins, has_missing)
+    out = np.zeros(N + 1, dtype=SPLIT_DTYPE)
+    _load().oracle_find_level_split(_ptr(hist), N, F, n_bins, int(has_missing),
+                                    int(k_g), int(k_h), float(lam), float(gamma), _ptr(out))
     return out
 
 

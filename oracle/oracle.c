@@ -17,6 +17,8 @@
  *   subtract      larger sibling = parent - smaller sibling, bin by bin.
  *   find_splits   scan each feature's bins with the XGBoost-style gain and pick
  *                 the best (feature, bin, default direction) per node.
+ *   find_level_split  the oblivious variant: one (feature, bin, direction)
+ *                 for all nodes of a level, by the gain summed over nodes.
  *   partition     route a node's rows to its two children by the chosen split
  *                 (used only to drive a multi-level tree in the tests).
  *   objective     per-row (grad, hess) of squared-error, logistic or Poisson
@@ -330,6 +332,145 @@ int32_t oracle_partition(const void* bins, int bin_bytes, int64_t n_rows,
         }
     }
     return n_children;
+}
+
+/*
+ * One split for a whole level: the oblivious (symmetric) tree, in which every
+ * node of a level uses the same feature and threshold.
+ *
+ * Basis: bonsai "10: CUDA histogram backend", section "The device context
+ * lifecycle" (the oblivious grower scans the frontier's histograms with
+ * find_level_split, the depthwise one with find_splits_many); ybb.press
+ * article, section 五 (symmetric trees: one feature and one threshold per
+ * level).  The pages give no formula; reading used here:
+ *
+ *   A candidate is (f, b, d) as in oracle_find_splits, the same for all nodes.
+ *   In each node it splits the node's rows as a depthwise split would, with
+ *   the node's own totals of feature f.  Its level score is the sum, over the
+ *   nodes where it is valid (both sides with a positive hessian sum), of that
+ *   node's gain (the oracle_find_splits gain, gamma included), added in node
+ *   order starting from 0.0; a node where it is not valid adds nothing.  A
+ *   candidate valid in no node is not a candidate.  The level split is the
+ *   candidate with the largest score; ties go to the smallest f, then b, then
+ *   right before left (the serial scan order, as for a node).
+ *
+ * out holds n_nodes + 1 records.  out[i] (i < n_nodes): the level's feature,
+ * bin and direction; gain = node i's term of the score (0.0 where the split is
+ * not valid in it); g_left, h_left = node i's left sums under the split;
+ * g_total, h_total = node i's totals (feature 0's slot sums).  out[n_nodes]:
+ * the level's feature, bin and direction, gain = the score, and the sums of
+ * the four integer fields over the nodes.  With no candidate at all every
+ * record has feature = bin = -1, default_left = 0, gain = -inf, g_left =
+ * h_left = 0, and its totals.
+ */
+void oracle_find_level_split(const int64_t* hist, int32_t n_nodes,
+                             int32_t n_features, int32_t n_bins, int32_t has_missing,
+                             int32_t k_g, int32_t k_h, double lambda, double gamma,
+                             oracle_split* out)
+{
+    const int64_t S = (int64_t)n_bins + (has_missing ? 1 : 0);
+    const int64_t node_elems = (int64_t)n_features * S * 2;
+    const int n_dirs = has_missing ? 2 : 1;
+    /* per node, for the feature being scanned: inclusive prefix sums of the
+     * value slots, the missing slot and the totals */
+    int64_t* pre = (int64_t*)malloc(sizeof(int64_t) * 2 * (size_t)(n_nodes > 0 ? n_nodes : 1)
+                                    * (size_t)(n_bins + 2));
+    int found = 0;
+    int32_t best_f = -1, best_b = -1, best_d = 0;
+    double best_score = -INFINITY;
+    for (int32_t f = 0; f < n_features && n_nodes > 0; ++f) {
+        for (int32_t node = 0; node < n_nodes; ++node) {
+            const int64_t* h_feat = hist + node * node_elems + (int64_t)f * S * 2;
+            int64_t* p = pre + (int64_t)node * 2 * (n_bins + 2);
+            int64_t G = 0, H = 0;
+            for (int32_t b = 0; b < n_bins; ++b) {
+                G += h_feat[2 * b + 0];
+                H += h_feat[2 * b + 1];
+                p[2 * b + 0] = G;
+                p[2 * b + 1] = H;
+            }
+            p[2 * n_bins + 0] = has_missing ? h_feat[2 * n_bins + 0] : 0;   /* missing slot */
+            p[2 * n_bins + 1] = has_missing ? h_feat[2 * n_bins + 1] : 0;
+            p[2 * n_bins + 2] = G + p[2 * n_bins + 0];                       /* totals */
+            p[2 * n_bins + 3] = H + p[2 * n_bins + 1];
+        }
+        for (int32_t b = 0; b < n_bins; ++b) {
+            for (int d = 0; d < n_dirs; ++d) {   /* d = 0: right, 1: left */
+                double score = 0.0;
+                int valid_somewhere = 0;
+                for (int32_t node = 0; node < n_nodes; ++node) {
+                    const int64_t* p = pre + (int64_t)node * 2 * (n_bins + 2);
+                    const int64_t G = p[2 * n_bins + 2], H = p[2 * n_bins + 3];
+                    const int64_t GL = p[2 * b + 0] + (d ? p[2 * n_bins + 0] : 0);
+                    const int64_t HL = p[2 * b + 1] + (d ? p[2 * n_bins + 1] : 0);
+                    const int64_t GR = G - GL;
+                    const int64_t HR = H - HL;
+                    if (!(HL > 0 && HR > 0)) continue;
+                    score += gain_of(ldexp((double)GL, -k_g), ldexp((double)HL, -k_h),
+                                     ldexp((double)GR, -k_g), ldexp((double)HR, -k_h),
+                                     ldexp((double)G, -k_g), ldexp((double)H, -k_h),
+                                     lambda, gamma);
+                    valid_somewhere = 1;
+                }
+                if (valid_somewhere && (!found || score > best_score)) {
+                    found = 1;
+                    best_f = f;
+                    best_b = b;
+                    best_d = d;
+                    best_score = score;
+                }
+            }
+        }
+    }
+    free(pre);
+
+    oracle_split level;
+    memset(&level, 0, sizeof level);
+    level.feature = found ? best_f : -1;
+    level.bin = found ? best_b : -1;
+    level.default_left = found ? best_d : 0;
+    level.gain = found ? best_score : -INFINITY;
+    for (int32_t node = 0; node < n_nodes; ++node) {
+        const int64_t* h_node = hist + node * node_elems;
+        oracle_split r;
+        memset(&r, 0, sizeof r);
+        for (int64_t s = 0; s < S; ++s) {   /* totals: feature 0's slots */
+            r.g_total += h_node[2 * s + 0];
+            r.h_total += h_node[2 * s + 1];
+        }
+        r.feature = level.feature;
+        r.bin = level.bin;
+        r.default_left = level.default_left;
+        r.gain = found ? 0.0 : -INFINITY;
+        if (found) {
+            const int64_t* h_feat = h_node + (int64_t)best_f * S * 2;
+            int64_t G = 0, H = 0, GL = 0, HL = 0;
+            for (int64_t s = 0; s < S; ++s) {
+                G += h_feat[2 * s + 0];
+                H += h_feat[2 * s + 1];
+            }
+            for (int32_t b = 0; b <= best_b; ++b) {
+                GL += h_feat[2 * b + 0];
+                HL += h_feat[2 * b + 1];
+            }
+            if (best_d) {
+                GL += h_feat[2 * n_bins + 0];
+                HL += h_feat[2 * n_bins + 1];
+            }
+            r.g_left = GL;
+            r.h_left = HL;
+            if (HL > 0 && H - HL > 0)
+                r.gain = gain_of(ldexp((double)GL, -k_g), ldexp((double)HL, -k_h),
+                                 ldexp((double)(G - GL), -k_g), ldexp((double)(H - HL), -k_h),
+                                 ldexp((double)G, -k_g), ldexp((double)H, -k_h), lambda, gamma);
+        }
+        level.g_left += r.g_left;
+        level.h_left += r.h_left;
+        level.g_total += r.g_total;
+        level.h_total += r.h_total;
+        out[node] = r;
+    }
+    out[n_nodes] = level;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -54,6 +54,11 @@ void oracle_find_splits(const int64_t* hist, int32_t n_nodes,
                         int32_t k_g, int32_t k_h, double lambda, double gamma,
                         oracle_split* out);
 
+void oracle_find_level_split(const int64_t* hist, int32_t n_nodes,
+                             int32_t n_features, int32_t n_bins, int32_t has_missing,
+                             int32_t k_g, int32_t k_h, double lambda, double gamma,
+                             oracle_split* out);
+
 int32_t oracle_partition(const void* bins, int bin_bytes, int64_t n_rows,
                          int32_t n_bins, const int32_t* row_index,
                          const int64_t* node_offsets, int32_t n_nodes,

@@ -166,3 +166,33 @@ def test_c3_objective_full_size(hgb, torch, bits):
     sub = oracle.build_hist(w.bins[:3], w.n_bins, False, want[:, 0], want[:, 1])
     assert np.array_equal(h[:3], sub[0])
     ctx.close()
+
+
+@pytest.mark.parametrize("grow", [False, True])
+def test_c3_tree_from_objective(hgb, torch, grow):
+    """A c3 tree (300,000 rows) started from the device objective, grown with
+    the host partition (replayed plan) or the device partition, equals the
+    oracle's tree grown from the oracle's logistic (g, h)."""
+    import dataclasses
+    from histogram_gradient_boosted_amd import tree
+    from test_gpu_parity import assert_splits, oracle_tree
+    say("c3 objective tree", grow)
+    w = synth.make("c3", n_rows=300_000)
+    g, h = oracle.objective("logistic", w.margin, w.label)
+    want = oracle_tree(dataclasses.replace(w, grad=g, hess=h), w.depth)
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    obj = tree.Objective("logistic", torch.from_numpy(w.margin).cuda(), torch.from_numpy(w.label).cuda())
+    if grow:
+        levels = tree.grow_tree_device(ctx, obj, None, w.depth, w.lam, w.gamma)
+        got = [(lv.hist, lv.splits, lv.n_nodes) for lv in levels]
+    else:
+        plans = tree.plan_tree(ctx, w.bins, w.n_bins, obj, None, w.depth, w.lam, w.gamma)
+        tree.replay_tree(ctx, plans, obj, None, w.lam, w.gamma)
+        ctx.sync()
+        got = [(lp.hist, lp.splits, lp.n_nodes) for lp in plans]
+    assert len(got) == len(want)
+    for d, ((hist, sp, nn), (_, _, whist, wsp)) in enumerate(zip(got, want)):
+        assert np.array_equal(hist.cpu().numpy(), whist), f"level {d}"
+        assert_splits(hgb.splits_to_numpy(sp)[:nn], wsp, f"level {d}")
+    ctx.close()
