@@ -33,7 +33,8 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
             "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
-            "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized")
+            "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized",
+            "hgb_find_level_split")
 
 # hgb_objective
 OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
@@ -93,6 +94,8 @@ def load():
     lib.hgb_subtract_siblings.restype = c_int
     lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_splits.restype = c_int
+    lib.hgb_find_level_split.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
+    lib.hgb_find_level_split.restype = c_int
     lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32), vp]
     lib.hgb_partition_level.restype = c_int
     lib.hgb_subtract_find_splits.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_double,
@@ -330,6 +333,15 @@ class Context:
             sp, op, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc),
             parent.ctypes.data_as(ctypes.c_void_p)), "partition_level")
         return child[: nc.value + 1].copy(), parent[: nc.value // 2].copy()
+
+    def find_level_split(self, hist, n_nodes: int, lam: float, gamma: float, out):
+        """Oblivious level split.  out: uint8 CUDA tensor of at least
+        (n_nodes + 1) * 56 bytes: the n_nodes node records, then the level's."""
+        torch = self._torch
+        hp = self._dev(hist, "hist", torch.int64, int(n_nodes) * self.node_elems)
+        op = self._dev(out, "out", torch.uint8, (int(n_nodes) + 1) * SPLIT_BYTES)
+        self._check(self._lib.hgb_find_level_split(self._h, hp, int(n_nodes), float(lam),
+                                                   float(gamma), op), "find_level_split")
 
     def find_splits(self, hist, n_nodes: int, lam: float, gamma: float, out):
         """out: uint8 CUDA tensor of at least n_nodes * 56 bytes (hgb_split records)."""

@@ -96,6 +96,10 @@ struct hgb_ctx {
     int64_t best_cap = 0;
     long long* totals = nullptr;
     int64_t totals_cap = 0;
+    double* level_terms = nullptr;        // find_level_split: [n_nodes][candidates] gains
+    int64_t level_terms_cap = 0;
+    LevelBest* level_best = nullptr;      // find_level_split: per-block winners
+    int64_t level_best_cap = 0;
 
     // small device words: [0..1] max patterns, [2] error flags
     uint32_t* dev_words = nullptr;
@@ -915,6 +919,8 @@ void hgb_destroy(hgb_ctx* c)
     if (c->part_host) (void)hipHostFree(c->part_host);
     (void)hipFree(c->best);
     (void)hipFree(c->totals);
+    (void)hipFree(c->level_terms);
+    (void)hipFree(c->level_best);
     (void)hipFree(c->dev_words);
     (void)hipHostFree(c->host_words);
     delete c;
@@ -1326,6 +1332,53 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F,
                                                              (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");
+    return HGB_OK;
+}
+
+hgb_status hgb_find_level_split(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
+                                double gamma, hgb_split* out)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "find_level_split before begin_tree");
+    if (n_nodes < 0 || n_nodes > 65535)
+        return fail(c, HGB_E_INVALID, "find_level_split: n_nodes out of range");
+    if (!(lambda >= 0.0) || !std::isfinite(lambda) || !std::isfinite(gamma))
+        return fail(c, HGB_E_INVALID, "find_level_split: lambda must be finite and >= 0, gamma finite");
+    if (!out || (n_nodes > 0 && !hist)) return fail(c, HGB_E_INVALID, "find_level_split: null pointer");
+    HGB_HIP(c, hipSetDevice(c->device));
+    const int n_dirs = c->has_missing ? 2 : 1;
+    const int64_t n_cand = (int64_t)c->F * c->B * n_dirs;
+    const int64_t n_blocks = n_nodes > 0 ? (n_cand + 255) / 256 : 0;
+    hgb_status st = grow(c, &c->level_terms, &c->level_terms_cap, std::max<int64_t>(1, n_cand * n_nodes));
+    if (st != HGB_OK) return st;
+    st = grow(c, &c->level_best, &c->level_best_cap, std::max<int64_t>(1, n_blocks));
+    if (st != HGB_OK) return st;
+    ProfScope ps(c, HGB_KERNEL_SPLIT);
+    if (n_nodes > 0) {
+        const int waves = 4;
+        dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
+        const int per = (c->B + kWave - 1) / kWave;
+        const bool aligned = ((uintptr_t)hist & 15) == 0;
+#define HGB_LEVEL(PER)                                                                              \
+    k_level_gain<PER><<<grid, waves * kWave, 0, c->stream>>>(                                       \
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
+        std::ldexp(1.0, -c->k_h), lambda, gamma, c->level_terms)
+        if (!aligned || per > 16) HGB_LEVEL(0);
+        else if (per <= 1) HGB_LEVEL(1);
+        else if (per <= 2) HGB_LEVEL(2);
+        else if (per <= 4) HGB_LEVEL(4);
+        else if (per <= 8) HGB_LEVEL(8);
+        else HGB_LEVEL(16);
+#undef HGB_LEVEL
+        HGB_LAUNCHED(c, "k_level_gain");
+        k_level_sum<<<(unsigned)n_blocks, 256, 0, c->stream>>>(c->level_terms, n_nodes, n_cand, c->level_best);
+        HGB_LAUNCHED(c, "k_level_sum");
+    }
+    k_level_final<<<1, 256, 0, c->stream>>>((const long long*)hist, c->level_terms, c->level_best,
+                                            (int)n_blocks, n_nodes, c->F, c->B, c->S, c->has_missing,
+                                            (SplitOut*)out);
+    HGB_LAUNCHED(c, "k_level_final");
     return HGB_OK;
 }
 

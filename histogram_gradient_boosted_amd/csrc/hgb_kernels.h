@@ -1130,26 +1130,34 @@ __device__ inline void load_lane_slots(const long long* __restrict__ hf, int n_b
     s.miss = has_missing ? make_longlong2(hf[2 * n_bins], hf[2 * n_bins + 1]) : make_longlong2(0, 0);
 }
 
-// The wave's best (bin, direction) of one feature: a lane-contiguous prefix
-// scan of the value slots, the gain of every candidate, a wave argmax.  Every
-// lane returns the result (gain -inf and code -1 when no candidate).  PER > 0
-// scans the registers in s; PER == 0 reads the slots from hf (any bin count).
+// The prefix scan of one feature's value slots across a wave.  Each lane owns
+// the value bins [b0, b1) = [lane * per, lane * per + per) clipped to n_bins.
+// wave_prefix scans the lane sums across the wave and returns the feature's
+// totals G, H (missing slot included) and the lane's exclusive prefix;
+// prefix_visit then calls visit(b, GL, HL) for each of the lane's bins in
+// increasing order, with the inclusive prefix sums of the value slots 0..b.
+// PER > 0 scans the registers in s; PER == 0 reads the slots from hf (any bin
+// count).
+struct WavePrefix {
+    long long G, H;     // totals
+    long long pg, ph;   // sums of the value slots before the lane's first bin
+    int b0, b1;
+};
+
 template <int PER>
-__device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins,
-                                     int has_missing, double scale_g, double scale_h, double lam,
-                                     double gamma)
+__device__ inline WavePrefix wave_prefix(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int per = PER > 0 ? PER : (n_bins + kWave - 1) / kWave;
-    const int b0 = lane * per;
-    const int b1 = min(b0 + per, n_bins);
-
+    WavePrefix p;
+    p.b0 = lane * per;
+    p.b1 = min(p.b0 + per, n_bins);
     long long sg = 0, sh = 0;
     if (PER > 0) {
 #pragma unroll
         for (int j = 0; j < (PER > 0 ? PER : 1); ++j) { sg += s.v[j].x; sh += s.v[j].y; }
     } else {
-        for (int b = b0; b < b1; ++b) { sg += hf[2 * b]; sh += hf[2 * b + 1]; }
+        for (int b = p.b0; b < p.b1; ++b) { sg += hf[2 * b]; sh += hf[2 * b + 1]; }
     }
     // inclusive scan of lane sums
     long long ig = sg, ih = sh;
@@ -1158,22 +1166,56 @@ __device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const Lan
         long long th = wave_shfl_up_i64(ih, d);
         if (lane >= d) { ig += tg; ih += th; }
     }
+    p.G = wave_shfl_i64(ig, kWave - 1) + s.miss.x;
+    p.H = wave_shfl_i64(ih, kWave - 1) + s.miss.y;
+    p.pg = ig - sg;
+    p.ph = ih - sh;
+    return p;
+}
+
+template <int PER, class Visit>
+__device__ inline void prefix_visit(const long long* __restrict__ hf, const LaneSlots<PER>& s,
+                                    const WavePrefix& p, Visit&& visit)
+{
+    long long pg = p.pg, ph = p.ph;
+    if (PER > 0) {
+#pragma unroll
+        for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
+            if (p.b0 + j < p.b1) {
+                pg += s.v[j].x;
+                ph += s.v[j].y;
+                visit(p.b0 + j, pg, ph);
+            }
+    } else {
+        for (int b = p.b0; b < p.b1; ++b) {
+            pg += hf[2 * b];
+            ph += hf[2 * b + 1];
+            visit(b, pg, ph);
+        }
+    }
+}
+
+// The wave's best (bin, direction) of one feature: the gain of every
+// candidate from the prefix scan, then a wave argmax.  Every lane returns the
+// result (gain -inf and code -1 when no candidate).
+template <int PER>
+__device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins,
+                                     int has_missing, double scale_g, double scale_h, double lam,
+                                     double gamma)
+{
+    const int lane = threadIdx.x & (kWave - 1);
     const long long miss_g = s.miss.x;
     const long long miss_h = s.miss.y;
-    const long long G = wave_shfl_i64(ig, kWave - 1) + miss_g;
-    const long long H = wave_shfl_i64(ih, kWave - 1) + miss_h;
+    const WavePrefix p = wave_prefix<PER>(hf, s, n_bins);
+    const long long G = p.G, H = p.H;
     const double g = (double)G * scale_g;
     const double h = (double)H * scale_h;
     const double parent = g * g / (h + lam);
-
     double bgain = 0.0;
     int bcode = -1;
     long long bgl = 0, bhl = 0;
-    long long pg = ig - sg, ph = ih - sh;   // exclusive prefix
     const int n_dirs = has_missing ? 2 : 1;
-    auto visit = [&](int b, longlong2 sv) {
-        pg += sv.x;
-        ph += sv.y;
+    prefix_visit<PER>(hf, s, p, [&](int b, long long pg, long long ph) {
         for (int d = 0; d < n_dirs; ++d) {
             const long long GL = pg + (d ? miss_g : 0);
             const long long HL = ph + (d ? miss_h : 0);
@@ -1190,14 +1232,7 @@ __device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const Lan
                 bhl = HL;
             }
         }
-    };
-    if (PER > 0) {
-#pragma unroll
-        for (int j = 0; j < (PER > 0 ? PER : 1); ++j)
-            if (b0 + j < b1) visit(b0 + j, s.v[j]);
-    } else {
-        for (int b = b0; b < b1; ++b) visit(b, make_longlong2(hf[2 * b], hf[2 * b + 1]));
-    }
+    });
     // wave argmax over (gain, code)
     int src = lane;
     double rg = bgain;
@@ -1361,6 +1396,209 @@ __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restr
             o.h_left = c.h_left;
         }
         out[node] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// find_level_split: one (feature, bin, direction) for every node of a level
+// (the oblivious tree).  A candidate's level score is the sum, in node order
+// from 0.0, of its gain in each node where it is valid; a floating-point sum
+// depends on its order, so the three passes keep that order exactly:
+//   k_level_gain   one wave per (node, feature): the gain of every candidate
+//                  in that node (-inf where invalid) into terms[node][c], with
+//                  c = (feature * n_bins + bin) * n_dirs + direction;
+//   k_level_sum    one thread per candidate: its terms added node by node,
+//                  then a block argmax (larger score, then smaller c);
+//   k_level_final  one block: the argmax over the block winners, in block
+//                  order, then every node's record and the level's.
+// ---------------------------------------------------------------------------
+struct LevelBest {
+    double score;
+    int32_t code;    // candidate index c; -1 when no candidate in the block
+    int32_t pad;
+};
+
+template <int PER>
+__global__ __launch_bounds__(256) void k_level_gain(const long long* __restrict__ hist, int n_features,
+                                                    int n_bins, int S, int has_missing, double scale_g,
+                                                    double scale_h, double lam, double gamma,
+                                                    double* __restrict__ terms)
+{
+    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int node = blockIdx.y;
+    if (f >= n_features) return;
+    const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
+    LaneSlots<PER> s;
+    load_lane_slots<PER>(hf, n_bins, has_missing, s);
+    const WavePrefix p = wave_prefix<PER>(hf, s, n_bins);
+    const double g = (double)p.G * scale_g;
+    const double h = (double)p.H * scale_h;
+    const double parent = g * g / (h + lam);
+    const int n_dirs = has_missing ? 2 : 1;
+    const int64_t n_cand = (int64_t)n_features * n_bins * n_dirs;
+    double* out = terms + (int64_t)node * n_cand + (int64_t)f * n_bins * n_dirs;
+    prefix_visit<PER>(hf, s, p, [&](int b, long long pg, long long ph) {
+        for (int d = 0; d < n_dirs; ++d) {
+            const long long GL = pg + (d ? s.miss.x : 0);
+            const long long HL = ph + (d ? s.miss.y : 0);
+            const long long GR = p.G - GL;
+            const long long HR = p.H - HL;
+            double t = -__builtin_inf();
+            if (HL > 0 && HR > 0)
+                t = split_gain((double)GL * scale_g, (double)HL * scale_h, (double)GR * scale_g,
+                               (double)HR * scale_h, parent, lam, gamma);
+            out[b * n_dirs + d] = t;
+        }
+    });
+}
+
+__device__ inline void block_argmax(double& score, int& code, double* s_score, int* s_code)
+{
+    s_score[threadIdx.x] = score;
+    s_code[threadIdx.x] = code;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            const double os = s_score[threadIdx.x + w];
+            const int oc = s_code[threadIdx.x + w];
+            if (better(os, oc, s_score[threadIdx.x], s_code[threadIdx.x])) {
+                s_score[threadIdx.x] = os;
+                s_code[threadIdx.x] = oc;
+            }
+        }
+        __syncthreads();
+    }
+    score = s_score[0];
+    code = s_code[0];
+}
+
+__global__ __launch_bounds__(256) void k_level_sum(const double* __restrict__ terms, int n_nodes,
+                                                   int64_t n_cand, LevelBest* __restrict__ block_best)
+{
+    __shared__ double s_score[256];
+    __shared__ int s_code[256];
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    double score = 0.0;
+    int code = -1;
+    if (c < n_cand) {
+        bool any = false;
+        const double* t = terms + c;
+#pragma unroll 8
+        for (int n = 0; n < n_nodes; ++n) {
+            const double v = t[(int64_t)n * n_cand];
+            if (v != -__builtin_inf()) {
+                score += v;
+                any = true;
+            }
+        }
+        code = any ? (int)c : -1;
+    }
+    block_argmax(score, code, s_score, s_code);
+    if (threadIdx.x == 0) {
+        LevelBest r;
+        r.score = code < 0 ? -__builtin_inf() : score;
+        r.code = code;
+        r.pad = 0;
+        block_best[blockIdx.x] = r;
+    }
+}
+
+// Sums over a wave of int64 values.
+__device__ inline long long wave_sum_i64(long long v)
+{
+    for (int off = kWave / 2; off > 0; off >>= 1) v += wave_shfl_xor_i64(v, off);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void k_level_final(const long long* __restrict__ hist,
+                                                     const double* __restrict__ terms,
+                                                     const LevelBest* __restrict__ block_best, int n_blocks,
+                                                     int n_nodes, int n_features, int n_bins, int S,
+                                                     int has_missing, SplitOut* __restrict__ out)
+{
+    __shared__ double s_score[256];
+    __shared__ int s_code[256];
+    __shared__ long long s_sum[256 / kWave][4];
+    // the winner: block results scanned in order per thread, then the tree
+    double score = 0.0;
+    int code = -1;
+    for (int i = threadIdx.x; i < n_blocks; i += blockDim.x) {
+        const LevelBest r = block_best[i];
+        if (better(r.score, r.code, score, code)) {
+            score = r.score;
+            code = r.code;
+        }
+    }
+    block_argmax(score, code, s_score, s_code);
+    const int n_dirs = has_missing ? 2 : 1;
+    const int64_t n_cand = (int64_t)n_features * n_bins * n_dirs;
+    const int f = code < 0 ? -1 : code / (n_bins * n_dirs);
+    const int b = code < 0 ? -1 : (code / n_dirs) % n_bins;
+    const int d = code < 0 ? 0 : code % n_dirs;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    long long acc[4] = {0, 0, 0, 0};   // g_left, h_left, g_total, h_total over this wave's nodes
+    for (int node = wv; node < n_nodes; node += blockDim.x / kWave) {
+        const long long* hn = hist + (int64_t)node * n_features * S * 2;
+        long long t[4] = {0, 0, 0, 0};
+        for (int j = lane; j < S; j += kWave) {   // totals: feature 0's slots
+            t[2] += hn[2 * j];
+            t[3] += hn[2 * j + 1];
+        }
+        if (code >= 0) {
+            const long long* hf = hn + (int64_t)f * S * 2;
+            for (int j = lane; j <= b; j += kWave) {
+                t[0] += hf[2 * j];
+                t[1] += hf[2 * j + 1];
+            }
+            if (d && lane == 0) {
+                t[0] += hf[2 * n_bins];
+                t[1] += hf[2 * n_bins + 1];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t[k] = wave_sum_i64(t[k]);
+        if (lane == 0) {
+            SplitOut o;
+            o.feature = f;
+            o.bin = b;
+            o.default_left = d;
+            o.pad = 0;
+            if (code < 0) {
+                o.gain = -__builtin_inf();
+            } else {
+                const double v = terms[(int64_t)node * n_cand + code];
+                o.gain = v == -__builtin_inf() ? 0.0 : v;
+            }
+            o.g_left = t[0];
+            o.h_left = t[1];
+            o.g_total = t[2];
+            o.h_total = t[3];
+            out[node] = o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] += t[k];
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s_sum[wv][k] = acc[k];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        long long tot[4] = {0, 0, 0, 0};
+        for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
+            for (int k = 0; k < 4; ++k) tot[k] += s_sum[w][k];
+        SplitOut o;
+        o.feature = f;
+        o.bin = b;
+        o.default_left = d;
+        o.pad = 0;
+        o.gain = code < 0 ? -__builtin_inf() : score;
+        o.g_left = tot[0];
+        o.h_left = tot[1];
+        o.g_total = tot[2];
+        o.h_total = tot[3];
+        out[n_nodes] = o;
     }
 }
 

@@ -230,3 +230,45 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
         levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
     ctx.sync()
     return levels
+
+
+def grow_oblivious_tree_device(ctx: Context, grad, hess, depth: int, lam: float,
+                               gamma: float) -> List[DeviceLevel]:
+    """Grow an oblivious (symmetric) tree of levels 0..depth-1 on the device:
+    every node of a level takes the level's one (feature, bin, direction) from
+    find_level_split, so every node of a split level gets two children (one
+    may be empty).  Per level: partition_level with the node records,
+    build_level of the smaller child of each pair, subtract_siblings for the
+    other, find_level_split over all children.  Each level's `splits` holds
+    n_nodes + 1 records, the last one the level's."""
+    import torch
+    dev = torch.device("cuda", ctx.device)
+    F, S = ctx.n_features, ctx.n_slots
+    begin(ctx, grad, hess)
+    hist = torch.empty((1, F, S, 2), dtype=torch.int64, device=dev)
+    sp = torch.empty(2 * SPLIT_BYTES, dtype=torch.uint8, device=dev)
+    ctx.build_level(hist)
+    ctx.find_level_split(hist, 1, lam, gamma, sp)
+    levels = [DeviceLevel(0, 1, None, None, hist, sp, ctx.n_rows)]
+    for d in range(1, depth):
+        prev = levels[-1]
+        total = ctx.n_rows if prev.rows is None else int(prev.offsets[-1])
+        out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        child, split_nodes = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
+        n_nodes = int(child.shape[0]) - 1
+        if n_nodes == 0:
+            break
+        counts = np.diff(child)
+        bir = _choose_built(counts)
+        P = n_nodes // 2
+        slots = np.full(n_nodes, -1, dtype=np.int32)
+        built = 2 * np.arange(P) + bir
+        slots[built] = built
+        hist = torch.empty((n_nodes, F, S, 2), dtype=torch.int64, device=dev)
+        sp = torch.empty((n_nodes + 1) * SPLIT_BYTES, dtype=torch.uint8, device=dev)
+        ctx.build_level(hist, out, child, slots)
+        ctx.subtract_siblings(prev.hist, hist, bir, split_nodes.astype(np.int32))
+        ctx.find_level_split(hist, n_nodes, lam, gamma, sp)
+        levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
+    ctx.sync()
+    return levels

@@ -234,6 +234,37 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
                            double lambda, double gamma, hgb_split* out_dev);
 
 /*
+ * The oblivious (symmetric) level split: one (feature, bin, direction) for all
+ * n_nodes nodes of a level ([bonsai-10] "The device context lifecycle":
+ * find_level_split is the oblivious grower's scan of the frontier; [ybb]
+ * section 5: every node of a level of a symmetric tree uses the same feature
+ * and threshold).
+ *
+ * Candidates, their validity in a node and a node's gain are those of
+ * hgb_find_splits, each node using its own totals.  A candidate's level score
+ * is the sum, in node order starting from 0.0, of its gain in each node where
+ * it is valid (a node where it leaves a side without hessian adds nothing); a
+ * candidate valid in no node is not a candidate.  The level split has the
+ * largest score; ties go to the smallest feature, then bin, then right before
+ * left.
+ *
+ * out_dev: hgb_split [n_nodes + 1] on the device.  Record i < n_nodes: the
+ * level's feature, bin, default_left; gain = node i's term of the score (0.0
+ * where the split is not valid in node i); g_left, h_left = node i's left
+ * sums under the split; g_total, h_total = node i's totals (feature 0).
+ * Record n_nodes: the level's feature, bin, default_left, gain = the score,
+ * and the integer fields summed over the nodes.  With no candidate every
+ * record has feature = bin = -1, default_left 0, gain -inf, g_left = h_left
+ * = 0.  The node records can be handed to hgb_partition_level as they are:
+ * every node then gets two children, one of them possibly empty.
+ *
+ * Scratch: n_nodes * n_features * n_bins * (1 or 2 directions) doubles.
+ * Errors: as hgb_find_splits.
+ */
+hgb_status hgb_find_level_split(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_nodes,
+                                double lambda, double gamma, hgb_split* out_dev);
+
+/*
  * subtract_siblings followed by find_splits over the 2 * n_pairs children, in
  * one pass over the histograms: the result (the other children written, one
  * hgb_split per child in out_dev) is exactly that of the two calls.  Arguments
