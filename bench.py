@@ -67,6 +67,26 @@ def fill_alg_bytes(w, built_rows: int, n_built_nodes: int, root: bool) -> int:
             + 16 * w.n_features * w.n_slots * n_built_nodes)
 
 
+def resolve_objective(w, objective: str):
+    """"auto" is the workload's own loss (logistic for c3, whose recipe has
+    scores and labels), else "none"; None if the workload cannot take it."""
+    if objective == "auto":
+        return "logistic" if w.margin is not None else "none"
+    if objective != "none" and w.margin is None:
+        return None
+    return objective
+
+
+def step_inputs(w, objective: str, torch):
+    """The resident inputs a step starts a tree from: (Objective, None) for a
+    device objective, else the (g, h) tensors."""
+    if objective != "none":
+        from histogram_gradient_boosted_amd import tree
+        return tree.Objective(objective, torch.from_numpy(w.margin).cuda(),
+                              torch.from_numpy(w.label).cuda()), None
+    return torch.from_numpy(w.grad).cuda(), torch.from_numpy(w.hess).cuda()
+
+
 def prepare(ctx, w, g, h, torch):
     """g may be a tree.Objective (h None): the tree then starts from the device objective."""
     from histogram_gradient_boosted_amd import tree
@@ -106,6 +126,9 @@ def prepare(ctx, w, g, h, torch):
 
 def step(ctx, w, plan, g, h):
     from histogram_gradient_boosted_amd import tree
+    if getattr(plan, "oblivious", False):
+        tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        return
     if getattr(plan, "grow", False):
         # the whole level loop on the device: partition, build, subtract, split
         tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
@@ -209,6 +232,32 @@ def cpu_baseline(w, objective: str = "none", min_s: float = 10.0, max_reps: int 
                       f"1 thread, {cells} built cells"}
 
 
+def lds_rates(device: int = 0):
+    """LDS atomic-add rates (lane-ops/s) from the microbenchmark library
+    (csrc/lds_rate.hip): u64 adds at uniformly random bins with 1, 2 and 16
+    lane-interleaved copies (the fill's layout), and conflict-free u64 adds
+    (every lane a distinct word).  None if the library is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "histogram_gradient_boosted_amd", "liblds_rate.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.lds_rate_measure
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                   ctypes.POINTER(ctypes.c_int)]
+    fn.restype = ctypes.c_int
+    out = {}
+    n_cu = ctypes.c_int(0)
+    for name, kind, copies in (("u64_random_bins_1_copy", 0, 1), ("u64_random_bins_2_copies", 0, 2),
+                               ("u64_random_bins_16_copies", 0, 16), ("u64_conflict_free", 1, 1)):
+        r = ctypes.c_double(0.0)
+        if fn(device, kind, copies, ctypes.byref(r), ctypes.byref(n_cu)) != 0:
+            return None
+        out[name] = r.value
+    out["n_cu"] = n_cu.value
+    return out
+
+
 def traffic_record(config: str, precision: int):
     """HBM traffic of the fill class measured with rocprofv3 counters
     (FETCH_SIZE, WRITE_SIZE, calibrated against a copy of known size) by
@@ -239,6 +288,9 @@ def main():
     ap.add_argument("--grow", action="store_true",
                     help="tree workloads: grow the tree each step with the device partition "
                          "(the level loop closed on the device) instead of replaying fixed row lists")
+    ap.add_argument("--oblivious", action="store_true",
+                    help="tree workloads: grow an oblivious tree (one split per level, "
+                         "find_level_split) on the device each step")
     ap.add_argument("--objective", default="auto", choices=["auto", "none", "logistic"],
                     help="start each tree from the device objective (logistic: the c3 recipe's "
                          "loss, from its scores and labels) or from resident (g, h) arrays (none); "
@@ -267,25 +319,29 @@ def main():
     ctx = binding.Context(0)
     ctx.set_precision(args.precision)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
-    objective = args.objective
-    if objective == "auto":
-        objective = "logistic" if w.margin is not None else "none"
-    if objective != "none":
-        if w.margin is None:
-            print(f"--objective {objective} needs a workload with scores and labels (c3)", file=sys.stderr)
-            sys.exit(2)
-        from histogram_gradient_boosted_amd import tree
-        g = tree.Objective(objective, torch.from_numpy(w.margin).cuda(), torch.from_numpy(w.label).cuda())
-        h = None
-    else:
-        g = torch.from_numpy(w.grad).cuda()
-        h = torch.from_numpy(w.hess).cuda()
+    objective = resolve_objective(w, args.objective)
+    if objective is None:
+        print(f"--objective {args.objective} needs a workload with scores and labels (c3)", file=sys.stderr)
+        sys.exit(2)
+    g, h = step_inputs(w, objective, torch)
     plan = prepare(ctx, w, g, h, torch)
-    if args.grow:
+    if args.grow or args.oblivious:
         if plan.tree is None:
-            print("--grow needs a tree workload (c3)", file=sys.stderr)
+            print("--grow / --oblivious need a tree workload (c3)", file=sys.stderr)
             sys.exit(2)
         plan.grow = True
+    if args.oblivious:
+        # the oblivious tree differs from the planned depthwise one: count its
+        # built cells from one untimed growth
+        from histogram_gradient_boosted_amd import tree
+        plan.oblivious = True
+        levels = tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        plan.cells = sum(lv.built_rows for lv in levels) * w.n_features
+        plan.fill_bytes = sum(fill_alg_bytes(w, lv.built_rows, 1 if lv.depth == 0 else lv.n_nodes // 2,
+                                             lv.depth == 0) for lv in levels)
+        plan.level_notes = [{"depth": lv.depth, "nodes": lv.n_nodes, "built_rows": lv.built_rows}
+                            for lv in levels]
+        del levels
     log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
 
     for _ in range(args.warmup):
@@ -355,10 +411,28 @@ def main():
         "precision_bits": args.precision,
         "gradients": "device objective: " + objective + " loss from resident scores and labels"
         if objective != "none" else "resident fp32 (g, h) arrays",
-        "step": "grow: partition + build + subtract + split per level, on the device" if args.grow
+        "step": "oblivious: partition + build + subtract + level split per level, on the device"
+        if args.oblivious else
+        "grow: partition + build + subtract + split per level, on the device" if args.grow
         else "replay: build + subtract + split per level on fixed row lists",
     }
     ctx.close()
+    # the LDS ceiling: the fill's atomic adds per step (two per cell in wide
+    # mode, P > 19; one in packed mode) against the microbenchmark's rates
+    rates = lds_rates(0)
+    atomics = plan.cells * (2 if args.precision > 19 else 1)
+    lds_achieved = atomics / (fill_ms_step * 1e-3) if fill_ms_step > 0 else 0.0
+    if rates:
+        result["lds_roofline"] = {
+            "kernel": FILL_KERNELS, "unit": "u64 LDS atomic adds (lane-ops)/s",
+            "atomics_per_step": atomics, "achieved": round(lds_achieved / 1e9, 1),
+            "peak": round(rates["u64_conflict_free"] / 1e9, 1),
+            "frac": round(lds_achieved / rates["u64_conflict_free"], 4),
+            "peak_kind": "measured: conflict-free u64 LDS atomic adds, whole chip (csrc/lds_rate.hip)",
+            "random_bins": {k: round(v / 1e9, 1) for k, v in rates.items() if k.startswith("u64_random")},
+            "scale": "G lane-ops/s", "n_cu": rates["n_cu"]}
+        log(f"[bench] LDS atomics {lds_achieved / 1e9:.0f} G/s in the fill; microbenchmark "
+            f"{ {k: round(v / 1e9) for k, v in rates.items() if k != 'n_cu'} } G/s")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(w, objective)

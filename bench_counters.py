@@ -7,7 +7,10 @@ Runs, each as its own child process under `rocprofv3 --pmc`:
   * the benchmark step driver (this file with --drive) for 1 and for 3 steps,
     once per counter.  The difference of the two runs, halved, is one step's
     traffic: the set-up work (data upload, the first tree that fixes the row
-    lists) cancels out.
+    lists) cancels out;
+  * the same pair of driver runs once more with four SQ counters of the LDS
+    (instructions, active cycles, bank- and address-conflict cycles), for the
+    fill's second ceiling.
 
 Writes profiles/counters_<config>_p<bits>.json (read by bench.py, which reports
 it as roofline.traffic while the kernel sources are unchanged) and a short text
@@ -32,8 +35,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 FILL_CLASS = ("k_fill_root", "k_fill_rows", "k_fill_cols", "k_merge")
-OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_split_feature", "k_split_reduce",
-         "k_quantize", "k_grad_hess_max")
+OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_subtract_split", "k_split_feature",
+         "k_split_reduce", "k_quantize", "k_grad_hess_max")
+# one --pmc pass of SQ counters for the LDS side of the fill (4 of the 8 SQ slots)
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT")
 SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boosted_amd/csrc/*.h",
            "include/*.h")
 
@@ -59,8 +64,7 @@ def drive(config: str, precision: int, steps: int) -> None:
     ctx = binding.Context(0)
     ctx.set_precision(precision)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
-    g = torch.from_numpy(w.grad).cuda()
-    h = torch.from_numpy(w.hess).cuda()
+    g, h = bench.step_inputs(w, bench.resolve_objective(w, "auto"), torch)
     plan = bench.prepare(ctx, w, g, h, torch)
     for _ in range(steps):
         bench.step(ctx, w, plan, g, h)
@@ -84,8 +88,9 @@ def copy_kernel() -> None:
 REUSE = False   # --reuse: read the databases a previous run left under --out
 
 
-def run_counter(counter: str, out_dir: str, args: list, log_path: str) -> str:
-    """One rocprofv3 pass (from /tmp, the program right after --)."""
+def run_counter(counter, out_dir: str, args: list, log_path: str) -> str:
+    """One rocprofv3 pass (from /tmp, the program right after --).  `counter`
+    is one counter name or a tuple of names collected together."""
     if REUSE:
         dbs = glob.glob(os.path.join(out_dir, "**", "*.db"), recursive=True)
         if not dbs:
@@ -94,7 +99,8 @@ def run_counter(counter: str, out_dir: str, args: list, log_path: str) -> str:
     if os.path.exists(out_dir):
         shutil.rmtree(out_dir)
     env = dict(os.environ, TMPDIR="/tmp")
-    cmd = ["timeout", "-s", "KILL", "600", "rocprofv3", "--pmc", counter, "-d", out_dir, "-o", "p",
+    names = [counter] if isinstance(counter, str) else list(counter)
+    cmd = ["timeout", "-s", "KILL", "600", "rocprofv3", "--pmc", *names, "-d", out_dir, "-o", "p",
            "--", sys.executable] + args
     print("[counters]", " ".join(cmd), flush=True)
     with open(log_path, "w") as log:
@@ -200,6 +206,24 @@ def main() -> None:
                              os.path.join(args.out, f"{args.config}_p{args.precision}_{tag}_{steps}.log"))
             raw[(counter, steps)] = read_counter(db, counter)
 
+    lds_raw = {}
+    for steps in (1, 3):
+        db = run_counter(LDS_COUNTERS, os.path.join(args.out, f"{args.config}_p{args.precision}_lds_{steps}"),
+                         [me, "--drive", "--config", args.config, "--precision", str(args.precision),
+                          "--steps", str(steps)],
+                         os.path.join(args.out, f"{args.config}_p{args.precision}_lds_{steps}.log"))
+        lds_raw[steps] = {c: read_counter(db, c) for c in LDS_COUNTERS}
+    lds = {}
+    for k in FILL_CLASS:
+        rec = {}
+        for c in LDS_COUNTERS:
+            a = lds_raw[3][c].get(k, [0.0, 0])
+            b = lds_raw[1][c].get(k, [0.0, 0])
+            rec[c] = (a[0] - b[0]) / 2.0
+        if rec["SQ_INSTS_LDS"] > 0:
+            rec["bank_conflict_per_active"] = round(rec["SQ_LDS_BANK_CONFLICT"] / max(rec["SQ_LDS_IDX_ACTIVE"], 1.0), 4)
+            lds[k] = rec
+
     kernels = sorted(set(k for d in raw.values() for k in d) & set(FILL_CLASS + OTHER))
     per_step = {}
     for k in kernels:
@@ -223,6 +247,7 @@ def main() -> None:
         "per_step": per_step,
         "fill_traffic": {"bytes_per_step": fill_fetch + fill_write, "fetch_bytes": fill_fetch,
                          "write_bytes": fill_write, "kernels": list(FILL_CLASS)},
+        "lds_per_step": lds,
         "seconds": round(time.time() - t0, 1),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -244,6 +269,15 @@ def main() -> None:
                      f"{rec['WRITE_SIZE']['bytes']:,} |")
     lines += ["", f"Fill class ({', '.join(FILL_CLASS)}): {fill_fetch + fill_write:,} bytes per step "
               f"({fill_fetch:,} fetched, {fill_write:,} written).", "",
+              f"LDS counters per step (rocprofv3 --pmc {' '.join(LDS_COUNTERS)}, same differencing; "
+              "summed over the chip's SQs; IDX_ACTIVE and the conflicts are cycles):", "",
+              "| kernel | LDS instructions | LDS active cycles | bank-conflict cycles | address-conflict cycles | bank conflicts / active |",
+              "|---|---|---|---|---|---|"]
+    for k, rec in lds.items():
+        lines.append(f"| {k} | {rec['SQ_INSTS_LDS']:,.0f} | {rec['SQ_LDS_IDX_ACTIVE']:,.0f} | "
+                     f"{rec['SQ_LDS_BANK_CONFLICT']:,.0f} | {rec['SQ_LDS_ADDR_CONFLICT']:,.0f} | "
+                     f"{rec['bank_conflict_per_active']:.3f} |")
+    lines += ["",
               f"Kernel sources sha256: `{record['source_hash']}`."]
     with open(base + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhgb.so")
 SOURCES = [os.path.join(CSRC, "hgb.hip")]
+# the LDS atomic-rate microbenchmark that bench.py reports beside the fill
+PROBE_LIB = os.path.join(PKG, "liblds_rate.so")
+PROBE_SOURCES = [os.path.join(CSRC, "lds_rate.hip")]
 HEADERS = [os.path.join(CSRC, "hgb_kernels.h"), os.path.join(INCLUDE, "hgb.h")]
 ARCH = "gfx950"
 
@@ -26,14 +29,20 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _compile(lib: str, sources, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libhgb.so and the LDS-rate microbenchmark library."""
+    _compile(LIB, SOURCES, verbose)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 

@@ -52,3 +52,19 @@ def test_binding_raises_without_device_instead_of_falling_back():
         pytest.skip("a device is present")
     with pytest.raises(Exception):
         binding.Context(0)
+
+
+def test_lds_rate_microbenchmark_exports_its_entry():
+    """bench.py reports the LDS atomic ceiling from this library."""
+    path = os.path.join(ROOT, "histogram_gradient_boosted_amd", "liblds_rate.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "lds_rate_measure")
+    fn = lib.lds_rate_measure
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                   ctypes.POINTER(ctypes.c_int)]
+    r, n = ctypes.c_double(0), ctypes.c_int(0)
+    # argument checks return before any device call
+    assert fn(0, 7, 1, ctypes.byref(r), ctypes.byref(n)) == 1
+    assert fn(0, 0, 3, ctypes.byref(r), ctypes.byref(n)) == 1
