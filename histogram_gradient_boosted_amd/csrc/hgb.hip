@@ -1375,10 +1375,14 @@ hgb_status hgb_find_level_split(hgb_ctx* c, const int64_t* hist, int32_t n_nodes
         k_level_sum<<<(unsigned)n_blocks, 256, 0, c->stream>>>(c->level_terms, n_nodes, n_cand, c->level_best);
         HGB_LAUNCHED(c, "k_level_sum");
     }
-    k_level_final<<<1, 256, 0, c->stream>>>((const long long*)hist, c->level_terms, c->level_best,
-                                            (int)n_blocks, n_nodes, c->F, c->B, c->S, c->has_missing,
-                                            (SplitOut*)out);
-    HGB_LAUNCHED(c, "k_level_final");
+    k_level_pick<<<1, 256, 0, c->stream>>>(c->level_best, (int)n_blocks, c->B, n_dirs, (SplitOut*)out + n_nodes);
+    HGB_LAUNCHED(c, "k_level_pick");
+    if (n_nodes > 0) {
+        const unsigned rblocks = (unsigned)std::min<int64_t>((n_nodes + 3) / 4, 64);
+        k_level_records<<<rblocks, 256, 0, c->stream>>>((const long long*)hist, c->level_terms, n_nodes, c->F,
+                                                        c->B, c->S, c->has_missing, (SplitOut*)out);
+        HGB_LAUNCHED(c, "k_level_records");
+    }
     return HGB_OK;
 }
 

@@ -1409,8 +1409,10 @@ __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restr
 //                  c = (feature * n_bins + bin) * n_dirs + direction;
 //   k_level_sum    one thread per candidate: its terms added node by node,
 //                  then a block argmax (larger score, then smaller c);
-//   k_level_final  one block: the argmax over the block winners, in block
-//                  order, then every node's record and the level's.
+//   k_level_pick   one block: the argmax over the block winners, into the
+//                  level's record;
+//   k_level_records  one wave per node: the node's record under the level's
+//                  split, and the level record's integer sums.
 // ---------------------------------------------------------------------------
 struct LevelBest {
     double score;
@@ -1510,16 +1512,14 @@ __device__ inline long long wave_sum_i64(long long v)
     return v;
 }
 
-__global__ __launch_bounds__(256) void k_level_final(const long long* __restrict__ hist,
-                                                     const double* __restrict__ terms,
-                                                     const LevelBest* __restrict__ block_best, int n_blocks,
-                                                     int n_nodes, int n_features, int n_bins, int S,
-                                                     int has_missing, SplitOut* __restrict__ out)
+// The winner: block results scanned in order per thread, then the block
+// argmax.  Writes the level record (its integer sums zeroed, for
+// k_level_records to add into).
+__global__ __launch_bounds__(256) void k_level_pick(const LevelBest* __restrict__ block_best, int n_blocks,
+                                                    int n_bins, int n_dirs, SplitOut* __restrict__ level)
 {
     __shared__ double s_score[256];
     __shared__ int s_code[256];
-    __shared__ long long s_sum[256 / kWave][4];
-    // the winner: block results scanned in order per thread, then the tree
     double score = 0.0;
     int code = -1;
     for (int i = threadIdx.x; i < n_blocks; i += blockDim.x) {
@@ -1530,15 +1530,42 @@ __global__ __launch_bounds__(256) void k_level_final(const long long* __restrict
         }
     }
     block_argmax(score, code, s_score, s_code);
+    if (threadIdx.x == 0) {
+        SplitOut o;
+        o.feature = code < 0 ? -1 : code / (n_bins * n_dirs);
+        o.bin = code < 0 ? -1 : (code / n_dirs) % n_bins;
+        o.default_left = code < 0 ? 0 : code % n_dirs;
+        o.pad = 0;
+        o.gain = code < 0 ? -__builtin_inf() : score;
+        o.g_left = 0;
+        o.h_left = 0;
+        o.g_total = 0;
+        o.h_total = 0;
+        *level = o;
+    }
+}
+
+// Every node's record under the level's split (one wave per node), and the
+// level record's integer sums: per block in registers and LDS, then one
+// atomic add per field per block (integer sums: any order gives the same).
+__global__ __launch_bounds__(256) void k_level_records(const long long* __restrict__ hist,
+                                                       const double* __restrict__ terms, int n_nodes,
+                                                       int n_features, int n_bins, int S, int has_missing,
+                                                       SplitOut* __restrict__ out)
+{
+    __shared__ long long s_sum[256 / kWave][4];
+    SplitOut* level = out + n_nodes;
+    const int f = level->feature;
+    const int b = level->bin;
+    const int d = level->default_left;
     const int n_dirs = has_missing ? 2 : 1;
     const int64_t n_cand = (int64_t)n_features * n_bins * n_dirs;
-    const int f = code < 0 ? -1 : code / (n_bins * n_dirs);
-    const int b = code < 0 ? -1 : (code / n_dirs) % n_bins;
-    const int d = code < 0 ? 0 : code % n_dirs;
+    const int code = f < 0 ? -1 : (f * n_bins + b) * n_dirs + d;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
+    const int waves = (int)(blockDim.x / kWave);
     long long acc[4] = {0, 0, 0, 0};   // g_left, h_left, g_total, h_total over this wave's nodes
-    for (int node = wv; node < n_nodes; node += blockDim.x / kWave) {
+    for (int node = blockIdx.x * waves + wv; node < n_nodes; node += gridDim.x * waves) {
         const long long* hn = hist + (int64_t)node * n_features * S * 2;
         long long t[4] = {0, 0, 0, 0};
         for (int j = lane; j < S; j += kWave) {   // totals: feature 0's slots
@@ -1584,21 +1611,11 @@ __global__ __launch_bounds__(256) void k_level_final(const long long* __restrict
         for (int k = 0; k < 4; ++k) s_sum[wv][k] = acc[k];
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        long long tot[4] = {0, 0, 0, 0};
-        for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
-            for (int k = 0; k < 4; ++k) tot[k] += s_sum[w][k];
-        SplitOut o;
-        o.feature = f;
-        o.bin = b;
-        o.default_left = d;
-        o.pad = 0;
-        o.gain = code < 0 ? -__builtin_inf() : score;
-        o.g_left = tot[0];
-        o.h_left = tot[1];
-        o.g_total = tot[2];
-        o.h_total = tot[3];
-        out[n_nodes] = o;
+    if (threadIdx.x < 4) {
+        long long v = 0;
+        for (int w = 0; w < waves; ++w) v += s_sum[w][threadIdx.x];
+        long long* dst = &level->g_left + threadIdx.x;   // g_left, h_left, g_total, h_total
+        atomicAdd((unsigned long long*)dst, (unsigned long long)v);
     }
 }
 

@@ -17,7 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace lds_probe {
 
 __device__ inline uint32_t xorshift(uint32_t x)
 {
@@ -66,7 +66,9 @@ hipError_t launch(int iters, int copies, int words, int blocks, unsigned long lo
     return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace lds_probe
+
+using namespace lds_probe;
 
 extern "C" {
 

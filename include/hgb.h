@@ -11,7 +11,8 @@
  *   [bonsai-10]  bonsai docs, "10: CUDA histogram backend"
  *   [bonsai-9]   bonsai guide, "9. Parallelism & determinism"
  *   [bonsai-E6]  bonsai engine notes, "E6. The wide-data wall"
- *   [ybb]        ybb.press article on GBDT engine engineering (sections 1-10)
+ *   [ybb]        ybb.press article on GBDT engine engineering (sections 一 to 九,
+ *                cited as 1 to 9)
  *
  * Conventions shared by every entry point:
  *   - n = rows, F = features, B = value bins per feature, S = B + has_missing
