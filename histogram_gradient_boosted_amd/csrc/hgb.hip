@@ -44,6 +44,9 @@ constexpr int kMergeGroup = 32;
 // below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
+// begin_tree's max pass: at most this many blocks, each writing its pair of
+// maxima for k_max_final.
+constexpr int kMaxBlocks = 4096;
 // Default fixed-point precision of begin_tree (bits below the largest value).
 constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 16;
@@ -104,6 +107,7 @@ struct hgb_ctx {
     // small device words: [0..1] max patterns, [2] error flags
     uint32_t* dev_words = nullptr;
     uint32_t* host_words = nullptr;   // pinned
+    uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
 
     Stage stage[kStages];
     int stage_next = 0;
@@ -791,14 +795,14 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
     c->have_tree = false;
     hgb_status st = grow(c, &c->q, &c->q_cap, c->n);
     if (st != HGB_OK) return st;
-    k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words, 2);
-    HGB_LAUNCHED(c, "k_clear_u32");
+    const int max_blocks = grid_for((c->n + 3) / 4, 256, kMaxBlocks);
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_grad_hess_max<Src><<<grid_for((c->n + 3) / 4, 256, 1024), 256, 0, c->stream>>>(src, c->n, vec,
-                                                                                       c->dev_words);
+        k_grad_hess_max<Src><<<max_blocks, 256, 0, c->stream>>>(src, c->n, vec, c->max_part);
+        HGB_LAUNCHED(c, "k_grad_hess_max");
+        k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words);
     }
-    HGB_LAUNCHED(c, "k_grad_hess_max");
+    HGB_LAUNCHED(c, "k_max_final");
     HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
     HGB_HIP(c, hipStreamSynchronize(c->stream));
     const uint32_t pg = c->host_words[0], ph = c->host_words[1];
@@ -883,6 +887,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
         c->n_cu = prop.multiProcessorCount;
     c->stream = (hipStream_t)hip_stream;
     if (hipMalloc((void**)&c->dev_words, 64) != hipSuccess ||
+        hipMalloc((void**)&c->max_part, sizeof(uint32_t) * 2 * kMaxBlocks) != hipSuccess ||
         hipHostMalloc((void**)&c->host_words, 64, hipHostMallocDefault) != hipSuccess ||
         hipMemset(c->dev_words, 0, 64) != hipSuccess) {
         hgb_destroy(c);
@@ -922,6 +927,7 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipFree(c->level_terms);
     (void)hipFree(c->level_best);
     (void)hipFree(c->dev_words);
+    (void)hipFree(c->max_part);
     (void)hipHostFree(c->host_words);
     delete c;
 }
@@ -1310,13 +1316,13 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
     if (st != HGB_OK) return st;
-    const int waves = 4;
-    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
     ProfScope ps(c, HGB_KERNEL_SPLIT);
     // a lane's bins in registers when there are at most 16 of them (and the
     // buffer is 16-byte aligned); otherwise read twice from memory
     const int per = (c->B + kWave - 1) / kWave;
     const bool aligned = ((uintptr_t)hist & 15) == 0;
+    const int waves = 4;
+    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
 #define HGB_SPLIT(PER)                                                                              \
     k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \

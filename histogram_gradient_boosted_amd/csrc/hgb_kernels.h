@@ -126,7 +126,8 @@ struct ObjectiveSource {
 };
 
 // Four rows per thread per step (16-byte loads, when `vec` says the source's
-// arrays are 16-byte aligned); the leftover rows one by one at the end.
+// arrays are 16-byte aligned); the leftover rows one by one at the end.  Each
+// block writes its pair of maxima to out[2 * block], out[2 * block + 1].
 template <class Src>
 __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int vec,
                                                        uint32_t* __restrict__ out)
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int v
         mg = max(mg, (uint32_t)__shfl_xor((int)mg, off, kWave));
         mh = max(mh, (uint32_t)__shfl_xor((int)mh, off, kWave));
     }
-    // one pair of atomics per block: same-address atomics serialize at the L2
+    // one pair of maxima per block, reduced by k_max_final (no same-address
+    // atomics, which serialize at the L2)
     __shared__ uint32_t red[2][256 / kWave];
     const int wv = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) {
@@ -175,8 +177,34 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int v
             mg = max(mg, red[0][i]);
             mh = max(mh, red[1][i]);
         }
-        atomicMax(&out[0], mg);
-        atomicMax(&out[1], mh);
+        out[2 * blockIdx.x] = mg;
+        out[2 * blockIdx.x + 1] = mh;
+    }
+}
+
+// The maxima of the per-block pairs, into out[0..1].
+__global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ part, int n_blocks,
+                                                   uint32_t* __restrict__ out)
+{
+    __shared__ uint32_t red[2][256];
+    uint32_t mg = 0, mh = 0;
+    for (int i = threadIdx.x; i < n_blocks; i += blockDim.x) {
+        mg = max(mg, part[2 * i]);
+        mh = max(mh, part[2 * i + 1]);
+    }
+    red[0][threadIdx.x] = mg;
+    red[1][threadIdx.x] = mh;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            red[0][threadIdx.x] = max(red[0][threadIdx.x], red[0][threadIdx.x + w]);
+            red[1][threadIdx.x] = max(red[1][threadIdx.x], red[1][threadIdx.x + w]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out[0] = red[0][0];
+        out[1] = red[1][0];
     }
 }
 

@@ -212,6 +212,18 @@ def test_subtract_find_splits(hgb, torch, case):
     run_level_both(hgb, torch, w, check_exact_gain=True, fused=True)
 
 
+@pytest.mark.parametrize("F,B,missing,fused", [(17, 64, True, True), (32, 255, False, True),
+                                               (33, 64, True, True), (32, 1024, True, True),
+                                               (31, 100, True, False), (33, 100, False, False)])
+def test_split_feature_counts(hgb, torch, F, B, missing, fused):
+    """Feature counts around a wave block's width (4 features per block of the
+    split grid), lane slot counts 1, 2, 4 and 16, with and without missing
+    values, through the fused tail and the two-pass path."""
+    say("split block boundary", F, B, missing, fused)
+    w = synth.random_small(90 + F, 30_000, F, B, missing, 10, u16=B > 255)
+    run_level_both(hgb, torch, w, check_exact_gain=True, fused=fused)
+
+
 def test_c1_full(hgb, torch):
     say("c1 full")
     run_root_both(hgb, torch, synth.make("c1"))
