@@ -937,15 +937,11 @@ const char* hgb_last_error(const hgb_ctx* c)
     return c ? c->err.c_str() : "null context";
 }
 
-hgb_status hgb_sync(hgb_ctx* c)
+// After a stream sync that followed a copy of the device error word into
+// host_words[2]: report (and clear) what the kernels flagged.
+static hgb_status take_flags(hgb_ctx* c)
 {
-    if (!c) return HGB_E_INVALID;
-    c->err.clear();
-    HGB_HIP(c, hipSetDevice(c->device));
-    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
-                              c->stream));
-    HGB_HIP(c, hipStreamSynchronize(c->stream));
-    uint32_t flags = c->host_words[2];
+    const uint32_t flags = c->host_words[2];
     if (flags) {
         k_clear_u32<<<1, 64, 0, c->stream>>>(c->dev_words + 2, 1);
         HGB_LAUNCHED(c, "k_clear_u32");
@@ -954,6 +950,17 @@ hgb_status hgb_sync(hgb_ctx* c)
             return fail(c, HGB_E_INVALID, "a row index outside [0, n_rows) was skipped");
     }
     return HGB_OK;
+}
+
+hgb_status hgb_sync(hgb_ctx* c)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    HGB_HIP(c, hipSetDevice(c->device));
+    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
+                              c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    return take_flags(c);
 }
 
 hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_device,
@@ -1558,9 +1565,12 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
             HGB_LAUNCHED(c, "k_part_scatter");
         }
     }
+    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost, c->stream));
     st = stage_release(c, sg);
     if (st != HGB_OK) return st;
-    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    HGB_HIP(c, hipStreamSynchronize(c->stream));   // the one wait: node records and error word
+    st = take_flags(c);                            // a row index outside [0, n)
+    if (st != HGB_OK) return st;
     int32_t nc = 0;
     child_offsets[0] = 0;
     for (int i = 0; i < n_nodes; ++i) {
@@ -1572,7 +1582,7 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         nc += 2;
     }
     *n_children = nc;
-    return hgb_sync(c);   // reports a row index outside [0, n)
+    return HGB_OK;
 }
 
 hgb_status hgb_profile_enable(hgb_ctx* c, int enable)
