@@ -23,6 +23,11 @@ namespace {
 
 // gfx950: 160 KiB of LDS per CU; every fill runs one 1024-thread block per CU.
 constexpr int64_t kFillLdsBudget = 160 * 1024;
+// What a tile may take of it: the rest holds the item's totals and the
+// features' recovered cells (kFixWords).
+// A feature's top slot is hot when it holds at least 1/kHotSlotShare of the rows.
+constexpr int64_t kHotSlotShare = 16;
+constexpr int64_t kTileLdsBudget = kFillLdsBudget - 8 * kFixWords;
 constexpr int kRootThreads = 1024;
 constexpr int kLevelThreads = 1024;
 // Fill items per CU: the root gets one equal share per CU (equal items finish
@@ -108,6 +113,8 @@ struct hgb_ctx {
     uint32_t* dev_words = nullptr;
     uint32_t* host_words = nullptr;   // pinned
     uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
+    int32_t* rot = nullptr;           // per feature: the skipped slot (stored bins are rotated by it)
+    bool skip = false;                // the fills skip each feature's slot 0 (a hot slot exists)
 
     Stage stage[kStages];
     int stage_next = 0;
@@ -359,7 +366,7 @@ FillPlan plan_rows(const hgb_ctx* c)
                     if (ra > 0 && nf * S > ra * kLevelThreads) continue;
                     const int e = ra > 0 ? kRegAccEntries : kWideRowEntries;
                     const int64_t words = (int64_t)nf * (acc == kWide ? 2 : 1) * (S << lc);
-                    if (words * 8 > kFillLdsBudget) continue;
+                    if (words * 8 > kTileLdsBudget) continue;
                     int drain = 0;
                     double drain_ops = 0.0;
                     if (acc == kPacked) {
@@ -378,7 +385,7 @@ FillPlan plan_rows(const hgb_ctx* c)
                         p.ra = ra;
                         p.drain = drain;
                         p.step_rows = (int64_t)kLevelThreads * e;
-                        p.lds_bytes = (size_t)words * 8;
+                        p.lds_bytes = (size_t)(words + kFixWords) * 8;
                     }
                 }
             }
@@ -392,7 +399,7 @@ FillPlan plan_rows(const hgb_ctx* c)
         p.ra = 0;
         p.drain = 0;
         p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
-        p.lds_bytes = (size_t)2 * S * 8;
+        p.lds_bytes = (size_t)(2 * S + kFixWords) * 8;
     }
     return p;
 }
@@ -408,7 +415,7 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
     auto per_thread_of = [&](int tile) {
         return p.kind == kFillRoot ? kRootRows : (p.kind == kFillCols ? cols_entries(tile) : kLevelEntries);
     };
-    const int64_t budget = kFillLdsBudget;
+    const int64_t budget = kTileLdsBudget;
     const int want_acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
     // Candidate tiles: NF in {1, 2, 4, 8} features (root, cols), or the
     // features of one 16/8/4/2-byte row load (rows).
@@ -458,7 +465,7 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
         // rows loads cover exactly `tile` features; the others take min(NF, F)
         while (p.tile > 1 && (p.tile >> 1) >= c->F) p.tile >>= 1;
     }
-    p.lds_bytes = (size_t)(p.tile * feature_lds(p.acc, S, p.lc));
+    p.lds_bytes = (size_t)(p.tile * feature_lds(p.acc, S, p.lc) + 8 * kFixWords);
     p.step_rows = (int64_t)p.threads * per_thread_of(p.tile);
     p.drain = p.acc == kPacked ? packed_drain_steps(p.threads, p.lc, per_thread_of(p.tile)) : 0;
     return p;
@@ -485,7 +492,7 @@ struct FillArgs {
     int64_t* partial;
 };
 
-template <typename BinT, int ACC>
+template <typename BinT, int ACC, bool SKIP>
 hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 {
     const int n_grid = p.kind == kFillRoot ? a.n_items : a.n_blocks;
@@ -501,7 +508,7 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
     } while (0)
     if (p.kind == kFillRoot) {
-#define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist)
+#define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, c->rot)
         switch (p.tile) {
         case 1: HGB_ROOT(1); break;
         case 2: HGB_ROOT(2); break;
@@ -515,15 +522,15 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 #undef HGB_ROOT
     } else if (p.kind == kFillCols) {
         switch (p.tile) {
-        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
-        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
-        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
-        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial); break;
+        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
+        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
+        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
+        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
         }
     } else {
         // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2)
+#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
@@ -552,11 +559,18 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 
 hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 {
+    if (c->skip) {
+        if (c->bin_bytes == 1)
+            return p.acc == kPacked ? launch_fill_acc<uint8_t, kPacked, true>(c, p, a)
+                                    : launch_fill_acc<uint8_t, kWide, true>(c, p, a);
+        return p.acc == kPacked ? launch_fill_acc<uint16_t, kPacked, true>(c, p, a)
+                                : launch_fill_acc<uint16_t, kWide, true>(c, p, a);
+    }
     if (c->bin_bytes == 1)
-        return p.acc == kPacked ? launch_fill_acc<uint8_t, kPacked>(c, p, a)
-                                : launch_fill_acc<uint8_t, kWide>(c, p, a);
-    return p.acc == kPacked ? launch_fill_acc<uint16_t, kPacked>(c, p, a)
-                            : launch_fill_acc<uint16_t, kWide>(c, p, a);
+        return p.acc == kPacked ? launch_fill_acc<uint8_t, kPacked, false>(c, p, a)
+                                : launch_fill_acc<uint8_t, kWide, false>(c, p, a);
+    return p.acc == kPacked ? launch_fill_acc<uint16_t, kPacked, false>(c, p, a)
+                            : launch_fill_acc<uint16_t, kWide, false>(c, p, a);
 }
 
 // Zero whole node slots of the level buffer.
@@ -928,6 +942,7 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipFree(c->level_best);
     (void)hipFree(c->dev_words);
     (void)hipFree(c->max_part);
+    (void)hipFree(c->rot);
     (void)hipHostFree(c->host_words);
     delete c;
 }
@@ -1012,6 +1027,54 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
     if (c->host_words[0] >= (uint32_t)S)
         return fail(c, HGB_E_INVALID, "upload_bins: stored value %u is not a slot (S = %d)",
                     c->host_words[0], S);
+    // Each feature's most frequent slot.  When some feature's holds at least
+    // 1/kHotSlotShare of the rows (a skewed feature, or a sparse column's
+    // missing slot), the copy is rotated per feature so that it reads as 0 and
+    // the fills skip it (recovering its cell by subtraction); otherwise the
+    // copy stays as given and the fills add every slot.
+    {
+        if (c->rot) HGB_HIP(c, hipFree(c->rot));
+        c->rot = nullptr;
+        c->skip = false;
+        HGB_HIP(c, hipMalloc((void**)&c->rot, sizeof(int32_t) * (size_t)n_features));
+        uint32_t* counts = nullptr;
+        const size_t n_counts = (size_t)n_features * S + n_features;   // counts, then each top count
+        HGB_HIP(c, hipMalloc((void**)&counts, sizeof(uint32_t) * n_counts));
+        HGB_HIP(c, hipMemsetAsync(counts, 0, sizeof(uint32_t) * n_counts, c->stream));
+        const dim3 cgrid((unsigned)((n_rows + kCountChunk - 1) / kCountChunk), (unsigned)n_features);
+        const size_t clds = sizeof(uint32_t) * (size_t)S * kCountCopies;
+        hgb_status st = bin_bytes == 1 ? set_lds(c, k_slot_counts<uint8_t>, clds)
+                                       : set_lds(c, k_slot_counts<uint16_t>, clds);
+        if (st != HGB_OK) {
+            (void)hipFree(counts);
+            return st;
+        }
+        if (bin_bytes == 1)
+            k_slot_counts<uint8_t><<<cgrid, 1024, clds, c->stream>>>((const uint8_t*)c->bins, n_rows, S, counts);
+        else
+            k_slot_counts<uint16_t><<<cgrid, 1024, clds, c->stream>>>((const uint16_t*)c->bins, n_rows, S, counts);
+        HGB_LAUNCHED(c, "k_slot_counts");
+        uint32_t* top = counts + (size_t)n_features * S;
+        k_hot_slot<<<(unsigned)n_features, 256, 0, c->stream>>>(counts, S, c->rot, top);
+        HGB_LAUNCHED(c, "k_hot_slot");
+        std::vector<uint32_t> top_host(n_features);
+        HGB_HIP(c, hipMemcpyAsync(top_host.data(), top, sizeof(uint32_t) * n_features, hipMemcpyDeviceToHost,
+                                  c->stream));
+        HGB_HIP(c, hipStreamSynchronize(c->stream));
+        HGB_HIP(c, hipFree(counts));
+        const uint32_t top_max = *std::max_element(top_host.begin(), top_host.end());
+        c->skip = (int64_t)top_max * kHotSlotShare >= (int64_t)n_rows;
+        if (c->skip) {
+            const dim3 rgrid((unsigned)grid_for(n_rows, 256, 64), (unsigned)n_features);
+            if (bin_bytes == 1)
+                k_rotate<uint8_t><<<rgrid, 256, 0, c->stream>>>((uint8_t*)c->bins, n_rows, S, c->rot);
+            else
+                k_rotate<uint16_t><<<rgrid, 256, 0, c->stream>>>((uint16_t*)c->bins, n_rows, S, c->rot);
+            HGB_LAUNCHED(c, "k_rotate");
+        } else {
+            HGB_HIP(c, hipMemsetAsync(c->rot, 0, sizeof(int32_t) * (size_t)n_features, c->stream));
+        }
+    }
     if ((int64_t)n_features * bin_bytes <= kRowMajorMaxRowBytes) {
         const int64_t stride = ((int64_t)n_features * bin_bytes + 15) / 16 * 16;
         // kRowMajorSlack bytes after the last row: a tile's load may run past
@@ -1246,7 +1309,7 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         if (items.empty()) continue;
         FillPlan gp = plan;
         gp.tile = wdt;
-        gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc));
+        gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc) + 8 * kFixWords);
         FillArgs a{};
         a.gh = c->q;
         a.items = (const FillItem*)(dev + offs[wdt]);
@@ -1545,11 +1608,11 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         if (n_items > 0) {
             if (c->bin_bytes == 1)
                 k_part_count<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint8_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->part_flags,
+                    (const uint8_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
                     c->dev_words + 2);
             else
                 k_part_count<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
-                    (const uint16_t*)c->bins, c->n, c->B, row_index, items_dev, sp, cnt, c->part_flags,
+                    (const uint16_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
                     c->dev_words + 2);
             HGB_LAUNCHED(c, "k_part_count");
         }

@@ -12,6 +12,36 @@ namespace hgb {
 constexpr int kWave = 64;
 constexpr uint32_t kErrRowIndex = 1u;
 
+// 64-bit values across a wave (two 32-bit shuffles each).
+__device__ inline long long wave_shfl_up_i64(long long v, int d)
+{
+    int lo = __shfl_up((int)(v & 0xffffffffll), d, kWave);
+    int hi = __shfl_up((int)(v >> 32), d, kWave);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+__device__ inline long long wave_shfl_i64(long long v, int src)
+{
+    int lo = __shfl((int)(v & 0xffffffffll), src, kWave);
+    int hi = __shfl((int)(v >> 32), src, kWave);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+__device__ inline long long wave_shfl_xor_i64(long long v, int mask)
+{
+    int lo = __shfl_xor((int)(v & 0xffffffffll), mask, kWave);
+    int hi = __shfl_xor((int)(v >> 32), mask, kWave);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Sums over a wave of int64 values.
+__device__ inline long long wave_sum_i64(long long v)
+{
+    for (int off = kWave / 2; off > 0; off >>= 1) v += wave_shfl_xor_i64(v, off);
+    return v;
+}
+
+
 // ---------------------------------------------------------------------------
 // begin_tree: exact maxima of |grad| and of hess as IEEE bit patterns.
 // For non-negative floats the bit pattern orders like the value, so an
@@ -232,6 +262,87 @@ __global__ __launch_bounds__(256) void k_quantize(Src src, int64_t n, int vec, d
         float a, b;
         src.fetch1(i, a, b);
         q[i] = enc(a, b);
+    }
+}
+
+// upload_bins: the skipped slot of each feature (the slot holding the most
+// rows; the smallest such slot on a tie), and the stored bins rotated so that
+// it reads as 0.  Counts per row chunk in LDS (kCountCopies lane-interleaved
+// copies, so a hot slot does not serialize), added into counts[f][S].
+constexpr int kCountCopies = 4;
+constexpr int64_t kCountChunk = 65536;
+
+template <typename BinT>
+__global__ __launch_bounds__(1024) void k_slot_counts(const BinT* __restrict__ bins, int64_t n, int S,
+                                                      uint32_t* __restrict__ counts)
+{
+    extern __shared__ uint32_t cnt[];   // [S][kCountCopies]
+    const int f = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * kCountChunk;
+    const int64_t r1 = min(n, r0 + kCountChunk);
+    for (int i = threadIdx.x; i < S * kCountCopies; i += blockDim.x) cnt[i] = 0u;
+    __syncthreads();
+    const BinT* col = bins + (int64_t)f * n;
+    const int cp = threadIdx.x & (kCountCopies - 1);
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+        const int v = (int)col[r];   // validated: < S
+        atomicAdd(&cnt[v * kCountCopies + cp], 1u);
+    }
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < S; sl += blockDim.x) {
+        uint32_t t = 0;
+        for (int k = 0; k < kCountCopies; ++k) t += cnt[sl * kCountCopies + k];
+        if (t) atomicAdd(&counts[(int64_t)f * S + sl], t);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_hot_slot(const uint32_t* __restrict__ counts, int S,
+                                                  int32_t* __restrict__ hot, uint32_t* __restrict__ hot_count)
+{
+    __shared__ uint32_t s_cnt[256];
+    __shared__ int s_slot[256];
+    const int f = blockIdx.x;
+    uint32_t best = 0;
+    int slot = 0;
+    for (int sl = threadIdx.x; sl < S; sl += blockDim.x) {
+        const uint32_t t = counts[(int64_t)f * S + sl];
+        if (t > best) {   // slots visited in increasing order: the first maximum
+            best = t;
+            slot = sl;
+        }
+    }
+    s_cnt[threadIdx.x] = best;
+    s_slot[threadIdx.x] = slot;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            const uint32_t ob = s_cnt[threadIdx.x + w];
+            const int os = s_slot[threadIdx.x + w];
+            if (ob > s_cnt[threadIdx.x] || (ob == s_cnt[threadIdx.x] && os < s_slot[threadIdx.x])) {
+                s_cnt[threadIdx.x] = ob;
+                s_slot[threadIdx.x] = os;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        hot[f] = s_slot[0];
+        hot_count[f] = s_cnt[0];
+    }
+}
+
+template <typename BinT>
+__global__ __launch_bounds__(256) void k_rotate(BinT* __restrict__ bins, int64_t n, int S,
+                                                const int32_t* __restrict__ hot)
+{
+    const int f = blockIdx.y;
+    const int h = hot[f];
+    BinT* col = bins + (int64_t)f * n;
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n;
+         r += (int64_t)gridDim.x * blockDim.x) {
+        int v = (int)col[r] - h;
+        if (v < 0) v += S;
+        col[r] = (BinT)v;
     }
 }
 
@@ -471,41 +582,106 @@ __device__ inline void lds_drain(unsigned long long* lds, int nf, int S, int pla
     }
 }
 
-// Sum the tile's copies (wide) or take the drained accumulator (packed) and
-// write the tile to the level buffer: a plain store when the item covers its
-// whole node, an int64 atomic add otherwise.
-template <int ACC>
+// ---------------------------------------------------------------------------
+// The skipped slot.  Each feature has one slot -- the one holding the most
+// rows of the matrix, found at upload -- whose adds the fills skip.  The
+// stored bins are rotated per feature so that this slot reads as 0 (a compare
+// with a constant), and each item recovers the slot's cell at the end as the
+// item's row totals minus the feature's other cells.  A hot bin (a skewed
+// feature, or the missing slot of a sparse column) would otherwise send most
+// lanes of a wave to one LDS word, which serializes the atomics; here it costs
+// nothing.  Exact: the recovery is an integer subtraction.
+// ---------------------------------------------------------------------------
+constexpr int kFixWords = 2 + 2 * 32;   // the item's row totals, then (g, h) per feature (<= 32)
+
+// The slot that rotated value s of a feature with rotation rot stands for.
+__device__ inline int unrotate(int s, int rot, int S)
+{
+    const int r = s + rot;
+    return r >= S ? r - S : r;
+}
+
+// The item's row totals into fix[0..1] (zeroed with the tile): each thread's
+// sums, wave-reduced, then one LDS atomic pair per wave.  Every thread calls.
+__device__ inline void add_item_totals(long long g, long long h, unsigned long long* fix)
+{
+    g = wave_sum_i64(g);
+    h = wave_sum_i64(h);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        atomicAdd(&fix[0], (unsigned long long)g);
+        atomicAdd(&fix[1], (unsigned long long)h);
+    }
+}
+
+// Sum the tile's copies (wide) or take the drained accumulator (packed),
+// recover each feature's skipped cell, and write the tile to the level
+// buffer at the real slots: a plain store when the item covers its whole
+// node, an int64 atomic add otherwise.  rot: the tile's rotations; fix: the
+// item's totals (complete: callers synchronize after add_item_totals).
+template <int ACC, bool SKIP>
 __device__ inline void lds_finish(unsigned long long* lds, int nf, int S, int plane, int lc,
-                                  unsigned long long* out, bool atomic_merge)
+                                  unsigned long long* out, bool atomic_merge,
+                                  const int32_t* __restrict__ rot, unsigned long long* fix)
 {
     if (ACC == kPacked) {
         lds_drain(lds, nf, S, plane, lc);
         __syncthreads();
     }
-    const int cells = nf * S;
     const int C = 1 << lc;
     const long long* acc = (const long long*)(lds + nf * plane);
-    for (int i = threadIdx.x; i < cells; i += blockDim.x) {
-        long long g = 0, h = 0;
+    auto cell = [&](int f, int sl, long long& g, long long& h) {
+        g = 0;
+        h = 0;
         if (ACC == kWide) {
-            const int f = i / S;
-            const int sl = i - f * S;
             const unsigned long long* pg = lds + f * 2 * plane + (sl << lc);
             for (int cc = 0; cc < C; ++cc) {
-                const int c = (cc + i) & (C - 1);
+                const int c = (cc + sl) & (C - 1);   // rotated start: neighbouring lanes, other banks
                 g += (long long)pg[c];
                 h += (long long)pg[plane + c];
             }
         } else {
-            g = acc[2 * i];
-            h = acc[2 * i + 1];
+            g = acc[2 * (f * S + sl)];
+            h = acc[2 * (f * S + sl) + 1];
         }
-        if (atomic_merge) {
-            if (g) atomicAdd(&out[2 * i], (unsigned long long)g);
-            if (h) atomicAdd(&out[2 * i + 1], (unsigned long long)h);
+    };
+    // each feature's skipped cell: the item's totals minus its other cells
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = (int)(blockDim.x / kWave);
+    const long long tg = (long long)fix[0], th = (long long)fix[1];
+    for (int f = (int)(threadIdx.x / kWave); SKIP && f < nf; f += waves) {
+        long long sg = 0, sh = 0;
+        for (int sl = 1 + lane; sl < S; sl += kWave) {
+            long long g, h;
+            cell(f, sl, g, h);
+            sg += g;
+            sh += h;
+        }
+        sg = wave_sum_i64(sg);
+        sh = wave_sum_i64(sh);
+        if (lane == 0) {
+            fix[2 + 2 * f] = (unsigned long long)(tg - sg);
+            fix[3 + 2 * f] = (unsigned long long)(th - sh);
+        }
+    }
+    if (SKIP) __syncthreads();
+    const int cells = nf * S;
+    for (int i = threadIdx.x; i < cells; i += blockDim.x) {
+        const int f = i / S;
+        const int sl = i - f * S;
+        long long g, h;
+        if (SKIP && sl == 0) {
+            g = (long long)fix[2 + 2 * f];
+            h = (long long)fix[3 + 2 * f];
         } else {
-            out[2 * i] = (unsigned long long)g;
-            out[2 * i + 1] = (unsigned long long)h;
+            cell(f, sl, g, h);
+        }
+        const int o = SKIP ? f * S + unrotate(sl, rot[f], S) : i;
+        if (atomic_merge) {
+            if (g) atomicAdd(&out[2 * o], (unsigned long long)g);
+            if (h) atomicAdd(&out[2 * o + 1], (unsigned long long)h);
+        } else {
+            out[2 * o] = (unsigned long long)g;
+            out[2 * o + 1] = (unsigned long long)h;
         }
     }
 }
@@ -551,13 +727,14 @@ struct RootStep {
     Bins8<BinT> b[NF];
 };
 
-template <typename BinT, int NF, int ACC>
+template <typename BinT, int NF, int ACC, bool SKIP>
 __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bins, int64_t n,
                                                     int n_features, int S, int lc,
                                                     const int2* __restrict__ q,
                                                     const FillItem* __restrict__ items, int n_items,
                                                     int vec_ok, int drain,
-                                                    unsigned long long* __restrict__ hist)
+                                                    unsigned long long* __restrict__ hist,
+                                                    const int32_t* __restrict__ rot)
 {
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
@@ -565,8 +742,10 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     const FillItem it = items[item];
     const int f0 = it.f0_nf & 0xffff;   // every item of this launch has exactly NF features
     const int plane = S << lc;
-    lds_zero(lds, tile_words(ACC, NF, S, lc));
+    unsigned long long* const fix = lds + tile_words(ACC, NF, S, lc);
+    lds_zero(lds, tile_words(ACC, NF, S, lc) + kFixWords);
     __syncthreads();
+    long long tg = 0, th = 0;   // the item's row totals (this thread's share)
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
     const BinT* const col0 = bins + (int64_t)f0 * n;
@@ -590,16 +769,30 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
             const int4 qq = st.q[j >> 1];
             const int gv = live ? ((j & 1) ? qq.z : qq.x) : 0;
             const int hv = live ? ((j & 1) ? qq.w : qq.y) : 0;
+            if (SKIP) {
+                tg += gv;
+                th += hv;
+            }
             const CellVal v = cell_val<ACC>(gv, hv);
 #pragma unroll
-            for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, st.b[f].at(j), v);
+            for (int f = 0; f < NF; ++f) {
+                const int b = st.b[f].at(j);
+                if (!SKIP || b != 0) lds_add<ACC>(lcopy, plane, lc, f, b, v);   // 0: the skipped slot
+            }
         }
     };
     auto add_row = [&](int64_t r) {
         const int2 g = q[r];
+        if (SKIP) {
+            tg += g.x;
+            th += g.y;
+        }
         const CellVal v = cell_val<ACC>(g.x, g.y);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) lds_add<ACC>(lcopy, plane, lc, f, (int)col0[(int64_t)f * n + r], v);
+        for (int f = 0; f < NF; ++f) {
+            const int b = (int)col0[(int64_t)f * n + r];
+            if (!SKIP || b != 0) lds_add<ACC>(lcopy, plane, lc, f, b, v);
+        }
     };
     // packed: decode the copies into the accumulator every `drain` steps (the
     // step loop is uniform across the block, so the barriers are too)
@@ -645,10 +838,11 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
             if (ACC == kPacked && ++dcount == drain * R) { drain_now(); dcount = 0; }
         }
     }
+    if (SKIP) add_item_totals(tg, th, fix);
     __syncthreads();
-    lds_finish<ACC>(lds, NF, S, plane, lc,
-                    hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                    it.dest == kDestAtomic);
+    lds_finish<ACC, SKIP>(lds, NF, S, plane, lc,
+                          hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                          it.dest == kDestAtomic, rot + f0, fix);
 }
 
 // Level fills read their rows through the row index.  Each thread takes
@@ -695,22 +889,25 @@ __device__ inline void check_entries(Entries<E>& en, int64_t n)
 
 // Feature-major level fill (wide matrices): NF features per block, each bin a
 // scattered one-element load.
-template <typename BinT, int NF, int ACC>
+template <typename BinT, int NF, int ACC, bool SKIP>
 __device__ inline void fill_cols_item(unsigned long long* lds, const FillItem& it,
                                       const BinT* __restrict__ bins, int64_t n, int n_features,
                                       int S, int lc, const int2* __restrict__ gh,
                                       const int32_t* __restrict__ row_index, int drain,
                                       unsigned long long* __restrict__ hist,
-                                      unsigned long long* __restrict__ partial)
+                                      unsigned long long* __restrict__ partial,
+                                      const int32_t* __restrict__ rot)
 {
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= NF
     const int plane = S << lc;
-    lds_zero(lds, tile_words(ACC, nf, S, lc));
+    unsigned long long* const fix = lds + tile_words(ACC, nf, S, lc);
+    lds_zero(lds, tile_words(ACC, nf, S, lc) + kFixWords);
     __syncthreads();
+    long long tg = 0, th = 0;   // the item's row totals (this thread's share)
 
     unsigned long long* const lcopy = lds + (threadIdx.x & ((1 << lc) - 1));
-    const int idle_bin = (int)((threadIdx.x >> lc) % (unsigned)S);
+    const int idle_bin = SKIP ? 0 : (int)((threadIdx.x >> lc) % (unsigned)S);
     const BinT* const col0 = bins + (int64_t)f0 * n;
     const int64_t rb = it.row_begin, re = it.row_end;
     constexpr int E = cols_entries(NF);
@@ -725,15 +922,23 @@ __device__ inline void fill_cols_item(unsigned long long* lds, const FillItem& i
 #pragma unroll
             for (int e = 0; e < E; ++e) d.b[f][e] = (int)col0[(int64_t)(f < nf ? f : nf - 1) * n + en.r[e]];
     };
+    // An idle entry adds zero to a lane's own bin (SKIP: reads as the skipped
+    // slot 0, so it adds nothing).
     auto accumulate = [&](const Entries<E>& en, const Data& d) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            // branch-free, as in the row-major fill
             const bool ok = en.ok[e];
-            const CellVal v = cell_val<ACC>(ok ? en.g[e].x : 0, ok ? en.g[e].y : 0);
+            const int gv = ok ? en.g[e].x : 0, hv = ok ? en.g[e].y : 0;
+            if (SKIP) {
+                tg += gv;
+                th += hv;
+            }
+            const CellVal v = cell_val<ACC>(gv, hv);
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
-                if (f < nf) lds_add<ACC>(lcopy, plane, lc, f, ok ? d.b[f][e] : idle_bin, v);
+            for (int f = 0; f < NF; ++f) {
+                const int b = ok ? d.b[f][e] : idle_bin;
+                if (f < nf && (!SKIP || b != 0)) lds_add<ACC>(lcopy, plane, lc, f, b, v);
+            }
         }
     };
 
@@ -759,18 +964,19 @@ __device__ inline void fill_cols_item(unsigned long long* lds, const FillItem& i
         ea = eb;
         base = nb;
     }
+    if (SKIP) add_item_totals(tg, th, fix);
     __syncthreads();
-    lds_finish<ACC>(lds, nf, S, plane, lc,
-                    (it.dest == kDestPartial ? partial : hist) +
-                        ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
-                    it.dest == kDestAtomic);
+    lds_finish<ACC, SKIP>(lds, nf, S, plane, lc,
+                          (it.dest == kDestPartial ? partial : hist) +
+                              ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
+                          it.dest == kDestAtomic, rot + f0, fix);
 }
 
 
 // Level fills run one block per CU-sized share of the level: block b takes
 // the items [block_first[b], block_first[b + 1]) in turn -- consecutive pieces
 // of the level order, one per node that the share touches.
-template <typename BinT, int NF, int ACC>
+template <typename BinT, int NF, int ACC, bool SKIP>
 __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
                                                    int n_features, int S, int lc,
                                                    const int2* __restrict__ gh,
@@ -778,15 +984,16 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
                                                    const FillItem* __restrict__ items,
                                                    const int32_t* __restrict__ block_first, int n_blocks,
                                                    int drain, unsigned long long* __restrict__ hist,
-                                                   unsigned long long* __restrict__ partial)
+                                                   unsigned long long* __restrict__ partial,
+                                                   const int32_t* __restrict__ rot)
 {
     extern __shared__ unsigned long long lds[];
     const int blk = xcd_item(blockIdx.x, n_blocks);
     if (blk >= n_blocks) return;
     const int i1 = block_first[blk + 1];
     for (int ii = block_first[blk]; ii < i1; ++ii) {
-        fill_cols_item<BinT, NF, ACC>(lds, items[ii], bins, n, n_features, S, lc, gh, row_index,
-                                      drain, hist, partial);
+        fill_cols_item<BinT, NF, ACC, SKIP>(lds, items[ii], bins, n, n_features, S, lc, gh, row_index,
+                                      drain, hist, partial, rot);
         __syncthreads();
     }
 }
@@ -870,20 +1077,57 @@ __device__ inline void reg_drain(unsigned long long* lds, int cells, int S, int 
     }
 }
 
-template <int RA>
-__device__ inline void reg_finish(const RegAcc<RA>& a, int cells, unsigned long long* out,
-                                  bool atomic_merge)
+// Write the register accumulator: each feature's skipped cell is the item's
+// totals minus the feature's other cells (summed into fix[2 + 2f], zeroed with
+// the tile; one LDS atomic pair per wave when a wave's cells share a feature),
+// and every cell goes to its real slot.
+template <int RA, bool SKIP>
+__device__ inline void reg_finish(const RegAcc<RA>& a, int cells, int S, unsigned long long* out,
+                                  bool atomic_merge, const int32_t* __restrict__ rot,
+                                  unsigned long long* fix)
 {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < (SKIP ? RA : 0); ++k) {
+        const int i = threadIdx.x + k * blockDim.x;
+        const bool live = i < cells;
+        const int f = live ? i / S : -1;
+        const int sl = live ? i - f * S : 0;
+        long long g = (live && sl != 0) ? a.g[k] : 0;
+        long long h = (live && sl != 0) ? a.h[k] : 0;
+        const int fw = __shfl(f, 0, kWave);
+        if (__all(f == fw)) {   // wave-uniform: one atomic pair
+            g = wave_sum_i64(g);
+            h = wave_sum_i64(h);
+            if (lane == 0 && fw >= 0) {
+                atomicAdd(&fix[2 + 2 * fw], (unsigned long long)g);
+                atomicAdd(&fix[3 + 2 * fw], (unsigned long long)h);
+            }
+        } else if (live && sl != 0) {
+            atomicAdd(&fix[2 + 2 * f], (unsigned long long)g);
+            atomicAdd(&fix[3 + 2 * f], (unsigned long long)h);
+        }
+    }
+    if (SKIP) __syncthreads();
+    const long long tg = (long long)fix[0], th = (long long)fix[1];
 #pragma unroll
     for (int k = 0; k < RA; ++k) {
         const int i = threadIdx.x + k * blockDim.x;
         if (i < cells) {
+            const int f = i / S;
+            const int sl = i - f * S;
+            long long g = a.g[k], h = a.h[k];
+            if (SKIP && sl == 0) {
+                g = tg - (long long)fix[2 + 2 * f];
+                h = th - (long long)fix[3 + 2 * f];
+            }
+            const int o = SKIP ? f * S + unrotate(sl, rot[f], S) : i;
             if (atomic_merge) {
-                if (a.g[k]) atomicAdd(&out[2 * i], (unsigned long long)a.g[k]);
-                if (a.h[k]) atomicAdd(&out[2 * i + 1], (unsigned long long)a.h[k]);
+                if (g) atomicAdd(&out[2 * o], (unsigned long long)g);
+                if (h) atomicAdd(&out[2 * o + 1], (unsigned long long)h);
             } else {
-                out[2 * i] = (unsigned long long)a.g[k];
-                out[2 * i + 1] = (unsigned long long)a.h[k];
+                out[2 * o] = (unsigned long long)g;
+                out[2 * o + 1] = (unsigned long long)h;
             }
         }
     }
@@ -891,14 +1135,15 @@ __device__ inline void reg_finish(const RegAcc<RA>& a, int cells, unsigned long 
 
 // RA > 0 (packed only): register accumulator of RA cells per thread; E
 // entries per thread and step.
-template <typename BinT, int LT, int ACC, int RA, int E>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
                                       int64_t n, int n_features, int S, int lc,
                                       const int2* __restrict__ q,
                                       const int32_t* __restrict__ row_index, int drain,
                                       unsigned long long* __restrict__ hist,
-                                      unsigned long long* __restrict__ partial, int& bad)
+                                      unsigned long long* __restrict__ partial, int& bad,
+                                      const int32_t* __restrict__ rot)
 {
     static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
     const int f0 = it.f0_nf & 0xffff;
@@ -906,8 +1151,10 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     constexpr int TF = LT / (int)sizeof(BinT);
     const int plane = S << lc;
     const int cells = nf * S;
-    lds_zero(lds, nf * (ACC == kWide ? 2 : 1) * plane);
+    unsigned long long* const fix = lds + nf * (ACC == kWide ? 2 : 1) * plane;
+    lds_zero(lds, nf * (ACC == kWide ? 2 : 1) * plane + kFixWords);
     __syncthreads();
+    long long tg = 0, th = 0;   // the item's row totals (this thread's share)
     RegAcc<(RA > 0 ? RA : 1)> racc;
 #pragma unroll
     for (int k = 0; k < (RA > 0 ? RA : 1); ++k) racc.g[k] = racc.h[k] = 0;
@@ -954,6 +1201,10 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             if (!d.ok[e]) continue;
+            if (SKIP) {
+                tg += d.g[e].x;
+                th += d.g[e].y;
+            }
             const CellVal v = cell_val<ACC>(d.g[e].x, d.g[e].y);
             // The feature's base offset is stepped here rather than hoisted:
             // 32 hoisted values would not fit the scalar registers.
@@ -964,7 +1215,7 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
                 const uint32_t w = d.c[e].word((f * (int)sizeof(BinT)) >> 2);
                 const int b = sizeof(BinT) == 1 ? (int)((w >> (8 * (f & 3))) & 0xffu)
                                                 : (int)((w >> (16 * (f & 1))) & 0xffffu);
-                lds_add_at<ACC>(lds + fb, cpy, plane, lc, 0, b, v);
+                if (!SKIP || b != 0) lds_add_at<ACC>(lds + fb, cpy, plane, lc, 0, b, v);   // 0: skipped
                 fb += (ACC == kWide ? 2 : 1) * plane;
                 asm volatile("" : "+s"(fb));
             }
@@ -1003,19 +1254,20 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
         if (s + 1 >= n_steps) break;
         run_step(s + 1, d1, d0);
     }
+    if (SKIP) add_item_totals(tg, th, fix);
     __syncthreads();
     unsigned long long* const out = (it.dest == kDestPartial ? partial : hist) +
                                     ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2;
     if (RA > 0) {
         reg_drain(lds, cells, S, plane, lc, racc);
-        reg_finish(racc, cells, out, it.dest == kDestAtomic);
+        reg_finish<(RA > 0 ? RA : 1), SKIP>(racc, cells, S, out, it.dest == kDestAtomic, rot + f0, fix);
     } else {
-        lds_finish<ACC>(lds, nf, S, plane, lc, out, it.dest == kDestAtomic);
+        lds_finish<ACC, SKIP>(lds, nf, S, plane, lc, out, it.dest == kDestAtomic, rot + f0, fix);
     }
 }
 
 
-template <typename BinT, int LT, int ACC, int RA, int E>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP>
 __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
                                                    int S, int lc, const int2* __restrict__ q,
@@ -1024,7 +1276,8 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
                                                    const int32_t* __restrict__ block_first, int n_blocks,
                                                    int drain, unsigned long long* __restrict__ hist,
                                                    unsigned long long* __restrict__ partial,
-                                                   uint32_t* __restrict__ err)
+                                                   uint32_t* __restrict__ err,
+                                                   const int32_t* __restrict__ rot)
 {
     extern __shared__ unsigned long long lds[];
     const int blk = xcd_item(blockIdx.x, n_blocks);
@@ -1032,8 +1285,8 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
     const int i1 = block_first[blk + 1];
     int bad = 0;   // a row index outside [0, n): skipped, and flagged
     for (int ii = block_first[blk]; ii < i1; ++ii) {
-        fill_rows_item<BinT, LT, ACC, RA, E>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
-                                             lc, q, row_index, drain, hist, partial, bad);
+        fill_rows_item<BinT, LT, ACC, RA, E, SKIP>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
+                                             lc, q, row_index, drain, hist, partial, bad, rot);
         __syncthreads();
     }
     if (bad) atomicOr(err, kErrRowIndex);
@@ -1078,26 +1331,6 @@ struct FeatureBest {
     long long h_left;
 };
 
-__device__ inline long long wave_shfl_up_i64(long long v, int d)
-{
-    int lo = __shfl_up((int)(v & 0xffffffffll), d, kWave);
-    int hi = __shfl_up((int)(v >> 32), d, kWave);
-    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
-
-__device__ inline long long wave_shfl_i64(long long v, int src)
-{
-    int lo = __shfl((int)(v & 0xffffffffll), src, kWave);
-    int hi = __shfl((int)(v >> 32), src, kWave);
-    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
-
-__device__ inline long long wave_shfl_xor_i64(long long v, int mask)
-{
-    int lo = __shfl_xor((int)(v & 0xffffffffll), mask, kWave);
-    int hi = __shfl_xor((int)(v >> 32), mask, kWave);
-    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
 
 // (gain, code) order: larger gain first; on equal gains the smaller code.
 // A code of -1 marks "no candidate" and loses to any candidate.
@@ -1533,12 +1766,6 @@ __global__ __launch_bounds__(256) void k_level_sum(const double* __restrict__ te
     }
 }
 
-// Sums over a wave of int64 values.
-__device__ inline long long wave_sum_i64(long long v)
-{
-    for (int off = kWave / 2; off > 0; off >>= 1) v += wave_shfl_xor_i64(v, off);
-    return v;
-}
 
 // The winner: block results scanned in order per thread, then the block
 // argmax.  Writes the level record (its integer sums zeroed, for
@@ -1677,6 +1904,7 @@ static_assert(kPartChunk == 1024 * kPartRows, "a chunk is one pass of a 1024-thr
 // (1 = left) for the scatter.
 template <typename BinT>
 __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
+                                                     int S, const int32_t* __restrict__ rot,
                                                      const int32_t* __restrict__ row_index,
                                                      const PartItem* __restrict__ items,
                                                      const SplitOut* __restrict__ splits,
@@ -1689,6 +1917,7 @@ __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bi
     int c = 0;
     if (sp.feature >= 0) {   // uniform
         const BinT* col = bins + (int64_t)sp.feature * n;
+        const int rf = rot[sp.feature];   // stored values are rotated per feature
         const int k0 = it.begin + (int)threadIdx.x * kPartRows;
         int64_t r[kPartRows];
 #pragma unroll
@@ -1702,7 +1931,7 @@ __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bi
         for (int j = 0; j < kPartRows; ++j) {
             const bool in = (uint64_t)r[j] < (uint64_t)n;
             bad |= !in && k0 + j < it.end;
-            v[j] = (int)col[in ? r[j] : 0];
+            v[j] = unrotate((int)col[in ? r[j] : 0], rf, S);
         }
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {

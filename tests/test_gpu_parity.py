@@ -259,6 +259,42 @@ def test_feature_major_levels(hgb, torch, missing, bits):
     run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
 
 
+def with_hot_slots(w, seed):
+    """The workload with hot slots planted: feature 0 constant, feature 1 with
+    90% of rows in bin 0, feature 2 with 90% in the last value bin, and (with
+    missing values) feature 3 with 60% missing -- so that the fills skip each
+    feature's most frequent slot and recover its cell by subtraction."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    b = w.bins.copy()
+    n = b.shape[1]
+    b[0, :] = 3 % w.n_bins
+    b[1, rng.random(n) < 0.9] = 0
+    b[2, rng.random(n) < 0.9] = w.n_bins - 1
+    if w.has_missing and b.shape[0] > 3:
+        b[3, rng.random(n) < 0.6] = w.n_bins
+    return dataclasses.replace(w, bins=b)
+
+
+@pytest.mark.parametrize("case", ["rows_u8", "rows_u16", "cols_u16"])
+@pytest.mark.parametrize("bits", [30, 19])
+def test_hot_slots(hgb, torch, case, bits):
+    """Matrices with hot slots (constant, skewed and mostly-missing features):
+    root and level histograms and splits equal the oracle's, through the
+    row-major fill (u8 and u16) and the feature-major fill."""
+    say("hot slots", case, bits)
+    if case == "rows_u8":
+        w = synth.random_small(120, 40_000, 6, 16, True, 8)
+    elif case == "rows_u16":
+        w = synth.random_small(121, 30_000, 5, 1024, True, 6, u16=True)
+    else:
+        w = synth.random_small(122, 1_200, 33_000, 64, True, 6, u16=True)
+    w = with_hot_slots(w, 7)
+    run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
+    if case != "cols_u16":
+        run_root_both(hgb, torch, w, bits=bits)
+
+
 def oracle_tree(w, depth, bits=30):
     qg, qh, kg, kh = oracle_quantized(w, bits)
     levels = []
