@@ -1382,7 +1382,9 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     if (!hist || !out) return fail(c, HGB_E_INVALID, "find_splits: null pointer");
     HGB_HIP(c, hipSetDevice(c->device));
     static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
-    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * c->F);
+    const int waves = 4;   // features per block; one best per block
+    const int n_entries = (c->F + waves - 1) / waves;
+    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * n_entries);
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
     if (st != HGB_OK) return st;
@@ -1391,8 +1393,7 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     // buffer is 16-byte aligned); otherwise read twice from memory
     const int per = (c->B + kWave - 1) / kWave;
     const bool aligned = ((uintptr_t)hist & 15) == 0;
-    const int waves = 4;
-    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_nodes);
+    dim3 grid((unsigned)n_entries, (unsigned)n_nodes);
 #define HGB_SPLIT(PER)                                                                              \
     k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
@@ -1405,7 +1406,7 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     else HGB_SPLIT(16);
 #undef HGB_SPLIT
     HGB_LAUNCHED(c, "k_split_feature");
-    k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F,
+    k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries,
                                                              (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");
     return HGB_OK;
@@ -1492,7 +1493,8 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     }
     HGB_HIP(c, hipSetDevice(c->device));
     const int n_nodes = 2 * n_pairs;
-    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * c->F);
+    const int n_entries = (c->F + 3) / 4;   // one best per block of 4 features
+    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * n_entries);
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
     if (st != HGB_OK) return st;
@@ -1507,7 +1509,7 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
         plan_dev = (const int32_t*)s->dev;
     }
     const int waves = 4;
-    dim3 grid((c->F + waves - 1) / waves, (unsigned)n_pairs);
+    dim3 grid((unsigned)n_entries, (unsigned)n_pairs);
     const double sg = std::ldexp(1.0, -c->k_g), sh = std::ldexp(1.0, -c->k_h);
     {
         ProfScope ps(c, HGB_KERNEL_SPLIT);
@@ -1522,7 +1524,7 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
         else HGB_SUBSPLIT(16);
 #undef HGB_SUBSPLIT
         HGB_LAUNCHED(c, "k_subtract_split");
-        k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, c->F, (SplitOut*)out);
+        k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries, (SplitOut*)out);
         HGB_LAUNCHED(c, "k_split_reduce");
     }
     return s ? stage_release(c, s) : HGB_OK;

@@ -1325,11 +1325,12 @@ __global__ __launch_bounds__(256) void k_subtract(const longlong2* __restrict__ 
 
 struct FeatureBest {
     double gain;
-    int32_t code;    // 2 * bin + (default left ? 1 : 0); -1 when no valid candidate
-    int32_t pad;
+    int32_t code;      // 2 * bin + (default left ? 1 : 0); -1 when no valid candidate
+    int32_t feature;   // the feature the candidate belongs to
     long long g_left;
     long long h_left;
 };
+
 
 
 // (gain, code) order: larger gain first; on equal gains the smaller code.
@@ -1341,6 +1342,18 @@ __device__ inline bool better(double ga, int ca, double gb, int cb)
     if (ga > gb) return true;
     if (ga < gb) return false;
     return ca < cb;
+}
+
+// The best of a block's waves (one feature each, in feature order), in the
+// serial order: larger gain, then the smaller feature.  s holds one entry per
+// wave; thread 0 returns the winner.
+__device__ inline FeatureBest block_feature_best(const FeatureBest* s, int waves)
+{
+    FeatureBest b = s[0];
+    for (int i = 1; i < waves; ++i)
+        if (better(s[i].gain, s[i].code < 0 ? -1 : s[i].feature, b.gain, b.code < 0 ? -1 : b.feature))
+            b = s[i];
+    return b;
 }
 
 #pragma clang fp contract(off)
@@ -1509,7 +1522,7 @@ __device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const Lan
     WaveBest r;
     r.fb.gain = rc < 0 ? -__builtin_inf() : rg;
     r.fb.code = rc;
-    r.fb.pad = 0;
+    r.fb.feature = -1;   // set by the caller
     r.fb.g_left = rc < 0 ? 0 : wgl;
     r.fb.h_left = rc < 0 ? 0 : whl;
     r.G = G;
@@ -1527,8 +1540,8 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
     return wave_scan<PER>(hf, s, n_bins, has_missing, scale_g, scale_h, lam, gamma);
 }
 
-// One wave per (node, feature), results to best[node][feature]; node totals
-// from feature 0.
+// One wave per (node, feature); the block's best of its features to
+// best[node][block]; node totals from feature 0.
 template <int PER>
 __global__ __launch_bounds__(256) void k_split_feature(const long long* __restrict__ hist,
                                                        int n_features, int n_bins, int S,
@@ -1537,16 +1550,27 @@ __global__ __launch_bounds__(256) void k_split_feature(const long long* __restri
                                                        FeatureBest* __restrict__ best,
                                                        long long* __restrict__ totals)
 {
+    __shared__ FeatureBest s_fb[256 / kWave];
     const int lane = threadIdx.x & (kWave - 1);
-    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int wv = threadIdx.x / kWave;
+    const int f = blockIdx.x * (blockDim.x / kWave) + wv;
     const int node = blockIdx.y;
-    if (f >= n_features) return;
-    const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
-    const WaveBest r = wave_feature_best<PER>(hf, n_bins, has_missing, scale_g, scale_h, lam, gamma);
-    if (lane == 0) {
-        best[(int64_t)node * n_features + f] = r.fb;
-        if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }
+    if (f < n_features) {   // uniform per wave
+        const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
+        const WaveBest r = wave_feature_best<PER>(hf, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+        if (lane == 0) {
+            s_fb[wv] = r.fb;
+            s_fb[wv].feature = f;
+            if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }
+        }
+    } else if (lane == 0) {
+        s_fb[wv].code = -1;
+        s_fb[wv].feature = -1;
+        s_fb[wv].gain = -__builtin_inf();
     }
+    __syncthreads();
+    if (threadIdx.x == 0)
+        best[(int64_t)node * gridDim.x + blockIdx.x] = block_feature_best(s_fb, blockDim.x / kWave);
 }
 
 // The level tail in one pass: one wave per (pair, feature) reads the parent
@@ -1563,41 +1587,57 @@ __global__ __launch_bounds__(256) void k_subtract_split(const long long* __restr
                                                         long long* __restrict__ totals)
 {
     static_assert(PER > 0, "the fused pass keeps the slots in registers");
+    __shared__ FeatureBest s_fb[2][256 / kWave];   // [0] the built child, [1] the other
     const int lane = threadIdx.x & (kWave - 1);
-    const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int wv = threadIdx.x / kWave;
+    const int f = blockIdx.x * (blockDim.x / kWave) + wv;
     const int pair = blockIdx.y;
-    if (f >= n_features) return;
     const int32_t pslot = plan ? plan[2 * pair] : inl.v[2 * pair];
     const int r = plan ? plan[2 * pair + 1] : inl.v[2 * pair + 1];
     const int nb = 2 * pair + r, no = 2 * pair + 1 - r;
-    const int64_t fs = (int64_t)S * 2;
-    const long long* hp = parent + ((int64_t)pslot * n_features + f) * fs;
-    const long long* hb = child + ((int64_t)nb * n_features + f) * fs;
-    long long* ho = child + ((int64_t)no * n_features + f) * fs;
-    LaneSlots<PER> sp, sb, so;
-    load_lane_slots<PER>(hp, n_bins, has_missing, sp);
-    load_lane_slots<PER>(hb, n_bins, has_missing, sb);
+    if (f >= n_features) {   // uniform per wave: no feature, no candidate
+        if (lane == 0)
+            for (int k = 0; k < 2; ++k) {
+                s_fb[k][wv].code = -1;
+                s_fb[k][wv].feature = -1;
+                s_fb[k][wv].gain = -__builtin_inf();
+            }
+    } else {
+        const int64_t fs = (int64_t)S * 2;
+        const long long* hp = parent + ((int64_t)pslot * n_features + f) * fs;
+        const long long* hb = child + ((int64_t)nb * n_features + f) * fs;
+        long long* ho = child + ((int64_t)no * n_features + f) * fs;
+        LaneSlots<PER> sp, sb, so;
+        load_lane_slots<PER>(hp, n_bins, has_missing, sp);
+        load_lane_slots<PER>(hb, n_bins, has_missing, sb);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(sp.v[j].x - sb.v[j].x, sp.v[j].y - sb.v[j].y);
-    so.miss = make_longlong2(sp.miss.x - sb.miss.x, sp.miss.y - sb.miss.y);
-    longlong2* o2 = (longlong2*)ho;
-    const int b0 = lane * PER;
+        for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(sp.v[j].x - sb.v[j].x, sp.v[j].y - sb.v[j].y);
+        so.miss = make_longlong2(sp.miss.x - sb.miss.x, sp.miss.y - sb.miss.y);
+        longlong2* o2 = (longlong2*)ho;
+        const int b0 = lane * PER;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if (b0 + j < n_bins) o2[b0 + j] = so.v[j];
-    if (has_missing && lane == 0) o2[n_bins] = so.miss;
-    const WaveBest wb = wave_scan<PER>(hb, sb, n_bins, has_missing, scale_g, scale_h, lam, gamma);
-    const WaveBest wo = wave_scan<PER>(ho, so, n_bins, has_missing, scale_g, scale_h, lam, gamma);
-    if (lane == 0) {
-        best[(int64_t)nb * n_features + f] = wb.fb;
-        best[(int64_t)no * n_features + f] = wo.fb;
-        if (f == 0) {
-            totals[2 * nb] = wb.G;
-            totals[2 * nb + 1] = wb.H;
-            totals[2 * no] = wo.G;
-            totals[2 * no + 1] = wo.H;
+        for (int j = 0; j < PER; ++j)
+            if (b0 + j < n_bins) o2[b0 + j] = so.v[j];
+        if (has_missing && lane == 0) o2[n_bins] = so.miss;
+        const WaveBest wb = wave_scan<PER>(hb, sb, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+        const WaveBest wo = wave_scan<PER>(ho, so, n_bins, has_missing, scale_g, scale_h, lam, gamma);
+        if (lane == 0) {
+            s_fb[0][wv] = wb.fb;
+            s_fb[0][wv].feature = f;
+            s_fb[1][wv] = wo.fb;
+            s_fb[1][wv].feature = f;
+            if (f == 0) {
+                totals[2 * nb] = wb.G;
+                totals[2 * nb + 1] = wb.H;
+                totals[2 * no] = wo.G;
+                totals[2 * no + 1] = wo.H;
+            }
         }
     }
+    __syncthreads();
+    if (threadIdx.x < 2)
+        best[(int64_t)(threadIdx.x == 0 ? nb : no) * gridDim.x + blockIdx.x] =
+            block_feature_best(s_fb[threadIdx.x], blockDim.x / kWave);
 }
 
 struct SplitOut {
@@ -1610,21 +1650,23 @@ struct SplitOut {
 // and then reducing across threads with the same (gain, feature) order.
 __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restrict__ best,
                                                       const long long* __restrict__ totals,
-                                                      int n_features, SplitOut* __restrict__ out)
+                                                      int n_entries, SplitOut* __restrict__ out)
 {
     __shared__ double s_gain[256];
     __shared__ int s_feat[256];
+    __shared__ int s_entry[256];
     const int node = blockIdx.x;
-    const FeatureBest* nb = best + (int64_t)node * n_features;
+    const FeatureBest* nb = best + (int64_t)node * n_entries;
     double bg = 0.0;
-    int bf = -1;
-    for (int f = threadIdx.x; f < n_features; f += blockDim.x) {
-        const FeatureBest c = nb[f];
+    int bf = -1, be = -1;
+    for (int e = threadIdx.x; e < n_entries; e += blockDim.x) {   // entries in feature order
+        const FeatureBest c = nb[e];
         if (c.code < 0) continue;
-        if (bf < 0 || c.gain > bg) { bg = c.gain; bf = f; }
+        if (bf < 0 || c.gain > bg) { bg = c.gain; bf = c.feature; be = e; }
     }
     s_gain[threadIdx.x] = bg;
     s_feat[threadIdx.x] = bf;
+    s_entry[threadIdx.x] = be;
     __syncthreads();
     for (int w = blockDim.x / 2; w > 0; w >>= 1) {
         if (threadIdx.x < w) {
@@ -1633,6 +1675,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restr
             if (better(og, of, s_gain[threadIdx.x], s_feat[threadIdx.x])) {
                 s_gain[threadIdx.x] = og;
                 s_feat[threadIdx.x] = of;
+                s_entry[threadIdx.x] = s_entry[threadIdx.x + w];
             }
         }
         __syncthreads();
@@ -1648,7 +1691,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restr
             o.gain = -__builtin_inf();
             o.g_left = 0; o.h_left = 0;
         } else {
-            const FeatureBest c = nb[f];
+            const FeatureBest c = nb[s_entry[0]];
             o.feature = f;
             o.bin = c.code >> 1;
             o.default_left = c.code & 1;
