@@ -17,6 +17,7 @@ built from rows) per second over the timed steps, in G cell-updates/s.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -281,7 +282,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 3; 25 for --grow / --oblivious, whose "
+                         "first few dozen trees run slower while the allocator and the device warm up)")
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -302,6 +305,8 @@ def main():
                          "P <= 19 selects the packed one-atomic fill")
     args = ap.parse_args()
 
+    if args.warmup is None:
+        args.warmup = 25 if (args.grow or args.oblivious) else 3
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -346,6 +351,11 @@ def main():
         del levels
     log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
 
+    # The set-up made millions of Python objects (torch's own, the workload);
+    # a full collection of them in the middle of the timed steps stalls the
+    # host for tens of milliseconds.  Freeze them out of the collector.
+    gc.collect()
+    gc.freeze()
     for _ in range(args.warmup):
         step(ctx, w, plan, g, h)
     ctx.sync()

@@ -56,6 +56,10 @@ constexpr int kMaxBlocks = 4096;
 constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 16;
 
+// Initial capacity of an upload stage: larger than any level's plan of the
+// workloads here (C4's level-3 fill plan is about 70 KB).
+constexpr size_t kStageMinBytes = 256 * 1024;
+
 struct Stage {
     void* host = nullptr;   // pinned
     void* dev = nullptr;
@@ -115,6 +119,7 @@ struct hgb_ctx {
     uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
     int32_t* rot = nullptr;           // per feature: the skipped slot (stored bins are rotated by it)
     bool skip = false;                // the fills skip each feature's slot 0 (a hot slot exists)
+    hipEvent_t part_ready = nullptr;  // partition: the node records are on the host
 
     Stage stage[kStages];
     int stage_next = 0;
@@ -195,11 +200,13 @@ hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
         s.pending = false;
     }
     if (bytes > s.cap) {
+        // Reallocating pinned memory is slow (and a free synchronizes the
+        // device), so a stage starts large and at least doubles.
         if (s.host) HGB_HIP(c, hipHostFree(s.host));
         if (s.dev) HGB_HIP(c, hipFree(s.dev));
         s.host = s.dev = nullptr;
+        const size_t want = std::max<size_t>(std::max<size_t>(bytes, 2 * s.cap), kStageMinBytes);
         s.cap = 0;
-        size_t want = std::max<size_t>(bytes, 4096);
         HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
         HGB_HIP(c, hipMalloc(&s.dev, want));
         s.cap = want;
@@ -928,6 +935,7 @@ void hgb_destroy(hgb_ctx* c)
             (void)hipEventDestroy(pr.second);
         }
     for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+    if (c->part_ready) (void)hipEventDestroy(c->part_ready);
     (void)hipFree(c->bins);
     (void)hipFree(c->bins_rm);
     (void)hipFree(c->q);
@@ -1624,17 +1632,22 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         HGB_LAUNCHED(c, "k_part_scan");
         HGB_HIP(c, hipMemcpyAsync(c->part_host, node_out, sizeof(int32_t) * 3 * (size_t)n_nodes,
                                   hipMemcpyDeviceToHost, c->stream));
+        // the count pass has set the error word by now too
+        HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost, c->stream));
+        if (!c->part_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->part_ready, hipEventDisableTiming));
+        HGB_HIP(c, hipEventRecord(c->part_ready, c->stream));
         if (n_items > 0) {
             k_part_scatter<<<(unsigned)n_items, 1024, 0, c->stream>>>(row_index, items_dev, sp, c->part_flags,
                                                                       left_base, node_out, out_rows);
             HGB_LAUNCHED(c, "k_part_scatter");
         }
     }
-    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost, c->stream));
     st = stage_release(c, sg);
     if (st != HGB_OK) return st;
-    HGB_HIP(c, hipStreamSynchronize(c->stream));   // the one wait: node records and error word
-    st = take_flags(c);                            // a row index outside [0, n)
+    // Wait for the node records only: the scatter keeps running while the
+    // caller plans the next level (the stream orders whatever reads its rows).
+    HGB_HIP(c, hipEventSynchronize(c->part_ready));
+    st = take_flags(c);   // a row index outside [0, n)
     if (st != HGB_OK) return st;
     int32_t nc = 0;
     child_offsets[0] = 0;

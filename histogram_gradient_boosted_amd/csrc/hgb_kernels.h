@@ -1146,6 +1146,7 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
                                       const int32_t* __restrict__ rot)
 {
     static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
+    static_assert(LT / (int)sizeof(BinT) <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= LT / sizeof(BinT)
     constexpr int TF = LT / (int)sizeof(BinT);
@@ -1607,12 +1608,13 @@ __global__ __launch_bounds__(256) void k_subtract_split(const long long* __restr
         const long long* hp = parent + ((int64_t)pslot * n_features + f) * fs;
         const long long* hb = child + ((int64_t)nb * n_features + f) * fs;
         long long* ho = child + ((int64_t)no * n_features + f) * fs;
-        LaneSlots<PER> sp, sb, so;
-        load_lane_slots<PER>(hp, n_bins, has_missing, sp);
+        // the parent's slots become the other child's in place (fewer registers)
+        LaneSlots<PER> so, sb;
+        load_lane_slots<PER>(hp, n_bins, has_missing, so);
         load_lane_slots<PER>(hb, n_bins, has_missing, sb);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(sp.v[j].x - sb.v[j].x, sp.v[j].y - sb.v[j].y);
-        so.miss = make_longlong2(sp.miss.x - sb.miss.x, sp.miss.y - sb.miss.y);
+        for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(so.v[j].x - sb.v[j].x, so.v[j].y - sb.v[j].y);
+        so.miss = make_longlong2(so.miss.x - sb.miss.x, so.miss.y - sb.miss.y);
         longlong2* o2 = (longlong2*)ho;
         const int b0 = lane * PER;
 #pragma unroll

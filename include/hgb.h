@@ -300,8 +300,10 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* ctx, const int64_t* parent_dev, int
  * n_children_host:      on return, 2c for c nodes with a split.
  * parent_node_host:     int32 [n_nodes] or NULL; on return entry j holds the
  *                       node whose children are 2j and 2j + 1.
- * Synchronizes the stream (the host needs the child sizes).  A row index
- * outside [0, n) is routed right and reported as HGB_E_INVALID by this call.
+ * Waits until the child sizes are on the host (the host plans the next level
+ * from them); the scatter of the rows may still be running then, ordered on
+ * the stream before any later work.  A row index outside [0, n) is routed
+ * right and reported as HGB_E_INVALID by this call.
  * Errors: HGB_E_STATE before upload_bins; HGB_E_INVALID for null pointers or
  *         bad offsets, n_nodes outside [1, 65535].
  */
