@@ -164,3 +164,34 @@ def test_c3_tree_device_partition(hgb, torch, n, bits):
         assert np.array_equal(lv.hist.cpu().numpy(), hist), f"level {d} histograms differ"
         assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"level {d}")
     ctx.close()
+
+
+@pytest.mark.parametrize("case", ["hot_u8", "c5"])
+def test_tree_device_partition_hot_slots(hgb, torch, case):
+    """A tree grown with the device partition on matrices whose stored bins are
+    rotated (a hot slot exists: constant, skewed and mostly-missing features,
+    or c5's 40% missing): the partition compares real bin values, and every
+    level equals the oracle's."""
+    say("device tree hot slots", case)
+    from histogram_gradient_boosted_amd import tree
+    from test_gpu_parity import with_hot_slots
+    if case == "hot_u8":
+        w = with_hot_slots(synth.random_small(123, 60_000, 6, 16, True, 0), 9)
+        depth = 6
+    else:
+        w = synth.make("c5", n_rows=200_000)
+        depth = 6
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    levels = tree.grow_tree_device(ctx, g, h, depth, w.lam, w.gamma)
+    want = oracle_tree(w, depth, 30)
+    assert len(levels) == len(want)
+    for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(levels, want)):
+        if d > 0:
+            assert np.array_equal(lv.offsets.astype(np.int64), offs), f"level {d} offsets"
+            assert np.array_equal(lv.rows.cpu().numpy()[: int(offs[-1])], rows), f"level {d} rows"
+        assert np.array_equal(lv.hist.cpu().numpy(), hist), f"level {d} histograms differ"
+        assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"level {d}")
+    ctx.close()
