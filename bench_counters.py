@@ -37,8 +37,9 @@ COPY_BYTES = 1 << 30
 FILL_CLASS = ("k_fill_root", "k_fill_rows", "k_fill_cols", "k_merge")
 OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_subtract_split", "k_split_feature",
          "k_split_reduce", "k_quantize", "k_grad_hess_max")
-# one --pmc pass of SQ counters for the LDS side of the fill (4 of the 8 SQ slots)
-LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT")
+# one --pmc pass of SQ counters for the LDS side of the fill (5 of the 8 SQ slots)
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_ATOMIC", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                "SQ_LDS_ADDR_CONFLICT")
 SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boosted_amd/csrc/*.h",
            "include/*.h")
 
@@ -271,12 +272,12 @@ def main() -> None:
               f"({fill_fetch:,} fetched, {fill_write:,} written).", "",
               f"LDS counters per step (rocprofv3 --pmc {' '.join(LDS_COUNTERS)}, same differencing; "
               "summed over the chip's SQs; IDX_ACTIVE and the conflicts are cycles):", "",
-              "| kernel | LDS instructions | LDS active cycles | bank-conflict cycles | address-conflict cycles | bank conflicts / active |",
-              "|---|---|---|---|---|---|"]
+              "| kernel | LDS instructions | of them atomics | LDS active cycles | bank-conflict cycles | address-conflict cycles | bank conflicts / active |",
+              "|---|---|---|---|---|---|---|"]
     for k, rec in lds.items():
-        lines.append(f"| {k} | {rec['SQ_INSTS_LDS']:,.0f} | {rec['SQ_LDS_IDX_ACTIVE']:,.0f} | "
-                     f"{rec['SQ_LDS_BANK_CONFLICT']:,.0f} | {rec['SQ_LDS_ADDR_CONFLICT']:,.0f} | "
-                     f"{rec['bank_conflict_per_active']:.3f} |")
+        lines.append(f"| {k} | {rec['SQ_INSTS_LDS']:,.0f} | {rec['SQ_INSTS_LDS_ATOMIC']:,.0f} | "
+                     f"{rec['SQ_LDS_IDX_ACTIVE']:,.0f} | {rec['SQ_LDS_BANK_CONFLICT']:,.0f} | "
+                     f"{rec['SQ_LDS_ADDR_CONFLICT']:,.0f} | {rec['bank_conflict_per_active']:.3f} |")
     lines += ["",
               f"Kernel sources sha256: `{record['source_hash']}`."]
     with open(base + ".md", "w") as f:

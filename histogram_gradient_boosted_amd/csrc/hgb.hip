@@ -120,6 +120,7 @@ struct hgb_ctx {
     int32_t* rot = nullptr;           // per feature: the skipped slot (stored bins are rotated by it)
     bool skip = false;                // the fills skip each feature's slot 0 (a hot slot exists)
     hipEvent_t part_ready = nullptr;  // partition: the node records are on the host
+    hipEvent_t host_ready = nullptr;  // begin_tree, sync: small results are on the host
 
     Stage stage[kStages];
     int stage_next = 0;
@@ -225,6 +226,21 @@ hgb_status stage_release(hgb_ctx* c, Stage* s)
     HGB_HIP(c, hipEventRecord(s->ev, c->stream));
     s->pending = true;
     return HGB_OK;
+}
+
+// Record `*ev` (created on first use) on the stream and poll it until the
+// work before it is done.  A level loop waits for small results (maxima, node
+// records) several times per tree; a blocking wait would add the host's
+// wake-up latency to each of them.
+hgb_status wait_here(hgb_ctx* c, hipEvent_t* ev)
+{
+    if (!*ev) HGB_HIP(c, hipEventCreateWithFlags(ev, hipEventDisableTiming));
+    HGB_HIP(c, hipEventRecord(*ev, c->stream));
+    for (;;) {
+        const hipError_t e = hipEventQuery(*ev);
+        if (e == hipSuccess) return HGB_OK;
+        if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
+    }
 }
 
 hipEvent_t pool_event(hgb_ctx* c)
@@ -825,7 +841,8 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
     }
     HGB_LAUNCHED(c, "k_max_final");
     HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
-    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    hgb_status wst = wait_here(c, &c->host_ready);
+    if (wst != HGB_OK) return wst;
     const uint32_t pg = c->host_words[0], ph = c->host_words[1];
     if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
     if (ph >= 0x7f800000u)
@@ -936,6 +953,7 @@ void hgb_destroy(hgb_ctx* c)
         }
     for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
     if (c->part_ready) (void)hipEventDestroy(c->part_ready);
+    if (c->host_ready) (void)hipEventDestroy(c->host_ready);
     (void)hipFree(c->bins);
     (void)hipFree(c->bins_rm);
     (void)hipFree(c->q);
@@ -982,7 +1000,8 @@ hgb_status hgb_sync(hgb_ctx* c)
     HGB_HIP(c, hipSetDevice(c->device));
     HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
                               c->stream));
-    HGB_HIP(c, hipStreamSynchronize(c->stream));
+    const hgb_status st = wait_here(c, &c->host_ready);
+    if (st != HGB_OK) return st;
     return take_flags(c);
 }
 
@@ -1646,7 +1665,11 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     if (st != HGB_OK) return st;
     // Wait for the node records only: the scatter keeps running while the
     // caller plans the next level (the stream orders whatever reads its rows).
-    HGB_HIP(c, hipEventSynchronize(c->part_ready));
+    for (;;) {
+        const hipError_t e = hipEventQuery(c->part_ready);
+        if (e == hipSuccess) break;
+        if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
+    }
     st = take_flags(c);   // a row index outside [0, n)
     if (st != HGB_OK) return st;
     int32_t nc = 0;

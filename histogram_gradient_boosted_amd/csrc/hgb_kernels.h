@@ -2018,6 +2018,31 @@ __device__ inline int block_exclusive_scan(int v, int* s, int* total)
     return incl - v;
 }
 
+// Block-wide exclusive scan of v with a wave scan in registers and one LDS
+// pass over the waves' totals (two barriers).  Uses s[blockDim.x / kWave].
+__device__ inline int block_exclusive_scan_waves(int v, int* s, int* total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int waves = (int)(blockDim.x / kWave);
+    int incl = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += t;
+    }
+    if (lane == kWave - 1) s[wv] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < waves; ++w) {
+        const int t = s[w];
+        before += w < wv ? t : 0;
+        all += t;
+    }
+    __syncthreads();   // s may be reused by the caller
+    *total = all;
+    return before + incl - v;
+}
+
 // One block.  left_base[item]: rows going left in the node's earlier chunks.
 // node_out[3 i + 0..2]: the node's first output position (its children's
 // rows follow those of earlier split nodes), its rows going left, and 1 when
@@ -2075,7 +2100,7 @@ __global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict
                                                        const int32_t* __restrict__ node_out,
                                                        int32_t* __restrict__ out_rows)
 {
-    __shared__ int s_scan[1024];
+    __shared__ int s_scan[1024 / kWave];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     if (sp.feature < 0) return;   // uniform: the node has no children
@@ -2096,7 +2121,7 @@ __global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict
             nr += 1 - f[j];
         }
     int tot;
-    const int ex = block_exclusive_scan(nl + (nr << 16), s_scan, &tot);
+    const int ex = block_exclusive_scan_waves(nl + (nr << 16), s_scan, &tot);
     const int lb = left_base[blockIdx.x];
     int lpos = node_out[3 * it.node] + lb + (ex & 0xffff);
     int rpos = node_out[3 * it.node] + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb) + (ex >> 16);
