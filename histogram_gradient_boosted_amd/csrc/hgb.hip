@@ -311,9 +311,9 @@ struct FillPlan {
 // Row-major level fills with a register accumulator: cells per thread and
 // entries per thread and step.
 constexpr int kRegAccCells = 8;
-constexpr int kRegAccEntries = 2;
+constexpr int kRegAccEntries = 1;
 // Entries per thread and step of the wide row-major fill.
-constexpr int kWideRowEntries = 4;
+constexpr int kWideRowEntries = 1;
 
 // LDS bytes per feature of a tile: the copies, plus the packed accumulator.
 int64_t feature_lds(int acc, int S, int lc)
