@@ -1341,9 +1341,9 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         a.gh = c->q;
         a.items = (const FillItem*)(dev + offs[wdt]);
         a.n_items = (int)items.size();
-        // 8-row vector loads need rows aligned to 8 (chunk starts are
-        // multiples of 128)
-        a.vec_ok = (c->n % 8 == 0) ? 1 : 0;
+        // whole-group vector loads need every column aligned to a group of
+        // kRootRows rows (chunk starts are multiples of 128)
+        a.vec_ok = (c->n % kRootRows == 0) ? 1 : 0;
         a.drain = std::max(plan.drain, 1);
         a.hist = hist;
         ProfScope ps(c, HGB_KERNEL_FILL);

@@ -693,38 +693,37 @@ __host__ __device__ inline int tile_words(int acc_mode, int nf, int S, int lc)
 }
 
 // Root fill: the level's one node holds every row in order, so each thread
-// reads 8 consecutive rows per step -- a 16-byte (g, h) load per two rows and
-// one 8- or 16-byte bin load per feature -- and loads the next step while it
-// adds the current one.  NF features per block.
-constexpr int kRootRows = 8;
+// reads 4 consecutive rows per step -- a 16-byte (g, h) load per two rows and
+// one 4- or 8-byte bin load per feature -- and loads the next step while it
+// adds the current one.  NF features per block.  (4 rows beat 8 and 2 on the
+// MI355X: fewer registers in flight per wave, the LDS adds interleave better.)
+constexpr int kRootRows = 4;
 
+// A thread's kRootRows consecutive bins of one feature, from one load.
 template <typename BinT>
-struct Bins8;
+struct RootBins;
 template <>
-struct Bins8<uint8_t> {
-    uint2 w;
-    __device__ inline void load(const uint8_t* p) { w = *(const uint2*)p; }
-    __device__ inline int at(int j) const
-    {
-        const uint32_t x = j < 4 ? w.x : w.y;
-        return (int)((x >> (8 * (j & 3))) & 0xffu);
-    }
+struct RootBins<uint8_t> {
+    uint32_t w;
+    __device__ inline void load(const uint8_t* p) { w = *(const uint32_t*)p; }
+    __device__ inline int at(int j) const { return (int)((w >> (8 * j)) & 0xffu); }
 };
 template <>
-struct Bins8<uint16_t> {
-    uint4 w;
-    __device__ inline void load(const uint16_t* p) { w = *(const uint4*)p; }
+struct RootBins<uint16_t> {
+    uint2 w;
+    __device__ inline void load(const uint16_t* p) { w = *(const uint2*)p; }
     __device__ inline int at(int j) const
     {
-        const uint32_t x = j < 2 ? w.x : (j < 4 ? w.y : (j < 6 ? w.z : w.w));
+        const uint32_t x = j < 2 ? w.x : w.y;
         return (int)((x >> (16 * (j & 1))) & 0xffffu);
     }
 };
+static_assert(kRootRows == 4, "RootBins loads 4 rows");
 
 template <typename BinT, int NF>
 struct RootStep {
     int4 q[kRootRows / 2];
-    Bins8<BinT> b[NF];
+    RootBins<BinT> b[NF];
 };
 
 template <typename BinT, int NF, int ACC, bool SKIP>
