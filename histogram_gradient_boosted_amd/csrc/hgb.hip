@@ -45,7 +45,7 @@ constexpr double kPieceRowsPerCell = 0.25;
 // into its zeroed slot with atomics.
 constexpr int kMergeGroup = 32;
 // Keep a row-major copy of the bins when a row takes at most this many bytes.
-// Rows up to this many bytes get a row-major copy (C4's 16 KB rows included):
+// Rows up to this many bytes get a row-major copy (16,384 one-byte features included):
 // below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
@@ -57,7 +57,7 @@ constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 16;
 
 // Initial capacity of an upload stage: larger than any level's plan of the
-// workloads here (C4's level-3 fill plan is about 70 KB).
+// matrices measured here (the level-3 plan of 131,072 x 16,384 is about 70 KB).
 constexpr size_t kStageMinBytes = 256 * 1024;
 
 struct Stage {
@@ -130,9 +130,10 @@ struct hgb_ctx {
     // HGB_FILL_TUNE="key=value,..." overrides the fill planner (developer
     // tuning): root_lc, root_tile, root_ipc, level_lc, level_tile, level_ipc
     // (ipc = items per CU), align (rows an item boundary is a multiple of),
-    // piece (fixed cost of a level item, in rows); -1 keeps the planner's
+    // piece (fixed cost of a level item, in rows), il (row-major wide fills:
+    // 1 slot-major interleaved tile, 0 feature-major); -1 keeps the planner's
     // choice.
-    int tune[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    int tune[9] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
     bool prof = false;
@@ -305,6 +306,7 @@ struct FillPlan {
     int64_t step_rows;  // rows a block consumes per step
     int drain;          // packed: steps between drains of the copies (0: wide)
     int ra;             // rows, packed: register-accumulator cells per thread (0: LDS)
+    int il;             // rows, wide: slot-major interleaved tile (lane-rotated features)
     size_t lds_bytes;
 };
 
@@ -350,16 +352,29 @@ double fill_cost(int acc, int lc, int tile, int w)
 // the packed drains: lane-contiguous LDS reads and writes); each row's lines
 // from HBM once at ~5 TB/s (the tiles of a share run side by side on one XCD
 // and share them through L2); and per tile a 64-byte L2 transfer of the row's
-// segment plus its index and (g, h), at ~10 TB/s (fitted to C3 and C4 level
+// segment plus its index and (g, h), at ~10 TB/s (fitted to 10M x 28 and 131K x 16K level
 // timings).
-double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, double drain_ops_per_row)
+double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, double drain_ops_per_row,
+                 int il = 0, int tile = 0)
 {
     static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
     const double clk = 2.4e9 * 256;
-    const double lds = F * (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * clk) + drain_ops_per_row / (16.0 * clk);
+    // The interleaved tile spreads a wave's adds over tile * 2^lc bank pairs
+    // (32 is conflict-free, ~9.9 lanes per clock; measured with lds_rate) but
+    // adds every one of the tile's positions, the unused ones included.
+    const int spread = tile << lc;
+    const double il_ops = spread >= 32 ? 9.0 : spread >= 16 ? 6.5 : spread >= 8 ? 5.0 : 4.3;
+    const double adds = il ? (double)n_tiles * tile : (double)F;
+    const double lds = adds * (acc == kWide ? 2.0 : 1.0) / ((il ? il_ops : kLdsOps[lc]) * clk) +
+                       drain_ops_per_row / (16.0 * clk);
+    // Vector ALU work per add, 64 lanes per clock per CU: about 3 instructions
+    // (unpack, address), 6 with the interleaved tile's rotation and per-lane
+    // feature offset.  It decides narrow matrices, where the gather dominates
+    // and the interleaved tile's faster adds buy nothing (a 28-feature matrix).
+    const double valu = adds * (il ? 6.0 : 3.0) / (64.0 * clk);
     const double lines = (double)std::max<int64_t>((row_bytes + 127) / 128, 1) * 128.0;
     const double mem = lines / 5.0e12 + n_tiles * (64.0 + 12.0) / 10.0e12;
-    return std::max(lds, mem) + 0.25 * std::min(lds, mem);
+    return std::max(lds, mem) + 0.25 * std::min(lds, mem) + valu;
 }
 
 FillPlan plan_rows(const hgb_ctx* c)
@@ -383,12 +398,14 @@ FillPlan plan_rows(const hgb_ctx* c)
             for (int lc = 4; lc >= 0; --lc) {
                 const int force_lc = c->tune[3];
                 if (force_lc >= 0 && lc != force_lc) continue;
-                {
+                for (int il = 0; il <= (acc == kWide ? 1 : 0); ++il) {
+                    if (c->tune[8] >= 0 && il != c->tune[8]) continue;
                     // packed sums live in registers, wide sums in LDS
                     const int ra = acc == kPacked ? kRegAccCells : 0;
                     if (ra > 0 && nf * S > ra * kLevelThreads) continue;
                     const int e = ra > 0 ? kRegAccEntries : kWideRowEntries;
-                    const int64_t words = (int64_t)nf * (acc == kWide ? 2 : 1) * (S << lc);
+                    const int64_t words = il ? (int64_t)2 * S * (tile << lc)
+                                             : (int64_t)nf * (acc == kWide ? 2 : 1) * (S << lc);
                     if (words * 8 > kTileLdsBudget) continue;
                     int drain = 0;
                     double drain_ops = 0.0;
@@ -397,7 +414,7 @@ FillPlan plan_rows(const hgb_ctx* c)
                         if (drain == 0) continue;
                         drain_ops = 2.0 * nf * S * (1 << lc) / ((double)kLevelThreads * e * drain) * n_tiles;
                     }
-                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops);
+                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops, il, tile);
                     if (cost < best) {
                         best = cost;
                         found = true;
@@ -406,6 +423,7 @@ FillPlan plan_rows(const hgb_ctx* c)
                         p.tile = tile;
                         p.lt = lt;
                         p.ra = ra;
+                        p.il = il;
                         p.drain = drain;
                         p.step_rows = (int64_t)kLevelThreads * e;
                         p.lds_bytes = (size_t)(words + kFixWords) * 8;
@@ -420,6 +438,7 @@ FillPlan plan_rows(const hgb_ctx* c)
         p.tile = 1;
         p.lt = w;
         p.ra = 0;
+        p.il = 0;
         p.drain = 0;
         p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
         p.lds_bytes = (size_t)(2 * S + kFixWords) * 8;
@@ -553,24 +572,34 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
     } else {
         // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-#define HGB_ROWS(LT, RA, E) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot)
+#define HGB_ROWS(LT, RA, E, IL) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP, IL>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
-            case 32: HGB_ROWS(32, kRegAccCells, kRegAccEntries); break;
-            case 16: HGB_ROWS(16, kRegAccCells, kRegAccEntries); break;
-            case 8: HGB_ROWS(8, kRegAccCells, kRegAccEntries); break;
-            case 4: HGB_ROWS(4, kRegAccCells, kRegAccEntries); break;
-            default: HGB_ROWS(2, kRegAccCells, kRegAccEntries); break;
+            case 32: HGB_ROWS(32, kRegAccCells, kRegAccEntries, false); break;
+            case 16: HGB_ROWS(16, kRegAccCells, kRegAccEntries, false); break;
+            case 8: HGB_ROWS(8, kRegAccCells, kRegAccEntries, false); break;
+            case 4: HGB_ROWS(4, kRegAccCells, kRegAccEntries, false); break;
+            default: HGB_ROWS(2, kRegAccCells, kRegAccEntries, false); break;
             }
         } else {
             if (p.ra != 0) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
-            switch (p.lt) {
-            case 32: HGB_ROWS(32, 0, kWideRowEntries); break;
-            case 16: HGB_ROWS(16, 0, kWideRowEntries); break;
-            case 8: HGB_ROWS(8, 0, kWideRowEntries); break;
-            case 4: HGB_ROWS(4, 0, kWideRowEntries); break;
-            default: HGB_ROWS(2, 0, kWideRowEntries); break;
+            if (p.il) {
+                switch (p.lt) {
+                case 32: HGB_ROWS(32, 0, kWideRowEntries, true); break;
+                case 16: HGB_ROWS(16, 0, kWideRowEntries, true); break;
+                case 8: HGB_ROWS(8, 0, kWideRowEntries, true); break;
+                case 4: HGB_ROWS(4, 0, kWideRowEntries, true); break;
+                default: HGB_ROWS(2, 0, kWideRowEntries, true); break;
+                }
+            } else {
+                switch (p.lt) {
+                case 32: HGB_ROWS(32, 0, kWideRowEntries, false); break;
+                case 16: HGB_ROWS(16, 0, kWideRowEntries, false); break;
+                case 8: HGB_ROWS(8, 0, kWideRowEntries, false); break;
+                case 4: HGB_ROWS(4, 0, kWideRowEntries, false); break;
+                default: HGB_ROWS(2, 0, kWideRowEntries, false); break;
+                }
             }
         }
 #undef HGB_ROWS
@@ -752,9 +781,9 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         return fail(c, HGB_E_UNSUPPORTED, "build_level: too many fill items");
     if (c->debug_plan)
         std::fprintf(stderr,
-                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d drain %d chunk %lld items %zu "
+                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d il %d drain %d chunk %lld items %zu "
                      "lds %zu blocks %d partials %lld merges %zu\n",
-                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.drain,
+                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.il, plan.drain,
                      (long long)len, items.size(), plan.lds_bytes, n_blocks, (long long)n_partial,
                      merges.size());
 
@@ -906,7 +935,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     c->device = device;
     if (const char* e = std::getenv("HGB_DEBUG_PLAN")) c->debug_plan = e[0] == '1';
     if (const char* e = std::getenv("HGB_FILL_TUNE")) {
-        static const char* keys[8] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align", "piece"};
+        static const char* keys[9] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align", "piece", "il"};
         std::string spec(e);
         size_t pos = 0;
         while (pos < spec.size()) {
@@ -915,7 +944,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
             const std::string kv = spec.substr(pos, end - pos);
             const size_t eq = kv.find('=');
             if (eq != std::string::npos)
-                for (int k = 0; k < 8; ++k)
+                for (int k = 0; k < 9; ++k)
                     if (kv.compare(0, eq, keys[k]) == 0) c->tune[k] = std::atoi(kv.c_str() + eq + 1);
             pos = end + 1;
         }

@@ -686,6 +686,78 @@ __device__ inline void lds_finish(unsigned long long* lds, int nf, int S, int pl
     }
 }
 
+// Slot-major ("interleaved") layout of a wide row-major tile of TF feature
+// positions and C = 2^lc copies: word ((slot * 2 + plane) * C + copy) * TF + f.
+// A wave's lanes take the features of a row in lane-rotated order (lane l adds
+// feature (l + j) mod TF at its j-th add) and copy (l / TF) mod C, so when
+// TF * C >= 32 the 64 lanes of one add land on 32 distinct u64 bank pairs,
+// two lanes each, whatever the bins: the LDS's conflict-free rate.  The
+// finish walks cells slot-major as well (lanes along features), so its LDS
+// reads are conflict-free too.
+template <bool SKIP, int TF>
+__device__ inline void lds_finish_il(const unsigned long long* lds, int nf, int S, int lc,
+                                     unsigned long long* out, bool atomic_merge,
+                                     const int32_t* __restrict__ rot, unsigned long long* fix)
+{
+    const int C = 1 << lc;
+    const int G = TF << lc;   // words per (slot, plane)
+    const int total = S * TF;
+    auto cell = [&](int i, long long& g, long long& h) {   // i = slot * TF + f
+        const unsigned long long* pg = lds + (i / TF) * 2 * G + (i & (TF - 1));
+        g = 0;
+        h = 0;
+        for (int c = 0; c < C; ++c) {
+            g += (long long)pg[c * TF];
+            h += (long long)pg[G + c * TF];
+        }
+    };
+    // A thread's cells all have feature threadIdx.x mod TF (blockDim.x is a
+    // multiple of TF): it sums its value cells, lanes of one feature combine
+    // by shuffles, and one LDS atomic pair per wave and feature lands in fix.
+    const int f_own = (int)(threadIdx.x & (TF - 1));
+    if (SKIP) {
+        long long sg = 0, sh = 0;
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            if (i < TF || f_own >= nf) continue;   // slot 0 is the skipped one
+            long long g, h;
+            cell(i, g, h);
+            sg += g;
+            sh += h;
+        }
+#pragma unroll
+        for (int o = TF; o < kWave; o <<= 1) {
+            sg += wave_shfl_xor_i64(sg, o);
+            sh += wave_shfl_xor_i64(sh, o);
+        }
+        if ((threadIdx.x & (kWave - 1)) < (unsigned)TF && f_own < nf) {
+            atomicAdd(&fix[2 + 2 * f_own], (unsigned long long)sg);
+            atomicAdd(&fix[3 + 2 * f_own], (unsigned long long)sh);
+        }
+        __syncthreads();
+    }
+    const long long tg = (long long)fix[0], th = (long long)fix[1];
+    for (int i = threadIdx.x; i < total; i += blockDim.x) {
+        const int f = i & (TF - 1);
+        if (f >= nf) continue;   // positions past the tile's features are never read
+        const int sl = i / TF;
+        long long g, h;
+        if (SKIP && sl == 0) {
+            g = tg - (long long)fix[2 + 2 * f];
+            h = th - (long long)fix[3 + 2 * f];
+        } else {
+            cell(i, g, h);
+        }
+        const int o = f * S + (SKIP ? unrotate(sl, rot[f], S) : sl);
+        if (atomic_merge) {
+            if (g) atomicAdd(&out[2 * o], (unsigned long long)g);
+            if (h) atomicAdd(&out[2 * o + 1], (unsigned long long)h);
+        } else {
+            out[2 * o] = (unsigned long long)g;
+            out[2 * o + 1] = (unsigned long long)h;
+        }
+    }
+}
+
 // LDS words of a tile: the copies, plus the packed accumulator.
 __host__ __device__ inline int tile_words(int acc_mode, int nf, int S, int lc)
 {
@@ -1004,6 +1076,31 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
 // its feature tile (LT / sizeof(BinT) features), read with one load per row.
 template <int LT>
 struct Chunk;
+// Rotate N dwords as one little-endian byte string: afterwards byte i holds
+// what byte (i + k) mod 4N held (0 <= k < 4N).  Whole dwords move in log2(N)
+// conditional stages, then one alignbyte per dword shifts the remaining 0-3
+// bytes.  Each lane may rotate by its own k.
+template <int N>
+__device__ inline void rotate_bytes(uint32_t (&d)[N], int k)
+{
+    const int kd = k >> 2;
+#pragma unroll
+    for (int s = 1; s < N; s <<= 1) {
+        const bool on = (kd & s) != 0;
+        uint32_t t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = on ? d[(i + s) % N] : d[i];
+#pragma unroll
+        for (int i = 0; i < N; ++i) d[i] = t[i];
+    }
+    const uint32_t kb = (uint32_t)k & 3u;
+    uint32_t t[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) t[i] = __builtin_amdgcn_alignbyte(d[(i + 1) % N], d[i], kb);
+#pragma unroll
+    for (int i = 0; i < N; ++i) d[i] = t[i];
+}
+
 template <>
 struct Chunk<32> {
     uint4 w0, w1;
@@ -1018,30 +1115,56 @@ struct Chunk<32> {
         const int j = i & 3;
         return j == 0 ? w.x : (j == 1 ? w.y : (j == 2 ? w.z : w.w));
     }
+    __device__ inline void rotate(int k)
+    {
+        uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        rotate_bytes(d, k);
+        w0 = make_uint4(d[0], d[1], d[2], d[3]);
+        w1 = make_uint4(d[4], d[5], d[6], d[7]);
+    }
 };
 template <>
 struct Chunk<16> {
     uint4 w;
     __device__ inline void load(const uint8_t* p) { w = *(const uint4*)p; }
     __device__ inline uint32_t word(int i) const { return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w)); }
+    __device__ inline void rotate(int k)
+    {
+        uint32_t d[4] = {w.x, w.y, w.z, w.w};
+        rotate_bytes(d, k);
+        w = make_uint4(d[0], d[1], d[2], d[3]);
+    }
 };
 template <>
 struct Chunk<8> {
     uint2 w;
     __device__ inline void load(const uint8_t* p) { w = *(const uint2*)p; }
     __device__ inline uint32_t word(int i) const { return i == 0 ? w.x : w.y; }
+    __device__ inline void rotate(int k)
+    {
+        uint32_t d[2] = {w.x, w.y};
+        rotate_bytes(d, k);
+        w = make_uint2(d[0], d[1]);
+    }
 };
 template <>
 struct Chunk<4> {
     uint32_t w;
     __device__ inline void load(const uint8_t* p) { w = *(const uint32_t*)p; }
     __device__ inline uint32_t word(int) const { return w; }
+    __device__ inline void rotate(int k)
+    {
+        uint32_t d[1] = {w};
+        rotate_bytes(d, k);
+        w = d[0];
+    }
 };
 template <>
 struct Chunk<2> {
     uint32_t w;   // low 16 bits hold the data
     __device__ inline void load(const uint8_t* p) { w = (uint32_t)*(const uint16_t*)p; }
     __device__ inline uint32_t word(int) const { return w; }
+    __device__ inline void rotate(int k) { w = k ? ((w >> 8) | (w << 8)) & 0xffffu : w; }   // k in {0, 1}
 };
 
 // Packed sums with the int64 accumulator in registers instead of LDS: thread t
@@ -1134,7 +1257,7 @@ __device__ inline void reg_finish(const RegAcc<RA>& a, int cells, int S, unsigne
 
 // RA > 0 (packed only): register accumulator of RA cells per thread; E
 // entries per thread and step.
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, bool IL>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
                                       int64_t n, int n_features, int S, int lc,
@@ -1146,14 +1269,26 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 {
     static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
     static_assert(LT / (int)sizeof(BinT) <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
+    static_assert(!IL || (ACC == kWide && RA == 0), "the interleaved layout holds wide sums in LDS");
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // <= LT / sizeof(BinT)
     constexpr int TF = LT / (int)sizeof(BinT);
+    constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
+    static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
     const int plane = S << lc;
     const int cells = nf * S;
-    unsigned long long* const fix = lds + nf * (ACC == kWide ? 2 : 1) * plane;
-    lds_zero(lds, nf * (ACC == kWide ? 2 : 1) * plane + kFixWords);
+    // Interleaved: every one of the TF positions has its words, even past nf
+    // (those lanes add the row's padding or the next tile's bins there, and
+    // nothing reads them back).
+    const int G = TF << lc;
+    const int tile_w = IL ? 2 * S * G : nf * (ACC == kWide ? 2 : 1) * plane;
+    unsigned long long* const fix = lds + tile_w;
+    lds_zero(lds, tile_w + kFixWords);
     __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rl = lane & (TF - 1);                        // interleaved: the lane's first feature
+    const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;   // and its copy's offset
+    const int gsh = 1 + lc + kLogTF;                       // slot stride: 2G words
     long long tg = 0, th = 0;   // the item's row totals (this thread's share)
     RegAcc<(RA > 0 ? RA : 1)> racc;
 #pragma unroll
@@ -1206,6 +1341,22 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
                 th += d.g[e].y;
             }
             const CellVal v = cell_val<ACC>(d.g[e].x, d.g[e].y);
+            if (IL) {
+                Chunk<LT> ch = d.c[e];
+                ch.rotate(rl * (int)sizeof(BinT));   // position j now holds feature (rl + j) mod TF
+#pragma unroll
+                for (int j = 0; j < TF; ++j) {
+                    const uint32_t w = ch.word((j * (int)sizeof(BinT)) >> 2);
+                    const int b = sizeof(BinT) == 1 ? (int)((w >> (8 * (j & 3))) & 0xffu)
+                                                    : (int)((w >> (16 * (j & 1))) & 0xffffu);
+                    const int word = (b << gsh) + cb + ((rl + j) & (TF - 1));
+                    if (!SKIP || b != 0) {   // 0: skipped
+                        atomicAdd(lds + word, v.a);
+                        atomicAdd(lds + word + G, v.b);
+                    }
+                }
+                continue;
+            }
             // The feature's base offset is stepped here rather than hoisted:
             // 32 hoisted values would not fit the scalar registers.
             int fb = 0;
@@ -1261,13 +1412,15 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     if (RA > 0) {
         reg_drain(lds, cells, S, plane, lc, racc);
         reg_finish<(RA > 0 ? RA : 1), SKIP>(racc, cells, S, out, it.dest == kDestAtomic, rot + f0, fix);
+    } else if (IL) {
+        lds_finish_il<SKIP, TF>(lds, nf, S, lc, out, it.dest == kDestAtomic, rot + f0, fix);
     } else {
         lds_finish<ACC, SKIP>(lds, nf, S, plane, lc, out, it.dest == kDestAtomic, rot + f0, fix);
     }
 }
 
 
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, bool IL>
 __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
                                                    int S, int lc, const int2* __restrict__ q,
@@ -1285,7 +1438,7 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
     const int i1 = block_first[blk + 1];
     int bad = 0;   // a row index outside [0, n): skipped, and flagged
     for (int ii = block_first[blk]; ii < i1; ++ii) {
-        fill_rows_item<BinT, LT, ACC, RA, E, SKIP>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
+        fill_rows_item<BinT, LT, ACC, RA, E, SKIP, IL>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
                                              lc, q, row_index, drain, hist, partial, bad, rot);
         __syncthreads();
     }

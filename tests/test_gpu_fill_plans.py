@@ -1,0 +1,110 @@
+"""GPU parity of the row-major level fill under each tile layout, forced
+through the planner's developer overrides (HGB_FILL_TUNE, read when a context
+is created) and confirmed from the plan it prints (HGB_DEBUG_PLAN=1).
+
+The interleaved (slot-major) tile has every lane add its row's features in a
+lane-rotated order; these cases cover tiles narrower than their load (28
+features in 32 positions: the spare positions take padding bytes), several
+tiles per row with a ragged last one, 2-byte bins with 1,025 slots, copies,
+and the skipped slot (hot features), against the oracle's histograms and
+splits."""
+import re
+
+import numpy as np
+import pytest
+
+from histogram_gradient_boosted_amd import synth
+
+from test_gpu_parity import run_level_both, run_root_both, say, with_hot_slots
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _torch
+    from histogram_gradient_boosted_amd import binding
+    if not _torch.cuda.is_available() or not binding.available():
+        pytest.skip("no HIP device")
+    return _torch
+
+
+@pytest.fixture(scope="module")
+def hgb(torch):
+    from histogram_gradient_boosted_amd import binding
+    return binding
+
+
+def level_plans(err):
+    """(copies, tile, il) of each row-major fill plan printed to stderr."""
+    out = []
+    for line in err.splitlines():
+        m = re.search(r"\[hgb\] fill kind 2 acc \d+ copies (\d+) tile (\d+) lt \d+ ra \d+ il (\d)", line)
+        if m:
+            out.append(tuple(int(x) for x in m.groups()))
+    return out
+
+
+U8_28 = ("u8, 28 features", lambda: synth.random_small(300, 60_000, 28, 256, False, 8))
+U8_70 = ("u8, 70 features", lambda: synth.random_small(301, 20_000, 70, 200, True, 6))
+U16_13 = ("u16, 13 features, 1,025 slots", lambda: synth.random_small(302, 30_000, 13, 1024, True, 10, u16=True))
+HOT_U8 = ("u8 hot slots", lambda: with_hot_slots(synth.random_small(303, 40_000, 6, 16, True, 8), 3))
+HOT_U16 = ("u16 hot slots", lambda: with_hot_slots(synth.random_small(304, 30_000, 5, 1024, True, 6, u16=True), 4))
+
+CASES = [
+    # workload, il, tile, copies
+    (U8_28, 1, 32, 1), (U8_28, 0, 32, 1), (U8_28, 1, 16, 2), (U8_28, 1, 8, 4), (U8_28, 1, 4, 8),
+    (U8_28, 1, 2, 16), (U8_70, 1, 32, 1), (U8_70, 1, 16, 2), (U8_70, 0, 16, 2),
+    (U16_13, 1, 8, 1), (U16_13, 1, 4, 2), (U16_13, 1, 1, 8), (U16_13, 0, 8, 1),
+    (HOT_U8, 1, 32, 1), (HOT_U8, 1, 8, 2), (HOT_U8, 0, 32, 1), (HOT_U16, 1, 8, 1), (HOT_U16, 1, 2, 4),
+]
+
+
+@pytest.mark.parametrize("bits", [30, 12])
+@pytest.mark.parametrize("case,il,tile,copies", CASES, ids=lambda v: v[0] if isinstance(v, tuple) else str(v))
+def test_row_fill_layouts(hgb, torch, monkeypatch, capfd, case, il, tile, copies, bits):
+    name, make = case
+    say("row fill layout", name, "il", il, "tile", tile, "copies", copies, "bits", bits)
+    lc = copies.bit_length() - 1
+    monkeypatch.setenv("HGB_FILL_TUNE", f"il={il},level_tile={tile},level_lc={lc}")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    w = make()
+    run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
+    plans = level_plans(capfd.readouterr().err)
+    assert plans, "no row-major fill ran"
+    assert set(plans) == {(copies, tile, il)}, plans
+    if il == 1 and tile == 32:
+        run_root_both(hgb, torch, w, bits=bits)
+
+
+def test_interleaved_tile_full_size_wide_level(hgb, torch, monkeypatch, capfd):
+    """131,072 x 16,384 bytes, the level of 8 nodes: the planner's own choice
+    (the interleaved 32-feature tile) against the oracle on sampled features."""
+    import oracle
+    from test_gpu_parity import oracle_quantized
+    say("interleaved full-size wide level")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    w = synth.make("c4")
+    L = w.level
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    ctx.begin_tree(torch.from_numpy(w.grad).cuda(), torch.from_numpy(w.hess).cuda())
+    dev = torch.device("cuda")
+    P = L.n_pairs
+    ch = torch.full((2 * P, w.n_features, w.n_slots, 2), -7, dtype=torch.int64, device=dev)
+    ctx.build_level(ch, torch.from_numpy(L.built_row_index).to(dev), L.built_offsets.astype(np.int32),
+                    L.built_slots)
+    ctx.sync()
+    plans = level_plans(capfd.readouterr().err)
+    assert plans and all(p[2] == 1 for p in plans), plans
+    qg, qh, _, _ = oracle_quantized(w)
+    rng = np.random.default_rng(9)
+    feats = np.sort(rng.choice(w.n_features, 96, replace=False))
+    feats = np.unique(np.concatenate([feats, [0, 31, 32, w.n_features - 1]]))
+    got = ch[:, torch.from_numpy(feats).to(dev)].cpu().numpy()
+    ctx.close()
+    want = oracle.build_hist(w.bins[feats], w.n_bins, w.has_missing, qg, qh,
+                             L.built_row_index, L.built_offsets)
+    for k in range(P):
+        s = int(L.built_slots[k])
+        assert np.array_equal(got[s], want[k]), f"built node {k} (slot {s}) differs"
