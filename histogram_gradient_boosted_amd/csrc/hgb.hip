@@ -130,10 +130,10 @@ struct hgb_ctx {
     // HGB_FILL_TUNE="key=value,..." overrides the fill planner (developer
     // tuning): root_lc, root_tile, root_ipc, level_lc, level_tile, level_ipc
     // (ipc = items per CU), align (rows an item boundary is a multiple of),
-    // piece (fixed cost of a level item, in rows), il (row-major wide fills:
-    // 1 slot-major interleaved tile, 0 feature-major); -1 keeps the planner's
-    // choice.
-    int tune[9] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
+    // piece (fixed cost of a level item, in rows), il and root_il (row-major
+    // level and root fills, wide sums: 1 slot-major interleaved tile, 0
+    // feature-major); -1 keeps the planner's choice.
+    int tune[10] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
     bool prof = false;
@@ -347,6 +347,23 @@ double fill_cost(int acc, int lc, int tile, int w)
     return lds + w / 6.0e12 + (8.0 / tile) / 30.0e12;
 }
 
+// The same for the root's interleaved tile of tf positions (wide sums), over
+// F features: the adds spread over tf * 2^lc bank pairs (32: conflict-free)
+// but every position is added, used or not; one (g, h) read serves tf
+// features; and the register rotation and per-lane feature offsets cost about
+// two vector instructions per add more than the feature-major tile (64 lanes
+// per clock per CU).
+double fill_cost_il(int lc, int tf, int F, int w)
+{
+    const double clk = 2.4e9 * 256;
+    const int spread = tf << lc;
+    const double ops = spread >= 32 ? 9.0 : spread >= 16 ? 6.5 : spread >= 8 ? 5.0 : 4.3;
+    const double waste = (double)((F + tf - 1) / tf * tf) / F;
+    const double lds = 2.0 * waste / (ops * clk);
+    const double valu = 2.0 * waste / (64.0 * clk);
+    return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
+}
+
 // Row-major level fills read scattered rows.  Cost per row (seconds) of a plan
 // with n_tiles feature tiles: the LDS adds at the same rates as above (plus
 // the packed drains: lane-contiguous LDS reads and writes); each row's lines
@@ -493,6 +510,35 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
                     p.lc = lc;
                     p.tile = tile;
                     p.lt = lt;
+                    p.il = 0;
+                }
+            }
+        }
+        // The root's interleaved tile (wide sums): tf positions of 2^lc copies.
+        // A position's bins take w registers per thread; 32 registers of them
+        // fit beside the skipped slot's bookkeeping only up to 16 bytes.
+        for (int tf = 32; root && acc == kWide && tf >= 8; tf >>= 1) {
+            if (tf * w > (c->skip ? 16 : 32)) continue;
+            if (c->tune[9] == 0) break;
+            if (c->tune[1] > 0 && tf != c->tune[1]) continue;
+            // Few tiles mean many row chunks per tile, whose partial histograms
+            // a k_merge launch sums: its launch and traffic, spread per cell.
+            const int64_t il_tiles = (c->F + tf - 1) / tf;
+            const int64_t il_chunks = std::max<int64_t>(1, kRootItemsPerCu * c->n_cu / il_tiles);
+            const double merge_s = il_chunks > 1 ? 4e-6 + 2.0 * il_chunks * c->F * S * 16.0 / 5.0e12 : 0.0;
+            const double cells = std::max(1.0, (double)c->n * c->F);
+            for (int lc = 0; lc <= 4; ++lc) {
+                if (c->tune[0] >= 0 && lc != c->tune[0]) continue;
+                if ((int64_t)2 * S * (tf << lc) * 8 > budget) continue;
+                const double cost = fill_cost_il(lc, tf, c->F, w) + merge_s / cells;
+                if (cost < best || (c->tune[9] == 1 && !(found && p.il))) {
+                    best = cost;
+                    found = true;
+                    p.acc = kWide;
+                    p.lc = lc;
+                    p.tile = tf;
+                    p.lt = 0;
+                    p.il = 1;
                 }
             }
         }
@@ -502,6 +548,14 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
         p.lc = 0;
         p.tile = 1;
         p.lt = p.kind == kFillRowsKind ? w : 0;
+        p.il = 0;
+    }
+    if (p.il) {
+        // the last tile may be partial; the tile itself never narrower than 8
+        p.lds_bytes = (size_t)(2 * S * (p.tile << p.lc) + kFixWords) * 8;
+        p.step_rows = (int64_t)p.threads * kRootRows;
+        p.drain = 0;
+        return p;
     }
     if (p.kind != kFillRowsKind) {
         // rows loads cover exactly `tile` features; the others take min(NF, F)
@@ -549,7 +603,32 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         if (st != HGB_OK) return st;                                                     \
         kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
     } while (0)
-    if (p.kind == kFillRoot) {
+    if (p.kind == kFillRoot && p.il) {
+        if constexpr (ACC == kWide) {
+#define HGB_ROOT_IL(TF) HGB_LAUNCH((k_fill_root_il<BinT, TF, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist, partial, c->rot)
+            // (the plan keeps TF * sizeof(BinT) <= 32, and <= 16 with SKIP)
+            constexpr int kMaxBytes = SKIP ? 16 : 32;
+            switch (p.tile) {
+            case 32:
+                if constexpr (32 * sizeof(BinT) <= kMaxBytes) {
+                    HGB_ROOT_IL(32);
+                    break;
+                }
+                return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            case 16:
+                if constexpr (16 * sizeof(BinT) <= kMaxBytes) {
+                    HGB_ROOT_IL(16);
+                    break;
+                }
+                return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            case 8: HGB_ROOT_IL(8); break;
+            default: return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            }
+#undef HGB_ROOT_IL
+        } else {
+            return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+        }
+    } else if (p.kind == kFillRoot) {
 #define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, c->rot)
         switch (p.tile) {
         case 1: HGB_ROOT(1); break;
@@ -935,7 +1014,8 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     c->device = device;
     if (const char* e = std::getenv("HGB_DEBUG_PLAN")) c->debug_plan = e[0] == '1';
     if (const char* e = std::getenv("HGB_FILL_TUNE")) {
-        static const char* keys[9] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile", "level_ipc", "align", "piece", "il"};
+        static const char* keys[10] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile",
+                                       "level_ipc", "align", "piece", "il", "root_il"};
         std::string spec(e);
         size_t pos = 0;
         while (pos < spec.size()) {
@@ -944,7 +1024,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
             const std::string kv = spec.substr(pos, end - pos);
             const size_t eq = kv.find('=');
             if (eq != std::string::npos)
-                for (int k = 0; k < 9; ++k)
+                for (int k = 0; k < 10; ++k)
                     if (kv.compare(0, eq, keys[k]) == 0) c->tune[k] = std::atoi(kv.c_str() + eq + 1);
             pos = end + 1;
         }
@@ -1273,7 +1353,7 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     // possibly narrower (those kernels take the width at run time).
     std::vector<std::pair<int, int>> tiles;
     FillPlan plan = plan0;
-    if (root) {
+    if (root && !plan.il) {
         // equal tiles when a divisor of F close to the planned width exists
         for (int d = plan.tile; d >= 1 && 2 * d > plan.tile; --d)
             if (c->F % d == 0) {
@@ -1285,7 +1365,7 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         int f0 = 0;
         for (; f0 + plan.tile <= c->F; f0 += plan.tile) tiles.emplace_back(f0, plan.tile);
         if (f0 < c->F) {
-            if (root) {
+            if (root && !plan.il) {
                 for (int wdt = plan.tile >> 1; wdt >= 1; wdt >>= 1)
                     if (f0 + wdt <= c->F) {
                         tiles.emplace_back(f0, wdt);
@@ -1298,7 +1378,7 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     }
     const int n_tiles = (int)tiles.size();
     for (const auto& t : tiles)
-        if (t.second < 1 || (root && t.second > 8) || t.first + t.second > c->F)
+        if (t.second < 1 || (root && t.second > (plan.il ? plan.tile : 8)) || t.first + t.second > c->F)
             return fail(c, HGB_E_DEVICE, "build_level: internal error in the tile plan");
 
     if (!root) return fill_level(c, plan, tiles, row_index, begin, count, slots, total, hist);
@@ -1317,55 +1397,85 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     ch = std::max<int64_t>((ch + align - 1) / align * align, align);
     const int64_t nchunks = (total + ch - 1) / ch;
 
+    // The interleaved tile covers many features, so a tile's chunks are
+    // many: each writes a partial histogram, summed by k_merge in groups of
+    // kMergeGroup (atomically when there are several groups).  Feature-major
+    // tiles have few chunks each and add theirs atomically.
+    const bool use_partial = plan.il && nchunks > 1;
+    std::vector<MergeEntry> merges;
+    if (use_partial) {
+        const int64_t n_groups = (nchunks + kMergeGroup - 1) / kMergeGroup;
+        for (int64_t g = 0; g < n_groups; ++g) {
+            MergeEntry m{};
+            m.out_slot = slots[0];
+            m.first = (int32_t)(g * kMergeGroup);
+            m.count = (int32_t)std::min<int64_t>(kMergeGroup, nchunks - g * kMergeGroup);
+            m.atomic = n_groups > 1 ? 1 : 0;
+            merges.push_back(m);
+        }
+        hgb_status gst = grow(c, &c->partial, &c->partial_cap, nchunks * (int64_t)c->F * c->S * 2);
+        if (gst != HGB_OK) return gst;
+    }
+    const bool zero_root = nchunks > 1 && (!use_partial || merges.size() > 1);
+
     // Item order (chunk, tile): the tiles of one row chunk read the same
     // (g, h) rows, and the kernel gives each XCD a contiguous run of items.
-    // groups[w]: the items of tiles of width w, one launch each.
+    // groups[w]: the items of tiles of width w, one launch each; with the
+    // interleaved tile every item (the last tile possibly partial) is in
+    // groups[0], one launch.
     std::vector<FillItem> groups[9];
     size_t n_items = 0;
     for (int64_t j = 0; j < nchunks; ++j)
         for (int t = 0; t < n_tiles; ++t) {
             FillItem it{};
-            it.out_slot = slots[0];
+            it.out_slot = use_partial ? (int32_t)j : slots[0];
             it.row_begin = (int32_t)(j * ch);
             it.row_end = (int32_t)std::min<int64_t>((j + 1) * ch, total);
             it.f0_nf = tiles[t].first | (tiles[t].second << 16);
-            it.dest = nchunks > 1 ? kDestAtomic : kDestStore;
-            groups[tiles[t].second].push_back(it);
+            it.dest = use_partial ? kDestPartial : (nchunks > 1 ? kDestAtomic : kDestStore);
+            groups[plan.il ? 0 : tiles[t].second].push_back(it);
             ++n_items;
         }
     if (c->debug_plan)
         std::fprintf(stderr,
-                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d drain %d chunk %lld items %zu lds %zu\n",
-                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.drain, (long long)ch,
-                     n_items, plan.lds_bytes);
-    // one upload: the root's slot (to zero before atomic merges), then each
-    // width's items (each part 256-byte aligned)
+                     "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d il %d drain %d chunk %lld items %zu "
+                     "lds %zu\n",
+                     (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.il, plan.drain,
+                     (long long)ch, n_items, plan.lds_bytes);
+    // one upload: the root's slot (to zero before atomic merges), each
+    // width's items, then the merges (each part 256-byte aligned)
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     size_t offs[9] = {};
     size_t bytes = 256;
-    for (int wdt = 8; wdt >= 1; --wdt) {
+    for (int wdt = 8; wdt >= 0; --wdt) {
         offs[wdt] = bytes;
         bytes += up(groups[wdt].size() * sizeof(FillItem));
     }
+    const size_t off_merges = bytes;
+    bytes += merges.size() * sizeof(MergeEntry);
     std::vector<uint8_t> blob(bytes, 0);
     std::memcpy(blob.data(), &slots[0], sizeof(int32_t));
-    for (int wdt = 8; wdt >= 1; --wdt)
+    for (int wdt = 8; wdt >= 0; --wdt)
         if (!groups[wdt].empty())
             std::memcpy(blob.data() + offs[wdt], groups[wdt].data(), groups[wdt].size() * sizeof(FillItem));
+    if (!merges.empty())
+        std::memcpy(blob.data() + off_merges, merges.data(), merges.size() * sizeof(MergeEntry));
     Stage* sg = nullptr;
     hgb_status st = stage_upload(c, blob.data(), bytes, &sg);
     if (st != HGB_OK) return st;
     const uint8_t* dev = (const uint8_t*)sg->dev;
-    if (nchunks > 1) {
+    if (zero_root) {
         st = launch_zero(c, hist, (const int32_t*)dev, 1);
         if (st != HGB_OK) return st;
     }
-    for (int wdt = 8; wdt >= 1; --wdt) {
+    for (int wdt = 8; wdt >= 0; --wdt) {
         std::vector<FillItem>& items = groups[wdt];
         if (items.empty()) continue;
         FillPlan gp = plan;
-        gp.tile = wdt;
-        gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc) + 8 * kFixWords);
+        if (wdt > 0) {
+            gp.tile = wdt;
+            gp.lds_bytes = (size_t)(wdt * feature_lds(plan.acc, c->S, plan.lc) + 8 * kFixWords);
+        }
         FillArgs a{};
         a.gh = c->q;
         a.items = (const FillItem*)(dev + offs[wdt]);
@@ -1375,9 +1485,18 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         a.vec_ok = (c->n % kRootRows == 0) ? 1 : 0;
         a.drain = std::max(plan.drain, 1);
         a.hist = hist;
+        a.partial = (int64_t*)c->partial;
         ProfScope ps(c, HGB_KERNEL_FILL);
         st = launch_fill(c, gp, a);
         if (st != HGB_OK) return st;
+    }
+    if (!merges.empty()) {
+        ProfScope ps(c, HGB_KERNEL_FILL);
+        const int64_t node_vec = (int64_t)c->F * c->S;
+        dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
+        k_merge<<<grid, 256, 0, c->stream>>>((const longlong2*)c->partial, (longlong2*)hist,
+                                             (const MergeEntry*)(dev + off_merges), node_vec);
+        HGB_LAUNCHED(c, "k_merge");
     }
     return stage_release(c, sg);
 }

@@ -779,6 +779,14 @@ struct RootBins<uint8_t> {
     uint32_t w;
     __device__ inline void load(const uint8_t* p) { w = *(const uint32_t*)p; }
     __device__ inline int at(int j) const { return (int)((w >> (8 * j)) & 0xffu); }
+    // on ? a : b, selected by value (a select of the structs' addresses would
+    // put a register array in scratch memory)
+    __device__ static inline RootBins pick(bool on, RootBins a, RootBins b)
+    {
+        RootBins r;
+        r.w = on ? a.w : b.w;
+        return r;
+    }
 };
 template <>
 struct RootBins<uint16_t> {
@@ -788,6 +796,13 @@ struct RootBins<uint16_t> {
     {
         const uint32_t x = j < 2 ? w.x : w.y;
         return (int)((x >> (16 * (j & 1))) & 0xffffu);
+    }
+    __device__ static inline RootBins pick(bool on, RootBins a, RootBins b)
+    {
+        RootBins r;
+        r.w.x = on ? a.w.x : b.w.x;
+        r.w.y = on ? a.w.y : b.w.y;
+        return r;
     }
 };
 static_assert(kRootRows == 4, "RootBins loads 4 rows");
@@ -914,6 +929,178 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     lds_finish<ACC, SKIP>(lds, NF, S, plane, lc,
                           hist + ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2,
                           it.dest == kDestAtomic, rot + f0, fix);
+}
+
+// Root fill with the interleaved (slot-major) tile, wide sums: an item covers
+// TF feature positions, of which the first nf are real features.  Each thread
+// loads kRootRows consecutive rows of every position (positions past nf
+// re-load the last real feature, and their adds land in words nothing reads),
+// rotates its registers so that lane l visits feature (l + p) mod TF at its
+// p-th position, and adds -- every wave-wide add spreads over the tile's
+// TF * 2^lc bank pairs whatever the bins.  One (g, h) load per row serves all
+// TF features.
+template <typename BinT, int TF>
+struct RootStepIL {
+    int4 q[kRootRows / 2];
+    RootBins<BinT> b[TF];
+};
+
+template <typename BinT, int TF>
+__device__ inline void rotate_root_bins(RootBins<BinT> (&b)[TF], int k)
+{
+#pragma unroll
+    for (int s = 1; s < TF; s <<= 1) {
+        const bool on = (k & s) != 0;
+        RootBins<BinT> t[TF];
+#pragma unroll
+        for (int i = 0; i < TF; ++i) t[i] = RootBins<BinT>::pick(on, b[(i + s) % TF], b[i]);
+#pragma unroll
+        for (int i = 0; i < TF; ++i) b[i] = t[i];
+    }
+}
+
+template <typename BinT, int TF, bool SKIP>
+__global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ bins, int64_t n,
+                                                       int n_features, int S, int lc,
+                                                       const int2* __restrict__ q,
+                                                       const FillItem* __restrict__ items, int n_items,
+                                                       int vec_ok, unsigned long long* __restrict__ hist,
+                                                       unsigned long long* __restrict__ partial,
+                                                       const int32_t* __restrict__ rot)
+{
+    static_assert(TF <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
+    constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
+    static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
+    extern __shared__ unsigned long long lds[];
+    const int item = xcd_item(blockIdx.x, n_items);
+    if (item >= n_items) return;
+    const FillItem it = items[item];
+    const int f0 = it.f0_nf & 0xffff;
+    const int nf = it.f0_nf >> 16;   // 1 <= nf <= TF
+    const int G = TF << lc;
+    const int tile_w = 2 * S * G;
+    unsigned long long* const fix = lds + tile_w;
+    lds_zero(lds, tile_w + kFixWords);
+    __syncthreads();
+    long long tg = 0, th = 0;   // the item's row totals (this thread's share)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rl = lane & (TF - 1);                             // the lane's first feature
+    const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;   // and its copy's offset
+    const int gsh = 1 + lc + kLogTF;                            // slot stride: 2G words
+
+    const BinT* const col0 = bins + (int64_t)f0 * n;
+    const int64_t rb = it.row_begin, re = it.row_end;
+    constexpr int R = kRootRows;
+    const int64_t step = (int64_t)blockDim.x * R;
+    const int64_t off = (int64_t)threadIdx.x * R;
+
+    auto load = [&](int64_t at, RootStepIL<BinT, TF>& st) {
+        const int4* g4 = (const int4*)(q + at);
+#pragma unroll
+        for (int j = 0; j < R / 2; ++j) st.q[j] = g4[j];
+#pragma unroll
+        for (int f = 0; f < TF; ++f) st.b[f].load(col0 + (int64_t)(f < nf ? f : nf - 1) * n + at);
+    };
+    // A step's work, taken out of its loads: the rows' cell values and the
+    // rotated bins (b[p] holds feature (rl + p) mod TF).  `live` is false for
+    // a thread whose group lies past the item: it then adds zeros (to valid
+    // bins), which keeps the loop free of divergence.
+    struct Work {
+        CellVal v[R];
+        RootBins<BinT> b[TF];
+    };
+    auto prepare = [&](const RootStepIL<BinT, TF>& st, bool live, Work& wk) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int4 qq = st.q[j >> 1];
+            const int gv = live ? ((j & 1) ? qq.z : qq.x) : 0;
+            const int hv = live ? ((j & 1) ? qq.w : qq.y) : 0;
+            if (SKIP) {
+                tg += gv;
+                th += hv;
+            }
+            wk.v[j] = cell_val<kWide>(gv, hv);
+        }
+#pragma unroll
+        for (int f = 0; f < TF; ++f) wk.b[f] = st.b[f];
+        rotate_root_bins<BinT, TF>(wk.b, rl);
+    };
+    auto accumulate = [&](const Work& wk) {
+        // The TF feature offsets are recomputed every step: hoisted out of the
+        // loop they would hold TF registers for the whole kernel.
+        int rs = rl;
+        asm volatile("" : "+v"(rs));
+#pragma unroll
+        for (int p = 0; p < TF; ++p) {
+            const int fo = cb + ((rs + p) & (TF - 1));
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int bin = wk.b[p].at(j);
+                if (!SKIP || bin != 0) {   // 0: the skipped slot
+                    const int word = (bin << gsh) + fo;
+                    atomicAdd(lds + word, wk.v[j].a);
+                    atomicAdd(lds + word + G, wk.v[j].b);
+                }
+            }
+        }
+    };
+    // One row, every real feature, in the lane's rotated order.
+    auto add_row = [&](int64_t r) {
+        const int2 g = q[r];
+        if (SKIP) {
+            tg += g.x;
+            th += g.y;
+        }
+        const CellVal v = cell_val<kWide>(g.x, g.y);
+        for (int p = 0; p < TF; ++p) {
+            const int f = (rl + p) & (TF - 1);
+            if (f >= nf) continue;
+            const int bin = (int)col0[(int64_t)f * n + r];
+            if (!SKIP || bin != 0) {
+                const int word = (bin << gsh) + cb + f;
+                atomicAdd(lds + word, v.a);
+                atomicAdd(lds + word + G, v.b);
+            }
+        }
+    };
+
+    if (vec_ok) {
+        // Whole groups of R rows; the rows after the last whole group are
+        // added one by one afterwards.  Loads are issued unconditionally
+        // (clamped to a valid group).  Each step first takes its work out of
+        // the load registers, then issues the next step's loads into them, so
+        // those are in flight while this step adds, with one set of load
+        // registers instead of two.
+        const int64_t full = (re - rb) / R;
+        const int64_t gend = rb + full * R;
+        const int64_t n_steps = (full + blockDim.x - 1) / blockDim.x;
+        const int64_t last = full > 0 ? gend - R : rb;
+        RootStepIL<BinT, TF> st;
+        Work wk;
+        if (n_steps > 0) load(rb + off + R <= gend ? rb + off : last, st);
+        for (int64_t s = 0; s < n_steps; ++s) {
+            const int64_t at = rb + s * step + off;
+            const int64_t nx = at + step;
+            prepare(st, at + R <= gend, wk);
+            __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+            load(nx + R <= gend ? nx : last, st);
+            __builtin_amdgcn_sched_barrier(0);
+            accumulate(wk);
+        }
+        if (threadIdx.x == 0)
+            for (int64_t r = gend; r < re; ++r) add_row(r);
+    } else {
+        const int64_t n_steps = (re - rb + blockDim.x - 1) / blockDim.x;
+        for (int64_t s = 0; s < n_steps; ++s) {
+            const int64_t r = rb + s * blockDim.x + threadIdx.x;
+            if (r < re) add_row(r);
+        }
+    }
+    if (SKIP) add_item_totals(tg, th, fix);
+    __syncthreads();
+    unsigned long long* const out = (it.dest == kDestPartial ? partial : hist) +
+                                    ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2;
+    lds_finish_il<SKIP, TF>(lds, nf, S, lc, out, it.dest == kDestAtomic, rot + f0, fix);
 }
 
 // Level fills read their rows through the row index.  Each thread takes

@@ -108,3 +108,44 @@ def test_interleaved_tile_full_size_wide_level(hgb, torch, monkeypatch, capfd):
     for k in range(P):
         s = int(L.built_slots[k])
         assert np.array_equal(got[s], want[k]), f"built node {k} (slot {s}) differs"
+
+
+def root_plans(err):
+    """(copies, tile, il) of each root fill plan printed to stderr."""
+    out = []
+    for line in err.splitlines():
+        m = re.search(r"\[hgb\] fill kind 0 acc \d+ copies (\d+) tile (\d+) lt \d+ ra \d+ il (\d)", line)
+        if m:
+            out.append(tuple(int(x) for x in m.groups()))
+    return out
+
+
+R_U8_28 = ("root u8, 28 features", lambda: synth.random_small(310, 60_000, 28, 256, False, 0))
+R_U8_70 = ("root u8, 70 features, ragged rows", lambda: synth.random_small(311, 20_003, 70, 200, True, 0))
+R_U16 = ("root u16, 300 bins", lambda: synth.random_small(312, 30_002, 13, 300, True, 0, u16=True))
+R_U16_1025 = ("root u16, 1,025 slots", lambda: synth.random_small(313, 12_000, 9, 1024, True, 0, u16=True))
+R_HOT_U8 = ("root u8 hot slots", lambda: with_hot_slots(synth.random_small(314, 40_000, 6, 16, True, 0), 5))
+R_HOT_U16 = ("root u16 hot slots", lambda: with_hot_slots(synth.random_small(315, 30_001, 5, 1024, True, 0, u16=True), 6))
+
+ROOT_CASES = [
+    # workload, tile (feature positions), copies
+    (R_U8_28, 32, 1), (R_U8_28, 16, 2), (R_U8_28, 8, 4), (R_U8_70, 32, 1), (R_U8_70, 16, 1),
+    (R_U8_70, 8, 2), (R_U16, 16, 1), (R_U16, 8, 2), (R_U16_1025, 8, 1), (R_HOT_U8, 16, 2),
+    (R_HOT_U8, 8, 1), (R_HOT_U16, 8, 1),
+]
+
+
+@pytest.mark.parametrize("bits", [30, 20])
+@pytest.mark.parametrize("case,tile,copies", ROOT_CASES, ids=lambda v: v[0] if isinstance(v, tuple) else str(v))
+def test_root_fill_interleaved(hgb, torch, monkeypatch, capfd, case, tile, copies, bits):
+    """The root's interleaved tile: full and partial tiles, rows in whole
+    groups of four and ragged (one row at a time), copies, 2-byte bins and
+    the skipped slot, against the oracle's root histogram and split."""
+    name, make = case
+    say("root interleaved", name, "tile", tile, "copies", copies, "bits", bits)
+    lc = copies.bit_length() - 1
+    monkeypatch.setenv("HGB_FILL_TUNE", f"root_il=1,root_tile={tile},root_lc={lc}")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    run_root_both(hgb, torch, make(), bits=bits)
+    plans = root_plans(capfd.readouterr().err)
+    assert plans == [(copies, tile, 1)], plans
