@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # The fill class timed for the roofline: the LDS fill kernels and the merge of
 # split nodes' partial histograms (bracketed together by the library's events
 # on its stream).
-FILL_KERNELS = "k_fill_root / k_fill_rows / k_fill_cols + k_merge"
+FILL_KERNELS = "k_fill_root / k_fill_root_il / k_fill_rows / k_fill_cols + k_merge"
 METRIC = "level histogram build G cell-updates/s (rows x features) + % of HBM peak"
 
 WORKLOAD_NAMES = {
@@ -264,12 +264,14 @@ def lds_rates(device: int = 0):
     return out
 
 
-def traffic_record(config: str, precision: int):
+def traffic_record(config: str, precision: int, mode: str = ""):
     """HBM traffic of the fill class measured with rocprofv3 counters
     (FETCH_SIZE, WRITE_SIZE, calibrated against a copy of known size) by
     bench_counters.py, per step; None when no record exists for this workload
-    or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"counters_{config}_p{precision}.json")
+    and step (mode "" is the replayed depthwise tree that bench_counters.py
+    drives; grown and oblivious trees have no record) or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{config}{mode}_p{precision}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -433,7 +435,8 @@ def main():
         "kernel_ms_per_step": breakdown,
         "roofline": {"bound": "hbm", "kernel": FILL_KERNELS, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(args.config, args.precision),
+                     "traffic": traffic_record(args.config, args.precision,
+                                               "_oblivious" if args.oblivious else "_grow" if args.grow else ""),
                      "traffic_unit": "HBM bytes per step (fetch + write, calibrated counters)",
                      "alg_bytes_per_step": plan.fill_bytes,
                      "launches_per_step": fill_launches // max(args.steps, 1),

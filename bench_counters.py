@@ -34,7 +34,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-FILL_CLASS = ("k_fill_root", "k_fill_rows", "k_fill_cols", "k_merge")
+FILL_CLASS = ("k_fill_root", "k_fill_root_il", "k_fill_rows", "k_fill_cols", "k_merge")
 OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_subtract_split", "k_split_feature",
          "k_split_reduce", "k_quantize", "k_grad_hess_max")
 # one --pmc pass of SQ counters for the LDS side of the fill (5 of the 8 SQ slots)
