@@ -229,19 +229,24 @@ hgb_status stage_release(hgb_ctx* c, Stage* s)
     return HGB_OK;
 }
 
-// Record `*ev` (created on first use) on the stream and poll it until the
-// work before it is done.  A level loop waits for small results (maxima, node
-// records) several times per tree; a blocking wait would add the host's
-// wake-up latency to each of them.
+// Poll `ev` until the work before it is done.  A level loop waits for small
+// results (maxima, node records) several times per tree; a blocking wait
+// would add the host's wake-up latency to each of them.
+hgb_status poll_event(hgb_ctx* c, hipEvent_t ev)
+{
+    for (;;) {
+        const hipError_t e = hipEventQuery(ev);
+        if (e == hipSuccess) return HGB_OK;
+        if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
+    }
+}
+
+// Record `*ev` (created on first use) on the stream and poll it.
 hgb_status wait_here(hgb_ctx* c, hipEvent_t* ev)
 {
     if (!*ev) HGB_HIP(c, hipEventCreateWithFlags(ev, hipEventDisableTiming));
     HGB_HIP(c, hipEventRecord(*ev, c->stream));
-    for (;;) {
-        const hipError_t e = hipEventQuery(*ev);
-        if (e == hipSuccess) return HGB_OK;
-        if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
-    }
+    return poll_event(c, *ev);
 }
 
 hipEvent_t pool_event(hgb_ctx* c)
@@ -945,11 +950,24 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
         k_grad_hess_max<Src><<<max_blocks, 256, 0, c->stream>>>(src, c->n, vec, c->max_part);
         HGB_LAUNCHED(c, "k_grad_hess_max");
-        k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words);
+        k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words, c->precision,
+                                              (double*)(c->dev_words + 4));
+        HGB_LAUNCHED(c, "k_max_final");
     }
-    HGB_LAUNCHED(c, "k_max_final");
+    // The maxima go back to the host (to check them, and to keep the
+    // exponents for the split pass) while the quantize pass, which takes its
+    // scales from the device, already runs: the host waits on an event
+    // recorded before that pass.
     HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
-    hgb_status wst = wait_here(c, &c->host_ready);
+    if (!c->host_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->host_ready, hipEventDisableTiming));
+    HGB_HIP(c, hipEventRecord(c->host_ready, c->stream));
+    {
+        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
+        k_quantize<Src><<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
+            src, c->n, vec, (const double*)(c->dev_words + 4), c->q);
+        HGB_LAUNCHED(c, "k_quantize");
+    }
+    hgb_status wst = poll_event(c, c->host_ready);
     if (wst != HGB_OK) return wst;
     const uint32_t pg = c->host_words[0], ph = c->host_words[1];
     if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
@@ -970,12 +988,6 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
     }
     c->k_g = k[0];
     c->k_h = k[1];
-    {
-        ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_quantize<Src><<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
-            src, c->n, vec, std::ldexp(1.0, k[0]), std::ldexp(1.0, k[1]), c->q);
-    }
-    HGB_LAUNCHED(c, "k_quantize");
     c->have_tree = true;
     return HGB_OK;
 }

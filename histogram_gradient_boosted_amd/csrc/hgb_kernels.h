@@ -213,8 +213,22 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int v
 }
 
 // The maxima of the per-block pairs, into out[0..1].
+// The scale 2^k of a maximum's fp32 bit pattern: k = precision - e with
+// 2^(e-1) <= M < 2^e (frexp's exponent), k = 0 for M = 0.  Inf or NaN (the
+// caller reports the error) gives 0.
+__device__ inline double scale_of_max(uint32_t pat, int precision)
+{
+    if (pat >= 0x7f800000u) return 0.0;
+    if (pat == 0u) return 1.0;
+    int e = 0;
+    (void)frexp((double)__uint_as_float(pat), &e);
+    return ldexp(1.0, precision - e);
+}
+
+// out[0..1]: the maxima's bit patterns; scales[0..1]: their scales (above).
 __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ part, int n_blocks,
-                                                   uint32_t* __restrict__ out)
+                                                   uint32_t* __restrict__ out, int precision,
+                                                   double* __restrict__ scales)
 {
     __shared__ uint32_t red[2][256];
     uint32_t mg = 0, mh = 0;
@@ -235,14 +249,18 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
     if (threadIdx.x == 0) {
         out[0] = red[0][0];
         out[1] = red[1][0];
+        scales[0] = scale_of_max(red[0][0], precision);
+        scales[1] = scale_of_max(red[1][0], precision);
     }
 }
 
 // q = round-half-even(c * 2^k), both components packed per row as (qg, qh).
 template <class Src>
-__global__ __launch_bounds__(256) void k_quantize(Src src, int64_t n, int vec, double scale_g,
-                                                  double scale_h, int2* __restrict__ q)
+__global__ __launch_bounds__(256) void k_quantize(Src src, int64_t n, int vec,
+                                                  const double* __restrict__ scales, int2* __restrict__ q)
 {
+    // the scales k_max_final derived on the device (no host round trip)
+    const double scale_g = scales[0], scale_h = scales[1];
     // exact: power-of-two scaling of an fp32 value in double, then ties-to-even
     auto enc = [&](float a, float b) {
         return make_int2((int)__builtin_rint((double)a * scale_g),
