@@ -216,6 +216,24 @@ def _oracle_pass(w, budget_s: float, objective: str = "none"):
     return cells, t_work, sample
 
 
+def host_cpu() -> dict:
+    """The host the oracle ran on: CPU model and the CPUs this process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 0
+    return {"cpu_model": model, "nproc": usable}
+
+
 def cpu_baseline(w, objective: str = "none", min_s: float = 10.0, max_reps: int = 30,
                  budget_s: float = 20.0):
     """The oracle timed on one host core: whole steps repeated until about
@@ -233,7 +251,7 @@ def cpu_baseline(w, objective: str = "none", min_s: float = 10.0, max_reps: int 
         t_work += t
         reps += 1
     return {"value": cells / t_work / 1e9, "unit": "G cell-updates/s", "cores": 1,
-            "kind": "oracle", "seconds": round(t_work, 3),
+            "kind": "oracle", "seconds": round(t_work, 3), "host": host_cpu(),
             "sample": f"{reps} x ({sample}) of workload {w.name}: serial C oracle (gcc -O2), "
                       f"1 thread, {cells} built cells"}
 

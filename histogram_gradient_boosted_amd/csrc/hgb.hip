@@ -138,6 +138,8 @@ struct hgb_ctx {
     // optional per-kernel timing
     bool prof = false;
     std::vector<hipEvent_t> ev_pool;
+    // kernels whose dynamic-LDS limit has been raised, and to what
+    std::vector<std::pair<const void*, size_t>> lds_set;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending[HGB_KERNEL_COUNT];
     double prof_ms[HGB_KERNEL_COUNT] = {};
     int64_t prof_launches[HGB_KERNEL_COUNT] = {};
@@ -575,8 +577,17 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
 template <typename K>
 hgb_status set_lds(hgb_ctx* c, K kernel, size_t bytes)
 {
-    HGB_HIP(c, hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)bytes));
+    // once per kernel and size: the attribute persists for the process
+    const void* fn = (const void*)kernel;
+    for (auto& e : c->lds_set)
+        if (e.first == fn) {
+            if (e.second >= bytes) return HGB_OK;
+            HGB_HIP(c, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
+            e.second = bytes;
+            return HGB_OK;
+        }
+    HGB_HIP(c, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
+    c->lds_set.emplace_back(fn, bytes);
     return HGB_OK;
 }
 
@@ -794,18 +805,29 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         if (open) share_first.push_back((int64_t)pieces.size());
         return (int64_t)share_first.size() - 1;
     };
-    // The smallest budget whose cut fits one round of blocks (binary search;
-    // a larger budget never needs more shares).
+    // A budget close to the smallest whose cut fits one round of blocks (a
+    // larger budget never needs more shares): gallop up from the lower bound,
+    // then bisect until the bracket is within 1/256 of the budget.  The host
+    // plans every level between device steps, so the search is kept short.
     {
         int64_t lo = std::max<int64_t>((built + piece_rows * nonempty + shares - 1) / shares,
                                        piece_rows + align);
-        int64_t hi = std::max<int64_t>(built + piece_rows * (nonempty + 1) + align, lo);
-        while (lo < hi) {
-            budget = lo + (hi - lo) / 2;
-            if (cut() <= shares) hi = budget;
-            else lo = budget + 1;
+        const int64_t cap = std::max<int64_t>(built + piece_rows * (nonempty + 1) + align, lo);
+        auto fits = [&](int64_t b) {
+            budget = b;
+            return cut() <= shares;
+        };
+        int64_t hi = lo;
+        while (hi < cap && !fits(hi)) {
+            lo = hi + 1;
+            hi = std::min<int64_t>(cap, 2 * hi);
         }
-        budget = lo;
+        while (hi - lo > std::max<int64_t>(align, hi / 256)) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (fits(mid)) hi = mid;
+            else lo = mid + 1;
+        }
+        budget = hi;
     }
     const int64_t n_shares = cut();
     const int64_t len = budget;

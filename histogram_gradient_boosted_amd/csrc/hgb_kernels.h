@@ -2296,9 +2296,10 @@ __device__ inline bool part_left(int v, int n_bins, const SplitOut& sp)
     return v == n_bins ? sp.default_left != 0 : v <= sp.bin;
 }
 
-// Each thread takes kPartRows consecutive positions of its chunk (1024
-// threads x kPartRows = kPartChunk), loads issued independently and clamped
-// into the chunk.
+// Each thread takes kPartRows positions of its chunk (1024 threads x
+// kPartRows = kPartChunk), position begin + j * 1024 + thread at its j-th
+// step, so that every index load and direction store of a wave is one
+// contiguous run; loads are issued independently and clamped into the chunk.
 constexpr int kPartRows = 8;
 static_assert(kPartChunk == 1024 * kPartRows, "a chunk is one pass of a 1024-thread block");
 
@@ -2320,11 +2321,12 @@ __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bi
     if (sp.feature >= 0) {   // uniform
         const BinT* col = bins + (int64_t)sp.feature * n;
         const int rf = rot[sp.feature];   // stored values are rotated per feature
-        const int k0 = it.begin + (int)threadIdx.x * kPartRows;
+        const int k0 = it.begin + (int)threadIdx.x;
+        const int kstep = (int)blockDim.x;
         int64_t r[kPartRows];
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {
-            const int kc = min(k0 + j, it.end - 1);
+            const int kc = min(k0 + j * kstep, it.end - 1);
             r[j] = row_index ? (int64_t)row_index[kc] : (int64_t)kc;
         }
         int v[kPartRows];
@@ -2332,12 +2334,12 @@ __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bi
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {
             const bool in = (uint64_t)r[j] < (uint64_t)n;
-            bad |= !in && k0 + j < it.end;
+            bad |= !in && k0 + j * kstep < it.end;
             v[j] = unrotate((int)col[in ? r[j] : 0], rf, S);
         }
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {
-            const int k = k0 + j;
+            const int k = k0 + j * kstep;
             // a row index outside [0, n) is routed right (and reported)
             const bool left = (uint64_t)r[j] < (uint64_t)n && part_left(v[j], n_bins, sp);
             if (k < it.end) {
@@ -2373,31 +2375,6 @@ __device__ inline int block_exclusive_scan(int v, int* s, int* total)
     *total = s[blockDim.x - 1];
     __syncthreads();
     return incl - v;
-}
-
-// Block-wide exclusive scan of v with a wave scan in registers and one LDS
-// pass over the waves' totals (two barriers).  Uses s[blockDim.x / kWave].
-__device__ inline int block_exclusive_scan_waves(int v, int* s, int* total)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    const int waves = (int)(blockDim.x / kWave);
-    int incl = v;
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += t;
-    }
-    if (lane == kWave - 1) s[wv] = incl;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int w = 0; w < waves; ++w) {
-        const int t = s[w];
-        before += w < wv ? t : 0;
-        all += t;
-    }
-    __syncthreads();   // s may be reused by the caller
-    *total = all;
-    return before + incl - v;
 }
 
 // One block.  left_base[item]: rows going left in the node's earlier chunks.
@@ -2446,9 +2423,12 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
 }
 
 // Write each row to its place: the chunk's left rows from its left base on,
-// its right rows from its right base on, in order.  One pass per chunk: the
-// thread's left and right counts are scanned across the block together (as
-// left + right * 2^16; a chunk holds at most kPartChunk < 2^16 rows).
+// its right rows from its right base on, in position order.  Step j covers
+// positions begin + j * 1024 .. + 1023: a lane's rank among the step's left
+// (right) rows is its wave's ballot below it plus the earlier waves' counts,
+// and the steps follow each other.  Every wave publishes its counts of all
+// steps at once, so one barrier serves the whole chunk.  The stores of a
+// wave's left (right) rows in one step are one contiguous run.
 __global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict__ row_index,
                                                        const PartItem* __restrict__ items,
                                                        const SplitOut* __restrict__ splits,
@@ -2457,37 +2437,60 @@ __global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict
                                                        const int32_t* __restrict__ node_out,
                                                        int32_t* __restrict__ out_rows)
 {
-    __shared__ int s_scan[1024 / kWave];
+    __shared__ int s_left[kPartRows][1024 / kWave];
+    __shared__ int s_all[kPartRows][1024 / kWave];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     if (sp.feature < 0) return;   // uniform: the node has no children
-    const int k0 = it.begin + (int)threadIdx.x * kPartRows;
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    const int wv = (int)(threadIdx.x / kWave);
+    const int waves = (int)(blockDim.x / kWave);
+    const int k0 = it.begin + (int)threadIdx.x;
+    const int kstep = (int)blockDim.x;
     int32_t r[kPartRows];
     uint8_t f[kPartRows];
 #pragma unroll
     for (int j = 0; j < kPartRows; ++j) {
-        const int kc = min(k0 + j, it.end - 1);
+        const int kc = min(k0 + j * kstep, it.end - 1);
         r[j] = row_index ? row_index[kc] : kc;
         f[j] = flags[kc];
     }
-    int nl = 0, nr = 0;
+    uint64_t bl[kPartRows], bi[kPartRows];   // per step: the wave's left rows, its rows
 #pragma unroll
-    for (int j = 0; j < kPartRows; ++j)
-        if (k0 + j < it.end) {
-            nl += f[j];
-            nr += 1 - f[j];
+    for (int j = 0; j < kPartRows; ++j) {
+        const bool in = k0 + j * kstep < it.end;
+        bl[j] = __ballot(in && f[j] != 0);
+        bi[j] = __ballot(in);
+        if (lane == 0) {
+            s_left[j][wv] = __popcll(bl[j]);
+            s_all[j][wv] = __popcll(bi[j]);
         }
-    int tot;
-    const int ex = block_exclusive_scan_waves(nl + (nr << 16), s_scan, &tot);
+    }
+    __syncthreads();
     const int lb = left_base[blockIdx.x];
-    int lpos = node_out[3 * it.node] + lb + (ex & 0xffff);
-    int rpos = node_out[3 * it.node] + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb) + (ex >> 16);
+    const int base = node_out[3 * it.node];
+    int lpos = base + lb;                                                            // next left slot
+    int rpos = base + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb);   // next right slot
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = 0; j < kPartRows; ++j)
-        if (k0 + j < it.end) {
-            if (f[j]) out_rows[lpos++] = r[j];
-            else out_rows[rpos++] = r[j];
+    for (int j = 0; j < kPartRows; ++j) {
+        int wl = 0, wa = 0, tl = 0, ta = 0;   // earlier waves' and all waves' counts
+        for (int w = 0; w < waves; ++w) {
+            const int nl = s_left[j][w], na = s_all[j][w];
+            wl += w < wv ? nl : 0;
+            wa += w < wv ? na : 0;
+            tl += nl;
+            ta += na;
         }
+        if ((bi[j] >> lane) & 1ull) {
+            if ((bl[j] >> lane) & 1ull)
+                out_rows[lpos + wl + __popcll(bl[j] & below)] = r[j];
+            else
+                out_rows[rpos + (wa - wl) + __popcll(bi[j] & ~bl[j] & below)] = r[j];
+        }
+        lpos += tl;
+        rpos += ta - tl;
+    }
 }
 
 }  // namespace hgb
