@@ -1592,28 +1592,38 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
     HGB_HIP(c, hipSetDevice(c->device));
     static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
     const int waves = 4;   // features per block; one best per block
-    const int n_entries = (c->F + waves - 1) / waves;
+    // a lane's bins in registers when there are at most 4 of them (one wave
+    // per feature) or at most 4 x 4 per wave of a sliced block (wide bins),
+    // the buffer 16-byte aligned; otherwise read twice from memory
+    const int per = (c->B + kWave - 1) / kWave;
+    const bool aligned = ((uintptr_t)hist & 15) == 0;
+    const bool sliced = aligned && per > 4 && per <= 4 * kSliceWaves;
+    const int n_entries = sliced ? c->F : (c->F + waves - 1) / waves;
     hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * n_entries);
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
     if (st != HGB_OK) return st;
     ProfScope ps(c, HGB_KERNEL_SPLIT);
-    // a lane's bins in registers when there are at most 16 of them (and the
-    // buffer is 16-byte aligned); otherwise read twice from memory
-    const int per = (c->B + kWave - 1) / kWave;
-    const bool aligned = ((uintptr_t)hist & 15) == 0;
     dim3 grid((unsigned)n_entries, (unsigned)n_nodes);
 #define HGB_SPLIT(PER)                                                                              \
     k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
         std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals)
-    if (!aligned || per > 16) HGB_SPLIT(0);
+#define HGB_SPLIT_SLICED(PER)                                                                       \
+    k_split_feature_sliced<PER><<<grid, kSliceWaves * kWave, 0, c->stream>>>(                       \
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
+        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals)
+    if (sliced) {
+        if (per <= 2 * kSliceWaves) HGB_SPLIT_SLICED(2);
+        else HGB_SPLIT_SLICED(4);
+    } else if (!aligned || per > 16) HGB_SPLIT(0);
     else if (per <= 1) HGB_SPLIT(1);
     else if (per <= 2) HGB_SPLIT(2);
     else if (per <= 4) HGB_SPLIT(4);
     else if (per <= 8) HGB_SPLIT(8);
     else HGB_SPLIT(16);
 #undef HGB_SPLIT
+#undef HGB_SPLIT_SLICED
     HGB_LAUNCHED(c, "k_split_feature");
     k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries,
                                                              (SplitOut*)out);
@@ -1702,7 +1712,10 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     }
     HGB_HIP(c, hipSetDevice(c->device));
     const int n_nodes = 2 * n_pairs;
-    const int n_entries = (c->F + 3) / 4;   // one best per block of 4 features
+    // one best per block of 4 features, or per feature for wide bins (a
+    // sliced block of kSliceWaves waves per feature)
+    const bool sliced = per > 4 && per <= 4 * kSliceWaves;
+    const int n_entries = sliced ? c->F : (c->F + 3) / 4;
     hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * n_entries);
     if (st != HGB_OK) return st;
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
@@ -1726,12 +1739,20 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     k_subtract_split<PER><<<grid, waves * kWave, 0, c->stream>>>(                                  \
         (const long long*)parent, (long long*)child, plan_dev, inl, c->F, c->B, c->S, c->has_missing, \
         sg, sh, lambda, gamma, c->best, c->totals)
-        if (per <= 1) HGB_SUBSPLIT(1);
+#define HGB_SUBSPLIT_SLICED(PER)                                                                   \
+    k_subtract_split_sliced<PER><<<grid, kSliceWaves * kWave, 0, c->stream>>>(                     \
+        (const long long*)parent, (long long*)child, plan_dev, inl, c->F, c->B, c->S, c->has_missing, \
+        sg, sh, lambda, gamma, c->best, c->totals)
+        if (sliced) {
+            if (per <= 2 * kSliceWaves) HGB_SUBSPLIT_SLICED(2);
+            else HGB_SUBSPLIT_SLICED(4);
+        } else if (per <= 1) HGB_SUBSPLIT(1);
         else if (per <= 2) HGB_SUBSPLIT(2);
         else if (per <= 4) HGB_SUBSPLIT(4);
         else if (per <= 8) HGB_SUBSPLIT(8);
         else HGB_SUBSPLIT(16);
 #undef HGB_SUBSPLIT
+#undef HGB_SUBSPLIT_SLICED
         HGB_LAUNCHED(c, "k_subtract_split");
         k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries, (SplitOut*)out);
         HGB_LAUNCHED(c, "k_split_reduce");

@@ -1831,14 +1831,13 @@ __device__ inline void prefix_visit(const long long* __restrict__ hf, const Lane
 // candidate from the prefix scan, then a wave argmax.  Every lane returns the
 // result (gain -inf and code -1 when no candidate).
 template <int PER>
-__device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins,
-                                     int has_missing, double scale_g, double scale_h, double lam,
-                                     double gamma)
+__device__ inline WaveBest scan_best(const long long* __restrict__ hf, const LaneSlots<PER>& s,
+                                     const WavePrefix& p, int has_missing, double scale_g, double scale_h,
+                                     double lam, double gamma)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const long long miss_g = s.miss.x;
     const long long miss_h = s.miss.y;
-    const WavePrefix p = wave_prefix<PER>(hf, s, n_bins);
     const long long G = p.G, H = p.H;
     const double g = (double)G * scale_g;
     const double h = (double)H * scale_h;
@@ -1886,6 +1885,78 @@ __device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const Lan
     r.G = G;
     r.H = H;
     return r;
+}
+
+template <int PER>
+__device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const LaneSlots<PER>& s, int n_bins,
+                                     int has_missing, double scale_g, double scale_h, double lam,
+                                     double gamma)
+{
+    return scan_best<PER>(hf, s, wave_prefix<PER>(hf, s, n_bins), has_missing, scale_g, scale_h, lam, gamma);
+}
+
+// Features with more bins than 64 * 4 (up to 1,024): one block of
+// kSliceWaves waves per feature, wave q owning the bins [q * 64 * PER,
+// (q + 1) * 64 * PER) in contiguous lane runs of PER <= 4.  A single wave
+// would hold up to 16 bins per lane and leave the chip with few waves; here
+// the slices' sums meet in LDS (the carry into each slice and the feature's
+// totals) and each wave scans its own slice.
+constexpr int kSliceWaves = 4;
+
+template <int PER>
+__device__ inline void load_slice_slots(const long long* __restrict__ hf, int n_bins, int has_missing,
+                                        int bin0, LaneSlots<PER>& s)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const longlong2* h2 = (const longlong2*)hf;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int b = bin0 + lane * PER + j;
+        const longlong2 t = h2[min(b, n_bins - 1)];   // unconditional, masked below
+        s.v[j] = b < n_bins ? t : make_longlong2(0, 0);
+    }
+    s.miss = has_missing ? make_longlong2(hf[2 * n_bins], hf[2 * n_bins + 1]) : make_longlong2(0, 0);
+}
+
+// The slice's prefix: the lane's exclusive prefix within the wave plus the
+// earlier slices' sums, and the feature's totals.  s_sum holds 2 * kSliceWaves
+// values; every thread of the block calls (one barrier).
+template <int PER>
+__device__ inline WavePrefix slice_prefix(const LaneSlots<PER>& s, int n_bins, int bin0, long long* s_sum)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x / kWave;
+    WavePrefix p;
+    p.b0 = bin0 + lane * PER;
+    p.b1 = min(p.b0 + PER, n_bins);
+    long long sg = 0, sh = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) { sg += s.v[j].x; sh += s.v[j].y; }
+    long long ig = sg, ih = sh;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const long long tg = wave_shfl_up_i64(ig, d);
+        const long long th = wave_shfl_up_i64(ih, d);
+        if (lane >= d) { ig += tg; ih += th; }
+    }
+    if (lane == kWave - 1) {
+        s_sum[2 * q] = ig;
+        s_sum[2 * q + 1] = ih;
+    }
+    __syncthreads();
+    long long cg = 0, ch = 0, tg = 0, th = 0;
+#pragma unroll
+    for (int k = 0; k < kSliceWaves; ++k) {
+        const long long xg = s_sum[2 * k], xh = s_sum[2 * k + 1];
+        cg += k < q ? xg : 0;
+        ch += k < q ? xh : 0;
+        tg += xg;
+        th += xh;
+    }
+    p.G = tg + s.miss.x;
+    p.H = th + s.miss.y;
+    p.pg = cg + ig - sg;
+    p.ph = ch + ih - sh;
+    return p;
 }
 
 template <int PER>
@@ -1997,6 +2068,93 @@ __global__ __launch_bounds__(256) void k_subtract_split(const long long* __restr
     if (threadIdx.x < 2)
         best[(int64_t)(threadIdx.x == 0 ? nb : no) * gridDim.x + blockIdx.x] =
             block_feature_best(s_fb[threadIdx.x], blockDim.x / kWave);
+}
+
+// One feature per block of kSliceWaves waves (wide bins): the feature's best
+// to best[node][feature]; node totals from feature 0.
+template <int PER>
+__global__ __launch_bounds__(kSliceWaves * kWave) void k_split_feature_sliced(
+    const long long* __restrict__ hist, int n_features, int n_bins, int S, int has_missing, double scale_g,
+    double scale_h, double lam, double gamma, FeatureBest* __restrict__ best, long long* __restrict__ totals)
+{
+    __shared__ long long s_sum[2 * kSliceWaves];
+    __shared__ FeatureBest s_fb[kSliceWaves];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x / kWave;
+    const int f = blockIdx.x;
+    const int node = blockIdx.y;
+    const long long* hf = hist + ((int64_t)node * n_features + f) * (int64_t)S * 2;
+    const int bin0 = q * kWave * PER;
+    LaneSlots<PER> sl;
+    load_slice_slots<PER>(hf, n_bins, has_missing, bin0, sl);
+    const WavePrefix p = slice_prefix<PER>(sl, n_bins, bin0, s_sum);
+    const WaveBest r = scan_best<PER>(hf, sl, p, has_missing, scale_g, scale_h, lam, gamma);
+    if (lane == 0) {
+        s_fb[q] = r.fb;
+        s_fb[q].feature = f;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // slices in bin order: on equal gains the earlier (smaller code) stays
+        best[(int64_t)node * gridDim.x + blockIdx.x] = block_feature_best(s_fb, kSliceWaves);
+        if (f == 0) { totals[2 * node] = r.G; totals[2 * node + 1] = r.H; }
+    }
+}
+
+// The fused level tail for wide bins: one (pair, feature) per block of
+// kSliceWaves waves, each wave a slice of both children.
+template <int PER>
+__global__ __launch_bounds__(kSliceWaves * kWave) void k_subtract_split_sliced(
+    const long long* __restrict__ parent, long long* __restrict__ child, const int32_t* __restrict__ plan,
+    const SubtractInline inl, int n_features, int n_bins, int S, int has_missing, double scale_g,
+    double scale_h, double lam, double gamma, FeatureBest* __restrict__ best, long long* __restrict__ totals)
+{
+    __shared__ long long s_sum[2][2 * kSliceWaves];
+    __shared__ FeatureBest s_fb[2][kSliceWaves];   // [0] the built child, [1] the other
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x / kWave;
+    const int f = blockIdx.x;
+    const int pair = blockIdx.y;
+    const int32_t pslot = plan ? plan[2 * pair] : inl.v[2 * pair];
+    const int r = plan ? plan[2 * pair + 1] : inl.v[2 * pair + 1];
+    const int nb = 2 * pair + r, no = 2 * pair + 1 - r;
+    const int64_t fs = (int64_t)S * 2;
+    const long long* hp = parent + ((int64_t)pslot * n_features + f) * fs;
+    const long long* hb = child + ((int64_t)nb * n_features + f) * fs;
+    long long* ho = child + ((int64_t)no * n_features + f) * fs;
+    const int bin0 = q * kWave * PER;
+    LaneSlots<PER> so, sb;
+    load_slice_slots<PER>(hp, n_bins, has_missing, bin0, so);
+    load_slice_slots<PER>(hb, n_bins, has_missing, bin0, sb);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) so.v[j] = make_longlong2(so.v[j].x - sb.v[j].x, so.v[j].y - sb.v[j].y);
+    so.miss = make_longlong2(so.miss.x - sb.miss.x, so.miss.y - sb.miss.y);
+    longlong2* o2 = (longlong2*)ho;
+    const int b0 = bin0 + lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (b0 + j < n_bins) o2[b0 + j] = so.v[j];
+    if (has_missing && threadIdx.x == 0) o2[n_bins] = so.miss;
+    const WavePrefix pb = slice_prefix<PER>(sb, n_bins, bin0, s_sum[0]);
+    const WavePrefix po = slice_prefix<PER>(so, n_bins, bin0, s_sum[1]);
+    const WaveBest wb = scan_best<PER>(hb, sb, pb, has_missing, scale_g, scale_h, lam, gamma);
+    const WaveBest wo = scan_best<PER>(ho, so, po, has_missing, scale_g, scale_h, lam, gamma);
+    if (lane == 0) {
+        s_fb[0][q] = wb.fb;
+        s_fb[0][q].feature = f;
+        s_fb[1][q] = wo.fb;
+        s_fb[1][q].feature = f;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2)
+        best[(int64_t)(threadIdx.x == 0 ? nb : no) * gridDim.x + blockIdx.x] =
+            block_feature_best(s_fb[threadIdx.x], kSliceWaves);
+    if (threadIdx.x == 0 && f == 0) {
+        totals[2 * nb] = wb.G;
+        totals[2 * nb + 1] = wb.H;
+        totals[2 * no] = wo.G;
+        totals[2 * no + 1] = wo.H;
+    }
 }
 
 struct SplitOut {
