@@ -36,7 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 FILL_CLASS = ("k_fill_root", "k_fill_root_il", "k_fill_rows", "k_fill_cols", "k_merge")
 OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_subtract_split", "k_split_feature",
-         "k_split_reduce", "k_quantize", "k_grad_hess_max")
+         "k_split_reduce", "k_split_feature_sliced", "k_subtract_split_sliced", "k_quantize",
+         "k_grad_hess_max")
 # one --pmc pass of SQ counters for the LDS side of the fill (5 of the 8 SQ slots)
 LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_ATOMIC", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
                 "SQ_LDS_ADDR_CONFLICT")
