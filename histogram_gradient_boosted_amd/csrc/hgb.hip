@@ -602,6 +602,7 @@ struct FillArgs {
     int drain;
     int64_t* hist;
     int64_t* partial;
+    ZeroList zero;   // level fills: node slots the fill clears first
 };
 
 template <typename BinT, int ACC, bool SKIP>
@@ -659,15 +660,15 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 #undef HGB_ROOT
     } else if (p.kind == kFillCols) {
         switch (p.tile) {
-        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
-        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
-        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
-        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot); break;
+        case 1: HGB_LAUNCH((k_fill_cols<BinT, 1, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot, a.zero); break;
+        case 2: HGB_LAUNCH((k_fill_cols<BinT, 2, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot, a.zero); break;
+        case 4: HGB_LAUNCH((k_fill_cols<BinT, 4, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot, a.zero); break;
+        default: HGB_LAUNCH((k_fill_cols<BinT, 8, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->rot, a.zero); break;
         }
     } else {
         // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-#define HGB_ROWS(LT, RA, E, IL) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP, IL>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot)
+#define HGB_ROWS(LT, RA, E, IL) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP, IL>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot, a.zero)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
@@ -927,12 +928,18 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
     Stage* sg = nullptr;
     st = stage_upload(c, blob.data(), bytes, &sg);
     if (st != HGB_OK) return st;
-    st = launch_zero(c, hist, (const int32_t*)((const uint8_t*)sg->dev + off_zero), zero_slots.size());
-    if (st != HGB_OK) return st;
-    if (items.empty()) return stage_release(c, sg);
     const uint8_t* dev = (const uint8_t*)sg->dev;
+    if (items.empty()) {   // nothing to fill: the slots to clear get their own launch
+        st = launch_zero(c, hist, (const int32_t*)(dev + off_zero), zero_slots.size());
+        if (st != HGB_OK) return st;
+        return stage_release(c, sg);
+    }
     {
         FillArgs a{};
+        // the fill clears the listed slots before k_merge adds into them
+        a.zero.slots = (const int32_t*)(dev + off_zero);
+        a.zero.n = (int)zero_slots.size();
+        a.zero.node_vec = (int64_t)c->F * c->S;
         a.gh = c->gh;
         a.row_index = row_index;
         a.items = (const FillItem*)dev;

@@ -1252,6 +1252,25 @@ __device__ inline void fill_cols_item(unsigned long long* lds, const FillItem& i
 // Level fills run one block per CU-sized share of the level: block b takes
 // the items [block_first[b], block_first[b + 1]) in turn -- consecutive pieces
 // of the level order, one per node that the share touches.
+// Node slots of the level buffer to clear (those k_merge adds into with
+// atomics, and empty nodes), cleared by the level fill itself: k_merge runs
+// after it, so no separate launch is needed.
+struct ZeroList {
+    const int32_t* slots;   // device
+    int n;
+    int64_t node_vec;       // longlong2 per node slot
+};
+
+__device__ inline void zero_listed(const ZeroList& z, unsigned long long* hist)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int k = 0; k < z.n; ++k) {
+        longlong2* dst = (longlong2*)hist + (int64_t)z.slots[k] * z.node_vec;
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < z.node_vec; e += stride)
+            dst[e] = make_longlong2(0, 0);
+    }
+}
+
 template <typename BinT, int NF, int ACC, bool SKIP>
 __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bins, int64_t n,
                                                    int n_features, int S, int lc,
@@ -1261,9 +1280,10 @@ __global__ __launch_bounds__(1024) void k_fill_cols(const BinT* __restrict__ bin
                                                    const int32_t* __restrict__ block_first, int n_blocks,
                                                    int drain, unsigned long long* __restrict__ hist,
                                                    unsigned long long* __restrict__ partial,
-                                                   const int32_t* __restrict__ rot)
+                                                   const int32_t* __restrict__ rot, const ZeroList zl)
 {
     extern __shared__ unsigned long long lds[];
+    zero_listed(zl, hist);
     const int blk = xcd_item(blockIdx.x, n_blocks);
     if (blk >= n_blocks) return;
     const int i1 = block_first[blk + 1];
@@ -1635,9 +1655,10 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
                                                    int drain, unsigned long long* __restrict__ hist,
                                                    unsigned long long* __restrict__ partial,
                                                    uint32_t* __restrict__ err,
-                                                   const int32_t* __restrict__ rot)
+                                                   const int32_t* __restrict__ rot, const ZeroList zl)
 {
     extern __shared__ unsigned long long lds[];
+    zero_listed(zl, hist);
     const int blk = xcd_item(blockIdx.x, n_blocks);
     if (blk >= n_blocks) return;
     const int i1 = block_first[blk + 1];
