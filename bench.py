@@ -273,7 +273,8 @@ def lds_rates(device: int = 0):
     out = {}
     n_cu = ctypes.c_int(0)
     for name, kind, copies in (("u64_random_bins_1_copy", 0, 1), ("u64_random_bins_2_copies", 0, 2),
-                               ("u64_random_bins_16_copies", 0, 16), ("u64_conflict_free", 1, 1)):
+                               ("u64_random_bins_16_copies", 0, 16), ("u64_conflict_free", 1, 1),
+                               ("u64_interleaved_tile_fill_shape", 3, 1)):
         r = ctypes.c_double(0.0)
         if fn(device, kind, copies, ctypes.byref(r), ctypes.byref(n_cu)) != 0:
             return None
@@ -481,6 +482,9 @@ def main():
             "frac": round(lds_achieved / rates["u64_conflict_free"], 4),
             "peak_kind": "measured: conflict-free u64 LDS atomic adds, whole chip (csrc/lds_rate.hip)",
             "random_bins": {k: round(v / 1e9, 1) for k, v in rates.items() if k.startswith("u64_random")},
+            # the fills' own pattern and launch shape: two lanes per bank pair,
+            # 16 waves per CU (the ceiling a 1024-thread fill block can reach)
+            "interleaved_tile_fill_shape": round(rates["u64_interleaved_tile_fill_shape"] / 1e9, 1),
             "scale": "G lane-ops/s", "n_cu": rates["n_cu"]}
         log(f"[bench] LDS atomics {lds_achieved / 1e9:.0f} G/s in the fill; microbenchmark "
             f"{ {k: round(v / 1e9) for k, v in rates.items() if k != 'n_cu'} } G/s")

@@ -9,8 +9,12 @@
 //   kind 1  u64 atomic add, every lane a distinct word (no bank or address
 //           conflicts: the conflict-free ceiling);
 //   kind 2  u32 atomic add, random bins as kind 0.
+//   kind 3  u64 atomic add in the fills' interleaved (slot-major) tile: word =
+//           bin * 64 + (lane + k) mod 32 for the k-th add -- two lanes per bank
+//           pair whatever the bins -- launched in the fills' shape, one block
+//           of 1024 threads and a 128 KB tile per CU (`copies` unused).
 //
-// Every launch fills the chip (8 blocks of 256 threads per CU) and each thread
+// Kinds 0-2 fill the chip with 8 blocks of 256 threads per CU; each thread
 // issues `iters` x 4 adds.  Indices are reduced modulo the allocated word count,
 // so every access stays inside the block's LDS allocation.  The result is read
 // back into a sink so the adds cannot be elided.
@@ -28,7 +32,7 @@ __device__ inline uint32_t xorshift(uint32_t x)
 }
 
 template <int KIND>
-__global__ __launch_bounds__(256) void k_lds_rate(int iters, int copies, int words, unsigned long long* sink)
+__global__ __launch_bounds__(1024) void k_lds_rate(int iters, int copies, int words, unsigned long long* sink)
 {
     extern __shared__ unsigned long long lds[];
     uint32_t* l32 = (uint32_t*)lds;
@@ -36,7 +40,7 @@ __global__ __launch_bounds__(256) void k_lds_rate(int iters, int copies, int wor
     const int lane = tid & 63;
     for (int i = tid; i < words; i += blockDim.x) lds[i] = 0;
     __syncthreads();
-    uint32_t s = 0x9e3779b9u * (uint32_t)(blockIdx.x * 256 + tid + 1);
+    uint32_t s = 0x9e3779b9u * (uint32_t)(blockIdx.x * blockDim.x + tid + 1);
     const uint32_t cm = (uint32_t)copies - 1;
     const uint32_t wm = (uint32_t)words - 1;        // words is a power of two
     for (int it = 0; it < iters; ++it) {
@@ -47,6 +51,7 @@ __global__ __launch_bounds__(256) void k_lds_rate(int iters, int copies, int wor
             if (KIND == 0) atomicAdd(&lds[(b * (uint32_t)copies + ((uint32_t)lane & cm)) & wm], 3ull);
             if (KIND == 1) atomicAdd(&lds[((uint32_t)lane + 64u * (uint32_t)k) & wm], 3ull);
             if (KIND == 2) atomicAdd(&l32[(b * (uint32_t)copies + ((uint32_t)lane & cm)) & (2 * wm + 1)], 3u);
+            if (KIND == 3) atomicAdd(&lds[((b << 6) | (((uint32_t)lane + (uint32_t)k) & 31u)) & wm], 3ull);
         }
     }
     __syncthreads();
@@ -56,13 +61,14 @@ __global__ __launch_bounds__(256) void k_lds_rate(int iters, int copies, int wor
 }
 
 template <int KIND>
-hipError_t launch(int iters, int copies, int words, int blocks, unsigned long long* sink, hipStream_t st)
+hipError_t launch(int iters, int copies, int words, int blocks, int threads, unsigned long long* sink,
+                  hipStream_t st)
 {
     const size_t bytes = (size_t)words * 8;
     hipError_t e = hipFuncSetAttribute((const void*)k_lds_rate<KIND>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    k_lds_rate<KIND><<<blocks, 256, bytes, st>>>(iters, copies, words, sink);
+    k_lds_rate<KIND><<<blocks, threads, bytes, st>>>(iters, copies, words, sink);
     return hipGetLastError();
 }
 
@@ -73,21 +79,25 @@ using namespace lds_probe;
 extern "C" {
 
 // Measures lane-level LDS atomic adds per second on `device` for pattern
-// `kind` (0, 1 or 2 above) with `copies` in {1, 2, 4, ..., 32}.  Writes the
+// `kind` (0 to 3 above) with `copies` in {1, 2, 4, ..., 32}.  Writes the
 // rate to *lane_ops_per_s and the number of compute units to *n_cu.  Returns 0
 // on success, 1 for bad arguments, 2 for a HIP error.
 int lds_rate_measure(int device, int kind, int copies, double* lane_ops_per_s, int* n_cu)
 {
-    if (!lane_ops_per_s || !n_cu || kind < 0 || kind > 2 || copies < 1 || copies > 32 ||
+    if (!lane_ops_per_s || !n_cu || kind < 0 || kind > 3 || copies < 1 || copies > 32 ||
         (copies & (copies - 1)) != 0)
         return 1;
     if (hipSetDevice(device) != hipSuccess) return 2;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 2;
     *n_cu = prop.multiProcessorCount;
-    const int blocks = prop.multiProcessorCount * 8;
+    const bool fill_shape = kind == 3;
+    const int blocks = prop.multiProcessorCount * (fill_shape ? 1 : 8);
+    const int threads = fill_shape ? 1024 : 256;
     const int iters = 2000;
-    const int words = 256 * copies;   // kind 1 uses the same allocation
+    // kind 1 uses kind 0's allocation; kind 3 a 128 KB tile (256 slots x 2
+    // planes x 32 positions)
+    const int words = fill_shape ? 256 * 64 : 256 * copies;
     unsigned long long* sink = nullptr;
     hipStream_t st = nullptr;
     hipEvent_t a = nullptr, b = nullptr;
@@ -98,15 +108,16 @@ int lds_rate_measure(int device, int kind, int copies, double* lane_ops_per_s, i
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) goto done;
     for (int rep = 0; rep < 2; ++rep) {   // the first launch warms up
         if (hipEventRecord(a, st) != hipSuccess) goto done;
-        hipError_t e = kind == 0   ? launch<0>(iters, copies, words, blocks, sink, st)
-                       : kind == 1 ? launch<1>(iters, copies, words, blocks, sink, st)
-                                   : launch<2>(iters, copies, words, blocks, sink, st);
+        hipError_t e = kind == 0   ? launch<0>(iters, copies, words, blocks, threads, sink, st)
+                       : kind == 1 ? launch<1>(iters, copies, words, blocks, threads, sink, st)
+                       : kind == 2 ? launch<2>(iters, copies, words, blocks, threads, sink, st)
+                                   : launch<3>(iters, copies, words, blocks, threads, sink, st);
         if (e != hipSuccess) goto done;
         if (hipEventRecord(b, st) != hipSuccess) goto done;
         if (hipEventSynchronize(b) != hipSuccess) goto done;
     }
     if (hipEventElapsedTime(&ms, a, b) != hipSuccess || ms <= 0.0f) goto done;
-    *lane_ops_per_s = (double)blocks * 256.0 * iters * 4.0 / (ms * 1e-3);
+    *lane_ops_per_s = (double)blocks * threads * (double)iters * 4.0 / (ms * 1e-3);
     rc = 0;
 done:
     if (a) (void)hipEventDestroy(a);
