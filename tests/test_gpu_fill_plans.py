@@ -149,3 +149,17 @@ def test_root_fill_interleaved(hgb, torch, monkeypatch, capfd, case, tile, copie
     run_root_both(hgb, torch, make(), bits=bits)
     plans = root_plans(capfd.readouterr().err)
     assert plans == [(copies, tile, 1)], plans
+
+
+@pytest.mark.parametrize("plan_host", ["0", "1"])
+def test_plan_staging_modes(hgb, torch, monkeypatch, plan_host):
+    """Launch plans read in place from pinned host memory (the default) or
+    from a device copy (HGB_PLAN_HOST=0): the same histograms and splits,
+    through the root, level fills with partial merges, the fused tail and a
+    level of 300 pairs (whose subtraction plan is staged too)."""
+    say("plan staging", plan_host)
+    monkeypatch.setenv("HGB_PLAN_HOST", plan_host)
+    run_root_both(hgb, torch, synth.random_small(320, 50_000, 28, 256, False, 0))
+    run_level_both(hgb, torch, synth.random_small(321, 60_000, 28, 256, False, 8), check_exact_gain=True)
+    run_level_both(hgb, torch, synth.random_small(322, 20_000, 3, 16, True, 600), check_exact_gain=True,
+                   fused=True)
