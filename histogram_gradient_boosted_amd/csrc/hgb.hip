@@ -989,14 +989,13 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
         k_grad_hess_max<Src><<<max_blocks, 256, 0, c->stream>>>(src, c->n, vec, c->max_part);
         HGB_LAUNCHED(c, "k_grad_hess_max");
         k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words, c->precision,
-                                              (double*)(c->dev_words + 4));
+                                              (double*)(c->dev_words + 4), c->host_words);
         HGB_LAUNCHED(c, "k_max_final");
     }
-    // The maxima go back to the host (to check them, and to keep the
-    // exponents for the split pass) while the quantize pass, which takes its
-    // scales from the device, already runs: the host waits on an event
-    // recorded before that pass.
-    HGB_HIP(c, hipMemcpyAsync(c->host_words, c->dev_words, 8, hipMemcpyDeviceToHost, c->stream));
+    // k_max_final wrote the maxima into pinned host memory too (the host
+    // checks them and keeps the exponents for the split pass); the quantize
+    // pass, which takes its scales from the device, already runs while the
+    // host waits on an event recorded before that pass.
     if (!c->host_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->host_ready, hipEventDisableTiming));
     HGB_HIP(c, hipEventRecord(c->host_ready, c->stream));
     {
@@ -1867,12 +1866,8 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         }
         k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
                                                (const int32_t*)(dev + off_offs), sp, n_nodes, left_base,
-                                               node_out);
-        HGB_LAUNCHED(c, "k_part_scan");
-        HGB_HIP(c, hipMemcpyAsync(c->part_host, node_out, sizeof(int32_t) * 3 * (size_t)n_nodes,
-                                  hipMemcpyDeviceToHost, c->stream));
-        // the count pass has set the error word by now too
-        HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost, c->stream));
+                                               node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
+        HGB_LAUNCHED(c, "k_part_scan");   // node records and error word written to pinned host memory
         if (!c->part_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->part_ready, hipEventDisableTiming));
         HGB_HIP(c, hipEventRecord(c->part_ready, c->stream));
         if (n_items > 0) {

@@ -228,7 +228,8 @@ __device__ inline double scale_of_max(uint32_t pat, int precision)
 // out[0..1]: the maxima's bit patterns; scales[0..1]: their scales (above).
 __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ part, int n_blocks,
                                                    uint32_t* __restrict__ out, int precision,
-                                                   double* __restrict__ scales)
+                                                   double* __restrict__ scales,
+                                                   uint32_t* __restrict__ host_out)
 {
     __shared__ uint32_t red[2][256];
     uint32_t mg = 0, mh = 0;
@@ -249,6 +250,8 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
     if (threadIdx.x == 0) {
         out[0] = red[0][0];
         out[1] = red[1][0];
+        host_out[0] = red[0][0];   // pinned host memory: no read-back copy
+        host_out[1] = red[1][0];
         scales[0] = scale_of_max(red[0][0], precision);
         scales[1] = scale_of_max(red[1][0], precision);
     }
@@ -2567,7 +2570,10 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ offsets,
                                                     const SplitOut* __restrict__ splits, int n_nodes,
                                                     int32_t* __restrict__ left_base,
-                                                    int32_t* __restrict__ node_out)
+                                                    int32_t* __restrict__ node_out,
+                                                    int32_t* __restrict__ host_out,
+                                                    const uint32_t* __restrict__ err_dev,
+                                                    uint32_t* __restrict__ err_host)
 {
     __shared__ int s_scan[1024];
     int carry = 0, tot = 0;
@@ -2599,6 +2605,11 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
         if (i < n_nodes) node_out[3 * i] = carry + ex;
         carry += tot;
     }
+    // the node records and the count pass's error word straight into pinned
+    // host memory: the host reads them once the stream passes this kernel
+    __syncthreads();
+    for (int i = threadIdx.x; i < 3 * n_nodes; i += blockDim.x) host_out[i] = node_out[i];
+    if (threadIdx.x == 0) *err_host = *err_dev;
 }
 
 // Write each row to its place: the chunk's left rows from its left base on,
