@@ -1855,11 +1855,11 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         ProfScope ps(c, HGB_KERNEL_PARTITION);
         if (n_items > 0) {
             if (c->bin_bytes == 1)
-                k_part_count<uint8_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                k_part_count<uint8_t><<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(
                     (const uint8_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
                     c->dev_words + 2);
             else
-                k_part_count<uint16_t><<<(unsigned)n_items, 1024, 0, c->stream>>>(
+                k_part_count<uint16_t><<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(
                     (const uint16_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
                     c->dev_words + 2);
             HGB_LAUNCHED(c, "k_part_count");
@@ -1871,7 +1871,7 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
         if (!c->part_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->part_ready, hipEventDisableTiming));
         HGB_HIP(c, hipEventRecord(c->part_ready, c->stream));
         if (n_items > 0) {
-            k_part_scatter<<<(unsigned)n_items, 1024, 0, c->stream>>>(row_index, items_dev, sp, c->part_flags,
+            k_part_scatter<<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(row_index, items_dev, sp, c->part_flags,
                                                                       left_base, node_out, out_rows);
             HGB_LAUNCHED(c, "k_part_scatter");
         }

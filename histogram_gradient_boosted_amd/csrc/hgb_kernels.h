@@ -2465,6 +2465,7 @@ __global__ __launch_bounds__(256) void k_level_records(const long long* __restri
 // rows going left per chunk; scan the counts per node and the output extents
 // over nodes; scatter each row to its place.
 // ---------------------------------------------------------------------------
+constexpr int kPartThreads = 1024;   // threads of a count or scatter block (256 measured slower)
 constexpr int kPartChunk = 8192;
 
 struct PartItem {
@@ -2478,17 +2479,17 @@ __device__ inline bool part_left(int v, int n_bins, const SplitOut& sp)
     return v == n_bins ? sp.default_left != 0 : v <= sp.bin;
 }
 
-// Each thread takes kPartRows positions of its chunk (1024 threads x
-// kPartRows = kPartChunk), position begin + j * 1024 + thread at its j-th
-// step, so that every index load and direction store of a wave is one
+// Each thread takes kPartRows positions of its chunk (kPartThreads threads x
+// kPartRows = kPartChunk), position begin + j * kPartThreads + thread at its
+// j-th step, so that every index load and direction store of a wave is one
 // contiguous run; loads are issued independently and clamped into the chunk.
 constexpr int kPartRows = 8;
-static_assert(kPartChunk == 1024 * kPartRows, "a chunk is one pass of a 1024-thread block");
+static_assert(kPartChunk == kPartThreads * kPartRows, "a chunk is one pass of a block");
 
 // Count the rows going left per chunk, and record each position's direction
 // (1 = left) for the scatter.
 template <typename BinT>
-__global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
+__global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
                                                      int S, const int32_t* __restrict__ rot,
                                                      const int32_t* __restrict__ row_index,
                                                      const PartItem* __restrict__ items,
@@ -2496,7 +2497,7 @@ __global__ __launch_bounds__(1024) void k_part_count(const BinT* __restrict__ bi
                                                      int32_t* __restrict__ cnt, uint8_t* __restrict__ flags,
                                                      uint32_t* __restrict__ err)
 {
-    __shared__ int s_sum[1024 / kWave];
+    __shared__ int s_sum[kPartThreads / kWave];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     int c = 0;
@@ -2619,7 +2620,7 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
 // and the steps follow each other.  Every wave publishes its counts of all
 // steps at once, so one barrier serves the whole chunk.  The stores of a
 // wave's left (right) rows in one step are one contiguous run.
-__global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict__ row_index,
+__global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __restrict__ row_index,
                                                        const PartItem* __restrict__ items,
                                                        const SplitOut* __restrict__ splits,
                                                        const uint8_t* __restrict__ flags,
@@ -2627,8 +2628,8 @@ __global__ __launch_bounds__(1024) void k_part_scatter(const int32_t* __restrict
                                                        const int32_t* __restrict__ node_out,
                                                        int32_t* __restrict__ out_rows)
 {
-    __shared__ int s_left[kPartRows][1024 / kWave];
-    __shared__ int s_all[kPartRows][1024 / kWave];
+    __shared__ int s_left[kPartRows][kPartThreads / kWave];
+    __shared__ int s_all[kPartRows][kPartThreads / kWave];
     const PartItem it = items[blockIdx.x];
     const SplitOut sp = splits[it.node];
     if (sp.feature < 0) return;   // uniform: the node has no children
