@@ -732,6 +732,23 @@ hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
 
 // Zero whole node slots of the level buffer.
 // Zero whole node slots of the level buffer; the slot list is on the device.
+// Sum partial histograms into their nodes' slots: the merge list inline in
+// the arguments when it is short, else read from its staged plan.
+hgb_status launch_merge(hgb_ctx* c, const std::vector<MergeEntry>& merges, const MergeEntry* staged,
+                        dim3 grid, int64_t* hist)
+{
+    const int64_t node_vec = (int64_t)c->F * c->S;
+    MergeInline inl{};
+    const MergeEntry* plan = staged;
+    if (merges.size() <= (size_t)kMergeInline) {
+        std::memcpy(inl.e, merges.data(), merges.size() * sizeof(MergeEntry));
+        plan = nullptr;
+    }
+    k_merge<<<grid, 256, 0, c->stream>>>((const longlong2*)c->partial, (longlong2*)hist, plan, inl, node_vec);
+    HGB_LAUNCHED(c, "k_merge");
+    return HGB_OK;
+}
+
 hgb_status launch_zero(hgb_ctx* c, int64_t* hist, const int32_t* slots_dev, size_t n_slots)
 {
     if (n_slots == 0) return HGB_OK;
@@ -963,9 +980,8 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         if (!merges.empty()) {
             const int64_t node_vec = (int64_t)c->F * c->S;
             dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
-            k_merge<<<grid, 256, 0, c->stream>>>((const longlong2*)c->partial, (longlong2*)hist,
-                                                 (const MergeEntry*)(dev + off_merges), node_vec);
-            HGB_LAUNCHED(c, "k_merge");
+            st = launch_merge(c, merges, (const MergeEntry*)(dev + off_merges), grid, hist);
+            if (st != HGB_OK) return st;
         }
     }
     return stage_release(c, sg);
@@ -1544,9 +1560,8 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         ProfScope ps(c, HGB_KERNEL_FILL);
         const int64_t node_vec = (int64_t)c->F * c->S;
         dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
-        k_merge<<<grid, 256, 0, c->stream>>>((const longlong2*)c->partial, (longlong2*)hist,
-                                             (const MergeEntry*)(dev + off_merges), node_vec);
-        HGB_LAUNCHED(c, "k_merge");
+        st = launch_merge(c, merges, (const MergeEntry*)(dev + off_merges), grid, hist);
+        if (st != HGB_OK) return st;
     }
     return stage_release(c, sg);
 }

@@ -457,11 +457,18 @@ struct MergeEntry {
     int32_t atomic;
 };
 
+// A short merge list travels in the kernel's arguments (none to fetch).
+constexpr int kMergeInline = 128;
+struct MergeInline {
+    MergeEntry e[kMergeInline];
+};
+
 __global__ __launch_bounds__(256) void k_merge(const longlong2* __restrict__ partial,
                                                longlong2* __restrict__ hist,
-                                               const MergeEntry* __restrict__ plan, int64_t node_vec)
+                                               const MergeEntry* __restrict__ plan, const MergeInline inl,
+                                               int64_t node_vec)
 {
-    const MergeEntry m = plan[blockIdx.y];
+    const MergeEntry m = plan ? plan[blockIdx.y] : inl.e[blockIdx.y];
     const longlong2* src = partial + (int64_t)m.first * node_vec;
     longlong2* dst = hist + (int64_t)m.out_slot * node_vec;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;

@@ -163,3 +163,20 @@ def test_plan_staging_modes(hgb, torch, monkeypatch, plan_host):
     run_level_both(hgb, torch, synth.random_small(321, 60_000, 28, 256, False, 8), check_exact_gain=True)
     run_level_both(hgb, torch, synth.random_small(322, 20_000, 3, 16, True, 600), check_exact_gain=True,
                    fused=True)
+
+
+@pytest.mark.parametrize("ipc", [1, 4])
+def test_merge_lists_short_and_long(hgb, torch, monkeypatch, capfd, ipc):
+    """Partial histograms summed by k_merge: a short merge list travels in the
+    kernel's arguments, a long one (more than 128 entries: here 4 shares per
+    CU over 200 built nodes, so most nodes span several shares) is read from
+    its staged plan; both against the oracle."""
+    say("merge lists", ipc)
+    monkeypatch.setenv("HGB_FILL_TUNE", f"level_ipc={ipc}")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    w = synth.random_small(330, 400_000, 28, 256, False, 400)
+    run_level_both(hgb, torch, w, check_exact_gain=True)
+    merges = [int(m) for m in re.findall(r"\[hgb\] fill kind 2 .* merges (\d+)", capfd.readouterr().err)]
+    assert merges, "no level fill ran"
+    if ipc == 4:
+        assert max(merges) > 128, merges
