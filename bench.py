@@ -427,6 +427,8 @@ def main():
     log(f"[bench] per-step device ms by kernel class: {breakdown}; launches {{{', '.join(f'{k}: {v[1] // args.steps}' for k, v in prof.items())}}}")
     log(f"[bench] wall ms/step {ms_per_step:.3f} (timed, events off), {wall_prof * 1e3 / args.steps:.3f} (events on)")
 
+    traffic = traffic_record(args.config, args.precision,
+                             "_oblivious" if args.oblivious else "_grow" if args.grow else "")
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -454,9 +456,11 @@ def main():
         "kernel_ms_per_step": breakdown,
         "roofline": {"bound": "hbm", "kernel": FILL_KERNELS, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(args.config, args.precision,
-                                               "_oblivious" if args.oblivious else "_grow" if args.grow else ""),
+                     "traffic": traffic,
                      "traffic_unit": "HBM bytes per step (fetch + write, calibrated counters)",
+                     # the bytes the fill class actually moves, per second of its time
+                     "traffic_gbs": round(traffic / (fill_ms_step * 1e-3) / 1e9, 1)
+                     if traffic and fill_ms_step > 0 else None,
                      "alg_bytes_per_step": plan.fill_bytes,
                      "launches_per_step": fill_launches // max(args.steps, 1),
                      "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
