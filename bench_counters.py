@@ -29,6 +29,7 @@ import os
 import shutil
 import sqlite3
 import subprocess
+import tempfile
 import sys
 import time
 
@@ -161,7 +162,8 @@ def main() -> None:
     ap.add_argument("--drive", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--steps", type=int, default=1, help=argparse.SUPPRESS)
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
+    ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "hgb_counters"),
+                    help="where the raw rocprofv3 databases go")
     ap.add_argument("--reuse", action="store_true",
                     help="summarize the databases already under --out instead of profiling")
     ap.add_argument("--trace-summary", metavar="DB",
