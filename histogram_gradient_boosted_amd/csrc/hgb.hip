@@ -240,6 +240,31 @@ hgb_status stage_release(hgb_ctx* c, Stage* s)
     return HGB_OK;
 }
 
+// A stage held from its upload until its consumers are enqueued.  release()
+// records the stage's event; on an early (error) return the destructor does,
+// so a plan that an already launched kernel reads is never handed out again
+// before that kernel is done.
+struct StageLease {
+    hgb_ctx* c;
+    Stage* s = nullptr;
+    explicit StageLease(hgb_ctx* ctx) : c(ctx) {}
+    StageLease(const StageLease&) = delete;
+    StageLease& operator=(const StageLease&) = delete;
+    hgb_status release()
+    {
+        Stage* t = s;
+        s = nullptr;
+        return t ? stage_release(c, t) : HGB_OK;
+    }
+    ~StageLease()
+    {
+        if (s) {
+            (void)hipEventRecord(s->ev, c->stream);
+            s->pending = true;
+        }
+    }
+};
+
 // Poll `ev` until the work before it is done.  A level loop waits for small
 // results (maxima, node records) several times per tree; a blocking wait
 // would add the host's wake-up latency to each of them.
@@ -951,14 +976,14 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         std::memcpy(blob.data() + off_merges, merges.data(), merges.size() * sizeof(MergeEntry));
     if (!zero_slots.empty())
         std::memcpy(blob.data() + off_zero, zero_slots.data(), zero_slots.size() * sizeof(int32_t));
-    Stage* sg = nullptr;
-    st = stage_upload(c, blob.data(), bytes, &sg);
+    StageLease sg(c);
+    st = stage_upload(c, blob.data(), bytes, &sg.s);
     if (st != HGB_OK) return st;
-    const uint8_t* dev = (const uint8_t*)sg->use;
+    const uint8_t* dev = (const uint8_t*)sg.s->use;
     if (items.empty()) {   // nothing to fill: the slots to clear get their own launch
         st = launch_zero(c, hist, (const int32_t*)(dev + off_zero), zero_slots.size());
         if (st != HGB_OK) return st;
-        return stage_release(c, sg);
+        return sg.release();
     }
     {
         FillArgs a{};
@@ -984,7 +1009,7 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
             if (st != HGB_OK) return st;
         }
     }
-    return stage_release(c, sg);
+    return sg.release();
 }
 
 }  // namespace
@@ -1526,10 +1551,10 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
             std::memcpy(blob.data() + offs[wdt], groups[wdt].data(), groups[wdt].size() * sizeof(FillItem));
     if (!merges.empty())
         std::memcpy(blob.data() + off_merges, merges.data(), merges.size() * sizeof(MergeEntry));
-    Stage* sg = nullptr;
-    hgb_status st = stage_upload(c, blob.data(), bytes, &sg);
+    StageLease sg(c);
+    hgb_status st = stage_upload(c, blob.data(), bytes, &sg.s);
     if (st != HGB_OK) return st;
-    const uint8_t* dev = (const uint8_t*)sg->use;
+    const uint8_t* dev = (const uint8_t*)sg.s->use;
     if (zero_root) {
         st = launch_zero(c, hist, (const int32_t*)dev, 1);
         if (st != HGB_OK) return st;
@@ -1563,7 +1588,7 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         st = launch_merge(c, merges, (const MergeEntry*)(dev + off_merges), grid, hist);
         if (st != HGB_OK) return st;
     }
-    return stage_release(c, sg);
+    return sg.release();
 }
 
 hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* child,
@@ -1590,14 +1615,14 @@ hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* chi
     const int64_t pair_vec = (int64_t)c->F * c->S;   // longlong2 per slot
     dim3 grid(grid_for(pair_vec, 256, 2048), (unsigned)n_pairs);
     SubtractInline inl{};
-    Stage* s = nullptr;
+    StageLease s(c);
     const int32_t* plan_dev = nullptr;
     if (n_pairs <= kSubtractInlinePairs) {
         std::memcpy(inl.v, plan.data(), plan.size() * sizeof(int32_t));
     } else {
-        hgb_status st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
+        hgb_status st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s.s);
         if (st != HGB_OK) return st;
-        plan_dev = (const int32_t*)s->use;
+        plan_dev = (const int32_t*)s.s->use;
     }
     {
         ProfScope ps(c, HGB_KERNEL_SUBTRACT);
@@ -1605,7 +1630,7 @@ hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* chi
                                                 inl, pair_vec);
     }
     HGB_LAUNCHED(c, "k_subtract");
-    return s ? stage_release(c, s) : HGB_OK;
+    return s.release();
 }
 
 hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
@@ -1752,14 +1777,14 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
     if (st != HGB_OK) return st;
     SubtractInline inl{};
-    Stage* s = nullptr;
+    StageLease s(c);
     const int32_t* plan_dev = nullptr;
     if (n_pairs <= kSubtractInlinePairs) {
         std::memcpy(inl.v, plan.data(), plan.size() * sizeof(int32_t));
     } else {
-        st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s);
+        st = stage_upload(c, plan.data(), plan.size() * sizeof(int32_t), &s.s);
         if (st != HGB_OK) return st;
-        plan_dev = (const int32_t*)s->use;
+        plan_dev = (const int32_t*)s.s->use;
     }
     const int waves = 4;
     dim3 grid((unsigned)n_entries, (unsigned)n_pairs);
@@ -1788,7 +1813,7 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
         k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries, (SplitOut*)out);
         HGB_LAUNCHED(c, "k_split_reduce");
     }
-    return s ? stage_release(c, s) : HGB_OK;
+    return s.release();
 }
 
 hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
@@ -1860,10 +1885,10 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     int32_t* left_base = c->part + n_items;
     int32_t* node_out = c->part + 2 * n_items;
 
-    Stage* sg = nullptr;
-    st = stage_upload(c, blob.data(), bytes, &sg);
+    StageLease sg(c);
+    st = stage_upload(c, blob.data(), bytes, &sg.s);
     if (st != HGB_OK) return st;
-    const uint8_t* dev = (const uint8_t*)sg->use;
+    const uint8_t* dev = (const uint8_t*)sg.s->use;
     const PartItem* items_dev = (const PartItem*)dev;
     const SplitOut* sp = (const SplitOut*)splits;
     {
@@ -1891,7 +1916,7 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
             HGB_LAUNCHED(c, "k_part_scatter");
         }
     }
-    st = stage_release(c, sg);
+    st = sg.release();
     if (st != HGB_OK) return st;
     // Wait for the node records only: the scatter keeps running while the
     // caller plans the next level (the stream orders whatever reads its rows).
