@@ -347,7 +347,7 @@ struct FillPlan {
     int64_t step_rows;  // rows a block consumes per step
     int drain;          // packed: steps between drains of the copies (0: wide)
     int ra;             // rows, packed: register-accumulator cells per thread (0: LDS)
-    int il;             // rows, wide: slot-major interleaved tile (lane-rotated features)
+    int il;             // slot-major interleaved tile (lane-rotated features)
     size_t lds_bytes;
 };
 
@@ -402,6 +402,21 @@ double fill_cost_il(int lc, int tf, int F, int w)
     const double waste = (double)((F + tf - 1) / tf * tf) / F;
     const double lds = 2.0 * waste / (ops * clk);
     const double valu = 2.0 * waste / (64.0 * clk);
+    return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
+}
+
+// The root's interleaved tile with packed sums: one add per position, plus
+// the drains -- every `drain` steps of 4 rows per thread, each of the tile's
+// S * tf * 2^lc words is exchanged with zero once (a conflict-free LDS
+// atomic) and two barriers stall the block.
+double fill_cost_il_packed(int lc, int tf, int F, int w, int S, int drain)
+{
+    const double clk = 2.4e9 * 256;
+    const double waste = (double)((F + tf - 1) / tf * tf) / F;
+    const double ops = 9.0;
+    const double drain_per_cell = (double)S * (1 << lc) / ((double)drain * kRootThreads * kRootRows);
+    const double lds = (waste + drain_per_cell) / (ops * clk);
+    const double valu = 1.5 * waste / (64.0 * clk);
     return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
 }
 
@@ -555,6 +570,38 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
                 }
             }
         }
+        // The root's interleaved tile with packed sums: 16 positions, 2^lc >= 2
+        // copies (so that the 64 lanes of an add meet 32 bank pairs and a
+        // step's 4 rows per thread put at most 2,048 rows on a copy), and
+        // each thread's share of the S * 16 cells in registers between drains.
+        // One-byte bins without the skipped slot: the register cells fit
+        // beside 16 positions of loads only there.
+        for (int lc = 1; root && acc == kPacked && lc <= 2; ++lc) {
+            const int tf = 16;
+            if (w != 1 || c->skip) break;
+            if (c->tune[9] == 0) break;
+            if (c->tune[1] > 0 && tf != c->tune[1]) break;
+            if (c->tune[0] >= 0 && lc != c->tune[0]) continue;
+            if ((int64_t)S * tf > (int64_t)kRootIlPackedCells * kRootThreads) break;
+            if ((int64_t)root_il_words(kPacked, tf, S, lc) * 8 > budget) continue;
+            const int drain = packed_drain_steps(kRootThreads, lc, kRootRows);
+            if (drain == 0) continue;
+            const int64_t il_tiles = (c->F + tf - 1) / tf;
+            const int64_t il_chunks = std::max<int64_t>(1, kRootItemsPerCu * c->n_cu / il_tiles);
+            const double merge_s = il_chunks > 1 ? 4e-6 + 2.0 * il_chunks * c->F * S * 16.0 / 5.0e12 : 0.0;
+            const double cells = std::max(1.0, (double)c->n * c->F);
+            const double cost = fill_cost_il_packed(lc, tf, c->F, w, S, drain) + merge_s / cells;
+            if (cost < best || (c->tune[9] == 1 && !(found && p.il))) {
+                best = cost;
+                found = true;
+                p.acc = kPacked;
+                p.lc = lc;
+                p.tile = tf;
+                p.lt = 0;
+                p.il = 1;
+                p.drain = drain;
+            }
+        }
         // The root's interleaved tile (wide sums): tf positions of 2^lc copies.
         // A position's bins take w registers per thread; 32 registers of them
         // fit beside the skipped slot's bookkeeping only up to 16 bytes.
@@ -580,6 +627,7 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
                     p.tile = tf;
                     p.lt = 0;
                     p.il = 1;
+                    p.drain = 0;
                 }
             }
         }
@@ -593,9 +641,9 @@ FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
     }
     if (p.il) {
         // the last tile may be partial; the tile itself never narrower than 8
-        p.lds_bytes = (size_t)(2 * S * (p.tile << p.lc) + kFixWords) * 8;
+        p.lds_bytes = (size_t)(root_il_words(p.acc, p.tile, S, p.lc) + kFixWords) * 8;
         p.step_rows = (int64_t)p.threads * kRootRows;
-        p.drain = 0;
+        if (p.acc == kWide) p.drain = 0;
         return p;
     }
     if (p.kind != kFillRowsKind) {
@@ -655,8 +703,19 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
     } while (0)
     if (p.kind == kFillRoot && p.il) {
-        if constexpr (ACC == kWide) {
-#define HGB_ROOT_IL(TF) HGB_LAUNCH((k_fill_root_il<BinT, TF, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, hist, partial, c->rot)
+#define HGB_ROOT_IL(TF) HGB_LAUNCH((k_fill_root_il<BinT, TF, SKIP, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, partial, c->rot)
+        if constexpr (ACC == kPacked) {
+            // (the plan keeps 16 positions, one-byte bins and no skipped slot)
+            if constexpr (!SKIP && sizeof(BinT) == 1) {
+                if (p.tile == 16 && p.drain > 0 && (int64_t)c->S * 16 <= (int64_t)kRootIlPackedCells * p.threads) {
+                    HGB_ROOT_IL(16);
+                } else {
+                    return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+                }
+            } else {
+                return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+            }
+        } else {
             // (the plan keeps TF * sizeof(BinT) <= 32, and <= 16 with SKIP)
             constexpr int kMaxBytes = SKIP ? 16 : 32;
             switch (p.tile) {
@@ -675,10 +734,8 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
             case 8: HGB_ROOT_IL(8); break;
             default: return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             }
-#undef HGB_ROOT_IL
-        } else {
-            return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
         }
+#undef HGB_ROOT_IL
     } else if (p.kind == kFillRoot) {
 #define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, c->rot)
         switch (p.tile) {

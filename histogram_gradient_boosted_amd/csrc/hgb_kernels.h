@@ -959,14 +959,23 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
                           it.dest == kDestAtomic, rot + f0, fix);
 }
 
-// Root fill with the interleaved (slot-major) tile, wide sums: an item covers
-// TF feature positions, of which the first nf are real features.  Each thread
-// loads kRootRows consecutive rows of every position (positions past nf
-// re-load the last real feature, and their adds land in words nothing reads),
-// rotates its registers so that lane l visits feature (l + p) mod TF at its
-// p-th position, and adds -- every wave-wide add spreads over the tile's
-// TF * 2^lc bank pairs whatever the bins.  One (g, h) load per row serves all
-// TF features.
+// Root fill with the interleaved (slot-major) tile: an item covers TF feature
+// positions, of which the first nf are real features.  Each thread loads
+// kRootRows consecutive rows of every position (positions past nf re-load the
+// last real feature, and their adds land in words nothing reads), rotates its
+// registers so that lane l visits feature (l + p) mod TF at its p-th
+// position, and adds -- every wave-wide add spreads over the tile's TF * 2^lc
+// bank pairs whatever the bins.  One (g, h) load per row serves all TF
+// features.
+//
+// Wide sums (ACC = kWide) keep G and H planes: word ((slot * 2 + plane) * C +
+// copy) * TF + f, two adds per cell.  Packed sums (ACC = kPacked, P <= 19)
+// add qh * 2^32 + qg once per cell into word (slot * C + copy) * TF + f; every
+// `drain` steps -- few enough rows per copy-slot for both halves to decode
+// exactly -- each thread takes the words of its own RA cells (cell i = slot *
+// TF + f, i = threadIdx.x + k * blockDim.x) out of the tile into int64
+// registers, zeroing them.  At the end the registers are written into the
+// wide layout with one copy, and the wide finish writes the tile out.
 template <typename BinT, int TF>
 struct RootStepIL {
     int4 q[kRootRows / 2];
@@ -987,18 +996,32 @@ __device__ inline void rotate_root_bins(RootBins<BinT> (&b)[TF], int k)
     }
 }
 
-template <typename BinT, int TF, bool SKIP>
+// LDS words of the interleaved root tile before its fixed words: the copies,
+// and for packed sums at least the one-copy wide layout the finish reads.
+__host__ __device__ inline int root_il_words(int acc_mode, int tf, int S, int lc)
+{
+    return acc_mode == kWide ? 2 * S * (tf << lc) : (S * (tf << lc) > 2 * S * tf ? S * (tf << lc) : 2 * S * tf);
+}
+
+// Register cells per thread of the packed interleaved root: 1024 threads
+// hold the 16 positions of up to 256 slots (one-byte bins).
+constexpr int kRootIlPackedCells = 4;
+
+template <typename BinT, int TF, bool SKIP, int ACC>
 __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ bins, int64_t n,
                                                        int n_features, int S, int lc,
                                                        const int2* __restrict__ q,
                                                        const FillItem* __restrict__ items, int n_items,
-                                                       int vec_ok, unsigned long long* __restrict__ hist,
+                                                       int vec_ok, int drain,
+                                                       unsigned long long* __restrict__ hist,
                                                        unsigned long long* __restrict__ partial,
                                                        const int32_t* __restrict__ rot)
 {
     static_assert(TF <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
     constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
     static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
+    constexpr bool kPack = ACC == kPacked;
+    constexpr int RA = kPack ? kRootIlPackedCells : 1;
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
     if (item >= n_items) return;
@@ -1006,7 +1029,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     const int f0 = it.f0_nf & 0xffff;
     const int nf = it.f0_nf >> 16;   // 1 <= nf <= TF
     const int G = TF << lc;
-    const int tile_w = 2 * S * G;
+    const int tile_w = root_il_words(ACC, TF, S, lc);
     unsigned long long* const fix = lds + tile_w;
     lds_zero(lds, tile_w + kFixWords);
     __syncthreads();
@@ -1014,7 +1037,36 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     const int lane = threadIdx.x & (kWave - 1);
     const int rl = lane & (TF - 1);                             // the lane's first feature
     const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;   // and its copy's offset
-    const int gsh = 1 + lc + kLogTF;                            // slot stride: 2G words
+    const int gsh = (kPack ? 0 : 1) + lc + kLogTF;              // slot stride: 2G words (G packed)
+    // packed: this thread's cells, drained out of the copies
+    long long ag[RA], ah[RA];
+#pragma unroll
+    for (int k = 0; k < RA; ++k) ag[k] = ah[k] = 0;
+    // Each thread takes its cells' words of every copy, so between the two
+    // barriers every word has one reader.  A wave's 64 cells span four slots
+    // of 16 positions; starting each slot at copy (slot mod C) spreads the
+    // lanes over the bank pairs.
+    auto drain_cells = [&]() {
+        __syncthreads();
+        const int C = 1 << lc;
+#pragma unroll
+        for (int k = 0; k < RA; ++k) {
+            const int i = (int)threadIdx.x + k * (int)blockDim.x;
+            if (i < S * TF) {
+                const int sl = i >> kLogTF;
+                unsigned long long* const base = lds + sl * G + (i & (TF - 1));
+                for (int cc = 0; cc < C; ++cc) {
+                    const int cp = (cc + sl) & (C - 1);
+                    const long long v = (long long)atomicExch(base + cp * TF, 0ull);
+                    const long long lo = (long long)(int)(uint32_t)(unsigned long long)v;
+                    ag[k] += lo;
+                    ah[k] += (v - lo) >> 32;
+                }
+            }
+        }
+        __syncthreads();
+    };
+    int dcount = 0;
 
     const BinT* const col0 = bins + (int64_t)f0 * n;
     const int64_t rb = it.row_begin, re = it.row_end;
@@ -1047,7 +1099,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
                 tg += gv;
                 th += hv;
             }
-            wk.v[j] = cell_val<kWide>(gv, hv);
+            wk.v[j] = cell_val<ACC>(gv, hv);
         }
 #pragma unroll
         for (int f = 0; f < TF; ++f) wk.b[f] = st.b[f];
@@ -1067,7 +1119,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
                 if (!SKIP || bin != 0) {   // 0: the skipped slot
                     const int word = (bin << gsh) + fo;
                     atomicAdd(lds + word, wk.v[j].a);
-                    atomicAdd(lds + word + G, wk.v[j].b);
+                    if (!kPack) atomicAdd(lds + word + G, wk.v[j].b);
                 }
             }
         }
@@ -1079,7 +1131,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
             tg += g.x;
             th += g.y;
         }
-        const CellVal v = cell_val<kWide>(g.x, g.y);
+        const CellVal v = cell_val<ACC>(g.x, g.y);
         for (int p = 0; p < TF; ++p) {
             const int f = (rl + p) & (TF - 1);
             if (f >= nf) continue;
@@ -1087,7 +1139,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
             if (!SKIP || bin != 0) {
                 const int word = (bin << gsh) + cb + f;
                 atomicAdd(lds + word, v.a);
-                atomicAdd(lds + word + G, v.b);
+                if (!kPack) atomicAdd(lds + word + G, v.b);
             }
         }
     };
@@ -1114,7 +1166,12 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
             load(nx + R <= gend ? nx : last, st);
             __builtin_amdgcn_sched_barrier(0);
             accumulate(wk);
+            if (kPack && ++dcount == drain) {
+                drain_cells();
+                dcount = 0;
+            }
         }
+        // (at most kRootRows - 1 rows on one copy: the drain period allows them)
         if (threadIdx.x == 0)
             for (int64_t r = gend; r < re; ++r) add_row(r);
     } else {
@@ -1122,13 +1179,31 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
         for (int64_t s = 0; s < n_steps; ++s) {
             const int64_t r = rb + s * blockDim.x + threadIdx.x;
             if (r < re) add_row(r);
+            if (kPack && ++dcount == drain) {   // one row per thread and step: within the period
+                drain_cells();
+                dcount = 0;
+            }
+        }
+    }
+    if (kPack) {
+        // the last rows, then the cells into the one-copy wide layout (word
+        // (slot * 2 + plane) * TF + f; every word was zeroed by the drain)
+        drain_cells();
+#pragma unroll
+        for (int k = 0; k < RA; ++k) {
+            const int i = (int)threadIdx.x + k * (int)blockDim.x;
+            if (i < S * TF) {
+                unsigned long long* const w = lds + (i >> kLogTF) * 2 * TF + (i & (TF - 1));
+                w[0] = (unsigned long long)ag[k];
+                w[TF] = (unsigned long long)ah[k];
+            }
         }
     }
     if (SKIP) add_item_totals(tg, th, fix);
     __syncthreads();
     unsigned long long* const out = (it.dest == kDestPartial ? partial : hist) +
                                     ((int64_t)it.out_slot * n_features + f0) * (int64_t)S * 2;
-    lds_finish_il<SKIP, TF>(lds, nf, S, lc, out, it.dest == kDestAtomic, rot + f0, fix);
+    lds_finish_il<SKIP, TF>(lds, nf, S, kPack ? 0 : lc, out, it.dest == kDestAtomic, rot + f0, fix);
 }
 
 // Level fills read their rows through the row index.  Each thread takes

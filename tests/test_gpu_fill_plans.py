@@ -151,6 +151,77 @@ def test_root_fill_interleaved(hgb, torch, monkeypatch, capfd, case, tile, copie
     assert plans == [(copies, tile, 1)], plans
 
 
+def root_plans_acc(err):
+    """(acc, copies, tile, il) of each root fill plan printed to stderr."""
+    out = []
+    for line in err.splitlines():
+        m = re.search(r"\[hgb\] fill kind 0 acc (\d+) copies (\d+) tile (\d+) lt \d+ ra \d+ il (\d)", line)
+        if m:
+            out.append(tuple(int(x) for x in m.groups()))
+    return out
+
+
+R_U8_256M = ("root u8, 255 bins + missing", lambda: synth.random_small(316, 50_000, 20, 255, True, 0))
+
+PACKED_ROOT_CASES = [
+    # workload, copies
+    (R_U8_28, 2), (R_U8_28, 4), (R_U8_70, 2), (R_U8_70, 4), (R_U8_256M, 2), (R_U8_256M, 4),
+]
+
+
+@pytest.mark.parametrize("bits", [19, 12])
+@pytest.mark.parametrize("case,copies", PACKED_ROOT_CASES,
+                         ids=lambda v: v[0] if isinstance(v, tuple) else str(v))
+def test_root_fill_interleaved_packed(hgb, torch, monkeypatch, capfd, case, copies, bits):
+    """The root's interleaved tile with packed sums (one add per cell, drained
+    into registers): 16 positions with 2 or 4 copies, a partial last tile,
+    rows in whole groups of four and ragged (one row at a time), and all 256
+    slots of one-byte bins (the missing slot included), against the oracle."""
+    name, make = case
+    say("root interleaved packed", name, "copies", copies, "bits", bits)
+    lc = copies.bit_length() - 1
+    monkeypatch.setenv("HGB_FILL_TUNE", f"root_il=1,root_tile=16,root_lc={lc}")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    run_root_both(hgb, torch, make(), bits=bits)
+    plans = root_plans_acc(capfd.readouterr().err)
+    assert plans == [(1, copies, 16, 1)], plans
+
+
+def saturated_root(sign):
+    """3,145,728 rows x 16 features where every row's |g| and h quantize to
+    exactly 2^19 at P = 19 (fp32 1 - 2^-24: e = 0, k = 19, rint rounds up),
+    and the rows come in runs of 12,288 -- one root item, three steps of the
+    fill -- that share one bin in every feature (18 bins, so no slot holds a
+    sixteenth of the rows and no slot is skipped).  Each copy-slot then takes
+    the most rows the drain period allows at the largest codes."""
+    n, F, run = 3_145_728, 16, 12_288
+    r = np.arange(n)
+    bins = np.stack([((r // run) + f) % 18 for f in range(F)]).astype(np.uint8)
+    v = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    g = np.full(n, sign * v, dtype=np.float32)
+    h = np.full(n, v, dtype=np.float32)
+    return synth.Workload("saturated", bins, 18, False, g, h, kind="root")
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("copies", [2, 4])
+def test_root_fill_interleaved_packed_drain_bound(hgb, torch, monkeypatch, capfd, sign, copies):
+    say("root interleaved packed, drain bound", sign, copies)
+    import oracle
+    w = saturated_root(sign)
+    qg, _ = oracle.quantize(w.grad, False, 19)
+    qh, _ = oracle.quantize(w.hess, True, 19)
+    assert (np.abs(qg) == 2 ** 19).all() and (qh == 2 ** 19).all()
+    lc = copies.bit_length() - 1
+    monkeypatch.setenv("HGB_FILL_TUNE", f"root_il=1,root_tile=16,root_lc={lc}")
+    monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
+    run_root_both(hgb, torch, w, bits=19)
+    err = capfd.readouterr().err
+    assert root_plans_acc(err) == [(1, copies, 16, 1)], err[-2000:]
+    chunks = re.findall(r"\[hgb\] fill kind 0 .* chunk (\d+) ", err)
+    assert chunks == ["12288"], chunks
+
+
 @pytest.mark.parametrize("plan_host", ["0", "1"])
 def test_plan_staging_modes(hgb, torch, monkeypatch, plan_host):
     """Launch plans read in place from pinned host memory (the default) or
