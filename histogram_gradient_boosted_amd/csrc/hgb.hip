@@ -450,6 +450,13 @@ double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, double 
     return std::max(lds, mem) + 0.25 * std::min(lds, mem) + valu;
 }
 
+// Threads of a k_split_reduce block: a node with many feature entries (a wide
+// matrix) takes 1,024, so each thread walks a few of them.
+unsigned split_reduce_threads(int n_entries)
+{
+    return n_entries >= 4096 ? (unsigned)kSplitReduceMaxThreads : 256u;
+}
+
 FillPlan plan_rows(const hgb_ctx* c)
 {
     FillPlan p{};
@@ -1738,7 +1745,7 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
 #undef HGB_SPLIT
 #undef HGB_SPLIT_SLICED
     HGB_LAUNCHED(c, "k_split_feature");
-    k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries,
+    k_split_reduce<<<(unsigned)n_nodes, split_reduce_threads(n_entries), 0, c->stream>>>(c->best, c->totals, n_entries,
                                                              (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");
     return HGB_OK;
@@ -1867,7 +1874,7 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
 #undef HGB_SUBSPLIT
 #undef HGB_SUBSPLIT_SLICED
         HGB_LAUNCHED(c, "k_subtract_split");
-        k_split_reduce<<<(unsigned)n_nodes, 256, 0, c->stream>>>(c->best, c->totals, n_entries, (SplitOut*)out);
+        k_split_reduce<<<(unsigned)n_nodes, split_reduce_threads(n_entries), 0, c->stream>>>(c->best, c->totals, n_entries, (SplitOut*)out);
         HGB_LAUNCHED(c, "k_split_reduce");
     }
     return s.release();

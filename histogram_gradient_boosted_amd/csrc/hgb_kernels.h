@@ -2269,24 +2269,36 @@ struct SplitOut {
     long long g_left, h_left, g_total, h_total;
 };
 
-// One block per node: the best feature, scanning features in order per thread
-// and then reducing across threads with the same (gain, feature) order.
-__global__ __launch_bounds__(256) void k_split_reduce(const FeatureBest* __restrict__ best,
-                                                      const long long* __restrict__ totals,
-                                                      int n_entries, SplitOut* __restrict__ out)
+// One block per node (256 or 1024 threads, a power of two): the best feature,
+// scanning features in order per thread -- four entries loaded before any is
+// compared -- and then reducing across threads with the same (gain, feature)
+// order.
+constexpr int kSplitReduceMaxThreads = 1024;
+__global__ __launch_bounds__(kSplitReduceMaxThreads) void k_split_reduce(
+    const FeatureBest* __restrict__ best, const long long* __restrict__ totals, int n_entries,
+    SplitOut* __restrict__ out)
 {
-    __shared__ double s_gain[256];
-    __shared__ int s_feat[256];
-    __shared__ int s_entry[256];
+    __shared__ double s_gain[kSplitReduceMaxThreads];
+    __shared__ int s_feat[kSplitReduceMaxThreads];
+    __shared__ int s_entry[kSplitReduceMaxThreads];
     const int node = blockIdx.x;
     const FeatureBest* nb = best + (int64_t)node * n_entries;
     double bg = 0.0;
     int bf = -1, be = -1;
-    for (int e = threadIdx.x; e < n_entries; e += blockDim.x) {   // entries in feature order
-        const FeatureBest c = nb[e];
-        if (c.code < 0) continue;
+    auto take = [&](const FeatureBest& c, int e) {
+        if (c.code < 0) return;
         if (bf < 0 || c.gain > bg) { bg = c.gain; bf = c.feature; be = e; }
+    };
+    const int bd = (int)blockDim.x;
+    int e = threadIdx.x;   // entries in feature order
+    for (; e + 3 * bd < n_entries; e += 4 * bd) {
+        FeatureBest c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c[u] = nb[e + u * bd];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) take(c[u], e + u * bd);
     }
+    for (; e < n_entries; e += bd) take(nb[e], e);
     s_gain[threadIdx.x] = bg;
     s_feat[threadIdx.x] = bf;
     s_entry[threadIdx.x] = be;

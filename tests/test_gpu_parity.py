@@ -224,6 +224,24 @@ def test_split_feature_counts(hgb, torch, F, B, missing, fused):
     run_level_both(hgb, torch, w, check_exact_gain=True, fused=fused)
 
 
+@pytest.mark.parametrize("n_const", [0, 16_000])
+def test_split_reduce_wide_ties(hgb, torch, n_const):
+    """16,400 identical features, so the root's per-feature winners all tie
+    on gain and the node's reduction runs 1,024 threads with several entries
+    each: the smallest feature wins.  With the first n_const features made
+    constant (no valid split) the first of the others wins."""
+    say("split reduce ties", n_const)
+    rng = np.random.default_rng(77)
+    n, F = 2048, 16_400
+    col = rng.integers(0, 256, n).astype(np.uint8)
+    bins = np.tile(col, (F, 1))
+    bins[:n_const] = 7
+    g = rng.standard_normal(n).astype(np.float32)
+    h = rng.uniform(0.1, 1.0, n).astype(np.float32)
+    sp = run_root_both(hgb, torch, synth.Workload("ties", bins, 256, False, g, h, kind="root"))
+    assert int(sp["feature"][0]) == n_const
+
+
 def test_c1_full(hgb, torch):
     say("c1 full")
     run_root_both(hgb, torch, synth.make("c1"))
