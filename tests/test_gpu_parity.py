@@ -259,12 +259,14 @@ def test_c5(hgb, torch, n, F):
     run_level_both(hgb, torch, synth.make("c5", n_rows=n, n_features=F), check_exact_gain=True)
 
 
-@pytest.mark.parametrize("n,F", [(8_192, 2_048), (None, None)])
-def test_c4(hgb, torch, n, F):
-    say("c4", n, F)
+@pytest.mark.parametrize("n,F,bits", [(8_192, 2_048, 30), (None, None, 30), (None, None, 19)])
+def test_c4(hgb, torch, n, F, bits):
+    """131,072 x 16,384 (and a slice of it): the root and the level of 8
+    nodes; at P = 19 the root takes the packed interleaved tile."""
+    say("c4", n, F, bits)
     w = synth.make("c4", n_rows=n, n_features=F)
-    run_root_both(hgb, torch, w)
-    run_level_both(hgb, torch, w, check_exact_gain=True)
+    run_root_both(hgb, torch, w, bits=bits)
+    run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
 
 
 @pytest.mark.parametrize("missing,bits", [(True, 30), (False, 19)])
