@@ -127,11 +127,31 @@ R_U16_1025 = ("root u16, 1,025 slots", lambda: synth.random_small(313, 12_000, 9
 R_HOT_U8 = ("root u8 hot slots", lambda: with_hot_slots(synth.random_small(314, 40_000, 6, 16, True, 0), 5))
 R_HOT_U16 = ("root u16 hot slots", lambda: with_hot_slots(synth.random_small(315, 30_001, 5, 1024, True, 0, u16=True), 6))
 
+# (a handful of rows puts at least 1/16 of them in some slot: these two run
+# with the skipped slot)
+R_TINY3 = ("root u8, 3 rows", lambda: synth.random_small(318, 3, 20, 255, True, 0))
+R_TINY7 = ("root u8, 7 rows", lambda: synth.random_small(319, 7, 33, 200, False, 0))
+
+
+def distinct_rows(seed, n, F):
+    """n <= 256 rows whose bins are distinct within every feature, so no slot
+    holds 1/16 of the rows (n >= 17) and no slot is skipped."""
+    rng = np.random.default_rng(seed)
+    bins = np.stack([rng.permutation(256)[:n] for _ in range(F)]).astype(np.uint8)
+    g = rng.standard_normal(n).astype(np.float32)
+    h = rng.uniform(0.1, 1.0, n).astype(np.float32)
+    return synth.Workload(f"distinct{n}", bins, 256, False, g, h, kind="root")
+
+
+R_FEW19 = ("root u8, 19 rows", lambda: distinct_rows(320, 19, 20))
+R_FEW20 = ("root u8, 20 rows", lambda: distinct_rows(321, 20, 37))
+
 ROOT_CASES = [
     # workload, tile (feature positions), copies
     (R_U8_28, 32, 1), (R_U8_28, 16, 2), (R_U8_28, 8, 4), (R_U8_70, 32, 1), (R_U8_70, 16, 1),
     (R_U8_70, 8, 2), (R_U16, 16, 1), (R_U16, 8, 2), (R_U16_1025, 8, 1), (R_HOT_U8, 16, 2),
-    (R_HOT_U8, 8, 1), (R_HOT_U16, 8, 1),
+    (R_HOT_U8, 8, 1), (R_HOT_U16, 8, 1), (R_TINY3, 16, 2), (R_TINY7, 8, 4), (R_FEW19, 32, 1),
+    (R_FEW20, 16, 1),
 ]
 
 
@@ -139,8 +159,9 @@ ROOT_CASES = [
 @pytest.mark.parametrize("case,tile,copies", ROOT_CASES, ids=lambda v: v[0] if isinstance(v, tuple) else str(v))
 def test_root_fill_interleaved(hgb, torch, monkeypatch, capfd, case, tile, copies, bits):
     """The root's interleaved tile: full and partial tiles, rows in whole
-    groups of four and ragged (one row at a time), copies, 2-byte bins and
-    the skipped slot, against the oracle's root histogram and split."""
+    groups of four and ragged (one row at a time), items of a few rows (3, 7,
+    19, 20), copies, 2-byte bins and the skipped slot, against the oracle's
+    root histogram and split."""
     name, make = case
     say("root interleaved", name, "tile", tile, "copies", copies, "bits", bits)
     lc = copies.bit_length() - 1
@@ -166,6 +187,7 @@ R_U8_256M = ("root u8, 255 bins + missing", lambda: synth.random_small(316, 50_0
 PACKED_ROOT_CASES = [
     # workload, copies
     (R_U8_28, 2), (R_U8_28, 4), (R_U8_70, 2), (R_U8_70, 4), (R_U8_256M, 2), (R_U8_256M, 4),
+    (R_FEW19, 2), (R_FEW20, 4),
 ]
 
 
@@ -175,8 +197,9 @@ PACKED_ROOT_CASES = [
 def test_root_fill_interleaved_packed(hgb, torch, monkeypatch, capfd, case, copies, bits):
     """The root's interleaved tile with packed sums (one add per cell, drained
     into registers): 16 positions with 2 or 4 copies, a partial last tile,
-    rows in whole groups of four and ragged (one row at a time), and all 256
-    slots of one-byte bins (the missing slot included), against the oracle."""
+    rows in whole groups of four and ragged (one row at a time), items of 19
+    and 20 rows, and all 256 slots of one-byte bins (the missing slot
+    included), against the oracle."""
     name, make = case
     say("root interleaved packed", name, "copies", copies, "bits", bits)
     lc = copies.bit_length() - 1
