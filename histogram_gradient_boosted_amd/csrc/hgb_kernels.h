@@ -1021,6 +1021,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
     static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
     constexpr bool kPack = ACC == kPacked;
+    static_assert(!kPack || TF == 16, "packed sums: 16 positions, whose 256 slots the register cells cover");
     constexpr int RA = kPack ? kRootIlPackedCells : 1;
     extern __shared__ unsigned long long lds[];
     const int item = xcd_item(blockIdx.x, n_items);
@@ -1044,8 +1045,9 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     for (int k = 0; k < RA; ++k) ag[k] = ah[k] = 0;
     // Each thread takes its cells' words of every copy, so between the two
     // barriers every word has one reader.  A wave's 64 cells span four slots
-    // of 16 positions; starting each slot at copy (slot mod C) spreads the
-    // lanes over the bank pairs.
+    // of the 16 positions; starting each slot at copy (slot mod C) spreads
+    // the lanes over the bank pairs.  (The host keeps S * 16 within the
+    // block's 1024 x RA cells.)
     auto drain_cells = [&]() {
         __syncthreads();
         const int C = 1 << lc;
