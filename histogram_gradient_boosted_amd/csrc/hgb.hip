@@ -134,9 +134,9 @@ struct hgb_ctx {
     // HGB_FILL_TUNE="key=value,..." overrides the fill planner (developer
     // tuning): root_lc, root_tile, root_ipc, level_lc, level_tile, level_ipc
     // (ipc = items per CU), align (rows an item boundary is a multiple of),
-    // piece (fixed cost of a level item, in rows), il and root_il (row-major
-    // level and root fills, wide sums: 1 slot-major interleaved tile, 0
-    // feature-major); -1 keeps the planner's choice.
+    // piece (fixed cost of a level item, in rows), il (row-major level fill,
+    // wide sums) and root_il (root fill, wide or packed sums): 1 slot-major
+    // interleaved tile, 0 feature-major; -1 keeps the planner's choice.
     int tune[10] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
