@@ -114,3 +114,18 @@ def test_precision_bits(bits):
 def test_precision_out_of_range(bits):
     with pytest.raises(oracle.OracleError):
         oracle.quantize(np.ones(3, dtype=np.float32), require_nonneg=True, bits=bits)
+
+
+@pytest.mark.parametrize("bits,expect", [(19, 2 ** 19), (23, 2 ** 23), (24, 2 ** 24 - 1), (30, 2 ** 30 - 64)])
+def test_largest_code_reaches_two_to_the_p(bits, expect):
+    """M = 1 - 2^-24 (the fp32 value below 1) has e = 0, so k = P and
+    M * 2^P = 2^P - 2^(P - 24): below P = 24 that is within half a step of
+    2^P and rounds up to it (the bound |q| <= 2^P is reached, which the
+    packed sums' drain period allows for); from P = 24 on it is an integer."""
+    m = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    assert float(m) == 1 - 2.0 ** -24
+    for sign, nonneg in ((1, False), (-1, False), (1, True)):
+        q, k = oracle.quantize(np.array([sign * m, 0.25 * sign * m], dtype=np.float32), require_nonneg=nonneg,
+                               bits=bits)
+        assert k == bits
+        assert q[0] == sign * expect
