@@ -57,6 +57,9 @@ class Plan:
         self.cells = 0            # built rows x features per step
         self.all_cells = 0        # rows x features of every node of every level (built or derived)
         self.fill_bytes = 0       # algorithmic bytes of the build kernels per step
+        self.root_bytes = 0       # ... of the root's fill
+        self.level_bytes = 0      # ... of the fills below the root
+        self.root_rows = 0        # rows of the root build per step
         self.level_notes = []
 
 
@@ -101,7 +104,13 @@ def prepare(ctx, w, g, h, torch):
             plan.cells += lp.built_rows * w.n_features
             level_rows = w.n_rows if lp.depth == 0 else int(lp.children_offsets[-1])
             plan.all_cells += level_rows * w.n_features
-            plan.fill_bytes += fill_alg_bytes(w, lp.built_rows, nb, lp.depth == 0)
+            b = fill_alg_bytes(w, lp.built_rows, nb, lp.depth == 0)
+            plan.fill_bytes += b
+            if lp.depth == 0:
+                plan.root_bytes += b
+                plan.root_rows += lp.built_rows
+            else:
+                plan.level_bytes += b
             plan.level_notes.append({"depth": lp.depth, "nodes": lp.n_nodes, "built_rows": lp.built_rows})
         return plan
     plan.tree = None
@@ -112,7 +121,10 @@ def prepare(ctx, w, g, h, torch):
         plan.levels.append(("root", rp, None))
         plan.cells += w.n_rows * w.n_features
         plan.all_cells += w.n_rows * w.n_features
-        plan.fill_bytes += fill_alg_bytes(w, w.n_rows, 1, True)
+        b = fill_alg_bytes(w, w.n_rows, 1, True)
+        plan.fill_bytes += b
+        plan.root_bytes += b
+        plan.root_rows += w.n_rows
         plan.level_notes.append({"depth": 0, "nodes": 1, "built_rows": w.n_rows})
     if w.kind in ("level", "root+level"):
         L = w.level
@@ -124,7 +136,9 @@ def prepare(ctx, w, g, h, torch):
         plan.levels.append(("level", lp, parents))
         plan.cells += lp.built_rows * w.n_features
         plan.all_cells += int(L.children_offsets[-1]) * w.n_features
-        plan.fill_bytes += fill_alg_bytes(w, lp.built_rows, lp.n_pairs, False)
+        b = fill_alg_bytes(w, lp.built_rows, lp.n_pairs, False)
+        plan.fill_bytes += b
+        plan.level_bytes += b
         plan.level_notes.append({"nodes": lp.n_nodes, "built_rows": lp.built_rows})
     ctx.sync()
     return plan
@@ -274,7 +288,8 @@ def lds_rates(device: int = 0):
     n_cu = ctypes.c_int(0)
     for name, kind, copies in (("u64_random_bins_1_copy", 0, 1), ("u64_random_bins_2_copies", 0, 2),
                                ("u64_random_bins_16_copies", 0, 16), ("u64_conflict_free", 1, 1),
-                               ("u64_interleaved_tile_fill_shape", 3, 1)):
+                               ("u64_interleaved_tile_fill_shape", 3, 1), ("u32_conflict_free", 4, 1),
+                               ("u32_random_bins_16_copies", 2, 16)):
         r = ctypes.c_double(0.0)
         if fn(device, kind, copies, ctypes.byref(r), ctypes.byref(n_cu)) != 0:
             return None
@@ -283,13 +298,12 @@ def lds_rates(device: int = 0):
     return out
 
 
-def traffic_record(config: str, precision: int, mode: str = ""):
-    """HBM traffic of the fill class measured with rocprofv3 counters
-    (FETCH_SIZE, WRITE_SIZE, calibrated against a copy of known size) by
-    bench_counters.py, per step; None when no record exists for this workload
+def counters_record(config: str, precision: int, mode: str = ""):
+    """The rocprofv3 counter record bench_counters.py wrote for this workload
     and step (mode "" is the replayed depthwise tree that bench_counters.py
-    drives; grown and oblivious trees have no record) or the kernel sources
-    changed since it was taken."""
+    drives; grown and oblivious trees have no record): HBM traffic per kernel
+    (FETCH_SIZE, WRITE_SIZE, calibrated against a copy of known size).  None
+    when there is no record or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"counters_{config}{mode}_p{precision}.json")
     if not os.path.exists(path):
         return None
@@ -299,9 +313,231 @@ def traffic_record(config: str, precision: int, mode: str = ""):
             rec = json.load(f)
         if rec.get("source_hash") != bench_counters.source_hash():
             return None
-        return int(rec["fill_traffic"]["bytes_per_step"])
+        return rec
     except Exception:
         return None
+
+
+def dominant_roofline(prof, plan, steps: int, counters):
+    """The roofline of the step's dominant build kernel: the level fill
+    (k_fill_rows / k_fill_cols, every level below the root) or the root fill
+    (k_fill_root / k_fill_root_il), whichever takes longer, each timed by the
+    library's events around its own launches.  achieved = its algorithmic bytes
+    per launch / its average launch duration."""
+    parts = {"fill_level": ("k_fill_rows / k_fill_cols (levels below the root)", plan.level_bytes),
+             "fill_root": ("k_fill_root / k_fill_root_il (the root)", plan.root_bytes)}
+    name = max(parts, key=lambda k: prof[k][0])
+    ms, launches = prof[name]
+    if launches == 0 or ms <= 0:
+        return None
+    kernel, alg_bytes = parts[name]
+    per_launch_bytes = alg_bytes / (launches / steps)
+    avg_s = ms * 1e-3 / launches
+    achieved = per_launch_bytes / avg_s / 1e9
+    traffic = None
+    if counters is not None:
+        kk = counters.get("kernels", {})
+        names = ("k_fill_rows", "k_fill_cols") if name == "fill_level" else ("k_fill_root", "k_fill_root_il")
+        tb = sum(int(kk[k]["fetch_bytes"]) + int(kk[k]["write_bytes"]) for k in names if k in kk)
+        dispatches = sum(int(kk[k]["dispatches"]) for k in names if k in kk)
+        if dispatches:
+            traffic = int(round(tb / dispatches))
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (fetch + write, calibrated counters)",
+            "alg_bytes_per_launch": int(round(per_launch_bytes)),
+            "launches_per_step": launches // steps, "avg_launch_us": round(avg_s * 1e6, 3)}
+
+
+def measure(config: str, precision: int, steps: int, warmup: int, seed: int, objective_arg: str,
+            grow: bool, oblivious: bool, flush_mib: int, cpu: bool, cpu_min_s: float = 10.0):
+    """Set up one workload, time `steps` steps after `warmup`, and return its
+    record (value, ms per step, the rooflines, optionally the oracle's rate)."""
+    import torch
+    from histogram_gradient_boosted_amd import binding, synth
+
+    t0 = time.time()
+    w = synth.make(config, seed=seed)
+    log(f"[bench] workload {config}: {w.n_rows} x {w.n_features}, generated in {time.time() - t0:.1f}s")
+    ctx = binding.Context(0)
+    ctx.set_precision(precision)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    objective = resolve_objective(w, objective_arg)
+    if objective is None:
+        print(f"--objective {objective_arg} needs a workload with scores and labels (c3)", file=sys.stderr)
+        sys.exit(2)
+    g, h = step_inputs(w, objective, torch)
+    plan = prepare(ctx, w, g, h, torch)
+    if grow or oblivious:
+        if plan.tree is None:
+            print("--grow / --oblivious need a tree workload (c3)", file=sys.stderr)
+            sys.exit(2)
+        plan.grow = True
+    if oblivious:
+        # the oblivious tree differs from the planned depthwise one: count its
+        # built cells from one untimed growth
+        from histogram_gradient_boosted_amd import tree
+        plan.oblivious = True
+        levels = tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        plan.cells = sum(lv.built_rows for lv in levels) * w.n_features
+        plan.all_cells = sum(w.n_rows if lv.depth == 0 else int(lv.offsets[-1]) for lv in levels) * w.n_features
+        plan.root_rows = sum(lv.built_rows for lv in levels if lv.depth == 0)
+        plan.root_bytes = sum(fill_alg_bytes(w, lv.built_rows, 1, True) for lv in levels if lv.depth == 0)
+        plan.level_bytes = sum(fill_alg_bytes(w, lv.built_rows, lv.n_nodes // 2, False)
+                               for lv in levels if lv.depth > 0)
+        plan.fill_bytes = plan.root_bytes + plan.level_bytes
+        plan.level_notes = [{"depth": lv.depth, "nodes": lv.n_nodes, "built_rows": lv.built_rows}
+                            for lv in levels]
+        del levels
+    log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
+
+    # The set-up made millions of Python objects (torch's own, the workload);
+    # a full collection of them in the middle of the timed steps stalls the
+    # host for tens of milliseconds.  Freeze them out of the collector.
+    gc.collect()
+    gc.freeze()
+    for _ in range(warmup):
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+
+    # The timed steps, back to back (no per-kernel events).  An event pair on
+    # the library's stream (torch's current stream) brackets each step, for the
+    # median and spread beside the mean.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    marks[0].record()
+    for i in range(steps):
+        step(ctx, w, plan, g, h)
+        marks[i + 1].record()
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+
+    # The same steps again with the library's per-kernel events (recorded on
+    # its own stream around each kernel class), for the breakdown and the fill
+    # kernels' duration.  Before each of these steps a scratch buffer larger
+    # than the 256 MB Infinity Cache is written, so the kernels start without
+    # the previous step's data in that cache (the write is not a library
+    # kernel, so no event brackets it).
+    flush = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda") if flush_mib else None
+    ctx.profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1.0)
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall_prof = time.perf_counter() - t1
+    del flush
+    prof = {k: ctx.profile_query(k) for k in binding.KERNELS}
+    ctx.profile_enable(False)
+
+    ms_per_step = wall * 1e3 / steps
+    value = plan.cells * steps / wall / 1e9
+    fill_ms, fill_launches = prof["fill"]
+    fill_ms_step = fill_ms / steps
+    achieved = plan.fill_bytes / (fill_ms_step * 1e-3) / 1e9 if fill_ms_step > 0 else 0.0
+    breakdown = {k: round(v[0] / steps, 4) for k, v in prof.items()}
+    log(f"[bench] per-step device ms by kernel class: {breakdown}; launches {{{', '.join(f'{k}: {v[1] // steps}' for k, v in prof.items())}}}")
+    log(f"[bench] wall ms/step {ms_per_step:.3f} (timed, events off; median {np.median(per_step):.3f}), "
+        f"{wall_prof * 1e3 / steps:.3f} (events on)")
+
+    counters = counters_record(config, precision,
+                               "_oblivious" if oblivious else "_grow" if grow else "")
+    traffic = int(counters["fill_traffic"]["bytes_per_step"]) if counters else None
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "G cell-updates/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        # per-step spans from an event pair around each timed step
+        "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
+                              "min": round(float(per_step.min()), 4),
+                              "p10": round(float(np.percentile(per_step, 10)), 4),
+                              "p90": round(float(np.percentile(per_step, 90)), 4),
+                              "max": round(float(per_step.max()), 4),
+                              "mean": round(float(per_step.mean()), 4)},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[config], "name": config,
+                   "rows": w.n_rows, "features": w.n_features, "bins": w.n_bins,
+                   "built_cells_per_step": plan.cells, "levels": plan.level_notes},
+        # every node's histogram per second, the derived siblings included
+        # (what the subtraction buys: cells that were never added)
+        "effective_gcells_per_s": round(plan.all_cells * steps / wall / 1e9, 3),
+        "build_only_gcells_per_s": round(plan.cells / (fill_ms_step + breakdown["gather"] + breakdown["zero"]) / 1e6, 3)
+        if fill_ms_step > 0 else None,
+        "ms_per_step_events_on": round(wall_prof * 1e3 / steps, 4),
+        "event_pass": f"per-kernel events, {flush_mib} MiB written before each step"
+        if flush_mib else "per-kernel events",
+        "kernel_ms_per_step": breakdown,
+        "roofline": dominant_roofline(prof, plan, steps, counters),
+        # the whole build class (every fill launch and the merges), the unit the
+        # level build's bandwidth target speaks of
+        "fill_class_roofline": {"bound": "hbm", "kernel": FILL_KERNELS, "achieved": round(achieved, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                "traffic": traffic,
+                                "traffic_unit": "HBM bytes per step (fetch + write, calibrated counters)",
+                                # the bytes the fill class actually moves, per second of its time
+                                "traffic_gbs": round(traffic / (fill_ms_step * 1e-3) / 1e9, 1)
+                                if traffic and fill_ms_step > 0 else None,
+                                "alg_bytes_per_step": plan.fill_bytes,
+                                "launches_per_step": fill_launches // max(steps, 1),
+                                "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
+        "precision_bits": precision,
+        "gradients": "device objective: " + objective + " loss from resident scores and labels"
+        if objective != "none" else "resident fp32 (g, h) arrays",
+        "step": "oblivious: partition + build + subtract + level split per level, on the device"
+        if oblivious else
+        "grow: partition + build + subtract + split per level, on the device" if grow
+        else "replay: build + subtract + split per level on fixed row lists",
+    }
+    ctx.close()
+    # the LDS ceiling: each fill's atomic adds per step (two per cell in wide
+    # mode, P > 19; one in packed mode) against the microbenchmark's rates
+    rates = lds_rates(0)
+    per_cell = 2 if precision > 19 else 1
+    if rates:
+        def lds(cells, ms):
+            a = cells * per_cell / (ms * 1e-3) if ms > 0 else 0.0
+            return {"atomics_per_step": cells * per_cell, "achieved": round(a / 1e9, 1),
+                    "frac": round(a / rates["u64_conflict_free"], 4)}
+        root_cells = plan.root_rows * w.n_features
+        result["lds_roofline"] = {
+            "kernel": FILL_KERNELS, "unit": "u64 LDS atomic adds (lane-ops)/s",
+            **lds(plan.cells, fill_ms_step),
+            "peak": round(rates["u64_conflict_free"] / 1e9, 1),
+            "peak_kind": "measured: conflict-free u64 LDS atomic adds, whole chip (csrc/lds_rate.hip)",
+            "root_fill": lds(root_cells, breakdown["fill_root"]) if root_cells else None,
+            "level_fill": lds(plan.cells - root_cells, breakdown["fill_level"]) if plan.cells > root_cells else None,
+            "random_bins": {k: round(v / 1e9, 1) for k, v in rates.items() if k.startswith("u64_random")},
+            # the fills' own pattern and launch shape: two lanes per bank pair,
+            # 16 waves per CU (the ceiling a 1024-thread fill block can reach)
+            "interleaved_tile_fill_shape": round(rates["u64_interleaved_tile_fill_shape"] / 1e9, 1),
+            # u32 adds, for a cell split into 32-bit halves (four adds instead of two)
+            "u32": {k: round(rates[k] / 1e9, 1) for k in ("u32_conflict_free", "u32_random_bins_16_copies")},
+            "scale": "G lane-ops/s", "n_cu": rates["n_cu"]}
+        log(f"[bench] LDS atomics {plan.cells * per_cell / (fill_ms_step * 1e-3) / 1e9:.0f} G/s in the fill; "
+            f"microbenchmark { {k: round(v / 1e9) for k, v in rates.items() if k != 'n_cu'} } G/s")
+    if cpu:
+        log(f"[bench] timing the oracle on the host ({config}) ...")
+        result["cpu_baseline"] = cpu_baseline(w, objective, min_s=cpu_min_s)
+    del w, plan, g, h
+    gc.unfreeze()
+    gc.collect()
+    torch.cuda.empty_cache()
+    return result
 
 
 def main():
@@ -313,6 +549,9 @@ def main():
                          "first few dozen trees run slower while the allocator and the device warm up)")
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the second measured workload (the wide 131,072 x 16,384 case, "
+                         "measured after the default one in the same process)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--grow", action="store_true",
                     help="tree workloads: grow the tree each step with the device partition "
@@ -339,162 +578,24 @@ def main():
         sys.exit(2)
 
     import torch
-    from histogram_gradient_boosted_amd import binding, synth
+    from histogram_gradient_boosted_amd import binding
 
     if not torch.cuda.is_available() or not binding.available():
         print("no HIP device available", file=sys.stderr)
         sys.exit(1)
-
-    t0 = time.time()
-    w = synth.make(args.config, seed=args.seed)
-    log(f"[bench] workload {args.config}: {w.n_rows} x {w.n_features}, generated in {time.time() - t0:.1f}s")
     torch.cuda.set_device(0)
-    ctx = binding.Context(0)
-    ctx.set_precision(args.precision)
-    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
-    objective = resolve_objective(w, args.objective)
-    if objective is None:
-        print(f"--objective {args.objective} needs a workload with scores and labels (c3)", file=sys.stderr)
-        sys.exit(2)
-    g, h = step_inputs(w, objective, torch)
-    plan = prepare(ctx, w, g, h, torch)
-    if args.grow or args.oblivious:
-        if plan.tree is None:
-            print("--grow / --oblivious need a tree workload (c3)", file=sys.stderr)
-            sys.exit(2)
-        plan.grow = True
-    if args.oblivious:
-        # the oblivious tree differs from the planned depthwise one: count its
-        # built cells from one untimed growth
-        from histogram_gradient_boosted_amd import tree
-        plan.oblivious = True
-        levels = tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
-        plan.cells = sum(lv.built_rows for lv in levels) * w.n_features
-        plan.all_cells = sum(w.n_rows if lv.depth == 0 else int(lv.offsets[-1]) for lv in levels) * w.n_features
-        plan.fill_bytes = sum(fill_alg_bytes(w, lv.built_rows, 1 if lv.depth == 0 else lv.n_nodes // 2,
-                                             lv.depth == 0) for lv in levels)
-        plan.level_notes = [{"depth": lv.depth, "nodes": lv.n_nodes, "built_rows": lv.built_rows}
-                            for lv in levels]
-        del levels
-    log(f"[bench] plan ready: {plan.cells} built cells per step, levels {plan.level_notes}")
-
-    # The set-up made millions of Python objects (torch's own, the workload);
-    # a full collection of them in the middle of the timed steps stalls the
-    # host for tens of milliseconds.  Freeze them out of the collector.
-    gc.collect()
-    gc.freeze()
-    for _ in range(args.warmup):
-        step(ctx, w, plan, g, h)
-    ctx.sync()
-    torch.cuda.synchronize()
-
-    # the timed steps (no per-kernel events)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step(ctx, w, plan, g, h)
-    ctx.sync()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-
-    # the same steps again with the library's per-kernel events (recorded on
-    # its own stream around each kernel class), for the breakdown and the
-    # fill kernels' duration.  Before each of these steps a scratch buffer
-    # larger than the 256 MB Infinity Cache is written, so the kernels start
-    # without the previous step's data in that cache (the write is not a
-    # library kernel, so no event brackets it).
-    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda") if args.flush_mib else None
-    ctx.profile_enable(True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        if flush is not None:
-            flush.fill_(1.0)
-        step(ctx, w, plan, g, h)
-    ctx.sync()
-    torch.cuda.synchronize()
-    wall_prof = time.perf_counter() - t1
-    del flush
-    prof = {k: ctx.profile_query(k) for k in binding.KERNELS}
-    ctx.profile_enable(False)
-
-    ms_per_step = wall * 1e3 / args.steps
-    value = plan.cells * args.steps / wall / 1e9
-    fill_ms, fill_launches = prof["fill"]
-    fill_ms_step = fill_ms / args.steps
-    achieved = plan.fill_bytes / (fill_ms_step * 1e-3) / 1e9 if fill_ms_step > 0 else 0.0
-    breakdown = {k: round(v[0] / args.steps, 4) for k, v in prof.items()}
-    log(f"[bench] per-step device ms by kernel class: {breakdown}; launches {{{', '.join(f'{k}: {v[1] // args.steps}' for k, v in prof.items())}}}")
-    log(f"[bench] wall ms/step {ms_per_step:.3f} (timed, events off), {wall_prof * 1e3 / args.steps:.3f} (events on)")
-
-    traffic = traffic_record(args.config, args.precision,
-                             "_oblivious" if args.oblivious else "_grow" if args.grow else "")
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "G cell-updates/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int64",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config,
-                   "rows": w.n_rows, "features": w.n_features, "bins": w.n_bins,
-                   "built_cells_per_step": plan.cells, "levels": plan.level_notes},
-        # every node's histogram per second, the derived siblings included
-        # (what the subtraction buys: cells that were never added)
-        "effective_gcells_per_s": round(plan.all_cells * args.steps / wall / 1e9, 3),
-        "build_only_gcells_per_s": round(plan.cells / (fill_ms_step + breakdown["gather"] + breakdown["zero"]) / 1e6, 3)
-        if fill_ms_step > 0 else None,
-        "ms_per_step_events_on": round(wall_prof * 1e3 / args.steps, 4),
-        "event_pass": f"per-kernel events, {args.flush_mib} MiB written before each step"
-        if args.flush_mib else "per-kernel events",
-        "kernel_ms_per_step": breakdown,
-        "roofline": {"bound": "hbm", "kernel": FILL_KERNELS, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "traffic_unit": "HBM bytes per step (fetch + write, calibrated counters)",
-                     # the bytes the fill class actually moves, per second of its time
-                     "traffic_gbs": round(traffic / (fill_ms_step * 1e-3) / 1e9, 1)
-                     if traffic and fill_ms_step > 0 else None,
-                     "alg_bytes_per_step": plan.fill_bytes,
-                     "launches_per_step": fill_launches // max(args.steps, 1),
-                     "avg_launch_us": round(fill_ms * 1e3 / max(fill_launches, 1), 3)},
-        "precision_bits": args.precision,
-        "gradients": "device objective: " + objective + " loss from resident scores and labels"
-        if objective != "none" else "resident fp32 (g, h) arrays",
-        "step": "oblivious: partition + build + subtract + level split per level, on the device"
-        if args.oblivious else
-        "grow: partition + build + subtract + split per level, on the device" if args.grow
-        else "replay: build + subtract + split per level on fixed row lists",
-    }
-    ctx.close()
-    # the LDS ceiling: the fill's atomic adds per step (two per cell in wide
-    # mode, P > 19; one in packed mode) against the microbenchmark's rates
-    rates = lds_rates(0)
-    atomics = plan.cells * (2 if args.precision > 19 else 1)
-    lds_achieved = atomics / (fill_ms_step * 1e-3) if fill_ms_step > 0 else 0.0
-    if rates:
-        result["lds_roofline"] = {
-            "kernel": FILL_KERNELS, "unit": "u64 LDS atomic adds (lane-ops)/s",
-            "atomics_per_step": atomics, "achieved": round(lds_achieved / 1e9, 1),
-            "peak": round(rates["u64_conflict_free"] / 1e9, 1),
-            "frac": round(lds_achieved / rates["u64_conflict_free"], 4),
-            "peak_kind": "measured: conflict-free u64 LDS atomic adds, whole chip (csrc/lds_rate.hip)",
-            "random_bins": {k: round(v / 1e9, 1) for k, v in rates.items() if k.startswith("u64_random")},
-            # the fills' own pattern and launch shape: two lanes per bank pair,
-            # 16 waves per CU (the ceiling a 1024-thread fill block can reach)
-            "interleaved_tile_fill_shape": round(rates["u64_interleaved_tile_fill_shape"] / 1e9, 1),
-            "scale": "G lane-ops/s", "n_cu": rates["n_cu"]}
-        log(f"[bench] LDS atomics {lds_achieved / 1e9:.0f} G/s in the fill; microbenchmark "
-            f"{ {k: round(v / 1e9) for k, v in rates.items() if k != 'n_cu'} } G/s")
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(w, objective)
+    result = measure(args.config, args.precision, args.steps, args.warmup, args.seed, args.objective,
+                     args.grow, args.oblivious, args.flush_mib, not args.no_cpu_baseline)
+    # The default run also measures the wide case (the other workload the
+    # bandwidth target names), in the same process after the headline one,
+    # with its own warm-up and a one-step oracle sample.
+    if (not args.no_targets and args.config == "c3" and not args.grow and not args.oblivious):
+        wide = measure("c4", args.precision, args.steps, 3, args.seed, "auto", False, False,
+                       args.flush_mib, not args.no_cpu_baseline, cpu_min_s=0.0)
+        keep = ("value", "unit", "ms_per_step", "ms_per_step_stats", "steps", "warmup", "config",
+                "kernel_ms_per_step", "roofline", "fill_class_roofline", "lds_roofline", "cpu_baseline",
+                "precision_bits", "effective_gcells_per_s")
+        result["targets"] = {"c4": {k: wide[k] for k in keep if k in wide}}
     print(json.dumps(result), flush=True)
 
 

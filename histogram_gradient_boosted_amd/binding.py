@@ -31,7 +31,8 @@ SPLIT_BYTES = 56
 
 EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb_sync",
             "hgb_upload_bins", "hgb_begin_tree", "hgb_get_scales", "hgb_build_level",
-            "hgb_subtract_siblings", "hgb_find_splits", "hgb_profile_enable",
+            "hgb_subtract_siblings", "hgb_subtract_siblings_slots", "hgb_find_splits",
+            "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
             "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized",
             "hgb_find_level_split")
@@ -40,7 +41,7 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
 OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
 
 KERNELS = {"quantize": 0, "gather": 1, "zero": 2, "fill": 3, "subtract": 4, "split": 5,
-           "partition": 6}
+           "partition": 6, "fill_root": 7, "fill_level": 8, "merge": 9}
 
 
 class HGBError(RuntimeError):
@@ -90,8 +91,10 @@ def load():
     lib.hgb_get_scales.restype = c_int
     lib.hgb_build_level.argtypes = [vp, vp, vp, i32, vp, vp]
     lib.hgb_build_level.restype = c_int
-    lib.hgb_subtract_siblings.argtypes = [vp, vp, vp, vp, vp, i32]
+    lib.hgb_subtract_siblings.argtypes = [vp, vp, vp, vp, i32]
     lib.hgb_subtract_siblings.restype = c_int
+    lib.hgb_subtract_siblings_slots.argtypes = [vp, vp, vp, vp, vp, i32]
+    lib.hgb_subtract_siblings_slots.restype = c_int
     lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_splits.restype = c_int
     lib.hgb_find_level_split.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
@@ -276,7 +279,8 @@ class Context:
             None if slots is None else slots.ctypes.data_as(ctypes.c_void_p)), "build_level")
 
     def subtract_siblings(self, parent, child, built_is_right, parent_slot=None):
-        """child[2i + 1 - r] = parent[parent_slot[i]] - child[2i + r], r = built_is_right[i]."""
+        """child[2i + 1 - r] = parent[parent_slot[i]] - child[2i + r], r = built_is_right[i]
+        (parent_slot None: parent[i], through the five-argument hgb_subtract_siblings)."""
         torch = self._torch
         bir = np.ascontiguousarray(np.asarray(built_is_right), dtype=np.uint8)
         P = int(bir.shape[0])
@@ -286,9 +290,13 @@ class Context:
         ptop = (int(ps.max()) + 1) if ps is not None and P else P
         pp = self._dev(parent, "parent", torch.int64, ptop * self.node_elems)
         cp = self._dev(child, "child", torch.int64, 2 * P * self.node_elems)
-        self._check(self._lib.hgb_subtract_siblings(
-            self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
-            None if ps is None else ps.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings")
+        if ps is None:   # the five-argument verb: pair i's parent at slot i
+            self._check(self._lib.hgb_subtract_siblings(
+                self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings")
+        else:
+            self._check(self._lib.hgb_subtract_siblings_slots(
+                self._h, pp, cp, bir.ctypes.data_as(ctypes.c_void_p),
+                ps.ctypes.data_as(ctypes.c_void_p), P), "subtract_siblings_slots")
 
     def subtract_find_splits(self, parent, child, built_is_right, lam: float, gamma: float, out,
                              parent_slot=None):

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -44,9 +45,8 @@ constexpr double kPieceRowsPerCell = 0.25;
 // A node split over more blocks than this is merged in several groups, added
 // into its zeroed slot with atomics.
 constexpr int kMergeGroup = 32;
-// Keep a row-major copy of the bins when a row takes at most this many bytes.
-// Rows up to this many bytes get a row-major copy (16,384 one-byte features included):
-// below the root, a level reads only its built rows' lines from it.
+// Rows up to this many bytes get a row-major copy (16,384 one-byte features
+// included): below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
 // begin_tree's max pass: at most this many blocks, each writing its pair of
@@ -265,16 +265,25 @@ struct StageLease {
     }
 };
 
-// Poll `ev` until the work before it is done.  A level loop waits for small
-// results (maxima, node records) several times per tree; a blocking wait
-// would add the host's wake-up latency to each of them.
+// Wait for `ev`: poll it for up to kPollMicros, then block.  A level loop
+// waits for small results (maxima, node records) several times per tree, most
+// of them ready within tens of microseconds, where a blocking wait would add
+// the host's wake-up latency; a longer wait (a large level still running)
+// blocks instead of holding a host core.
+constexpr int64_t kPollMicros = 200;
+
 hgb_status poll_event(hgb_ctx* c, hipEvent_t ev)
 {
+    const auto t0 = std::chrono::steady_clock::now();
     for (;;) {
         const hipError_t e = hipEventQuery(ev);
         if (e == hipSuccess) return HGB_OK;
         if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
+        const auto waited = std::chrono::steady_clock::now() - t0;
+        if (std::chrono::duration_cast<std::chrono::microseconds>(waited).count() >= kPollMicros) break;
     }
+    HGB_HIP(c, hipEventSynchronize(ev));
+    return HGB_OK;
 }
 
 // Record `*ev` (created on first use) on the stream and poll it.
@@ -819,8 +828,6 @@ hgb_status launch_fill(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
                             : launch_fill_acc<uint16_t, kWide, false>(c, p, a);
 }
 
-// Zero whole node slots of the level buffer.
-// Zero whole node slots of the level buffer; the slot list is on the device.
 // Sum partial histograms into their nodes' slots: the merge list inline in
 // the arguments when it is short, else read from its staged plan.
 hgb_status launch_merge(hgb_ctx* c, const std::vector<MergeEntry>& merges, const MergeEntry* staged,
@@ -838,6 +845,7 @@ hgb_status launch_merge(hgb_ctx* c, const std::vector<MergeEntry>& merges, const
     return HGB_OK;
 }
 
+// Zero whole node slots of the level buffer; the slot list is staged.
 hgb_status launch_zero(hgb_ctx* c, int64_t* hist, const int32_t* slots_dev, size_t n_slots)
 {
     if (n_slots == 0) return HGB_OK;
@@ -1063,10 +1071,13 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
         a.drain = std::max(plan.drain, 1);
         a.hist = hist;
         a.partial = (int64_t*)c->partial;
-        ProfScope ps(c, HGB_KERNEL_FILL);
-        st = launch_fill(c, plan, a);
+        {
+            ProfScope pl(c, HGB_KERNEL_FILL_LEVEL);
+            st = launch_fill(c, plan, a);
+        }
         if (st != HGB_OK) return st;
         if (!merges.empty()) {
+            ProfScope pm(c, HGB_KERNEL_MERGE);
             const int64_t node_vec = (int64_t)c->F * c->S;
             dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
             st = launch_merge(c, merges, (const MergeEntry*)(dev + off_merges), grid, hist);
@@ -1641,12 +1652,12 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
         a.drain = std::max(plan.drain, 1);
         a.hist = hist;
         a.partial = (int64_t*)c->partial;
-        ProfScope ps(c, HGB_KERNEL_FILL);
+        ProfScope pr(c, HGB_KERNEL_FILL_ROOT);
         st = launch_fill(c, gp, a);
         if (st != HGB_OK) return st;
     }
     if (!merges.empty()) {
-        ProfScope ps(c, HGB_KERNEL_FILL);
+        ProfScope pm(c, HGB_KERNEL_MERGE);
         const int64_t node_vec = (int64_t)c->F * c->S;
         dim3 grid(grid_for(node_vec, 256, 1024), (unsigned)merges.size());
         st = launch_merge(c, merges, (const MergeEntry*)(dev + off_merges), grid, hist);
@@ -1656,8 +1667,14 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
 }
 
 hgb_status hgb_subtract_siblings(hgb_ctx* c, const int64_t* parent, int64_t* child,
-                                 const uint8_t* built_is_right, const int32_t* parent_slot,
-                                 int32_t n_pairs)
+                                 const uint8_t* built_is_right, int32_t n_pairs)
+{
+    return hgb_subtract_siblings_slots(c, parent, child, built_is_right, nullptr, n_pairs);
+}
+
+hgb_status hgb_subtract_siblings_slots(hgb_ctx* c, const int64_t* parent, int64_t* child,
+                                       const uint8_t* built_is_right, const int32_t* parent_slot,
+                                       int32_t n_pairs)
 {
     if (!c) return HGB_E_INVALID;
     c->err.clear();
@@ -1819,7 +1836,7 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     const int per = (c->B + kWave - 1) / kWave;
     const bool aligned = ((uintptr_t)parent & 15) == 0 && ((uintptr_t)child & 15) == 0;
     if (!aligned || per > 16) {   // the two passes
-        hgb_status st = hgb_subtract_siblings(c, parent, child, built_is_right, parent_slot, n_pairs);
+        hgb_status st = hgb_subtract_siblings_slots(c, parent, child, built_is_right, parent_slot, n_pairs);
         if (st != HGB_OK) return st;
         return hgb_find_splits(c, child, 2 * n_pairs, lambda, gamma, out);
     }
@@ -1918,8 +1935,9 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     std::vector<int32_t> first(n_nodes + 1);
     for (int i = 0; i < n_nodes; ++i) {
         first[i] = (int32_t)items.size();
-        for (int32_t b = offs[i]; b < offs[i + 1]; b += kPartChunk)
-            items.push_back({i, b, std::min(b + kPartChunk, offs[i + 1]), offs[i]});
+        // 64-bit steps: the last chunk of a node may end within kPartChunk of 2^31
+        for (int64_t b = offs[i]; b < offs[i + 1]; b += kPartChunk)
+            items.push_back({i, (int32_t)b, (int32_t)std::min<int64_t>(b + kPartChunk, offs[i + 1]), offs[i]});
     }
     first[n_nodes] = (int32_t)items.size();
     const int64_t n_items = (int64_t)items.size();
@@ -1984,11 +2002,8 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     if (st != HGB_OK) return st;
     // Wait for the node records only: the scatter keeps running while the
     // caller plans the next level (the stream orders whatever reads its rows).
-    for (;;) {
-        const hipError_t e = hipEventQuery(c->part_ready);
-        if (e == hipSuccess) break;
-        if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
-    }
+    st = poll_event(c, c->part_ready);
+    if (st != HGB_OK) return st;
     st = take_flags(c);   // a row index outside [0, n)
     if (st != HGB_OK) return st;
     int32_t nc = 0;
@@ -2042,6 +2057,13 @@ hgb_status hgb_profile_query(hgb_ctx* c, int kernel, double* total_ms, int64_t* 
             c->ev_pool.push_back(pr.second);
         }
         c->ev_pending[k].clear();
+    }
+    if (kernel == HGB_KERNEL_FILL) {   // the sum of its three parts, each timed on its own
+        *total_ms = c->prof_ms[HGB_KERNEL_FILL_ROOT] + c->prof_ms[HGB_KERNEL_FILL_LEVEL] +
+                    c->prof_ms[HGB_KERNEL_MERGE];
+        *launches = c->prof_launches[HGB_KERNEL_FILL_ROOT] + c->prof_launches[HGB_KERNEL_FILL_LEVEL] +
+                    c->prof_launches[HGB_KERNEL_MERGE];
+        return HGB_OK;
     }
     *total_ms = c->prof_ms[kernel];
     *launches = c->prof_launches[kernel];

@@ -917,7 +917,7 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     };
 
     if (vec_ok) {
-        // Whole 8-row groups; the rows after the last whole group are added
+        // Whole R-row groups; the rows after the last whole group are added
         // one by one afterwards.  Loads are issued unconditionally (clamped to
         // a valid group), since a load under a branch would make the compiler
         // wait for it at the join; the next step's loads are in flight while
@@ -2600,13 +2600,14 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
     if (sp.feature >= 0) {   // uniform
         const BinT* col = bins + (int64_t)sp.feature * n;
         const int rf = rot[sp.feature];   // stored values are rotated per feature
-        const int k0 = it.begin + (int)threadIdx.x;
-        const int kstep = (int)blockDim.x;
+        // positions in 64 bits: a chunk may end within kPartChunk of 2^31
+        const int64_t k0 = (int64_t)it.begin + threadIdx.x;
+        const int64_t kstep = blockDim.x;
         int64_t r[kPartRows];
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {
-            const int kc = min(k0 + j * kstep, it.end - 1);
-            r[j] = row_index ? (int64_t)row_index[kc] : (int64_t)kc;
+            const int64_t kc = min(k0 + j * kstep, (int64_t)it.end - 1);
+            r[j] = row_index ? (int64_t)row_index[kc] : kc;
         }
         int v[kPartRows];
         bool bad = false;
@@ -2618,7 +2619,7 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
         }
 #pragma unroll
         for (int j = 0; j < kPartRows; ++j) {
-            const int k = k0 + j * kstep;
+            const int64_t k = k0 + j * kstep;
             // a row index outside [0, n) is routed right (and reported)
             const bool left = (uint64_t)r[j] < (uint64_t)n && part_left(v[j], n_bins, sp);
             if (k < it.end) {
@@ -2732,14 +2733,14 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
     const int lane = (int)(threadIdx.x & (kWave - 1));
     const int wv = (int)(threadIdx.x / kWave);
     const int waves = (int)(blockDim.x / kWave);
-    const int k0 = it.begin + (int)threadIdx.x;
-    const int kstep = (int)blockDim.x;
+    const int64_t k0 = (int64_t)it.begin + threadIdx.x;   // 64 bits: see k_part_count
+    const int64_t kstep = blockDim.x;
     int32_t r[kPartRows];
     uint8_t f[kPartRows];
 #pragma unroll
     for (int j = 0; j < kPartRows; ++j) {
-        const int kc = min(k0 + j * kstep, it.end - 1);
-        r[j] = row_index ? row_index[kc] : kc;
+        const int64_t kc = min(k0 + j * kstep, (int64_t)it.end - 1);
+        r[j] = row_index ? row_index[kc] : (int32_t)kc;
         f[j] = flags[kc];
     }
     uint64_t bl[kPartRows], bi[kPartRows];   // per step: the wave's left rows, its rows

@@ -13,8 +13,11 @@
 //           bin * 64 + (lane + k) mod 32 for the k-th add -- two lanes per bank
 //           pair whatever the bins -- launched in the fills' shape, one block
 //           of 1024 threads and a 128 KB tile per CU (`copies` unused).
+//   kind 4  u32 atomic add, every lane a distinct word (the u32 conflict-free
+//           ceiling, for comparison with kind 1: a cell split into 32-bit
+//           halves would take four of these instead of two u64 adds).
 //
-// Kinds 0-2 fill the chip with 8 blocks of 256 threads per CU; each thread
+// Kinds 0-2 and 4 fill the chip with 8 blocks of 256 threads per CU; each thread
 // issues `iters` x 4 adds.  Indices are reduced modulo the allocated word count,
 // so every access stays inside the block's LDS allocation.  The result is read
 // back into a sink so the adds cannot be elided.
@@ -52,6 +55,7 @@ __global__ __launch_bounds__(1024) void k_lds_rate(int iters, int copies, int wo
             if (KIND == 1) atomicAdd(&lds[((uint32_t)lane + 64u * (uint32_t)k) & wm], 3ull);
             if (KIND == 2) atomicAdd(&l32[(b * (uint32_t)copies + ((uint32_t)lane & cm)) & (2 * wm + 1)], 3u);
             if (KIND == 3) atomicAdd(&lds[((b << 6) | (((uint32_t)lane + (uint32_t)k) & 31u)) & wm], 3ull);
+            if (KIND == 4) atomicAdd(&l32[((uint32_t)lane + 64u * (uint32_t)k) & (2 * wm + 1)], 3u);
         }
     }
     __syncthreads();
@@ -79,12 +83,12 @@ using namespace lds_probe;
 extern "C" {
 
 // Measures lane-level LDS atomic adds per second on `device` for pattern
-// `kind` (0 to 3 above) with `copies` in {1, 2, 4, ..., 32}.  Writes the
+// `kind` (0 to 4 above) with `copies` in {1, 2, 4, ..., 32}.  Writes the
 // rate to *lane_ops_per_s and the number of compute units to *n_cu.  Returns 0
 // on success, 1 for bad arguments, 2 for a HIP error.
 int lds_rate_measure(int device, int kind, int copies, double* lane_ops_per_s, int* n_cu)
 {
-    if (!lane_ops_per_s || !n_cu || kind < 0 || kind > 3 || copies < 1 || copies > 32 ||
+    if (!lane_ops_per_s || !n_cu || kind < 0 || kind > 4 || copies < 1 || copies > 32 ||
         (copies & (copies - 1)) != 0)
         return 1;
     if (hipSetDevice(device) != hipSuccess) return 2;
@@ -95,7 +99,7 @@ int lds_rate_measure(int device, int kind, int copies, double* lane_ops_per_s, i
     const int blocks = prop.multiProcessorCount * (fill_shape ? 1 : 8);
     const int threads = fill_shape ? 1024 : 256;
     const int iters = 2000;
-    // kind 1 uses kind 0's allocation; kind 3 a 128 KB tile (256 slots x 2
+    // kinds 1, 2 and 4 use kind 0's allocation; kind 3 a 128 KB tile (256 slots x 2
     // planes x 32 positions)
     const int words = fill_shape ? 256 * 64 : 256 * copies;
     unsigned long long* sink = nullptr;
@@ -111,7 +115,8 @@ int lds_rate_measure(int device, int kind, int copies, double* lane_ops_per_s, i
         hipError_t e = kind == 0   ? launch<0>(iters, copies, words, blocks, threads, sink, st)
                        : kind == 1 ? launch<1>(iters, copies, words, blocks, threads, sink, st)
                        : kind == 2 ? launch<2>(iters, copies, words, blocks, threads, sink, st)
-                                   : launch<3>(iters, copies, words, blocks, threads, sink, st);
+                       : kind == 3 ? launch<3>(iters, copies, words, blocks, threads, sink, st)
+                                   : launch<4>(iters, copies, words, blocks, threads, sink, st);
         if (e != hipSuccess) goto done;
         if (hipEventRecord(b, st) != hipSuccess) goto done;
         if (hipEventSynchronize(b) != hipSuccess) goto done;

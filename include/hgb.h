@@ -2,9 +2,9 @@
  * hgb -- level histogram build for histogram gradient-boosted trees, MI355X
  * (gfx950) native.  C ABI over hand-written HIP kernels.
  *
- * The operation, per tree level: for every row of every node that is built
- * from rows, add the row's (gradient, hessian) into one bin of every feature's
- * histogram; derive each larger sibling as parent minus the smaller one; scan
+ * The operation, per tree level: each node built from rows gets, per feature,
+ * the (gradient, hessian) sums of its rows grouped by the rows' bins; each
+ * larger sibling is derived as parent minus the smaller one; scan
  * every feature's bins with the XGBoost-style gain and pick each node's split.
  *
  * Sources (the pages this library restates):
@@ -66,23 +66,37 @@ typedef struct {
 /* Largest S = n_bins + has_missing the kernels accept. */
 #define HGB_MAX_SLOTS 4096
 
-/* 1 when a HIP device is present and usable, else 0 (tests skip on 0). */
+/* 1 when a HIP device is present and usable, else 0 ([bonsai-10] "Always
+ * registered, capability at runtime": the library always loads, and whether it
+ * can run is a runtime question; its tests skip where there is no device).
+ * Counts devices only; touches no device state. */
 int hgb_available(void);
 
 /* Create a context on `device`, enqueueing on `hip_stream` (a hipStream_t;
- * NULL selects the device's null stream).  *out receives the context. */
+ * NULL selects the device's null stream).  *out receives the context
+ * ([bonsai-10] "The device context lifecycle": one device context owns the
+ * resident state of a fit, split by lifetime into the dataset, the per-tree
+ * gradients and the per-level buffers).  The caller owns the stream.
+ * Errors: HGB_E_INVALID for a null `out` or a device index out of range;
+ *         HGB_E_DEVICE when no device is usable or an allocation fails. */
 hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out);
 
-/* Release the context and everything it owns.  Synchronizes its stream. */
+/* Release the context and everything it owns ([bonsai-10] "The device
+ * context lifecycle").  Synchronizes its stream first.  NULL is a no-op. */
 void hgb_destroy(hgb_ctx* ctx);
 
-/* Message describing the last failed call on this context ("" if none).
- * Valid until the next call on the context. */
+/* Message describing the last failed call on this context ("" if none;
+ * "null context" for NULL).  Valid until the next call on the context
+ * ([bonsai-10] "The kernel": a shape the device path cannot take is declined
+ * up front, with a reason, so the caller can fall back; a call that passed
+ * its checks does not fail later). */
 const char* hgb_last_error(const hgb_ctx* ctx);
 
-/* Block until the context's stream has drained.  Returns HGB_E_INVALID if a
- * kernel met a row index outside [0, n) since the previous hgb_sync (those
- * entries were skipped), HGB_E_DEVICE on a runtime error, else HGB_OK. */
+/* Block until the context's stream has drained ([bonsai-10] "The device
+ * context lifecycle": the host reads results once the level's work is done).
+ * Returns HGB_E_INVALID if a kernel met a row index outside [0, n) since the
+ * previous hgb_sync (those entries were skipped), HGB_E_DEVICE on a runtime
+ * error, else HGB_OK. */
 hgb_status hgb_sync(hgb_ctx* ctx);
 
 /*
@@ -165,14 +179,18 @@ hgb_status hgb_copy_quantized(hgb_ctx* ctx, int32_t* q_dev);
  * Errors: HGB_E_INVALID for bits outside [1, 30]. */
 hgb_status hgb_set_precision(hgb_ctx* ctx, int32_t bits);
 
-/* The current tree's scales: a fixed-point sum X stands for X * 2^-k. */
+/* The current tree's scales: a fixed-point sum X stands for X * 2^-k
+ * ([bonsai-9] "The idea": the device cells are int64 fixed point; these are
+ * the exponents that turn them back into gradient and hessian sums).
+ * Errors: HGB_E_INVALID for a null pointer; HGB_E_STATE before begin_tree. */
 hgb_status hgb_get_scales(const hgb_ctx* ctx, int32_t* k_g, int32_t* k_h);
 
 /*
  * Build the histograms of a level's nodes from rows ([bonsai-E6] "Two fills,
- * one choice": for every row of a node, add its gradient and hessian into one
- * bin of every feature's histogram; [bonsai-10] "Level batching": all nodes of
- * a level in one pass).  Cells are exact int64 sums of the fixed-point values.
+ * one choice": each row of a node contributes its gradient and hessian to the
+ * bin it falls in, in each feature's histogram; [bonsai-10] "Level batching":
+ * all nodes of a level in one pass).  Cells are exact int64 sums of the
+ * fixed-point values.
  *
  * row_index_dev:     int32, the nodes' row lists concatenated, node i owning
  *                    entries [node_offsets[i], node_offsets[i+1]).  Order within
@@ -198,21 +216,34 @@ hgb_status hgb_build_level(hgb_ctx* ctx, const int32_t* row_index_dev,
 
 /*
  * Derive every pair's other child: other = parent - built, slot by slot, exact
- * ([ybb] section 3, histogram subtraction; integer cells need no clamp).
+ * ([ybb] section 3, histogram subtraction: the larger child's histogram is the
+ * parent's minus the smaller one's; integer cells need no clamp).
  *
- * parent_dev:          level buffer of the parents; pair i's parent is at node
- *                      slot parent_slot_host[i] (i when parent_slot_host is NULL).
+ * parent_dev:          [n_pairs][F][S][2] int64; pair i's parent is node slot i.
  * child_dev:           [2*n_pairs][F][S][2] int64; pair i's children are node
  *                      slots 2i (left) and 2i+1 (right).  The built child is at
  *                      2i + built_is_right_host[i]; the other one is written.
- * built_is_right_host: uint8 [n_pairs].
- * parent_slot_host:    int32 [n_pairs] or NULL.
+ * built_is_right_host: uint8 [n_pairs] (nonzero: the right child was built).
  * Errors: HGB_E_STATE before upload_bins; HGB_E_INVALID for n_pairs outside
- *         [0, 65535] or a negative parent slot.
+ *         [0, 65535] or a null pointer with n_pairs > 0.
  */
 hgb_status hgb_subtract_siblings(hgb_ctx* ctx, const int64_t* parent_dev, int64_t* child_dev,
-                                 const uint8_t* built_is_right_host,
-                                 const int32_t* parent_slot_host, int32_t n_pairs);
+                                 const uint8_t* built_is_right_host, int32_t n_pairs);
+
+/*
+ * hgb_subtract_siblings with the parents anywhere in a level buffer: pair i's
+ * parent is node slot parent_slot_host[i] of parent_dev (i when
+ * parent_slot_host is NULL), so the parents can stay where the previous level
+ * left them ([bonsai-10] "The device context lifecycle": the previous
+ * frontier's histograms stay resident and the children are derived from them
+ * in place).  Otherwise as hgb_subtract_siblings.
+ *
+ * parent_slot_host:    int32 [n_pairs] or NULL.
+ * Errors: as hgb_subtract_siblings; HGB_E_INVALID for a negative parent slot.
+ */
+hgb_status hgb_subtract_siblings_slots(hgb_ctx* ctx, const int64_t* parent_dev, int64_t* child_dev,
+                                       const uint8_t* built_is_right_host,
+                                       const int32_t* parent_slot_host, int32_t n_pairs);
 
 /*
  * Best split of every node of a level ([ybb] section 1: the gain
@@ -266,11 +297,13 @@ hgb_status hgb_find_level_split(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n
                                 double lambda, double gamma, hgb_split* out_dev);
 
 /*
- * subtract_siblings followed by find_splits over the 2 * n_pairs children, in
- * one pass over the histograms: the result (the other children written, one
- * hgb_split per child in out_dev) is exactly that of the two calls.  Arguments
- * as for those calls; out_dev holds 2 * n_pairs records.
- * Errors: as for subtract_siblings and find_splits.
+ * hgb_subtract_siblings_slots followed by hgb_find_splits over the 2 * n_pairs
+ * children, in one pass over the histograms ([ybb] section 3 subtraction and
+ * section 1 gain; [bonsai-10] "Level batching": the level's tail in a fixed
+ * number of launches): the result (the other children written, one hgb_split
+ * per child in out_dev) is exactly that of the two calls.  Arguments as for
+ * those calls; out_dev holds 2 * n_pairs records.
+ * Errors: as for those calls; HGB_E_INVALID for n_pairs above 32767.
  */
 hgb_status hgb_subtract_find_splits(hgb_ctx* ctx, const int64_t* parent_dev, int64_t* child_dev,
                                     const uint8_t* built_is_right_host,
@@ -322,11 +355,15 @@ typedef enum {
     HGB_KERNEL_QUANTIZE = 0,   /* begin_tree: max-reduce + quantize */
     HGB_KERNEL_GATHER = 1,     /* build_level: level-order (g, h) gather */
     HGB_KERNEL_ZERO = 2,       /* build_level: zeroing of atomically merged slices */
-    HGB_KERNEL_FILL = 3,       /* build_level: LDS histogram fill + merge */
+    HGB_KERNEL_FILL = 3,       /* build_level: LDS histogram fill + merge (the sum of 7, 8, 9) */
     HGB_KERNEL_SUBTRACT = 4,   /* subtract_siblings */
     HGB_KERNEL_SPLIT = 5,      /* find_splits (both kernels) */
     HGB_KERNEL_PARTITION = 6,  /* partition_level (three kernels) */
-    HGB_KERNEL_COUNT = 7
+    /* the parts of HGB_KERNEL_FILL, each launch bracketed on its own: */
+    HGB_KERNEL_FILL_ROOT = 7,  /* the root's fill launches */
+    HGB_KERNEL_FILL_LEVEL = 8, /* the fill launch of a level below the root */
+    HGB_KERNEL_MERGE = 9,      /* merges of nodes' partial histograms */
+    HGB_KERNEL_COUNT = 10
 } hgb_kernel;
 
 /* Turn timing on (nonzero) or off, and reset the counters. */

@@ -12,8 +12,8 @@
  *   quantize      per-tree fixed-point encoding of (grad, hess) into integers
  *                 (the pages fix "int64 fixed point" cells but not the scale;
  *                 the scale rule below is this project's reading).
- *   build_hist    for every row of a node, add the row's (g, h) into one bin of
- *                 every feature's histogram.
+ *   build_hist    per node and feature, the (g, h) sums of the node's rows,
+ *                 grouped by the slot each row's bin names.
  *   subtract      larger sibling = parent - smaller sibling, bin by bin.
  *   find_splits   scan each feature's bins with the XGBoost-style gain and pick
  *                 the best (feature, bin, default direction) per node.
@@ -110,8 +110,8 @@ int oracle_check_bins(const void* bins, int bin_bytes, int64_t n_rows,
  * Histogram of every node on a level.
  *
  * Basis: bonsai "E6. The wide-data wall", section "Two fills, one choice":
- * for every row in a node, add that row's gradient and hessian into one bin
- * of every feature's histogram.  The cells are int64 (bonsai "9. Parallelism &
+ * each row of a node contributes its (qg, qh) to the slot its bin names, in
+ * each feature's histogram.  The cells are int64 (bonsai "9. Parallelism &
  * determinism", "The idea"), so the sum is exact and order-free.  This loop
  * walks node -> feature -> the node's rows, i.e. the feature-parallel fill of
  * the same page, run on one thread.

@@ -434,6 +434,34 @@ def test_subtract_plan_sizes(hgb, torch, n_pairs):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("n_pairs", [1, 300])
+def test_subtract_five_argument_form(hgb, torch, n_pairs):
+    """hgb_subtract_siblings called with exactly the five arguments of its
+    prototype (ctypes, no wrapper): pair i's parent is slot i.  Against the
+    oracle's subtraction."""
+    import ctypes
+    say("five-argument subtract", n_pairs)
+    w = synth.random_small(44, 1_000, 3, 16, True, 0)
+    F, S = w.n_features, w.n_slots
+    rng = np.random.default_rng(100 + n_pairs)
+    parent = rng.integers(-2**40, 2**40, size=(n_pairs, F, S, 2), dtype=np.int64)
+    child = rng.integers(-2**40, 2**40, size=(2 * n_pairs, F, S, 2), dtype=np.int64)
+    bir = rng.integers(0, 2, size=n_pairs).astype(np.uint8)
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    par_t = torch.from_numpy(parent).cuda()
+    ch_t = torch.from_numpy(child).cuda()
+    lib = hgb.load()
+    st = lib.hgb_subtract_siblings(ctx._h, ctypes.c_void_p(par_t.data_ptr()), ctypes.c_void_p(ch_t.data_ptr()),
+                                   bir.ctypes.data_as(ctypes.c_void_p), ctypes.c_int32(n_pairs))
+    assert st == hgb.HGB_OK
+    ctx.sync()
+    got = ch_t.cpu().numpy()
+    ctx.close()
+    want = oracle.subtract(parent, child.copy(), bir)
+    assert np.array_equal(got, want)
+
+
 # ----------------------------------------------------------------- errors ---
 
 def test_error_paths(hgb, torch):
