@@ -35,7 +35,7 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
             "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
             "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized",
-            "hgb_find_level_split")
+            "hgb_find_level_split", "hgb_find_splits_noalloc")
 
 # hgb_objective
 OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
@@ -97,6 +97,8 @@ def load():
     lib.hgb_subtract_siblings_slots.restype = c_int
     lib.hgb_find_splits.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_splits.restype = c_int
+    lib.hgb_find_splits_noalloc.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
+    lib.hgb_find_splits_noalloc.restype = c_int
     lib.hgb_find_level_split.argtypes = [vp, vp, i32, ctypes.c_double, ctypes.c_double, vp]
     lib.hgb_find_level_split.restype = c_int
     lib.hgb_partition_level.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32), vp]
@@ -350,6 +352,15 @@ class Context:
         op = self._dev(out, "out", torch.uint8, (int(n_nodes) + 1) * SPLIT_BYTES)
         self._check(self._lib.hgb_find_level_split(self._h, hp, int(n_nodes), float(lam),
                                                    float(gamma), op), "find_level_split")
+
+    def find_splits_noalloc(self, hist, n_nodes: int, lam: float, gamma: float, out):
+        """find_splits with its scratch in the library's fixed per-device array
+        (no allocation in the call); out as for find_splits."""
+        torch = self._torch
+        hp = self._dev(hist, "hist", torch.int64, int(n_nodes) * self.node_elems)
+        op = self._dev(out, "out", torch.uint8, int(n_nodes) * SPLIT_BYTES)
+        self._check(self._lib.hgb_find_splits_noalloc(self._h, hp, int(n_nodes), float(lam),
+                                                      float(gamma), op), "find_splits_noalloc")
 
     def find_splits(self, hist, n_nodes: int, lam: float, gamma: float, out):
         """out: uint8 CUDA tensor of at least n_nodes * 56 bytes (hgb_split records)."""

@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -59,6 +60,16 @@ constexpr int kStages = 16;
 // Initial capacity of an upload stage: larger than any level's plan of the
 // matrices measured here (the level-3 plan of 131,072 x 16,384 is about 70 KB).
 constexpr size_t kStageMinBytes = 256 * 1024;
+
+// Scratch of hgb_find_splits_noalloc: one array per device, held until the
+// process ends.  In host code `scratch` is only a stand-in for the device
+// array: hgb_create looks up its address on each device (hipGetSymbolAddress)
+// and every host use goes through that address.
+constexpr size_t kNoAllocScratchBytes = HGB_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_dev;   // per device: the address of `scratch` there
 
 struct Stage {
     void* host = nullptr;   // pinned
@@ -113,6 +124,9 @@ struct hgb_ctx {
     int64_t level_terms_cap = 0;
     LevelBest* level_best = nullptr;      // find_level_split: per-block winners
     int64_t level_best_cap = 0;
+
+    // this device's copy of the no-allocation scratch array (set up by hgb_create)
+    unsigned char* noalloc_scratch = nullptr;
 
     // small device words: [0..1] max patterns, [2] error flags
     uint32_t* dev_words = nullptr;
@@ -1199,6 +1213,21 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
         c->n_cu = prop.multiProcessorCount;
     c->stream = (hipStream_t)hip_stream;
+    {
+        // the no-allocation scratch: its address on this device, looked up
+        // once per device with the device current
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_dev.size() < (size_t)n) g_scratch_dev.resize((size_t)n, nullptr);
+        if (!g_scratch_dev[device]) {
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+                delete c;
+                return HGB_E_DEVICE;
+            }
+            g_scratch_dev[device] = ptr;
+        }
+        c->noalloc_scratch = (unsigned char*)g_scratch_dev[device];
+    }
     if (hipMalloc((void**)&c->dev_words, 64) != hipSuccess ||
         hipMalloc((void**)&c->max_part, sizeof(uint32_t) * 2 * kMaxBlocks) != hipSuccess ||
         hipHostMalloc((void**)&c->host_words, 64, hipHostMallocDefault) != hipSuccess ||
@@ -1714,46 +1743,62 @@ hgb_status hgb_subtract_siblings_slots(hgb_ctx* c, const int64_t* parent, int64_
     return s.release();
 }
 
-hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
-                           double gamma, hgb_split* out)
+// Checks of find_splits' arguments (both entry points).
+static hgb_status check_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
+                                    double gamma, const hgb_split* out, const char* who)
 {
-    if (!c) return HGB_E_INVALID;
-    c->err.clear();
-    if (!c->have_tree) return fail(c, HGB_E_STATE, "find_splits before begin_tree");
-    if (n_nodes < 0 || n_nodes > 65535)
-        return fail(c, HGB_E_INVALID, "find_splits: n_nodes out of range");
+    if (!c->have_tree) return fail(c, HGB_E_STATE, "%s before begin_tree", who);
+    if (n_nodes < 0 || n_nodes > 65535) return fail(c, HGB_E_INVALID, "%s: n_nodes out of range", who);
     if (!(lambda >= 0.0) || !std::isfinite(lambda) || !std::isfinite(gamma))
-        return fail(c, HGB_E_INVALID, "find_splits: lambda must be finite and >= 0, gamma finite");
-    if (n_nodes == 0) return HGB_OK;
-    if (!hist || !out) return fail(c, HGB_E_INVALID, "find_splits: null pointer");
-    HGB_HIP(c, hipSetDevice(c->device));
-    static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
-    const int waves = 4;   // features per block; one best per block
+        return fail(c, HGB_E_INVALID, "%s: lambda must be finite and >= 0, gamma finite", who);
+    if (n_nodes > 0 && (!hist || !out)) return fail(c, HGB_E_INVALID, "%s: null pointer", who);
+    return HGB_OK;
+}
+
+// The split scan's shape: per node, n_entries per-block winners (one per block
+// of 4 features, or per feature for wide bins), and how the lanes hold bins.
+struct SplitShape {
+    int per;        // bins per lane
+    bool aligned;   // the histogram is 16-byte aligned
+    bool sliced;    // wide bins: one block of kSliceWaves waves per feature
+    int n_entries;
+};
+
+static SplitShape split_shape(const hgb_ctx* c, const int64_t* hist)
+{
+    SplitShape sh;
     // a lane's bins in registers when there are at most 4 of them (one wave
     // per feature) or at most 4 x 4 per wave of a sliced block (wide bins),
     // the buffer 16-byte aligned; otherwise read twice from memory
-    const int per = (c->B + kWave - 1) / kWave;
-    const bool aligned = ((uintptr_t)hist & 15) == 0;
-    const bool sliced = aligned && per > 4 && per <= 4 * kSliceWaves;
-    const int n_entries = sliced ? c->F : (c->F + waves - 1) / waves;
-    hgb_status st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * n_entries);
-    if (st != HGB_OK) return st;
-    st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
-    if (st != HGB_OK) return st;
-    ProfScope ps(c, HGB_KERNEL_SPLIT);
-    dim3 grid((unsigned)n_entries, (unsigned)n_nodes);
+    sh.per = (c->B + kWave - 1) / kWave;
+    sh.aligned = ((uintptr_t)hist & 15) == 0;
+    sh.sliced = sh.aligned && sh.per > 4 && sh.per <= 4 * kSliceWaves;
+    sh.n_entries = sh.sliced ? c->F : (c->F + 3) / 4;
+    return sh;
+}
+
+// The per-feature scan into best/totals (device scratch of the shape's size),
+// then the per-node reduction into out.
+static hgb_status launch_find_splits(hgb_ctx* c, const SplitShape& sh, const int64_t* hist, int32_t n_nodes,
+                                     double lambda, double gamma, hgb_split* out, FeatureBest* best,
+                                     long long* totals)
+{
+    static_assert(sizeof(SplitOut) == sizeof(hgb_split), "split record layout");
+    const int waves = 4;   // features per block; one best per block
+    dim3 grid((unsigned)sh.n_entries, (unsigned)n_nodes);
 #define HGB_SPLIT(PER)                                                                              \
     k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
-        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals)
+        std::ldexp(1.0, -c->k_h), lambda, gamma, best, totals)
 #define HGB_SPLIT_SLICED(PER)                                                                       \
     k_split_feature_sliced<PER><<<grid, kSliceWaves * kWave, 0, c->stream>>>(                       \
         (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
-        std::ldexp(1.0, -c->k_h), lambda, gamma, c->best, c->totals)
-    if (sliced) {
+        std::ldexp(1.0, -c->k_h), lambda, gamma, best, totals)
+    const int per = sh.per;
+    if (sh.sliced) {
         if (per <= 2 * kSliceWaves) HGB_SPLIT_SLICED(2);
         else HGB_SPLIT_SLICED(4);
-    } else if (!aligned || per > 16) HGB_SPLIT(0);
+    } else if (!sh.aligned || per > 16) HGB_SPLIT(0);
     else if (per <= 1) HGB_SPLIT(1);
     else if (per <= 2) HGB_SPLIT(2);
     else if (per <= 4) HGB_SPLIT(4);
@@ -1762,10 +1807,58 @@ hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, dou
 #undef HGB_SPLIT
 #undef HGB_SPLIT_SLICED
     HGB_LAUNCHED(c, "k_split_feature");
-    k_split_reduce<<<(unsigned)n_nodes, split_reduce_threads(n_entries), 0, c->stream>>>(c->best, c->totals, n_entries,
-                                                             (SplitOut*)out);
+    k_split_reduce<<<(unsigned)n_nodes, split_reduce_threads(sh.n_entries), 0, c->stream>>>(
+        best, totals, sh.n_entries, (SplitOut*)out);
     HGB_LAUNCHED(c, "k_split_reduce");
     return HGB_OK;
+}
+
+hgb_status hgb_find_splits(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
+                           double gamma, hgb_split* out)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    hgb_status st = check_find_splits(c, hist, n_nodes, lambda, gamma, out, "find_splits");
+    if (st != HGB_OK || n_nodes == 0) return st;
+    HGB_HIP(c, hipSetDevice(c->device));
+    const SplitShape sh = split_shape(c, hist);
+    st = grow(c, &c->best, &c->best_cap, (int64_t)n_nodes * sh.n_entries);
+    if (st != HGB_OK) return st;
+    st = grow(c, &c->totals, &c->totals_cap, (int64_t)2 * n_nodes);
+    if (st != HGB_OK) return st;
+    ProfScope ps(c, HGB_KERNEL_SPLIT);
+    return launch_find_splits(c, sh, hist, n_nodes, lambda, gamma, out, c->best, c->totals);
+}
+
+// Bytes of the no-allocation scratch a find_splits of n_nodes would use: the
+// per-block winners (256-byte aligned), then the node totals.
+static size_t noalloc_split_bytes(const SplitShape& sh, int32_t n_nodes, size_t* totals_off)
+{
+    const size_t best = (size_t)n_nodes * (size_t)sh.n_entries * sizeof(FeatureBest);
+    *totals_off = (best + 255) / 256 * 256;
+    return *totals_off + (size_t)2 * n_nodes * sizeof(long long);
+}
+
+hgb_status hgb_find_splits_noalloc(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,
+                                   double gamma, hgb_split* out)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    hgb_status st = check_find_splits(c, hist, n_nodes, lambda, gamma, out, "find_splits_noalloc");
+    if (st != HGB_OK || n_nodes == 0) return st;
+    if (!c->noalloc_scratch) return fail(c, HGB_E_DEVICE, "find_splits_noalloc: no scratch on this device");
+    const SplitShape sh = split_shape(c, hist);
+    size_t totals_off = 0;
+    const size_t need = noalloc_split_bytes(sh, n_nodes, &totals_off);
+    if (need > kNoAllocScratchBytes)
+        return fail(c, HGB_E_UNSUPPORTED,
+                    "find_splits_noalloc: %d nodes x %d features need %zu bytes of scratch, more than its %zu",
+                    n_nodes, c->F, need, kNoAllocScratchBytes);
+    HGB_HIP(c, hipSetDevice(c->device));
+    // Every entry the reduction reads is written by the scan first, so the
+    // scratch needs no clearing (it keeps the last call's contents).
+    return launch_find_splits(c, sh, hist, n_nodes, lambda, gamma, out, (FeatureBest*)c->noalloc_scratch,
+                              (long long*)(c->noalloc_scratch + totals_off));
 }
 
 hgb_status hgb_find_level_split(hgb_ctx* c, const int64_t* hist, int32_t n_nodes, double lambda,

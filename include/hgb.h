@@ -266,6 +266,30 @@ hgb_status hgb_find_splits(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_node
                            double lambda, double gamma, hgb_split* out_dev);
 
 /*
+ * hgb_find_splits for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as hgb_find_splits, but its intermediate
+ * per-feature winners and node totals live in one fixed array of
+ * HGB_NOALLOC_SCRATCH_BYTES per device, allocated with the library and held
+ * until the process ends, so the call itself allocates nothing (no hipMalloc,
+ * no hipFree, no event, no staging buffer) and is not timed by
+ * hgb_profile_enable.  The caller still passes the histograms and the output.
+ *
+ * The array is shared by every context and call on a device and keeps the
+ * last call's contents (nothing in it needs clearing: each call writes every
+ * entry it reads).  Calls that overlap on one device -- on different streams,
+ * or from different host threads -- race on it; order them on one stream.
+ *
+ * Limit: n_nodes * ceil(F / 4) * 32 bytes (n_nodes * F * 32 with more than
+ * 256 bins per feature), rounded up to 256, plus n_nodes * 16 must not exceed
+ * HGB_NOALLOC_SCRATCH_BYTES.
+ * Errors: as hgb_find_splits; HGB_E_UNSUPPORTED beyond the limit.
+ */
+#define HGB_NOALLOC_SCRATCH_BYTES (16u << 20)
+hgb_status hgb_find_splits_noalloc(hgb_ctx* ctx, const int64_t* hist_dev, int32_t n_nodes,
+                                   double lambda, double gamma, hgb_split* out_dev);
+
+/*
  * The oblivious (symmetric) level split: one (feature, bin, direction) for all
  * n_nodes nodes of a level ([bonsai-10] "The device context lifecycle":
  * find_level_split is the oblivious grower's scan of the frontier; [ybb]
