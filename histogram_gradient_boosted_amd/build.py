@@ -15,7 +15,8 @@ SOURCES = [os.path.join(CSRC, "hgb.hip")]
 # the LDS atomic-rate microbenchmark that bench.py reports beside the fill
 PROBE_LIB = os.path.join(PKG, "liblds_rate.so")
 PROBE_SOURCES = [os.path.join(CSRC, "lds_rate.hip")]
-HEADERS = [os.path.join(CSRC, "hgb_kernels.h"), os.path.join(INCLUDE, "hgb.h")]
+HEADERS = [os.path.join(CSRC, "hgb_kernels.h"), os.path.join(CSRC, "hgb_layout.h"), os.path.join(CSRC, "hgb_plan.h"),
+           os.path.join(INCLUDE, "hgb.h")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -5,6 +5,7 @@
 // hgb_kernels.h.
 #include "hgb.h"
 #include "hgb_kernels.h"
+#include "hgb_plan.h"
 
 #include <hip/hip_runtime.h>
 
@@ -23,29 +24,9 @@ using namespace hgb;
 
 namespace {
 
-// gfx950: 160 KiB of LDS per CU; every fill runs one 1024-thread block per CU.
-constexpr int64_t kFillLdsBudget = 160 * 1024;
-// What a tile may take of it: the rest holds the item's totals and the
-// features' recovered cells (kFixWords).
+// (The fill planner's constants are in hgb_plan.h.)
 // A feature's top slot is hot when it holds at least 1/kHotSlotShare of the rows.
 constexpr int64_t kHotSlotShare = 16;
-constexpr int64_t kTileLdsBudget = kFillLdsBudget - 8 * kFixWords;
-constexpr int kRootThreads = 1024;
-constexpr int kLevelThreads = 1024;
-// Fill items per CU: the root gets one equal share per CU (equal items finish
-// together, and fewer items mean fewer merges of partial histograms); other
-// levels, with nodes of very different sizes, get several smaller items per
-// CU for balance.
-constexpr int64_t kRootItemsPerCu = 1;
-// Level fills: blocks per CU, each taking an equal share of the level's rows.
-constexpr int64_t kLevelBlocksPerCu = 1;
-// Fixed cost of one fill item, in rows per cell of its tile: zeroing the tile,
-// the pipeline's ramp and writing the tile out weigh about as much as this
-// many rows.
-constexpr double kPieceRowsPerCell = 0.25;
-// A node split over more blocks than this is merged in several groups, added
-// into its zeroed slot with atomics.
-constexpr int kMergeGroup = 32;
 // Rows up to this many bytes get a row-major copy (16,384 one-byte features
 // included): below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
@@ -353,337 +334,20 @@ int grid_for(int64_t work, int threads, int cap)
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-// ---------------------------------------------------------------------------
-// Fill planning
-// ---------------------------------------------------------------------------
-
-enum FillKind { kFillRoot = 0, kFillCols = 1, kFillRowsKind = 2 };
-
-// Launch shape of one build_level fill.
-struct FillPlan {
-    FillKind kind;
-    int acc;            // kWide / kPacked
-    int lc;             // log2 of the privatized copy count
-    int tile;           // features per item (root, cols: NF; rows: features per load)
-    int lt;             // rows: bytes loaded per row
-    int threads;
-    int64_t step_rows;  // rows a block consumes per step
-    int drain;          // packed: steps between drains of the copies (0: wide)
-    int ra;             // rows, packed: register-accumulator cells per thread (0: LDS)
-    int il;             // slot-major interleaved tile (lane-rotated features)
-    size_t lds_bytes;
-};
-
-// Row-major level fills with a register accumulator: cells per thread and
-// entries per thread and step.
-constexpr int kRegAccCells = 8;
-constexpr int kRegAccEntries = 1;
-// Entries per thread and step of the wide row-major fill.
-constexpr int kWideRowEntries = 1;
-
-// LDS bytes per feature of a tile: the copies, plus the packed accumulator.
-int64_t feature_lds(int acc, int S, int lc)
+// What the planner (hgb_plan.h) reads of a context.
+PlanCtx plan_ctx(const hgb_ctx* c)
 {
-    return (int64_t)tile_words(acc, 1, S, lc) * 8;
-}
-
-// Packed sums stay exact while every copy-slot sees at most
-// kPackedRowsPerCopy rows between drains.  Copy c is used by threads / C
-// threads, each taking `per_thread` rows per step; the root kernel may add up
-// to kRootRows - 1 tail rows on one copy after its last step.  Returns the
-// steps between drains (0: not even one step fits).
-int packed_drain_steps(int threads, int lc, int per_thread)
-{
-    const int64_t per_copy_step = (int64_t)(threads >> lc) * per_thread;
-    return (int)((kPackedRowsPerCopy - (kRootRows - 1)) / per_copy_step);
-}
-
-// Cost model of the root and feature-major fills per cell (seconds), fitted
-// to measurements on the MI355X: random-bin ds_add_u64 runs at kLdsOps[lc]
-// lanes per clock per CU with 2^lc lane-interleaved copies, bins stream from
-// HBM at ~6 TB/s, and every feature tile of a row chunk re-reads and unpacks
-// the (g, h) pair (~30 TB/s equivalent).  In these kernels the terms add up
-// rather than overlap.
-double fill_cost(int acc, int lc, int tile, int w)
-{
-    static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
-    const double lds = (acc == kWide ? 2.0 : 1.0) / (kLdsOps[lc] * 2.4e9 * 256);
-    return lds + w / 6.0e12 + (8.0 / tile) / 30.0e12;
-}
-
-// The same for the root's interleaved tile of tf positions (wide sums), over
-// F features: the adds spread over tf * 2^lc bank pairs (32: conflict-free)
-// but every position is added, used or not; one (g, h) read serves tf
-// features; and the register rotation and per-lane feature offsets cost about
-// two vector instructions per add more than the feature-major tile (64 lanes
-// per clock per CU).
-double fill_cost_il(int lc, int tf, int F, int w)
-{
-    const double clk = 2.4e9 * 256;
-    const int spread = tf << lc;
-    const double ops = spread >= 32 ? 9.0 : spread >= 16 ? 6.5 : spread >= 8 ? 5.0 : 4.3;
-    const double waste = (double)((F + tf - 1) / tf * tf) / F;
-    const double lds = 2.0 * waste / (ops * clk);
-    const double valu = 2.0 * waste / (64.0 * clk);
-    return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
-}
-
-// The root's interleaved tile with packed sums: one add per position, plus
-// the drains -- every `drain` steps of 4 rows per thread, each of the tile's
-// S * tf * 2^lc words is exchanged with zero once (a conflict-free LDS
-// atomic) and two barriers stall the block.
-double fill_cost_il_packed(int lc, int tf, int F, int w, int S, int drain)
-{
-    const double clk = 2.4e9 * 256;
-    const double waste = (double)((F + tf - 1) / tf * tf) / F;
-    const double ops = 9.0;
-    const double drain_per_cell = (double)S * (1 << lc) / ((double)drain * kRootThreads * kRootRows);
-    const double lds = (waste + drain_per_cell) / (ops * clk);
-    const double valu = 1.5 * waste / (64.0 * clk);
-    return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
-}
-
-// Row-major level fills read scattered rows.  Cost per row (seconds) of a plan
-// with n_tiles feature tiles: the LDS adds at the same rates as above (plus
-// the packed drains: lane-contiguous LDS reads and writes); each row's lines
-// from HBM once at ~5 TB/s (the tiles of a share run side by side on one XCD
-// and share them through L2); and per tile a 64-byte L2 transfer of the row's
-// segment plus its index and (g, h), at ~10 TB/s (fitted to 10M x 28 and 131K x 16K level
-// timings).
-double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, double drain_ops_per_row,
-                 int il = 0, int tile = 0)
-{
-    static const double kLdsOps[5] = {4.3, 4.75, 5.4, 6.9, 8.4};
-    const double clk = 2.4e9 * 256;
-    // The interleaved tile spreads a wave's adds over tile * 2^lc bank pairs
-    // (32 is conflict-free, ~9.9 lanes per clock; measured with lds_rate) but
-    // adds every one of the tile's positions, the unused ones included.
-    const int spread = tile << lc;
-    const double il_ops = spread >= 32 ? 9.0 : spread >= 16 ? 6.5 : spread >= 8 ? 5.0 : 4.3;
-    const double adds = il ? (double)n_tiles * tile : (double)F;
-    const double lds = adds * (acc == kWide ? 2.0 : 1.0) / ((il ? il_ops : kLdsOps[lc]) * clk) +
-                       drain_ops_per_row / (16.0 * clk);
-    // Vector ALU work per add, 64 lanes per clock per CU: about 3 instructions
-    // (unpack, address), 6 with the interleaved tile's rotation and per-lane
-    // feature offset.  It decides narrow matrices, where the gather dominates
-    // and the interleaved tile's faster adds buy nothing (a 28-feature matrix).
-    const double valu = adds * (il ? 6.0 : 3.0) / (64.0 * clk);
-    const double lines = (double)std::max<int64_t>((row_bytes + 127) / 128, 1) * 128.0;
-    const double mem = lines / 5.0e12 + n_tiles * (64.0 + 12.0) / 10.0e12;
-    return std::max(lds, mem) + 0.25 * std::min(lds, mem) + valu;
-}
-
-// Threads of a k_split_reduce block: a node with many feature entries (a wide
-// matrix) takes 1,024, so each thread walks a few of them.
-unsigned split_reduce_threads(int n_entries)
-{
-    return n_entries >= 4096 ? (unsigned)kSplitReduceMaxThreads : 256u;
-}
-
-FillPlan plan_rows(const hgb_ctx* c)
-{
-    FillPlan p{};
-    p.kind = kFillRowsKind;
-    p.threads = kLevelThreads;
-    const int S = c->S, w = c->bin_bytes, F = c->F;
-    const int want_acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
-    double best = 1e300;
-    bool found = false;
-    for (int acc : {want_acc, (int)kWide}) {
-        if (found) break;
-        for (int lt = 32; lt >= 2; lt >>= 1) {
-            if (lt < w) continue;
-            const int tile = lt / w;
-            const int force_tile = c->tune[4];
-            if (force_tile > 0 && tile != force_tile) continue;
-            const int nf = std::min(tile, F);
-            const int n_tiles = (F + nf - 1) / nf;
-            for (int lc = 4; lc >= 0; --lc) {
-                const int force_lc = c->tune[3];
-                if (force_lc >= 0 && lc != force_lc) continue;
-                for (int il = 0; il <= (acc == kWide ? 1 : 0); ++il) {
-                    if (c->tune[8] >= 0 && il != c->tune[8]) continue;
-                    // packed sums live in registers, wide sums in LDS
-                    const int ra = acc == kPacked ? kRegAccCells : 0;
-                    if (ra > 0 && nf * S > ra * kLevelThreads) continue;
-                    const int e = ra > 0 ? kRegAccEntries : kWideRowEntries;
-                    const int64_t words = il ? (int64_t)2 * S * (tile << lc)
-                                             : (int64_t)nf * (acc == kWide ? 2 : 1) * (S << lc);
-                    if (words * 8 > kTileLdsBudget) continue;
-                    int drain = 0;
-                    double drain_ops = 0.0;
-                    if (acc == kPacked) {
-                        drain = packed_drain_steps(kLevelThreads, lc, e);
-                        if (drain == 0) continue;
-                        drain_ops = 2.0 * nf * S * (1 << lc) / ((double)kLevelThreads * e * drain) * n_tiles;
-                    }
-                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops, il, tile);
-                    if (cost < best) {
-                        best = cost;
-                        found = true;
-                        p.acc = acc;
-                        p.lc = lc;
-                        p.tile = tile;
-                        p.lt = lt;
-                        p.ra = ra;
-                        p.il = il;
-                        p.drain = drain;
-                        p.step_rows = (int64_t)kLevelThreads * e;
-                        p.lds_bytes = (size_t)(words + kFixWords) * 8;
-                    }
-                }
-            }
-        }
-    }
-    if (!found) {   // one wide feature of one copy always fits (S <= HGB_MAX_SLOTS)
-        p.acc = kWide;
-        p.lc = 0;
-        p.tile = 1;
-        p.lt = w;
-        p.ra = 0;
-        p.il = 0;
-        p.drain = 0;
-        p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
-        p.lds_bytes = (size_t)(2 * S + kFixWords) * 8;
-    }
-    return p;
-}
-
-FillPlan plan_fill(const hgb_ctx* c, bool root, bool rm)
-{
-    if (!root && rm) return plan_rows(c);
-    FillPlan p{};
-    const int S = c->S;
-    const int w = c->bin_bytes;
-    p.kind = root ? kFillRoot : (rm ? kFillRowsKind : kFillCols);
-    p.threads = root ? kRootThreads : kLevelThreads;
-    auto per_thread_of = [&](int tile) {
-        return p.kind == kFillRoot ? kRootRows : (p.kind == kFillCols ? cols_entries(tile) : kLevelEntries);
-    };
-    const int64_t budget = kTileLdsBudget;
-    const int want_acc = c->precision <= kPackedMaxBits ? kPacked : kWide;
-    // Candidate tiles: NF in {1, 2, 4, 8} features (root, cols), or the
-    // features of one 16/8/4/2-byte row load (rows).
-    double best = 1e300;
-    bool found = false;
-    for (int acc : {want_acc, (int)kWide}) {
-        if (found) break;   // fall back to wide sums only when packed cannot fit
-        for (int lc = 4; lc >= 0; --lc) {
-            const int64_t per_feature = feature_lds(acc, S, lc);
-            const int force_lc = c->tune[root ? 0 : 3];
-            if (force_lc >= 0 && lc != force_lc) continue;
-            for (int k = 0; k < 4; ++k) {
-                int tile, lt = 0;
-                if (p.kind == kFillRowsKind) {
-                    lt = 16 >> k;
-                    if (lt < w) continue;
-                    tile = lt / w;
-                } else {
-                    tile = 8 >> k;
-                }
-                const int force_tile = c->tune[root ? 1 : 4];
-                if (force_tile > 0 && tile != force_tile) continue;
-                if (tile * per_feature > budget) continue;
-                if (p.kind == kFillRoot && w == 2 && tile > 4) continue;   // register-bound
-                if (acc == kPacked && packed_drain_steps(p.threads, lc, per_thread_of(tile)) == 0) continue;
-                // a tile much wider than the matrix wastes nothing but LDS
-                const int eff = std::min(tile, c->F);
-                const double cost = fill_cost(acc, lc, eff, w);
-                if (cost < best) {
-                    best = cost;
-                    found = true;
-                    p.acc = acc;
-                    p.lc = lc;
-                    p.tile = tile;
-                    p.lt = lt;
-                    p.il = 0;
-                }
-            }
-        }
-        // The root's interleaved tile with packed sums: 16 positions, 2^lc >= 2
-        // copies (so that the 64 lanes of an add meet 32 bank pairs and a
-        // step's 4 rows per thread put at most 2,048 rows on a copy), and
-        // each thread's share of the S * 16 cells in registers between drains.
-        // One-byte bins without the skipped slot: the register cells fit
-        // beside 16 positions of loads only there.
-        for (int lc = 1; root && acc == kPacked && lc <= 2; ++lc) {
-            const int tf = 16;
-            if (w != 1 || c->skip) break;
-            if (c->tune[9] == 0) break;
-            if (c->tune[1] > 0 && tf != c->tune[1]) break;
-            if (c->tune[0] >= 0 && lc != c->tune[0]) continue;
-            if ((int64_t)S * tf > (int64_t)kRootIlPackedCells * kRootThreads) break;
-            if ((int64_t)root_il_words(kPacked, tf, S, lc) * 8 > budget) continue;
-            const int drain = packed_drain_steps(kRootThreads, lc, kRootRows);
-            if (drain == 0) continue;
-            const int64_t il_tiles = (c->F + tf - 1) / tf;
-            const int64_t il_chunks = std::max<int64_t>(1, kRootItemsPerCu * c->n_cu / il_tiles);
-            const double merge_s = il_chunks > 1 ? 4e-6 + 2.0 * il_chunks * c->F * S * 16.0 / 5.0e12 : 0.0;
-            const double cells = std::max(1.0, (double)c->n * c->F);
-            const double cost = fill_cost_il_packed(lc, tf, c->F, w, S, drain) + merge_s / cells;
-            if (cost < best || (c->tune[9] == 1 && !(found && p.il))) {
-                best = cost;
-                found = true;
-                p.acc = kPacked;
-                p.lc = lc;
-                p.tile = tf;
-                p.lt = 0;
-                p.il = 1;
-                p.drain = drain;
-            }
-        }
-        // The root's interleaved tile (wide sums): tf positions of 2^lc copies.
-        // A position's bins take w registers per thread; 32 registers of them
-        // fit beside the skipped slot's bookkeeping only up to 16 bytes.
-        for (int tf = 32; root && acc == kWide && tf >= 8; tf >>= 1) {
-            if (tf * w > (c->skip ? 16 : 32)) continue;
-            if (c->tune[9] == 0) break;
-            if (c->tune[1] > 0 && tf != c->tune[1]) continue;
-            // Few tiles mean many row chunks per tile, whose partial histograms
-            // a k_merge launch sums: its launch and traffic, spread per cell.
-            const int64_t il_tiles = (c->F + tf - 1) / tf;
-            const int64_t il_chunks = std::max<int64_t>(1, kRootItemsPerCu * c->n_cu / il_tiles);
-            const double merge_s = il_chunks > 1 ? 4e-6 + 2.0 * il_chunks * c->F * S * 16.0 / 5.0e12 : 0.0;
-            const double cells = std::max(1.0, (double)c->n * c->F);
-            for (int lc = 0; lc <= 4; ++lc) {
-                if (c->tune[0] >= 0 && lc != c->tune[0]) continue;
-                if ((int64_t)2 * S * (tf << lc) * 8 > budget) continue;
-                const double cost = fill_cost_il(lc, tf, c->F, w) + merge_s / cells;
-                if (cost < best || (c->tune[9] == 1 && !(found && p.il))) {
-                    best = cost;
-                    found = true;
-                    p.acc = kWide;
-                    p.lc = lc;
-                    p.tile = tf;
-                    p.lt = 0;
-                    p.il = 1;
-                    p.drain = 0;
-                }
-            }
-        }
-    }
-    if (!found) {   // one wide feature of one copy always fits (S <= HGB_MAX_SLOTS)
-        p.acc = kWide;
-        p.lc = 0;
-        p.tile = 1;
-        p.lt = p.kind == kFillRowsKind ? w : 0;
-        p.il = 0;
-    }
-    if (p.il) {
-        // the last tile may be partial; the tile itself never narrower than 8
-        p.lds_bytes = (size_t)(root_il_words(p.acc, p.tile, S, p.lc) + kFixWords) * 8;
-        p.step_rows = (int64_t)p.threads * kRootRows;
-        if (p.acc == kWide) p.drain = 0;
-        return p;
-    }
-    if (p.kind != kFillRowsKind) {
-        // rows loads cover exactly `tile` features; the others take min(NF, F)
-        while (p.tile > 1 && (p.tile >> 1) >= c->F) p.tile >>= 1;
-    }
-    p.lds_bytes = (size_t)(p.tile * feature_lds(p.acc, S, p.lc) + 8 * kFixWords);
-    p.step_rows = (int64_t)p.threads * per_thread_of(p.tile);
-    p.drain = p.acc == kPacked ? packed_drain_steps(p.threads, p.lc, per_thread_of(p.tile)) : 0;
-    return p;
+    PlanCtx pc;
+    pc.n = c->n;
+    pc.F = c->F;
+    pc.S = c->S;
+    pc.bin_bytes = c->bin_bytes;
+    pc.precision = c->precision;
+    pc.skip = c->skip;
+    pc.rm_stride = c->bins_rm ? c->rm_stride : 0;
+    pc.n_cu = c->n_cu;
+    for (int k = 0; k < 10; ++k) pc.tune[k] = c->tune[k];
+    return pc;
 }
 
 template <typename K>
@@ -873,167 +537,35 @@ hgb_status launch_zero(hgb_ctx* c, int64_t* hist, const int32_t* slots_dev, size
     return HGB_OK;
 }
 
-// Fill of a level below the root.  The level order is cut into equal shares
-// of rows, one per block (kLevelBlocksPerCu per CU, divided among the feature
-// tiles), so every CU gets the same work whatever the node sizes.  A share
-// crosses node boundaries: its block takes one item per node it touches, in
-// order.  A node that lies inside one share is stored straight into its slot;
-// a node split over several shares leaves one partial histogram per share,
-// and a merge kernel sums them into the slot (coalesced, no contended
-// atomics).
+// Fill of a level below the root: the cut (hgb_plan.h cut_level), then one
+// fill launch (which also clears the slots that merges add into, and empty
+// nodes' slots) and one merge launch for the nodes split over several blocks.
 hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::pair<int, int>>& tiles,
                       const int32_t* row_index, const std::vector<int64_t>& begin,
                       const std::vector<int64_t>& count, const std::vector<int32_t>& slots,
                       int64_t total, int64_t* hist)
 {
-    const int n_nodes = (int)begin.size();
-    const int n_tiles = (int)tiles.size();
     const int64_t node_elems = (int64_t)c->F * c->S * 2;
-    int64_t bpc = kLevelBlocksPerCu;
-    if (c->tune[5] > 0) bpc = c->tune[5];
-    const int64_t shares = std::max<int64_t>(1, bpc * c->n_cu / n_tiles);
-    int64_t align = 128;
-    if (c->tune[6] > 0) align = (c->tune[6] + 7) / 8 * 8;
-    // Balance shares by cost, not rows: a piece costs its rows plus a fixed
-    // kPieceRows (zeroing the tile, the pipeline's ramp, writing the tile
-    // out), so a share that touches many small nodes takes fewer rows.
-    int64_t piece_rows = std::max<int64_t>((int64_t)(kPieceRowsPerCell * std::min(plan.tile, c->F) * c->S), 1);
-    if (c->tune[7] >= 0) piece_rows = std::max(c->tune[7], 1);
-    int64_t nonempty = 0, built = 0;   // skipped nodes count 0 rows
-    for (int i = 0; i < n_nodes; ++i) {
-        nonempty += count[i] > 0;
-        built += count[i];
-    }
-    int64_t budget = 0;
-
-    // pieces of each share, in level order: (node, begin, end, chunk of node)
-    struct Piece {
-        int node;
-        int64_t rb, re;
-        int chunk;
-    };
-    std::vector<Piece> pieces;
-    std::vector<int64_t> share_first;
-    std::vector<int> pieces_of;
-    auto cut = [&]() {
-        pieces.clear();
-        share_first.assign(1, 0);
-        pieces_of.assign(n_nodes, 0);
-        int64_t left = budget;   // cost left in the current share
-        bool open = false;       // the current share holds a piece
-        for (int i = 0; i < n_nodes; ++i) {
-            int64_t at = begin[i];
-            const int64_t end = begin[i] + count[i];
-            while (at < end) {
-                if (open && left < piece_rows + align) {   // close the share
-                    share_first.push_back((int64_t)pieces.size());
-                    left = budget;
-                    open = false;
-                }
-                int64_t take = std::min(end - at, left - piece_rows);
-                // inside a node, cut on multiples of `align` rows
-                if (at + take < end) take = std::max<int64_t>(take / align * align, align);
-                take = std::min(take, end - at);
-                pieces.push_back({i, at, at + take, pieces_of[i]++});
-                left -= piece_rows + take;
-                open = true;
-                at += take;
-            }
-        }
-        if (open) share_first.push_back((int64_t)pieces.size());
-        return (int64_t)share_first.size() - 1;
-    };
-    // A budget close to the smallest whose cut fits one round of blocks (a
-    // larger budget never needs more shares): gallop up from the lower bound,
-    // then bisect until the bracket is within 1/256 of the budget.  The host
-    // plans every level between device steps, so the search is kept short.
-    {
-        int64_t lo = std::max<int64_t>((built + piece_rows * nonempty + shares - 1) / shares,
-                                       piece_rows + align);
-        const int64_t cap = std::max<int64_t>(built + piece_rows * (nonempty + 1) + align, lo);
-        auto fits = [&](int64_t b) {
-            budget = b;
-            return cut() <= shares;
-        };
-        int64_t hi = lo;
-        while (hi < cap && !fits(hi)) {
-            lo = hi + 1;
-            hi = std::min<int64_t>(cap, 2 * hi);
-        }
-        while (hi - lo > std::max<int64_t>(align, hi / 256)) {
-            const int64_t mid = lo + (hi - lo) / 2;
-            if (fits(mid)) hi = mid;
-            else lo = mid + 1;
-        }
-        budget = hi;
-    }
-    const int64_t n_shares = cut();
-    const int64_t len = budget;
-
-    // partial slots and merges of split nodes; slots to zero first
-    std::vector<int32_t> partial_base(n_nodes, -1);
-    std::vector<MergeEntry> merges;
-    std::vector<int32_t> zero_slots;
-    int64_t n_partial = 0;
-    for (int i = 0; i < n_nodes; ++i) {
-        if (count[i] == 0 && slots[i] >= 0) zero_slots.push_back(slots[i]);   // -1: skipped
-        if (pieces_of[i] <= 1) continue;
-        partial_base[i] = (int32_t)n_partial;
-        const int groups = (pieces_of[i] + kMergeGroup - 1) / kMergeGroup;
-        if (groups > 1) zero_slots.push_back(slots[i]);
-        for (int g = 0; g < groups; ++g) {
-            MergeEntry m{};
-            m.out_slot = slots[i];
-            m.first = (int32_t)(n_partial + (int64_t)g * kMergeGroup);
-            m.count = std::min(kMergeGroup, pieces_of[i] - g * kMergeGroup);
-            m.atomic = groups > 1 ? 1 : 0;
-            merges.push_back(m);
-        }
-        n_partial += pieces_of[i];
-    }
-    if (n_partial > INT32_MAX / 2 || (int64_t)merges.size() > 65535)
-        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many partial histograms");
-
-    // blocks (share, tile), tile fastest: the tiles of one share read the same
-    // rows, and the kernel gives each XCD a contiguous run of blocks
-    std::vector<FillItem> items;
-    std::vector<int32_t> block_first;
-    items.reserve(pieces.size() * (size_t)n_tiles);
-    block_first.reserve((size_t)n_shares * n_tiles + 1);
-    for (int64_t r = 0; r < n_shares; ++r)
-        for (int t = 0; t < n_tiles; ++t) {
-            block_first.push_back((int32_t)items.size());
-            for (int64_t k = share_first[r]; k < share_first[r + 1]; ++k) {
-                const Piece& pc = pieces[k];
-                FillItem it{};
-                if (partial_base[pc.node] >= 0) {
-                    it.out_slot = partial_base[pc.node] + pc.chunk;
-                    it.dest = kDestPartial;
-                } else {
-                    it.out_slot = slots[pc.node];
-                    it.dest = kDestStore;
-                }
-                it.row_begin = (int32_t)pc.rb;
-                it.row_end = (int32_t)pc.re;
-                it.f0_nf = tiles[t].first | (tiles[t].second << 16);
-                items.push_back(it);
-            }
-        }
-    block_first.push_back((int32_t)items.size());
+    const PlanCtx pc = plan_ctx(c);
+    LevelCut cut;
+    if (const char* msg = cut_level(&pc, plan, tiles, begin, count, slots, &cut))
+        return fail(c, HGB_E_UNSUPPORTED, "%s", msg);
+    const std::vector<FillItem>& items = cut.items;
+    const std::vector<int32_t>& block_first = cut.block_first;
+    const std::vector<MergeEntry>& merges = cut.merges;
+    const std::vector<int32_t>& zero_slots = cut.zero_slots;
     const int n_blocks = (int)(block_first.size() - 1);
-    if (items.size() > (size_t)INT32_MAX / 8 || n_blocks > INT32_MAX / 8)
-        return fail(c, HGB_E_UNSUPPORTED, "build_level: too many fill items");
     if (c->debug_plan)
         std::fprintf(stderr,
                      "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d il %d drain %d chunk %lld items %zu "
                      "lds %zu blocks %d partials %lld merges %zu\n",
                      (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.il, plan.drain,
-                     (long long)len, items.size(), plan.lds_bytes, n_blocks, (long long)n_partial,
+                     (long long)cut.budget, items.size(), plan.lds_bytes, n_blocks, (long long)cut.n_partial,
                      merges.size());
 
     hgb_status st = HGB_OK;
-    if (n_partial > 0) {
-        st = grow(c, &c->partial, &c->partial_cap, n_partial * node_elems);
+    if (cut.n_partial > 0) {
+        st = grow(c, &c->partial, &c->partial_cap, cut.n_partial * node_elems);
         if (st != HGB_OK) return st;
     }
     // the row-major fill reads each row's (g, h) itself; the others read
@@ -1540,103 +1072,30 @@ hgb_status hgb_build_level(hgb_ctx* c, const int32_t* row_index, const int32_t* 
     // The root reads rows in order; other levels read through the row index,
     // from the row-major copy when there is one.
     const bool rm = !root && c->bins_rm != nullptr;
-    const FillPlan plan0 = plan_fill(c, root, rm);
-
-    // Feature tiles (f0, width).  Root tiles have exactly the kernel's width:
-    // full tiles of plan.tile, then the remainder split into powers of two,
-    // each width its own launch.  Level tiles are plan.tile wide, the last one
-    // possibly narrower (those kernels take the width at run time).
-    std::vector<std::pair<int, int>> tiles;
-    FillPlan plan = plan0;
-    if (root && !plan.il) {
-        // equal tiles when a divisor of F close to the planned width exists
-        for (int d = plan.tile; d >= 1 && 2 * d > plan.tile; --d)
-            if (c->F % d == 0) {
-                plan.tile = d;
-                break;
-            }
-    }
-    {
-        int f0 = 0;
-        for (; f0 + plan.tile <= c->F; f0 += plan.tile) tiles.emplace_back(f0, plan.tile);
-        if (f0 < c->F) {
-            if (root && !plan.il) {
-                for (int wdt = plan.tile >> 1; wdt >= 1; wdt >>= 1)
-                    if (f0 + wdt <= c->F) {
-                        tiles.emplace_back(f0, wdt);
-                        f0 += wdt;
-                    }
-            } else {
-                tiles.emplace_back(f0, c->F - f0);
-            }
-        }
-    }
-    const int n_tiles = (int)tiles.size();
+    const PlanCtx pc = plan_ctx(c);
+    FillPlan plan = plan_fill(&pc, root, rm);
+    const std::vector<std::pair<int, int>> tiles = feature_tiles(&pc, plan, root);
     for (const auto& t : tiles)
         if (t.second < 1 || (root && t.second > (plan.il ? plan.tile : 8)) || t.first + t.second > c->F)
             return fail(c, HGB_E_DEVICE, "build_level: internal error in the tile plan");
 
     if (!root) return fill_level(c, plan, tiles, row_index, begin, count, slots, total, hist);
 
-    // Root items: about (items per CU) x (CUs) items of equal size, a multiple
-    // of 128 rows, which keeps the bin and (g, h) loads cache-line aligned.
-    int64_t ipc = kRootItemsPerCu;
-    if (c->tune[2] > 0) ipc = c->tune[2];
-    const int64_t target = ipc * c->n_cu;
-    int64_t align = 128;
-    if (c->tune[6] > 0) align = (c->tune[6] + 7) / 8 * 8;
-    // Equal items, at most `target` of them: one item more than a multiple of
-    // the resident blocks would cost a whole extra round.
-    const int64_t chunks = std::max<int64_t>(1, target / n_tiles);
-    int64_t ch = (total + chunks - 1) / chunks;
-    ch = std::max<int64_t>((ch + align - 1) / align * align, align);
-    const int64_t nchunks = (total + ch - 1) / ch;
-
-    // The interleaved tile covers many features, so a tile's chunks are
-    // many: each writes a partial histogram, summed by k_merge in groups of
-    // kMergeGroup (atomically when there are several groups).  Feature-major
-    // tiles have few chunks each and add theirs atomically.
-    const bool use_partial = plan.il && nchunks > 1;
-    std::vector<MergeEntry> merges;
-    if (use_partial) {
-        const int64_t n_groups = (nchunks + kMergeGroup - 1) / kMergeGroup;
-        for (int64_t g = 0; g < n_groups; ++g) {
-            MergeEntry m{};
-            m.out_slot = slots[0];
-            m.first = (int32_t)(g * kMergeGroup);
-            m.count = (int32_t)std::min<int64_t>(kMergeGroup, nchunks - g * kMergeGroup);
-            m.atomic = n_groups > 1 ? 1 : 0;
-            merges.push_back(m);
-        }
-        hgb_status gst = grow(c, &c->partial, &c->partial_cap, nchunks * (int64_t)c->F * c->S * 2);
+    RootCut rc;
+    cut_root(&pc, plan, tiles, total, slots[0], &rc);
+    std::vector<FillItem>* groups = rc.groups;
+    const std::vector<MergeEntry>& merges = rc.merges;
+    const bool zero_root = rc.zero_root;
+    if (rc.use_partial) {
+        hgb_status gst = grow(c, &c->partial, &c->partial_cap, rc.n_chunks * (int64_t)c->F * c->S * 2);
         if (gst != HGB_OK) return gst;
     }
-    const bool zero_root = nchunks > 1 && (!use_partial || merges.size() > 1);
-
-    // Item order (chunk, tile): the tiles of one row chunk read the same
-    // (g, h) rows, and the kernel gives each XCD a contiguous run of items.
-    // groups[w]: the items of tiles of width w, one launch each; with the
-    // interleaved tile every item (the last tile possibly partial) is in
-    // groups[0], one launch.
-    std::vector<FillItem> groups[9];
-    size_t n_items = 0;
-    for (int64_t j = 0; j < nchunks; ++j)
-        for (int t = 0; t < n_tiles; ++t) {
-            FillItem it{};
-            it.out_slot = use_partial ? (int32_t)j : slots[0];
-            it.row_begin = (int32_t)(j * ch);
-            it.row_end = (int32_t)std::min<int64_t>((j + 1) * ch, total);
-            it.f0_nf = tiles[t].first | (tiles[t].second << 16);
-            it.dest = use_partial ? kDestPartial : (nchunks > 1 ? kDestAtomic : kDestStore);
-            groups[plan.il ? 0 : tiles[t].second].push_back(it);
-            ++n_items;
-        }
     if (c->debug_plan)
         std::fprintf(stderr,
                      "[hgb] fill kind %d acc %d copies %d tile %d lt %d ra %d il %d drain %d chunk %lld items %zu "
                      "lds %zu\n",
                      (int)plan.kind, plan.acc, 1 << plan.lc, plan.tile, plan.lt, plan.ra, plan.il, plan.drain,
-                     (long long)ch, n_items, plan.lds_bytes);
+                     (long long)rc.chunk, rc.n_items, plan.lds_bytes);
     // one upload: the root's slot (to zero before atomic merges), each
     // width's items, then the merges (each part 256-byte aligned)
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
@@ -2025,14 +1484,8 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
 
     // chunks of each node's rows, in node order
     std::vector<PartItem> items;
-    std::vector<int32_t> first(n_nodes + 1);
-    for (int i = 0; i < n_nodes; ++i) {
-        first[i] = (int32_t)items.size();
-        // 64-bit steps: the last chunk of a node may end within kPartChunk of 2^31
-        for (int64_t b = offs[i]; b < offs[i + 1]; b += kPartChunk)
-            items.push_back({i, (int32_t)b, (int32_t)std::min<int64_t>(b + kPartChunk, offs[i + 1]), offs[i]});
-    }
-    first[n_nodes] = (int32_t)items.size();
+    std::vector<int32_t> first;
+    part_chunks(offs, n_nodes, &items, &first);
     const int64_t n_items = (int64_t)items.size();
 
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };

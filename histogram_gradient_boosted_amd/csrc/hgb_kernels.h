@@ -7,9 +7,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hgb_layout.h"
+
 namespace hgb {
 
-constexpr int kWave = 64;
 constexpr uint32_t kErrRowIndex = 1u;
 
 // 64-bit values across a wave (two 32-bit shuffles each).
@@ -432,33 +433,7 @@ __global__ __launch_bounds__(256) void k_gather(const int2* __restrict__ q,
     }
 }
 
-// One unit of fill work: rows [row_begin, row_end) of the level order, features
-// [f0, f0 + nf), accumulated for one node.  `dest` says where the sums go:
-// stored into slot out_slot of the level buffer (kDestStore), stored into
-// slot out_slot of the partial buffer (kDestPartial: a node split over several
-// items, merged afterwards), or added there with int64 atomics (kDestAtomic).
-enum { kDestStore = 0, kDestPartial = 1, kDestAtomic = 2 };
-struct FillItem {
-    int32_t out_slot;
-    int32_t row_begin;
-    int32_t row_end;
-    int32_t f0_nf;       // f0 | (nf << 16)
-    int32_t dest;
-    int32_t pad[3];
-};
-
-// Merge of a node split over several items: the sum of `count` partial slots
-// from `first` on, stored into (or, for a node merged in several groups,
-// added with atomics to) slot out_slot of the level buffer.
-struct MergeEntry {
-    int32_t out_slot;
-    int32_t first;
-    int32_t count;
-    int32_t atomic;
-};
-
 // A short merge list travels in the kernel's arguments (none to fetch).
-constexpr int kMergeInline = 128;
 struct MergeInline {
     MergeEntry e[kMergeInline];
 };
@@ -524,18 +499,9 @@ __device__ inline int xcd_item(int bid, int n_items)
 // covers its whole node, an int64 atomic add otherwise.  Integer adds make the
 // result independent of the order in which lanes, waves and blocks land.
 //
-// Two accumulation modes:
-//   kWide    two ds_add_u64 per cell, one per component (gradient and hessian
-//            planes, [nf][2][S][C] u64).  Exact for any fixed-point precision.
-//   kPacked  one ds_add_u64 per cell on qh * 2^32 + qg ([nf][S][C] u64).  Each
-//            copy-slot sums at most kPackedRowsPerCopy rows of |q| <= 2^19
-//            between drains into an int64 accumulator, so the low half never
-//            leaves the int32 range and both sums decode exactly:
-//            G = sign-extended low 32 bits, H = (V - G) / 2^32.
+// Two accumulation modes, kWide and kPacked (hgb_layout.h): [nf][2][S][C] u64
+// gradient and hessian planes, or [nf][S][C] packed u64 words.
 // ---------------------------------------------------------------------------
-enum { kWide = 0, kPacked = 1 };
-constexpr int kPackedMaxBits = 19;
-constexpr int kPackedRowsPerCopy = 4095;
 
 struct CellVal {
     unsigned long long a, b;
@@ -620,7 +586,6 @@ __device__ inline void lds_drain(unsigned long long* lds, int nf, int S, int pla
 // lanes of a wave to one LDS word, which serializes the atomics; here it costs
 // nothing.  Exact: the recovery is an integer subtraction.
 // ---------------------------------------------------------------------------
-constexpr int kFixWords = 2 + 2 * 32;   // the item's row totals, then (g, h) per feature (<= 32)
 
 // The slot that rotated value s of a feature with rotation rot stands for.
 __device__ inline int unrotate(int s, int rot, int S)
@@ -786,18 +751,12 @@ __device__ inline void lds_finish_il(const unsigned long long* lds, int nf, int 
     }
 }
 
-// LDS words of a tile: the copies, plus the packed accumulator.
-__host__ __device__ inline int tile_words(int acc_mode, int nf, int S, int lc)
-{
-    return acc_mode == kWide ? nf * 2 * (S << lc) : nf * (S << lc) + nf * S * 2;
-}
-
 // Root fill: the level's one node holds every row in order, so each thread
 // reads 4 consecutive rows per step -- a 16-byte (g, h) load per two rows and
 // one 4- or 8-byte bin load per feature -- and loads the next step while it
 // adds the current one.  NF features per block.  (4 rows beat 8 and 2 on the
 // MI355X: fewer registers in flight per wave, the LDS adds interleave better.)
-constexpr int kRootRows = 4;
+// (kRootRows = 4, hgb_layout.h)
 
 // A thread's kRootRows consecutive bins of one feature, from one load.
 template <typename BinT>
@@ -996,16 +955,6 @@ __device__ inline void rotate_root_bins(RootBins<BinT> (&b)[TF], int k)
     }
 }
 
-// LDS words of the interleaved root tile before its fixed words: the copies,
-// and for packed sums at least the one-copy wide layout the finish reads.
-__host__ __device__ inline int root_il_words(int acc_mode, int tf, int S, int lc)
-{
-    return acc_mode == kWide ? 2 * S * (tf << lc) : (S * (tf << lc) > 2 * S * tf ? S * (tf << lc) : 2 * S * tf);
-}
-
-// Register cells per thread of the packed interleaved root: 1024 threads
-// hold the 16 positions of up to 256 slots (one-byte bins).
-constexpr int kRootIlPackedCells = 4;
 
 template <typename BinT, int TF, bool SKIP, int ACC>
 __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ bins, int64_t n,
@@ -1213,10 +1162,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
 // (g, h) loads stay coalesced and only the bin loads scatter, in a two-stage
 // pipeline: the next step's indices are in flight while this step's bins
 // load, and this step's bins while the previous step adds.
-constexpr int kLevelEntries = 8;
-// Entries per thread and step of the feature-major level fill with NF features
-// (fewer for wide tiles, so the step's bins stay in registers).
-__host__ __device__ constexpr int cols_entries(int nf) { return nf >= 8 ? 4 : kLevelEntries; }
+// (kLevelEntries, cols_entries: hgb_layout.h)
 
 template <int E>
 struct Entries {
@@ -1762,7 +1708,6 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
 // subtract_siblings: other = parent - built, for every pair, elementwise.
 // ---------------------------------------------------------------------------
 // A small plan travels in the kernel's arguments (no upload).
-constexpr int kSubtractInlinePairs = 256;
 struct SubtractInline {
     int32_t v[2 * kSubtractInlinePairs];   // per pair: parent slot, built side
 };
@@ -2008,8 +1953,7 @@ __device__ inline WaveBest wave_scan(const long long* __restrict__ hf, const Lan
 // (q + 1) * 64 * PER) in contiguous lane runs of PER <= 4.  A single wave
 // would hold up to 16 bins per lane and leave the chip with few waves; here
 // the slices' sums meet in LDS (the carry into each slice and the feature's
-// totals) and each wave scans its own slice.
-constexpr int kSliceWaves = 4;
+// totals) and each wave scans its own slice.  (kSliceWaves: hgb_layout.h)
 
 template <int PER>
 __device__ inline void load_slice_slots(const long long* __restrict__ hf, int n_bins, int has_missing,
@@ -2274,8 +2218,7 @@ struct SplitOut {
 // One block per node (256 or 1024 threads, a power of two): the best feature,
 // scanning features in order per thread -- four entries loaded before any is
 // compared -- and then reducing across threads with the same (gain, feature)
-// order.
-constexpr int kSplitReduceMaxThreads = 1024;
+// order.  (kSplitReduceMaxThreads: hgb_layout.h)
 __global__ __launch_bounds__(kSplitReduceMaxThreads) void k_split_reduce(
     const FeatureBest* __restrict__ best, const long long* __restrict__ totals, int n_entries,
     SplitOut* __restrict__ out)
@@ -2560,15 +2503,8 @@ __global__ __launch_bounds__(256) void k_level_records(const long long* __restri
 // a split.  Three passes over fixed-size chunks of each node's rows: count the
 // rows going left per chunk; scan the counts per node and the output extents
 // over nodes; scatter each row to its place.
+// (kPartThreads, kPartChunk, PartItem: hgb_layout.h)
 // ---------------------------------------------------------------------------
-constexpr int kPartThreads = 1024;   // threads of a count or scatter block (256 measured slower)
-constexpr int kPartChunk = 8192;
-
-struct PartItem {
-    int32_t node;
-    int32_t begin, end;   // positions [begin, end) of the node's rows
-    int32_t node_begin;   // the node's first position
-};
 
 __device__ inline bool part_left(int v, int n_bins, const SplitOut& sp)
 {

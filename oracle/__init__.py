@@ -21,6 +21,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _HDR = os.path.join(_HERE, "oracle.h")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1: build and load a copy instrumented with the address and
+# undefined-behaviour sanitizers (the process must preload the ASan runtime;
+# tests/test_sanitizers.py runs the oracle's tests that way).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE", "") == "1"
+if _SANITIZE:
+    _LIB = os.path.join(_HERE, "liboracle_san.so")
 
 OK = 0
 E_INVALID = 1
@@ -53,6 +59,9 @@ def build(force: bool = False) -> str:
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
                "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        if _SANITIZE:
+            cmd[1:1] = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
