@@ -361,6 +361,10 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
     log(f"[bench] workload {config}: {w.n_rows} x {w.n_features}, generated in {time.time() - t0:.1f}s")
     ctx = binding.Context(0)
     ctx.set_precision(precision)
+    # begin_tree enqueues its passes and returns: no host round trip between
+    # a tree's start and its first level (the check of the maxima happens at
+    # the next sync)
+    ctx.set_async_begin(True)
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     objective = resolve_objective(w, objective_arg)
     if objective is None:

@@ -35,7 +35,7 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
             "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
             "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized",
-            "hgb_find_level_split", "hgb_find_splits_noalloc")
+            "hgb_find_level_split", "hgb_find_splits_noalloc", "hgb_set_async_begin")
 
 # hgb_objective
 OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
@@ -85,6 +85,8 @@ def load():
     lib.hgb_begin_tree_objective.restype = c_int
     lib.hgb_copy_quantized.argtypes = [vp, vp]
     lib.hgb_copy_quantized.restype = c_int
+    lib.hgb_set_async_begin.argtypes = [vp, c_int]
+    lib.hgb_set_async_begin.restype = c_int
     lib.hgb_set_precision.argtypes = [vp, i32]
     lib.hgb_set_precision.restype = c_int
     lib.hgb_get_scales.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -250,6 +252,11 @@ class Context:
         q = self._dev(out, "out", torch.int32, 2 * self.n_rows)
         self._check(self._lib.hgb_copy_quantized(self._h, q), "copy_quantized")
         return out
+
+    def set_async_begin(self, on: bool = True):
+        """begin_tree without waiting for the maxima; a non-finite value is
+        then reported by the next sync()."""
+        self._check(self._lib.hgb_set_async_begin(self._h, int(bool(on))), "set_async_begin")
 
     def set_precision(self, bits: int):
         """Fixed-point precision (bits below the largest |value|) of the next begin_tree."""

@@ -85,6 +85,13 @@ struct hgb_ctx {
     int precision = kDefaultPrecision;
     int k_g = 0, k_h = 0;
     bool have_tree = false;
+    // hgb_set_async_begin: begin_tree returns without waiting for the maxima;
+    // the host reads them (and checks them) at the next call that needs them
+    bool async_begin = false;
+    bool scales_pending = false;          // the current tree's maxima are not read yet
+    int tree_precision = 30;              // the precision the current tree was started with
+    hgb_status deferred = HGB_OK;         // a started tree's non-finite values, for hgb_sync
+    std::string deferred_msg;
 
     // level scratch
     int2* gh = nullptr;
@@ -109,7 +116,8 @@ struct hgb_ctx {
     // this device's copy of the no-allocation scratch array (set up by hgb_create)
     unsigned char* noalloc_scratch = nullptr;
 
-    // small device words: [0..1] max patterns, [2] error flags
+    // small device words: [0..1] max patterns, [2] error flags, [4..11] the
+    // quantize scales 2^k and the split scales 2^-k (four doubles)
     uint32_t* dev_words = nullptr;
     uint32_t* host_words = nullptr;   // pinned
     uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
@@ -333,6 +341,11 @@ int grid_for(int64_t work, int threads, int cap)
     int64_t g = (work + threads - 1) / threads;
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
+
+// The current tree's inverse scales 2^-k_g, 2^-k_h on the device, written by
+// k_max_final: the split kernels read them there, so no host round trip
+// stands between begin_tree and a level's launches.
+const double* inv_scales(const hgb_ctx* c) { return (const double*)(c->dev_words + 4) + 2; }
 
 // What the planner (hgb_plan.h) reads of a context.
 PlanCtx plan_ctx(const hgb_ctx* c)
@@ -635,13 +648,60 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
 
 }  // namespace
 
+// The current tree's exponents from the maxima k_max_final wrote into pinned
+// host memory (the event host_ready has passed).  Returns nullptr, or what
+// was not finite.
+static const char* read_scales(hgb_ctx* c)
+{
+    const uint32_t pg = c->host_words[0], ph = c->host_words[1];
+    if (pg >= 0x7f800000u) return "begin_tree: NaN or Inf gradient";
+    if (ph >= 0x7f800000u) return "begin_tree: NaN, Inf or negative hessian";
+    int k[2];
+    const uint32_t pat[2] = {pg, ph};
+    for (int i = 0; i < 2; ++i) {
+        float m;
+        std::memcpy(&m, &pat[i], 4);
+        if (m == 0.0f) {
+            k[i] = 0;
+        } else {
+            int e = 0;
+            (void)std::frexp((double)m, &e);
+            k[i] = c->tree_precision - e;
+        }
+    }
+    c->k_g = k[0];
+    c->k_h = k[1];
+    return nullptr;
+}
+
+// A tree started by an asynchronous begin_tree: wait for its maxima, keep
+// its exponents, and hold a non-finite value for the next hgb_sync.
+static hgb_status resolve_scales(hgb_ctx* c)
+{
+    if (!c->scales_pending) return HGB_OK;
+    const hgb_status st = poll_event(c, c->host_ready);
+    if (st != HGB_OK) return st;
+    c->scales_pending = false;
+    if (const char* bad = read_scales(c)) {
+        c->deferred = HGB_E_NONFINITE;
+        c->deferred_msg = bad;
+    }
+    return HGB_OK;
+}
+
 // Start a tree from any row source: exact maxima of |g| and of h, the scales
-// from their exponents (one stream sync), then the quantize pass, which
-// re-derives each row's (g, h) from the source.
+// from their exponents (on the device, for the quantize pass and the split
+// kernels), then the quantize pass, which re-derives each row's (g, h) from
+// the source.  The host reads the maxima back to check them and keep the
+// exponents: right away (one wait), or, with async_begin, when a later call
+// needs them.
 template <class Src>
 static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
 {
     HGB_HIP(c, hipSetDevice(c->device));
+    // the previous tree's maxima, before this tree's overwrite them
+    hgb_status rst = resolve_scales(c);
+    if (rst != HGB_OK) return rst;
     c->have_tree = false;
     hgb_status st = grow(c, &c->q, &c->q_cap, c->n);
     if (st != HGB_OK) return st;
@@ -666,27 +726,15 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
             src, c->n, vec, (const double*)(c->dev_words + 4), c->q);
         HGB_LAUNCHED(c, "k_quantize");
     }
+    c->tree_precision = c->precision;
+    if (c->async_begin) {
+        c->scales_pending = true;
+        c->have_tree = true;
+        return HGB_OK;
+    }
     hgb_status wst = poll_event(c, c->host_ready);
     if (wst != HGB_OK) return wst;
-    const uint32_t pg = c->host_words[0], ph = c->host_words[1];
-    if (pg >= 0x7f800000u) return fail(c, HGB_E_NONFINITE, "begin_tree: NaN or Inf gradient");
-    if (ph >= 0x7f800000u)
-        return fail(c, HGB_E_NONFINITE, "begin_tree: NaN, Inf or negative hessian");
-    int k[2];
-    const uint32_t pat[2] = {pg, ph};
-    for (int i = 0; i < 2; ++i) {
-        float m;
-        std::memcpy(&m, &pat[i], 4);
-        if (m == 0.0f) {
-            k[i] = 0;
-        } else {
-            int e = 0;
-            (void)std::frexp((double)m, &e);
-            k[i] = c->precision - e;
-        }
-    }
-    c->k_g = k[0];
-    c->k_h = k[1];
+    if (const char* bad = read_scales(c)) return fail(c, HGB_E_NONFINITE, "%s", bad);
     c->have_tree = true;
     return HGB_OK;
 }
@@ -836,9 +884,25 @@ hgb_status hgb_sync(hgb_ctx* c)
     HGB_HIP(c, hipSetDevice(c->device));
     HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
                               c->stream));
-    const hgb_status st = wait_here(c, &c->host_ready);
+    hgb_status st = wait_here(c, &c->host_ready);
     if (st != HGB_OK) return st;
-    return take_flags(c);
+    st = resolve_scales(c);
+    if (st != HGB_OK) return st;
+    st = take_flags(c);
+    if (c->deferred != HGB_OK) {   // reported once, before a skipped row index
+        const hgb_status d = c->deferred;
+        c->deferred = HGB_OK;
+        return fail(c, d, "%s", c->deferred_msg.c_str());
+    }
+    return st;
+}
+
+hgb_status hgb_set_async_begin(hgb_ctx* c, int enable)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    c->async_begin = enable != 0;
+    return HGB_OK;
 }
 
 hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_device,
@@ -860,6 +924,10 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
         return fail(c, HGB_E_UNSUPPORTED, "upload_bins: %d slots exceed the LDS plan (%d)", S,
                     HGB_MAX_SLOTS);
     HGB_HIP(c, hipSetDevice(c->device));
+    {   // the current tree's maxima first: this call reuses their host words
+        const hgb_status rst = resolve_scales(c);
+        if (rst != HGB_OK) return rst;
+    }
     c->have_tree = false;
     c->have_data = false;
     const int64_t total = (int64_t)n_rows * n_features;
@@ -1007,15 +1075,23 @@ hgb_status hgb_set_precision(hgb_ctx* c, int32_t bits)
     c->err.clear();
     if (bits < 1 || bits > 30)
         return fail(c, HGB_E_INVALID, "set_precision: bits must be in [1, 30]");
+    const hgb_status rst = resolve_scales(c);
+    if (rst != HGB_OK) return rst;
     c->precision = bits;
     c->have_tree = false;
     return HGB_OK;
 }
 
-hgb_status hgb_get_scales(const hgb_ctx* c, int32_t* k_g, int32_t* k_h)
+hgb_status hgb_get_scales(const hgb_ctx* cc, int32_t* k_g, int32_t* k_h)
 {
-    if (!c || !k_g || !k_h) return HGB_E_INVALID;
+    if (!cc || !k_g || !k_h) return HGB_E_INVALID;
+    // reading the scales of an asynchronously started tree waits for them
+    // (the context is logically unchanged)
+    hgb_ctx* c = const_cast<hgb_ctx*>(cc);
     if (!c->have_tree) return HGB_E_STATE;
+    const hgb_status st = resolve_scales(c);
+    if (st != HGB_OK) return st;
+    if (c->deferred != HGB_OK) return c->deferred;   // still reported by the next hgb_sync
     *k_g = c->k_g;
     *k_h = c->k_h;
     return HGB_OK;
@@ -1247,12 +1323,12 @@ static hgb_status launch_find_splits(hgb_ctx* c, const SplitShape& sh, const int
     dim3 grid((unsigned)sh.n_entries, (unsigned)n_nodes);
 #define HGB_SPLIT(PER)                                                                              \
     k_split_feature<PER><<<grid, waves * kWave, 0, c->stream>>>(                                    \
-        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
-        std::ldexp(1.0, -c->k_h), lambda, gamma, best, totals)
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, inv_scales(c), lambda, gamma, best, \
+        totals)
 #define HGB_SPLIT_SLICED(PER)                                                                       \
     k_split_feature_sliced<PER><<<grid, kSliceWaves * kWave, 0, c->stream>>>(                       \
-        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
-        std::ldexp(1.0, -c->k_h), lambda, gamma, best, totals)
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, inv_scales(c), lambda, gamma, best, \
+        totals)
     const int per = sh.per;
     if (sh.sliced) {
         if (per <= 2 * kSliceWaves) HGB_SPLIT_SLICED(2);
@@ -1347,8 +1423,8 @@ hgb_status hgb_find_level_split(hgb_ctx* c, const int64_t* hist, int32_t n_nodes
         const bool aligned = ((uintptr_t)hist & 15) == 0;
 #define HGB_LEVEL(PER)                                                                              \
     k_level_gain<PER><<<grid, waves * kWave, 0, c->stream>>>(                                       \
-        (const long long*)hist, c->F, c->B, c->S, c->has_missing, std::ldexp(1.0, -c->k_g),         \
-        std::ldexp(1.0, -c->k_h), lambda, gamma, c->level_terms)
+        (const long long*)hist, c->F, c->B, c->S, c->has_missing, inv_scales(c), lambda, gamma,      \
+        c->level_terms)
         if (!aligned || per > 16) HGB_LEVEL(0);
         else if (per <= 1) HGB_LEVEL(1);
         else if (per <= 2) HGB_LEVEL(2);
@@ -1421,17 +1497,17 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     }
     const int waves = 4;
     dim3 grid((unsigned)n_entries, (unsigned)n_pairs);
-    const double sg = std::ldexp(1.0, -c->k_g), sh = std::ldexp(1.0, -c->k_h);
+    const double* sc = inv_scales(c);
     {
         ProfScope ps(c, HGB_KERNEL_SPLIT);
 #define HGB_SUBSPLIT(PER)                                                                          \
     k_subtract_split<PER><<<grid, waves * kWave, 0, c->stream>>>(                                  \
         (const long long*)parent, (long long*)child, plan_dev, inl, c->F, c->B, c->S, c->has_missing, \
-        sg, sh, lambda, gamma, c->best, c->totals)
+        sc, lambda, gamma, c->best, c->totals)
 #define HGB_SUBSPLIT_SLICED(PER)                                                                   \
     k_subtract_split_sliced<PER><<<grid, kSliceWaves * kWave, 0, c->stream>>>(                     \
         (const long long*)parent, (long long*)child, plan_dev, inl, c->F, c->B, c->S, c->has_missing, \
-        sg, sh, lambda, gamma, c->best, c->totals)
+        sc, lambda, gamma, c->best, c->totals)
         if (sliced) {
             if (per <= 2 * kSliceWaves) HGB_SUBSPLIT_SLICED(2);
             else HGB_SUBSPLIT_SLICED(4);

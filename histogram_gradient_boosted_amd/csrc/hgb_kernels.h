@@ -226,7 +226,19 @@ __device__ inline double scale_of_max(uint32_t pat, int precision)
     return ldexp(1.0, precision - e);
 }
 
-// out[0..1]: the maxima's bit patterns; scales[0..1]: their scales (above).
+// Its inverse 2^-k, the factor that turns a fixed-point sum back into a value
+// (1 for M = 0; 0 for Inf or NaN, as above).
+__device__ inline double inv_scale_of_max(uint32_t pat, int precision)
+{
+    if (pat >= 0x7f800000u) return 0.0;
+    if (pat == 0u) return 1.0;
+    int e = 0;
+    (void)frexp((double)__uint_as_float(pat), &e);
+    return ldexp(1.0, e - precision);
+}
+
+// out[0..1]: the maxima's bit patterns; scales[0..1]: their scales 2^k (above),
+// scales[2..3]: the inverses 2^-k that the split kernels read.
 __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ part, int n_blocks,
                                                    uint32_t* __restrict__ out, int precision,
                                                    double* __restrict__ scales,
@@ -255,6 +267,8 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
         host_out[1] = red[1][0];
         scales[0] = scale_of_max(red[0][0], precision);
         scales[1] = scale_of_max(red[1][0], precision);
+        scales[2] = inv_scale_of_max(red[0][0], precision);
+        scales[3] = inv_scale_of_max(red[1][0], precision);
     }
 }
 
@@ -2026,11 +2040,12 @@ __device__ inline WaveBest wave_feature_best(const long long* __restrict__ hf, i
 template <int PER>
 __global__ __launch_bounds__(256) void k_split_feature(const long long* __restrict__ hist,
                                                        int n_features, int n_bins, int S,
-                                                       int has_missing, double scale_g,
-                                                       double scale_h, double lam, double gamma,
+                                                       int has_missing, const double* __restrict__ inv_scale,
+                                                       double lam, double gamma,
                                                        FeatureBest* __restrict__ best,
                                                        long long* __restrict__ totals)
 {
+    const double scale_g = inv_scale[0], scale_h = inv_scale[1];   // 2^-k, from k_max_final
     __shared__ FeatureBest s_fb[256 / kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -2063,10 +2078,11 @@ __global__ __launch_bounds__(256) void k_subtract_split(const long long* __restr
                                                         const int32_t* __restrict__ plan,
                                                         const SubtractInline inl, int n_features,
                                                         int n_bins, int S, int has_missing,
-                                                        double scale_g, double scale_h, double lam,
+                                                        const double* __restrict__ inv_scale, double lam,
                                                         double gamma, FeatureBest* __restrict__ best,
                                                         long long* __restrict__ totals)
 {
+    const double scale_g = inv_scale[0], scale_h = inv_scale[1];   // 2^-k, from k_max_final
     static_assert(PER > 0, "the fused pass keeps the slots in registers");
     __shared__ FeatureBest s_fb[2][256 / kWave];   // [0] the built child, [1] the other
     const int lane = threadIdx.x & (kWave - 1);
@@ -2126,9 +2142,11 @@ __global__ __launch_bounds__(256) void k_subtract_split(const long long* __restr
 // to best[node][feature]; node totals from feature 0.
 template <int PER>
 __global__ __launch_bounds__(kSliceWaves * kWave) void k_split_feature_sliced(
-    const long long* __restrict__ hist, int n_features, int n_bins, int S, int has_missing, double scale_g,
-    double scale_h, double lam, double gamma, FeatureBest* __restrict__ best, long long* __restrict__ totals)
+    const long long* __restrict__ hist, int n_features, int n_bins, int S, int has_missing,
+    const double* __restrict__ inv_scale, double lam, double gamma, FeatureBest* __restrict__ best,
+    long long* __restrict__ totals)
 {
+    const double scale_g = inv_scale[0], scale_h = inv_scale[1];   // 2^-k, from k_max_final
     __shared__ long long s_sum[2 * kSliceWaves];
     __shared__ FeatureBest s_fb[kSliceWaves];
     const int lane = threadIdx.x & (kWave - 1);
@@ -2158,9 +2176,11 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void k_split_feature_sliced(
 template <int PER>
 __global__ __launch_bounds__(kSliceWaves * kWave) void k_subtract_split_sliced(
     const long long* __restrict__ parent, long long* __restrict__ child, const int32_t* __restrict__ plan,
-    const SubtractInline inl, int n_features, int n_bins, int S, int has_missing, double scale_g,
-    double scale_h, double lam, double gamma, FeatureBest* __restrict__ best, long long* __restrict__ totals)
+    const SubtractInline inl, int n_features, int n_bins, int S, int has_missing,
+    const double* __restrict__ inv_scale, double lam, double gamma, FeatureBest* __restrict__ best,
+    long long* __restrict__ totals)
 {
+    const double scale_g = inv_scale[0], scale_h = inv_scale[1];   // 2^-k, from k_max_final
     __shared__ long long s_sum[2][2 * kSliceWaves];
     __shared__ FeatureBest s_fb[2][kSliceWaves];   // [0] the built child, [1] the other
     const int lane = threadIdx.x & (kWave - 1);
@@ -2306,10 +2326,11 @@ struct LevelBest {
 
 template <int PER>
 __global__ __launch_bounds__(256) void k_level_gain(const long long* __restrict__ hist, int n_features,
-                                                    int n_bins, int S, int has_missing, double scale_g,
-                                                    double scale_h, double lam, double gamma,
+                                                    int n_bins, int S, int has_missing,
+                                                    const double* __restrict__ inv_scale, double lam, double gamma,
                                                     double* __restrict__ terms)
 {
+    const double scale_g = inv_scale[0], scale_h = inv_scale[1];   // 2^-k, from k_max_final
     const int f = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
     const int node = blockIdx.y;
     if (f >= n_features) return;

@@ -94,9 +94,10 @@ const char* hgb_last_error(const hgb_ctx* ctx);
 
 /* Block until the context's stream has drained ([bonsai-10] "The device
  * context lifecycle": the host reads results once the level's work is done).
- * Returns HGB_E_INVALID if a kernel met a row index outside [0, n) since the
- * previous hgb_sync (those entries were skipped), HGB_E_DEVICE on a runtime
- * error, else HGB_OK. */
+ * Returns HGB_E_NONFINITE if a tree started asynchronously since the previous
+ * hgb_sync had a non-finite value (hgb_set_async_begin), else HGB_E_INVALID
+ * if a kernel met a row index outside [0, n) since the previous hgb_sync
+ * (those entries were skipped), HGB_E_DEVICE on a runtime error, else HGB_OK. */
 hgb_status hgb_sync(hgb_ctx* ctx);
 
 /*
@@ -130,11 +131,32 @@ hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on
  * the context's precision (hgb_set_precision, default 30).
  *
  * grad_dev, hess_dev: fp32 [n_rows] device arrays (n_rows of upload_bins).
- * Synchronizes the stream once (the scales are needed on the host).
+ * Waits once for the two maxima, to check them (unless hgb_set_async_begin
+ * is on).  The scales stay on the device for the later kernels.
  * Errors: HGB_E_STATE before upload_bins; HGB_E_NONFINITE for a NaN/Inf value
  *         or a hessian < 0 (-0.0 counts as 0) -- no tree is started then.
+ *         With hgb_set_async_begin on, the non-finite check is deferred (see
+ *         there).
  */
 hgb_status hgb_begin_tree(hgb_ctx* ctx, const float* grad_dev, const float* hess_dev);
+
+/*
+ * Asynchronous begin_tree (enable nonzero) or the default, waiting one
+ * (enable 0) ([bonsai-10] "Deferred": once the kernels are on the device, host
+ * orchestration is what remains between the levels; here no host round trip
+ * stands between a tree's start and its first level's launches).
+ *
+ * When on, hgb_begin_tree and hgb_begin_tree_objective enqueue their passes
+ * and return HGB_OK without waiting for the maxima.  Everything the tree's
+ * kernels need stays on the device.  The host reads the maxima back at the
+ * next call that needs them: hgb_get_scales (which waits for them), the next
+ * begin_tree, upload_bins, set_precision or hgb_sync.  A NaN/Inf value or a
+ * negative hessian is then reported once, as HGB_E_NONFINITE, by the next
+ * hgb_sync (hgb_get_scales also returns it); the histograms and splits of
+ * that tree are meaningless.
+ * Errors: HGB_E_INVALID for a null context.
+ */
+hgb_status hgb_set_async_begin(hgb_ctx* ctx, int enable);
 
 /* Losses that hgb_begin_tree_objective differentiates. */
 typedef enum {
@@ -182,7 +204,10 @@ hgb_status hgb_set_precision(hgb_ctx* ctx, int32_t bits);
 /* The current tree's scales: a fixed-point sum X stands for X * 2^-k
  * ([bonsai-9] "The idea": the device cells are int64 fixed point; these are
  * the exponents that turn them back into gradient and hessian sums).
- * Errors: HGB_E_INVALID for a null pointer; HGB_E_STATE before begin_tree. */
+ * Waits for them after an asynchronous begin_tree.
+ * Errors: HGB_E_INVALID for a null pointer; HGB_E_STATE before begin_tree;
+ *         HGB_E_NONFINITE for a tree started asynchronously from non-finite
+ *         values. */
 hgb_status hgb_get_scales(const hgb_ctx* ctx, int32_t* k_g, int32_t* k_h);
 
 /*
