@@ -405,19 +405,27 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
     ctx.sync()
     torch.cuda.synchronize()
 
-    # The timed steps, back to back (no per-kernel events).  An event pair on
-    # the library's stream (torch's current stream) brackets each step, for the
-    # median and spread beside the mean.
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # The timed steps, back to back, with nothing else on the stream.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    for _ in range(steps):
+        step(ctx, w, plan, g, h)
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    # The same steps with an event on the library's stream (torch's current
+    # stream) between consecutive steps, for the median and spread of the
+    # per-step times beside the mean (each marker adds a little host and
+    # device time of its own).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
     marks[0].record()
     for i in range(steps):
         step(ctx, w, plan, g, h)
         marks[i + 1].record()
     ctx.sync()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
 
     # The same steps again with the library's per-kernel events (recorded on
@@ -462,7 +470,7 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
-        # per-step spans from an event pair around each timed step
+        # per-step spans from events between consecutive steps (a second pass)
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
                               "min": round(float(per_step.min()), 4),
                               "p10": round(float(np.percentile(per_step, 10)), 4),
