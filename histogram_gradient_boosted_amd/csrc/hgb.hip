@@ -882,8 +882,8 @@ hgb_status hgb_sync(hgb_ctx* c)
     if (!c) return HGB_E_INVALID;
     c->err.clear();
     HGB_HIP(c, hipSetDevice(c->device));
-    HGB_HIP(c, hipMemcpyAsync(c->host_words + 2, c->dev_words + 2, 4, hipMemcpyDeviceToHost,
-                              c->stream));
+    k_post_u32<<<1, 64, 0, c->stream>>>(c->dev_words + 2, c->host_words + 2);
+    HGB_LAUNCHED(c, "k_post_u32");
     hgb_status st = wait_here(c, &c->host_ready);
     if (st != HGB_OK) return st;
     st = resolve_scales(c);

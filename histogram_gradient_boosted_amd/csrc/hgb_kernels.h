@@ -57,6 +57,13 @@ __global__ void k_clear_u32(uint32_t* p, int n)
     if (i < n) p[i] = 0u;
 }
 
+// The error word into pinned host memory, in stream order (a store from the
+// device instead of a copy command).
+__global__ void k_post_u32(const uint32_t* __restrict__ src, uint32_t* __restrict__ host_dst)
+{
+    if (threadIdx.x == 0) *host_dst = *src;
+}
+
 __device__ inline uint32_t abs_pattern(float x) { return __float_as_uint(x) & 0x7fffffffu; }
 __device__ inline uint32_t hess_pattern(float x)
 {
