@@ -42,6 +42,10 @@ OTHER = ("k_gather", "k_zero_slices", "k_subtract", "k_subtract_split", "k_split
 # one --pmc pass of SQ counters for the LDS side of the fill (5 of the 8 SQ slots)
 LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_ATOMIC", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
                 "SQ_LDS_ADDR_CONFLICT")
+# one --pmc pass of the L2's memory read requests by size (3 of the 4 TCC
+# slots): all requests, the 32-byte ones, and the 128-byte ones (BUBBLE);
+# the rest are 64-byte.  FETCH_SIZE is derived from these three.
+REQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum")
 SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boosted_amd/csrc/*.h",
            "include/*.h")
 
@@ -66,6 +70,7 @@ def drive(config: str, precision: int, steps: int) -> None:
     w = synth.make(config)
     ctx = binding.Context(0)
     ctx.set_precision(precision)
+    ctx.set_async_begin(True)   # as bench.py runs it
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g, h = bench.step_inputs(w, bench.resolve_objective(w, "auto"), torch)
     plan = bench.prepare(ctx, w, g, h, torch)
@@ -228,6 +233,37 @@ def main() -> None:
             rec["bank_conflict_per_active"] = round(rec["SQ_LDS_BANK_CONFLICT"] / max(rec["SQ_LDS_IDX_ACTIVE"], 1.0), 4)
             lds[k] = rec
 
+    # read requests by size: the copy (whose bytes are known), then the step
+    req_raw = {}
+    db = run_counter(REQ_COUNTERS, os.path.join(args.out, "copy_req"), [me, "--copy"],
+                     os.path.join(args.out, "copy_req.log"))
+    copy_req = {c: read_counter(db, c) for c in REQ_COUNTERS}
+    for steps in (1, 3):
+        db = run_counter(REQ_COUNTERS, os.path.join(args.out, f"{args.config}_p{args.precision}_req_{steps}"),
+                         [me, "--drive", "--config", args.config, "--precision", str(args.precision),
+                          "--steps", str(steps)],
+                         os.path.join(args.out, f"{args.config}_p{args.precision}_req_{steps}.log"))
+        req_raw[steps] = {c: read_counter(db, c) for c in REQ_COUNTERS}
+
+    def req_split(vals):
+        total, r32, r128 = (vals[c] for c in REQ_COUNTERS)
+        return {"requests": total, "req_32B": r32, "req_128B": r128, "req_64B": total - r32 - r128,
+                "bytes": 32 * r32 + 64 * (total - r32 - r128) + 128 * r128}
+    copy_name = max((k for k in copy_req[REQ_COUNTERS[0]] if "copy" in k.lower()),
+                    key=lambda k: copy_req[REQ_COUNTERS[0]][k][0])
+    copy_n = copy_req[REQ_COUNTERS[0]][copy_name][1]
+    req_copy = req_split({c: copy_req[c].get(copy_name, [0.0, 1])[0] / copy_n for c in REQ_COUNTERS})
+    req_copy["copy_bytes_read"] = COPY_BYTES
+    requests = {}
+    for k in FILL_CLASS + OTHER:
+        vals = {}
+        for c in REQ_COUNTERS:
+            a = req_raw[3][c].get(k, [0.0, 0])
+            b = req_raw[1][c].get(k, [0.0, 0])
+            vals[c] = (a[0] - b[0]) / 2.0
+        if vals[REQ_COUNTERS[0]] > 0:
+            requests[k] = req_split(vals)
+
     kernels = sorted(set(k for d in raw.values() for k in d) & set(FILL_CLASS + OTHER))
     per_step = {}
     for k in kernels:
@@ -252,6 +288,8 @@ def main() -> None:
         "fill_traffic": {"bytes_per_step": fill_fetch + fill_write, "fetch_bytes": fill_fetch,
                          "write_bytes": fill_write, "kernels": list(FILL_CLASS)},
         "lds_per_step": lds,
+        "read_requests_per_step": requests,
+        "read_requests_copy": req_copy,
         "seconds": round(time.time() - t0, 1),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -281,6 +319,17 @@ def main() -> None:
         lines.append(f"| {k} | {rec['SQ_INSTS_LDS']:,.0f} | {rec['SQ_INSTS_LDS_ATOMIC']:,.0f} | "
                      f"{rec['SQ_LDS_IDX_ACTIVE']:,.0f} | {rec['SQ_LDS_BANK_CONFLICT']:,.0f} | "
                      f"{rec['SQ_LDS_ADDR_CONFLICT']:,.0f} | {rec['bank_conflict_per_active']:.3f} |")
+    lines += ["",
+              f"L2 read requests to memory per step by size (rocprofv3 --pmc {' '.join(REQ_COUNTERS)}, "
+              "same differencing; 64-byte = all - 32-byte - 128-byte).  The 1 GiB copy reads with "
+              f"{req_copy['req_32B']:,.0f} 32-byte, {req_copy['req_64B']:,.0f} 64-byte and "
+              f"{req_copy['req_128B']:,.0f} 128-byte requests: {req_copy['bytes']:,.0f} bytes by that count "
+              f"for {COPY_BYTES:,} read.", "",
+              "| kernel | requests | 32-byte | 64-byte | 128-byte | bytes by size |",
+              "|---|---|---|---|---|---|"]
+    for k, r in requests.items():
+        lines.append(f"| {k} | {r['requests']:,.0f} | {r['req_32B']:,.0f} | {r['req_64B']:,.0f} | "
+                     f"{r['req_128B']:,.0f} | {r['bytes']:,.0f} |")
     lines += ["",
               f"Kernel sources sha256: `{record['source_hash']}`."]
     with open(base + ".md", "w") as f:
