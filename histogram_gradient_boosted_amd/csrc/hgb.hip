@@ -116,8 +116,9 @@ struct hgb_ctx {
     // this device's copy of the no-allocation scratch array (set up by hgb_create)
     unsigned char* noalloc_scratch = nullptr;
 
-    // small device words: [0..1] max patterns, [2] error flags, [4..11] the
-    // quantize scales 2^k and the split scales 2^-k (four doubles)
+    // small device words: [0..1] max patterns, [2] error flags, [3] 1 when the
+    // quantize pass must encode the rows again, [4..11] the quantize scales
+    // 2^k (also the next tree's guess) and the split scales 2^-k (four doubles)
     uint32_t* dev_words = nullptr;
     uint32_t* host_words = nullptr;   // pinned
     uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
@@ -708,10 +709,12 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
     const int max_blocks = grid_for((c->n + 3) / 4, 256, kMaxBlocks);
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
-        k_grad_hess_max<Src><<<max_blocks, 256, 0, c->stream>>>(src, c->n, vec, c->max_part);
+        k_grad_hess_max<Src><<<max_blocks, 256, 0, c->stream>>>(src, c->n, vec, c->max_part,
+                                                                 (const double*)(c->dev_words + 4), c->q);
         HGB_LAUNCHED(c, "k_grad_hess_max");
         k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words, c->precision,
-                                              (double*)(c->dev_words + 4), c->host_words);
+                                              (double*)(c->dev_words + 4), c->host_words, c->dev_words + 3,
+                                              Src::kGuess ? 1 : 0);
         HGB_LAUNCHED(c, "k_max_final");
     }
     // k_max_final wrote the maxima into pinned host memory too (the host
@@ -723,7 +726,7 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
         k_quantize<Src><<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
-            src, c->n, vec, (const double*)(c->dev_words + 4), c->q);
+            src, c->n, vec, (const double*)(c->dev_words + 4), c->dev_words + 3, c->q);
         HGB_LAUNCHED(c, "k_quantize");
     }
     c->tree_precision = c->precision;

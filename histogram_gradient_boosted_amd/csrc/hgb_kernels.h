@@ -76,6 +76,9 @@ __device__ inline uint32_t hess_pattern(float x)
 // rows at a time from 16-byte loads (fetch4) or one at a time (fetch1).
 // ---------------------------------------------------------------------------
 struct GradSource {   // (g, h) handed in directly
+    // the quantize pass reads the pairs again (cheaper than writing guessed
+    // codes in the max pass: both passes are memory-bound)
+    static constexpr bool kGuess = false;
     const float* __restrict__ g;
     const float* __restrict__ h;
     __device__ void fetch4(int64_t i4, float4& a, float4& b) const
@@ -144,6 +147,10 @@ __device__ inline void objective_row(float m32, float y32, float w32, float& g, 
 
 template <int OBJ, bool WEIGHTED>
 struct ObjectiveSource {
+    // deriving (g, h) costs fp64 work: the max pass also writes the codes at
+    // the previous tree's scales, and the quantize pass reruns only when this
+    // tree's scales differ
+    static constexpr bool kGuess = true;
     const float* __restrict__ m;
     const float* __restrict__ y;
     const float* __restrict__ w;
@@ -166,16 +173,38 @@ struct ObjectiveSource {
 // Four rows per thread per step (16-byte loads, when `vec` says the source's
 // arrays are 16-byte aligned); the leftover rows one by one at the end.  Each
 // block writes its pair of maxima to out[2 * block], out[2 * block + 1].
+// The fixed-point pair of one row at the given scales: exact power-of-two
+// scaling of an fp32 value in double, then round half to even.  (A scale
+// that is not the tree's own -- a guess -- may saturate the conversion; such
+// codes are always rewritten.)
+__device__ inline int2 encode_row(float a, float b, double scale_g, double scale_h)
+{
+    return make_int2((int)__builtin_rint((double)a * scale_g), (int)__builtin_rint((double)b * scale_h));
+}
+
+// Block maxima of |g| and h for k_max_final.  For a source with kGuess the
+// same pass also writes each row's fixed-point pair at the previous tree's
+// scales (scales[0..1], still in place): when this tree's scales turn out
+// the same, k_max_final says so and the quantize pass has nothing to redo.
 template <class Src>
 __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int vec,
-                                                       uint32_t* __restrict__ out)
+                                                       uint32_t* __restrict__ out,
+                                                       const double* __restrict__ scales,
+                                                       int2* __restrict__ q)
 {
     uint32_t mg = 0, mh = 0;
+    const double guess_g = scales[0], guess_h = scales[1];
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t n4 = vec ? (n >> 2) : 0;
-    auto fold = [&](const float4& a, const float4& b) {
+    int4* q4 = (int4*)q;
+    auto fold = [&](int64_t i4, const float4& a, const float4& b) {
         mg = max(mg, max(max(abs_pattern(a.x), abs_pattern(a.y)), max(abs_pattern(a.z), abs_pattern(a.w))));
         mh = max(mh, max(max(hess_pattern(b.x), hess_pattern(b.y)), max(hess_pattern(b.z), hess_pattern(b.w))));
+        if constexpr (!Src::kGuess) return;
+        const int2 r0 = encode_row(a.x, b.x, guess_g, guess_h), r1 = encode_row(a.y, b.y, guess_g, guess_h);
+        const int2 r2 = encode_row(a.z, b.z, guess_g, guess_h), r3 = encode_row(a.w, b.w, guess_g, guess_h);
+        q4[2 * i4] = make_int4(r0.x, r0.y, r1.x, r1.y);
+        q4[2 * i4 + 1] = make_int4(r2.x, r2.y, r3.x, r3.y);
     };
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     // four strided groups in flight per thread
@@ -184,18 +213,19 @@ __global__ __launch_bounds__(256) void k_grad_hess_max(Src src, int64_t n, int v
 #pragma unroll
         for (int u = 0; u < 4; ++u) src.fetch4(i + u * stride, a[u], b[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) fold(a[u], b[u]);
+        for (int u = 0; u < 4; ++u) fold(i + u * stride, a[u], b[u]);
     }
     for (; i < n4; i += stride) {
         float4 a, b;
         src.fetch4(i, a, b);
-        fold(a, b);
+        fold(i, a, b);
     }
     for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         float a, b;
         src.fetch1(i, a, b);
         mg = max(mg, abs_pattern(a));
         mh = max(mh, hess_pattern(b));
+        if constexpr (Src::kGuess) q[i] = encode_row(a, b, guess_g, guess_h);
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
         mg = max(mg, (uint32_t)__shfl_xor((int)mg, off, kWave));
@@ -245,11 +275,15 @@ __device__ inline double inv_scale_of_max(uint32_t pat, int precision)
 }
 
 // out[0..1]: the maxima's bit patterns; scales[0..1]: their scales 2^k (above),
-// scales[2..3]: the inverses 2^-k that the split kernels read.
+// scales[2..3]: the inverses 2^-k that the split kernels read; *redo: 1 when
+// the scales differ from the ones k_grad_hess_max encoded the rows with (the
+// previous contents of scales[0..1]) or the max pass did not encode them
+// (guessed 0), so that k_quantize must encode the rows.
 __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ part, int n_blocks,
                                                    uint32_t* __restrict__ out, int precision,
                                                    double* __restrict__ scales,
-                                                   uint32_t* __restrict__ host_out)
+                                                   uint32_t* __restrict__ host_out, uint32_t* __restrict__ redo,
+                                                   int guessed)
 {
     __shared__ uint32_t red[2][256];
     uint32_t mg = 0, mh = 0;
@@ -272,8 +306,10 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
         out[1] = red[1][0];
         host_out[0] = red[0][0];   // pinned host memory: no read-back copy
         host_out[1] = red[1][0];
-        scales[0] = scale_of_max(red[0][0], precision);
-        scales[1] = scale_of_max(red[1][0], precision);
+        const double sg = scale_of_max(red[0][0], precision), sh = scale_of_max(red[1][0], precision);
+        *redo = (!guessed || sg != scales[0] || sh != scales[1]) ? 1u : 0u;
+        scales[0] = sg;
+        scales[1] = sh;
         scales[2] = inv_scale_of_max(red[0][0], precision);
         scales[3] = inv_scale_of_max(red[1][0], precision);
     }
@@ -282,15 +318,14 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
 // q = round-half-even(c * 2^k), both components packed per row as (qg, qh).
 template <class Src>
 __global__ __launch_bounds__(256) void k_quantize(Src src, int64_t n, int vec,
-                                                  const double* __restrict__ scales, int2* __restrict__ q)
+                                                  const double* __restrict__ scales,
+                                                  const uint32_t* __restrict__ redo, int2* __restrict__ q)
 {
+    // the rows already hold their codes when the max pass guessed the scales
+    if (*redo == 0u) return;
     // the scales k_max_final derived on the device (no host round trip)
     const double scale_g = scales[0], scale_h = scales[1];
-    // exact: power-of-two scaling of an fp32 value in double, then ties-to-even
-    auto enc = [&](float a, float b) {
-        return make_int2((int)__builtin_rint((double)a * scale_g),
-                         (int)__builtin_rint((double)b * scale_h));
-    };
+    auto enc = [&](float a, float b) { return encode_row(a, b, scale_g, scale_h); };
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t n4 = vec ? (n >> 2) : 0;
     int4* q4 = (int4*)q;

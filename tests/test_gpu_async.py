@@ -129,3 +129,72 @@ def test_async_nonfinite_reported_by_sync_once(hgb, torch):
     assert e.value.status == hgb.HGB_E_NONFINITE
     ctx.sync()
     ctx.close()
+
+
+@pytest.mark.parametrize("asyn", [False, True])
+def test_consecutive_trees_codes(hgb, torch, asyn):
+    """Trees one after another on one context, with scales that repeat and
+    that change (the max pass encodes the rows at the previous tree's scales
+    and the quantize pass re-encodes them only when the scales differ): every
+    tree's codes and root histogram equal the oracle's."""
+    w = synth.random_small(65, 30_001, 5, 64, False, 0)
+    ctx = hgb.Context(0)
+    ctx.set_async_begin(asyn)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    t = torch.empty((1, 5, 64, 2), dtype=torch.int64, device="cuda")
+    q = torch.empty((w.n_rows, 2), dtype=torch.int32, device="cuda")
+    plan = [(1.0, 1.0, 30), (1.0, 1.0, 30), (8.0, 1.0, 30), (8.0, 1.0, 30), (8.0, 0.25, 30),
+            (8.0, 0.25, 20), (8.0, 0.25, 20), (1.0, 1.0, 30)]
+    for i, (sg, sh, bits) in enumerate(plan):
+        say("tree", i, sg, sh, bits)
+        ctx.set_precision(bits)
+        grad = (w.grad * np.float32(sg)).astype(np.float32)
+        hess = (w.hess * np.float32(sh)).astype(np.float32)
+        ctx.begin_tree(torch.from_numpy(grad).cuda(), torch.from_numpy(hess).cuda())
+        ctx.copy_quantized(q)
+        ctx.build_level(t)
+        ctx.sync()
+        qg, kg = oracle.quantize(grad, False, bits)
+        qh, kh = oracle.quantize(hess, True, bits)
+        assert ctx.get_scales() == (kg, kh)
+        got = q.cpu().numpy()
+        assert np.array_equal(got[:, 0], qg) and np.array_equal(got[:, 1], qh), f"tree {i}"
+        assert np.array_equal(t.cpu().numpy(), oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh))
+    ctx.close()
+
+
+@pytest.mark.parametrize("asyn", [False, True])
+def test_consecutive_objective_trees_codes(hgb, torch, asyn):
+    """The same on the device objective, whose max pass writes the codes at
+    the previous tree's scales: weighted squared and logistic trees whose
+    scales repeat and change (weights x1, x1, x8, x8, logistic, logistic, P
+    = 21); every tree's codes and root histogram equal the oracle's."""
+    w = synth.random_small(66, 20_003, 4, 32, False, 0)
+    m, y, _ = synth.objective_inputs(6, w.n_rows, "squared")
+    ml, yl, _ = synth.objective_inputs(7, w.n_rows, "logistic")
+    ones = np.ones(w.n_rows, np.float32)
+    ctx = hgb.Context(0)
+    ctx.set_async_begin(asyn)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    t = torch.empty((1, 4, 32, 2), dtype=torch.int64, device="cuda")
+    q = torch.empty((w.n_rows, 2), dtype=torch.int32, device="cuda")
+    plan = [("squared", m, y, 1.0, 30), ("squared", m, y, 1.0, 30), ("squared", m, y, 8.0, 30),
+            ("squared", m, y, 8.0, 30), ("logistic", ml, yl, 1.0, 30), ("logistic", ml, yl, 1.0, 30),
+            ("logistic", ml, yl, 1.0, 21), ("squared", m, y, 1.0, 30)]
+    for i, (kind, mm, yy, wt, bits) in enumerate(plan):
+        say("objective tree", i, kind, wt, bits)
+        ctx.set_precision(bits)
+        wv = (ones * np.float32(wt)).astype(np.float32)
+        ctx.begin_tree_objective(kind, torch.from_numpy(mm).cuda(), torch.from_numpy(yy).cuda(),
+                                 torch.from_numpy(wv).cuda())
+        ctx.copy_quantized(q)
+        ctx.build_level(t)
+        ctx.sync()
+        g, h = oracle.objective(kind, mm, yy, wv)
+        qg, kg = oracle.quantize(g, False, bits)
+        qh, kh = oracle.quantize(h, True, bits)
+        assert ctx.get_scales() == (kg, kh)
+        got = q.cpu().numpy()
+        assert np.array_equal(got[:, 0], qg) and np.array_equal(got[:, 1], qh), f"tree {i}"
+        assert np.array_equal(t.cpu().numpy(), oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh))
+    ctx.close()
