@@ -295,6 +295,13 @@ def lds_rates(device: int = 0):
             return None
         out[name] = r.value
     out["n_cu"] = n_cu.value
+    if hasattr(lib, "gather_rate_measure"):
+        g = lib.gather_rate_measure
+        g.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+        g.restype = ctypes.c_int
+        r = ctypes.c_double(0.0)
+        if g(device, ctypes.byref(r)) == 0:
+            out["random_lines_per_s"] = r.value
     return out
 
 
@@ -552,6 +559,23 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
             # u32 adds, for a cell split into 32-bit halves (four adds instead of two)
             "u32": {k: round(rates[k] / 1e9, 1) for k in ("u32_conflict_free", "u32_random_bins_16_copies")},
             "scale": "G lane-ops/s", "n_cu": rates["n_cu"]}
+        # The level fill of a narrow matrix reads its built rows and their (g, h)
+        # scattered: its ceiling is the rate of scattered 128-byte line fetches
+        # (every read the L2 sends to memory is a whole line), measured by the
+        # same library.  Lines per step from the counters' read requests.
+        kk = (counters or {}).get("read_requests_per_step", {})
+        lines = sum(kk[k]["requests"] for k in ("k_fill_rows", "k_fill_cols") if k in kk)
+        if "random_lines_per_s" in rates and breakdown["fill_level"] > 0:
+            # (achieved and frac null when the committed counters are not of these sources)
+            ach = lines / (breakdown["fill_level"] * 1e-3) if lines > 0 else None
+            result["gather_roofline"] = {
+                "kernel": "k_fill_rows / k_fill_cols (levels below the root)",
+                "unit": "128-byte line fetches/s", "lines_per_step": int(lines) if lines > 0 else None,
+                "achieved": round(ach / 1e9, 2) if ach else None,
+                "peak": round(rates["random_lines_per_s"] / 1e9, 2),
+                "frac": round(ach / rates["random_lines_per_s"], 4) if ach else None, "scale": "G lines/s",
+                "peak_kind": "measured: random 128-byte line reads, 8 in flight per thread, 640 MiB buffer "
+                             "(csrc/lds_rate.hip gather_rate_measure)"}
         log(f"[bench] LDS atomics {plan.cells * per_cell / (fill_ms_step * 1e-3) / 1e9:.0f} G/s in the fill; "
             f"microbenchmark { {k: round(v / 1e9) for k, v in rates.items() if k != 'n_cu'} } G/s")
     if cpu:
@@ -618,7 +642,7 @@ def main():
                        args.flush_mib, not args.no_cpu_baseline, cpu_min_s=0.0)
         keep = ("value", "unit", "ms_per_step", "ms_per_step_stats", "steps", "warmup", "config",
                 "kernel_ms_per_step", "roofline", "fill_class_roofline", "lds_roofline", "cpu_baseline",
-                "precision_bits", "effective_gcells_per_s")
+                "precision_bits", "effective_gcells_per_s", "gather_roofline")
         result["targets"] = {"c4": {k: wide[k] for k in keep if k in wide}}
     print(json.dumps(result), flush=True)
 

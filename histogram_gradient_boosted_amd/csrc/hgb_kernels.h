@@ -1393,17 +1393,21 @@ struct Chunk;
 // Rotate N dwords as one little-endian byte string: afterwards byte i holds
 // what byte (i + k) mod 4N held (0 <= k < 4N).  Whole dwords move in log2(N)
 // conditional stages, then one alignbyte per dword shifts the remaining 0-3
-// bytes.  Each lane may rotate by its own k.
+// bytes.  Each lane may rotate by its own k.  A stage is one bitfield insert
+// per dword under an all-ones or all-zero mask that the compiler cannot see
+// through: with plain selects it merges the stages into an N-way select per
+// dword (N - 1 compares and N - 1 selects each, four times the work).
 template <int N>
 __device__ inline void rotate_bytes(uint32_t (&d)[N], int k)
 {
     const int kd = k >> 2;
 #pragma unroll
     for (int s = 1; s < N; s <<= 1) {
-        const bool on = (kd & s) != 0;
+        uint32_t m = (kd & s) != 0 ? ~0u : 0u;
+        asm("" : "+v"(m));   // opaque; a function of k alone, so hoisted out of row loops
         uint32_t t[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) t[i] = on ? d[(i + s) % N] : d[i];
+        for (int i = 0; i < N; ++i) t[i] = (d[(i + s) % N] & m) | (d[i] & ~m);
 #pragma unroll
         for (int i = 0; i < N; ++i) d[i] = t[i];
     }

@@ -1,4 +1,5 @@
-// LDS atomic-add rate microbenchmark (gfx950).  The level histogram fill adds
+// LDS atomic-add rate microbenchmark (gfx950), and the rate of scattered
+// line reads (gather_rate_measure, at the end).  The level histogram fill adds
 // 64-bit integers into block-private LDS histograms at data-dependent bins, so
 // its second ceiling, after HBM, is the rate at which a CU retires LDS atomic
 // adds.  This measures that rate for the access patterns the fill produces:
@@ -76,6 +77,32 @@ hipError_t launch(int iters, int copies, int words, int blocks, int threads, uns
     return hipGetLastError();
 }
 
+// Random 128-byte line reads: every thread reads 16 bytes from each of U
+// lines at pseudo-random line indices of a buffer larger than the 256 MB
+// Infinity Cache (indices reduced modulo the line count: every read stays in
+// the buffer), with all U loads issued before any is used.  The chip's rate
+// of scattered line fetches: the ceiling of a gather that touches one line
+// per row.
+template <int U>
+__global__ __launch_bounds__(256) void k_rand_lines(const uint4* __restrict__ buf, uint64_t n_lines, int iters,
+                                                    unsigned long long* sink)
+{
+    uint32_t h = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 12345u;
+    unsigned long long acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            h = h * 1664525u + 1013904223u;
+            const uint64_t line = ((uint64_t)h * n_lines) >> 32;   // < n_lines
+            v[u] = buf[line * 8];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += v[u].x ^ v[u].w;
+    }
+    if (acc == 0x1234567ull) sink[0] = acc;   // practically never: keeps the loads live
+}
+
 }  // namespace lds_probe
 
 using namespace lds_probe;
@@ -129,6 +156,46 @@ done:
     if (b) (void)hipEventDestroy(b);
     if (st) (void)hipStreamDestroy(st);
     (void)hipFree(sink);
+    return rc;
+}
+
+// Scattered 128-byte line reads per second on `device` (k_rand_lines over a
+// 640 MiB buffer, 8 lines in flight per thread).  Returns 0 on success, 2 for
+// a HIP error.
+int gather_rate_measure(int device, double* lines_per_s)
+{
+    if (!lines_per_s) return 1;
+    if (hipSetDevice(device) != hipSuccess) return 2;
+    const uint64_t bytes = 640ull << 20;
+    const uint64_t n_lines = bytes / 128;
+    const int blocks = 16384, iters = 4;
+    uint4* buf = nullptr;
+    unsigned long long* sink = nullptr;
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    int rc = 2;
+    float ms = 0.0f;
+    if (hipMalloc(&buf, bytes) != hipSuccess) return 2;
+    if (hipMalloc(&sink, 64) != hipSuccess) goto done;
+    if (hipStreamCreate(&st) != hipSuccess) goto done;
+    if (hipMemsetAsync(buf, 1, bytes, st) != hipSuccess) goto done;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) goto done;
+    for (int rep = 0; rep < 2; ++rep) {   // the first launch warms up
+        if (hipEventRecord(a, st) != hipSuccess) goto done;
+        k_rand_lines<8><<<blocks, 256, 0, st>>>(buf, n_lines, iters, sink);
+        if (hipGetLastError() != hipSuccess) goto done;
+        if (hipEventRecord(b, st) != hipSuccess) goto done;
+        if (hipEventSynchronize(b) != hipSuccess) goto done;
+    }
+    if (hipEventElapsedTime(&ms, a, b) != hipSuccess || ms <= 0.0f) goto done;
+    *lines_per_s = (double)blocks * 256.0 * iters * 8.0 / (ms * 1e-3);
+    rc = 0;
+done:
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    if (st) (void)hipStreamDestroy(st);
+    (void)hipFree(sink);
+    (void)hipFree(buf);
     return rc;
 }
 

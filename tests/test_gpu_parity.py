@@ -242,6 +242,45 @@ def test_split_reduce_wide_ties(hgb, torch, n_const):
     assert int(sp["feature"][0]) == n_const
 
 
+@pytest.mark.parametrize("B", [32, 600])
+def test_split_calls_in_a_row(hgb, torch, B):
+    """One context, its split scratch reused across calls: find_splits and
+    subtract_find_splits over node counts that grow and shrink (3,000, 1,000,
+    3,000 nodes; 1,500 then 200 pairs), each against the oracle.  600 bins
+    take the sliced scan (one block per feature)."""
+    say("split calls in a row", B)
+    rng = np.random.default_rng(B)
+    n, F, N = 40_000, 6, 3_000
+    w = synth.random_small(7 + B, n, F, B, True, 0, u16=B > 255)
+    node = rng.integers(0, N, n)
+    ri = np.argsort(node, kind="stable").astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(np.bincount(node, minlength=N))]).astype(np.int64)
+    qg, qh, kg, kh = oracle_quantized(w)
+    hist = oracle.build_hist(w.bins, w.n_bins, w.has_missing, qg, qh, ri, offs)
+    ctx, g, h = new_ctx(hgb, w, torch)
+    hist_t = torch.from_numpy(hist).cuda()
+    for m in (N, 1_000, N):
+        sp = gpu_splits(hgb, ctx, hist_t, m, w.lam, w.gamma, torch)
+        want = oracle.find_splits(hist[:m], w.n_bins, w.has_missing, kg, kh, w.lam, w.gamma)
+        assert_splits(sp, want, f"find_splits {m} nodes")
+    for P in (1_500, 200):
+        parent = hist[:P] + hist[P:2 * P]   # pair i's parent: nodes i and P + i together
+        child = np.empty((2 * P,) + hist.shape[1:], dtype=np.int64)
+        bir = rng.integers(0, 2, P).astype(np.uint8)
+        for i in range(P):
+            child[2 * i + int(bir[i])] = hist[i]
+        ch_t = torch.from_numpy(child).cuda()
+        out = torch.empty(2 * P * hgb.SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+        ctx.subtract_find_splits(torch.from_numpy(parent).cuda(), ch_t, bir, w.lam, w.gamma, out)
+        ctx.sync()
+        sp = hgb.splits_to_numpy(out)[: 2 * P]
+        want_ch = oracle.subtract(parent, child.copy(), bir)
+        assert np.array_equal(ch_t.cpu().numpy(), want_ch), f"{P} pairs: children differ"
+        want = oracle.find_splits(want_ch, w.n_bins, w.has_missing, kg, kh, w.lam, w.gamma)
+        assert_splits(sp, want, f"subtract_find_splits {P} pairs")
+    ctx.close()
+
+
 def test_c1_full(hgb, torch):
     say("c1 full")
     run_root_both(hgb, torch, synth.make("c1"))
