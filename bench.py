@@ -343,10 +343,10 @@ def dominant_roofline(prof, plan, steps: int, counters):
     achieved = per_launch_bytes / avg_s / 1e9
     traffic = None
     if counters is not None:
-        kk = counters.get("kernels", {})
+        kk = counters.get("per_step", {})
         names = ("k_fill_rows", "k_fill_cols") if name == "fill_level" else ("k_fill_root", "k_fill_root_il")
-        tb = sum(int(kk[k]["fetch_bytes"]) + int(kk[k]["write_bytes"]) for k in names if k in kk)
-        dispatches = sum(int(kk[k]["dispatches"]) for k in names if k in kk)
+        tb = sum(int(kk[k]["FETCH_SIZE"]["bytes"]) + int(kk[k]["WRITE_SIZE"]["bytes"]) for k in names if k in kk)
+        dispatches = sum(int(kk[k]["FETCH_SIZE"]["dispatches"]) for k in names if k in kk)
         if dispatches:
             traffic = int(round(tb / dispatches))
     return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -136,16 +136,21 @@ def read_counter(db: str, counter: str) -> dict:
 
 
 def trace_summary(db: str, step_equiv: int, command: str) -> str:
-    """Per-kernel durations from a rocprofv3 --kernel-trace database."""
+    """Per-kernel durations from a rocprofv3 --kernel-trace database.  With
+    step_equiv 0 the trees are counted from the trace: every tree starts with
+    one k_max_final (the end of begin_tree's maxima)."""
     con = sqlite3.connect(db)
     rows = con.execute("select name, start, end from kernels").fetchall()
     per = collections.defaultdict(list)
     for name, start, end in rows:
         per[name.split("(")[0].replace("void ", "").strip()].append((end - start) / 1e3)
+    if step_equiv <= 0:
+        step_equiv = max(1, sum(len(ds) for name, ds in per.items() if name.split("::")[-1] == "k_max_final"))
     lines = [f"# Kernel trace: `{command}`", "",
              "rocprofv3 --kernel-trace --stats; durations in microseconds.  One process runs "
              f"{step_equiv} step-equivalents of the tree (the set-up tree, warm-up, the timed and "
-             "the event-timed passes); 'per step' divides the total by that.", "",
+             "the event-timed passes, counted by begin_tree's k_max_final); 'per step' divides "
+             "the total by that.", "",
              "| kernel | dispatches | total us | avg us | min us | max us | us per step |",
              "|---|---|---|---|---|---|---|"]
     fill_total = 0.0
@@ -173,7 +178,8 @@ def main() -> None:
                     help="summarize the databases already under --out instead of profiling")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="summarize a rocprofv3 kernel-trace database instead")
-    ap.add_argument("--step-equiv", type=int, default=44)
+    ap.add_argument("--step-equiv", type=int, default=0,
+                    help="trees the traced process ran (0: count them from the trace)")
     ap.add_argument("--trace-command", default="")
     ap.add_argument("--trace-out")
     args = ap.parse_args()
