@@ -1611,9 +1611,14 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
                     c->dev_words + 2);
             HGB_LAUNCHED(c, "k_part_count");
         }
-        k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
-                                               (const int32_t*)(dev + off_offs), sp, n_nodes, left_base,
-                                               node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
+        if (n_items <= kPartScanLdsItems && n_nodes <= kPartScanLdsNodes)
+            k_part_scan_lds<kPartScanLdsItems, kPartScanLdsNodes><<<1, 1024, 0, c->stream>>>(
+                cnt, (int)n_items, (const int32_t*)(dev + off_first), (const int32_t*)(dev + off_offs), sp, n_nodes,
+                left_base, node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
+        else
+            k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
+                                                   (const int32_t*)(dev + off_offs), sp, n_nodes, left_base,
+                                                   node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
         HGB_LAUNCHED(c, "k_part_scan");   // node records and error word written to pinned host memory
         if (!c->part_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->part_ready, hipEventDisableTiming));
         HGB_HIP(c, hipEventRecord(c->part_ready, c->stream));

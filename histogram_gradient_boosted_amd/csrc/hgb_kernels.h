@@ -2598,40 +2598,44 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
 {
     __shared__ int s_sum[kPartThreads / kWave];
     const PartItem it = items[blockIdx.x];
-    const SplitOut sp = splits[it.node];
-    int c = 0;
-    if (sp.feature >= 0) {   // uniform
-        const BinT* col = bins + (int64_t)sp.feature * n;
-        const int rf = rot[sp.feature];   // stored values are rotated per feature
-        // positions in 64 bits: a chunk may end within kPartChunk of 2^31
-        const int64_t k0 = (int64_t)it.begin + threadIdx.x;
-        const int64_t kstep = blockDim.x;
-        int64_t r[kPartRows];
+    // The row indices do not depend on the split: they are loaded while the
+    // split record is on its way, and nothing branches on the split (a node
+    // without one reads feature 0's column and sends every row right), so the
+    // compiler keeps the loads ahead of it.  Positions in 64 bits: a chunk may
+    // end within kPartChunk of 2^31.
+    const int64_t k0 = (int64_t)it.begin + threadIdx.x;
+    const int64_t kstep = blockDim.x;
+    int64_t r[kPartRows];
 #pragma unroll
-        for (int j = 0; j < kPartRows; ++j) {
-            const int64_t kc = min(k0 + j * kstep, (int64_t)it.end - 1);
-            r[j] = row_index ? (int64_t)row_index[kc] : kc;
-        }
-        int v[kPartRows];
-        bool bad = false;
-#pragma unroll
-        for (int j = 0; j < kPartRows; ++j) {
-            const bool in = (uint64_t)r[j] < (uint64_t)n;
-            bad |= !in && k0 + j * kstep < it.end;
-            v[j] = unrotate((int)col[in ? r[j] : 0], rf, S);
-        }
-#pragma unroll
-        for (int j = 0; j < kPartRows; ++j) {
-            const int64_t k = k0 + j * kstep;
-            // a row index outside [0, n) is routed right (and reported)
-            const bool left = (uint64_t)r[j] < (uint64_t)n && part_left(v[j], n_bins, sp);
-            if (k < it.end) {
-                c += left ? 1 : 0;
-                flags[k] = left ? 1 : 0;
-            }
-        }
-        if (bad) atomicOr(err, kErrRowIndex);
+    for (int j = 0; j < kPartRows; ++j) {
+        const int64_t kc = min(k0 + j * kstep, (int64_t)it.end - 1);
+        r[j] = row_index ? (int64_t)row_index[kc] : kc;
     }
+    const SplitOut sp = splits[it.node];
+    const bool has = sp.feature >= 0;   // uniform
+    const int fe = has ? sp.feature : 0;
+    const BinT* col = bins + (int64_t)fe * n;
+    const int rf = rot[fe];   // stored values are rotated per feature
+    int v[kPartRows];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kPartRows; ++j) {
+        const bool in = (uint64_t)r[j] < (uint64_t)n;
+        bad |= has && !in && k0 + j * kstep < it.end;
+        v[j] = unrotate((int)col[in ? r[j] : 0], rf, S);
+    }
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kPartRows; ++j) {
+        const int64_t k = k0 + j * kstep;
+        // a row index outside [0, n) is routed right (and reported)
+        const bool left = has && (uint64_t)r[j] < (uint64_t)n && part_left(v[j], n_bins, sp);
+        if (k < it.end) {
+            c += left ? 1 : 0;
+            flags[k] = left ? 1 : 0;
+        }
+    }
+    if (bad) atomicOr(err, kErrRowIndex);
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     if ((threadIdx.x & (kWave - 1)) == 0) s_sum[threadIdx.x / kWave] = c;
     __syncthreads();
@@ -2642,22 +2646,35 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
     }
 }
 
-// Block-wide exclusive scan of v (blockDim.x values), returning this thread's
-// prefix; *total receives the sum.  Uses s[blockDim.x].
+// Block-wide exclusive scan of v (blockDim.x values, a multiple of 64 up to
+// 1,024), returning this thread's prefix; *total receives the sum.  Each wave
+// scans its 64 values with shuffles, wave 0 scans the waves' totals, and three
+// barriers serve the whole block (a scan through LDS alone takes two per
+// doubling step, twenty for 1,024 threads).  Uses s[blockDim.x / 64].
 __device__ inline int block_exclusive_scan(int v, int* s, int* total)
 {
-    s[threadIdx.x] = v;
-    __syncthreads();
-    for (int d = 1; d < (int)blockDim.x; d <<= 1) {
-        const int t = threadIdx.x >= (unsigned)d ? s[threadIdx.x - d] : 0;
-        __syncthreads();
-        s[threadIdx.x] += t;
-        __syncthreads();
+    const int lane = (int)(threadIdx.x & (kWave - 1)), w = (int)(threadIdx.x / kWave);
+    const int nw = (int)(blockDim.x / kWave);
+    int x = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
     }
-    const int incl = s[threadIdx.x];
-    *total = s[blockDim.x - 1];
+    if (lane == kWave - 1) s[w] = x;   // the wave's total
     __syncthreads();
-    return incl - v;
+    if (w == 0) {
+        int t = lane < nw ? s[lane] : 0;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(t, d, kWave);
+            if (lane >= d) t += y;
+        }
+        if (lane < nw) s[lane] = t;    // the waves' inclusive prefixes
+    }
+    __syncthreads();
+    const int before = w > 0 ? s[w - 1] : 0;
+    *total = s[nw - 1];
+    __syncthreads();   // s is free again for the next call
+    return before + x - v;
 }
 
 // One block.  left_base[item]: rows going left in the node's earlier chunks.
@@ -2713,6 +2730,101 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
     if (threadIdx.x == 0) *err_host = *err_dev;
 }
 
+// k_part_scan for a level of at most MAXI chunks and MAXN nodes, by one block
+// of 1,024 threads: the same outputs, from one round of loads issued together
+// (each thread's counts and node records, held in registers until all are
+// issued, then put in LDS), with the scans, the rebase and each chunk's node
+// (a binary search of the nodes' first chunks) done in LDS.  A single block
+// pays every global round trip in full; the chunk records themselves (in
+// pinned host memory) are not read at all.
+template <int MAXI, int MAXN>
+__global__ __launch_bounds__(1024) void k_part_scan_lds(const int32_t* __restrict__ cnt, int n_items,
+                                                        const int32_t* __restrict__ first_item,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const SplitOut* __restrict__ splits, int n_nodes,
+                                                        int32_t* __restrict__ left_base,
+                                                        int32_t* __restrict__ node_out,
+                                                        int32_t* __restrict__ host_out,
+                                                        const uint32_t* __restrict__ err_dev,
+                                                        uint32_t* __restrict__ err_host)
+{
+    constexpr int kT = 1024;
+    constexpr int IP = MAXI / kT, NP = MAXN / kT;   // entries per thread
+    static_assert(IP * kT == MAXI && NP * kT == MAXN, "whole passes of the block");
+    __shared__ int s_ex[MAXI];         // the counts, then their exclusive scan
+    __shared__ int s_first[MAXN + 1];  // each node's first chunk
+    __shared__ int s_rows[MAXN];       // each node's rows, -1 without a split
+    __shared__ int s_scan[kT];
+    const int t = threadIdx.x;
+    int c[IP], fi[NP], o0[NP], o1[NP], ft[NP];
+#pragma unroll
+    for (int u = 0; u < IP; ++u) {
+        const int j = t + u * kT;
+        c[u] = j < n_items ? cnt[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int i = t + u * kT;
+        const bool in = i < n_nodes;
+        fi[u] = in ? first_item[i] : 0;
+        o0[u] = in ? offsets[i] : 0;
+        o1[u] = in ? offsets[i + 1] : 0;
+        ft[u] = in ? splits[i].feature : -1;
+    }
+    const int fi_last = t == 0 ? first_item[n_nodes] : 0;
+#pragma unroll
+    for (int u = 0; u < IP; ++u) s_ex[t + u * kT] = c[u];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int i = t + u * kT;
+        if (i < n_nodes) {
+            s_first[i] = fi[u];
+            s_rows[i] = ft[u] >= 0 ? o1[u] - o0[u] : -1;
+        }
+    }
+    if (t == 0) s_first[n_nodes] = fi_last;
+    __syncthreads();
+    int carry = 0, tot = 0;
+    for (int base = 0; base < n_items; base += kT) {   // exclusive scan of the counts
+        const int j = base + t;
+        const int v = j < n_items ? s_ex[j] : 0;
+        const int ex = block_exclusive_scan(v, s_scan, &tot);   // (its barriers order the writes below)
+        if (j < n_items) s_ex[j] = carry + ex;
+        carry += tot;
+    }
+    const int all = carry;
+    __syncthreads();
+    // rows going left in the node's earlier chunks; chunk j's node is the
+    // last node whose first chunk is at most j (empty nodes own no chunk)
+    for (int j = t; j < n_items; j += kT) {
+        int lo = 0, hi = n_nodes - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_first[mid] <= j) lo = mid;
+            else hi = mid - 1;
+        }
+        left_base[j] = s_ex[j] - s_ex[s_first[lo]];
+    }
+    carry = 0;
+    for (int base = 0; base < n_nodes; base += kT) {   // output extents over nodes
+        const int i = base + t;
+        const int v = i < n_nodes && s_rows[i] > 0 ? s_rows[i] : 0;
+        const int ex = block_exclusive_scan(v, s_scan, &tot);
+        if (i < n_nodes) {
+            const int f0 = s_first[i], f1 = s_first[i + 1];
+            const int e0 = f0 < n_items ? s_ex[f0] : all;
+            const int e1 = f1 < n_items ? s_ex[f1] : all;
+            const int rec[3] = {carry + ex, e1 - e0, s_rows[i] >= 0 ? 1 : 0};
+            for (int k = 0; k < 3; ++k) {
+                node_out[3 * i + k] = rec[k];
+                host_out[3 * i + k] = rec[k];   // pinned host memory: the host reads it after the stream passes
+            }
+        }
+        carry += tot;
+    }
+    if (t == 0) *err_host = *err_dev;
+}
+
 // Write each row to its place: the chunk's left rows from its left base on,
 // its right rows from its right base on, in position order.  Step j covers
 // positions begin + j * 1024 .. + 1023: a lane's rank among the step's left
@@ -2731,8 +2843,12 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
     __shared__ int s_left[kPartRows][kPartThreads / kWave];
     __shared__ int s_all[kPartRows][kPartThreads / kWave];
     const PartItem it = items[blockIdx.x];
-    const SplitOut sp = splits[it.node];
-    if (sp.feature < 0) return;   // uniform: the node has no children
+    // Every load below depends on the chunk record alone, so all of them are
+    // in flight together; a node without a split (no children) stores nothing.
+    const bool has = splits[it.node].feature >= 0;   // uniform
+    const int lb = left_base[blockIdx.x];
+    const int base = node_out[3 * it.node];
+    const int n_left = node_out[3 * it.node + 1];
     const int lane = (int)(threadIdx.x & (kWave - 1));
     const int wv = (int)(threadIdx.x / kWave);
     const int waves = (int)(blockDim.x / kWave);
@@ -2749,7 +2865,7 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
     uint64_t bl[kPartRows], bi[kPartRows];   // per step: the wave's left rows, its rows
 #pragma unroll
     for (int j = 0; j < kPartRows; ++j) {
-        const bool in = k0 + j * kstep < it.end;
+        const bool in = has && k0 + j * kstep < it.end;
         bl[j] = __ballot(in && f[j] != 0);
         bi[j] = __ballot(in);
         if (lane == 0) {
@@ -2758,10 +2874,8 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
         }
     }
     __syncthreads();
-    const int lb = left_base[blockIdx.x];
-    const int base = node_out[3 * it.node];
-    int lpos = base + lb;                                                            // next left slot
-    int rpos = base + node_out[3 * it.node + 1] + (it.begin - it.node_begin - lb);   // next right slot
+    int lpos = base + lb;                                          // next left slot
+    int rpos = base + n_left + (it.begin - it.node_begin - lb);   // next right slot
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < kPartRows; ++j) {

@@ -88,8 +88,15 @@ constexpr int kSliceWaves = 4;
 constexpr int kSplitReduceMaxThreads = 1024;
 
 // partition_level: fixed-size chunks of each node's rows, one block each.
-constexpr int kPartThreads = 1024;   // threads of a count or scatter block (256 measured slower)
-constexpr int kPartChunk = 8192;
+// 512 threads of 8 positions: against 1,024 x 8, 1,024 x 16, 512 x 16,
+// 512 x 12, 512 x 4, 384 x 8, 256 x 8, 256 x 16 and 256 x 32 the fastest
+// count + scatter on a grown 10M x 28 tree (smaller chunks cost the scan more
+// chunks than they save)
+constexpr int kPartThreads = 512;   // threads of a count or scatter block
+constexpr int kPartChunk = 4096;
+// Largest level whose scan runs in LDS (k_part_scan_lds): chunks and nodes.
+constexpr int kPartScanLdsItems = 8192;
+constexpr int kPartScanLdsNodes = 4096;
 struct PartItem {
     int32_t node;
     int32_t begin, end;   // positions [begin, end) of the node's rows

@@ -75,6 +75,29 @@ def test_partition_vs_oracle(hgb, torch, seed, n, F, B, missing, children, u16):
     assert np.array_equal(got_rows, want_rows)
 
 
+@pytest.mark.parametrize("n_nodes", [4096, 4097])
+def test_partition_many_nodes(hgb, torch, n_nodes):
+    """Levels of 4,096 nodes (the scan held in LDS) and 4,097 (the scan in
+    global memory), with empty nodes, nodes without a split and nodes of one
+    row, against the oracle's partition."""
+    say("partition many nodes", n_nodes)
+    rng = np.random.default_rng(n_nodes)
+    w = synth.random_small(70, 60_000, 3, 16, True, 0)
+    node = rng.integers(0, n_nodes, w.n_rows)
+    node[node % 97 == 5] = 0   # some nodes left empty
+    rows = np.argsort(node, kind="stable").astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(np.bincount(node, minlength=n_nodes))]).astype(np.int32)
+    sp = np.zeros(n_nodes, dtype=oracle.SPLIT_DTYPE)
+    sp["feature"] = rng.integers(0, 3, n_nodes)
+    sp["bin"] = rng.integers(0, 16, n_nodes)
+    sp["default_left"] = rng.integers(0, 2, n_nodes)
+    sp["feature"][rng.random(n_nodes) < 0.1] = -1
+    want_rows, want_offs = oracle.partition(w.bins, w.n_bins, rows, offs, sp)
+    got_rows, got_offs = gpu_partition(hgb, torch, w, sp, rows, offs)
+    assert np.array_equal(got_offs.astype(np.int64), want_offs)
+    assert np.array_equal(got_rows, want_rows)
+
+
 def test_partition_every_direction(hgb, torch):
     """Splits chosen by hand on every feature and bin edge, both default
     directions, including bin n_bins - 1 (everything left) and missing rows."""
