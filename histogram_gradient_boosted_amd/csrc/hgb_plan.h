@@ -173,10 +173,12 @@ inline double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, 
 }
 
 // Threads of a k_split_reduce block: a node with many feature entries (a wide
-// matrix) takes 1,024, so each thread walks a few of them.
+// matrix) takes 1,024, so each thread walks a few of them; a node with at most
+// 64 entries (a narrow matrix) takes one wave, whose reduction steps need no
+// wait on other waves.
 inline unsigned split_reduce_threads(int n_entries)
 {
-    return n_entries >= 4096 ? (unsigned)kSplitReduceMaxThreads : 256u;
+    return n_entries >= 4096 ? (unsigned)kSplitReduceMaxThreads : n_entries <= 64 ? 64u : 256u;
 }
 
 inline FillPlan plan_rows(const PlanCtx* c)
