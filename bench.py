@@ -146,12 +146,14 @@ def prepare(ctx, w, g, h, torch):
 
 def step(ctx, w, plan, g, h):
     from histogram_gradient_boosted_amd import tree
+    # (grown trees: the library's error word is checked by the hgb_sync that
+    # follows the timed steps, as for the replayed ones)
     if getattr(plan, "oblivious", False):
-        tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        tree.grow_oblivious_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, sync=False)
         return
     if getattr(plan, "grow", False):
         # the whole level loop on the device: partition, build, subtract, split
-        tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+        tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, sync=False)
         return
     if plan.tree is not None:
         tree.replay_tree(ctx, plan.tree, g, h, w.lam, w.gamma)

@@ -35,7 +35,8 @@ EXPORTED = ("hgb_available", "hgb_create", "hgb_destroy", "hgb_last_error", "hgb
             "hgb_profile_enable",
             "hgb_profile_query", "hgb_set_precision", "hgb_partition_level",
             "hgb_subtract_find_splits", "hgb_begin_tree_objective", "hgb_copy_quantized",
-            "hgb_find_level_split", "hgb_find_splits_noalloc", "hgb_set_async_begin")
+            "hgb_find_level_split", "hgb_find_splits_noalloc", "hgb_set_async_begin",
+            "hgb_grow_level")
 
 # hgb_objective
 OBJECTIVES = {"squared": 0, "logistic": 1, "poisson": 2}
@@ -108,6 +109,9 @@ def load():
     lib.hgb_subtract_find_splits.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_double,
                                              ctypes.c_double, vp]
     lib.hgb_subtract_find_splits.restype = c_int
+    lib.hgb_grow_level.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp,
+                                   ctypes.POINTER(ctypes.c_int64), ctypes.c_double, ctypes.c_double, i32]
+    lib.hgb_grow_level.restype = c_int
     lib.hgb_profile_enable.argtypes = [vp, c_int]
     lib.hgb_profile_enable.restype = c_int
     lib.hgb_profile_query.argtypes = [vp, c_int, ctypes.POINTER(ctypes.c_double),
@@ -350,6 +354,42 @@ class Context:
             sp, op, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc),
             parent.ctypes.data_as(ctypes.c_void_p)), "partition_level")
         return child[: nc.value + 1].copy(), parent[: nc.value // 2].copy()
+
+    def grow_level(self, parent_hist, parent_splits, parent_rows, parent_offsets, child_rows, child_hist,
+                   child_splits, lam: float, gamma: float, oblivious: bool = False):
+        """One level in one call (hgb_grow_level): partition the parents' rows
+        into `child_rows`, build the smaller child of each pair into
+        `child_hist` (room for 2 * n_parents slots), derive the other and
+        score every child into `child_splits` (depthwise splits, or with
+        oblivious the level split: room for 2 * n_parents + 1 records).
+        parent_rows / parent_offsets None: the root.  Returns (child offsets,
+        built_is_right, parents, built rows) as numpy arrays and an int; no
+        children (offsets [0]) ends the tree."""
+        torch = self._torch
+        if parent_rows is None:
+            n_par, offs, pr, total = 1, None, None, self.n_rows
+        else:
+            offs = _i32_host(parent_offsets)
+            n_par = int(offs.shape[0]) - 1
+            total = int(offs[-1])
+            pr = self._dev(parent_rows, "parent_rows", torch.int32, total)
+        ph = self._dev(parent_hist, "parent_hist", torch.int64, n_par * self.node_elems)
+        ps = self._dev(parent_splits, "parent_splits", torch.uint8, n_par * SPLIT_BYTES)
+        cr = self._dev(child_rows, "child_rows", torch.int32, total) if total else None
+        ch = self._dev(child_hist, "child_hist", torch.int64, 2 * n_par * self.node_elems)
+        cs = self._dev(child_splits, "child_splits", torch.uint8, (2 * n_par + (1 if oblivious else 0)) * SPLIT_BYTES)
+        child = np.zeros(2 * n_par + 1, dtype=np.int32)
+        bir = np.zeros(n_par, dtype=np.uint8)
+        parent = np.zeros(n_par, dtype=np.int32)
+        nc = ctypes.c_int32(0)
+        built = ctypes.c_int64(0)
+        self._check(self._lib.hgb_grow_level(
+            self._h, ph, ps, pr, None if offs is None else offs.ctypes.data_as(ctypes.c_void_p), n_par,
+            cr, ch, cs, child.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc),
+            bir.ctypes.data_as(ctypes.c_void_p), parent.ctypes.data_as(ctypes.c_void_p), ctypes.byref(built),
+            ctypes.c_double(lam), ctypes.c_double(gamma), 1 if oblivious else 0), "grow_level")
+        P = nc.value // 2
+        return child[: nc.value + 1].copy(), bir[:P].copy(), parent[:P].copy(), int(built.value)
 
     def find_level_split(self, hist, n_nodes: int, lam: float, gamma: float, out):
         """Oblivious level split.  out: uint8 CUDA tensor of at least

@@ -1650,6 +1650,52 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     return HGB_OK;
 }
 
+hgb_status hgb_grow_level(hgb_ctx* c, const int64_t* parent_hist, const hgb_split* parent_splits,
+                          const int32_t* parent_rows, const int32_t* parent_offsets, int32_t n_parents,
+                          int32_t* child_rows, int64_t* child_hist, hgb_split* child_splits,
+                          int32_t* child_offsets, int32_t* n_children, uint8_t* built_is_right,
+                          int32_t* parent_node, int64_t* built_rows, double lambda, double gamma,
+                          int32_t oblivious)
+{
+    if (!c) return HGB_E_INVALID;
+    c->err.clear();
+    if (!parent_hist || !child_hist || !child_splits || !child_offsets || !n_children || !built_is_right)
+        return fail(c, HGB_E_INVALID, "grow_level: null pointer");
+    if (n_parents < 1 || n_parents > 32767)
+        return fail(c, HGB_E_INVALID, "grow_level: n_parents must be in [1, 32767]");
+    std::vector<int32_t> parents((size_t)n_parents);
+    hgb_status st = hgb_partition_level(c, parent_rows, parent_offsets, n_parents, parent_splits, child_rows,
+                                        child_offsets, n_children, parents.data());
+    if (st != HGB_OK) return st;
+    const int32_t nc = *n_children;
+    if (built_rows) *built_rows = 0;
+    if (nc == 0) return HGB_OK;
+    const int32_t n_pairs = nc / 2;
+    // the smaller child of each pair is built (the left one on a tie); the
+    // other's slot is -1, so its rows are not read
+    std::vector<int32_t> slots((size_t)nc, -1);
+    int64_t rows = 0;
+    for (int32_t j = 0; j < n_pairs; ++j) {
+        const int32_t nl = child_offsets[2 * j + 1] - child_offsets[2 * j];
+        const int32_t nr = child_offsets[2 * j + 2] - child_offsets[2 * j + 1];
+        const uint8_t right = nr < nl ? 1 : 0;
+        built_is_right[j] = right;
+        slots[2 * j + right] = 2 * j + right;
+        rows += right ? nr : nl;
+        if (parent_node) parent_node[j] = parents[j];
+    }
+    if (built_rows) *built_rows = rows;
+    st = hgb_build_level(c, child_rows, child_offsets, nc, child_hist, slots.data());
+    if (st != HGB_OK) return st;
+    if (oblivious) {
+        st = hgb_subtract_siblings_slots(c, parent_hist, child_hist, built_is_right, parents.data(), n_pairs);
+        if (st != HGB_OK) return st;
+        return hgb_find_level_split(c, child_hist, nc, lambda, gamma, child_splits);
+    }
+    return hgb_subtract_find_splits(c, parent_hist, child_hist, built_is_right, parents.data(), n_pairs, lambda,
+                                    gamma, child_splits);
+}
+
 hgb_status hgb_profile_enable(hgb_ctx* c, int enable)
 {
     if (!c) return HGB_E_INVALID;

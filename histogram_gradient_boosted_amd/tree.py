@@ -191,7 +191,8 @@ class DeviceLevel:
     built_rows: int = 0
 
 
-def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: float) -> List[DeviceLevel]:
+def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: float,
+                     sync: bool = True, fused: bool = True) -> List[DeviceLevel]:
     """Grow levels 0..depth-1 with the rows partitioned on the device.
 
     Each level: hgb_partition_level lays out the children of the previous
@@ -199,7 +200,11 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
     smaller child of each pair from that layout (the other node's slot is -1,
     so its rows are skipped); subtract_find_splits derives the other and scores
     every child.  Only the child sizes and each pair's parent come back
-    to the host (to size and plan the next level)."""
+    to the host (to size and plan the next level).  fused: the three calls of
+    a level as one hgb_grow_level (nothing runs on the host between them);
+    otherwise one call each, with the choice of the built children here.
+    sync: wait for the tree at the end (hgb_sync, which also reports a bad row
+    index); without it the caller syncs later."""
     import torch
     dev = torch.device("cuda", ctx.device)
     F, S = ctx.n_features, ctx.n_slots
@@ -213,6 +218,19 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
         prev = levels[-1]
         total = ctx.n_rows if prev.rows is None else int(prev.offsets[-1])
         out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        if fused:
+            # room for every child of every parent: the level's size is known
+            # only once the rows are partitioned, inside the call
+            hist = torch.empty((2 * prev.n_nodes, F, S, 2), dtype=torch.int64, device=dev)
+            sp = torch.empty(2 * prev.n_nodes * SPLIT_BYTES, dtype=torch.uint8, device=dev)
+            child, _, _, built_rows = ctx.grow_level(prev.hist, prev.splits, prev.rows, prev.offsets, out,
+                                                     hist, sp, lam, gamma)
+            n_nodes = int(child.shape[0]) - 1
+            if n_nodes == 0:
+                break
+            levels.append(DeviceLevel(d, n_nodes, out, child, hist[:n_nodes], sp[: n_nodes * SPLIT_BYTES],
+                                      built_rows))
+            continue
         child, split_nodes = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
         n_nodes = int(child.shape[0]) - 1
         if n_nodes == 0:
@@ -228,19 +246,21 @@ def grow_tree_device(ctx: Context, grad, hess, depth: int, lam: float, gamma: fl
         ctx.build_level(hist, out, child, slots)
         ctx.subtract_find_splits(prev.hist, hist, bir, lam, gamma, sp, split_nodes.astype(np.int32))
         levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
-    ctx.sync()
+    if sync:
+        ctx.sync()
     return levels
 
 
 def grow_oblivious_tree_device(ctx: Context, grad, hess, depth: int, lam: float,
-                               gamma: float) -> List[DeviceLevel]:
+                               gamma: float, sync: bool = True, fused: bool = True) -> List[DeviceLevel]:
     """Grow an oblivious (symmetric) tree of levels 0..depth-1 on the device:
     every node of a level takes the level's one (feature, bin, direction) from
     find_level_split, so every node of a split level gets two children (one
     may be empty).  Per level: partition_level with the node records,
     build_level of the smaller child of each pair, subtract_siblings for the
     other, find_level_split over all children.  Each level's `splits` holds
-    n_nodes + 1 records, the last one the level's."""
+    n_nodes + 1 records, the last one the level's.  sync, fused: as for
+    grow_tree_device."""
     import torch
     dev = torch.device("cuda", ctx.device)
     F, S = ctx.n_features, ctx.n_slots
@@ -254,6 +274,17 @@ def grow_oblivious_tree_device(ctx: Context, grad, hess, depth: int, lam: float,
         prev = levels[-1]
         total = ctx.n_rows if prev.rows is None else int(prev.offsets[-1])
         out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        if fused:
+            hist = torch.empty((2 * prev.n_nodes, F, S, 2), dtype=torch.int64, device=dev)
+            sp = torch.empty((2 * prev.n_nodes + 1) * SPLIT_BYTES, dtype=torch.uint8, device=dev)
+            child, _, _, built_rows = ctx.grow_level(prev.hist, prev.splits, prev.rows, prev.offsets, out,
+                                                     hist, sp, lam, gamma, oblivious=True)
+            n_nodes = int(child.shape[0]) - 1
+            if n_nodes == 0:
+                break
+            levels.append(DeviceLevel(d, n_nodes, out, child, hist[:n_nodes], sp[: (n_nodes + 1) * SPLIT_BYTES],
+                                      built_rows))
+            continue
         child, split_nodes = ctx.partition_level(prev.splits, out, prev.rows, prev.offsets)
         n_nodes = int(child.shape[0]) - 1
         if n_nodes == 0:
@@ -270,5 +301,6 @@ def grow_oblivious_tree_device(ctx: Context, grad, hess, depth: int, lam: float,
         ctx.subtract_siblings(prev.hist, hist, bir, split_nodes.astype(np.int32))
         ctx.find_level_split(hist, n_nodes, lam, gamma, sp)
         levels.append(DeviceLevel(d, n_nodes, out, child, hist, sp, int(counts[built].sum())))
-    ctx.sync()
+    if sync:
+        ctx.sync()
     return levels

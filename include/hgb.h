@@ -400,6 +400,54 @@ hgb_status hgb_partition_level(hgb_ctx* ctx, const int32_t* row_index_dev,
                                int32_t* parent_node_host);
 
 /*
+ * One level of a depthwise tree grown on the device, in one call: the level
+ * loop of [bonsai-10] "The device context lifecycle" (partition the previous
+ * level's rows on the device, build the new level, find its splits; only the
+ * child sizes cross the bus), with the histogram subtraction of [ybb] §3
+ * (build the child with fewer rows, the left one on a tie, and derive its
+ * sibling as parent minus built).  Exactly the calls
+ *   hgb_partition_level(parent_rows, parent_offsets, n_parents, parent_splits)
+ *   hgb_build_level(child_rows, child_offsets, n_children, child_hist, slots)
+ *       with slots[i] = i for the built child of each pair, -1 for the other
+ *   hgb_subtract_find_splits(parent_hist, child_hist, built_is_right,
+ *       parent_node, n_children / 2, lambda, gamma, child_splits)
+ * made back to back from the library, with no return to the caller in
+ * between: the host plans the build while the partition's scatter runs.
+ * With oblivious nonzero (the symmetric tree of [ybb] §5) the last call is
+ *   hgb_subtract_siblings_slots(parent_hist, child_hist, built_is_right,
+ *       parent_node, n_children / 2) then
+ *   hgb_find_level_split(child_hist, n_children, lambda, gamma, child_splits)
+ * and child_splits receives n_children + 1 records (the level's last).
+ *
+ * parent_hist_dev:      int64 [n_parents][F][S][2], the previous level's
+ *                       histograms (device).
+ * parent_splits_dev:    hgb_split [n_parents] (device).
+ * parent_rows_dev, parent_offsets_host, n_parents: the previous level's nodes
+ *                       as for hgb_partition_level (NULL, NULL, 1: the root).
+ * child_rows_dev:       int32 (device), room for every row of the parents.
+ * child_hist_dev:       int64 (device), room for 2 * n_parents node slots.
+ * child_splits_dev:     hgb_split (device), room for 2 * n_parents records
+ *                       (2 * n_parents + 1 when oblivious).
+ * child_offsets_host:   int32 [2 * n_parents + 1]; on return [0, n_children]
+ *                       hold the children's offsets into child_rows_dev.
+ * n_children_host:      on return, 2c for c parents with a split; 0 means the
+ *                       tree ends here (nothing is built).
+ * built_is_right_host:  uint8 [n_parents]; on return entry j is 1 when child
+ *                       2j + 1 (right) was built, 0 for child 2j.
+ * parent_node_host:     int32 [n_parents] or NULL; on return entry j holds the
+ *                       parent of children 2j and 2j + 1.
+ * built_rows_host:      int64 or NULL; on return the rows of the built children.
+ * Errors: as for the three calls (the first failing one's status; the calls
+ *         after it are not made).
+ */
+hgb_status hgb_grow_level(hgb_ctx* ctx, const int64_t* parent_hist_dev, const hgb_split* parent_splits_dev,
+                          const int32_t* parent_rows_dev, const int32_t* parent_offsets_host, int32_t n_parents,
+                          int32_t* child_rows_dev, int64_t* child_hist_dev, hgb_split* child_splits_dev,
+                          int32_t* child_offsets_host, int32_t* n_children_host, uint8_t* built_is_right_host,
+                          int32_t* parent_node_host, int64_t* built_rows_host, double lambda, double gamma,
+                          int32_t oblivious);
+
+/*
  * Per-kernel device timing ([bonsai-10] "The kernel": the pages' backend
  * prints an upload / gpu / unpack breakdown when asked).  When enabled, every
  * launch is bracketed by HIP events on the context's stream.

@@ -137,8 +137,9 @@ def oracle_oblivious_tree(w, depth, bits):
     return levels
 
 
-@pytest.mark.parametrize("name,n,bits", [("c3", 300_000, 30), ("c3", 300_000, 19), ("c5", 200_000, 30)])
-def test_oblivious_tree(hgb, torch, name, n, bits):
+@pytest.mark.parametrize("name,n,bits,fused", [("c3", 300_000, 30, True), ("c3", 300_000, 30, False),
+                                               ("c3", 300_000, 19, True), ("c5", 200_000, 30, True)])
+def test_oblivious_tree(hgb, torch, name, n, bits, fused):
     """A whole oblivious tree grown on the device (partition, build, subtract,
     level split per level) equals the oracle's, level by level."""
     say("oblivious tree", name, n, bits)
@@ -151,7 +152,7 @@ def test_oblivious_tree(hgb, torch, name, n, bits):
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
-    levels = tree.grow_oblivious_tree_device(ctx, g, h, depth, w.lam, w.gamma)
+    levels = tree.grow_oblivious_tree_device(ctx, g, h, depth, w.lam, w.gamma, fused=fused)
     assert len(levels) == len(want)
     for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(levels, want)):
         say("oblivious level", d, lv.n_nodes)

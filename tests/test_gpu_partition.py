@@ -164,11 +164,13 @@ def test_build_level_skips_slot_minus_one(hgb, torch):
             assert (got[i] == -9).all(), f"slot {i} was written"
 
 
-@pytest.mark.parametrize("n,bits", [(300_000, 30), (300_000, 19), (None, 30)])
-def test_c3_tree_device_partition(hgb, torch, n, bits):
+@pytest.mark.parametrize("n,bits,fused", [(300_000, 30, True), (300_000, 30, False), (300_000, 19, True),
+                                          (None, 30, True)])
+def test_c3_tree_device_partition(hgb, torch, n, bits, fused):
     """A whole c3 tree grown with the device partition equals the oracle's tree:
-    row lists, offsets, histograms and splits at every level."""
-    say("c3 device tree", n, bits)
+    row lists, offsets, histograms and splits at every level (fused: each
+    level one hgb_grow_level; else partition, build and tail called apart)."""
+    say("c3 device tree", n, bits, fused)
     from histogram_gradient_boosted_amd import tree
     w = synth.make("c3", n_rows=n)
     ctx = hgb.Context(0)
@@ -176,7 +178,7 @@ def test_c3_tree_device_partition(hgb, torch, n, bits):
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
-    levels = tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma)
+    levels = tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, fused=fused)
     want = oracle_tree(w, w.depth, bits)
     assert len(levels) == len(want)
     for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(levels, want)):
@@ -217,4 +219,31 @@ def test_tree_device_partition_hot_slots(hgb, torch, case):
             assert np.array_equal(lv.rows.cpu().numpy()[: int(offs[-1])], rows), f"level {d} rows"
         assert np.array_equal(lv.hist.cpu().numpy(), hist), f"level {d} histograms differ"
         assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"level {d}")
+    ctx.close()
+
+
+def test_grow_level_without_splits(hgb, torch):
+    """hgb_grow_level on parents none of which has a split: no children, and
+    nothing is built (the output buffers keep their poison)."""
+    say("grow level, no splits")
+    w = synth.random_small(71, 5_000, 3, 16, False, 4)
+    rows, offs = w.level.children_row_index, w.level.children_offsets
+    F, S = w.n_features, w.n_slots
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    ctx.begin_tree(g, h)
+    sp = np.zeros(4, dtype=oracle.SPLIT_DTYPE)
+    sp["feature"] = -1
+    parent_hist = torch.zeros((4, F, S, 2), dtype=torch.int64, device="cuda")
+    child_hist = torch.full((8, F, S, 2), -9, dtype=torch.int64, device="cuda")
+    child_sp = torch.full((8 * hgb.SPLIT_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    out = torch.full((int(offs[-1]),), -5, dtype=torch.int32, device="cuda")
+    child, bir, parents, built = ctx.grow_level(parent_hist, splits_dev(torch, sp),
+                                                torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int32)).cuda(),
+                                                offs, out, child_hist, child_sp, w.lam, w.gamma)
+    ctx.sync()
+    assert child.tolist() == [0] and bir.size == 0 and parents.size == 0 and built == 0
+    assert (child_hist.cpu().numpy() == -9).all() and (child_sp.cpu().numpy() == 7).all()
     ctx.close()
