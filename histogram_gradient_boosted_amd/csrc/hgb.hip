@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -18,6 +19,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 using namespace hgb;
@@ -37,6 +39,12 @@ constexpr int kMaxBlocks = 4096;
 // Default fixed-point precision of begin_tree (bits below the largest value).
 constexpr int kDefaultPrecision = 30;
 constexpr int kStages = 16;
+constexpr int kEpochEvents = 4;
+constexpr int kEpochUses = 6;
+// Pinned host words (host_words, 16 of them): [0..1] the maxima, [2] the
+// error word, and the sequence numbers kernels post after their results.
+constexpr int kHostTreeSeq = 8;
+constexpr int kHostPartSeq = 9;
 
 // Initial capacity of an upload stage: larger than any level's plan of the
 // matrices measured here (the level-3 plan of 131,072 x 16,384 is about 70 KB).
@@ -56,7 +64,7 @@ struct Stage {
     void* host = nullptr;   // pinned
     void* dev = nullptr;
     size_t cap = 0;
-    hipEvent_t ev = nullptr;
+    uint64_t release_seq = 0;    // the context's release count when its consumers were enqueued
     bool pending = false;
     const void* use = nullptr;   // what the kernels read: dev, or the pinned host copy
 };
@@ -124,11 +132,24 @@ struct hgb_ctx {
     uint32_t* max_part = nullptr;     // begin_tree: per-block maxima, 2 x kMaxBlocks
     int32_t* rot = nullptr;           // per feature: the skipped slot (stored bins are rotated by it)
     bool skip = false;                // the fills skip each feature's slot 0 (a hot slot exists)
-    hipEvent_t part_ready = nullptr;  // partition: the node records are on the host
-    hipEvent_t host_ready = nullptr;  // begin_tree, sync: small results are on the host
+    hipEvent_t host_ready = nullptr;  // hgb_sync: the stream has drained
 
     Stage stage[kStages];
     int stage_next = 0;
+    // Stage releases record no event of their own (an event on the stream
+    // costs the device about 3 us): every kEpochUses releases, one event of a
+    // small ring marks the stream, and a stage is reused once an event
+    // recorded after its release has passed.
+    uint64_t stage_seq = 0;                     // releases so far
+    hipEvent_t epoch_ev[kEpochEvents] = {};
+    uint64_t epoch_seq[kEpochEvents] = {};      // releases covered by each event
+    int epoch_next = 0;
+    uint64_t last_epoch_seq = 0;
+    // sequence numbers of the results kernels post to pinned host memory:
+    // the maxima of each tree (host_words[8]) and the node records of each
+    // partition (host_words[9])
+    uint32_t tree_seq = 0;
+    uint32_t part_seq = 0;
 
     // HGB_DEBUG_PLAN=1 in the environment prints each fill plan to stderr
     bool debug_plan = false;
@@ -197,78 +218,6 @@ hgb_status grow(hgb_ctx* c, T** p, int64_t* cap, int64_t need)
     return HGB_OK;
 }
 
-// Stage `bytes` of host data (a launch plan: items, slot lists) for the
-// kernels.  By default the kernels read it in place from the stage's pinned
-// host buffer: a plan is read once per block, and a copy kernel on the stream
-// would sit between a level's kernels (in place measured 1% faster for the
-// 10M x 28 tree, 6% for the grown one, whose next level is planned while the
-// device waits).  HGB_PLAN_HOST=0 copies it to the stage's device buffer on
-// the stream instead.  The stage is released (event recorded) by
-// stage_release after its consumers have been enqueued; a stage is reused
-// only once that event has completed.  (Copies on a second stream ordered by
-// events measured slower than either.)
-hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
-{
-    Stage& s = c->stage[c->stage_next];
-    c->stage_next = (c->stage_next + 1) % kStages;
-    if (s.pending) {
-        HGB_HIP(c, hipEventSynchronize(s.ev));
-        s.pending = false;
-    }
-    if (bytes > s.cap) {
-        // Reallocating pinned memory is slow (and a free synchronizes the
-        // device), so a stage starts large and at least doubles.
-        if (s.host) HGB_HIP(c, hipHostFree(s.host));
-        if (s.dev) HGB_HIP(c, hipFree(s.dev));
-        s.host = s.dev = nullptr;
-        const size_t want = std::max<size_t>(std::max<size_t>(bytes, 2 * s.cap), kStageMinBytes);
-        s.cap = 0;
-        HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
-        HGB_HIP(c, hipMalloc(&s.dev, want));
-        s.cap = want;
-    }
-    if (!s.ev) HGB_HIP(c, hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
-    if (bytes) {
-        std::memcpy(s.host, src, bytes);
-        if (!c->plan_host) HGB_HIP(c, hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, c->stream));
-    }
-    s.use = c->plan_host ? s.host : s.dev;
-    *out = &s;
-    return HGB_OK;
-}
-
-hgb_status stage_release(hgb_ctx* c, Stage* s)
-{
-    HGB_HIP(c, hipEventRecord(s->ev, c->stream));
-    s->pending = true;
-    return HGB_OK;
-}
-
-// A stage held from its upload until its consumers are enqueued.  release()
-// records the stage's event; on an early (error) return the destructor does,
-// so a plan that an already launched kernel reads is never handed out again
-// before that kernel is done.
-struct StageLease {
-    hgb_ctx* c;
-    Stage* s = nullptr;
-    explicit StageLease(hgb_ctx* ctx) : c(ctx) {}
-    StageLease(const StageLease&) = delete;
-    StageLease& operator=(const StageLease&) = delete;
-    hgb_status release()
-    {
-        Stage* t = s;
-        s = nullptr;
-        return t ? stage_release(c, t) : HGB_OK;
-    }
-    ~StageLease()
-    {
-        if (s) {
-            (void)hipEventRecord(s->ev, c->stream);
-            s->pending = true;
-        }
-    }
-};
-
 // Wait for `ev`: poll it for up to kPollMicros, then block.  A level loop
 // waits for small results (maxima, node records) several times per tree, most
 // of them ready within tens of microseconds, where a blocking wait would add
@@ -289,6 +238,132 @@ hgb_status poll_event(hgb_ctx* c, hipEvent_t ev)
     HGB_HIP(c, hipEventSynchronize(ev));
     return HGB_OK;
 }
+
+// Wait until a kernel has stored `want` into the pinned word w (its last
+// store, after the results it hands the host): poll for up to kPollMicros,
+// then keep polling but yield the core between checks (a sleep would wake
+// tens of microseconds late, and the device waits for the host's next
+// launches).  Every 64th check also asks the stream: one that has drained
+// without the store (a launch that failed) is an error, not a hang.
+hgb_status wait_word(hgb_ctx* c, const uint32_t* w, uint32_t want)
+{
+    const volatile uint32_t* vw = w;
+    const auto t0 = std::chrono::steady_clock::now();
+    bool spin = true;
+    for (uint64_t i = 0;; ++i) {
+        if (*vw == want) {
+            std::atomic_thread_fence(std::memory_order_acquire);
+            return HGB_OK;
+        }
+        if (spin) {
+            const auto waited = std::chrono::steady_clock::now() - t0;
+            spin = std::chrono::duration_cast<std::chrono::microseconds>(waited).count() < kPollMicros;
+            continue;
+        }
+        if ((i & 63) == 0) {
+            const hipError_t e = hipStreamQuery(c->stream);
+            if (*vw == want) continue;   // (taken at the top)
+            if (e == hipSuccess) return fail(c, HGB_E_DEVICE, "the stream drained without a kernel's result");
+            if (e != hipErrorNotReady) return fail(c, HGB_E_DEVICE, "HIP error: %s", hipGetErrorString(e));
+        }
+        std::this_thread::yield();
+    }
+}
+
+// Mark the stream with the next event of the epoch ring: it covers every
+// stage released so far.
+hgb_status record_epoch(hgb_ctx* c)
+{
+    const int k = c->epoch_next;
+    if (!c->epoch_ev[k]) HGB_HIP(c, hipEventCreateWithFlags(&c->epoch_ev[k], hipEventDisableTiming));
+    HGB_HIP(c, hipEventRecord(c->epoch_ev[k], c->stream));
+    c->epoch_seq[k] = c->stage_seq;
+    c->last_epoch_seq = c->stage_seq;
+    c->epoch_next = (k + 1) % kEpochEvents;
+    return HGB_OK;
+}
+
+// Stage `bytes` of host data (a launch plan: items, slot lists) for the
+// kernels.  By default the kernels read it in place from the stage's pinned
+// host buffer: a plan is read once per block, and a copy kernel on the stream
+// would sit between a level's kernels (in place measured 1% faster for the
+// 10M x 28 tree, 6% for the grown one, whose next level is planned while the
+// device waits).  HGB_PLAN_HOST=0 copies it to the stage's device buffer on
+// the stream instead.  The stage is released by stage_release after its
+// consumers have been enqueued; it is reused only once an epoch event
+// recorded after that release has passed (one is recorded then if none
+// was).  (Copies on a second stream ordered by events measured slower than
+// either.)
+hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
+{
+    Stage& s = c->stage[c->stage_next];
+    c->stage_next = (c->stage_next + 1) % kStages;
+    if (s.pending) {
+        // the earliest epoch event that covers the release
+        int best = -1;
+        for (int k = 0; k < kEpochEvents; ++k)
+            if (c->epoch_ev[k] && c->epoch_seq[k] >= s.release_seq &&
+                (best < 0 || c->epoch_seq[k] < c->epoch_seq[best]))
+                best = k;
+        if (best < 0) {
+            best = c->epoch_next;
+            hgb_status st = record_epoch(c);
+            if (st != HGB_OK) return st;
+        }
+        hgb_status st = poll_event(c, c->epoch_ev[best]);
+        if (st != HGB_OK) return st;
+        s.pending = false;
+    }
+    if (bytes > s.cap) {
+        // Reallocating pinned memory is slow (and a free synchronizes the
+        // device), so a stage starts large and at least doubles.
+        if (s.host) HGB_HIP(c, hipHostFree(s.host));
+        if (s.dev) HGB_HIP(c, hipFree(s.dev));
+        s.host = s.dev = nullptr;
+        const size_t want = std::max<size_t>(std::max<size_t>(bytes, 2 * s.cap), kStageMinBytes);
+        s.cap = 0;
+        HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
+        HGB_HIP(c, hipMalloc(&s.dev, want));
+        s.cap = want;
+    }
+    if (bytes) {
+        std::memcpy(s.host, src, bytes);
+        if (!c->plan_host) HGB_HIP(c, hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, c->stream));
+    }
+    s.use = c->plan_host ? s.host : s.dev;
+    *out = &s;
+    return HGB_OK;
+}
+
+hgb_status stage_release(hgb_ctx* c, Stage* s)
+{
+    s->release_seq = ++c->stage_seq;
+    s->pending = true;
+    if (c->stage_seq - c->last_epoch_seq >= (uint64_t)kEpochUses) return record_epoch(c);
+    return HGB_OK;
+}
+
+// A stage held from its upload until its consumers are enqueued.  release()
+// marks it released; on an early (error) return the destructor does, so a
+// plan that an already launched kernel reads is never handed out again
+// before that kernel is done.
+struct StageLease {
+    hgb_ctx* c;
+    Stage* s = nullptr;
+    explicit StageLease(hgb_ctx* ctx) : c(ctx) {}
+    StageLease(const StageLease&) = delete;
+    StageLease& operator=(const StageLease&) = delete;
+    hgb_status release()
+    {
+        Stage* t = s;
+        s = nullptr;
+        return t ? stage_release(c, t) : HGB_OK;
+    }
+    ~StageLease()
+    {
+        if (s) (void)stage_release(c, s);
+    }
+};
 
 // Record `*ev` (created on first use) on the stream and poll it.
 hgb_status wait_here(hgb_ctx* c, hipEvent_t* ev)
@@ -650,7 +725,7 @@ hgb_status fill_level(hgb_ctx* c, const FillPlan& plan, const std::vector<std::p
 }  // namespace
 
 // The current tree's exponents from the maxima k_max_final wrote into pinned
-// host memory (the event host_ready has passed).  Returns nullptr, or what
+// host memory (the tree's number has arrived after them).  Returns nullptr, or what
 // was not finite.
 static const char* read_scales(hgb_ctx* c)
 {
@@ -680,7 +755,7 @@ static const char* read_scales(hgb_ctx* c)
 static hgb_status resolve_scales(hgb_ctx* c)
 {
     if (!c->scales_pending) return HGB_OK;
-    const hgb_status st = poll_event(c, c->host_ready);
+    const hgb_status st = wait_word(c, c->host_words + kHostTreeSeq, c->tree_seq);
     if (st != HGB_OK) return st;
     c->scales_pending = false;
     if (const char* bad = read_scales(c)) {
@@ -714,15 +789,13 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
         HGB_LAUNCHED(c, "k_grad_hess_max");
         k_max_final<<<1, 256, 0, c->stream>>>(c->max_part, max_blocks, c->dev_words, c->precision,
                                               (double*)(c->dev_words + 4), c->host_words, c->dev_words + 3,
-                                              Src::kGuess ? 1 : 0);
+                                              Src::kGuess ? 1 : 0, c->host_words + kHostTreeSeq, ++c->tree_seq);
         HGB_LAUNCHED(c, "k_max_final");
     }
     // k_max_final wrote the maxima into pinned host memory too (the host
-    // checks them and keeps the exponents for the split pass); the quantize
-    // pass, which takes its scales from the device, already runs while the
-    // host waits on an event recorded before that pass.
-    if (!c->host_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->host_ready, hipEventDisableTiming));
-    HGB_HIP(c, hipEventRecord(c->host_ready, c->stream));
+    // checks them and keeps the exponents for the split pass), then the
+    // tree's number; the quantize pass, which takes its scales from the
+    // device, already runs while the host waits for that number.
     {
         ProfScope ps(c, HGB_KERNEL_QUANTIZE);
         k_quantize<Src><<<grid_for((c->n + 3) / 4, 256, 8192), 256, 0, c->stream>>>(
@@ -735,7 +808,7 @@ static hgb_status begin_tree_from(hgb_ctx* c, const Src& src, int vec)
         c->have_tree = true;
         return HGB_OK;
     }
-    hgb_status wst = poll_event(c, c->host_ready);
+    hgb_status wst = wait_word(c, c->host_words + kHostTreeSeq, c->tree_seq);
     if (wst != HGB_OK) return wst;
     if (const char* bad = read_scales(c)) return fail(c, HGB_E_NONFINITE, "%s", bad);
     c->have_tree = true;
@@ -818,6 +891,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
         hgb_destroy(c);
         return HGB_E_DEVICE;
     }
+    std::memset(c->host_words, 0, 64);   // no sequence number posted yet
     *out = c;
     return HGB_OK;
 }
@@ -829,17 +903,17 @@ void hgb_destroy(hgb_ctx* c)
     (void)hipSetDevice(c->device);
     (void)hipStreamSynchronize(c->stream);
     for (Stage& s : c->stage) {
-        if (s.ev) (void)hipEventDestroy(s.ev);
         if (s.host) (void)hipHostFree(s.host);
         if (s.dev) (void)hipFree(s.dev);
     }
+    for (hipEvent_t e : c->epoch_ev)
+        if (e) (void)hipEventDestroy(e);
     for (auto& v : c->ev_pending)
         for (auto& pr : v) {
             (void)hipEventDestroy(pr.first);
             (void)hipEventDestroy(pr.second);
         }
     for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
-    if (c->part_ready) (void)hipEventDestroy(c->part_ready);
     if (c->host_ready) (void)hipEventDestroy(c->host_ready);
     (void)hipFree(c->bins);
     (void)hipFree(c->bins_rm);
@@ -1611,17 +1685,19 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
                     c->dev_words + 2);
             HGB_LAUNCHED(c, "k_part_count");
         }
+        const uint32_t seq = ++c->part_seq;
         if (n_items <= kPartScanLdsItems && n_nodes <= kPartScanLdsNodes)
             k_part_scan_lds<kPartScanLdsItems, kPartScanLdsNodes><<<1, 1024, 0, c->stream>>>(
                 cnt, (int)n_items, (const int32_t*)(dev + off_first), (const int32_t*)(dev + off_offs), sp, n_nodes,
-                left_base, node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
+                left_base, node_out, c->part_host, c->dev_words + 2, c->host_words + 2,
+                c->host_words + kHostPartSeq, seq);
         else
             k_part_scan<<<1, 1024, 0, c->stream>>>(cnt, items_dev, (int)n_items, (const int32_t*)(dev + off_first),
                                                    (const int32_t*)(dev + off_offs), sp, n_nodes, left_base,
-                                                   node_out, c->part_host, c->dev_words + 2, c->host_words + 2);
-        HGB_LAUNCHED(c, "k_part_scan");   // node records and error word written to pinned host memory
-        if (!c->part_ready) HGB_HIP(c, hipEventCreateWithFlags(&c->part_ready, hipEventDisableTiming));
-        HGB_HIP(c, hipEventRecord(c->part_ready, c->stream));
+                                                   node_out, c->part_host, c->dev_words + 2, c->host_words + 2,
+                                                   c->host_words + kHostPartSeq, seq);
+        // node records, error word, then the level's number, into pinned host memory
+        HGB_LAUNCHED(c, "k_part_scan");
         if (n_items > 0) {
             k_part_scatter<<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(row_index, items_dev, sp, c->part_flags,
                                                                       left_base, node_out, out_rows);
@@ -1632,7 +1708,7 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     if (st != HGB_OK) return st;
     // Wait for the node records only: the scatter keeps running while the
     // caller plans the next level (the stream orders whatever reads its rows).
-    st = poll_event(c, c->part_ready);
+    st = wait_word(c, c->host_words + kHostPartSeq, c->part_seq);
     if (st != HGB_OK) return st;
     st = take_flags(c);   // a row index outside [0, n)
     if (st != HGB_OK) return st;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
                                                    uint32_t* __restrict__ out, int precision,
                                                    double* __restrict__ scales,
                                                    uint32_t* __restrict__ host_out, uint32_t* __restrict__ redo,
-                                                   int guessed)
+                                                   int guessed, uint32_t* __restrict__ host_seq, uint32_t seq)
 {
     __shared__ uint32_t red[2][256];
     uint32_t mg = 0, mh = 0;
@@ -312,6 +312,10 @@ __global__ __launch_bounds__(256) void k_max_final(const uint32_t* __restrict__ 
         scales[1] = sh;
         scales[2] = inv_scale_of_max(red[0][0], precision);
         scales[3] = inv_scale_of_max(red[1][0], precision);
+        // the tree's number last, once the maxima are visible to the host:
+        // the host waits for it instead of for an event on the stream
+        __threadfence_system();
+        *host_seq = seq;
     }
 }
 
@@ -2646,6 +2650,16 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
     }
 }
 
+// The block's results for the host are in pinned memory: every thread makes
+// its own stores visible system-wide, then thread 0 stores the sequence
+// number the host waits for.  Every thread calls.
+__device__ inline void publish_seq(uint32_t* host_seq, uint32_t seq)
+{
+    __threadfence_system();
+    __syncthreads();
+    if (threadIdx.x == 0) *host_seq = seq;
+}
+
 // Block-wide exclusive scan of v (blockDim.x values, a multiple of 64 up to
 // 1,024), returning this thread's prefix; *total receives the sum.  Each wave
 // scans its 64 values with shuffles, wave 0 scans the waves' totals, and three
@@ -2691,7 +2705,8 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ node_out,
                                                     int32_t* __restrict__ host_out,
                                                     const uint32_t* __restrict__ err_dev,
-                                                    uint32_t* __restrict__ err_host)
+                                                    uint32_t* __restrict__ err_host,
+                                                    uint32_t* __restrict__ host_seq, uint32_t seq)
 {
     __shared__ int s_scan[1024];
     int carry = 0, tot = 0;
@@ -2724,10 +2739,12 @@ __global__ __launch_bounds__(1024) void k_part_scan(const int32_t* __restrict__ 
         carry += tot;
     }
     // the node records and the count pass's error word straight into pinned
-    // host memory: the host reads them once the stream passes this kernel
+    // host memory, then the level's number once they are visible (the host
+    // waits for it)
     __syncthreads();
     for (int i = threadIdx.x; i < 3 * n_nodes; i += blockDim.x) host_out[i] = node_out[i];
     if (threadIdx.x == 0) *err_host = *err_dev;
+    publish_seq(host_seq, seq);
 }
 
 // k_part_scan for a level of at most MAXI chunks and MAXN nodes, by one block
@@ -2746,7 +2763,8 @@ __global__ __launch_bounds__(1024) void k_part_scan_lds(const int32_t* __restric
                                                         int32_t* __restrict__ node_out,
                                                         int32_t* __restrict__ host_out,
                                                         const uint32_t* __restrict__ err_dev,
-                                                        uint32_t* __restrict__ err_host)
+                                                        uint32_t* __restrict__ err_host,
+                                                        uint32_t* __restrict__ host_seq, uint32_t seq)
 {
     constexpr int kT = 1024;
     constexpr int IP = MAXI / kT, NP = MAXN / kT;   // entries per thread
@@ -2823,6 +2841,7 @@ __global__ __launch_bounds__(1024) void k_part_scan_lds(const int32_t* __restric
         carry += tot;
     }
     if (t == 0) *err_host = *err_dev;
+    publish_seq(host_seq, seq);
 }
 
 // Write each row to its place: the chunk's left rows from its left base on,
