@@ -147,6 +147,8 @@ def trace_summary(db: str, step_equiv: int, command: str) -> str:
     if step_equiv <= 0:
         step_equiv = max(1, sum(len(ds) for name, ds in per.items() if name.split("::")[-1] == "k_max_final"))
     lines = [f"# Kernel trace: `{command}`", "",
+             f"Summarized by `python bench_counters.py --trace-summary <dir>/kt_results.db --trace-command "
+             f"'<the command above>' --trace-out <this file>`.", "",
              "rocprofv3 --kernel-trace --stats; durations in microseconds.  One process runs "
              f"{step_equiv} step-equivalents of the tree (the set-up tree, warm-up, the timed and "
              "the event-timed passes, counted by begin_tree's k_max_final); 'per step' divides "
