@@ -247,3 +247,39 @@ def test_grow_level_without_splits(hgb, torch):
     assert child.tolist() == [0] and bir.size == 0 and parents.size == 0 and built == 0
     assert (child_hist.cpu().numpy() == -9).all() and (child_sp.cpu().numpy() == 7).all()
     ctx.close()
+
+
+def test_many_trees_on_one_context(hgb, torch):
+    """Twelve grown trees of eight levels on one context, queued without a
+    wait between trees: the launch plans' staging slots are reused many
+    times behind the library's stream markers, and the maxima and node
+    records are read back through the sequence words.  Every tree equals the
+    first, level by level, and the first equals the oracle's."""
+    say("many trees, one context")
+    from histogram_gradient_boosted_amd import tree
+    w = synth.make("c3", n_rows=200_000)
+    ctx = hgb.Context(0)
+    ctx.set_async_begin(True)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    trees = [tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, sync=False) for _ in range(12)]
+    ctx.sync()
+    want = oracle_tree(w, w.depth, 30)
+    first = trees[0]
+    assert len(first) == len(want)
+    for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(first, want)):
+        if d > 0:
+            assert np.array_equal(lv.offsets.astype(np.int64), offs), f"level {d} offsets"
+        assert np.array_equal(lv.hist.cpu().numpy(), hist), f"level {d} histograms differ"
+        assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"level {d}")
+    for t, levels in enumerate(trees[1:], 1):
+        assert len(levels) == len(first), f"tree {t}"
+        for d, (a, b) in enumerate(zip(first, levels)):
+            assert a.n_nodes == b.n_nodes, f"tree {t} level {d}"
+            if d > 0:
+                assert np.array_equal(a.offsets, b.offsets), f"tree {t} level {d} offsets"
+                assert torch.equal(a.rows[: int(a.offsets[-1])], b.rows[: int(b.offsets[-1])]), f"tree {t} level {d} rows"
+            assert torch.equal(a.hist, b.hist), f"tree {t} level {d} histograms"
+            assert torch.equal(a.splits, b.splits), f"tree {t} level {d} splits"
+    ctx.close()
