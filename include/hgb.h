@@ -437,8 +437,11 @@ hgb_status hgb_partition_level(hgb_ctx* ctx, const int32_t* row_index_dev,
  * parent_node_host:     int32 [n_parents] or NULL; on return entry j holds the
  *                       parent of children 2j and 2j + 1.
  * built_rows_host:      int64 or NULL; on return the rows of the built children.
- * Errors: as for the three calls (the first failing one's status; the calls
- *         after it are not made).
+ * lambda, gamma:        as for hgb_find_splits.
+ * oblivious:            nonzero for the oblivious level split (above).
+ * Errors: HGB_E_INVALID for null output pointers or n_parents outside
+ *         [1, 32767]; otherwise as for the three calls (the first failing
+ *         one's status; the calls after it are not made).
  */
 hgb_status hgb_grow_level(hgb_ctx* ctx, const int64_t* parent_hist_dev, const hgb_split* parent_splits_dev,
                           const int32_t* parent_rows_dev, const int32_t* parent_offsets_host, int32_t n_parents,
