@@ -283,3 +283,37 @@ def test_many_trees_on_one_context(hgb, torch):
             assert torch.equal(a.hist, b.hist), f"tree {t} level {d} histograms"
             assert torch.equal(a.splits, b.splits), f"tree {t} level {d} splits"
     ctx.close()
+
+
+def test_grow_level_errors(hgb, torch):
+    """hgb_grow_level's own checks, through the C ABI: null outputs and a
+    parent count outside [1, 32767] are HGB_E_INVALID, before any work."""
+    say("grow level errors")
+    import ctypes
+    w = synth.random_small(72, 2_000, 2, 8, False, 0)
+    ctx = hgb.Context(0)
+    ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
+    g = torch.from_numpy(w.grad).cuda()
+    h = torch.from_numpy(w.hess).cuda()
+    ctx.begin_tree(g, h)
+    lib = hgb.load()
+    F, S = w.n_features, w.n_slots
+    ph = torch.zeros((1, F, S, 2), dtype=torch.int64, device="cuda")
+    ps = torch.zeros(hgb.SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    cr = torch.zeros(w.n_rows, dtype=torch.int32, device="cuda")
+    ch = torch.zeros((2, F, S, 2), dtype=torch.int64, device="cuda")
+    cs = torch.zeros(3 * hgb.SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    offs = np.zeros(3, dtype=np.int32)
+    bir = np.zeros(1, dtype=np.uint8)
+    nc = ctypes.c_int32(0)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    def call(n_parents, hist_out=True):
+        return lib.hgb_grow_level(ctx._h, p(ph), p(ps), None, None, n_parents, p(cr),
+                                  p(ch) if hist_out else None, p(cs), offs.ctypes.data_as(ctypes.c_void_p),
+                                  ctypes.byref(nc), bir.ctypes.data_as(ctypes.c_void_p), None, None,
+                                  ctypes.c_double(1.0), ctypes.c_double(0.0), 0)
+    assert call(1, hist_out=False) == hgb.HGB_E_INVALID
+    assert call(0) == hgb.HGB_E_INVALID
+    assert call(32768) == hgb.HGB_E_INVALID
+    ctx.sync()
+    ctx.close()
