@@ -442,6 +442,59 @@ struct LevelCut {
     int64_t align = 128;                 // cuts inside a node fall on multiples of this
 };
 
+// x rounded down to a multiple of `align` (> 0); a mask when align is a power
+// of two, as it is unless overridden (a 64-bit division costs tens of cycles
+// and the level cut rounds once per piece).
+inline int64_t round_down(int64_t x, int64_t align)
+{
+    return (align & (align - 1)) == 0 ? x & ~(align - 1) : x / align * align;
+}
+
+// The number of shares the level cut makes from nodes of count[] rows with a
+// cost budget b per share (each piece costs piece_rows plus its rows; b is at
+// least piece_rows + align), or a number above `limit` once it passes it.  The
+// cut fills shares greedily in level order: a share is closed once less than
+// piece_rows + align of its budget is left; a piece that does not end its node
+// ends on a multiple of align rows.  A fresh share's piece that does not end
+// its node therefore takes `full` = round_down(b - piece_rows) rows and closes
+// the share (less than align is left), so a node's run of such pieces is
+// counted with one division instead of piece by piece.
+inline int64_t level_shares(const std::vector<int64_t>& count, int64_t b, int64_t piece_rows, int64_t align,
+                            int64_t limit)
+{
+    const int64_t room = b - piece_rows;   // >= align
+    const int64_t full = round_down(room, align);
+    int64_t left = b, n = 0;
+    bool open = false;
+    for (const int64_t rows : count) {
+        int64_t rem = rows;
+        while (rem > 0) {
+            if (open && left < piece_rows + align) {
+                if (++n > limit) return n;
+                left = b;
+                open = false;
+            }
+            if (!open && rem > room) {
+                // k fresh shares of `full` rows until at most `room` are left
+                // (rem stays > 0: full <= room); all but the last are closed
+                const int64_t k = (rem - room + full - 1) / full;
+                n += k - 1;
+                if (n > limit) return n;
+                rem -= k * full;
+                left = room - full;
+                open = true;
+                continue;
+            }
+            int64_t take = std::min(rem, left - piece_rows);
+            if (take < rem) take = std::min(std::max<int64_t>(round_down(take, align), align), rem);
+            left -= piece_rows + take;
+            open = true;
+            rem -= take;
+        }
+    }
+    return n + (open ? 1 : 0);
+}
+
 // begin[i], count[i]: node i's rows in the level order (count 0: empty or
 // skipped); slots[i]: its output slot (-1: skipped).  Returns nullptr, or a
 // message when the level needs more partial histograms or items than the
@@ -492,7 +545,7 @@ inline const char* cut_level(const PlanCtx* c, const FillPlan& plan, const std::
                 }
                 int64_t take = std::min(end - at, left - piece_rows);
                 // inside a node, cut on multiples of `align` rows
-                if (at + take < end) take = std::max<int64_t>(take / align * align, align);
+                if (at + take < end) take = std::max<int64_t>(round_down(take, align), align);
                 take = std::min(take, end - at);
                 pieces.push_back({i, at, at + take, pieces_of[i]++});
                 left -= piece_rows + take;
@@ -511,10 +564,7 @@ inline const char* cut_level(const PlanCtx* c, const FillPlan& plan, const std::
         int64_t lo = std::max<int64_t>((built + piece_rows * nonempty + shares - 1) / shares,
                                        piece_rows + align);
         const int64_t cap = std::max<int64_t>(built + piece_rows * (nonempty + 1) + align, lo);
-        auto fits = [&](int64_t b) {
-            budget = b;
-            return cut() <= shares;
-        };
+        auto fits = [&](int64_t b) { return level_shares(count, b, piece_rows, align, shares) <= shares; };
         int64_t hi = lo;
         while (hi < cap && !fits(hi)) {
             lo = hi + 1;

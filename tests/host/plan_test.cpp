@@ -2,7 +2,7 @@
 // tiles, the level cut, the root cut and the partition's chunks, on the five
 // workloads' shapes and on adversarial node lists (65,535 nodes, empty and
 // skipped nodes, one giant node, level orders ending near 2^31).  Built with
-// the address and undefined-behaviour sanitizers by tests/test_host_plan.py.
+// the address and undefined-behaviour sanitizers by tests/test_sanitizers.py.
 #include "hgb_plan.h"
 
 #include <cstdio>
@@ -97,6 +97,8 @@ static void check_level(const PlanCtx& c, const FillPlan& p, const std::vector<s
     CHECK(cut.n_shares <= shares_cap, "%s: %lld shares > one round of %lld", what, (long long)cut.n_shares,
           (long long)shares_cap);
     CHECK(cut.block_first.front() == 0 && cut.block_first.back() == (int32_t)cut.items.size(), "%s: block list", what);
+    CHECK(level_shares(count, cut.budget, cut.piece_rows, cut.align, INT64_MAX) == cut.n_shares,
+          "%s: counted shares differ from the cut's %lld", what, (long long)cut.n_shares);
     // node of each item: by its row range (the nodes' ranges are disjoint and ordered)
     std::vector<std::pair<int64_t, int>> starts;
     for (int i = 0; i < n_nodes; ++i)
@@ -231,6 +233,43 @@ static void check_root(const PlanCtx& c, FillPlan p, const char* what)
     }
 }
 
+// level_shares against the greedy rule applied piece by piece: a share takes
+// pieces while at least piece_rows + align of its budget is left, each piece
+// as many rows as the rest of the budget allows after its piece_rows, cut to
+// a multiple of align unless it ends the node.  Also the early exit: a
+// count above `limit` is reported as such.
+static void check_level_shares(std::mt19937_64& rng)
+{
+    for (int k = 0; k < 3000; ++k) {
+        const int nn = 1 + (int)(rng() % 40);
+        std::vector<int64_t> count(nn);
+        for (auto& v : count) v = rng() % 4 == 0 ? 0 : (int64_t)(rng() % (rng() % 2 ? 300 : 30000));
+        const int64_t align = rng() % 3 == 0 ? 8 * (1 + (int64_t)(rng() % 40)) : (int64_t)1 << (3 + rng() % 6);
+        const int64_t piece_rows = 1 + (int64_t)(rng() % 2000);
+        const int64_t b = piece_rows + align + (int64_t)(rng() % (rng() % 2 ? 500 : 20000));
+        int64_t shares = 0, left = 0;
+        for (const int64_t rows : count)
+            for (int64_t done = 0; done < rows;) {
+                if (shares == 0 || left < piece_rows + align) {
+                    ++shares;
+                    left = b;
+                }
+                int64_t take = left - piece_rows;
+                if (take < rows - done) take = std::max<int64_t>(take - take % align, align);
+                take = std::min(take, rows - done);
+                left -= piece_rows + take;
+                done += take;
+            }
+        CHECK(level_shares(count, b, piece_rows, align, INT64_MAX) == shares,
+              "level_shares (b %lld, piece %lld, align %lld): %lld != %lld", (long long)b, (long long)piece_rows,
+              (long long)align, (long long)level_shares(count, b, piece_rows, align, INT64_MAX), (long long)shares);
+        if (shares > 0) {
+            const int64_t limit = (int64_t)(rng() % (uint64_t)shares);
+            CHECK(level_shares(count, b, piece_rows, align, limit) > limit, "early exit at %lld", (long long)limit);
+        }
+    }
+}
+
 static void check_part(const std::vector<int32_t>& offs, const char* what)
 {
     const int n_nodes = (int)offs.size() - 1;
@@ -348,6 +387,7 @@ int main()
             run(cnt, slots_for(cnt.size()), "random level");
         }
     }
+    check_level_shares(rng);
     // Partition chunks, including nodes that end at 2^31 - 1.
     check_part({0, 1, 8192, 8193, 20000}, "small");
     check_part({0, INT32_MAX - 5000, INT32_MAX - 1, INT32_MAX}, "ending at 2^31 - 1");
