@@ -33,6 +33,7 @@ constexpr int64_t kHotSlotShare = 16;
 // included): below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
+constexpr int64_t kTransposeMaxBlocks = 65536;   // k_transpose's blocks per feature group (they stride)
 // begin_tree's max pass: at most this many blocks, each writing its pair of
 // maxima for k_max_final.
 constexpr int kMaxBlocks = 4096;
@@ -1090,7 +1091,8 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
         HGB_HIP(c, hipMalloc(&c->bins_rm, (size_t)(stride * n_rows + kRowMajorSlack)));
         HGB_HIP(c, hipMemsetAsync(c->bins_rm, 0, (size_t)(stride * n_rows + kRowMajorSlack), c->stream));
         c->rm_stride = stride;
-        dim3 tgrid((unsigned)((n_rows + 63) / 64), (unsigned)((n_features + 63) / 64));
+        dim3 tgrid((unsigned)std::min<int64_t>(((int64_t)n_rows + 63) / 64, kTransposeMaxBlocks),
+                   (unsigned)((n_features + 63) / 64));
         if (bin_bytes == 1)
             k_transpose<uint8_t><<<tgrid, 256, 0, c->stream>>>((const uint8_t*)c->bins,
                                                               (uint8_t*)c->bins_rm, n_rows, n_features, stride);

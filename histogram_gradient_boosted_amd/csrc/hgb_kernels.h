@@ -448,27 +448,33 @@ __global__ __launch_bounds__(256) void k_bins_max(const BinT* __restrict__ bins,
 
 // upload_bins: row-major copy of the feature-major matrix, dst row r at byte
 // r * row_stride (row_stride >= F * sizeof(BinT), padding zeroed beforehand),
-// through a 64 x 64 LDS tile so both sides stay coalesced.
+// through a 64 x 64 LDS tile so both sides stay coalesced.  Blocks stride
+// over the 64-row tiles (a launch's blocks times threads must stay below
+// 2^32, fewer than 2^31 rows need up to 2^25 tiles).
 template <typename BinT>
 __global__ __launch_bounds__(256) void k_transpose(const BinT* __restrict__ src,
                                                    uint8_t* __restrict__ dst, int64_t n, int F,
                                                    int64_t row_stride)
 {
     __shared__ BinT tile[64][65];
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int f0 = blockIdx.y * 64;
     const int tx = threadIdx.x & 63;
     const int ty = threadIdx.x >> 6;
-    for (int j = ty; j < 64; j += 4) {
-        const int f = f0 + j;
-        const int64_t r = r0 + tx;
-        if (f < F && r < n) tile[j][tx] = src[(int64_t)f * n + r];
-    }
-    __syncthreads();
-    for (int j = ty; j < 64; j += 4) {
-        const int64_t r = r0 + j;
-        const int f = f0 + tx;
-        if (r < n && f < F) ((BinT*)(dst + r * row_stride))[f] = tile[tx][j];
+    const int64_t n_tiles = (n + 63) / 64;
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {   // uniform across the block
+        const int64_t r0 = t * 64;
+        for (int j = ty; j < 64; j += 4) {
+            const int f = f0 + j;
+            const int64_t r = r0 + tx;
+            if (f < F && r < n) tile[j][tx] = src[(int64_t)f * n + r];
+        }
+        __syncthreads();
+        for (int j = ty; j < 64; j += 4) {
+            const int64_t r = r0 + j;
+            const int f = f0 + tx;
+            if (r < n && f < F) ((BinT*)(dst + r * row_stride))[f] = tile[tx][j];
+        }
+        __syncthreads();   // the tile is rewritten next
     }
 }
 

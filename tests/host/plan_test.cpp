@@ -291,11 +291,12 @@ static void check_part(const std::vector<int32_t>& offs, const char* what)
 
 int main()
 {
-    // The five workloads' shapes: plans and tiles at P = 30 and 19, with and
+    // The five workloads' shapes and 2^31 - 1 rows: plans and tiles at P = 30, 19 and 12, with and
     // without the skipped slot.
     struct Shape { int64_t n; int F, S, w; } shapes[] = {
         {4096, 8, 256, 1}, {1000000, 100, 256, 1}, {10000000, 28, 256, 1}, {131072, 16384, 256, 1},
-        {2000000, 50, 1025, 2}, {50000, 12, 257, 2}, {20000, 33000, 5, 2}, {1000, 3, 4096, 2}};
+        {2000000, 50, 1025, 2}, {50000, 12, 257, 2}, {20000, 33000, 5, 2}, {1000, 3, 4096, 2},
+        {INT32_MAX, 2, 256, 1}, {INT32_MAX, 1, 4096, 2}};
     for (const Shape& sh : shapes)
         for (int prec : {30, 19, 12})
             for (bool skip : {false, true})
@@ -363,6 +364,7 @@ int main()
         run({INT32_MAX - 3}, slots_for(1), "one node of 2^31 - 4 rows");
         run({5, INT32_MAX - 200, 0, 190}, slots_for(4), "giant node among small ones, total 2^31 - 5");
         run({1, 2, 3}, slots_for(3), "tiny level");
+        run({1 << 30, (1 << 30) - 1}, {-1, 1}, "skipped left child of 2^30 rows, built right one of 2^30 - 1");
         run({0}, slots_for(1), "one empty node");
         // skipped nodes (slot -1) and scattered output slots
         {
