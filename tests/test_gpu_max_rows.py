@@ -6,7 +6,9 @@ The inputs are patterns whose exact histograms have closed forms, so nothing
 here walks two billion rows on the host:
 
 - feature 0 holds r mod 256, feature 1 holds (r div 256) mod 256 (u8, 256 bins);
-- g = +1 when bit 15 of r is clear and -1 when it is set, h = 1.
+- g = +1 when bit 15 of r is clear and -1 when it is set, h = 1: given as
+  fp32 arrays, or derived on the device from the squared loss with score 0
+  and label -g (g = m - y, h = 1).
 
 Both maxima are 1, so the scale exponent is k = P - 1 = 29 at P = 30 and
 every code is +-2^29.  Bit 15 of r is bit 7 of feature 1's bin, so the best
@@ -104,12 +106,15 @@ def assert_ascending_with_bit15(torch, x, bit, first, last, count):
 
 @pytest.mark.gpu
 @pytest.mark.timeout(300)
-def test_max_rows_root_and_level(hgb, torch):
+@pytest.mark.parametrize("source,oblivious", [("grad", False), ("squared", True)])
+def test_max_rows_root_and_level(hgb, torch, source, oblivious):
+    """Root and one level; the second case grows the level as an oblivious
+    tree (its records: the two children's, then the level's)."""
     torch.cuda.empty_cache()
     free, _ = torch.cuda.mem_get_info()
     if free < 100 * 2**30:
         pytest.skip(f"needs about 80 GB of device memory, {free / 2**30:.0f} GiB free")
-    say("max rows: n = 2^31 - 1, two u8 features")
+    say("max rows: n = 2^31 - 1, two u8 features,", source)
     root_want, right_want = expected_histograms(N)
     left_want = root_want - right_want
     lam, gamma = 1.0, 0.0
@@ -120,14 +125,21 @@ def test_max_rows_root_and_level(hgb, torch):
     bins[1] = ((ar >> 8) & 255).to(torch.uint8)
     g = ((ar >> 15) & 1).to(torch.float32).mul_(-2.0).add_(1.0)
     del ar
-    h = torch.ones(N, dtype=torch.float32, device="cuda")
+    if source == "grad":
+        h = torch.ones(N, dtype=torch.float32, device="cuda")
+    else:
+        h = torch.zeros(N, dtype=torch.float32, device="cuda")   # the score
+        g.neg_()                                                  # the label
     torch.cuda.synchronize()
 
     ctx = hgb.Context(0)
     try:
         ctx.upload_bins(bins, BINS, False)
         del bins
-        ctx.begin_tree(g, h)
+        if source == "grad":
+            ctx.begin_tree(g, h)
+        else:
+            ctx.begin_tree_objective("squared", h, g)
         assert ctx.get_scales() == (29, 29)
         say("max rows: root fill")
         hist = torch.empty((1, 2, BINS, 2), dtype=torch.int64, device="cuda")
@@ -144,9 +156,10 @@ def test_max_rows_root_and_level(hgb, torch):
         say("max rows: partition and level 1")
         child_rows = torch.empty(N, dtype=torch.int32, device="cuda")
         child_hist = torch.empty((2, 2, BINS, 2), dtype=torch.int64, device="cuda")
-        child_sp = torch.empty(2 * hgb.SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+        n_rec = 3 if oblivious else 2
+        child_sp = torch.empty(n_rec * hgb.SPLIT_BYTES, dtype=torch.uint8, device="cuda")
         offs, bir, parents, built = ctx.grow_level(hist, sp_root, None, None, child_rows, child_hist,
-                                                   child_sp, lam, gamma)
+                                                   child_sp, lam, gamma, oblivious=oblivious)
         ctx.sync()
         n_left = 2**30   # rows with bit 15 clear: 32,768 per 65,536, the last cycle one short of full
         assert offs.tolist() == [0, n_left, N]
@@ -157,8 +170,12 @@ def test_max_rows_root_and_level(hgb, torch):
         got = child_hist.cpu().numpy()
         assert np.array_equal(got[1], right_want), "built (right) child"
         assert np.array_equal(got[0], left_want), "derived (left) child"
-        want_csp = oracle.find_splits(np.stack([left_want, right_want]), BINS, False, 29, 29, lam, gamma)
-        assert_splits(hgb.splits_to_numpy(child_sp)[:2], want_csp, "level 1")
+        both = np.stack([left_want, right_want])
+        if oblivious:
+            want_csp = oracle.find_level_split(both, BINS, False, 29, 29, lam, gamma)
+        else:
+            want_csp = oracle.find_splits(both, BINS, False, 29, 29, lam, gamma)
+        assert_splits(hgb.splits_to_numpy(child_sp)[:n_rec], want_csp, "level 1")
     finally:
         ctx.close()
         del g, h
