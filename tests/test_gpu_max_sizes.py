@@ -1,9 +1,15 @@
-"""The largest matrix the boundary takes: n = 2^31 - 1 rows (the most an int32
-row count holds), through upload, begin_tree, the root fill, the split scan,
-the device partition and one grown level, about 80 GB of device memory in all.
+"""The largest sizes the boundary takes.
 
-The inputs are patterns whose exact histograms have closed forms, so nothing
-here walks two billion rows on the host:
+Features: 65,535 (the most a 16-bit feature field holds), one-byte bins whose
+rows fit the row-major copy (64 KiB) and two-byte bins with a missing slot
+whose rows do not (the feature-major fills), root and a level, against the
+oracle.
+
+Rows: n = 2^31 - 1 (the most an int32 row count holds), through upload,
+begin_tree, the root fill, the split scan, the device partition and one
+grown level, about 80 GB of device memory in all.  The inputs are patterns
+whose exact histograms have closed forms, so nothing here walks two billion
+rows on the host:
 
 - feature 0 holds r mod 256, feature 1 holds (r div 256) mod 256 (u8, 256 bins);
 - g = +1 when bit 15 of r is clear and -1 when it is set, h = 1: given as
@@ -22,7 +28,9 @@ import pytest
 
 import oracle
 
-from test_gpu_parity import assert_splits, say
+from histogram_gradient_boosted_amd import synth
+
+from test_gpu_parity import assert_splits, run_level_both, run_root_both, say
 
 N = 2**31 - 1
 Q = 2**29        # the code of +-1 at k = 29
@@ -42,6 +50,20 @@ def torch():
 def hgb(torch):
     from histogram_gradient_boosted_amd import binding
     return binding
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed,n,B,missing,u16", [(90, 1200, 256, False, False), (91, 800, 300, True, True)])
+def test_max_features(hgb, torch, seed, n, B, missing, u16):
+    """65,535 features: the root, then four children built from their
+    parents (parents, built children, subtraction, splits), bit-exact."""
+    say("max features", seed, n, B, missing, u16)
+    torch.cuda.empty_cache()
+    w = synth.random_small(seed, n, 65535, B, missing, 0, u16=u16)
+    run_root_both(hgb, torch, w)
+    w = synth.random_small(seed, n, 65535, B, missing, 4, u16=u16)
+    run_level_both(hgb, torch, w, check_exact_gain=True)
+    torch.cuda.empty_cache()
 
 
 def zeros_among(m):
