@@ -5,6 +5,8 @@ rows fit the row-major copy (64 KiB) and two-byte bins with a missing slot
 whose rows do not (the feature-major fills), root and a level, against the
 oracle.
 
+Slots: 4,096 per feature (4,096 value bins, or 4,095 and the missing slot).
+
 Rows: n = 2^31 - 1 (the most an int32 row count holds), through upload,
 begin_tree, the root fill, the split scan, the device partition and one
 grown level, about 80 GB of device memory in all.  The inputs are patterns
@@ -64,6 +66,19 @@ def test_max_features(hgb, torch, seed, n, B, missing, u16):
     w = synth.random_small(seed, n, 65535, B, missing, 4, u16=u16)
     run_level_both(hgb, torch, w, check_exact_gain=True)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed,n,F,B,missing", [(92, 50_000, 5, 4096, False), (93, 30_000, 40, 4095, True)])
+@pytest.mark.parametrize("bits", [30, 19])
+def test_max_slots(hgb, torch, seed, n, F, B, missing, bits):
+    """4,096 slots per feature: the root and six children, bit-exact, with
+    wide and packed sums."""
+    say("max slots", seed, n, F, B, missing, bits)
+    w = synth.random_small(seed, n, F, B, missing, 0, u16=True)
+    run_root_both(hgb, torch, w, bits)
+    w = synth.random_small(seed, n, F, B, missing, 6, u16=True)
+    run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
 
 
 def zeros_among(m):
