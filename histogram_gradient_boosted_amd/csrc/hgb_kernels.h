@@ -2852,11 +2852,13 @@ __global__ __launch_bounds__(1024) void k_part_scan_lds(const int32_t* __restric
 
 // Write each row to its place: the chunk's left rows from its left base on,
 // its right rows from its right base on, in position order.  Step j covers
-// positions begin + j * 1024 .. + 1023: a lane's rank among the step's left
-// (right) rows is its wave's ballot below it plus the earlier waves' counts,
-// and the steps follow each other.  Every wave publishes its counts of all
-// steps at once, so one barrier serves the whole chunk.  The stores of a
-// wave's left (right) rows in one step are one contiguous run.
+// positions begin + j * kPartThreads .. + kPartThreads - 1: a lane's rank
+// among the step's left (right) rows is its wave's ballot below it plus the
+// counts of every (step, wave) before its own in position order.  Every wave
+// publishes its counts of all steps at once; wave 0 turns the 64 (step,
+// wave) counts into exclusive prefixes with one shuffle scan, so each lane
+// reads two prefixes per step.  The stores of a wave's left (right) rows in
+// one step are one contiguous run.
 __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __restrict__ row_index,
                                                        const PartItem* __restrict__ items,
                                                        const SplitOut* __restrict__ splits,
@@ -2865,8 +2867,10 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
                                                        const int32_t* __restrict__ node_out,
                                                        int32_t* __restrict__ out_rows)
 {
-    __shared__ int s_left[kPartRows][kPartThreads / kWave];
-    __shared__ int s_all[kPartRows][kPartThreads / kWave];
+    constexpr int kWaves = kPartThreads / kWave;
+    static_assert(kPartRows * kWaves == kWave, "one lane of wave 0 per (step, wave)");
+    __shared__ int s_left[kPartRows * kWaves];   // per (step, wave): its left rows, then those before it
+    __shared__ int s_all[kPartRows * kWaves];    // the same for all its rows
     const PartItem it = items[blockIdx.x];
     // Every load below depends on the chunk record alone, so all of them are
     // in flight together; a node without a split (no children) stores nothing.
@@ -2876,7 +2880,6 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
     const int n_left = node_out[3 * it.node + 1];
     const int lane = (int)(threadIdx.x & (kWave - 1));
     const int wv = (int)(threadIdx.x / kWave);
-    const int waves = (int)(blockDim.x / kWave);
     const int64_t k0 = (int64_t)it.begin + threadIdx.x;   // 64 bits: see k_part_count
     const int64_t kstep = blockDim.x;
     int32_t r[kPartRows];
@@ -2894,32 +2897,37 @@ __global__ __launch_bounds__(kPartThreads) void k_part_scatter(const int32_t* __
         bl[j] = __ballot(in && f[j] != 0);
         bi[j] = __ballot(in);
         if (lane == 0) {
-            s_left[j][wv] = __popcll(bl[j]);
-            s_all[j][wv] = __popcll(bi[j]);
+            s_left[j * kWaves + wv] = __popcll(bl[j]);
+            s_all[j * kWaves + wv] = __popcll(bi[j]);
         }
     }
     __syncthreads();
-    int lpos = base + lb;                                          // next left slot
-    int rpos = base + n_left + (it.begin - it.node_begin - lb);   // next right slot
+    if (wv == 0) {
+        const int l = s_left[lane], a = s_all[lane];
+        int xl = l, xa = a;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int yl = __shfl_up(xl, d, kWave), ya = __shfl_up(xa, d, kWave);
+            if (lane >= d) {
+                xl += yl;
+                xa += ya;
+            }
+        }
+        s_left[lane] = xl - l;
+        s_all[lane] = xa - a;
+    }
+    __syncthreads();
+    const int lbase = base + lb;                                   // the chunk's first left slot
+    const int rbase = base + n_left + (it.begin - it.node_begin - lb);   // and its first right slot
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < kPartRows; ++j) {
-        int wl = 0, wa = 0, tl = 0, ta = 0;   // earlier waves' and all waves' counts
-        for (int w = 0; w < waves; ++w) {
-            const int nl = s_left[j][w], na = s_all[j][w];
-            wl += w < wv ? nl : 0;
-            wa += w < wv ? na : 0;
-            tl += nl;
-            ta += na;
-        }
+        const int pl = s_left[j * kWaves + wv], pa = s_all[j * kWaves + wv];
         if ((bi[j] >> lane) & 1ull) {
             if ((bl[j] >> lane) & 1ull)
-                out_rows[lpos + wl + __popcll(bl[j] & below)] = r[j];
+                out_rows[lbase + pl + __popcll(bl[j] & below)] = r[j];
             else
-                out_rows[rpos + (wa - wl) + __popcll(bi[j] & ~bl[j] & below)] = r[j];
+                out_rows[rbase + (pa - pl) + __popcll(bi[j] & ~bl[j] & below)] = r[j];
         }
-        lpos += tl;
-        rpos += ta - tl;
     }
 }
 
