@@ -1604,9 +1604,11 @@ hgb_status hgb_subtract_find_splits(hgb_ctx* c, const int64_t* parent, int64_t* 
     return s.release();
 }
 
-hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
-                               int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
-                               int32_t* child_offsets, int32_t* n_children, int32_t* parent_node)
+// The partition; nt: read the split features' bins with non-temporal loads
+// (depthwise levels, whose nodes split on many features).
+static hgb_status partition_impl(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
+                                 int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
+                                 int32_t* child_offsets, int32_t* n_children, int32_t* parent_node, bool nt)
 {
     if (!c) return HGB_E_INVALID;
     c->err.clear();
@@ -1677,14 +1679,18 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     {
         ProfScope ps(c, HGB_KERNEL_PARTITION);
         if (n_items > 0) {
-            if (c->bin_bytes == 1)
-                k_part_count<uint8_t><<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(
-                    (const uint8_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
-                    c->dev_words + 2);
-            else
-                k_part_count<uint16_t><<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(
-                    (const uint16_t*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags,
-                    c->dev_words + 2);
+#define HGB_PART_COUNT(BinT, NT)                                                                      \
+    k_part_count<BinT, NT><<<(unsigned)n_items, kPartThreads, 0, c->stream>>>(                        \
+        (const BinT*)c->bins, c->n, c->B, c->S, c->rot, row_index, items_dev, sp, cnt, c->part_flags, \
+        c->dev_words + 2)
+            if (c->bin_bytes == 1) {
+                if (nt) HGB_PART_COUNT(uint8_t, true);
+                else HGB_PART_COUNT(uint8_t, false);
+            } else {
+                if (nt) HGB_PART_COUNT(uint16_t, true);
+                else HGB_PART_COUNT(uint16_t, false);
+            }
+#undef HGB_PART_COUNT
             HGB_LAUNCHED(c, "k_part_count");
         }
         const uint32_t seq = ++c->part_seq;
@@ -1728,6 +1734,14 @@ hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32
     return HGB_OK;
 }
 
+hgb_status hgb_partition_level(hgb_ctx* c, const int32_t* row_index, const int32_t* node_offsets,
+                               int32_t n_nodes, const hgb_split* splits, int32_t* out_rows,
+                               int32_t* child_offsets, int32_t* n_children, int32_t* parent_node)
+{
+    return partition_impl(c, row_index, node_offsets, n_nodes, splits, out_rows, child_offsets, n_children,
+                          parent_node, false);
+}
+
 hgb_status hgb_grow_level(hgb_ctx* c, const int64_t* parent_hist, const hgb_split* parent_splits,
                           const int32_t* parent_rows, const int32_t* parent_offsets, int32_t n_parents,
                           int32_t* child_rows, int64_t* child_hist, hgb_split* child_splits,
@@ -1742,8 +1756,8 @@ hgb_status hgb_grow_level(hgb_ctx* c, const int64_t* parent_hist, const hgb_spli
     if (n_parents < 1 || n_parents > 32767)
         return fail(c, HGB_E_INVALID, "grow_level: n_parents must be in [1, 32767]");
     std::vector<int32_t> parents((size_t)n_parents);
-    hgb_status st = hgb_partition_level(c, parent_rows, parent_offsets, n_parents, parent_splits, child_rows,
-                                        child_offsets, n_children, parents.data());
+    hgb_status st = partition_impl(c, parent_rows, parent_offsets, n_parents, parent_splits, child_rows,
+                                   child_offsets, n_children, parents.data(), !oblivious);
     if (st != HGB_OK) return st;
     const int32_t nc = *n_children;
     if (built_rows) *built_rows = 0;

@@ -2596,8 +2596,12 @@ constexpr int kPartRows = 8;
 static_assert(kPartChunk == kPartThreads * kPartRows, "a chunk is one pass of a block");
 
 // Count the rows going left per chunk, and record each position's direction
-// (1 = left) for the scatter.
-template <typename BinT>
+// (1 = left) for the scatter.  NT reads the split features' bins with
+// non-temporal loads: when the nodes split on many features those scattered
+// lines are read once and would only push the next level fill's rows out of
+// the caches; when they share one feature (an oblivious level) the lines are
+// read again by other chunks and stay cached.
+template <typename BinT, bool NT>
 __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restrict__ bins, int64_t n, int n_bins,
                                                      int S, const int32_t* __restrict__ rot,
                                                      const int32_t* __restrict__ row_index,
@@ -2632,7 +2636,8 @@ __global__ __launch_bounds__(kPartThreads) void k_part_count(const BinT* __restr
     for (int j = 0; j < kPartRows; ++j) {
         const bool in = (uint64_t)r[j] < (uint64_t)n;
         bad |= has && !in && k0 + j * kstep < it.end;
-        v[j] = unrotate((int)col[in ? r[j] : 0], rf, S);
+        const BinT* at = col + (in ? r[j] : 0);
+        v[j] = unrotate((int)(NT ? __builtin_nontemporal_load(at) : *at), rf, S);
     }
     int c = 0;
 #pragma unroll
