@@ -2291,7 +2291,7 @@ struct SplitOut {
     long long g_left, h_left, g_total, h_total;
 };
 
-// One block per node (256 or 1024 threads, a power of two): the best feature,
+// One block per node (64, 256 or 1,024 threads, a power of two): the best feature,
 // scanning features in order per thread -- four entries loaded before any is
 // compared -- and then reducing across threads with the same (gain, feature)
 // order.  (kSplitReduceMaxThreads: hgb_layout.h)
