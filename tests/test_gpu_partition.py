@@ -285,6 +285,46 @@ def test_many_trees_on_one_context(hgb, torch):
     ctx.close()
 
 
+def test_two_contexts_on_two_streams(hgb, torch):
+    """Two contexts, each on a stream of its own, grow trees of different
+    matrices (one-byte bins, and two-byte bins with a missing slot and hot
+    slots) with their work queued together on the device: each tree equals
+    its oracle's, so nothing of one context (staging, scratch, sequence
+    words, launch attributes) leaks into the other."""
+    say("two contexts, two streams")
+    from histogram_gradient_boosted_amd import tree
+    wa = synth.make("c3", n_rows=150_000)
+    wb = synth.make("c5", n_rows=60_000)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ca, cb = hgb.Context(0, sa), hgb.Context(0, sb)
+    ca.set_async_begin(True)
+    cb.set_async_begin(True)
+    ga, ha = torch.from_numpy(wa.grad).cuda(), torch.from_numpy(wa.hess).cuda()
+    gb, hb = torch.from_numpy(wb.grad).cuda(), torch.from_numpy(wb.hess).cuda()
+    torch.cuda.synchronize()
+    ca.upload_bins(wa.bins, wa.n_bins, wa.has_missing)
+    cb.upload_bins(wb.bins, wb.n_bins, wb.has_missing)
+    got = {"a": [], "b": []}
+    for _ in range(3):   # alternate whole trees: each queues behind the other's on the device
+        with torch.cuda.stream(sa):
+            got["a"].append(tree.grow_tree_device(ca, ga, ha, 6, wa.lam, wa.gamma, sync=False))
+        with torch.cuda.stream(sb):
+            got["b"].append(tree.grow_tree_device(cb, gb, hb, 6, wb.lam, wb.gamma, sync=False))
+    ca.sync()
+    cb.sync()
+    for key, w in (("a", wa), ("b", wb)):
+        want = oracle_tree(w, 6, 30)
+        for t, levels in enumerate(got[key]):
+            assert len(levels) == len(want), f"{key} tree {t}"
+            for d, (lv, (rows, offs, hist, sp)) in enumerate(zip(levels, want)):
+                if d > 0:
+                    assert np.array_equal(lv.offsets.astype(np.int64), offs), f"{key} tree {t} level {d} offsets"
+                assert np.array_equal(lv.hist.cpu().numpy(), hist), f"{key} tree {t} level {d} histograms"
+                assert_splits(hgb.splits_to_numpy(lv.splits)[: lv.n_nodes], sp, f"{key} tree {t} level {d}")
+    ca.close()
+    cb.close()
+
+
 def test_grow_level_errors(hgb, torch):
     """hgb_grow_level's own checks, through the C ABI: null outputs and a
     parent count outside [1, 32767] are HGB_E_INVALID, before any work."""
