@@ -33,6 +33,13 @@ constexpr int64_t kHotSlotShare = 16;
 // included): below the root, a level reads only its built rows' lines from it.
 constexpr int64_t kRowMajorMaxRowBytes = 65536;
 constexpr int64_t kRowMajorSlack = 32;   // >= the widest row-tile load
+// A row of the row-major copy is padded to a multiple of 16 bytes, and by
+// kRowMajorSkew more when that is a multiple of kRowMajorSkewPeriod: with a
+// stride of a large power of two (16,384 one-byte features), one tile's
+// chunks of every row share their low address bits, and the level fill that
+// reads them ran about 4% slower.
+constexpr int64_t kRowMajorSkew = 128;
+constexpr int64_t kRowMajorSkewPeriod = 1024;
 constexpr int64_t kTransposeMaxBlocks = 65536;   // k_transpose's blocks per feature group (they stride)
 // begin_tree's max pass: at most this many blocks, each writing its pair of
 // maxima for k_max_final.
@@ -162,8 +169,10 @@ struct hgb_ctx {
     // (ipc = items per CU), align (rows an item boundary is a multiple of),
     // piece (fixed cost of a level item, in rows), il (row-major level fill,
     // wide sums) and root_il (root fill, wide or packed sums): 1 slot-major
-    // interleaved tile, 0 feature-major; -1 keeps the planner's choice.
-    int tune[10] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+    // interleaved tile, 0 feature-major; pair (row-major interleaved level
+    // fills with 32-byte chunks: 1 two lanes per row, 0 one); -1 keeps the
+    // planner's choice.
+    int tune[kTuneKeys] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
     // optional per-kernel timing
     bool prof = false;
@@ -436,7 +445,7 @@ PlanCtx plan_ctx(const hgb_ctx* c)
     pc.skip = c->skip;
     pc.rm_stride = c->bins_rm ? c->rm_stride : 0;
     pc.n_cu = c->n_cu;
-    for (int k = 0; k < 10; ++k) pc.tune[k] = c->tune[k];
+    for (int k = 0; k < kTuneKeys; ++k) pc.tune[k] = c->tune[k];
     return pc;
 }
 
@@ -547,29 +556,32 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
-            case 32: HGB_ROWS(32, kRegAccCells, kRegAccEntries, false); break;
-            case 16: HGB_ROWS(16, kRegAccCells, kRegAccEntries, false); break;
-            case 8: HGB_ROWS(8, kRegAccCells, kRegAccEntries, false); break;
-            case 4: HGB_ROWS(4, kRegAccCells, kRegAccEntries, false); break;
-            default: HGB_ROWS(2, kRegAccCells, kRegAccEntries, false); break;
+            case 32: HGB_ROWS(32, kRegAccCells, kRegAccEntries, 0); break;
+            case 16: HGB_ROWS(16, kRegAccCells, kRegAccEntries, 0); break;
+            case 8: HGB_ROWS(8, kRegAccCells, kRegAccEntries, 0); break;
+            case 4: HGB_ROWS(4, kRegAccCells, kRegAccEntries, 0); break;
+            default: HGB_ROWS(2, kRegAccCells, kRegAccEntries, 0); break;
             }
         } else {
             if (p.ra != 0) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
-            if (p.il) {
+            if (p.il == 2) {   // lane pairs: 32-byte chunks only
+                if (p.lt != 2 * kPairHalfBytes) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
+                HGB_ROWS(32, 0, kWideRowEntries, 2);
+            } else if (p.il) {
                 switch (p.lt) {
-                case 32: HGB_ROWS(32, 0, kWideRowEntries, true); break;
-                case 16: HGB_ROWS(16, 0, kWideRowEntries, true); break;
-                case 8: HGB_ROWS(8, 0, kWideRowEntries, true); break;
-                case 4: HGB_ROWS(4, 0, kWideRowEntries, true); break;
-                default: HGB_ROWS(2, 0, kWideRowEntries, true); break;
+                case 32: HGB_ROWS(32, 0, kWideRowEntries, 1); break;
+                case 16: HGB_ROWS(16, 0, kWideRowEntries, 1); break;
+                case 8: HGB_ROWS(8, 0, kWideRowEntries, 1); break;
+                case 4: HGB_ROWS(4, 0, kWideRowEntries, 1); break;
+                default: HGB_ROWS(2, 0, kWideRowEntries, 1); break;
                 }
             } else {
                 switch (p.lt) {
-                case 32: HGB_ROWS(32, 0, kWideRowEntries, false); break;
-                case 16: HGB_ROWS(16, 0, kWideRowEntries, false); break;
-                case 8: HGB_ROWS(8, 0, kWideRowEntries, false); break;
-                case 4: HGB_ROWS(4, 0, kWideRowEntries, false); break;
-                default: HGB_ROWS(2, 0, kWideRowEntries, false); break;
+                case 32: HGB_ROWS(32, 0, kWideRowEntries, 0); break;
+                case 16: HGB_ROWS(16, 0, kWideRowEntries, 0); break;
+                case 8: HGB_ROWS(8, 0, kWideRowEntries, 0); break;
+                case 4: HGB_ROWS(4, 0, kWideRowEntries, 0); break;
+                default: HGB_ROWS(2, 0, kWideRowEntries, 0); break;
                 }
             }
         }
@@ -851,8 +863,8 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
     if (const char* e = std::getenv("HGB_DEBUG_PLAN")) c->debug_plan = e[0] == '1';
     if (const char* e = std::getenv("HGB_PLAN_HOST")) c->plan_host = e[0] != '0';
     if (const char* e = std::getenv("HGB_FILL_TUNE")) {
-        static const char* keys[10] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile",
-                                       "level_ipc", "align", "piece", "il", "root_il"};
+        static const char* keys[kTuneKeys] = {"root_lc", "root_tile", "root_ipc", "level_lc", "level_tile",
+                                              "level_ipc", "align", "piece", "il", "root_il", "pair"};
         std::string spec(e);
         size_t pos = 0;
         while (pos < spec.size()) {
@@ -861,7 +873,7 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
             const std::string kv = spec.substr(pos, end - pos);
             const size_t eq = kv.find('=');
             if (eq != std::string::npos)
-                for (int k = 0; k < 10; ++k)
+                for (int k = 0; k < kTuneKeys; ++k)
                     if (kv.compare(0, eq, keys[k]) == 0) c->tune[k] = std::atoi(kv.c_str() + eq + 1);
             pos = end + 1;
         }
@@ -1085,7 +1097,8 @@ hgb_status hgb_upload_bins(hgb_ctx* c, const void* bins, int bin_bytes, int on_d
         }
     }
     if ((int64_t)n_features * bin_bytes <= kRowMajorMaxRowBytes) {
-        const int64_t stride = ((int64_t)n_features * bin_bytes + 15) / 16 * 16;
+        int64_t stride = ((int64_t)n_features * bin_bytes + 15) / 16 * 16;
+        if (stride % kRowMajorSkewPeriod == 0) stride += kRowMajorSkew;
         // kRowMajorSlack bytes after the last row: a tile's load may run past
         // the end of a row, into the next row or this slack
         HGB_HIP(c, hipMalloc(&c->bins_rm, (size_t)(stride * n_rows + kRowMajorSlack)));

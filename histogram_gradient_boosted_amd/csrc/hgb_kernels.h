@@ -1584,8 +1584,9 @@ __device__ inline void reg_finish(const RegAcc<RA>& a, int cells, int S, unsigne
 }
 
 // RA > 0 (packed only): register accumulator of RA cells per thread; E
-// entries per thread and step.
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, bool IL>
+// entries per thread and step.  IL: 0 feature-major tile; 1 interleaved tile,
+// one lane per row; 2 interleaved tile, two lanes per row (kPairLanes).
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
                                       int64_t n, int n_features, int S, int lc,
@@ -1603,6 +1604,13 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     constexpr int TF = LT / (int)sizeof(BinT);
     constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
     static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
+    // Lane pairs: lanes 2i and 2i + 1 take the two halves of one row's chunk
+    // (HT positions each), so one load instruction reads a row's whole chunk
+    // and the pair's two 16-byte pieces of a line go out as one request.
+    constexpr bool PAIR = IL == 2;
+    static_assert(!PAIR || LT == 2 * kPairHalfBytes, "lane pairs split a 32-byte chunk");
+    constexpr int HT = PAIR ? TF / 2 : TF;       // positions a lane adds per row
+    constexpr int kLanesPerRow = PAIR ? 2 : 1;
     const int plane = S << lc;
     const int cells = nf * S;
     // Interleaved: every one of the TF positions has its words, even past nf
@@ -1614,8 +1622,12 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     lds_zero(lds, tile_w + kFixWords);
     __syncthreads();
     const int lane = threadIdx.x & (kWave - 1);
-    const int rl = lane & (TF - 1);                        // interleaved: the lane's first feature
-    const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;   // and its copy's offset
+    // interleaved: the lane's first position (of its half with lane pairs),
+    // the half's first position, and the lane's copy's offset.  Either way
+    // the 64 lanes of one add meet every (copy, position) word equally often.
+    const int rl = PAIR ? (lane >> 1) & (HT - 1) : lane & (TF - 1);
+    const int hb = PAIR ? (lane & 1) * HT : 0;
+    const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;
     const int gsh = 1 + lc + kLogTF;                       // slot stride: 2G words
     long long tg = 0, th = 0;   // the item's row totals (this thread's share)
     RegAcc<(RA > 0 ? RA : 1)> racc;
@@ -1623,14 +1635,16 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     for (int k = 0; k < (RA > 0 ? RA : 1); ++k) racc.g[k] = racc.h[k] = 0;
 
     const int cpy = threadIdx.x & ((1 << lc) - 1);
-    const uint8_t* const tile = bins_rm + (int64_t)f0 * sizeof(BinT);
+    const uint8_t* const tile = bins_rm + (int64_t)f0 * sizeof(BinT) + (PAIR ? (lane & 1) * kPairHalfBytes : 0);
     const int64_t rb = it.row_begin, re = it.row_end;
-    const int64_t step = (int64_t)blockDim.x * E;
+    const int rows_per_pass = (int)blockDim.x / kLanesPerRow;   // entries one pass of the block takes
+    const int my_entry = (int)threadIdx.x / kLanesPerRow;
+    const int64_t step = (int64_t)rows_per_pass * E;
 
     // Per step: the row chunks and (g, h) pairs of E entries per thread, the
     // entries strided by the block size (index and (g, h) loads coalesced).
     struct Data {
-        Chunk<LT> c[E];
+        Chunk<(PAIR ? LT / 2 : LT)> c[E];
         int2 g[E];
         bool ok[E];
     };
@@ -1642,7 +1656,7 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     auto load_index = [&](int64_t s, Index& x) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const int64_t kk = rb + s * step + (int64_t)e * blockDim.x + threadIdx.x;
+            const int64_t kk = rb + s * step + (int64_t)e * rows_per_pass + my_entry;
             x.in[e] = kk < re;
             x.r[e] = row_index[x.in[e] ? kk : rb];   // past the end: a valid address, masked
         }
@@ -1664,20 +1678,20 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             if (!d.ok[e]) continue;
-            if (SKIP) {
+            if (SKIP && hb == 0) {   // a row's (g, h) counted once, by its first lane
                 tg += d.g[e].x;
                 th += d.g[e].y;
             }
             const CellVal v = cell_val<ACC>(d.g[e].x, d.g[e].y);
             if (IL) {
-                Chunk<LT> ch = d.c[e];
-                ch.rotate(rl * (int)sizeof(BinT));   // position j now holds feature (rl + j) mod TF
+                auto ch = d.c[e];
+                ch.rotate(rl * (int)sizeof(BinT));   // position j now holds the half's feature (rl + j) mod HT
 #pragma unroll
-                for (int j = 0; j < TF; ++j) {
+                for (int j = 0; j < HT; ++j) {
                     const uint32_t w = ch.word((j * (int)sizeof(BinT)) >> 2);
                     const int b = sizeof(BinT) == 1 ? (int)((w >> (8 * (j & 3))) & 0xffu)
                                                     : (int)((w >> (16 * (j & 1))) & 0xffffu);
-                    const int word = (b << gsh) + cb + ((rl + j) & (TF - 1));
+                    const int word = (b << gsh) + cb + hb + ((rl + j) & (HT - 1));
                     if (!SKIP || b != 0) {   // 0: skipped
                         atomicAdd(lds + word, v.a);
                         atomicAdd(lds + word + G, v.b);
@@ -1748,7 +1762,7 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 }
 
 
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, bool IL>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL>
 __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
                                                    int S, int lc, const int2* __restrict__ q,

@@ -22,6 +22,11 @@ enum { kWide = 0, kPacked = 1 };
 constexpr int kPackedMaxBits = 19;
 constexpr int kPackedRowsPerCopy = 4095;
 
+// Row-major level fills with the interleaved tile and 32-byte row chunks may
+// give each row to two lanes, each loading one half of the chunk (il = 2 in
+// the plan; il = 1 is one lane per row).
+constexpr int kPairHalfBytes = 16;
+
 // LDS words after a fill's tile: the item's row totals, then (g, h) per
 // feature of the tile (<= 32): the skipped slot's recovered cells.
 constexpr int kFixWords = 2 + 2 * 32;

@@ -41,15 +41,16 @@ constexpr int kMaxLevelNodes = 65535;
 // What the planner reads of a context: the resident matrix's shape, the
 // precision, whether the skipped slot is on, the chip's CU count and the
 // developer overrides (HGB_FILL_TUNE: root_lc, root_tile, root_ipc,
-// level_lc, level_tile, level_ipc, align, piece, il, root_il; -1 = the
+// level_lc, level_tile, level_ipc, align, piece, il, root_il, pair; -1 = the
 // planner's choice).
+constexpr int kTuneKeys = 11;
 struct PlanCtx {
     int64_t n = 0;
     int F = 0, S = 0, bin_bytes = 1, precision = 30;
     bool skip = false;
     int64_t rm_stride = 0;   // bytes per row of the row-major copy (0: none)
     int n_cu = 256;
-    int tune[10] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+    int tune[kTuneKeys] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 };
 
 // ---------------------------------------------------------------------------
@@ -246,6 +247,15 @@ inline FillPlan plan_rows(const PlanCtx* c)
         p.drain = 0;
         p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
         p.lds_bytes = (size_t)(2 * S + kFixWords) * 8;
+    }
+    // An interleaved tile over 32-byte chunks takes each row on two lanes
+    // (il = 2), one 16-byte half each: a lane alone loads its chunk in two
+    // instructions, and when rows lie far apart (a wide matrix) each of them
+    // is its own request to L2, which is what throttles that fill; a pair's
+    // halves leave one load instruction as one request.
+    if (p.il == 1 && p.lt == 2 * kPairHalfBytes && c->tune[10] != 0) {
+        p.il = 2;
+        p.step_rows = (int64_t)kLevelThreads / 2 * kWideRowEntries;
     }
     return p;
 }

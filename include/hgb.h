@@ -117,8 +117,9 @@ hgb_status hgb_sync(hgb_ctx* ctx);
  *         device, synchronously); HGB_E_UNSUPPORTED when S > HGB_MAX_SLOTS.
  * Device memory: the context keeps the feature-major copy and, when a row
  * takes at most 64 KiB, a row-major copy for the level fills (each row padded
- * to a multiple of 16 bytes): about twice the matrix in all, e.g. 2 GiB + 2 GiB
- * for 131,072 x 16,384 one-byte bins, whose transpose takes about 3.4 ms once.
+ * to a multiple of 16 bytes, plus 128 bytes when that is a multiple of 1 KiB):
+ * about twice the matrix in all, e.g. 2 GiB + 2 GiB + 16 MiB for 131,072 x
+ * 16,384 one-byte bins, whose transpose takes about 3.4 ms once.
  * Invalidates the current tree (begin_tree must be called again).
  */
 hgb_status hgb_upload_bins(hgb_ctx* ctx, const void* bins, int bin_bytes, int on_device,

@@ -65,6 +65,10 @@ static void check_plan(const PlanCtx& c, const FillPlan& p, bool root, bool rm)
         CHECK(p.kind == kFillRowsKind, "rows kind");
         CHECK(p.lt >= c.bin_bytes && p.lt % c.bin_bytes == 0 && p.tile == p.lt / c.bin_bytes, "lt %d", p.lt);
         if (p.acc == kPacked) CHECK(p.ra > 0 && (int64_t)std::min(p.tile, c.F) * c.S <= (int64_t)p.ra * 1024, "ra");
+        CHECK(p.il >= 0 && p.il <= 2, "il %d", p.il);
+        // lane pairs: interleaved wide sums over 32-byte chunks, unless switched off
+        if (p.il == 2) CHECK(p.lt == 2 * kPairHalfBytes && p.acc == kWide && c.tune[10] != 0, "pair plan");
+        if (p.il == 1) CHECK(p.lt != 2 * kPairHalfBytes || c.tune[10] == 0, "a 32-byte interleaved plan without pairs");
     }
 }
 

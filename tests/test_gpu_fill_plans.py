@@ -50,13 +50,18 @@ U8_70 = ("u8, 70 features", lambda: synth.random_small(301, 20_000, 70, 200, Tru
 U16_13 = ("u16, 13 features, 1,025 slots", lambda: synth.random_small(302, 30_000, 13, 1024, True, 10, u16=True))
 HOT_U8 = ("u8 hot slots", lambda: with_hot_slots(synth.random_small(303, 40_000, 6, 16, True, 8), 3))
 HOT_U16 = ("u16 hot slots", lambda: with_hot_slots(synth.random_small(304, 30_000, 5, 1024, True, 6, u16=True), 4))
+# 201 slots: a 16-position u16 tile (32-byte chunks, lane pairs) fits in LDS
+U16_201 = ("u16, 13 features, 201 slots", lambda: synth.random_small(305, 30_000, 13, 200, True, 10, u16=True))
+HOT_U16_201 = ("u16 hot slots, 201 slots",
+               lambda: with_hot_slots(synth.random_small(306, 30_000, 5, 200, True, 6, u16=True), 4))
 
 CASES = [
-    # workload, il, tile, copies
-    (U8_28, 1, 32, 1), (U8_28, 0, 32, 1), (U8_28, 1, 16, 2), (U8_28, 1, 8, 4), (U8_28, 1, 4, 8),
-    (U8_28, 1, 2, 16), (U8_70, 1, 32, 1), (U8_70, 1, 16, 2), (U8_70, 0, 16, 2),
-    (U16_13, 1, 8, 1), (U16_13, 1, 4, 2), (U16_13, 1, 1, 8), (U16_13, 0, 8, 1),
-    (HOT_U8, 1, 32, 1), (HOT_U8, 1, 8, 2), (HOT_U8, 0, 32, 1), (HOT_U16, 1, 8, 1), (HOT_U16, 1, 2, 4),
+    # workload, il (2: interleaved with two lanes per row), tile, copies
+    (U8_28, 2, 32, 1), (U8_28, 1, 32, 1), (U8_28, 0, 32, 1), (U8_28, 1, 16, 2), (U8_28, 1, 8, 4),
+    (U8_28, 1, 4, 8), (U8_28, 1, 2, 16), (U8_70, 2, 32, 1), (U8_70, 1, 32, 1), (U8_70, 1, 16, 2),
+    (U8_70, 0, 16, 2), (U16_201, 2, 16, 2), (U16_201, 2, 16, 1), (U16_201, 1, 16, 2), (U16_13, 1, 8, 1),
+    (U16_13, 1, 4, 2), (U16_13, 1, 1, 8), (U16_13, 0, 8, 1), (HOT_U8, 2, 32, 1), (HOT_U8, 1, 32, 1),
+    (HOT_U8, 1, 8, 2), (HOT_U8, 0, 32, 1), (HOT_U16_201, 2, 16, 2), (HOT_U16, 1, 8, 1), (HOT_U16, 1, 2, 4),
 ]
 
 
@@ -66,20 +71,22 @@ def test_row_fill_layouts(hgb, torch, monkeypatch, capfd, case, il, tile, copies
     name, make = case
     say("row fill layout", name, "il", il, "tile", tile, "copies", copies, "bits", bits)
     lc = copies.bit_length() - 1
-    monkeypatch.setenv("HGB_FILL_TUNE", f"il={il},level_tile={tile},level_lc={lc}")
+    pair = 1 if il == 2 else 0   # a 32-byte interleaved plan takes lane pairs unless pair=0
+    monkeypatch.setenv("HGB_FILL_TUNE", f"il={min(il, 1)},pair={pair},level_tile={tile},level_lc={lc}")
     monkeypatch.setenv("HGB_DEBUG_PLAN", "1")
     w = make()
     run_level_both(hgb, torch, w, check_exact_gain=True, bits=bits)
     plans = level_plans(capfd.readouterr().err)
     assert plans, "no row-major fill ran"
     assert set(plans) == {(copies, tile, il)}, plans
-    if il == 1 and tile == 32:
+    if il == 2 and tile == 32:
         run_root_both(hgb, torch, w, bits=bits)
 
 
 def test_interleaved_tile_full_size_wide_level(hgb, torch, monkeypatch, capfd):
     """131,072 x 16,384 bytes, the level of 8 nodes: the planner's own choice
-    (the interleaved 32-feature tile) against the oracle on sampled features."""
+    (the interleaved 32-feature tile, two lanes per row) against the oracle on
+    sampled features."""
     import oracle
     from test_gpu_parity import oracle_quantized
     say("interleaved full-size wide level")
@@ -96,7 +103,7 @@ def test_interleaved_tile_full_size_wide_level(hgb, torch, monkeypatch, capfd):
                     L.built_slots)
     ctx.sync()
     plans = level_plans(capfd.readouterr().err)
-    assert plans and all(p[2] == 1 for p in plans), plans
+    assert plans and all(p[2] == 2 for p in plans), plans
     qg, qh, _, _ = oracle_quantized(w)
     rng = np.random.default_rng(9)
     feats = np.sort(rng.choice(w.n_features, 96, replace=False))
