@@ -332,7 +332,11 @@ hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
         s.host = s.dev = nullptr;
         const size_t want = std::max<size_t>(std::max<size_t>(bytes, 2 * s.cap), kStageMinBytes);
         s.cap = 0;
-        HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocDefault));
+        // Coherent (fine-grained) pinned memory: the kernels read plans in
+        // place, and the host rewrites a stage for later kernels.  Default
+        // pinned memory is non-coherent, and the GPU's L2 may keep a line of
+        // the stage's previous plan past the kernel boundary.
+        HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocCoherent));
         HGB_HIP(c, hipMalloc(&s.dev, want));
         s.cap = want;
     }

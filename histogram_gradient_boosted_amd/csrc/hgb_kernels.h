@@ -1625,7 +1625,11 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
     // interleaved: the lane's first position (of its half with lane pairs),
     // the half's first position, and the lane's copy's offset.  Either way
     // the 64 lanes of one add meet every (copy, position) word equally often.
-    const int rl = PAIR ? (lane >> 1) & (HT - 1) : lane & (TF - 1);
+    // The LDS serves 16 lanes of a 64-bit add at a time, and positions 16
+    // apart share a bank pair: a pair's second lane starts HT / 2 further on,
+    // so that any 16 consecutive lanes meet 16 positions distinct mod 16 (the
+    // halves' own offsets, 0 and HT, do not separate them when HT = 16).
+    const int rl = PAIR ? ((lane >> 1) + (lane & 1) * (HT / 2)) & (HT - 1) : lane & (TF - 1);
     const int hb = PAIR ? (lane & 1) * HT : 0;
     const int cb = ((lane >> kLogTF) & ((1 << lc) - 1)) * TF;
     const int gsh = 1 + lc + kLogTF;                       // slot stride: 2G words
