@@ -333,9 +333,8 @@ hgb_status stage_upload(hgb_ctx* c, const void* src, size_t bytes, Stage** out)
         const size_t want = std::max<size_t>(std::max<size_t>(bytes, 2 * s.cap), kStageMinBytes);
         s.cap = 0;
         // Coherent (fine-grained) pinned memory: the kernels read plans in
-        // place, and the host rewrites a stage for later kernels.  Default
-        // pinned memory is non-coherent, and the GPU's L2 may keep a line of
-        // the stage's previous plan past the kernel boundary.
+        // place, and the host rewrites a stage for later kernels; in default
+        // (non-coherent) pinned memory the GPU's L2 may cache its lines.
         HGB_HIP(c, hipHostMalloc(&s.host, want, hipHostMallocCoherent));
         HGB_HIP(c, hipMalloc(&s.dev, want));
         s.cap = want;
@@ -901,9 +900,15 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
         }
         c->noalloc_scratch = (unsigned char*)g_scratch_dev[device];
     }
+    // The words kernels post for the host (maxima, error word, sequence
+    // numbers) are in coherent pinned memory, as are the partition's node
+    // records: a kernel's stores there reach the host in the order its fences
+    // give them.  In default (non-coherent) pinned memory they pass through
+    // the GPU's write-back L2, and a sequence number could reach the host
+    // before the results it vouches for.
     if (hipMalloc((void**)&c->dev_words, 64) != hipSuccess ||
         hipMalloc((void**)&c->max_part, sizeof(uint32_t) * 2 * kMaxBlocks) != hipSuccess ||
-        hipHostMalloc((void**)&c->host_words, 64, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&c->host_words, 64, hipHostMallocCoherent) != hipSuccess ||
         hipMemset(c->dev_words, 0, 64) != hipSuccess) {
         hgb_destroy(c);
         return HGB_E_DEVICE;
@@ -1678,7 +1683,7 @@ static hgb_status partition_impl(hgb_ctx* c, const int32_t* row_index, const int
         c->part_host = nullptr;
         c->part_host_cap = 0;
         HGB_HIP(c, hipHostMalloc((void**)&c->part_host, sizeof(int32_t) * 3 * (size_t)n_nodes,
-                                 hipHostMallocDefault));
+                                 hipHostMallocCoherent));   // (see host_words)
         c->part_host_cap = 3 * (int64_t)n_nodes;
     }
     st = grow(c, &c->part_flags, &c->part_flags_cap, std::max<int64_t>(offs[n_nodes], 1));

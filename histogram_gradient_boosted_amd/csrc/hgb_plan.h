@@ -143,6 +143,12 @@ inline double fill_cost_il_packed(int lc, int tf, int F, int w, int S, int drain
     return lds + w / 6.0e12 + (8.0 / tf) / 30.0e12 + valu;
 }
 
+// Lane pairs (il = 2): an interleaved tile over 32-byte chunks takes each row
+// on two lanes, one 16-byte half each.  A lane alone loads its chunk in two
+// instructions, and when rows lie far apart (a wide matrix) each of them is a
+// request of its own to L2, which is what throttled that fill; a pair's halves
+// leave one load instruction as one request.
+//
 // Row-major level fills read scattered rows.  Cost per row (seconds) of a plan
 // with n_tiles feature tiles: the LDS adds at the same rates as above (plus
 // the packed drains: lane-contiguous LDS reads and writes); each row's lines
@@ -165,9 +171,10 @@ inline double rows_cost(int acc, int lc, int F, int n_tiles, int64_t row_bytes, 
                        drain_ops_per_row / (16.0 * clk);
     // Vector ALU work per add, 64 lanes per clock per CU: about 3 instructions
     // (unpack, address), 6 with the interleaved tile's rotation and per-lane
-    // feature offset.  It decides narrow matrices, where the gather dominates
-    // and the interleaved tile's faster adds buy nothing (a 28-feature matrix).
-    const double valu = adds * (il ? 6.0 : 3.0) / (64.0 * clk);
+    // feature offset, 5 when a lane pair shares the row (each lane rotates
+    // half the chunk).  It decides narrow matrices, where the gather dominates
+    // and the interleaved tile's faster adds buy little (a 28-feature matrix).
+    const double valu = adds * (il == 2 ? 5.0 : il ? 6.0 : 3.0) / (64.0 * clk);
     const double lines = (double)std::max<int64_t>((row_bytes + 127) / 128, 1) * 128.0;
     const double mem = lines / 5.0e12 + n_tiles * (64.0 + 12.0) / 10.0e12;
     return std::max(lds, mem) + 0.25 * std::min(lds, mem) + valu;
@@ -219,7 +226,10 @@ inline FillPlan plan_rows(const PlanCtx* c)
                         if (drain == 0) continue;
                         drain_ops = 2.0 * nf * S * (1 << lc) / ((double)kLevelThreads * e * drain) * n_tiles;
                     }
-                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops, il, tile);
+                    // an interleaved tile over 32-byte chunks takes each row on
+                    // two lanes (il = 2) unless switched off
+                    const int il_mode = il && lt == 2 * kPairHalfBytes && c->tune[10] != 0 ? 2 : il;
+                    const double cost = rows_cost(acc, lc, F, n_tiles, c->rm_stride, drain_ops, il_mode, tile);
                     if (cost < best) {
                         best = cost;
                         found = true;
@@ -228,9 +238,9 @@ inline FillPlan plan_rows(const PlanCtx* c)
                         p.tile = tile;
                         p.lt = lt;
                         p.ra = ra;
-                        p.il = il;
+                        p.il = il_mode;
                         p.drain = drain;
-                        p.step_rows = (int64_t)kLevelThreads * e;
+                        p.step_rows = (int64_t)kLevelThreads / (il_mode == 2 ? 2 : 1) * e;
                         p.lds_bytes = (size_t)(words + kFixWords) * 8;
                     }
                 }
@@ -247,15 +257,6 @@ inline FillPlan plan_rows(const PlanCtx* c)
         p.drain = 0;
         p.step_rows = (int64_t)kLevelThreads * kWideRowEntries;
         p.lds_bytes = (size_t)(2 * S + kFixWords) * 8;
-    }
-    // An interleaved tile over 32-byte chunks takes each row on two lanes
-    // (il = 2), one 16-byte half each: a lane alone loads its chunk in two
-    // instructions, and when rows lie far apart (a wide matrix) each of them
-    // is its own request to L2, which is what throttles that fill; a pair's
-    // halves leave one load instruction as one request.
-    if (p.il == 1 && p.lt == 2 * kPairHalfBytes && c->tune[10] != 0) {
-        p.il = 2;
-        p.step_rows = (int64_t)kLevelThreads / 2 * kWideRowEntries;
     }
     return p;
 }
