@@ -187,7 +187,9 @@ def test_small_random(hgb, torch, seed, n, F, B, missing, children, u16, wide, b
 @pytest.mark.parametrize("name,n,F", [("c2", 300_000, 100), ("c5", 300_000, 50),
                                       ("c4", 8_192, 1_024), ("c1", None, None)])
 def test_packed_precision_configs(hgb, torch, name, n, F):
-    """Precision 19 selects packed (g, h) accumulation in the fill."""
+    """Precision 19 selects packed (g, h) accumulation in the root fill, and
+    in the level fills where no wide plan with lane pairs fits (the 2-byte,
+    1,025-slot matrix)."""
     say("packed", name, n, F)
     w = synth.make(name, n_rows=n, n_features=F)
     if w.level is not None:

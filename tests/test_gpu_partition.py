@@ -249,13 +249,15 @@ def test_grow_level_without_splits(hgb, torch):
     ctx.close()
 
 
-def test_many_trees_on_one_context(hgb, torch):
+@pytest.mark.parametrize("fused", [True, False], ids=["one call per level", "three calls per level"])
+def test_many_trees_on_one_context(hgb, torch, fused):
     """Twelve grown trees of eight levels on one context, queued without a
     wait between trees: the launch plans' staging slots are reused many
     times behind the library's stream markers, and the maxima and node
-    records are read back through the sequence words.  Every tree equals the
+    records are read back through the sequence words (each level's records
+    must be that level's, not the previous one's).  Every tree equals the
     first, level by level, and the first equals the oracle's."""
-    say("many trees, one context")
+    say("many trees, one context", "fused" if fused else "apart")
     from histogram_gradient_boosted_amd import tree
     w = synth.make("c3", n_rows=200_000)
     ctx = hgb.Context(0)
@@ -263,7 +265,7 @@ def test_many_trees_on_one_context(hgb, torch):
     ctx.upload_bins(w.bins, w.n_bins, w.has_missing)
     g = torch.from_numpy(w.grad).cuda()
     h = torch.from_numpy(w.hess).cuda()
-    trees = [tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, sync=False) for _ in range(12)]
+    trees = [tree.grow_tree_device(ctx, g, h, w.depth, w.lam, w.gamma, sync=False, fused=fused) for _ in range(12)]
     ctx.sync()
     want = oracle_tree(w, w.depth, 30)
     first = trees[0]
