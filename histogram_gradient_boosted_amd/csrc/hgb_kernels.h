@@ -1585,7 +1585,8 @@ __device__ inline void reg_finish(const RegAcc<RA>& a, int cells, int S, unsigne
 
 // RA > 0 (packed only): register accumulator of RA cells per thread; E
 // entries per thread and step.  IL: 0 feature-major tile; 1 interleaved tile,
-// one lane per row; 2 interleaved tile, two lanes per row (kPairLanes).
+// one lane per row; 2 interleaved tile over 32-byte chunks, two lanes per row
+// (one kPairHalfBytes half each).
 template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
