@@ -46,6 +46,17 @@ LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_ATOMIC", "SQ_LDS_IDX_ACTIVE", "SQ_
 # slots): all requests, the 32-byte ones, and the 128-byte ones (BUBBLE);
 # the rest are 64-byte.  FETCH_SIZE is derived from these three.
 REQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum")
+# --stalls: what holds the fills up, one --pmc pass per set: the vector L1's
+# requests to L2, their summed latency and its stalls (in-flight limit, data
+# pending from L2); the address unit stalled by the L1 and the data unit by
+# it; the SQ's wave cycles, waits and instruction counts
+STALL_SETS = (
+    ("TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_UTCL1_STALL_INFLIGHT_MAX_sum",
+     "TCP_PENDING_STALL_CYCLES_sum"),
+    ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TD_TC_STALL_sum"),
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+     "SQ_INSTS_VMEM_RD", "SQ_LDS_BANK_CONFLICT"),
+)
 SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boosted_amd/csrc/*.h",
            "include/*.h")
 
@@ -135,6 +146,63 @@ def read_counter(db: str, counter: str) -> dict:
     return dict(out)
 
 
+def stalls(args, me: str) -> None:
+    """--stalls: STALL_SETS per step for the fill class and the level tail
+    (3-step run - 1-step run, halved), written to
+    profiles/stalls_<config>_p<bits><tag>.{json,md}.  HGB_FILL_TUNE, if set,
+    is passed to the step driver and recorded with the command."""
+    t0 = time.time()
+    per_step = collections.defaultdict(dict)
+    for i, names in enumerate(STALL_SETS):
+        got = {}
+        for steps in (1, 3):
+            db = run_counter(names, os.path.join(args.out, f"{args.config}_p{args.precision}_stall{i}_{steps}"),
+                             [me, "--drive", "--config", args.config, "--precision", str(args.precision),
+                              "--steps", str(steps)],
+                             os.path.join(args.out, f"{args.config}_p{args.precision}_stall{i}_{steps}.log"))
+            got[steps] = {c: read_counter(db, c) for c in names}
+        for c in names:
+            for k in FILL_CLASS + OTHER:
+                a = got[3][c].get(k, [0.0, 0])
+                b = got[1][c].get(k, [0.0, 0])
+                if a[1] > b[1]:
+                    per_step[k][c] = (a[0] - b[0]) / 2.0
+    tune = os.environ.get("HGB_FILL_TUNE", "")
+    cmd = (f"HGB_FILL_TUNE={tune} " if tune else "") + \
+        f"python bench_counters.py --stalls --config {args.config} --precision {args.precision}" + \
+        (f" --tag {args.tag}" if args.tag else "")
+    record = {"config": args.config, "precision": args.precision, "fill_tune": tune, "source_hash": source_hash(),
+              "command": cmd, "per_step": per_step, "seconds": round(time.time() - t0, 1)}
+    base = os.path.join(ROOT, "profiles", f"stalls_{args.config}_p{args.precision}{args.tag}")
+    with open(base + ".json", "w") as f:
+        json.dump(record, f, indent=1)
+    lines = [f"# Stall counters per step, {args.config}, P = {args.precision}" +
+             (f", HGB_FILL_TUNE={tune}" if tune else ""), "",
+             f"Command: `{cmd}` (rocprofv3 --pmc, one pass per counter set; per step = (3-step run - 1-step run) / 2;",
+             "summed over the chip's instances).  L2 latency is TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ; the",
+             "SQ wait counters are wave-cycles (in units of 4 cycles), shown as shares of SQ_WAVE_CYCLES.", "",
+             "| kernel | L1->L2 read requests | mean L2 latency (cycles) | L1 in-flight-limit stall | L1 pending-data stall "
+             "| address unit stalled by L1 | data unit stalled by L1 | wait on an instruction | of it on LDS "
+             "| VALU / LDS instructions | LDS bank-conflict cycles |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in FILL_CLASS + OTHER:
+        r = per_step.get(k)
+        if not r or r.get("TCP_TCC_READ_REQ_sum", 0) <= 0:
+            continue
+        wave = max(r.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        lines.append(
+            f"| {k} | {r['TCP_TCC_READ_REQ_sum']:,.0f} | "
+            f"{r.get('TCP_TCC_READ_REQ_LATENCY_sum', 0) / r['TCP_TCC_READ_REQ_sum']:.0f} | "
+            f"{r.get('TCP_UTCL1_STALL_INFLIGHT_MAX_sum', 0):,.0f} | {r.get('TCP_PENDING_STALL_CYCLES_sum', 0):,.0f} | "
+            f"{r.get('TA_ADDR_STALLED_BY_TC_CYCLES_sum', 0):,.0f} | {r.get('TD_TC_STALL_sum', 0):,.0f} | "
+            f"{r.get('SQ_WAIT_INST_ANY', 0) / wave:.2f} | {r.get('SQ_WAIT_INST_LDS', 0) / wave:.2f} | "
+            f"{r.get('SQ_INSTS_VALU', 0) / max(r.get('SQ_INSTS_LDS', 0), 1):.2f} | "
+            f"{r.get('SQ_LDS_BANK_CONFLICT', 0):,.0f} |")
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def trace_summary(db: str, step_equiv: int, command: str) -> str:
     """Per-kernel durations from a rocprofv3 --kernel-trace database.  With
     step_equiv 0 the trees are counted from the trace: every tree starts with
@@ -184,6 +252,9 @@ def main() -> None:
                     help="trees the traced process ran (0: count them from the trace)")
     ap.add_argument("--trace-command", default="")
     ap.add_argument("--trace-out")
+    ap.add_argument("--stalls", action="store_true",
+                    help="collect the stall counters (profiles/stalls_*) instead of the traffic counters")
+    ap.add_argument("--tag", default="", help="--stalls: suffix of the output files")
     args = ap.parse_args()
     if args.trace_summary:
         text = trace_summary(args.trace_summary, args.step_equiv, args.trace_command)
@@ -203,6 +274,9 @@ def main() -> None:
     REUSE = args.reuse
     me = os.path.abspath(__file__)
     os.makedirs(args.out, exist_ok=True)
+    if args.stalls:
+        stalls(args, me)
+        return
     t0 = time.time()
     raw = {}
     cal = {}
