@@ -556,7 +556,8 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
     } else {
         // row-major: packed sums in registers (ra cells per thread), wide sums in LDS
         const uint8_t* rm = (const uint8_t*)c->bins_rm;
-#define HGB_ROWS(LT, RA, E, IL) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP, IL>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot, a.zero)
+#define HGB_ROWS(LT, RA, E, IL) HGB_ROWS_LC(LT, RA, E, IL, false)
+#define HGB_ROWS_LC(LT, RA, E, IL, LC0) HGB_LAUNCH((k_fill_rows<BinT, LT, ACC, RA, E, SKIP, IL, LC0>), rm, c->rm_stride, c->n, c->F, c->S, p.lc, c->q, a.row_index, a.items, a.block_first, a.n_blocks, a.drain, hist, partial, c->dev_words + 2, c->rot, a.zero)
         if constexpr (ACC == kPacked) {
             if (p.ra != kRegAccCells) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             switch (p.lt) {
@@ -570,7 +571,8 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
             if (p.ra != 0) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
             if (p.il == 2) {   // lane pairs: 32-byte chunks only
                 if (p.lt != 2 * kPairHalfBytes) return fail(c, HGB_E_DEVICE, "fill: internal error in the plan");
-                HGB_ROWS(32, 0, kWideRowEntries, 2);
+                if (p.lc == 0) HGB_ROWS_LC(32, 0, kWideRowEntries, 2, true);
+                else HGB_ROWS(32, 0, kWideRowEntries, 2);
             } else if (p.il) {
                 switch (p.lt) {
                 case 32: HGB_ROWS(32, 0, kWideRowEntries, 1); break;
@@ -590,6 +592,7 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
             }
         }
 #undef HGB_ROWS
+#undef HGB_ROWS_LC
     }
 #undef HGB_LAUNCH
     HGB_LAUNCHED(c, "fill");

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "hgb_layout.h"
 
 namespace hgb {
@@ -902,12 +904,15 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
     };
     // `live` is false for a thread whose group lies past the item: it then
     // adds zeros (to valid bins), which keeps the loop free of divergence.
-    auto accumulate = [&](const RootStep<BinT, NF>& st, bool live) {
+    // Only an item's last step can hold such threads; the others take
+    // ALL_LIVE and skip the selects.
+    auto accumulate = [&](const RootStep<BinT, NF>& st, bool live, auto all_live) {
+        constexpr bool ALL_LIVE = decltype(all_live)::value;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int4 qq = st.q[j >> 1];
-            const int gv = live ? ((j & 1) ? qq.z : qq.x) : 0;
-            const int hv = live ? ((j & 1) ? qq.w : qq.y) : 0;
+            const int gv = (ALL_LIVE || live) ? ((j & 1) ? qq.z : qq.x) : 0;
+            const int hv = (ALL_LIVE || live) ? ((j & 1) ? qq.w : qq.y) : 0;
             if (SKIP) {
                 tg += gv;
                 th += hv;
@@ -953,17 +958,26 @@ __global__ __launch_bounds__(1024) void k_fill_root(const BinT* __restrict__ bin
         const int64_t last = full > 0 ? gend - R : rb;
         int dcount = 0;
         RootStep<BinT, NF> A, B;
-        if (n_steps > 0) load(rb + off + R <= gend ? rb + off : last, A);
+        // Steps before the item's last have every thread's group inside the
+        // item (n_steps = ceil(full / threads)): their loads need no clamp
+        // and their adds no select.  The step loop is uniform across the
+        // block, so these branches do not diverge.
+        using Live = std::true_type;
+        using Maybe = std::false_type;
+        auto at_of = [&](int64_t at, int64_t s) { return s < n_steps - 1 || at + R <= gend ? at : last; };
+        if (n_steps > 0) load(at_of(rb + off, 0), A);
         for (int64_t s = 0; s < n_steps; s += 2) {
             const int64_t a_at = rb + s * step + off;
             const int64_t b_at = a_at + step;
-            load(b_at + R <= gend ? b_at : last, B);
-            accumulate(A, a_at + R <= gend);
+            load(at_of(b_at, s + 1), B);
+            if (s + 1 < n_steps) accumulate(A, true, Live{});
+            else accumulate(A, a_at + R <= gend, Maybe{});
             if (ACC == kPacked && ++dcount == drain) { drain_now(); dcount = 0; }
             if (s + 1 >= n_steps) break;
             const int64_t c_at = b_at + step;
-            load(c_at + R <= gend ? c_at : last, A);
-            accumulate(B, b_at + R <= gend);
+            load(at_of(c_at, s + 2), A);
+            if (s + 2 < n_steps) accumulate(B, true, Live{});
+            else accumulate(B, b_at + R <= gend, Maybe{});
             if (ACC == kPacked && ++dcount == drain) { drain_now(); dcount = 0; }
         }
         if (threadIdx.x == 0)
@@ -1586,17 +1600,20 @@ __device__ inline void reg_finish(const RegAcc<RA>& a, int cells, int S, unsigne
 // RA > 0 (packed only): register accumulator of RA cells per thread; E
 // entries per thread and step.  IL: 0 feature-major tile; 1 interleaved tile,
 // one lane per row; 2 interleaved tile over 32-byte chunks, two lanes per row
-// (one kPairHalfBytes half each).
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL>
+// (one kPairHalfBytes half each).  LC0: the plan has one copy (lc_arg = 0),
+// so the interleaved tile's H plane is a constant offset from its G plane,
+// which the LDS instruction carries instead of a vector add per cell.
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL, bool LC0>
 __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& it,
                                       const uint8_t* __restrict__ bins_rm, int64_t row_stride,
-                                      int64_t n, int n_features, int S, int lc,
+                                      int64_t n, int n_features, int S, int lc_arg,
                                       const int2* __restrict__ q,
                                       const int32_t* __restrict__ row_index, int drain,
                                       unsigned long long* __restrict__ hist,
                                       unsigned long long* __restrict__ partial, int& bad,
                                       const int32_t* __restrict__ rot)
 {
+    const int lc = LC0 ? 0 : lc_arg;
     static_assert((RA > 0) == (ACC == kPacked), "packed sums live in registers, wide sums in LDS");
     static_assert(LT / (int)sizeof(BinT) <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
     static_assert(!IL || (ACC == kWide && RA == 0), "the interleaved layout holds wide sums in LDS");
@@ -1767,7 +1784,7 @@ __device__ inline void fill_rows_item(unsigned long long* lds, const FillItem& i
 }
 
 
-template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL>
+template <typename BinT, int LT, int ACC, int RA, int E, bool SKIP, int IL, bool LC0>
 __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ bins_rm,
                                                    int64_t row_stride, int64_t n, int n_features,
                                                    int S, int lc, const int2* __restrict__ q,
@@ -1786,7 +1803,7 @@ __global__ __launch_bounds__(1024) void k_fill_rows(const uint8_t* __restrict__ 
     const int i1 = block_first[blk + 1];
     int bad = 0;   // a row index outside [0, n): skipped, and flagged
     for (int ii = block_first[blk]; ii < i1; ++ii) {
-        fill_rows_item<BinT, LT, ACC, RA, E, SKIP, IL>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
+        fill_rows_item<BinT, LT, ACC, RA, E, SKIP, IL, LC0>(lds, items[ii], bins_rm, row_stride, n, n_features, S,
                                              lc, q, row_index, drain, hist, partial, bad, rot);
         __syncthreads();
     }
