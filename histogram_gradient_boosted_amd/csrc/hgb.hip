@@ -500,7 +500,8 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
         kern<<<grid, p.threads, p.lds_bytes, c->stream>>>(__VA_ARGS__);                  \
     } while (0)
     if (p.kind == kFillRoot && p.il) {
-#define HGB_ROOT_IL(TF) HGB_LAUNCH((k_fill_root_il<BinT, TF, SKIP, ACC>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, partial, c->rot)
+#define HGB_ROOT_IL_LC(TF, LC0) HGB_LAUNCH((k_fill_root_il<BinT, TF, SKIP, ACC, LC0>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, partial, c->rot)
+#define HGB_ROOT_IL(TF) do { if (p.lc == 0) HGB_ROOT_IL_LC(TF, true); else HGB_ROOT_IL_LC(TF, false); } while (0)
         if constexpr (ACC == kPacked) {
             // (the plan keeps 16 positions, one-byte bins and no skipped slot)
             if constexpr (!SKIP && sizeof(BinT) == 1) {
@@ -533,6 +534,7 @@ hgb_status launch_fill_acc(hgb_ctx* c, const FillPlan& p, const FillArgs& a)
             }
         }
 #undef HGB_ROOT_IL
+#undef HGB_ROOT_IL_LC
     } else if (p.kind == kFillRoot) {
 #define HGB_ROOT(NF) HGB_LAUNCH((k_fill_root<BinT, NF, ACC, SKIP>), bins, c->n, c->F, c->S, p.lc, a.gh, a.items, a.n_items, a.vec_ok, a.drain, hist, c->rot)
         switch (p.tile) {

@@ -1036,9 +1036,11 @@ __device__ inline void rotate_root_bins(RootBins<BinT> (&b)[TF], int k)
 }
 
 
-template <typename BinT, int TF, bool SKIP, int ACC>
+// LC0: one copy (lc_arg = 0), so that the H plane's offset from the G plane
+// is a constant the LDS instruction carries (no vector add per cell).
+template <typename BinT, int TF, bool SKIP, int ACC, bool LC0>
 __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ bins, int64_t n,
-                                                       int n_features, int S, int lc,
+                                                       int n_features, int S, int lc_arg,
                                                        const int2* __restrict__ q,
                                                        const FillItem* __restrict__ items, int n_items,
                                                        int vec_ok, int drain,
@@ -1049,6 +1051,7 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     static_assert(TF <= (kFixWords - 2) / 2, "a recovered cell per feature of the tile");
     constexpr int kLogTF = TF >= 32 ? 5 : TF >= 16 ? 4 : TF >= 8 ? 3 : TF >= 4 ? 2 : TF >= 2 ? 1 : 0;
     static_assert((1 << kLogTF) == TF, "feature positions per tile: a power of two");
+    const int lc = LC0 ? 0 : lc_arg;
     constexpr bool kPack = ACC == kPacked;
     static_assert(!kPack || TF == 16, "packed sums: 16 positions, whose 256 slots the register cells cover");
     constexpr int RA = kPack ? kRootIlPackedCells : 1;
@@ -1115,17 +1118,20 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
     // A step's work, taken out of its loads: the rows' cell values and the
     // rotated bins (b[p] holds feature (rl + p) mod TF).  `live` is false for
     // a thread whose group lies past the item: it then adds zeros (to valid
-    // bins), which keeps the loop free of divergence.
+    // bins), which keeps the loop free of divergence.  Only an item's last
+    // step can hold such threads; the others take ALL_LIVE and skip the
+    // selects.
     struct Work {
         CellVal v[R];
         RootBins<BinT> b[TF];
     };
-    auto prepare = [&](const RootStepIL<BinT, TF>& st, bool live, Work& wk) {
+    auto prepare = [&](const RootStepIL<BinT, TF>& st, bool live, Work& wk, auto all_live) {
+        constexpr bool ALL_LIVE = decltype(all_live)::value;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int4 qq = st.q[j >> 1];
-            const int gv = live ? ((j & 1) ? qq.z : qq.x) : 0;
-            const int hv = live ? ((j & 1) ? qq.w : qq.y) : 0;
+            const int gv = (ALL_LIVE || live) ? ((j & 1) ? qq.z : qq.x) : 0;
+            const int hv = (ALL_LIVE || live) ? ((j & 1) ? qq.w : qq.y) : 0;
             if (SKIP) {
                 tg += gv;
                 th += hv;
@@ -1188,13 +1194,18 @@ __global__ __launch_bounds__(1024) void k_fill_root_il(const BinT* __restrict__ 
         const int64_t last = full > 0 ? gend - R : rb;
         RootStepIL<BinT, TF> st;
         Work wk;
-        if (n_steps > 0) load(rb + off + R <= gend ? rb + off : last, st);
+        // Steps before the item's last have every thread's group inside the
+        // item (n_steps = ceil(full / threads)): no clamp, no select.  The
+        // step loop is uniform across the block.
+        auto at_of = [&](int64_t a, int64_t s) { return s < n_steps - 1 || a + R <= gend ? a : last; };
+        if (n_steps > 0) load(at_of(rb + off, 0), st);
         for (int64_t s = 0; s < n_steps; ++s) {
             const int64_t at = rb + s * step + off;
             const int64_t nx = at + step;
-            prepare(st, at + R <= gend, wk);
+            if (s + 1 < n_steps) prepare(st, true, wk, std::true_type{});
+            else prepare(st, at + R <= gend, wk, std::false_type{});
             __builtin_amdgcn_sched_barrier(0);   // keep the issue order
-            load(nx + R <= gend ? nx : last, st);
+            load(at_of(nx, s + 1), st);
             __builtin_amdgcn_sched_barrier(0);
             accumulate(wk);
             if (kPack && ++dcount == drain) {
