@@ -358,6 +358,12 @@ def dominant_roofline(prof, plan, steps: int, counters):
             "launches_per_step": launches // steps, "avg_launch_us": round(avg_s * 1e6, 3)}
 
 
+# untimed steps of the set-up before the warm-up: at least this many, for at
+# least this long
+SETTLE_STEPS = 10
+SETTLE_S = 0.05
+
+
 def spin_until_done(torch):
     """Poll an event recorded after the queued work until the device has done
     it, so that the blocking synchronize after it returns at once (its
@@ -419,6 +425,19 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
     # host for tens of milliseconds.  Freeze them out of the collector.
     gc.collect()
     gc.freeze()
+    # Settle, as part of the set-up: untimed steps for at least SETTLE_S and
+    # SETTLE_STEPS.  A few steps of a sub-millisecond tree do not reach the
+    # steady state of a fit (131,072 x 16,384 after 3 steps: its first timed
+    # pass ran 1.52 ms a step against 1.46 ms for every later one; after 30,
+    # 1.46 ms from the first).  Then the W warm-up steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while settle_steps < SETTLE_STEPS or time.perf_counter() - t_settle < SETTLE_S:
+        step(ctx, w, plan, g, h)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            ctx.sync()   # keeps the host within a few trees of the device
+    ctx.sync()
     for _ in range(warmup):
         step(ctx, w, plan, g, h)
     ctx.sync()
@@ -490,6 +509,7 @@ def measure(config: str, precision: int, steps: int, warmup: int, seed: int, obj
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         # per-step spans from events between consecutive steps (a second pass)
         "ms_per_step_stats": {"median": round(float(np.median(per_step)), 4),
@@ -642,7 +662,7 @@ def main():
     if (not args.no_targets and args.config == "c3" and not args.grow and not args.oblivious):
         wide = measure("c4", args.precision, args.steps, 3, args.seed, "auto", False, False,
                        args.flush_mib, not args.no_cpu_baseline, cpu_min_s=0.0)
-        keep = ("value", "unit", "ms_per_step", "ms_per_step_stats", "steps", "warmup", "config",
+        keep = ("value", "unit", "ms_per_step", "ms_per_step_stats", "steps", "warmup", "settle_steps", "config",
                 "kernel_ms_per_step", "roofline", "fill_class_roofline", "lds_roofline", "cpu_baseline",
                 "precision_bits", "effective_gcells_per_s", "gather_roofline")
         result["targets"] = {"c4": {k: wide[k] for k in keep if k in wide}}

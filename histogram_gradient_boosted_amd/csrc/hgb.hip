@@ -920,6 +920,18 @@ hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out)
         return HGB_E_DEVICE;
     }
     std::memset(c->host_words, 0, 64);   // no sequence number posted yet
+    // The launch-plan stages at their initial size, now: a pinned allocation
+    // takes a few hundred microseconds, and made on first use it stalled the
+    // first trees of a fit (131,072 x 16,384 uses four stages a tree, so its
+    // fifth tree still allocated some).
+    for (Stage& st : c->stage) {
+        if (hipHostMalloc(&st.host, kStageMinBytes, hipHostMallocCoherent) != hipSuccess ||
+            hipMalloc(&st.dev, kStageMinBytes) != hipSuccess) {
+            hgb_destroy(c);
+            return HGB_E_DEVICE;
+        }
+        st.cap = kStageMinBytes;
+    }
     *out = c;
     return HGB_OK;
 }
