@@ -77,6 +77,10 @@ int hgb_available(void);
  * ([bonsai-10] "The device context lifecycle": one device context owns the
  * resident state of a fit, split by lifetime into the dataset, the per-tree
  * gradients and the per-level buffers).  The caller owns the stream.
+ * Memory: a context allocates at creation 4 MiB of pinned host memory and 4
+ * MiB of device memory for its launch plans (16 stages of 256 KiB, grown when a
+ * plan needs more), and a few small coherent pinned buffers through which
+ * kernels post results to the host.
  * Errors: HGB_E_INVALID for a null `out` or a device index out of range;
  *         HGB_E_DEVICE when no device is usable or an allocation fails. */
 hgb_status hgb_create(int device, void* hip_stream, hgb_ctx** out);
