@@ -26,6 +26,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import shutil
 import sqlite3
 import subprocess
@@ -61,14 +62,23 @@ SOURCES = ("histogram_gradient_boosted_amd/csrc/*.hip", "histogram_gradient_boos
            "include/*.h")
 
 
+def _code_only(text: str) -> str:
+    """The text without its comments and with whitespace collapsed, so that a
+    change to comments alone keeps the hash (the counters measure the code).
+    The sources hold no comment markers inside string literals."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """sha256 over the HIP sources and the public header."""
+    """sha256 over the code of the HIP sources and the public header."""
     h = hashlib.sha256()
     for pat in SOURCES:
         for path in sorted(glob.glob(os.path.join(ROOT, pat))):
             h.update(os.path.relpath(path, ROOT).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
