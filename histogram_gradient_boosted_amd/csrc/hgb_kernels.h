@@ -2338,6 +2338,69 @@ struct SplitOut {
     long long g_left, h_left, g_total, h_total;
 };
 
+// A node's record: no candidate (f < 0) reads feature and bin -1, gain -inf.
+__device__ inline void split_out_write(SplitOut* out, int node, int f, int code, double gain, long long gl,
+                                       long long hl, long long tg, long long th)
+{
+    SplitOut o;
+    o.pad = 0;
+    o.g_total = tg;
+    o.h_total = th;
+    if (f < 0) {
+        o.feature = -1; o.bin = -1; o.default_left = 0;
+        o.gain = -__builtin_inf();
+        o.g_left = 0; o.h_left = 0;
+    } else {
+        o.feature = f;
+        o.bin = code >> 1;
+        o.default_left = code & 1;
+        o.gain = gain;
+        o.g_left = gl;
+        o.h_left = hl;
+    }
+    out[node] = o;
+}
+
+// k_split_reduce for at most kWave entries: lane e holds entry e, and the
+// lanes exchange (gain, feature) with the winner's record through xor
+// shuffles, 32 apart first.  Lane 0 then has combined the same pairs, in the
+// same order and orientation, as the block-wide tree below does with one
+// wave, so it picks the same entry; the record needs no second load.
+__device__ inline void split_reduce_wave(const FeatureBest* __restrict__ nb, const long long* __restrict__ totals,
+                                         int n_entries, int node, SplitOut* __restrict__ out)
+{
+    const int lane = (int)threadIdx.x;
+    const long long tg = totals[2 * node], th = totals[2 * node + 1];
+    double bg = 0.0;
+    int bf = -1, code = -1;
+    long long gl = 0, hl = 0;
+    if (lane < n_entries) {
+        const FeatureBest c = nb[lane];
+        if (c.code >= 0) {
+            bg = c.gain;
+            bf = c.feature;
+            code = c.code;
+            gl = c.g_left;
+            hl = c.h_left;
+        }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const double og = __shfl_xor(bg, off, kWave);
+        const int of = __shfl_xor(bf, off, kWave);
+        const int oc = __shfl_xor(code, off, kWave);
+        const long long ogl = __shfl_xor(gl, off, kWave);
+        const long long ohl = __shfl_xor(hl, off, kWave);
+        if (better(og, of, bg, bf)) {
+            bg = og;
+            bf = of;
+            code = oc;
+            gl = ogl;
+            hl = ohl;
+        }
+    }
+    if (lane == 0) split_out_write(out, node, bf, code, bg, gl, hl, tg, th);
+}
+
 // One block per node (64, 256 or 1,024 threads, a power of two): the best feature,
 // scanning features in order per thread -- four entries loaded before any is
 // compared -- and then reducing across threads with the same (gain, feature)
@@ -2351,6 +2414,10 @@ __global__ __launch_bounds__(kSplitReduceMaxThreads) void k_split_reduce(
     __shared__ int s_entry[kSplitReduceMaxThreads];
     const int node = blockIdx.x;
     const FeatureBest* nb = best + (int64_t)node * n_entries;
+    if (blockDim.x == kWave && n_entries <= kWave) {   // one wave, at most one entry per lane
+        split_reduce_wave(nb, totals, n_entries, node, out);
+        return;
+    }
     double bg = 0.0;
     int bf = -1, be = -1;
     auto take = [&](const FeatureBest& c, int e) {
@@ -2384,25 +2451,14 @@ __global__ __launch_bounds__(kSplitReduceMaxThreads) void k_split_reduce(
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        SplitOut o;
         const int f = s_feat[0];
-        o.pad = 0;
-        o.g_total = totals[2 * node];
-        o.h_total = totals[2 * node + 1];
         if (f < 0) {
-            o.feature = -1; o.bin = -1; o.default_left = 0;
-            o.gain = -__builtin_inf();
-            o.g_left = 0; o.h_left = 0;
+            split_out_write(out, node, -1, -1, 0.0, 0, 0, totals[2 * node], totals[2 * node + 1]);
         } else {
             const FeatureBest c = nb[s_entry[0]];
-            o.feature = f;
-            o.bin = c.code >> 1;
-            o.default_left = c.code & 1;
-            o.gain = c.gain;
-            o.g_left = c.g_left;
-            o.h_left = c.h_left;
+            split_out_write(out, node, f, c.code, c.gain, c.g_left, c.h_left, totals[2 * node],
+                            totals[2 * node + 1]);
         }
-        out[node] = o;
     }
 }
 
