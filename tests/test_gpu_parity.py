@@ -226,15 +226,18 @@ def test_split_feature_counts(hgb, torch, F, B, missing, fused):
     run_level_both(hgb, torch, w, check_exact_gain=True, fused=fused)
 
 
-@pytest.mark.parametrize("n_const", [0, 16_000])
-def test_split_reduce_wide_ties(hgb, torch, n_const):
-    """16,400 identical features, so the root's per-feature winners all tie
-    on gain and the node's reduction runs 1,024 threads with several entries
-    each: the smallest feature wins.  With the first n_const features made
-    constant (no valid split) the first of the others wins."""
-    say("split reduce ties", n_const)
+@pytest.mark.parametrize("F,n_const", [(16_400, 0), (16_400, 16_000), (200, 0), (200, 150), (256, 255)])
+def test_split_reduce_wide_ties(hgb, torch, F, n_const):
+    """F identical features, so the root's per-feature winners all tie on
+    gain: the smallest feature wins.  16,400 features run the node's
+    reduction on 1,024 threads with several entries each; 200 and 256
+    features (50 and 64 entries of four features) run it on one wave with
+    lane exchanges.  With the first n_const features made constant (no valid
+    split) the first of the others wins (256 and 255: only the last lane's
+    entry is valid)."""
+    say("split reduce ties", F, n_const)
     rng = np.random.default_rng(77)
-    n, F = 2048, 16_400
+    n = 2048
     col = rng.integers(0, 256, n).astype(np.uint8)
     bins = np.tile(col, (F, 1))
     bins[:n_const] = 7
