@@ -6,7 +6,11 @@ without the missing slot, one- and two-byte bins, roots and levels of up to
 included.  Then whole trees grown on the device (depthwise and oblivious,
 one call per level or three) on random shapes, level by level against the
 oracle's trees.  The shapes are drawn once from a fixed seed, so every run
-checks the same cases; the ids name them."""
+checks the same cases; the ids name them.  HGB_SWEEP_SEED=k draws both
+sweeps from seeds derived from k instead, for a run over shapes not seen
+before (the ids still name each case)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -16,6 +20,8 @@ from test_gpu_level_split import assert_records, oracle_oblivious_tree
 from test_gpu_parity import assert_splits, oracle_tree, run_level_both, run_root_both, say
 
 pytestmark = pytest.mark.gpu
+
+_RESEED = os.environ.get("HGB_SWEEP_SEED")
 
 
 def _cases(count=200, seed=2718):
@@ -37,7 +43,7 @@ def _cases(count=200, seed=2718):
     return out
 
 
-CASES = _cases()
+CASES = _cases() if _RESEED is None else _cases(seed=2 * int(_RESEED) + 100_003)
 
 
 @pytest.mark.parametrize("seed,n,F,B,missing,children,u16,bits", CASES,
@@ -69,7 +75,7 @@ def _tree_cases(count=120, seed=3141):
     return out
 
 
-TREES = _tree_cases()
+TREES = _tree_cases() if _RESEED is None else _tree_cases(seed=2 * int(_RESEED) + 100_004)
 
 
 @pytest.mark.parametrize("seed,n,F,B,missing,u16,depth,oblivious,fused,bits", TREES,
